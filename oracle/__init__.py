@@ -1,0 +1,31 @@
+"""Oracle for the forward NHWC convolution (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the HIP library and never
+imports it.  Every function cites the page passage it follows; the pages are
+three API documentation pages of Modular's kernel library:
+
+  page 1  "dispatch_amd_4wave_conv2d"          (MI355X dispatcher)
+  page 2  "dispatch_fused_im2col_conv2d_apple" (Apple fused online-im2col conv)
+  page 3  "conv_transposed_gpu"                (cuDNN transposed conv)
+
+Parity status of each function (what pins it is in tests/test_oracle_pins.py):
+  conv2d, conv2d_points  pinned: brute force, hand-worked example, 1x1 matmul
+                          closed form, delta filters, border counts,
+                          stride subsampling, layout and bilinearity
+                          invariants, residual identities.
+  filter_to_nk           pinned: element-wise brute force from the index
+                          formula on small filters.
+  gate_accepts           pinned: hand-written case table from page 1's
+                          Parameters/Args rules (tests/golden/gate_cases.txt).
+"""
+from .reference import (  # noqa: F401
+    DTYPES,
+    conv2d,
+    conv2d_points,
+    filter_dims_rscf,
+    filter_to_nk,
+    gate_accepts,
+    num_threads,
+    out_size,
+)

@@ -1,0 +1,196 @@
+"""Oracle functions (TEST INFRASTRUCTURE ONLY; see the package docstring).
+
+Inputs are torch tensors in their stored dtype (bfloat16, float16 or
+float8_e4m3fn).  They are upcast to float64 by torch, which is exact for all
+three formats (the fp8 decode is checked code by code against the OCP
+definition in the tests), and handed to the C oracle in conv_oracle.c.
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from . import build as _build
+
+_LIB = None
+
+# Element types the MI355X dispatcher accepts, and the output type each one
+# produces: page 1 ("dispatch_amd_4wave_conv2d"), Parameters section,
+# input_type / filter_type / output_type.
+DTYPES = {
+    "bfloat16": "bfloat16",
+    "float16": "float16",
+    "float8_e4m3fn": "bfloat16",
+}
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        i64, dp, ip = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.c_int
+        lib.oracle_conv2d_f64.argtypes = [
+            dp, i64, i64, i64, i64, dp, ip, i64, i64, i64, i64, i64, i64, i64,
+            dp, ctypes.c_double, dp, i64, i64]
+        lib.oracle_conv2d_f64.restype = ctypes.c_int
+        lib.oracle_conv2d_points_f64.argtypes = [
+            dp, i64, i64, i64, i64, dp, ip, i64, i64, i64, i64, i64, i64, i64,
+            dp, ctypes.c_double, ctypes.POINTER(ctypes.c_int64), i64, dp, i64, i64]
+        lib.oracle_conv2d_points_f64.restype = ctypes.c_int
+        lib.oracle_out_size.argtypes = [i64, i64, i64, i64]
+        lib.oracle_out_size.restype = i64
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_lib().oracle_num_threads())
+
+
+def out_size(n_in: int, k: int, stride: int, pad: int) -> int:
+    """Ho = floor((H + 2p - R) / stride) + 1, or 0 when the padded input is
+    shorter than the filter.  Floor rounding is the standard reading; the
+    pages state no formula (page 1, Args: stride and symmetric_padding)."""
+    return int(_lib().oracle_out_size(n_in, k, stride, pad))
+
+
+def filter_dims_rscf(w_shape, filter_is_fcrs: bool):
+    """(R, S, C_in, C_out) of a filter stored as FCRS [C_out, C_in, R, S] or
+    RSCF [R, S, C_in, C_out] (page 2, Parameters: filter_is_fcrs)."""
+    if filter_is_fcrs:
+        f, c, r, s = w_shape
+    else:
+        r, s, c, f = w_shape
+    return int(r), int(s), int(c), int(f)
+
+
+def _f64(t):
+    if isinstance(t, np.ndarray):
+        return np.ascontiguousarray(t, dtype=np.float64)
+    return np.ascontiguousarray(t.detach().cpu().to(torch.float64).numpy())
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _prep(x, w, filter_is_fcrs, stride, padding, source):
+    sh, sw = (stride, stride) if isinstance(stride, int) else stride
+    ph, pw = (padding, padding) if isinstance(padding, int) else padding
+    x64 = _f64(x)
+    w64 = _f64(w)
+    n, h, wd, c = x64.shape
+    r, s, cw, f = filter_dims_rscf(w64.shape, filter_is_fcrs)
+    if cw != c:
+        raise ValueError(f"filter C_in {cw} != input C_in {c}")
+    ho, wo = out_size(h, r, sh, ph), out_size(wd, s, sw, pw)
+    src64 = None if source is None else _f64(source)
+    if src64 is not None and src64.shape != (n, ho, wo, f):
+        raise ValueError("source must have the output's NHWC shape")
+    return x64, w64, (n, h, wd, c, r, s, f, sh, sw, ph, pw, ho, wo), src64
+
+
+def conv2d(x, w, *, filter_is_fcrs: bool, stride=1, padding=0, source=None,
+           beta: float = 0.0) -> np.ndarray:
+    """Forward convolution of an NHWC input with an RSCF/FCRS filter, fp64.
+
+    Follows page 1 ("dispatch_amd_4wave_conv2d"): summary (D = Conv + beta *
+    source with an NHWC source of the output's shape) and Args (NHWC input and
+    output, FCRS or RSCF filter, stride [sh, sw], symmetric padding [ph, pw]).
+    Returns the unrounded float64 result, shape [N, Ho, Wo, C_out].
+    """
+    x64, w64, d, src64 = _prep(x, w, filter_is_fcrs, stride, padding, source)
+    n, h, wd, c, r, s, f, sh, sw, ph, pw, ho, wo = d
+    y = np.zeros((n, ho, wo, f), dtype=np.float64)
+    rc = _lib().oracle_conv2d_f64(
+        _ptr(x64), n, h, wd, c, _ptr(w64), int(bool(filter_is_fcrs)), r, s, f,
+        sh, sw, ph, pw, None if src64 is None else _ptr(src64), float(beta),
+        _ptr(y), ho, wo)
+    if rc != 0:
+        raise ValueError("oracle rejected the convolution arguments")
+    return y
+
+
+def conv2d_points(x, w, pix, *, filter_is_fcrs: bool, stride=1, padding=0,
+                  source=None, beta: float = 0.0) -> np.ndarray:
+    """The same definition as conv2d, evaluated only at the flattened output
+    pixels pix[i] = (n*Ho + oh)*Wo + ow.  Returns [len(pix), C_out] float64."""
+    x64, w64, d, src64 = _prep(x, w, filter_is_fcrs, stride, padding, source)
+    n, h, wd, c, r, s, f, sh, sw, ph, pw, ho, wo = d
+    pix = np.ascontiguousarray(np.asarray(pix, dtype=np.int64))
+    y = np.zeros((pix.shape[0], f), dtype=np.float64)
+    rc = _lib().oracle_conv2d_points_f64(
+        _ptr(x64), n, h, wd, c, _ptr(w64), int(bool(filter_is_fcrs)), r, s, f,
+        sh, sw, ph, pw, None if src64 is None else _ptr(src64), float(beta),
+        pix.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), pix.shape[0],
+        _ptr(y), ho, wo)
+    if rc != 0:
+        raise ValueError("oracle rejected the convolution arguments")
+    return y
+
+
+def filter_to_nk(w: torch.Tensor, filter_is_fcrs: bool, k_pad: int = None) -> torch.Tensor:
+    """The filter as the (C_out, K = R*S*C_in) "NK" matrix of page 2
+    ("dispatch_fused_im2col_conv2d_apple", summary), k ordered (r, s, ci)
+    with ci fastest, i.e. NK[co, (r*S + s)*C_in + ci] = Wt(r, s, ci, co).
+
+    A pure bit copy: the element bits are moved, never converted.  Columns
+    K..k_pad-1 (when k_pad > K) are zero.  Returns a CPU tensor of w's dtype.
+    """
+    r, s, c, f = filter_dims_rscf(w.shape, filter_is_fcrs)
+    k = r * s * c
+    bits = w.detach().cpu().contiguous()
+    bits = bits.view(torch.int16) if bits.element_size() == 2 else bits.view(torch.uint8)
+    if filter_is_fcrs:   # [F, C, R, S] -> [F, R, S, C]
+        nk = bits.permute(0, 2, 3, 1)
+    else:                # [R, S, C, F] -> [F, R, S, C]
+        nk = bits.permute(3, 0, 1, 2)
+    nk = nk.reshape(f, k)
+    if k_pad is not None and k_pad > k:
+        nk = torch.cat([nk, torch.zeros(f, k_pad - k, dtype=nk.dtype)], dim=1)
+    return nk.contiguous().view(w.dtype)
+
+
+def gate_accepts(dtype: str, filter_dtype: str, out_dtype: str, in_nhwc,
+                 filt_dims, filter_is_fcrs: bool, out_nhwc, stride, dilation,
+                 padding, groups) -> bool:
+    """Whether page 1's dispatcher would take the call.
+
+    Rules, all from page 1 ("dispatch_amd_4wave_conv2d"):
+      Parameters: input dtype is float8_e4m3fn, bfloat16 or float16; the
+        filter dtype equals it; the output dtype is bfloat16 for fp8 inputs,
+        otherwise the input dtype.
+      Args: stride (1,1) or (2,2); dilation (1,1); symmetric padding (0,0),
+        (1,1) or (2,2); groups 1; the filter's C_in equals the input's; the
+        output is NHWC [N, Ho, Wo, C_out].
+    Reading where the page is silent: a filter larger than the padded input
+    (Ho or Wo < 1) or with R or S < 1 is not a convolution and is declined;
+    an empty batch or C_out = 0 is accepted (nothing to compute).
+    """
+    if dtype not in DTYPES or filter_dtype != dtype or out_dtype != DTYPES[dtype]:
+        return False
+    if tuple(stride) not in ((1, 1), (2, 2)):
+        return False
+    if tuple(dilation) != (1, 1):
+        return False
+    if tuple(padding) not in ((0, 0), (1, 1), (2, 2)):
+        return False
+    if groups != 1:
+        return False
+    n, h, w, c = in_nhwc
+    r, s, cf, f = filter_dims_rscf(filt_dims, filter_is_fcrs)
+    if min(n, h, w, c, f) < 0 or r < 1 or s < 1:
+        return False
+    if cf != c:
+        return False
+    ho = out_size(h, r, stride[0], padding[0])
+    wo = out_size(w, s, stride[1], padding[1])
+    if ho < 1 or wo < 1:
+        return False
+    return tuple(out_nhwc) == (n, ho, wo, f)

@@ -1,0 +1,365 @@
+"""Pins the oracle to facts other than itself (CPU only).
+
+Each test checks the oracle against something the pages or mathematics fix:
+hand-worked examples, brute force written independently, closed forms,
+special cases, invariants, or a library routine.  A plausible mistake in the
+oracle (dropped term, wrong sign or index, transposed operand, wrong padding
+side, flipped filter) fails at least one of them.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(1234)
+
+
+def _rand(shape):
+    return RNG.standard_normal(shape)
+
+
+def _brute(x, w, fcrs, st, p, src=None, beta=0.0):
+    """Pure-Python convolution over an explicitly zero-padded copy, each sum
+    correctly rounded by math.fsum.  Filter read with natural 4-D indexing.
+    st and p are ints or (height, width) pairs."""
+    sh, sw = (st, st) if isinstance(st, int) else st
+    ph, pw = (p, p) if isinstance(p, int) else p
+    n_, h, wd, c = x.shape
+    if fcrs:
+        f, _, r_, s_ = w.shape
+        tap = lambda r, s, ci, co: w[co, ci, r, s]  # noqa: E731
+    else:
+        r_, s_, _, f = w.shape
+        tap = lambda r, s, ci, co: w[r, s, ci, co]  # noqa: E731
+    xp = np.zeros((n_, h + 2 * ph, wd + 2 * pw, c))
+    xp[:, ph:ph + h, pw:pw + wd, :] = x
+    ho = (h + 2 * ph - r_) // sh + 1
+    wo = (wd + 2 * pw - s_) // sw + 1
+    y = np.zeros((n_, ho, wo, f))
+    for n, oh, ow, co in itertools.product(range(n_), range(ho), range(wo), range(f)):
+        terms = [xp[n, oh * sh + r, ow * sw + s, ci] * tap(r, s, ci, co)
+                 for r in range(r_) for s in range(s_) for ci in range(c)]
+        v = math.fsum(terms)
+        if src is not None:
+            v = v + beta * src[n, oh, ow, co]
+        y[n, oh, ow, co] = v
+    return y
+
+
+def _rel(a, b):
+    scale = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / scale)
+
+
+# ----------------------------------------------------------------- golden
+def _read_handworked():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "handworked_conv.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tag, *vals = line.split()
+            if tag == "case":
+                cur = dict(name=vals[0], dims=[int(v) for v in vals[1:10]],
+                           beta=float(vals[10]))
+                cases.append(cur)
+            elif vals == ["none"]:
+                cur[tag] = None
+            else:
+                cur[tag] = np.array([float(v) for v in vals])
+    return cases
+
+
+@pytest.mark.parametrize("case", _read_handworked(), ids=lambda c: c["name"])
+def test_handworked_examples(case):
+    n, h, w, c, r, s, f, st, p = case["dims"]
+    x = case["x"].reshape(n, h, w, c)
+    wt = case["w"].reshape(r, s, c, f)
+    ho = (h + 2 * p - r) // st + 1
+    wo = (w + 2 * p - s) // st + 1
+    src = None if case["src"] is None else case["src"].reshape(n, ho, wo, f)
+    y = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p,
+                      source=src, beta=case["beta"])
+    np.testing.assert_array_equal(y.reshape(-1), case["y"])
+    # the same filter stored FCRS must give the same bits
+    y2 = oracle.conv2d(x, wt.transpose(3, 2, 0, 1).copy(), filter_is_fcrs=True,
+                       stride=st, padding=p, source=src, beta=case["beta"])
+    np.testing.assert_array_equal(y2, y)
+
+
+# ------------------------------------------------------------- brute force
+BRUTE_CASES = [
+    # N H W C F R S st p fcrs residual
+    (1, 5, 5, 1, 1, 3, 3, 1, 1, False, False),
+    (2, 6, 7, 3, 2, 3, 3, 1, 1, True, False),
+    (1, 7, 6, 2, 3, 5, 5, 1, 2, False, True),
+    (2, 7, 7, 4, 2, 3, 3, 2, 1, True, True),
+    (1, 6, 6, 2, 2, 2, 2, 2, 0, False, False),
+    (1, 7, 5, 3, 1, 1, 1, 2, 0, True, False),
+    (2, 4, 5, 2, 3, 3, 2, 1, 2, False, False),
+    (1, 5, 7, 4, 2, 5, 3, 2, 2, True, True),
+    (1, 3, 3, 1, 2, 5, 5, 1, 2, False, False),
+    (1, 7, 7, 1, 1, 2, 3, 1, 0, True, False),
+]
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES)
+def test_brute_force_tiny(case):
+    n, h, w, c, f, r, s, st, p, fcrs, resid = case
+    x = _rand((n, h, w, c))
+    wt = _rand((f, c, r, s) if fcrs else (r, s, c, f))
+    ho = (h + 2 * p - r) // st + 1
+    wo = (w + 2 * p - s) // st + 1
+    src = _rand((n, ho, wo, f)) if resid else None
+    beta = 0.75 if resid else 0.0
+    y = oracle.conv2d(x, wt, filter_is_fcrs=fcrs, stride=st, padding=p,
+                      source=src, beta=beta)
+    yb = _brute(x, wt, fcrs, st, p, src, beta)
+    assert y.shape == yb.shape
+    assert _rel(y, yb) <= 1e-12
+
+
+@pytest.mark.parametrize("st,p,fcrs", [((1, 2), (2, 0), False), ((2, 1), (0, 1), True),
+                                       ((3, 1), (1, 2), False)])
+def test_brute_force_anisotropic(st, p, fcrs):
+    """Unequal height/width strides and paddings: the oracle is general even
+    though the dispatcher only accepts equal pairs; pins that the height
+    parameters act on R/H and the width parameters on S/W."""
+    x = _rand((2, 7, 6, 3))
+    wt = _rand((2, 3, 3, 2) if fcrs else (3, 3, 3, 2))
+    y = oracle.conv2d(x, wt, filter_is_fcrs=fcrs, stride=st, padding=p)
+    yb = _brute(x, wt, fcrs, st, p)
+    assert y.shape == yb.shape
+    assert _rel(y, yb) <= 1e-12
+
+
+# ------------------------------------------------------ library routine
+@pytest.mark.parametrize("n,h,w,c,f,r,s,st,p", [
+    (2, 13, 11, 8, 6, 3, 3, 1, 1),
+    (1, 16, 16, 16, 5, 5, 5, 2, 2),
+    (3, 9, 12, 4, 7, 3, 2, 2, 0),
+    (1, 20, 20, 24, 3, 3, 3, 1, 0),
+])
+def test_matches_torch_conv2d_f64(n, h, w, c, f, r, s, st, p):
+    x = torch.randn(n, h, w, c, dtype=torch.float64)
+    wf = torch.randn(f, c, r, s, dtype=torch.float64)
+    ref = torch.nn.functional.conv2d(x.permute(0, 3, 1, 2), wf, stride=st,
+                                     padding=p).permute(0, 2, 3, 1).numpy()
+    y = oracle.conv2d(x, wf, filter_is_fcrs=True, stride=st, padding=p)
+    assert _rel(y, ref) <= 1e-12
+    y2 = oracle.conv2d(x, wf.permute(2, 3, 1, 0).contiguous(), filter_is_fcrs=False,
+                       stride=st, padding=p)
+    np.testing.assert_array_equal(y2, y)
+
+
+# ----------------------------------------------------------- closed forms
+@pytest.mark.parametrize("fcrs", [False, True])
+def test_1x1_stride1_is_matmul(fcrs):
+    n, h, w, c, f = 2, 5, 6, 7, 9
+    x = _rand((n, h, w, c))
+    wm = _rand((c, f))
+    wt = wm.T.reshape(f, c, 1, 1).copy() if fcrs else wm.reshape(1, 1, c, f).copy()
+    y = oracle.conv2d(x, wt, filter_is_fcrs=fcrs, stride=1, padding=0)
+    ref = (x.reshape(n * h * w, c) @ wm).reshape(n, h, w, f)
+    assert _rel(y, ref) <= 1e-13
+
+
+@pytest.mark.parametrize("k,st", [(1, 1), (3, 1), (5, 1), (3, 2), (5, 2)])
+def test_centered_delta_reproduces_input(k, st):
+    p = (k - 1) // 2
+    if p > 2:
+        pytest.skip("padding above 2")
+    n, h, w, c = 2, 7, 9, 5
+    x = _rand((n, h, w, c))
+    wt = np.zeros((k, k, c, c))
+    for ci in range(c):
+        wt[p, p, ci, ci] = 1.0
+    y = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p)
+    np.testing.assert_array_equal(y, x[:, ::st, ::st, :])
+
+
+@pytest.mark.parametrize("r0,s0,st,p", [(0, 0, 1, 1), (2, 1, 1, 1), (0, 2, 1, 2),
+                                       (4, 3, 1, 2), (1, 0, 2, 1), (2, 2, 2, 0)])
+def test_off_center_delta_pins_orientation(r0, s0, st, p):
+    """A single tap at (r0, s0) moves the input by (r0 - p, s0 - p): pins no
+    filter flip, the padding side and R <-> H, S <-> W."""
+    n, h, w, c, k = 1, 6, 7, 3, 5 if max(r0, s0) > 2 else 3
+    x = _rand((n, h, w, c))
+    wt = np.zeros((k, k, c, c))
+    for ci in range(c):
+        wt[r0, s0, ci, ci] = 1.0
+    y = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p)
+    ho, wo = y.shape[1:3]
+    for oh in range(ho):
+        for ow in range(wo):
+            ih, iw = oh * st - p + r0, ow * st - p + s0
+            want = x[0, ih, iw] if (0 <= ih < h and 0 <= iw < w) else np.zeros(c)
+            np.testing.assert_array_equal(y[0, oh, ow], want)
+
+
+@pytest.mark.parametrize("k,st,p", [(3, 1, 1), (3, 2, 1), (5, 1, 2), (5, 2, 2),
+                                    (3, 1, 0), (2, 2, 2), (1, 1, 2)])
+def test_all_ones_border_counts(k, st, p):
+    n, h, w, c, f = 1, 7, 8, 6, 2
+    x = np.ones((n, h, w, c))
+    wt = np.ones((k, k, c, f))
+    y = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p)
+
+    def cnt(o, size):
+        return sum(1 for r in range(k) if 0 <= o * st - p + r < size)
+
+    for oh in range(y.shape[1]):
+        for ow in range(y.shape[2]):
+            assert np.all(y[0, oh, ow] == c * cnt(oh, h) * cnt(ow, w))
+
+
+# ------------------------------------------------------------- invariants
+@pytest.mark.parametrize("k,p", [(3, 1), (5, 2), (3, 0), (2, 1)])
+def test_stride2_subsamples_stride1(k, p):
+    x = _rand((2, 9, 8, 3))
+    wt = _rand((k, k, 3, 4))
+    y1 = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=1, padding=p)
+    y2 = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=2, padding=p)
+    np.testing.assert_array_equal(y2, y1[:, ::2, ::2, :][:, :y2.shape[1], :y2.shape[2]])
+
+
+def test_bilinear_in_input_and_filter():
+    x1, x2 = _rand((2, 8, 7, 5)), _rand((2, 8, 7, 5))
+    w1, w2 = _rand((3, 3, 5, 4)), _rand((3, 3, 5, 4))
+    a, b = 0.75, -1.5
+    cv = lambda x, w: oracle.conv2d(x, w, filter_is_fcrs=False, stride=1, padding=1)  # noqa: E731
+    assert _rel(cv(a * x1 + b * x2, w1), a * cv(x1, w1) + b * cv(x2, w1)) <= 1e-12
+    assert _rel(cv(x1, a * w1 + b * w2), a * cv(x1, w1) + b * cv(x1, w2)) <= 1e-12
+
+
+def test_residual_identities():
+    x, wt = _rand((2, 6, 6, 4)), _rand((3, 3, 4, 5))
+    src = _rand((2, 6, 6, 5))
+    y = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=1, padding=1)
+    d0 = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=1, padding=1, source=src, beta=0.0)
+    np.testing.assert_array_equal(d0, y)
+    d1 = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=1, padding=1, source=src, beta=1.0)
+    np.testing.assert_array_equal(d1, y + src)
+    dh = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=1, padding=1, source=src, beta=-0.5)
+    np.testing.assert_array_equal(dh, y - 0.5 * src)
+
+
+def test_points_equal_full():
+    x, wt = _rand((2, 9, 10, 3)), _rand((4, 3, 3, 3))
+    src = _rand((2, 5, 5, 4))
+    y = oracle.conv2d(x, wt, filter_is_fcrs=True, stride=2, padding=1, source=src, beta=0.3)
+    pix = [0, 7, 24, 25, 49]
+    yp = oracle.conv2d_points(x, wt, pix, filter_is_fcrs=True, stride=2, padding=1,
+                              source=src, beta=0.3)
+    np.testing.assert_array_equal(yp, y.reshape(-1, 4)[pix])
+
+
+def test_empty_and_degenerate():
+    wt = _rand((3, 3, 4, 2))
+    y = oracle.conv2d(np.zeros((0, 5, 5, 4)), wt, filter_is_fcrs=False, stride=1, padding=1)
+    assert y.shape == (0, 5, 5, 2)
+    y = oracle.conv2d(_rand((1, 5, 5, 0)), np.zeros((3, 3, 0, 2)), filter_is_fcrs=False,
+                      stride=1, padding=1)
+    np.testing.assert_array_equal(y, np.zeros((1, 5, 5, 2)))
+    assert oracle.out_size(2, 5, 1, 1) == 0
+    assert oracle.out_size(56, 3, 2, 1) == 28
+    assert oracle.out_size(7, 3, 2, 0) == 3
+
+
+# ----------------------------------------------------------- input decode
+def test_fp8_e4m3fn_decode_all_codes():
+    """torch's fp8 -> float64 upcast (the oracle's input path) against the OCP
+    E4M3 definition: bias 7, subnormals at exponent 0, no infinities,
+    S.1111.111 is NaN, largest finite 448."""
+    codes = torch.arange(256, dtype=torch.int64).to(torch.uint8)
+    got = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(256):
+        sign = -1.0 if b >> 7 else 1.0
+        e, m = (b >> 3) & 0xF, b & 0x7
+        if e == 15 and m == 7:
+            assert math.isnan(got[b])
+            continue
+        want = sign * (m / 8.0) * 2.0 ** -6 if e == 0 else sign * (1 + m / 8.0) * 2.0 ** (e - 7)
+        assert got[b] == want, (b, got[b], want)
+    assert np.nanmax(np.abs(got)) == 448.0
+
+
+def test_bf16_fp16_decode_samples():
+    bits = torch.tensor([0x0000, 0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F], dtype=torch.int32)
+    bf = bits.to(torch.int16).view(torch.bfloat16).to(torch.float64).numpy()
+    want = [np.frombuffer(np.array([int(b) << 16], dtype=np.uint32).tobytes(), np.float32)[0]
+            for b in bits.tolist()]
+    np.testing.assert_array_equal(bf, np.array(want, dtype=np.float64))
+    hb = torch.tensor([0x3C00, 0x0001, 0x7BFF, 0xC000], dtype=torch.int32).to(torch.int16)
+    np.testing.assert_array_equal(hb.view(torch.float16).to(torch.float64).numpy(),
+                                  [1.0, 2.0 ** -24, 65504.0, -2.0])
+
+
+# ------------------------------------------------------------ NK transpose
+@pytest.mark.parametrize("fcrs", [False, True])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float8_e4m3fn])
+def test_filter_to_nk_brute(fcrs, dtype):
+    r, s, c, f = 3, 2, 5, 4
+    shape = (f, c, r, s) if fcrs else (r, s, c, f)
+    w = torch.randn(shape).clamp(-400, 400).to(dtype)
+    k = r * s * c
+    nk = oracle.filter_to_nk(w, fcrs, k_pad=k + 6)
+    assert nk.shape == (f, k + 6) and nk.dtype == dtype
+    nkb = nk.view(torch.uint8 if dtype == torch.float8_e4m3fn else torch.int16)
+    wb = w.view(nkb.dtype)
+    for co in range(f):
+        for rr in range(r):
+            for ss in range(s):
+                for ci in range(c):
+                    src = wb[co, ci, rr, ss] if fcrs else wb[rr, ss, ci, co]
+                    assert nkb[co, (rr * s + ss) * c + ci] == src
+        assert torch.all(nkb[co, k:] == 0)
+
+
+# --------------------------------------------------------------- the gate
+def _gate_cases():
+    rows = []
+    with open(os.path.join(GOLDEN, "gate_cases.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            t = line.split()
+            rows.append(dict(expect=bool(int(t[0])), dt=t[1], fdt=t[2], odt=t[3],
+                             stride=(int(t[4]), int(t[5])), dil=(int(t[6]), int(t[7])),
+                             pad=(int(t[8]), int(t[9])), groups=int(t[10]),
+                             note=" ".join(t[11:])))
+    return rows
+
+
+@pytest.mark.parametrize("row", _gate_cases(), ids=lambda r: r["note"])
+def test_gate_table(row):
+    n, h, w, c, f, k = 2, 9, 9, 32, 48, 3
+    st, p = row["stride"][0], row["pad"][0]
+    ho = (h + 2 * p - k) // st + 1
+    ok = oracle.gate_accepts(row["dt"], row["fdt"], row["odt"], (n, h, w, c),
+                             (k, k, c, f), False, (n, ho, ho, f), row["stride"],
+                             row["dil"], row["pad"], row["groups"])
+    assert ok == row["expect"]
+
+
+def test_gate_shape_rules():
+    base = dict(dtype="bfloat16", filter_dtype="bfloat16", out_dtype="bfloat16",
+                filter_is_fcrs=False, stride=(1, 1), dilation=(1, 1),
+                padding=(1, 1), groups=1)
+    g = lambda i, fd, o, **kw: oracle.gate_accepts(  # noqa: E731
+        in_nhwc=i, filt_dims=fd, out_nhwc=o, **{**base, **kw})
+    assert g((2, 8, 8, 16), (3, 3, 16, 4), (2, 8, 8, 4))
+    assert not g((2, 8, 8, 16), (3, 3, 32, 4), (2, 8, 8, 4))        # C_in mismatch
+    assert not g((2, 8, 8, 16), (3, 3, 16, 4), (2, 8, 8, 5))        # C_out mismatch
+    assert not g((2, 8, 8, 16), (3, 3, 16, 4), (2, 7, 8, 4))        # wrong Ho
+    assert g((2, 8, 8, 16), (4, 16, 3, 3), (2, 8, 8, 4), filter_is_fcrs=True)
+    assert not g((1, 1, 1, 16), (5, 5, 16, 4), (1, 0, 0, 4))        # filter > padded input
+    assert g((0, 8, 8, 16), (3, 3, 16, 4), (0, 8, 8, 4))            # empty batch
