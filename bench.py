@@ -1,0 +1,265 @@
+"""Benchmark: forward NHWC convolution as an implicit GEMM on one MI355X.
+
+One step = the whole path on one batch: the host gate, the filter transpose
+to NK (conv2d_filter_to_nk) and the implicit-GEMM kernel with its fused
+epilogue (conv2d_fwd_nk) -- exactly what conv2d_fwd enqueues, split in two
+calls so HIP events can bracket the GEMM kernel alone.
+
+Headline workload: the ResNet-style 3x3 body conv (N=32, 56x56, 64->64,
+stride 1, padding 1, bf16, FCRS filter).  value = 2*N*Ho*Wo*C_out*R*S*C_in /
+step time, in TFLOP/s.  Inputs are resident in HBM: each step uses the next
+of several identical buffer sets whose total size (>= 640 MB) exceeds the
+256 MB Infinity Cache and the L2s, so no step finds its operands in cache.
+
+Also reported on the same line:
+  roofline      the GEMM kernel's algorithmic bytes (or FLOPs) per launch over
+                its mean duration from HIP events, against the MI355X peak;
+  cpu_baseline  the fp64 oracle timed on this host's cores on the same
+                workload (the full batch);
+  shapes        the same measurement for each of the five named workloads.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HEADLINE = "resnet_3x3_64c_n32"
+PEAK = {"bf16_tflops": 2516.6, "fp16_tflops": 2516.6, "fp8_tflops": 5033.2,
+        "hbm_gbs": 8000.0}
+RIDGE_BF16 = PEAK["bf16_tflops"] * 1e12 / (PEAK["hbm_gbs"] * 1e9)
+ROTATE_BYTES = 640 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "igemm_fwd_resnet_3x3_64c_n32_traffic.txt")
+
+
+def _source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "implicit_gemm_nhwc_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()
+
+
+def _algorithmic(spec):
+    """FLOPs and bytes (input + filter + source + output, each once)."""
+    n, h, w, c, f, r, s = (spec[k] for k in ("N", "H", "W", "C", "F", "R", "S"))
+    ho, wo = spec["out_hw"]
+    eb = 1 if spec["dtype"] == "float8_e4m3fn" else 2
+    flops = 2 * n * ho * wo * f * r * s * c
+    nbytes = n * h * w * c * eb + r * s * c * f * eb + n * ho * wo * f * 2
+    if spec["src"] is not None:
+        nbytes += n * ho * wo * f * 2
+    return flops, nbytes
+
+
+def _bound(spec, flops, nbytes):
+    peak_t = PEAK["fp8_tflops"] if spec["dtype"] == "float8_e4m3fn" else PEAK["bf16_tflops"]
+    ridge = peak_t * 1e12 / (PEAK["hbm_gbs"] * 1e9)
+    return ("mfma" if flops / nbytes >= ridge else "hbm"), peak_t
+
+
+class Bufsets:
+    """Identical copies of one workload's tensors, rotated across steps."""
+
+    def __init__(self, torch, igc, spec, x, w, src):
+        dev = torch.device("cuda:0")
+        self.spec = spec
+        self.fcrs = spec["fcrs"]
+        n, f = spec["N"], spec["F"]
+        ho, wo = spec["out_hw"]
+        out_dt = {"bfloat16": torch.bfloat16, "float16": torch.float16,
+                  "float8_e4m3fn": torch.bfloat16}[spec["dtype"]]
+        nk_bytes = igc.conv2d_workspace_bytes(w.shape, self.fcrs, w.dtype)
+        per_set = (x.numel() * x.element_size() + w.numel() * w.element_size() +
+                   nk_bytes + n * ho * wo * f * 2 * (2 if src is not None else 1))
+        self.nsets = max(2, -(-ROTATE_BYTES // per_set))
+        xd, wd = x.to(dev), w.to(dev)
+        sd = None if src is None else src.to(dev)
+        self.sets = []
+        for _ in range(self.nsets):
+            self.sets.append(dict(
+                x=xd.clone(), w=wd.clone(),
+                nk=torch.empty(max(nk_bytes, 16), dtype=torch.uint8, device=dev),
+                y=torch.empty((n, ho, wo, f), dtype=out_dt, device=dev),
+                src=None if sd is None else sd.clone()))
+        torch.cuda.synchronize()
+
+    def step(self, igc, i, ev=None):
+        b = self.sets[i % self.nsets]
+        sp = self.spec
+        rc = igc.conv2d_filter_to_nk(b["w"], b["nk"], filter_is_fcrs=self.fcrs)
+        if rc != 1:
+            raise RuntimeError(f"conv2d_filter_to_nk returned {rc}")
+        if ev is not None:
+            ev[0].record()
+        rc = igc.conv2d_fwd_nk(b["x"], b["nk"], b["w"].shape, b["y"], filter_is_fcrs=self.fcrs,
+                               stride=sp["stride"], padding=sp["pad"], source=b["src"],
+                               beta=sp["beta"])
+        if ev is not None:
+            ev[1].record()
+        if rc != 1:
+            raise RuntimeError(f"conv2d_fwd_nk returned {rc}")
+
+
+def measure(torch, igc, name, steps, warmup):
+    import datagen
+
+    spec, x, w, src = datagen.make_workload(name)
+    bufs = Bufsets(torch, igc, spec, x, w, src)
+    for i in range(warmup):
+        bufs.step(igc, i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        bufs.step(igc, warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = sorted(e0.elapsed_time(e1) for e0, e1 in events)
+    flops, nbytes = _algorithmic(spec)
+    ms_step = (t1 - t0) * 1e3 / steps
+    kmean = sum(kern_ms) / len(kern_ms)
+    bound, peak_t = _bound(spec, flops, nbytes)
+    res = dict(workload=name, dtype=spec["dtype"], ms_per_step=ms_step,
+               step_tflops=flops / (ms_step * 1e-3) / 1e12,
+               kernel_us_mean=kmean * 1e3, kernel_us_median=kern_ms[len(kern_ms) // 2] * 1e3,
+               kernel_tflops=flops / (kmean * 1e-3) / 1e12,
+               kernel_gbs=nbytes / (kmean * 1e-3) / 1e9, flops=flops, alg_bytes=nbytes,
+               bound=bound, rotating_sets=bufs.nsets)
+    res["frac_mfma"] = res["kernel_tflops"] / peak_t
+    res["frac_hbm"] = res["kernel_gbs"] / PEAK["hbm_gbs"]
+    del bufs
+    torch.cuda.empty_cache()
+    return res, spec, x, w
+
+
+def cpu_baseline(spec, x, w, budget_s=10.0):
+    """The fp64 oracle, as it stands, on the full batch of the workload."""
+    import oracle
+
+    flops = _algorithmic(spec)[0]
+    runs, t_total = 0, 0.0
+    while runs < 1 or (t_total < budget_s and runs < 5):
+        t0 = time.perf_counter()
+        oracle.conv2d(x, w, filter_is_fcrs=spec["fcrs"], stride=spec["stride"],
+                      padding=spec["pad"])
+        t_total += time.perf_counter() - t0
+        runs += 1
+    per = t_total / runs
+    return {"value": flops / per / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"full batch of {spec['N']} images, {runs} run(s), "
+                      f"{per:.2f} s per run (fp64 direct convolution, OpenMP)"}
+
+
+def _traffic(res):
+    """HBM bytes per launch from committed FETCH_SIZE/WRITE_SIZE counters, if
+    they were taken on the current kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.loads(fh.read().split("---json---", 1)[1])
+    except (IndexError, ValueError):
+        return None
+    if rec.get("source_sha256") != _source_digest():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-shapes", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="run only this workload's timed loop (for profiling); prints one line")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the path shards by batch with no exchange step; see the design "
+              "notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import implicit_gemm_nhwc_amd as igc
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(igc.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    igc.lib()
+
+    if args.only:
+        res, _, _, _ = measure(torch, igc, args.only, args.steps, args.warmup)
+        print(json.dumps(res), flush=True)
+        return
+
+    head, spec, x, w = measure(torch, igc, args.workload, args.steps, args.warmup)
+    flops, nbytes = head["flops"], head["alg_bytes"]
+    if head["bound"] == "hbm":
+        achieved, peak, unit = head["kernel_gbs"], PEAK["hbm_gbs"], "GB/s"
+    else:
+        achieved, peak, unit = head["kernel_tflops"], _bound(spec, flops, nbytes)[1], "TFLOP/s"
+    roofline = {"bound": head["bound"], "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": _traffic(head),
+                "kernel": "igemm_fwd_kernel", "kernel_us_mean": round(head["kernel_us_mean"], 3),
+                "alg_bytes_per_launch": nbytes, "flops_per_launch": flops}
+
+    shapes = {}
+    if not args.no_shapes:
+        import datagen
+        for name in datagen.WORKLOAD_ORDER:
+            r, _, _, _ = measure(torch, igc, name, max(10, args.steps // 2), args.warmup)
+            shapes[name] = {k: (round(v, 4) if isinstance(v, float) else v)
+                            for k, v in r.items() if k not in ("flops", "alg_bytes")}
+            print(f"# {name}: step {r['ms_per_step'] * 1e3:.1f} us, kernel "
+                  f"{r['kernel_us_mean']:.1f} us = {r['kernel_tflops']:.1f} TFLOP/s "
+                  f"({100 * r['frac_mfma']:.1f}% MFMA peak), {r['kernel_gbs']:.0f} GB/s "
+                  f"({100 * r['frac_hbm']:.1f}% HBM), bound {r['bound']}",
+                  file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(spec, x, w)
+    line = {
+        "metric": "conv2d fwd TFLOP/s per shape + % of MFMA peak (or % HBM BW if memory-bound)",
+        "value": round(head["step_tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec["dtype"].replace("bfloat16", "bf16").replace("float16", "fp16")
+                                .replace("float8_e4m3fn", "fp8_e4m3fn"),
+        "data": "synthetic",
+        "config": {"workload": args.workload, "N": spec["N"], "H": spec["H"], "W": spec["W"],
+                   "C_in": spec["C"], "C_out": spec["F"], "R": spec["R"], "S": spec["S"],
+                   "stride": spec["stride"], "pad": spec["pad"],
+                   "filter_layout": "FCRS" if spec["fcrs"] else "RSCF",
+                   "residual": spec["src"] is not None, "parallelism": "single_gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "shapes": shapes,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+"""Python binding of libigemmconv.so: forward NHWC convolution as an implicit
+GEMM on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation (filter transpose,
+gather, MFMA contraction, masks, residual epilogue) runs in the HIP kernels
+behind the C ABI declared in include/igemm_conv.h; torch supplies device
+memory and streams.  There is no fallback: if the library is not built, or a
+call is declined, these functions say so instead of computing anything.
+
+Names mirror the C entry points:
+  conv2d_fwd, conv2d_fwd_check, conv2d_fwd_nk, conv2d_filter_to_nk,
+  conv2d_workspace_bytes, conv2d_nk_row_pitch, conv2d_reason_string,
+  conv2d_abi_version
+plus conv2d(), which allocates the output and calls conv2d_fwd.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libigemmconv.so")
+
+DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1, torch.float8_e4m3fn: 2}
+OUT_DTYPES = {torch.bfloat16: torch.bfloat16, torch.float16: torch.float16,
+              torch.float8_e4m3fn: torch.bfloat16}
+
+# decline reason codes (IGC_DECLINE_* in include/igemm_conv.h)
+REASONS = {0: "ok", 1: "dtype", 2: "stride", 3: "dilation", 4: "padding", 5: "groups",
+           6: "shape", 7: "output_shape", 8: "vector_width", 9: "alignment",
+           10: "null_pointer", 11: "overlap", 12: "workspace", 13: "size_limit"}
+
+_lib = None
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class Declined(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded C library with argument types set.  Raises if not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryNotBuilt(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` "
+            "(or python implicit_gemm_nhwc_amd/_build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)
+    i32p, f32, sz = ctypes.POINTER(ctypes.c_int32), ctypes.c_float, ctypes.c_size_t
+    conv_head = [vp, i64p, vp, i32, i64p, vp, i64p, i32p, i32p, i32p, i32, i32, vp, f32]
+    L.conv2d_abi_version.argtypes, L.conv2d_abi_version.restype = [], i32
+    L.conv2d_reason_string.argtypes, L.conv2d_reason_string.restype = [i32], ctypes.c_char_p
+    L.conv2d_fwd_check.argtypes = conv_head + [vp, sz]
+    L.conv2d_fwd_check.restype = i32
+    L.conv2d_fwd.argtypes = conv_head + [vp, sz, vp]
+    L.conv2d_fwd.restype = i32
+    L.conv2d_fwd_nk.argtypes = conv_head + [vp]
+    L.conv2d_fwd_nk.restype = i32
+    L.conv2d_workspace_bytes.argtypes, L.conv2d_workspace_bytes.restype = [i64p, i32, i32], sz
+    L.conv2d_nk_row_pitch.argtypes = [i64p, i32, i32]
+    L.conv2d_nk_row_pitch.restype = ctypes.c_int64
+    L.conv2d_filter_to_nk.argtypes = [vp, i32, i64p, i32, vp, sz, vp]
+    L.conv2d_filter_to_nk.restype = i32
+    _lib = L
+    return L
+
+
+def _i64(vals):
+    return (ctypes.c_int64 * 4)(*[int(v) for v in vals])
+
+
+def _pair(v):
+    if isinstance(v, int):
+        v = (v, v)
+    return (ctypes.c_int32 * 2)(int(v[0]), int(v[1]))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream, ref):
+    if stream is None:
+        if isinstance(ref, torch.Tensor) and ref.is_cuda:
+            return torch.cuda.current_stream(ref.device).cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dtype_code(dtype):
+    if dtype not in DTYPE_CODES:
+        return -1
+    return DTYPE_CODES[dtype]
+
+
+def _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding, groups,
+               dtype, source, beta, in_shape=None, filt_shape=None, out_shape=None):
+    in_shape = input.shape if in_shape is None else in_shape
+    filt_shape = filter.shape if filt_shape is None else filt_shape
+    out_shape = output.shape if out_shape is None else out_shape
+    if dtype is None:
+        dtype = dtype_code(input.dtype)
+    return [_ptr(input), _i64(in_shape), _ptr(filter), int(bool(filter_is_fcrs)),
+            _i64(filt_shape), _ptr(output), _i64(out_shape), _pair(stride), _pair(dilation),
+            _pair(padding), int(groups), int(dtype), _ptr(source), float(beta)]
+
+
+def conv2d_abi_version() -> int:
+    return lib().conv2d_abi_version()
+
+
+def conv2d_reason_string(code: int) -> str:
+    return lib().conv2d_reason_string(int(code)).decode()
+
+
+def conv2d_fwd_check(input, filter, output, *, filter_is_fcrs, stride=1, padding=0,
+                     dilation=1, groups=1, source=None, beta=0.0, workspace=None,
+                     workspace_bytes=0, dtype=None, in_shape=None, filt_shape=None,
+                     out_shape=None) -> int:
+    """Host-only gate: 0 or a decline reason code.  Tensors or raw ints."""
+    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
+                      groups, dtype, source, beta, in_shape, filt_shape, out_shape)
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return lib().conv2d_fwd_check(*head, _ptr(workspace), int(workspace_bytes))
+
+
+def conv2d_fwd(input, filter, output, *, filter_is_fcrs, stride=1, padding=0, dilation=1,
+               groups=1, source=None, beta=0.0, workspace=None, workspace_bytes=0,
+               stream=None, dtype=None, in_shape=None, filt_shape=None,
+               out_shape=None) -> int:
+    """Enqueue the forward convolution.  1 handled, 0 declined, < 0 HIP error."""
+    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
+                      groups, dtype, source, beta, in_shape, filt_shape, out_shape)
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return lib().conv2d_fwd(*head, _ptr(workspace), int(workspace_bytes),
+                            _stream(stream, output))
+
+
+def conv2d_fwd_nk(input, nk, filt_shape, output, *, filter_is_fcrs, stride=1, padding=0,
+                  dilation=1, groups=1, source=None, beta=0.0, stream=None, dtype=None,
+                  in_shape=None, out_shape=None) -> int:
+    """Enqueue the implicit-GEMM kernel on an NK matrix from conv2d_filter_to_nk."""
+    head = _conv_head(input, nk, filter_is_fcrs, output, stride, dilation, padding, groups,
+                      dtype, source, beta, in_shape=in_shape, filt_shape=filt_shape,
+                      out_shape=out_shape)
+    return lib().conv2d_fwd_nk(*head, _stream(stream, output))
+
+
+def conv2d_workspace_bytes(filt_shape, filter_is_fcrs, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(lib().conv2d_workspace_bytes(_i64(filt_shape), int(bool(filter_is_fcrs)), code))
+
+
+def conv2d_nk_row_pitch(filt_shape, filter_is_fcrs, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(lib().conv2d_nk_row_pitch(_i64(filt_shape), int(bool(filter_is_fcrs)), code))
+
+
+def conv2d_filter_to_nk(filter, nk, *, filter_is_fcrs, stream=None, dtype=None,
+                        filt_shape=None, nk_bytes=None) -> int:
+    """Enqueue the filter transpose into nk.  1 enqueued, 0 declined, < 0 error."""
+    filt_shape = filter.shape if filt_shape is None else filt_shape
+    code = dtype_code(filter.dtype) if dtype is None else dtype
+    if nk_bytes is None:
+        nk_bytes = nk.numel() * nk.element_size()
+    return lib().conv2d_filter_to_nk(_ptr(filter), int(bool(filter_is_fcrs)),
+                                     _i64(filt_shape), int(code), _ptr(nk), int(nk_bytes),
+                                     _stream(stream, nk))
+
+
+def out_hw(h, w, r, s, stride, padding):
+    """Output size of the convolution (floor rounding)."""
+    return (h + 2 * padding - r) // stride + 1, (w + 2 * padding - s) // stride + 1
+
+
+def conv2d(input, filter, *, filter_is_fcrs, stride=1, padding=0, source=None, beta=0.0,
+           stream=None):
+    """Allocate the NHWC output (torch memory) and run conv2d_fwd into it."""
+    if filter_is_fcrs:
+        f, _, r, s = filter.shape
+    else:
+        r, s, _, f = filter.shape
+    n, h, w, _ = input.shape
+    ho, wo = out_hw(h, w, r, s, stride, padding)
+    out = torch.empty((n, ho, wo, f), dtype=OUT_DTYPES.get(input.dtype, input.dtype),
+                      device=input.device)
+    ws_bytes = conv2d_workspace_bytes(filter.shape, filter_is_fcrs, input.dtype)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=input.device)
+    rc = conv2d_fwd(input, filter, out, filter_is_fcrs=filter_is_fcrs, stride=stride,
+                    padding=padding, source=source, beta=beta, workspace=ws, stream=stream)
+    if rc == 0:
+        reason = conv2d_fwd_check(input, filter, out, filter_is_fcrs=filter_is_fcrs,
+                                  stride=stride, padding=padding, source=source, beta=beta,
+                                  workspace=ws)
+        raise Declined(f"conv2d_fwd declined: {REASONS.get(reason, reason)}")
+    if rc < 0:
+        raise RuntimeError(f"conv2d_fwd failed with HIP error {-rc}")
+    return out

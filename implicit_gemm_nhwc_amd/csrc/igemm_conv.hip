@@ -1,0 +1,329 @@
+// C-ABI entry points of the forward NHWC implicit-GEMM convolution
+// (declarations and contracts in include/igemm_conv.h).
+//
+// Host side: the acceptance gate of the page "dispatch_amd_4wave_conv2d"
+// (Parameters and Args sections) plus this library's own limits, the NK
+// workspace, tile-shape selection by C_out, and the launches.  Every step of
+// the computation runs in the kernels of igemm_kernels.hpp.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "igemm_conv.h"
+#include "igemm_kernels.hpp"
+
+namespace {
+
+using namespace igc;
+
+constexpr int32_t kAbiVersion = 1;
+
+int elem_bytes(int32_t dtype) { return dtype == IGC_DTYPE_FP8_E4M3FN ? 1 : 2; }
+
+struct Shape {
+    int64_t N, H, W, C, R, S, F, Ho, Wo, M, K, kpitch;
+    int32_t st, pad;
+};
+
+void filter_rscf(const int64_t* fd, int32_t fcrs, int64_t* R, int64_t* S, int64_t* C, int64_t* F) {
+    if (fcrs) { *F = fd[0]; *C = fd[1]; *R = fd[2]; *S = fd[3]; }
+    else { *R = fd[0]; *S = fd[1]; *C = fd[2]; *F = fd[3]; }
+}
+
+int64_t out_size(int64_t in, int64_t k, int64_t st, int64_t pad) {
+    const int64_t span = in + 2 * pad - k;
+    return span < 0 ? 0 : span / st + 1;
+}
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Shape-only part of the gate: page rules, shape consistency, limits.
+int32_t check_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_dims[4],
+                     const int64_t out_nhwc[4], const int32_t stride[2],
+                     const int32_t dilation[2], const int32_t padding[2], int32_t groups,
+                     int32_t dtype, Shape* sh) {
+    if (!in_nhwc || !filt_dims || !out_nhwc || !stride || !dilation || !padding)
+        return IGC_DECLINE_NULL_POINTER;
+    if (dtype != IGC_DTYPE_BF16 && dtype != IGC_DTYPE_FP16 && dtype != IGC_DTYPE_FP8_E4M3FN)
+        return IGC_DECLINE_DTYPE;
+    if (!((stride[0] == 1 && stride[1] == 1) || (stride[0] == 2 && stride[1] == 2)))
+        return IGC_DECLINE_STRIDE;
+    if (dilation[0] != 1 || dilation[1] != 1) return IGC_DECLINE_DILATION;
+    if (padding[0] != padding[1] || padding[0] < 0 || padding[0] > 2) return IGC_DECLINE_PADDING;
+    if (groups != 1) return IGC_DECLINE_GROUPS;
+
+    Shape s{};
+    s.N = in_nhwc[0]; s.H = in_nhwc[1]; s.W = in_nhwc[2]; s.C = in_nhwc[3];
+    filter_rscf(filt_dims, fcrs, &s.R, &s.S, &s.C, &s.F);
+    const int64_t cin = in_nhwc[3];
+    if (s.N < 0 || s.H < 0 || s.W < 0 || cin < 0 || s.F < 0 || s.C < 0 || s.R < 1 || s.S < 1)
+        return IGC_DECLINE_SHAPE;
+    if (s.C != cin) return IGC_DECLINE_SHAPE;
+    s.st = stride[0];
+    s.pad = padding[0];
+    s.Ho = out_size(s.H, s.R, s.st, s.pad);
+    s.Wo = out_size(s.W, s.S, s.st, s.pad);
+    if (s.Ho < 1 || s.Wo < 1) return IGC_DECLINE_OUTPUT_SHAPE;
+    if (out_nhwc[0] != s.N || out_nhwc[1] != s.Ho || out_nhwc[2] != s.Wo || out_nhwc[3] != s.F)
+        return IGC_DECLINE_OUTPUT_SHAPE;
+    const int64_t eb = elem_bytes(dtype);
+    if ((s.C * eb) % 16 != 0) return IGC_DECLINE_VECTOR_WIDTH;
+
+    const int64_t lim = (int64_t)1 << 31;
+    if (s.H >= lim || s.W >= lim || s.R >= lim || s.S >= lim || s.C >= lim || s.F >= lim)
+        return IGC_DECLINE_SIZE_LIMIT;
+    s.M = s.N * s.Ho * s.Wo;
+    s.K = s.R * s.S * s.C;
+    if (s.Ho > lim / (s.Wo > 0 ? s.Wo : 1) || s.M >= lim || s.K >= lim ||
+        (s.R * s.W + s.S) * s.C >= lim)
+        return IGC_DECLINE_SIZE_LIMIT;
+    s.kpitch = round_up(s.K, KT_BYTES / eb);
+    if (s.kpitch >= lim) return IGC_DECLINE_SIZE_LIMIT;
+    if (sh) *sh = s;
+    return IGC_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Full gate: shapes plus pointers.  filter may be the NK matrix (nk_bytes
+// then gives its size); workspace is NULL for conv2d_fwd_nk.
+int32_t check_all(const void* input, const int64_t in_nhwc[4], const void* filter,
+                  size_t filter_bytes_override, int32_t fcrs, const int64_t filt_dims[4],
+                  const void* output, const int64_t out_nhwc[4], const int32_t stride[2],
+                  const int32_t dilation[2], const int32_t padding[2], int32_t groups,
+                  int32_t dtype, const void* source, const void* workspace,
+                  size_t workspace_bytes, Shape* out_shape) {
+    Shape s;
+    int32_t rc = check_shapes(in_nhwc, fcrs, filt_dims, out_nhwc, stride, dilation, padding,
+                              groups, dtype, &s);
+    if (rc != IGC_OK) return rc;
+    const size_t eb = (size_t)elem_bytes(dtype);
+    const size_t in_bytes = (size_t)(s.N * s.H * s.W * s.C) * eb;
+    const size_t f_bytes = filter_bytes_override ? filter_bytes_override
+                                                 : (size_t)(s.R * s.S * s.C * s.F) * eb;
+    const size_t out_bytes = (size_t)(s.M * s.F) * 2;
+    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * eb;
+    if ((in_bytes && !input) || (f_bytes && !filter) || (out_bytes && !output))
+        return IGC_DECLINE_NULL_POINTER;
+    if (!aligned16(input) || !aligned16(filter) || !aligned16(output) || !aligned16(source) ||
+        !aligned16(workspace))
+        return IGC_DECLINE_ALIGNMENT;
+    if (overlaps(output, out_bytes, input, in_bytes) || overlaps(output, out_bytes, filter, f_bytes))
+        return IGC_DECLINE_OVERLAP;
+    if (workspace && overlaps(output, out_bytes, workspace, nk_bytes)) return IGC_DECLINE_OVERLAP;
+    if (workspace && (overlaps(workspace, nk_bytes, input, in_bytes) ||
+                      overlaps(workspace, nk_bytes, filter, f_bytes)))
+        return IGC_DECLINE_OVERLAP;
+    if (source && source != output && overlaps(source, out_bytes, output, out_bytes))
+        return IGC_DECLINE_OVERLAP;
+    if (workspace && workspace_bytes < nk_bytes) return IGC_DECLINE_WORKSPACE;
+    if (out_shape) *out_shape = s;
+    return IGC_OK;
+}
+
+int32_t hip_fail(hipError_t e) { return e == hipSuccess ? 1 : -(int32_t)e; }
+
+// ---- launches -----------------------------------------------------------
+
+hipError_t launch_transpose(const void* filter, int32_t fcrs, const Shape& s, int32_t dtype,
+                            void* nk, hipStream_t stream) {
+    const int eb = elem_bytes(dtype);
+    const int64_t chunks = s.F * (s.kpitch / (16 / eb));
+    if (chunks == 0) return hipSuccess;
+    const int blocks = (int)((chunks + 255) / 256);
+    if (eb == 2)
+        hipLaunchKernelGGL(filter_to_nk_kernel<2>, dim3(blocks), dim3(256), 0, stream,
+                           (const uint8_t*)filter, (uint8_t*)nk, fcrs, (int)s.R, (int)s.S,
+                           (int)s.C, (int)s.F, (int)s.K, (int)s.kpitch);
+    else
+        hipLaunchKernelGGL(filter_to_nk_kernel<1>, dim3(blocks), dim3(256), 0, stream,
+                           (const uint8_t*)filter, (uint8_t*)nk, fcrs, (int)s.R, (int)s.S,
+                           (int)s.C, (int)s.F, (int)s.K, (int)s.kpitch);
+    return hipGetLastError();
+}
+
+template <int DT, int BCO, int BPX, int WCO, int WPX, bool RESID>
+hipError_t launch_tile(ConvArgs a, hipStream_t stream) {
+    constexpr size_t lds = 2 * (size_t)(BCO + BPX) * KT_BYTES;
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    auto kern = igemm_fwd_kernel<DT, BCO, BPX, WCO, WPX, RESID>;
+    std::call_once(once, [&] {
+        attr_err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    a.px_tiles = (a.M + BPX - 1) / BPX;
+    a.co_tiles = (a.F + BCO - 1) / BCO;
+    const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NTHREADS), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT, bool RESID>
+hipError_t launch_dt(const ConvArgs& a, hipStream_t stream) {
+    // Tile by C_out: one 16x16 MFMA row block per wave for tiny C_out, up to
+    // 128 x 128 workgroup tiles (64 x 64 per wave) for wide layers.
+    if (a.F <= 16) return launch_tile<DT, 16, 256, 1, 4, RESID>(a, stream);
+    if (a.F <= 32) return launch_tile<DT, 32, 256, 1, 4, RESID>(a, stream);
+    if (a.F <= 64) return launch_tile<DT, 64, 256, 1, 4, RESID>(a, stream);
+    return launch_tile<DT, 128, 128, 2, 2, RESID>(a, stream);
+}
+
+hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
+                        float beta, const Shape& s, int32_t dtype, hipStream_t stream) {
+    ConvArgs a{};
+    a.x = (const uint8_t*)input;
+    a.nk = (const uint8_t*)nk;
+    a.y = (uint16_t*)output;
+    a.src = (const uint16_t*)source;
+    a.beta = beta;
+    a.H = (int)s.H; a.W = (int)s.W; a.C = (int)s.C;
+    a.Ho = (int)s.Ho; a.Wo = (int)s.Wo; a.F = (int)s.F;
+    a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
+    a.K = (int)s.K; a.kpitch = (int)s.kpitch; a.M = (int)s.M;
+    a.ktiles = (int)(s.kpitch / (KT_BYTES / elem_bytes(dtype)));
+    if (s.M == 0 || s.F == 0) return hipSuccess;
+    const bool resid = source != nullptr;
+    switch (dtype) {
+        case IGC_DTYPE_BF16:
+            return resid ? launch_dt<DT_BF16, true>(a, stream) : launch_dt<DT_BF16, false>(a, stream);
+        case IGC_DTYPE_FP16:
+            return resid ? launch_dt<DT_FP16, true>(a, stream) : launch_dt<DT_FP16, false>(a, stream);
+        default:
+            return resid ? launch_dt<DT_FP8, true>(a, stream) : launch_dt<DT_FP8, false>(a, stream);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t conv2d_abi_version(void) { return kAbiVersion; }
+
+const char* conv2d_reason_string(int32_t reason) {
+    switch (reason) {
+        case IGC_OK: return "ok";
+        case IGC_DECLINE_DTYPE: return "dtype";
+        case IGC_DECLINE_STRIDE: return "stride";
+        case IGC_DECLINE_DILATION: return "dilation";
+        case IGC_DECLINE_PADDING: return "padding";
+        case IGC_DECLINE_GROUPS: return "groups";
+        case IGC_DECLINE_SHAPE: return "shape";
+        case IGC_DECLINE_OUTPUT_SHAPE: return "output_shape";
+        case IGC_DECLINE_VECTOR_WIDTH: return "vector_width";
+        case IGC_DECLINE_ALIGNMENT: return "alignment";
+        case IGC_DECLINE_NULL_POINTER: return "null_pointer";
+        case IGC_DECLINE_OVERLAP: return "overlap";
+        case IGC_DECLINE_WORKSPACE: return "workspace";
+        case IGC_DECLINE_SIZE_LIMIT: return "size_limit";
+        default: return "unknown";
+    }
+}
+
+int32_t conv2d_fwd_check(const void* input, const int64_t in_nhwc[4], const void* filter,
+                         int32_t filter_is_fcrs, const int64_t filt_dims[4], const void* output,
+                         const int64_t out_nhwc[4], const int32_t stride[2],
+                         const int32_t dilation[2], const int32_t padding[2], int32_t groups,
+                         int32_t dtype, const void* source, float beta, const void* workspace,
+                         size_t workspace_bytes) {
+    (void)beta;
+    return check_all(input, in_nhwc, filter, 0, filter_is_fcrs, filt_dims, output, out_nhwc,
+                     stride, dilation, padding, groups, dtype, source, workspace,
+                     workspace_bytes, nullptr);
+}
+
+size_t conv2d_workspace_bytes(const int64_t filt_dims[4], int32_t filter_is_fcrs, int32_t dtype) {
+    const int64_t p = conv2d_nk_row_pitch(filt_dims, filter_is_fcrs, dtype);
+    if (p < 0) return 0;
+    int64_t R, S, C, F;
+    filter_rscf(filt_dims, filter_is_fcrs, &R, &S, &C, &F);
+    return (size_t)(F * p) * (size_t)elem_bytes(dtype);
+}
+
+int64_t conv2d_nk_row_pitch(const int64_t filt_dims[4], int32_t filter_is_fcrs, int32_t dtype) {
+    if (!filt_dims) return -1;
+    if (dtype != IGC_DTYPE_BF16 && dtype != IGC_DTYPE_FP16 && dtype != IGC_DTYPE_FP8_E4M3FN)
+        return -1;
+    int64_t R, S, C, F;
+    filter_rscf(filt_dims, filter_is_fcrs, &R, &S, &C, &F);
+    if (R < 0 || S < 0 || C < 0 || F < 0) return -1;
+    return round_up(R * S * C, KT_BYTES / elem_bytes(dtype));
+}
+
+int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs, const int64_t filt_dims[4],
+                            int32_t dtype, void* nk, size_t nk_bytes, void* stream) {
+    if (!filt_dims) return 0;
+    if (dtype != IGC_DTYPE_BF16 && dtype != IGC_DTYPE_FP16 && dtype != IGC_DTYPE_FP8_E4M3FN)
+        return 0;
+    Shape s{};
+    filter_rscf(filt_dims, filter_is_fcrs, &s.R, &s.S, &s.C, &s.F);
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t lim = (int64_t)1 << 31;
+    if (s.R < 1 || s.S < 1 || s.C < 0 || s.F < 0 || (s.C * eb) % 16 != 0) return 0;
+    if (s.R >= lim || s.S >= lim || s.C >= lim || s.F >= lim) return 0;
+    s.K = s.R * s.S * s.C;
+    if (s.K >= lim) return 0;
+    s.kpitch = round_up(s.K, KT_BYTES / eb);
+    const size_t need = (size_t)(s.F * s.kpitch) * (size_t)eb;
+    const size_t fbytes = (size_t)(s.K * s.F) * (size_t)eb;
+    if (nk_bytes < need) return 0;
+    if ((fbytes && !filter) || (need && !nk)) return 0;
+    if (!aligned16(nk) || !aligned16(filter)) return 0;
+    if (overlaps(nk, need, filter, fbytes)) return 0;
+    return hip_fail(launch_transpose(filter, filter_is_fcrs, s, dtype, nk, (hipStream_t)stream));
+}
+
+int32_t conv2d_fwd_nk(const void* input, const int64_t in_nhwc[4], const void* nk,
+                      int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
+                      const int64_t out_nhwc[4], const int32_t stride[2],
+                      const int32_t dilation[2], const int32_t padding[2], int32_t groups,
+                      int32_t dtype, const void* source, float beta, void* stream) {
+    Shape s;
+    size_t nk_bytes = conv2d_workspace_bytes(filt_dims, filter_is_fcrs, dtype);
+    const int32_t rc = check_all(input, in_nhwc, nk, nk_bytes ? nk_bytes : 1, filter_is_fcrs,
+                                 filt_dims, output, out_nhwc, stride, dilation, padding, groups,
+                                 dtype, source, nullptr, 0, &s);
+    if (rc != IGC_OK) return 0;
+    return hip_fail(launch_igemm(input, nk, output, source, beta, s, dtype, (hipStream_t)stream));
+}
+
+int32_t conv2d_fwd(const void* input, const int64_t in_nhwc[4], const void* filter,
+                   int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
+                   const int64_t out_nhwc[4], const int32_t stride[2], const int32_t dilation[2],
+                   const int32_t padding[2], int32_t groups, int32_t dtype, const void* source,
+                   float beta, void* workspace, size_t workspace_bytes, void* stream) {
+    Shape s;
+    const int32_t rc = check_all(input, in_nhwc, filter, 0, filter_is_fcrs, filt_dims, output,
+                                 out_nhwc, stride, dilation, padding, groups, dtype, source,
+                                 workspace, workspace_bytes, &s);
+    if (rc != IGC_OK) return 0;
+    if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
+    hipStream_t st = (hipStream_t)stream;
+    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
+    void* nk = workspace;
+    bool owned = false;
+    if (!nk && nk_bytes) {
+        hipError_t e = hipMallocAsync(&nk, nk_bytes, st);
+        if (e != hipSuccess) return -(int32_t)e;
+        owned = true;
+    }
+    hipError_t e = launch_transpose(filter, filter_is_fcrs, s, dtype, nk, st);
+    if (e == hipSuccess) e = launch_igemm(input, nk, output, source, beta, s, dtype, st);
+    if (owned) {
+        hipError_t f = hipFreeAsync(nk, st);
+        if (e == hipSuccess) e = f;
+    }
+    return hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+/*
+ * igemm_conv.h -- forward 2-D convolution as an implicit GEMM on MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * The operation is the one documented on the page "dispatch_amd_4wave_conv2d"
+ * (Modular kernel library, nn/conv/gpu/amd/dispatch):
+ *   - summary: try to run a forward Conv2D on the GPU; report whether the call
+ *     was handled or declined so the caller can fall back; with a residual
+ *     source compute D = Conv(A, B) + beta * source in-kernel, where source is
+ *     NHWC-contiguous with the output's shape;
+ *   - Parameters: input type float8_e4m3fn, bfloat16 or float16; filter type
+ *     equal to it; output bfloat16 for fp8 inputs, otherwise the input type;
+ *     filter_is_fcrs selects the FCRS or RSCF filter layout;
+ *   - Args: NHWC input, FCRS or RSCF filter, NHWC output; stride (1,1) or
+ *     (2,2); dilation (1,1); symmetric padding (0,0), (1,1) or (2,2); one group.
+ * The filter is first transposed into the (C_out, K = R*S*C_in) "NK" matrix,
+ * and the GEMM gathers its other operand from the NHWC input on the fly so no
+ * im2col matrix is written to memory (page "dispatch_fused_im2col_conv2d_apple",
+ * summary).
+ *
+ * Definition computed (cross-correlation, zero padding on both sides):
+ *   y[n,oh,ow,co] = sum_{r<R, s<S, ci<C_in}
+ *                     x[n, oh*st - p + r, ow*st - p + s, ci] * W(r, s, ci, co)
+ *   Ho = floor((H + 2p - R) / st) + 1,  Wo = floor((W + 2p - S) / st) + 1
+ *   D  = y + beta * source  (when source != NULL), one rounding to the output
+ *        type at the end (round to nearest even); accumulation is fp32.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device pointers to caller-owned memory
+ *     (hipMalloc / torch allocations).  The library keeps no tensor state.
+ *   - Shapes are int64 arrays: in_nhwc = {N, H, W, C_in};
+ *     filt_dims is the filter's stored shape: {R, S, C_in, C_out} for RSCF
+ *     (filter_is_fcrs = 0) or {C_out, C_in, R, S} for FCRS (filter_is_fcrs = 1);
+ *     out_nhwc = {N, Ho, Wo, C_out}.  All tensors are densely packed.
+ *   - stride, dilation, padding are int32 pairs {height, width}.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously; the caller synchronizes.
+ *   - No exceptions cross the ABI; the functions are thread-safe.
+ */
+#ifndef IGEMM_CONV_H
+#define IGEMM_CONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type codes (page "dispatch_amd_4wave_conv2d", Parameters). */
+enum {
+    IGC_DTYPE_BF16 = 0,        /* bfloat16 in, bfloat16 out            */
+    IGC_DTYPE_FP16 = 1,        /* float16 in, float16 out              */
+    IGC_DTYPE_FP8_E4M3FN = 2   /* OCP float8 e4m3fn in, bfloat16 out   */
+};
+
+/* Reasons a call is declined (0 = accepted).  The first five follow the
+ * page's rules; the rest are this library's own limits. */
+enum {
+    IGC_OK = 0,
+    IGC_DECLINE_DTYPE = 1,         /* dtype code not one of the three        */
+    IGC_DECLINE_STRIDE = 2,        /* stride not (1,1) or (2,2)              */
+    IGC_DECLINE_DILATION = 3,      /* dilation not (1,1)                     */
+    IGC_DECLINE_PADDING = 4,       /* padding not (0,0), (1,1) or (2,2)      */
+    IGC_DECLINE_GROUPS = 5,        /* groups not 1                           */
+    IGC_DECLINE_SHAPE = 6,         /* negative dims, R or S < 1, or the
+                                      filter's C_in differs from the input's */
+    IGC_DECLINE_OUTPUT_SHAPE = 7,  /* Ho or Wo < 1, or out_nhwc is not
+                                      {N, Ho, Wo, C_out}                     */
+    IGC_DECLINE_VECTOR_WIDTH = 8,  /* C_in * element bytes not a multiple of
+                                      16 (the gather moves 16-byte vectors)  */
+    IGC_DECLINE_ALIGNMENT = 9,     /* a tensor pointer not 16-byte aligned   */
+    IGC_DECLINE_NULL_POINTER = 10, /* NULL pointer for a non-empty tensor,
+                                      or NULL shape/parameter array          */
+    IGC_DECLINE_OVERLAP = 11,      /* output overlaps input, filter or
+                                      workspace; or source overlaps output
+                                      without being exactly the output       */
+    IGC_DECLINE_WORKSPACE = 12,    /* workspace given but smaller than
+                                      conv2d_workspace_bytes()               */
+    IGC_DECLINE_SIZE_LIMIT = 13    /* a size beyond the kernels' 32-bit index
+                                      ranges (see conv2d_fwd_check)          */
+};
+
+/* Version of this ABI. */
+int32_t conv2d_abi_version(void);
+
+/* Human-readable name of a decline reason code (static string). */
+const char* conv2d_reason_string(int32_t reason);
+
+/*
+ * Host-only acceptance check (no HIP call, no memory access): the gate of
+ * the page's dispatcher plus this library's limits.  Pointers are only
+ * compared and tested for alignment, never dereferenced.  workspace may be
+ * NULL (the library then allocates).  Returns IGC_OK or a decline reason.
+ * Size limits: N*Ho*Wo, C_out, R*S*C_in, and (R*W + S)*C_in each below 2^31.
+ */
+int32_t conv2d_fwd_check(const void* input, const int64_t in_nhwc[4],
+                         const void* filter, int32_t filter_is_fcrs,
+                         const int64_t filt_dims[4],
+                         const void* output, const int64_t out_nhwc[4],
+                         const int32_t stride[2], const int32_t dilation[2],
+                         const int32_t padding[2], int32_t groups,
+                         int32_t dtype, const void* source, float beta,
+                         const void* workspace, size_t workspace_bytes);
+
+/*
+ * Forward convolution (page "dispatch_amd_4wave_conv2d", whole page).
+ *   input    [N, H, W, C_in] of dtype.
+ *   filter   RSCF or FCRS (filter_is_fcrs) of dtype.
+ *   output   [N, Ho, Wo, C_out] of the output type; fully overwritten.
+ *   source   NULL, or [N, Ho, Wo, C_out] of the output type; then
+ *            output = conv + beta * source.  source == output (in place) is
+ *            allowed.  beta is applied literally (IEEE: 0 * NaN is NaN).
+ *   workspace  device scratch for the NK filter of at least
+ *            conv2d_workspace_bytes() bytes; NULL makes the library take it
+ *            stream-ordered from hipMallocAsync and release it with
+ *            hipFreeAsync on the same stream.
+ * Enqueues the filter transpose and the implicit-GEMM kernel on stream.
+ * Returns 1 = handled (work enqueued), 0 = declined (nothing enqueued, no
+ * memory touched; conv2d_fwd_check gives the reason), or -(hipError_t) if a
+ * HIP call failed.
+ */
+int32_t conv2d_fwd(const void* input, const int64_t in_nhwc[4],
+                   const void* filter, int32_t filter_is_fcrs,
+                   const int64_t filt_dims[4],
+                   void* output, const int64_t out_nhwc[4],
+                   const int32_t stride[2], const int32_t dilation[2],
+                   const int32_t padding[2], int32_t groups,
+                   int32_t dtype, const void* source, float beta,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of the NK filter matrix: C_out rows of conv2d_nk_row_pitch()
+ * elements each.  0 for an invalid dtype or negative dims.
+ */
+size_t conv2d_workspace_bytes(const int64_t filt_dims[4],
+                              int32_t filter_is_fcrs, int32_t dtype);
+
+/*
+ * Elements per NK row: K = R*S*C_in rounded up to a multiple of
+ * 128 bytes' worth of elements (64 for bf16/fp16, 128 for fp8).
+ */
+int64_t conv2d_nk_row_pitch(const int64_t filt_dims[4], int32_t filter_is_fcrs,
+                            int32_t dtype);
+
+/*
+ * Filter transpose alone (page "dispatch_fused_im2col_conv2d_apple", summary:
+ * the filter becomes the (C_out, K = R*S*C_in) NK matrix):
+ *   nk[co * pitch + (r*S + s)*C_in + ci] = W(r, s, ci, co)   for k < K
+ *   nk[co * pitch + k] = 0                                     for K <= k < pitch
+ * with pitch = conv2d_nk_row_pitch().  A bit copy: values are not converted.
+ * nk must be 16-byte aligned and hold nk_bytes >= conv2d_workspace_bytes().
+ * Returns 1 = enqueued, 0 = declined (bad dtype/dims/pointers, too small),
+ * or -(hipError_t).
+ */
+int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs,
+                            const int64_t filt_dims[4], int32_t dtype,
+                            void* nk, size_t nk_bytes, void* stream);
+
+/*
+ * The implicit-GEMM kernel alone, on an NK matrix made by
+ * conv2d_filter_to_nk from a filter of shape filt_dims / filter_is_fcrs.
+ * Arguments and returns as conv2d_fwd, with nk in place of the filter and no
+ * workspace.  The gather, the MFMA contraction, the edge masks and the fused
+ * residual epilogue all run in this one launch.
+ */
+int32_t conv2d_fwd_nk(const void* input, const int64_t in_nhwc[4],
+                      const void* nk, int32_t filter_is_fcrs,
+                      const int64_t filt_dims[4],
+                      void* output, const int64_t out_nhwc[4],
+                      const int32_t stride[2], const int32_t dilation[2],
+                      const int32_t padding[2], int32_t groups,
+                      int32_t dtype, const void* source, float beta,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IGEMM_CONV_H */

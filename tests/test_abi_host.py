@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI (CPU only: no GPU call is made).
+
+The library must load and export every function include/igemm_conv.h
+declares; the acceptance gate must decline exactly what the page's rules and
+the library's stated limits decline, before any HIP call.  Fake, aligned,
+non-overlapping pointer values are used: a declined call never dereferences
+them.
+"""
+import glob
+import itertools
+import os
+import re
+
+import pytest
+
+import implicit_gemm_nhwc_amd as igc
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def setup_module(_):
+    if not os.path.exists(igc.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+def _declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert "conv2d_fwd" in names and "conv2d_fwd_nk" in names and len(names) >= 8
+    lib = igc.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_reason_names():
+    assert igc.conv2d_abi_version() == 1
+    for code, name in igc.REASONS.items():
+        assert igc.conv2d_reason_string(code) == name
+    assert igc.conv2d_reason_string(999) == "unknown"
+
+
+X, W, Y, SRC, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+BASE = dict(in_shape=(2, 9, 9, 32), filt_shape=(3, 3, 32, 48), out_shape=(2, 9, 9, 48),
+            filter_is_fcrs=False, stride=1, padding=1, dilation=1, groups=1, dtype=0)
+
+
+def _check(**kw):
+    args = {**BASE, **kw}
+    inp = args.pop("input", X)
+    flt = args.pop("filter", W)
+    out = args.pop("output", Y)
+    return igc.conv2d_fwd_check(inp, flt, out, **args)
+
+
+def test_base_case_accepted():
+    assert _check() == 0
+    assert _check(source=SRC, beta=0.5) == 0
+    assert _check(source=Y, beta=1.0) == 0            # in-place residual
+    assert _check(workspace=WS, workspace_bytes=48 * 320 * 2) == 0
+
+
+@pytest.mark.parametrize("kw,reason", [
+    (dict(dtype=3), "dtype"),
+    (dict(dtype=-1), "dtype"),
+    (dict(stride=3), "stride"),
+    (dict(stride=(1, 2)), "stride"),
+    (dict(dilation=2), "dilation"),
+    (dict(dilation=(1, 2)), "dilation"),
+    (dict(padding=3, out_shape=(2, 13, 13, 48)), "padding"),
+    (dict(padding=(0, 1)), "padding"),
+    (dict(groups=2), "groups"),
+    (dict(groups=0), "groups"),
+    (dict(filt_shape=(3, 3, 16, 48)), "shape"),
+    (dict(filt_shape=(0, 3, 32, 48)), "shape"),
+    (dict(in_shape=(-1, 9, 9, 32)), "shape"),
+    (dict(out_shape=(2, 9, 9, 47)), "output_shape"),
+    (dict(out_shape=(2, 8, 9, 48)), "output_shape"),
+    (dict(in_shape=(1, 1, 1, 32), filt_shape=(5, 5, 32, 48), padding=1,
+          out_shape=(1, 0, 0, 48)), "output_shape"),
+    (dict(in_shape=(2, 9, 9, 12), filt_shape=(3, 3, 12, 48)), "vector_width"),
+    (dict(dtype=2, in_shape=(2, 9, 9, 8), filt_shape=(3, 3, 8, 48)), "vector_width"),
+    (dict(input=X + 8), "alignment"),
+    (dict(output=Y + 2), "alignment"),
+    (dict(source=SRC + 4), "alignment"),
+    (dict(input=0), "null_pointer"),
+    (dict(output=0), "null_pointer"),
+    (dict(output=X + 1024), "overlap"),
+    (dict(output=W), "overlap"),
+    (dict(source=Y + 64), "overlap"),
+    (dict(workspace=Y + 256, workspace_bytes=1 << 20), "overlap"),
+    (dict(workspace=WS, workspace_bytes=100), "workspace"),
+    (dict(in_shape=(300000, 100, 100, 32), out_shape=(300000, 100, 100, 48)), "size_limit"),
+])
+def test_decline_paths(kw, reason):
+    assert igc.REASONS[_check(**kw)] == reason
+
+
+def test_declined_call_enqueues_nothing():
+    # No GPU here: a declined conv2d_fwd must return 0 before any HIP call.
+    assert igc.conv2d_fwd(X, W, Y, **{**BASE, "stride": 3}) == 0
+    assert igc.conv2d_fwd(X, W, Y, **{**BASE, "groups": 2}) == 0
+    assert igc.conv2d_fwd_nk(X, W, BASE["filt_shape"], Y, filter_is_fcrs=False, stride=1,
+                             padding=1, dtype=5, in_shape=BASE["in_shape"],
+                             out_shape=BASE["out_shape"]) == 0
+    lib = igc.lib()
+    assert lib.conv2d_filter_to_nk(W, 0, igc._i64((3, 3, 32, 48)), 7, WS, 1 << 20, None) == 0
+    assert lib.conv2d_filter_to_nk(W, 0, igc._i64((3, 3, 32, 48)), 0, WS, 10, None) == 0
+    assert lib.conv2d_filter_to_nk(W, 0, igc._i64((3, 3, 32, 48)), 0, WS + 4, 1 << 20, None) == 0
+
+
+def test_empty_output_is_handled_without_launch():
+    # N = 0: accepted, nothing to compute, no HIP call.
+    args = dict(BASE, in_shape=(0, 9, 9, 32), out_shape=(0, 9, 9, 48))
+    assert _check(**args) == 0
+    inp, flt, out = X, W, Y
+    assert igc.conv2d_fwd(inp, flt, out, **args) == 1
+
+
+def test_workspace_and_pitch():
+    assert igc.conv2d_nk_row_pitch((3, 3, 16, 16), False, 0) == 192       # 144 -> 3*64
+    assert igc.conv2d_nk_row_pitch((64, 64, 3, 3), True, 0) == 576
+    assert igc.conv2d_nk_row_pitch((5, 5, 256, 256), False, 2) == 6400
+    assert igc.conv2d_nk_row_pitch((3, 3, 16, 16), False, 2) == 256       # 144 -> 2*128
+    assert igc.conv2d_workspace_bytes((3, 3, 128, 3), False, 0) == 3 * 1152 * 2
+    assert igc.conv2d_workspace_bytes((256, 128, 3, 3), True, 1) == 256 * 1152 * 2
+    assert igc.conv2d_workspace_bytes((3, 3, 16, 16), False, 9) == 0
+
+
+DT_NAMES = {0: ("bfloat16", "bfloat16", "bfloat16"), 1: ("float16", "float16", "float16"),
+            2: ("float8_e4m3fn", "float8_e4m3fn", "bfloat16"), 3: ("float32",) * 3}
+
+
+def test_gate_matches_oracle_gate():
+    """The C gate and the oracle's reading of the page agree on every
+    combination (shapes chosen so the library's own limits never bind)."""
+    n = 0
+    for dt, st, dil, pad, groups, (h, k, c, f), fcrs in itertools.product(
+            [0, 1, 2, 3], [(1, 1), (2, 2), (3, 3), (1, 2)], [(1, 1), (2, 2)],
+            [(0, 0), (1, 1), (2, 2), (3, 3), (1, 0)], [1, 2],
+            [(9, 3, 32, 48), (5, 5, 16, 3), (2, 5, 64, 8), (7, 1, 32, 1)], [False, True]):
+        ho = oracle.out_size(h, k, st[0], pad[0])
+        wo = oracle.out_size(h, k, st[1], pad[1])
+        in_shape = (2, h, h, c)
+        filt = (f, c, k, k) if fcrs else (k, k, c, f)
+        out_shape = (2, max(ho, 0), max(wo, 0), f)
+        names = DT_NAMES[dt]
+        want = oracle.gate_accepts(names[0], names[1], names[2], in_shape, filt, fcrs,
+                                   out_shape, st, dil, pad, groups)
+        got = _check(in_shape=in_shape, filt_shape=filt, out_shape=out_shape,
+                     filter_is_fcrs=fcrs, stride=st, dilation=dil, padding=pad,
+                     groups=groups, dtype=dt)
+        assert (got == 0) == want, (dt, st, dil, pad, groups, h, k, c, f, fcrs, got)
+        n += 1
+    assert n > 1000

@@ -1,0 +1,361 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerance (from the arithmetic: fp32 accumulation of exactly-rounded inputs,
+one final rounding to bf16/fp16 with a relative error of at most 2^-9 / 2^-11):
+  max|gpu - ref| <= 1e-2 * max|ref|  for bf16 / fp16 inputs,
+  max|gpu - ref| <= 4e-2 * max|ref|  for fp8 e4m3fn inputs (bf16 output),
+over the whole tensor (or over the sampled pixels for the largest workload),
+with every output finite.  Where the exact result is representable in the
+output type (delta filters, all-ones border counts) the test asks for exact
+bits.  Bitwise checks compare two GPU calls (layouts, residual forms,
+in-place, determinism).
+"""
+import itertools
+import os
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import implicit_gemm_nhwc_amd as igc
+import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = {"bfloat16": 1e-2, "float16": 1e-2, "float8_e4m3fn": 4e-2}
+
+
+def setup_module(_):
+    if not os.path.exists(igc.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bits(t):
+    t = t.detach().cpu().contiguous()
+    if t.element_size() == 2:
+        return t.view(torch.int16)
+    return t.view(torch.uint8)
+
+
+def _assert_close(got, ref, tol, what=""):
+    g = got.detach().cpu().to(torch.float64).numpy()
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"non-finite GPU output {what}"
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(g - ref))) if ref.size else 0.0
+    if scale == 0.0:
+        assert err == 0.0, what
+    else:
+        assert err <= tol * scale, f"{what}: max|err| {err:.4g} > {tol} * {scale:.4g}"
+    return err, scale
+
+
+def _run(x, w, *, fcrs, stride, pad, src=None, beta=0.0, ws=True):
+    """conv2d_fwd on device copies; returns the output tensor (on device)."""
+    xd, wd = x.to(DEV), w.to(DEV)
+    sd = None if src is None else src.to(DEV)
+    if fcrs:
+        f, _, r, s = w.shape
+    else:
+        r, s, _, f = w.shape
+    n, h, wi, _ = x.shape
+    ho, wo = igc.out_hw(h, wi, r, s, stride, pad)
+    out = torch.empty((n, ho, wo, f), dtype=datagen.OUT_DTYPES[_name(x.dtype)], device=DEV)
+    wsd = None
+    if ws:
+        nb = igc.conv2d_workspace_bytes(w.shape, fcrs, x.dtype)
+        wsd = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    rc = igc.conv2d_fwd(xd, wd, out, filter_is_fcrs=fcrs, stride=stride, padding=pad,
+                        source=sd, beta=beta, workspace=wsd)
+    assert rc == 1, f"conv2d_fwd returned {rc}"
+    torch.cuda.synchronize()
+    return out
+
+
+def _name(dtype):
+    return {torch.bfloat16: "bfloat16", torch.float16: "float16",
+            torch.float8_e4m3fn: "float8_e4m3fn"}[dtype]
+
+
+# ------------------------------------------------------------------ NK
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16", "float8_e4m3fn"])
+@pytest.mark.parametrize("fcrs", [False, True])
+@pytest.mark.parametrize("r,s,c,f", [(3, 3, 16, 16), (3, 3, 64, 64), (5, 5, 32, 3),
+                                     (1, 1, 48, 17), (3, 2, 128, 5)])
+def test_filter_to_nk_bit_exact(dtype, fcrs, r, s, c, f):
+    if dtype == "float8_e4m3fn" and c % 16:
+        pytest.skip("fp8 needs C_in % 16 == 0")
+    _say(f"NK transpose {dtype} fcrs={fcrs} R{r} S{s} C{c} F{f}")
+    _, w, _ = datagen.make_case(N=1, H=1, W=1, C=c, F=f, R=r, S=s, dtype=dtype, fcrs=fcrs,
+                                x_dist=("normal", 1.0), w_dist=("normal", 1.0), seed=3)
+    pitch = igc.conv2d_nk_row_pitch(w.shape, fcrs, w.dtype)
+    nk = torch.full((f, pitch), 0x55 if dtype == "float8_e4m3fn" else 0x5555,
+                    dtype=torch.uint8 if dtype == "float8_e4m3fn" else torch.int16,
+                    device=DEV)
+    assert igc.conv2d_filter_to_nk(w.to(DEV), nk, filter_is_fcrs=fcrs) == 1
+    torch.cuda.synchronize()
+    want = _bits(oracle.filter_to_nk(w, fcrs, k_pad=pitch))
+    assert torch.equal(nk.cpu().view(want.dtype), want)
+
+
+# ----------------------------------------------------- named workloads
+SAMPLED = {"fp8_5x5_256c_residual_n16"}
+
+
+def _sample_pixels(n, ho, wo, count, seed):
+    rng = np.random.default_rng(seed)
+    pix = set(rng.integers(0, n * ho * wo, size=count).tolist())
+    for b in (0, n - 1):
+        for oh in range(ho):
+            for ow in (0, 1, wo - 2, wo - 1):
+                pix.add((b * ho + oh) * wo + ow)
+        for ow in range(wo):
+            for oh in (0, 1, ho - 2, ho - 1):
+                pix.add((b * ho + oh) * wo + ow)
+    pix.add(n * ho * wo - 1)
+    return np.array(sorted(pix), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", datagen.WORKLOAD_ORDER)
+def test_workload_parity(name):
+    spec, x, w, src = datagen.make_workload(name)
+    _say(f"workload {name}: {spec['dtype']} N{spec['N']} {spec['H']}x{spec['W']} "
+         f"C{spec['C']}->{spec['F']} {spec['R']}x{spec['S']} st{spec['stride']} "
+         f"p{spec['pad']} fcrs={spec['fcrs']} residual={src is not None}")
+    out = _run(x, w, fcrs=spec["fcrs"], stride=spec["stride"], pad=spec["pad"], src=src,
+               beta=spec["beta"])
+    tol = TOL[spec["dtype"]]
+    if name in SAMPLED:
+        n, ho, wo, f = out.shape
+        pix = _sample_pixels(n, ho, wo, 768, seed=5)
+        ref = oracle.conv2d_points(x, w, pix, filter_is_fcrs=spec["fcrs"],
+                                   stride=spec["stride"], padding=spec["pad"], source=src,
+                                   beta=spec["beta"])
+        got = out.reshape(-1, f)[torch.as_tensor(pix, device=DEV)]
+        assert torch.isfinite(out.float()).all()
+        err, scale = _assert_close(got, ref, tol, name)
+    else:
+        ref = oracle.conv2d(x, w, filter_is_fcrs=spec["fcrs"], stride=spec["stride"],
+                            padding=spec["pad"], source=src, beta=spec["beta"])
+        err, scale = _assert_close(out, ref, tol, name)
+    _say(f"  max|err|/max|ref| = {err / max(scale, 1e-300):.3e}")
+
+
+def test_fp8_workload_fcrs_variant_bitwise():
+    """The fp8 workload's filter stored FCRS gives the same bits as RSCF."""
+    spec, x, w, src = datagen.make_workload("fp8_5x5_256c_residual_n16")
+    _say("fp8 workload, RSCF vs FCRS")
+    wf = w.view(torch.uint8).permute(3, 2, 0, 1).contiguous().view(w.dtype)
+    a = _run(x, w, fcrs=False, stride=1, pad=2, src=src, beta=0.5)
+    b = _run(x, wf, fcrs=True, stride=1, pad=2, src=src, beta=0.5)
+    assert torch.equal(_bits(a), _bits(b))
+
+
+# ------------------------------------------------------ randomized sweep
+def _sweep_cases():
+    rng = np.random.default_rng(2024)
+    dtypes = ["bfloat16", "float16", "float8_e4m3fn"]
+    couts = [1, 2, 3, 4, 5, 8, 15, 16, 17, 33, 64, 100, 130]
+    cases = []
+    for i, (dt, fcrs, st, p, resid) in enumerate(itertools.product(
+            dtypes, [False, True], [1, 2], [0, 1, 2], [False, True])):
+        f = couts[i % len(couts)]
+        c = int(rng.choice([16, 32, 48, 64, 128] if dt != "float8_e4m3fn" else [16, 32, 64, 128]))
+        r = int(rng.choice([1, 2, 3, 5]))
+        s = int(rng.choice([1, 3, 5]))
+        h = int(rng.integers(max(r, 3), 19))
+        w = int(rng.integers(max(s, 3), 19))
+        n = int(rng.integers(1, 3))
+        cases.append((dt, fcrs, st, p, resid, n, h, w, c, f, r, s))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_random_sweep(case):
+    dt, fcrs, st, p, resid, n, h, w, c, f, r, s = case
+    ho, wo = oracle.out_size(h, r, st, p), oracle.out_size(w, s, st, p)
+    _say(f"sweep {case} -> out {n}x{ho}x{wo}x{f}")
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype=dt, fcrs=fcrs,
+                                   x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0) if resid else None,
+                                   out_hw=(ho, wo), seed=zlib.crc32(repr(case).encode()) % 1000)
+    beta = -0.75 if resid else 0.0
+    out = _run(x, wt, fcrs=fcrs, stride=st, pad=p, src=src, beta=beta)
+    ref = oracle.conv2d(x, wt, filter_is_fcrs=fcrs, stride=st, padding=p, source=src, beta=beta)
+    _assert_close(out, ref, TOL[dt], str(case))
+
+
+@pytest.mark.parametrize("dt", ["bfloat16", "float8_e4m3fn"])
+@pytest.mark.parametrize("m_extra", [1, 15, 17, 255, 257])
+def test_pixel_tails(dt, m_extra):
+    """M just past tile multiples: M = Wo = 256 + m_extra (one row, 1x3 filter)."""
+    n, h, w = 1, 1, 258 + m_extra
+    _say(f"pixel tail {dt} M={256 + m_extra}")
+    x, wt, _ = datagen.make_case(N=n, H=h, W=w, C=32, F=40, R=1, S=3, dtype=dt, fcrs=False,
+                                 x_dist=("normal", 1.0), w_dist=("normal", 1.0), seed=7)
+    out = _run(x, wt, fcrs=False, stride=1, pad=0, src=None)
+    assert out.shape[2] == 256 + m_extra
+    ref = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=1, padding=0)
+    _assert_close(out, ref, TOL[dt])
+
+
+# ------------------------------------------------------ exact special cases
+@pytest.mark.parametrize("dt", ["bfloat16", "float16", "float8_e4m3fn"])
+@pytest.mark.parametrize("k,st", [(1, 1), (3, 1), (5, 1), (3, 2)])
+def test_centered_delta_bit_exact(dt, k, st):
+    p = (k - 1) // 2
+    c = 32
+    _say(f"delta {dt} k{k} st{st}")
+    x, _, _ = datagen.make_case(N=2, H=9, W=11, C=c, F=c, R=1, S=1, dtype=dt, fcrs=False,
+                                x_dist=("normal", 2.0), w_dist=("normal", 1.0), seed=11)
+    w = torch.zeros((k, k, c, c), dtype=torch.float32)
+    for ci in range(c):
+        w[p, p, ci, ci] = 1.0
+    w = w.to(x.dtype)
+    out = _run(x, w, fcrs=False, stride=st, pad=p)
+    want = x[:, ::st, ::st, :].to(torch.float32).to(out.dtype)  # exact in bf16/fp16
+    assert torch.equal(_bits(out), _bits(want))
+
+
+def test_fp8_every_code_through_delta():
+    """Every finite e4m3fn code passes through a 1x1 identity filter into bf16
+    bit-exactly (the two NaN codes are replaced by +-0: a NaN would spread to
+    its whole pixel through NaN * 0)."""
+    _say("fp8 all codes via identity")
+    codes = torch.arange(256, dtype=torch.int64)
+    codes[0x7F], codes[0xFF] = 0x00, 0x80
+    x = codes.to(torch.uint8).reshape(1, 1, 16, 16).view(torch.float8_e4m3fn).contiguous()
+    w = torch.eye(16, dtype=torch.float32).reshape(1, 1, 16, 16).to(torch.float8_e4m3fn)
+    out = _run(x, w, fcrs=False, stride=1, pad=0)
+    want = x.to(torch.float32).to(torch.bfloat16)
+    assert torch.equal(_bits(out), _bits(want))
+
+
+@pytest.mark.parametrize("k,st,p", [(3, 1, 1), (3, 2, 1), (5, 1, 2), (5, 2, 2), (3, 1, 0),
+                                    (2, 2, 2)])
+def test_all_ones_border_exact(k, st, p):
+    n, h, w, c, f = 2, 13, 10, 16, 20
+    _say(f"all-ones k{k} st{st} p{p}")
+    x = torch.ones((n, h, w, c), dtype=torch.bfloat16)
+    wt = torch.ones((k, k, c, f), dtype=torch.bfloat16)
+    out = _run(x, wt, fcrs=False, stride=st, pad=p)
+    ref = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p)
+    np.testing.assert_array_equal(out.cpu().to(torch.float64).numpy(), ref)
+
+
+# --------------------------------------------------------------- invariants
+@pytest.mark.parametrize("dt", ["bfloat16", "float16", "float8_e4m3fn"])
+def test_layouts_bitwise_equal(dt):
+    _say(f"layouts {dt}")
+    x, w, _ = datagen.make_case(N=2, H=14, W=9, C=64, F=48, R=3, S=3, dtype=dt, fcrs=False,
+                                x_dist=("normal", 1.0), w_dist=("normal", 0.2), seed=13)
+    wb = _bits(w)
+    wf = wb.permute(3, 2, 0, 1).contiguous().view(w.dtype)
+    a = _run(x, w, fcrs=False, stride=1, pad=1)
+    b = _run(x, wf, fcrs=True, stride=1, pad=1)
+    assert torch.equal(_bits(a), _bits(b))
+
+
+@pytest.mark.parametrize("dt", ["bfloat16", "float16", "float8_e4m3fn"])
+def test_residual_forms(dt):
+    _say(f"residual forms {dt}")
+    x, w, src = datagen.make_case(N=2, H=10, W=12, C=32, F=36, R=3, S=3, dtype=dt, fcrs=True,
+                                  x_dist=("normal", 1.0), w_dist=("normal", 0.3),
+                                  src_dist=("normal", 1.0), out_hw=(10, 12), seed=17)
+    plain = _run(x, w, fcrs=True, stride=1, pad=1)
+    zero = _run(x, w, fcrs=True, stride=1, pad=1, src=src, beta=0.0)
+    assert torch.equal(_bits(plain), _bits(zero))        # beta = 0: D == conv
+    d = _run(x, w, fcrs=True, stride=1, pad=1, src=src, beta=1.0)
+    ref = oracle.conv2d(x, w, filter_is_fcrs=True, stride=1, padding=1, source=src, beta=1.0)
+    _assert_close(d, ref, TOL[dt])
+    # in place: source == output
+    inplace = src.to(DEV).clone()
+    rc = igc.conv2d_fwd(x.to(DEV), w.to(DEV), inplace, filter_is_fcrs=True, stride=1,
+                        padding=1, source=inplace, beta=1.0)
+    assert rc == 1
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(inplace), _bits(d))
+
+
+def test_fwd_nk_and_nullptr_workspace_match_fwd():
+    _say("fwd_nk / NULL workspace")
+    x, w, _ = datagen.make_case(N=2, H=17, W=15, C=64, F=64, R=3, S=3, dtype="bfloat16",
+                                fcrs=True, x_dist=("normal", 1.0), w_dist=("normal", 0.1),
+                                seed=19)
+    a = _run(x, w, fcrs=True, stride=2, pad=1)
+    b = _run(x, w, fcrs=True, stride=2, pad=1, ws=False)
+    assert torch.equal(_bits(a), _bits(b))
+    nk = torch.empty(igc.conv2d_workspace_bytes(w.shape, True, w.dtype), dtype=torch.uint8,
+                     device=DEV)
+    assert igc.conv2d_filter_to_nk(w.to(DEV), nk, filter_is_fcrs=True) == 1
+    c = torch.empty_like(a)
+    assert igc.conv2d_fwd_nk(x.to(DEV), nk, w.shape, c, filter_is_fcrs=True, stride=2,
+                             padding=1) == 1
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a), _bits(c))
+
+
+def test_deterministic():
+    _say("determinism")
+    x, w, _ = datagen.make_case(N=4, H=28, W=28, C=128, F=256, R=3, S=3, dtype="float16",
+                                fcrs=False, x_dist=("uniform", 1.0), w_dist=("uniform", 1.0),
+                                seed=23)
+    a = _run(x, w, fcrs=False, stride=1, pad=1)
+    b = _run(x, w, fcrs=False, stride=1, pad=1)
+    assert torch.equal(_bits(a), _bits(b))
+
+
+@pytest.mark.parametrize("f", [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 33, 63, 65, 129])
+def test_store_masks_guard_bands(f):
+    """Output inside a larger buffer: the guard bands on both sides must keep
+    their sentinel bits (no store past co >= C_out or m >= M)."""
+    n, h, w, c = 1, 7, 13, 32
+    _say(f"guard bands C_out={f}")
+    x, wt, _ = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=3, S=3, dtype="bfloat16",
+                                 fcrs=False, x_dist=("normal", 1.0), w_dist=("normal", 0.2),
+                                 seed=29)
+    numel = n * h * w * f
+    guard = 4096
+    buf = torch.full((guard + numel + guard,), -12345, dtype=torch.int16, device=DEV)
+    out = buf[guard:guard + numel].view(torch.bfloat16).view(n, h, w, f)
+    nb = igc.conv2d_workspace_bytes(wt.shape, False, wt.dtype)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    rc = igc.conv2d_fwd(x.to(DEV), wt.to(DEV), out, filter_is_fcrs=False, stride=1, padding=1,
+                        workspace=ws)
+    assert rc == 1
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.all(b[:guard] == -12345) and torch.all(b[guard + numel:] == -12345)
+    ref = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=1, padding=1)
+    _assert_close(out, ref, 1e-2)
+
+
+# ---------------------------------------------------------- degenerate cases
+def test_empty_batch_and_zero_channels():
+    _say("empty batch / C_in = 0")
+    x = torch.empty((0, 8, 8, 16), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones((3, 3, 16, 8), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((0, 8, 8, 8), dtype=torch.bfloat16, device=DEV)
+    assert igc.conv2d_fwd(x, w, out, filter_is_fcrs=False, stride=1, padding=1) == 1
+    # C_in = 0: K = 0, the result is beta * source (or zeros)
+    x0 = torch.empty((1, 6, 6, 0), dtype=torch.bfloat16, device=DEV)
+    w0 = torch.empty((3, 3, 0, 8), dtype=torch.bfloat16, device=DEV)
+    src = torch.randn((1, 6, 6, 8), device=DEV).to(torch.bfloat16)
+    out0 = torch.full((1, 6, 6, 8), 7.0, dtype=torch.bfloat16, device=DEV)
+    assert igc.conv2d_fwd(x0, w0, out0, filter_is_fcrs=False, stride=1, padding=1,
+                          source=src, beta=2.0) == 1
+    torch.cuda.synchronize()
+    assert torch.equal(out0.float(), 2.0 * src.float())
+    out1 = torch.full((1, 6, 6, 8), 7.0, dtype=torch.bfloat16, device=DEV)
+    assert igc.conv2d_fwd(x0, w0, out1, filter_is_fcrs=False, stride=1, padding=1) == 1
+    torch.cuda.synchronize()
+    assert torch.all(out1.float() == 0)
