@@ -222,21 +222,23 @@ def test_centered_delta_bit_exact(dt, k, st):
         w[p, p, ci, ci] = 1.0
     w = w.to(x.dtype)
     out = _run(x, w, fcrs=False, stride=st, pad=p)
-    want = x[:, ::st, ::st, :].to(torch.float32).to(out.dtype)  # exact in bf16/fp16
+    # exact in bf16/fp16; "+ 0.0" because a sum that starts at +0 turns -0 into +0
+    want = (x[:, ::st, ::st, :].to(torch.float32) + 0.0).to(out.dtype)
     assert torch.equal(_bits(out), _bits(want))
 
 
 def test_fp8_every_code_through_delta():
     """Every finite e4m3fn code passes through a 1x1 identity filter into bf16
     bit-exactly (the two NaN codes are replaced by +-0: a NaN would spread to
-    its whole pixel through NaN * 0)."""
+    its whole pixel through NaN * 0; -0 comes out as +0, as in IEEE sums
+    started at +0)."""
     _say("fp8 all codes via identity")
     codes = torch.arange(256, dtype=torch.int64)
     codes[0x7F], codes[0xFF] = 0x00, 0x80
     x = codes.to(torch.uint8).reshape(1, 1, 16, 16).view(torch.float8_e4m3fn).contiguous()
     w = torch.eye(16, dtype=torch.float32).reshape(1, 1, 16, 16).to(torch.float8_e4m3fn)
     out = _run(x, w, fcrs=False, stride=1, pad=0)
-    want = x.to(torch.float32).to(torch.bfloat16)
+    want = (x.to(torch.float32) + 0.0).to(torch.bfloat16)   # -0 sums to +0
     assert torch.equal(_bits(out), _bits(want))
 
 
