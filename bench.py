@@ -35,7 +35,7 @@ HEADLINE = "resnet_3x3_64c_n32"
 PEAK = {"bf16_tflops": 2516.6, "fp16_tflops": 2516.6, "fp8_tflops": 5033.2,
         "hbm_gbs": 8000.0}
 RIDGE_BF16 = PEAK["bf16_tflops"] * 1e12 / (PEAK["hbm_gbs"] * 1e9)
-ROTATE_BYTES = 640 << 20
+ROTATE_BYTES = 640 << 20   # default; --rotate-mib 0 = one set (warm caches, labelled)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "igemm_fwd_resnet_3x3_64c_n32_traffic.txt")
 
 
@@ -69,7 +69,7 @@ def _bound(spec, flops, nbytes):
 class Bufsets:
     """Identical copies of one workload's tensors, rotated across steps."""
 
-    def __init__(self, torch, igc, spec, x, w, src):
+    def __init__(self, torch, igc, spec, x, w, src, rotate_bytes=ROTATE_BYTES):
         dev = torch.device("cuda:0")
         self.spec = spec
         self.fcrs = spec["fcrs"]
@@ -80,7 +80,7 @@ class Bufsets:
         nk_bytes = igc.conv2d_workspace_bytes(w.shape, self.fcrs, w.dtype)
         per_set = (x.numel() * x.element_size() + w.numel() * w.element_size() +
                    nk_bytes + n * ho * wo * f * 2 * (2 if src is not None else 1))
-        self.nsets = max(2, -(-ROTATE_BYTES // per_set))
+        self.nsets = max(1, -(-rotate_bytes // per_set))
         xd, wd = x.to(dev), w.to(dev)
         sd = None if src is None else src.to(dev)
         self.sets = []
@@ -109,11 +109,11 @@ class Bufsets:
             raise RuntimeError(f"conv2d_fwd_nk returned {rc}")
 
 
-def measure(torch, igc, name, steps, warmup):
+def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES):
     import datagen
 
     spec, x, w, src = datagen.make_workload(name)
-    bufs = Bufsets(torch, igc, spec, x, w, src)
+    bufs = Bufsets(torch, igc, spec, x, w, src, rotate_bytes)
     for i in range(warmup):
         bufs.step(igc, i)
     torch.cuda.synchronize()
@@ -186,6 +186,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="run only this workload's timed loop (for profiling); prints one line")
+    ap.add_argument("--rotate-mib", type=int, default=ROTATE_BYTES >> 20,
+                    help="total size of the rotated buffer sets; 0 keeps one set, so "
+                         "operands stay in cache (warm figures, labelled as such)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 3 times "
+                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -205,12 +211,26 @@ def main():
         __graft_entry__.build()
     igc.lib()
 
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
+
     if args.only:
-        res, _, _, _ = measure(torch, igc, args.only, args.steps, args.warmup)
+        res, _, _, _ = measure(torch, igc, args.only, args.steps, args.warmup,
+                               args.rotate_mib << 20)
+        res["caches"] = "cold" if args.rotate_mib else "warm"
         print(json.dumps(res), flush=True)
         return
 
-    head, spec, x, w = measure(torch, igc, args.workload, args.steps, args.warmup)
+    rotate = args.rotate_mib << 20
+    head, spec, x, w = measure(torch, igc, args.workload, args.steps, args.warmup, rotate)
     flops, nbytes = head["flops"], head["alg_bytes"]
     if head["bound"] == "hbm":
         achieved, peak, unit = head["kernel_gbs"], PEAK["hbm_gbs"], "GB/s"
@@ -225,7 +245,7 @@ def main():
     if not args.no_shapes:
         import datagen
         for name in datagen.WORKLOAD_ORDER:
-            r, _, _, _ = measure(torch, igc, name, max(10, args.steps // 2), args.warmup)
+            r, _, _, _ = measure(torch, igc, name, max(10, args.steps // 2), args.warmup, rotate)
             shapes[name] = {k: (round(v, 4) if isinstance(v, float) else v)
                             for k, v in r.items() if k not in ("flops", "alg_bytes")}
             print(f"# {name}: step {r['ms_per_step'] * 1e3:.1f} us, kernel "

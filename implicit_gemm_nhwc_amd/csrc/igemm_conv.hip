@@ -169,6 +169,182 @@ hipError_t launch_tile(ConvArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+constexpr size_t kResidentLdsMax = 80 * 1024;  // two workgroups per CU
+constexpr int kResidentTN = 4;                   // 64 pixels per wave
+
+template <int DT, int TM, bool RESID, bool ALIGNED>
+hipError_t launch_resident(ConvArgs a, hipStream_t stream) {
+    constexpr int E = DtTraits<DT>::E;
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    auto kern = igemm_fwd_resident_kernel<DT, TM, kResidentTN, RESID, ALIGNED>;
+    std::call_once(once, [&] {
+        attr_err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kResidentLdsMax);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    // the filter is staged in whole 1 KB blocks: round the allocation up
+    const size_t lds = ((size_t)TM * 16 * ((size_t)a.kpitch * E + 16) + 1023) / 1024 * 1024;
+    const int64_t wtiles = ((int64_t)a.M + kResidentTN * 16 - 1) / (kResidentTN * 16);
+    const int64_t blocks = (wtiles + RES_WAVES - 1) / RES_WAVES;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(RES_WAVES * 64), lds, stream, a);
+    return hipGetLastError();
+}
+
+// The filter-resident kernel applies when the padded NK matrix fits its LDS
+// budget and every wave's gather window (the images its 64 pixels touch)
+// stays below the 2^31-byte buffer range.
+bool resident_ok(const Shape& s, int32_t dtype) {
+    if (s.F > 64) return false;
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t rows = (s.F + 15) / 16 * 16;
+    if ((rows * (s.kpitch * eb + 16) + 1023) / 1024 * 1024 > (int64_t)kResidentLdsMax) return false;
+    const int64_t howo = s.Ho * s.Wo;
+    int64_t imgs = (kResidentTN * 16 - 1) / howo + 2;
+    if (imgs > s.N) imgs = s.N;
+    return imgs * s.H * s.W * s.C * eb < ((int64_t)1 << 31);
+}
+
+template <int DT, bool RESID, bool ALIGNED>
+hipError_t launch_resident_tm(const ConvArgs& a, hipStream_t stream) {
+    if (a.F <= 16) return launch_resident<DT, 1, RESID, ALIGNED>(a, stream);
+    if (a.F <= 32) return launch_resident<DT, 2, RESID, ALIGNED>(a, stream);
+    if (a.F <= 48) return launch_resident<DT, 3, RESID, ALIGNED>(a, stream);
+    return launch_resident<DT, 4, RESID, ALIGNED>(a, stream);
+}
+
+// C_in a multiple of the 128-byte k-tile: each k-tile sits inside one tap.
+template <int DT, bool RESID>
+hipError_t launch_resident_dt(const ConvArgs& a, hipStream_t stream) {
+    constexpr int KT = KT_BYTES / DtTraits<DT>::E;
+    if (a.C > 0 && a.C % KT == 0) return launch_resident_tm<DT, RESID, true>(a, stream);
+    return launch_resident_tm<DT, RESID, false>(a, stream);
+}
+
+// ---- band kernel planning ------------------------------------------------
+constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
+constexpr int kNumCUs = 256;
+
+struct BandPlan {
+    int TH, TW, PH, PW, TN, fpitch, ppitch, spitch, lds, tiles_h, tiles_w;
+    int64_t tiles;
+};
+
+// 32-pixel blocks per wave the band kernel is built for.
+int band_tn(int64_t blocks_per_wave) {
+    for (int tn : {1, 2, 3, 4})
+        if (blocks_per_wave <= tn) return tn;
+    return 0;
+}
+
+int log2_exact(int64_t v) {
+    int l = 0;
+    while (((int64_t)1 << l) < v) ++l;
+    return ((int64_t)1 << l) == v ? l : -1;
+}
+
+// Pick the output tile (TH x TW) for the band kernel, or return false when
+// the layer does not fit it (C_out > 64, filter + smallest patch > LDS, or
+// C_in not a power-of-two number of MFMA k-steps).  The estimate charges
+// each round of resident workgroups its load time (filter + patch at
+// ~48 B/clk/CU plus a fixed latency) and its MFMA time (32 clk per 32x32
+// block step, one wave per SIMD, TN blocks per wave including padding).
+bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
+    const int64_t E = elem_bytes(dtype);
+    const int64_t ksb = dtype == IGC_DTYPE_FP8_E4M3FN ? 64 : 32;
+    if (s.F > 64 || s.F < 1 || s.C < 1 || (s.C * E) % ksb != 0) return false;
+    if (log2_exact(s.C * E / 16) < 0) return false;
+    if (s.H * s.W * s.C * E >= ((int64_t)1 << 31)) return false;
+    const int64_t tm = s.F <= 32 ? 1 : 2;
+    const int64_t fpitch = s.kpitch * E + 16;
+    const int64_t fbytes = tm * 32 * fpitch;
+    const int64_t ppitch = s.C * E + 16;
+    const int64_t spitch = tm * 32 + 4;
+    const int64_t ksteps = s.R * s.S * (s.C * E / ksb);
+    if (fbytes >= kLdsBytes) return false;
+    int tws[6], ntw = 0;
+    if (s.Wo <= 128) tws[ntw++] = (int)s.Wo;
+    for (int c : {128, 64, 32})
+        if (c < s.Wo) tws[ntw++] = c;
+    double best = 1e300;
+    bool found = false;
+    for (int k = 0; k < ntw; ++k) {
+        const int64_t tw = tws[k];
+        for (int64_t th = 1; th <= s.Ho && th * tw <= 32 * BAND_MAX_TN * BAND_WAVES; ++th) {
+            const int64_t P = th * tw, NB = (P + 31) / 32;
+            const int tn = band_tn((NB + BAND_WAVES - 1) / BAND_WAVES);
+            if (tn == 0) continue;
+            const int64_t ph = (th - 1) * s.st + s.R, pw = (tw - 1) * s.st + s.S;
+            const int64_t patch = ph * pw * ppitch;
+            int64_t lds = fbytes + patch;
+            const int64_t stage = P * spitch * 4;
+            if (stage > lds) lds = stage;
+            lds = (lds + 15) / 16 * 16;
+            if (lds > kLdsBytes) continue;
+            const int64_t th_tiles = (s.Ho + th - 1) / th, tw_tiles = (s.Wo + tw - 1) / tw;
+            const int64_t tiles = s.N * th_tiles * tw_tiles;
+            const int64_t per_cu = kLdsBytes / lds;
+            const int64_t rounds = (tiles + kNumCUs * per_cu - 1) / (kNumCUs * per_cu);
+            const int64_t conc = tiles < kNumCUs * per_cu ? (tiles + kNumCUs - 1) / kNumCUs : per_cu;
+            const double load = (double)(fbytes + patch) / 48.0 + 2500.0;
+            const double mfma = (double)tn * tm * ksteps * 32.0;
+            const double cost = rounds * (load + mfma * (double)conc);
+            if (cost < best) {
+                best = cost;
+                found = true;
+                *out = BandPlan{(int)th, (int)tw, (int)ph, (int)pw, tn, (int)fpitch, (int)ppitch,
+                                (int)spitch, (int)lds, (int)th_tiles, (int)tw_tiles, tiles};
+            }
+        }
+    }
+    return found;
+}
+
+template <int DT, int TM, int TN, bool RESID>
+hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    auto kern = igemm_fwd_band_kernel<DT, TM, TN, RESID>;
+    std::call_once(once, [&] {
+        attr_err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    a.TH = bp.TH; a.TW = bp.TW; a.PH = bp.PH; a.PW = bp.PW;
+    a.tiles_h = bp.tiles_h; a.tiles_w = bp.tiles_w;
+    a.fpitch = bp.fpitch; a.ppitch = bp.ppitch; a.spitch = bp.spitch;
+    a.patch_off = TM * 32 * bp.fpitch;
+    {
+        const int E = DtTraits<DT>::E;
+        const int cpr = a.kpitch * E / 16, cpp = a.C * E / 16, rc = bp.PW * cpp;
+        a.f_dr = BAND_WAVES * 64 / cpr; a.f_dc = BAND_WAVES * 64 % cpr;
+        a.p_dpx = BAND_WAVES * 64 / rc; a.p_dcc = BAND_WAVES * 64 % rc;
+        a.cpp_log2 = log2_exact(cpp);
+    }
+    if (bp.tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(kern, dim3((unsigned)bp.tiles), dim3(BAND_WAVES * 64), (size_t)bp.lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <int DT, int TM, bool RESID>
+hipError_t launch_band_tm(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
+    switch (bp.TN) {
+        case 1: return launch_band<DT, TM, 1, RESID>(a, bp, stream);
+        case 2: return launch_band<DT, TM, 2, RESID>(a, bp, stream);
+        case 3: return launch_band<DT, TM, 3, RESID>(a, bp, stream);
+        default: return launch_band<DT, TM, 4, RESID>(a, bp, stream);
+    }
+}
+
+template <int DT, bool RESID>
+hipError_t launch_band_dt(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
+    if (a.F <= 32) return launch_band_tm<DT, 1, RESID>(a, bp, stream);
+    return launch_band_tm<DT, 2, RESID>(a, bp, stream);
+}
+
 template <int DT, bool RESID>
 hipError_t launch_dt(const ConvArgs& a, hipStream_t stream) {
     // Tile by C_out: one 16x16 MFMA row block per wave for tiny C_out, up to
@@ -189,11 +365,38 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
     a.beta = beta;
     a.H = (int)s.H; a.W = (int)s.W; a.C = (int)s.C;
     a.Ho = (int)s.Ho; a.Wo = (int)s.Wo; a.F = (int)s.F;
-    a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
+    a.R = (int)s.R; a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
     a.K = (int)s.K; a.kpitch = (int)s.kpitch; a.M = (int)s.M;
     a.ktiles = (int)(s.kpitch / (KT_BYTES / elem_bytes(dtype)));
     if (s.M == 0 || s.F == 0) return hipSuccess;
     const bool resid = source != nullptr;
+    BandPlan bp;
+    if (band_plan(s, dtype, &bp)) {
+        switch (dtype) {
+            case IGC_DTYPE_BF16:
+                return resid ? launch_band_dt<DT_BF16, true>(a, bp, stream)
+                             : launch_band_dt<DT_BF16, false>(a, bp, stream);
+            case IGC_DTYPE_FP16:
+                return resid ? launch_band_dt<DT_FP16, true>(a, bp, stream)
+                             : launch_band_dt<DT_FP16, false>(a, bp, stream);
+            default:
+                return resid ? launch_band_dt<DT_FP8, true>(a, bp, stream)
+                             : launch_band_dt<DT_FP8, false>(a, bp, stream);
+        }
+    }
+    if (resident_ok(s, dtype)) {
+        switch (dtype) {
+            case IGC_DTYPE_BF16:
+                return resid ? launch_resident_dt<DT_BF16, true>(a, stream)
+                             : launch_resident_dt<DT_BF16, false>(a, stream);
+            case IGC_DTYPE_FP16:
+                return resid ? launch_resident_dt<DT_FP16, true>(a, stream)
+                             : launch_resident_dt<DT_FP16, false>(a, stream);
+            default:
+                return resid ? launch_resident_dt<DT_FP8, true>(a, stream)
+                             : launch_resident_dt<DT_FP8, false>(a, stream);
+        }
+    }
     switch (dtype) {
         case IGC_DTYPE_BF16:
             return resid ? launch_dt<DT_BF16, true>(a, stream) : launch_dt<DT_BF16, false>(a, stream);

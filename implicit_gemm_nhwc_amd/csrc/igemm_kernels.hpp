@@ -51,12 +51,26 @@ struct ConvArgs {
     int H, W, C;        // input (N only enters through M)
     int Ho, Wo, F;      // output spatial size and C_out
     int S, stride, pad;
+    int R;              // filter height
     int K;              // R*S*C elements
     int kpitch;         // elements per NK row
     int M;              // N*Ho*Wo
     int ktiles;         // kpitch / (KT_BYTES / E)
     int px_tiles;       // ceil(M / BPX)
     int co_tiles;       // ceil(F / BCO)
+    // band kernel: output tile TH x TW, input patch PH x PW (LDS)
+    int TH, TW, PH, PW;
+    int tiles_h, tiles_w;  // tiles per image along Ho / Wo
+    int fpitch;            // LDS bytes per filter row
+    int ppitch;            // LDS bytes per patch pixel (all C_in channels + 16)
+    int patch_off;         // LDS byte offset of the patch
+    int spitch;            // LDS floats per staged output pixel (epilogue)
+    // phase-A address walks: a thread's chunk index grows by the block size
+    // (256) per load; these are that step split into (quotient, remainder)
+    // for the filter rows (cpr chunks per row) and the patch rows
+    int f_dr, f_dc;        // 256 / cpr, 256 % cpr
+    int p_dpx, p_dcc;      // 256 / rc, 256 % rc (rc = chunks per patch row)
+    int cpp_log2;          // log2(16-byte chunks per input pixel)
 };
 
 // Workgroup b is placed on XCD b % 8 by the hardware's round-robin
@@ -374,6 +388,554 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
                     }
                 }
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Filter-resident implicit GEMM for narrow layers (C_out <= 64).
+//
+// The whole NK matrix (TM*16 rows, zero past C_out) is copied into LDS once
+// per workgroup; after one barrier every wave runs on its own: it owns
+// TN*16 consecutive output pixels and all TM*16 output channels, gathers its
+// pixel operand straight from global memory into MFMA-layout registers with
+// 16-byte buffer loads, and reads the filter fragments from LDS.  There are
+// no barriers in the K loop, and the gather runs PREFETCH k-tiles ahead.
+//
+// Gather masking is done by the buffer unit: a lane whose tap falls in the
+// padding (or past M or K) gets an offset beyond the buffer's num_records
+// and the load returns zero without touching memory.  Every load is
+// therefore issued unconditionally and the memory-count waits stay exact.
+// The buffer is based at the first image the wave touches; the host gate
+// guarantees every valid offset of the wave fits below 2^31 bytes.
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+constexpr int RES_WAVES = 4;
+constexpr int PREFETCH = 3;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // raw buffer: stride 0, num_records = bytes, default data format word
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int DT, int TM, int TN, bool RESID, bool TAP_ALIGNED>
+__global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(ConvArgs a) {
+    constexpr int E = DtTraits<DT>::E;
+    constexpr int VEC = 16 / E;
+    constexpr int KT = KT_BYTES / E;
+    constexpr int ROWS = TM * 16;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler keep the
+    // buffer descriptors derived from it in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lpitch = a.kpitch * E + 16;  // +16 B per row: conflict-free fragment reads
+
+    // ---- stage the filter (all of K) in LDS, rows >= C_out as zeros.
+    // Direct-to-LDS buffer loads: each wave instruction fills one contiguous
+    // 1 KB block (lane t -> 16-byte slot t), so each lane picks the NK chunk
+    // that belongs at its slot of the padded layout; the pad slot of a row
+    // and rows >= C_out get an out-of-range offset and are zero-filled.  All
+    // loads are issued back to back, then waited for once.
+    {
+        const int cpr = a.kpitch * E / 16;          // chunks per NK row
+        const int slots = ROWS * (cpr + 1);         // +1: the 16-byte row pad
+        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, (uint32_t)(a.F * cpr * 16));
+        for (int s0 = wave * 64; s0 < slots; s0 += RES_WAVES * 64) {
+            const int slot = s0 + lane;
+            const int row = slot / (cpr + 1), c = slot - row * (cpr + 1);
+            const uint32_t off = (slot < slots && row < a.F && c < cpr)
+                                     ? (uint32_t)(row * cpr + c) * 16u : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(frs, (__attribute__((address_space(3))) void*)(lds + s0 * 16),
+                                                     16, off, 0, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+
+    const int n_wtiles = (a.M + TN * 16 - 1) / (TN * 16);
+    const int wtile = xcd_remap(blockIdx.x, gridDim.x) * RES_WAVES + wave;
+    if (wtile >= n_wtiles) return;  // no barrier follows
+    const int m0 = wtile * TN * 16;
+
+    const int frag_row = lane & 15;
+    const int grp = lane >> 4;
+    const int howo = a.Ho * a.Wo;
+    const int64_t img = (int64_t)a.H * a.W * a.C;   // elements per image
+    const int n0 = m0 / howo;
+    const int64_t base_el = (int64_t)n0 * img;
+    const int64_t total_el = (int64_t)(a.M / howo) * img;
+    int64_t span = (total_el - base_el) * E;
+    const uint32_t nrec = span > (int64_t)OOB_OFFSET ? OOB_OFFSET : (uint32_t)span;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.x + base_el * E, nrec);
+
+    // pixel rows of this lane: one per 16-wide block
+    int prel[TN], pih[TN], piw[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int m = m0 + j * 16 + frag_row;
+        if (m < a.M) {
+            const int n = m / howo;
+            const int rem = m - n * howo;
+            const int oh = rem / a.Wo;
+            const int ow = rem - oh * a.Wo;
+            pih[j] = oh * a.stride - a.pad;
+            piw[j] = ow * a.stride - a.pad;
+            prel[j] = (int)((int64_t)(n - n0) * img + ((int64_t)pih[j] * a.W + piw[j]) * a.C);
+        } else {
+            pih[j] = -(1 << 30);
+            piw[j] = 0;
+            prel[j] = 0;
+        }
+    }
+    // The two 16-byte chunks of each k-tile this lane supplies to the MFMA.
+    // Offsets are computed branch-free: a masked lane (padding, m >= M,
+    // k >= K) gets bit 31 set, which is past num_records, so the load
+    // returns zero; every load is issued and the wait counts stay exact.
+    const int chunk0 = (DT == DT_FP8) ? 2 * grp : grp;
+    const int chunk1 = (DT == DT_FP8) ? 2 * grp + 1 : 4 + grp;
+    i32x4 vb[PREFETCH][TN][2];
+
+    // TAP_ALIGNED (C_in is a multiple of the k-tile): a k-tile lies inside
+    // one filter tap, shared by both chunks; the tap advances by at most one
+    // per k-tile, with selects only.
+    int t_ci = 0, t_r = 0, t_s = 0, t_kt = 0;
+    // general case: each chunk tracks its own (k, tap, channel)
+    int kk[2], ci[2], fr[2], fs[2];
+    if constexpr (!TAP_ALIGNED) {
+        const int Cdiv = a.C > 0 ? a.C : 1;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            kk[t] = (t == 0 ? chunk0 : chunk1) * VEC;
+            const int tap = kk[t] / Cdiv;
+            ci[t] = kk[t] - tap * Cdiv;
+            fr[t] = tap / a.S;
+            fs[t] = tap - fr[t] * a.S;
+        }
+    }
+
+    auto gather = [&](i32x4 (&v)[TN][2]) {
+        if constexpr (TAP_ALIGNED) {
+            const bool kin = t_kt < a.ktiles;
+            const int koff = (t_r * a.W + t_s) * a.C + t_ci;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const bool ok = kin & ((unsigned)(pih[j] + t_r) < (unsigned)a.H) &
+                                ((unsigned)(piw[j] + t_s) < (unsigned)a.W);
+                const uint32_t bad = (uint32_t)(!ok) << 31;
+                const uint32_t o = (uint32_t)(prel[j] + koff) * E;
+                v[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (o + chunk0 * 16) | bad, 0, 0);
+                v[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (o + chunk1 * 16) | bad, 0, 0);
+            }
+            ++t_kt;
+            t_ci += KT;
+            const bool wrap = t_ci >= a.C;
+            t_ci = wrap ? 0 : t_ci;
+            t_s += wrap ? 1 : 0;
+            const bool wrap2 = t_s >= a.S;
+            t_s = wrap2 ? 0 : t_s;
+            t_r += wrap2 ? 1 : 0;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bool kin = kk[t] < a.K;
+                const int koff = (fr[t] * a.W + fs[t]) * a.C + ci[t];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const bool ok = kin & ((unsigned)(pih[j] + fr[t]) < (unsigned)a.H) &
+                                    ((unsigned)(piw[j] + fs[t]) < (unsigned)a.W);
+                    const uint32_t bad = (uint32_t)(!ok) << 31;
+                    v[j][t] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rsrc, ((uint32_t)(prel[j] + koff) * E) | bad, 0, 0);
+                }
+                kk[t] += KT;
+                ci[t] += KT;
+                while (ci[t] >= a.C && a.C > 0) {
+                    ci[t] -= a.C;
+                    if (++fs[t] == a.S) { fs[t] = 0; ++fr[t]; }
+                }
+            }
+        }
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int kt, const i32x4 (&v)[TN][2]) {
+        const uint8_t* arow = lds + frag_row * lpitch + kt * KT_BYTES;
+        if constexpr (DT == DT_FP8) {
+            i32x4 af[TM][2];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                af[i][0] = *reinterpret_cast<const i32x4*>(arow + i * 16 * lpitch + (2 * grp) * 16);
+                af[i][1] = *reinterpret_cast<const i32x4*>(arow + i * 16 * lpitch + (2 * grp + 1) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < TM; ++i) acc[i][j] = mfma_step<DT>(af[i], v[j], acc[i][j]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                i32x4 af[TM];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    af[i] = *reinterpret_cast<const i32x4*>(arow + i * 16 * lpitch + (4 * h + grp) * 16);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+                        acc[i][j] = mfma_step<DT>(&af[i], &v[j][h], acc[i][j]);
+            }
+        }
+    };
+
+    const int nkt = a.ktiles;
+#pragma unroll
+    for (int p = 0; p < PREFETCH - 1; ++p) gather(vb[p]);
+    for (int kt = 0; kt < nkt; kt += PREFETCH) {
+#pragma unroll
+        for (int u = 0; u < PREFETCH; ++u) {
+            // always gather (past the last k-tile every lane is masked, so the
+            // loads return zeros and only keep the wait counts uniform)
+            gather(vb[(u + PREFETCH - 1) % PREFETCH]);
+            // keep the loads ahead of this k-tile's MFMAs (the scheduler would
+            // otherwise sink them and shrink the prefetch distance)
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + u < nkt) compute(kt + u, vb[u]);
+        }
+    }
+
+    // ---- epilogue (same lane mapping as the tiled kernel)
+    constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
+    const bool vec_ok = (a.F & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int m = m0 + j * 16 + frag_row;
+        if (m >= a.M) continue;
+        const int64_t obase = (int64_t)m * a.F;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int co = i * 16 + grp * 4;
+            if (co >= a.F) continue;
+            float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            if (vec_ok) {
+                if constexpr (RESID) {
+                    const u16x4 s = *reinterpret_cast<const u16x4*>(a.src + obase + co);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a.beta, out_to_f32(s[q], ODT), v[q]);
+                }
+                u16x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = f32_to_out(v[q], ODT);
+                *reinterpret_cast<u16x4*>(a.y + obase + co) = o;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (co + q < a.F) {
+                        float d = v[q];
+                        if constexpr (RESID) d = __builtin_fmaf(a.beta, out_to_f32(a.src[obase + co + q], ODT), d);
+                        a.y[obase + co + q] = f32_to_out(d, ODT);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Band kernel: narrow layers (C_out <= 64) whose whole NK filter and one
+// tile's input patch fit in LDS together.
+//
+// A workgroup owns a TH x TW rectangle of output pixels of one image and all
+// output channels.  Phase A copies the padded filter and the tile's input
+// patch (the (TH-1)*st + R rows and (TW-1)*st + S columns it reads, padding
+// as zeros) into LDS with coalesced 16-byte loads, so every input line is
+// fetched once per tile instead of once per filter tap.  After one barrier
+// each wave runs its MFMAs from LDS alone: for every tap (r, s) the B operand
+// of output pixel (th, tw) is patch pixel (th*st + r, tw*st + s).  The fp32
+// results go through LDS and leave with coalesced 16-byte stores; the
+// residual is added there, before the single rounding.
+// Exact n / d for 0 <= n < 2^22 and d >= 1 via a float reciprocal and one
+// correction step (|n * (1/d) - n/d| < 1 there); a handful of full-rate
+// VALU ops instead of a ~30-instruction integer division.
+__device__ __forceinline__ int small_div(int n, int d, float inv_d) {
+    int q = (int)((float)n * inv_d);
+    const int r = n - __mul24(q, d);
+    q += (r >= d) ? 1 : 0;
+    q -= (r < 0) ? 1 : 0;
+    return q;
+}
+
+constexpr int BAND_WAVES = 4;
+constexpr int BAND_MAX_TN = 4;   // 32-pixel blocks per wave at most (tile <= 512 px)
+constexpr int BAND_LB = 20;      // loads per thread per stream in one phase-A batch
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32 MFMA steps (one wave per SIMD keeps these near full rate):
+//   bf16/fp16  v_mfma_f32_32x32x16_{bf16,f16}: lane l supplies row (l & 31)
+//              and 8 consecutive k at offset 8 * (l >> 5) of the 16-wide step;
+//   fp8        v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3, unit E8M0 scales):
+//              lane l supplies 32 consecutive bytes of row (l & 31).
+// Result: lane l holds column (l & 31), rows 8*(v>>2) + 4*(l>>5) + (v&3).
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(const i32x4* a, const i32x4* b, f32x16 acc);
+template <>
+__device__ __forceinline__ f32x16 mfma32<DT_BF16>(const i32x4* a, const i32x4* b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                                   __builtin_bit_cast(bf16x8, b[0]), acc, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<DT_FP16>(const i32x4* a, const i32x4* b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]),
+                                                  __builtin_bit_cast(f16x8, b[0]), acc, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<DT_FP8>(const i32x4* a, const i32x4* b, f32x16 acc) {
+    i32x8 av = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
+    i32x8 bv = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+}
+
+// Band kernel: narrow layers (C_out <= 64) whose whole NK filter and one
+// tile's input patch fit in LDS together.
+//
+// A workgroup owns a TH x TW rectangle of output pixels of one image and all
+// output channels.  Phase A copies the padded filter and the tile's input
+// patch (the (TH-1)*st + R rows and (TW-1)*st + S columns it reads, padding
+// as zeros) into LDS with coalesced 16-byte loads, so every input line is
+// fetched once per tile instead of once per filter tap.  After one barrier
+// each wave runs its MFMAs from LDS alone: for every tap (r, s) the B operand
+// of output pixel (th, tw) is patch pixel (th*st + r, tw*st + s).  The fp32
+// results go through LDS and leave with coalesced 16-byte stores; the
+// residual is added there, before the single rounding.
+//
+// TM: 32-row blocks of output channels; TN: 32-pixel blocks per wave.  The
+// input pixel size C_in * elem bytes is a power-of-two multiple of the MFMA
+// k-step (cpp_log2 = log2 of its 16-byte chunks).
+template <int DT, int TM, int TN, bool RESID>
+__global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArgs a) {
+    constexpr int E = DtTraits<DT>::E;
+    constexpr int KSB = (DT == DT_FP8) ? 64 : 32;   // K bytes per 32x32 MFMA
+    constexpr int FR = (DT == DT_FP8) ? 2 : 1;      // 16-byte chunks per fragment
+    constexpr int NT = BAND_WAVES * 64;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int frag_row = lane & 31;
+    const int half = lane >> 5;
+
+    const int per_img = a.tiles_h * a.tiles_w;
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int n = tile / per_img;
+    const int trem = tile - n * per_img;
+    const int oh0 = (trem / a.tiles_w) * a.TH;
+    const int ow0 = (trem % a.tiles_w) * a.TW;
+    const int ih0 = oh0 * a.stride - a.pad;
+    const int iw0 = ow0 * a.stride - a.pad;
+    const int cbytes = a.C * E;  // bytes of one input pixel
+    const int lg = a.cpp_log2;   // log2(chunks per input pixel)
+
+    // ---- phase A: filter rows [TM*32][fpitch] and the input patch
+    // [PH][PW][ppitch] into LDS.  Each batch issues every load of both
+    // streams before the first wait.  Thread t handles chunk indices t,
+    // t+256, ...; the decompositions advance by add-and-carry.
+    {
+        const int cpr = a.kpitch * E / 16;               // chunks per filter row
+        const int ftotal = TM * 32 * cpr;
+        const int rc = a.PW << lg;                       // chunks per patch row
+        const int ptotal = a.PH * rc;
+        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, (uint32_t)(a.F * cpr * 16));
+        const int64_t img = (int64_t)a.H * a.W * cbytes;
+        const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (int64_t)n * img, (uint32_t)img);
+        uint8_t* patch = lds + a.patch_off;
+        const int per_batch = NT * BAND_LB;
+        const int nb = max((ftotal + per_batch - 1) / per_batch, (ptotal + per_batch - 1) / per_batch);
+        const int row_step = a.W * cbytes;               // global bytes per patch row
+        const int prow_lds = a.PW * a.ppitch;            // LDS bytes per patch row
+        int f_row = tid / cpr, f_c = tid - (tid / cpr) * cpr;
+        int p_row = tid / rc, p_cr = tid - (tid / rc) * rc;
+        int p_ih = ih0 + p_row;
+        int p_gbase = (ih0 + p_row) * row_step + iw0 * cbytes;   // may be negative
+        int idx = tid;
+        for (int b = 0; b < nb; ++b) {
+            i32x4 fv[BAND_LB], pv[BAND_LB];
+            int fdst[BAND_LB], pdst[BAND_LB];
+#pragma unroll
+            for (int u = 0; u < BAND_LB; ++u) {
+                const bool fin = (idx < ftotal) & (f_row < a.F);
+                fv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    frs, ((uint32_t)idx * 16u) | ((uint32_t)!fin << 31), 0, 0);
+                fdst[u] = (idx < ftotal) ? f_row * a.fpitch + f_c * 16 : -1;
+                const int pw = p_cr >> lg;
+                const bool pin = (idx < ptotal) & ((unsigned)p_ih < (unsigned)a.H) &
+                                 ((unsigned)(iw0 + pw) < (unsigned)a.W);
+                pv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    xrs, (uint32_t)(p_gbase + p_cr * 16) | ((uint32_t)!pin << 31), 0, 0);
+                pdst[u] = (idx < ptotal) ? p_row * prow_lds + (p_cr + pw) * 16 : -1;
+                idx += NT;
+                f_c += a.f_dc;
+                const int fcar = f_c >= cpr ? 1 : 0;
+                f_c -= fcar ? cpr : 0;
+                f_row += a.f_dr + fcar;
+                p_cr += a.p_dcc;
+                const int pcar = p_cr >= rc ? 1 : 0;
+                p_cr -= pcar ? rc : 0;
+                p_row += a.p_dpx + pcar;
+                p_ih += a.p_dpx + pcar;
+                p_gbase += (a.p_dpx + pcar) * row_step;
+            }
+#pragma unroll
+            for (int u = 0; u < BAND_LB; ++u)
+                if (fdst[u] >= 0) *reinterpret_cast<i32x4*>(lds + fdst[u]) = fv[u];
+#pragma unroll
+            for (int u = 0; u < BAND_LB; ++u)
+                if (pdst[u] >= 0) *reinterpret_cast<i32x4*>(patch + pdst[u]) = pv[u];
+        }
+    }
+    __syncthreads();
+
+    // ---- phase B: MFMAs from LDS.  Wave w owns pixel blocks w, w+4, ...,
+    // always TN of them; blocks past the tile read patch pixel 0 and are
+    // never stored.  Fragments of step q+1 load while step q multiplies.
+    const int P = a.TH * a.TW;
+    int pb[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        const int p = (wave + BAND_WAVES * t) * 32 + frag_row;
+        const int tp = p / a.TW, tq = p - tp * a.TW;
+        pb[t] = a.patch_off + half * 16 * FR +
+                ((p < P) ? (tp * a.stride * a.PW + tq * a.stride) * a.ppitch : 0);
+    }
+    const uint8_t* frow = lds + frag_row * a.fpitch + half * 16 * FR;
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[i][t] = f32x16{};
+
+    const int ksteps = cbytes / KSB;
+    const int Q = a.R * a.S * ksteps;
+    // uniform walk over k-steps: (r, s, kc) -> patch and filter byte offsets;
+    // past the last step it wraps to step 0 so the spare prefetch of the
+    // final iteration still reads valid LDS
+    int q_r = 0, q_s = 0, q_kc = 0;
+    auto offsets = [&](int& poff, int& foff) {
+        poff = (q_r * a.PW + q_s) * a.ppitch + q_kc * KSB;
+        foff = (q_r * a.S + q_s) * cbytes + q_kc * KSB;
+        if (++q_kc == ksteps) {
+            q_kc = 0;
+            if (++q_s == a.S) { q_s = 0; if (++q_r == a.R) q_r = 0; }
+        }
+    };
+    i32x4 fa[2][TM][FR], fb[2][TN][FR];
+    auto load = [&](int buf) {
+        int poff, foff;
+        offsets(poff, foff);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int h = 0; h < FR; ++h)
+                fa[buf][i][h] = *reinterpret_cast<const i32x4*>(frow + i * 32 * a.fpitch + foff + h * 16);
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int h = 0; h < FR; ++h)
+                fb[buf][t][h] = *reinterpret_cast<const i32x4*>(lds + pb[t] + poff + h * 16);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int i = 0; i < TM; ++i) acc[i][t] = mfma32<DT>(fa[buf][i], fb[buf][t], acc[i][t]);
+    };
+    // Interleave the next step's fragment reads with this step's MFMAs so
+    // the LDS latency hides behind matrix work.
+    constexpr int MPG = (TM * TN + TM + TN - 1) / (TM + TN);
+    auto interleave = [&]() {
+#pragma unroll
+        for (int g = 0; g < TM + TN; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);   // DS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);  // MFMAs
+        }
+    };
+    // Two steps per iteration with no early exit, so every accumulator
+    // stays in place across the loop; an odd last step runs after it.
+    if (Q > 0) load(0);
+    int q = 0;
+    for (; q + 2 <= Q; q += 2) {
+        load(1);      // step q+1
+        mma(0);       // step q
+        interleave();
+        load(0);      // step q+2 (a harmless re-read past the end)
+        mma(1);       // step q+1
+        interleave();
+    }
+    if (q < Q) mma(0);
+    __syncthreads();  // patch and filter no longer read
+
+    // ---- epilogue: fp32 tile -> LDS [P][spitch floats] -> coalesced stores
+    float* stage = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        const int p = (wave + BAND_WAVES * t) * 32 + frag_row;
+        if (p < P) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v4 = {acc[i][t][4 * g], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2],
+                                      acc[i][t][4 * g + 3]};
+                    *reinterpret_cast<f32x4*>(stage + p * a.spitch + i * 32 + g * 8 + half * 4) = v4;
+                }
+        }
+    }
+    __syncthreads();
+    constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
+    const int th_n = min(a.TH, a.Ho - oh0);
+    const int tw_n = min(a.TW, a.Wo - ow0);
+    const float inv_twn = 1.0f / (float)tw_n;
+    if ((a.F & 7) == 0) {
+        const int c8n = a.F / 8;
+        const float inv_c8n = 1.0f / (float)c8n;
+        const int items = th_n * tw_n * c8n;
+        for (int it = tid; it < items; it += NT) {
+            const int q = small_div(it, c8n, inv_c8n), c8 = it - q * c8n;
+            const int th = small_div(q, tw_n, inv_twn), tw = q - th * tw_n;
+            const float* sp = stage + (th * a.TW + tw) * a.spitch + c8 * 8;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 4);
+            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int64_t o = ((int64_t)(n * a.Ho + oh0 + th) * a.Wo + ow0 + tw) * a.F + c8 * 8;
+            if constexpr (RESID) {
+                const i32x4 sv = *reinterpret_cast<const i32x4*>(a.src + o);
+                const uint16_t* sh = reinterpret_cast<const uint16_t*>(&sv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(a.beta, out_to_f32(sh[e], ODT), v[e]);
+            }
+            union { i32x4 v; uint16_t h[8]; } ov;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ov.h[e] = f32_to_out(v[e], ODT);
+            *reinterpret_cast<i32x4*>(a.y + o) = ov.v;
+        }
+    } else {
+        const int items = th_n * tw_n * a.F;
+        const float inv_f = 1.0f / (float)a.F;
+        for (int it = tid; it < items; it += NT) {
+            const int q = small_div(it, a.F, inv_f), co = it - q * a.F;
+            const int th = small_div(q, tw_n, inv_twn), tw = q - th * tw_n;
+            float v = stage[(th * a.TW + tw) * a.spitch + co];
+            const int64_t o = ((int64_t)(n * a.Ho + oh0 + th) * a.Wo + ow0 + tw) * a.F + co;
+            if constexpr (RESID) v = __builtin_fmaf(a.beta, out_to_f32(a.src[o], ODT), v);
+            a.y[o] = f32_to_out(v, ODT);
         }
     }
 }
