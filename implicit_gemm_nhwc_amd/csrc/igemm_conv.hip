@@ -23,7 +23,9 @@ constexpr int32_t kAbiVersion = 1;
 int elem_bytes(int32_t dtype) { return dtype == IGC_DTYPE_FP8_E4M3FN ? 1 : 2; }
 
 struct Shape {
-    int64_t N, H, W, C, R, S, F, Ho, Wo, M, K, kpitch;
+    int64_t N, H, W, C, R, S, F, Ho, Wo, M, K;
+    int64_t kpad;    // K rounded up to whole 128-byte k-tiles (elements)
+    int64_t kpitch;  // NK row stride: kpad plus a 16-byte zero pad (elements)
     int32_t st, pad;
 };
 
@@ -79,7 +81,8 @@ int32_t check_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_
     if (s.Ho > lim / (s.Wo > 0 ? s.Wo : 1) || s.M >= lim || s.K >= lim ||
         (s.R * s.W + s.S) * s.C >= lim)
         return IGC_DECLINE_SIZE_LIMIT;
-    s.kpitch = round_up(s.K, KT_BYTES / eb);
+    s.kpad = round_up(s.K, KT_BYTES / eb);
+    s.kpitch = s.kpad + 16 / eb;
     if (s.kpitch >= lim) return IGC_DECLINE_SIZE_LIMIT;
     if (sh) *sh = s;
     return IGC_OK;
@@ -185,7 +188,7 @@ hipError_t launch_resident(ConvArgs a, hipStream_t stream) {
     });
     if (attr_err != hipSuccess) return attr_err;
     // the filter is staged in whole 1 KB blocks: round the allocation up
-    const size_t lds = ((size_t)TM * 16 * ((size_t)a.kpitch * E + 16) + 1023) / 1024 * 1024;
+    const size_t lds = ((size_t)TM * 16 * ((size_t)a.kpitch * E) + 1023) / 1024 * 1024;
     const int64_t wtiles = ((int64_t)a.M + kResidentTN * 16 - 1) / (kResidentTN * 16);
     const int64_t blocks = (wtiles + RES_WAVES - 1) / RES_WAVES;
     if (blocks == 0) return hipSuccess;
@@ -200,7 +203,7 @@ bool resident_ok(const Shape& s, int32_t dtype) {
     if (s.F > 64) return false;
     const int64_t eb = elem_bytes(dtype);
     const int64_t rows = (s.F + 15) / 16 * 16;
-    if ((rows * (s.kpitch * eb + 16) + 1023) / 1024 * 1024 > (int64_t)kResidentLdsMax) return false;
+    if ((rows * s.kpitch * eb + 1023) / 1024 * 1024 > (int64_t)kResidentLdsMax) return false;
     const int64_t howo = s.Ho * s.Wo;
     int64_t imgs = (kResidentTN * 16 - 1) / howo + 2;
     if (imgs > s.N) imgs = s.N;
@@ -258,7 +261,7 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
     if (log2_exact(s.C * E / 16) < 0) return false;
     if (s.H * s.W * s.C * E >= ((int64_t)1 << 31)) return false;
     const int64_t tm = s.F <= 32 ? 1 : 2;
-    const int64_t fpitch = s.kpitch * E + 16;
+    const int64_t fpitch = s.kpitch * E;
     const int64_t fbytes = tm * 32 * fpitch;
     const int64_t ppitch = s.C * E + 16;
     const int64_t spitch = tm * 32 + 4;
@@ -277,6 +280,7 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
             const int tn = band_tn((NB + BAND_WAVES - 1) / BAND_WAVES);
             if (tn == 0) continue;
             const int64_t ph = (th - 1) * s.st + s.R, pw = (tw - 1) * s.st + s.S;
+            if (pw * (s.C * E / 16) > 64 * BAND_NJ) continue;
             const int64_t patch = ph * pw * ppitch;
             int64_t lds = fbytes + patch;
             const int64_t stage = P * spitch * 4;
@@ -318,10 +322,7 @@ hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     a.patch_off = TM * 32 * bp.fpitch;
     {
         const int E = DtTraits<DT>::E;
-        const int cpr = a.kpitch * E / 16, cpp = a.C * E / 16, rc = bp.PW * cpp;
-        a.f_dr = BAND_WAVES * 64 / cpr; a.f_dc = BAND_WAVES * 64 % cpr;
-        a.p_dpx = BAND_WAVES * 64 / rc; a.p_dcc = BAND_WAVES * 64 % rc;
-        a.cpp_log2 = log2_exact(cpp);
+        a.cpp_log2 = log2_exact(a.C * E / 16);
     }
     if (bp.tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)bp.tiles), dim3(BAND_WAVES * 64), (size_t)bp.lds,
@@ -367,7 +368,7 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
     a.Ho = (int)s.Ho; a.Wo = (int)s.Wo; a.F = (int)s.F;
     a.R = (int)s.R; a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
     a.K = (int)s.K; a.kpitch = (int)s.kpitch; a.M = (int)s.M;
-    a.ktiles = (int)(s.kpitch / (KT_BYTES / elem_bytes(dtype)));
+    a.ktiles = (int)(s.kpad / (KT_BYTES / elem_bytes(dtype)));
     if (s.M == 0 || s.F == 0) return hipSuccess;
     const bool resid = source != nullptr;
     BandPlan bp;
@@ -460,7 +461,7 @@ int64_t conv2d_nk_row_pitch(const int64_t filt_dims[4], int32_t filter_is_fcrs, 
     int64_t R, S, C, F;
     filter_rscf(filt_dims, filter_is_fcrs, &R, &S, &C, &F);
     if (R < 0 || S < 0 || C < 0 || F < 0) return -1;
-    return round_up(R * S * C, KT_BYTES / elem_bytes(dtype));
+    return round_up(R * S * C, KT_BYTES / elem_bytes(dtype)) + 16 / elem_bytes(dtype);
 }
 
 int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs, const int64_t filt_dims[4],
@@ -476,7 +477,8 @@ int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs, const in
     if (s.R >= lim || s.S >= lim || s.C >= lim || s.F >= lim) return 0;
     s.K = s.R * s.S * s.C;
     if (s.K >= lim) return 0;
-    s.kpitch = round_up(s.K, KT_BYTES / eb);
+    s.kpad = round_up(s.K, KT_BYTES / eb);
+    s.kpitch = s.kpad + 16 / eb;
     const size_t need = (size_t)(s.F * s.kpitch) * (size_t)eb;
     const size_t fbytes = (size_t)(s.K * s.F) * (size_t)eb;
     if (nk_bytes < need) return 0;

@@ -53,9 +53,9 @@ struct ConvArgs {
     int S, stride, pad;
     int R;              // filter height
     int K;              // R*S*C elements
-    int kpitch;         // elements per NK row
+    int kpitch;         // elements per NK row (stride; includes a 16-byte zero pad)
     int M;              // N*Ho*Wo
-    int ktiles;         // kpitch / (KT_BYTES / E)
+    int ktiles;         // 128-byte k-tiles covering K
     int px_tiles;       // ceil(M / BPX)
     int co_tiles;       // ceil(F / BCO)
     // band kernel: output tile TH x TW, input patch PH x PW (LDS)
@@ -65,11 +65,6 @@ struct ConvArgs {
     int ppitch;            // LDS bytes per patch pixel (all C_in channels + 16)
     int patch_off;         // LDS byte offset of the patch
     int spitch;            // LDS floats per staged output pixel (epilogue)
-    // phase-A address walks: a thread's chunk index grows by the block size
-    // (256) per load; these are that step split into (quotient, remainder)
-    // for the filter rows (cpr chunks per row) and the patch rows
-    int f_dr, f_dc;        // 256 / cpr, 256 % cpr
-    int p_dpx, p_dcc;      // 256 / rc, 256 % rc (rc = chunks per patch row)
     int cpp_log2;          // log2(16-byte chunks per input pixel)
 };
 
@@ -431,25 +426,22 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
     // wave-uniform by construction; readfirstlane lets the compiler keep the
     // buffer descriptors derived from it in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lpitch = a.kpitch * E + 16;  // +16 B per row: conflict-free fragment reads
+    const int lpitch = a.kpitch * E;  // includes the 16-byte pad: conflict-free fragment reads
 
     // ---- stage the filter (all of K) in LDS, rows >= C_out as zeros.
-    // Direct-to-LDS buffer loads: each wave instruction fills one contiguous
-    // 1 KB block (lane t -> 16-byte slot t), so each lane picks the NK chunk
-    // that belongs at its slot of the padded layout; the pad slot of a row
-    // and rows >= C_out get an out-of-range offset and are zero-filled.  All
-    // loads are issued back to back, then waited for once.
+    // NK rows already carry their 16-byte zero pad, so the LDS image is the
+    // first ROWS rows copied byte for byte.  Direct-to-LDS buffer loads: each
+    // wave instruction fills one contiguous 1 KB block; bytes past C_out's
+    // rows are out of range and zero-filled.  All loads are issued back to
+    // back, then waited for once.
     {
-        const int cpr = a.kpitch * E / 16;          // chunks per NK row
-        const int slots = ROWS * (cpr + 1);         // +1: the 16-byte row pad
-        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, (uint32_t)(a.F * cpr * 16));
+        const int slots = ROWS * a.kpitch * E / 16;
+        const uint32_t valid = (uint32_t)(a.F * a.kpitch * E);
+        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, valid);
         for (int s0 = wave * 64; s0 < slots; s0 += RES_WAVES * 64) {
-            const int slot = s0 + lane;
-            const int row = slot / (cpr + 1), c = slot - row * (cpr + 1);
-            const uint32_t off = (slot < slots && row < a.F && c < cpr)
-                                     ? (uint32_t)(row * cpr + c) * 16u : OOB_OFFSET;
+            const uint32_t off = (uint32_t)(s0 + lane) * 16u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(frs, (__attribute__((address_space(3))) void*)(lds + s0 * 16),
-                                                     16, off, 0, 0, 0);
+                                                     16, off < valid ? off : OOB_OFFSET, 0, 0, 0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -674,7 +666,9 @@ __device__ __forceinline__ int small_div(int n, int d, float inv_d) {
 
 constexpr int BAND_WAVES = 4;
 constexpr int BAND_MAX_TN = 4;   // 32-pixel blocks per wave at most (tile <= 512 px)
-constexpr int BAND_LB = 20;      // loads per thread per stream in one phase-A batch
+constexpr int BAND_LBF = 20;     // filter loads per thread in one phase-A batch
+constexpr int BAND_RB = 3;       // patch rows per wave in one phase-A batch
+constexpr int BAND_NJ = 8;       // 64-chunk slots per patch row (row <= 8 KB)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -745,60 +739,71 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     const int lg = a.cpp_log2;   // log2(chunks per input pixel)
 
     // ---- phase A: filter rows [TM*32][fpitch] and the input patch
-    // [PH][PW][ppitch] into LDS.  Each batch issues every load of both
-    // streams before the first wait.  Thread t handles chunk indices t,
-    // t+256, ...; the decompositions advance by add-and-carry.
+    // [PH][PW][ppitch] into LDS.  One batch issues every load of both
+    // streams before the first wait.
+    //  * filter: NK rows already carry their 16-byte zero pad, so the LDS
+    //    image is a straight copy of the first TM*32 rows (rows >= C_out read
+    //    out of range, i.e. zero);
+    //  * patch: wave w stages patch rows w, w+4, ...; lane l covers chunks
+    //    l, l+64, ... of the row (a patch row is one contiguous run of x), so
+    //    the per-slot offsets and column masks are lane constants.
     {
-        const int cpr = a.kpitch * E / 16;               // chunks per filter row
-        const int ftotal = TM * 32 * cpr;
+        const int fchunks = TM * 32 * a.fpitch / 16;
+        const uint32_t fvalid = (uint32_t)(a.F * a.fpitch);
+        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, fvalid);
         const int rc = a.PW << lg;                       // chunks per patch row
-        const int ptotal = a.PH * rc;
-        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, (uint32_t)(a.F * cpr * 16));
+        const int prow_lds = a.PW * a.ppitch;            // LDS bytes per patch row
+        const int row_step = a.W * cbytes;               // x bytes per input row
         const int64_t img = (int64_t)a.H * a.W * cbytes;
         const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (int64_t)n * img, (uint32_t)img);
         uint8_t* patch = lds + a.patch_off;
-        const int per_batch = NT * BAND_LB;
-        const int nb = max((ftotal + per_batch - 1) / per_batch, (ptotal + per_batch - 1) / per_batch);
-        const int row_step = a.W * cbytes;               // global bytes per patch row
-        const int prow_lds = a.PW * a.ppitch;            // LDS bytes per patch row
-        int f_row = tid / cpr, f_c = tid - (tid / cpr) * cpr;
-        int p_row = tid / rc, p_cr = tid - (tid / rc) * rc;
-        int p_ih = ih0 + p_row;
-        int p_gbase = (ih0 + p_row) * row_step + iw0 * cbytes;   // may be negative
-        int idx = tid;
-        for (int b = 0; b < nb; ++b) {
-            i32x4 fv[BAND_LB], pv[BAND_LB];
-            int fdst[BAND_LB], pdst[BAND_LB];
+        int voff[BAND_NJ], loff[BAND_NJ];
+        bool colok[BAND_NJ];
 #pragma unroll
-            for (int u = 0; u < BAND_LB; ++u) {
-                const bool fin = (idx < ftotal) & (f_row < a.F);
+        for (int j = 0; j < BAND_NJ; ++j) {
+            const int c = lane + 64 * j, pw = c >> lg;
+            voff[j] = c * 16;
+            loff[j] = (c + pw) * 16;
+            colok[j] = (c < rc) & ((unsigned)(iw0 + pw) < (unsigned)a.W);
+        }
+        const int fbatches = (fchunks + NT * BAND_LBF - 1) / (NT * BAND_LBF);
+        const int pbatches = (a.PH + BAND_WAVES * BAND_RB - 1) / (BAND_WAVES * BAND_RB);
+        const int nb = max(fbatches, pbatches);
+        for (int b = 0; b < nb; ++b) {
+            i32x4 fv[BAND_LBF], pv[BAND_RB][BAND_NJ];
+#pragma unroll
+            for (int u = 0; u < BAND_LBF; ++u) {
+                const int idx = (b * BAND_LBF + u) * NT + tid;
+                const uint32_t off = (uint32_t)idx * 16u;
                 fv[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                    frs, ((uint32_t)idx * 16u) | ((uint32_t)!fin << 31), 0, 0);
-                fdst[u] = (idx < ftotal) ? f_row * a.fpitch + f_c * 16 : -1;
-                const int pw = p_cr >> lg;
-                const bool pin = (idx < ptotal) & ((unsigned)p_ih < (unsigned)a.H) &
-                                 ((unsigned)(iw0 + pw) < (unsigned)a.W);
-                pv[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                    xrs, (uint32_t)(p_gbase + p_cr * 16) | ((uint32_t)!pin << 31), 0, 0);
-                pdst[u] = (idx < ptotal) ? p_row * prow_lds + (p_cr + pw) * 16 : -1;
-                idx += NT;
-                f_c += a.f_dc;
-                const int fcar = f_c >= cpr ? 1 : 0;
-                f_c -= fcar ? cpr : 0;
-                f_row += a.f_dr + fcar;
-                p_cr += a.p_dcc;
-                const int pcar = p_cr >= rc ? 1 : 0;
-                p_cr -= pcar ? rc : 0;
-                p_row += a.p_dpx + pcar;
-                p_ih += a.p_dpx + pcar;
-                p_gbase += (a.p_dpx + pcar) * row_step;
+                    frs, off | ((uint32_t)!(off < fvalid) << 31), 0, 0);
             }
 #pragma unroll
-            for (int u = 0; u < BAND_LB; ++u)
-                if (fdst[u] >= 0) *reinterpret_cast<i32x4*>(lds + fdst[u]) = fv[u];
+            for (int rb = 0; rb < BAND_RB; ++rb) {
+                const int row = (b * BAND_RB + rb) * BAND_WAVES + wave;   // uniform
+                const int ih = ih0 + row;
+                const bool rowok = (row < a.PH) & ((unsigned)ih < (unsigned)a.H);
+                const int gbase = ih * row_step + iw0 * cbytes;         // may be < 0
 #pragma unroll
-            for (int u = 0; u < BAND_LB; ++u)
-                if (pdst[u] >= 0) *reinterpret_cast<i32x4*>(patch + pdst[u]) = pv[u];
+                for (int j = 0; j < BAND_NJ; ++j)
+                    pv[rb][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                        xrs, (uint32_t)(gbase + voff[j]) | ((uint32_t)!(rowok & colok[j]) << 31), 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < BAND_LBF; ++u) {
+                const int idx = (b * BAND_LBF + u) * NT + tid;
+                if (idx < fchunks) *reinterpret_cast<i32x4*>(lds + idx * 16) = fv[u];
+            }
+#pragma unroll
+            for (int rb = 0; rb < BAND_RB; ++rb) {
+                const int row = (b * BAND_RB + rb) * BAND_WAVES + wave;
+                if (row < a.PH) {
+                    uint8_t* dst = patch + row * prow_lds;
+#pragma unroll
+                    for (int j = 0; j < BAND_NJ; ++j)
+                        if (lane + 64 * j < rc) *reinterpret_cast<i32x4*>(dst + loff[j]) = pv[rb][j];
+                }
+            }
         }
     }
     __syncthreads();

@@ -67,7 +67,7 @@ def test_base_case_accepted():
     assert _check() == 0
     assert _check(source=SRC, beta=0.5) == 0
     assert _check(source=Y, beta=1.0) == 0            # in-place residual
-    assert _check(workspace=WS, workspace_bytes=48 * 320 * 2) == 0
+    assert _check(workspace=WS, workspace_bytes=48 * 328 * 2) == 0
 
 
 @pytest.mark.parametrize("kw,reason", [
@@ -128,12 +128,13 @@ def test_empty_output_is_handled_without_launch():
 
 
 def test_workspace_and_pitch():
-    assert igc.conv2d_nk_row_pitch((3, 3, 16, 16), False, 0) == 192       # 144 -> 3*64
-    assert igc.conv2d_nk_row_pitch((64, 64, 3, 3), True, 0) == 576
-    assert igc.conv2d_nk_row_pitch((5, 5, 256, 256), False, 2) == 6400
-    assert igc.conv2d_nk_row_pitch((3, 3, 16, 16), False, 2) == 256       # 144 -> 2*128
-    assert igc.conv2d_workspace_bytes((3, 3, 128, 3), False, 0) == 3 * 1152 * 2
-    assert igc.conv2d_workspace_bytes((256, 128, 3, 3), True, 1) == 256 * 1152 * 2
+    # K rounded up to whole 128-byte k-tiles, plus a 16-byte zero pad per row
+    assert igc.conv2d_nk_row_pitch((3, 3, 16, 16), False, 0) == 192 + 8     # 144 -> 3*64
+    assert igc.conv2d_nk_row_pitch((64, 64, 3, 3), True, 0) == 576 + 8
+    assert igc.conv2d_nk_row_pitch((5, 5, 256, 256), False, 2) == 6400 + 16
+    assert igc.conv2d_nk_row_pitch((3, 3, 16, 16), False, 2) == 256 + 16    # 144 -> 2*128
+    assert igc.conv2d_workspace_bytes((3, 3, 128, 3), False, 0) == 3 * 1160 * 2
+    assert igc.conv2d_workspace_bytes((256, 128, 3, 3), True, 1) == 256 * 1160 * 2
     assert igc.conv2d_workspace_bytes((3, 3, 16, 16), False, 9) == 0
 
 
