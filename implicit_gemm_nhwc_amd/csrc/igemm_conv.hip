@@ -280,12 +280,11 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
             const int tn = band_tn((NB + BAND_WAVES - 1) / BAND_WAVES);
             if (tn == 0) continue;
             const int64_t ph = (th - 1) * s.st + s.R, pw = (tw - 1) * s.st + s.S;
-            if (pw * (s.C * E / 16) > 64 * BAND_NJ) continue;
-            const int64_t patch = ph * pw * ppitch;
-            int64_t lds = fbytes + patch;
+            // filter and patch are each staged in whole 1 KB blocks
+            const int64_t patch = (ph * pw * ppitch + 1023) / 1024 * 1024;
+            int64_t lds = (fbytes + 1023) / 1024 * 1024 + patch;
             const int64_t stage = P * spitch * 4;
             if (stage > lds) lds = stage;
-            lds = (lds + 15) / 16 * 16;
             if (lds > kLdsBytes) continue;
             const int64_t th_tiles = (s.Ho + th - 1) / th, tw_tiles = (s.Wo + tw - 1) / tw;
             const int64_t tiles = s.N * th_tiles * tw_tiles;
@@ -319,7 +318,7 @@ hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     a.TH = bp.TH; a.TW = bp.TW; a.PH = bp.PH; a.PW = bp.PW;
     a.tiles_h = bp.tiles_h; a.tiles_w = bp.tiles_w;
     a.fpitch = bp.fpitch; a.ppitch = bp.ppitch; a.spitch = bp.spitch;
-    a.patch_off = TM * 32 * bp.fpitch;
+    a.patch_off = (TM * 32 * bp.fpitch + 1023) / 1024 * 1024;
     {
         const int E = DtTraits<DT>::E;
         a.cpp_log2 = log2_exact(a.C * E / 16);
@@ -344,6 +343,60 @@ template <int DT, bool RESID>
 hipError_t launch_band_dt(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
     if (a.F <= 32) return launch_band_tm<DT, 1, RESID>(a, bp, stream);
     return launch_band_tm<DT, 2, RESID>(a, bp, stream);
+}
+
+// ---- wide-layer tiled kernel ----------------------------------------------
+template <int DT, int TM, int TN, int WCO, int WPX, bool RESID, bool TAPK, bool PIPE2>
+hipError_t launch_tiled(ConvArgs a, hipStream_t stream) {
+    constexpr int BCO = WCO * TM * 32, BPX = WPX * TN * 32;
+    constexpr size_t lds = 2 * (size_t)(BCO + BPX) * TILE_RP;
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    auto kern = igemm_fwd_tiled_kernel<DT, TM, TN, WCO, WPX, RESID, TAPK, PIPE2>;
+    std::call_once(once, [&] {
+        attr_err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    a.px_tiles = (a.M + BPX - 1) / BPX;
+    a.co_tiles = (a.F + BCO - 1) / BCO;
+    const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WCO * WPX * 64), lds, stream, a);
+    return hipGetLastError();
+}
+
+// Tile choice for C_out > 64, four waves (one per SIMD).  256 x 256 tiles
+// (128 x 128 per wave, 256 accumulator registers: LDS traffic ~11 bytes per
+// kFLOP) whenever that still gives a tile per CU; else 256 x 128 (128 x 64
+// per wave, loads two k-tiles ahead); 128 x 128 for C_out <= 128.
+template <int DT, bool RESID, bool TAPK>
+hipError_t launch_tiled_dt(const ConvArgs& a, hipStream_t stream) {
+    const int64_t co_tiles256 = (a.F + 255) / 256;
+    const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
+    if (a.F > 128) {
+        if (px_tiles256 * co_tiles256 >= kNumCUs)
+            return launch_tiled<DT, 4, 4, 2, 2, RESID, TAPK, false>(a, stream);  // 256 x 256
+        return launch_tiled<DT, 4, 2, 2, 2, RESID, TAPK, true>(a, stream);       // 256 x 128
+    }
+    return launch_tiled<DT, 2, 2, 2, 2, RESID, TAPK, true>(a, stream);           // 128 x 128
+}
+
+// The tiled kernel bases each tile's pixel buffer at its first image; the
+// images one tile's 256 pixels can touch must fit the 2^31-byte range.
+bool tiled_ok(const Shape& s, int32_t dtype) {
+    if (s.F <= 64) return false;
+    const int64_t howo = s.Ho * s.Wo;
+    int64_t imgs = 255 / howo + 2;
+    if (imgs > s.N) imgs = s.N;
+    return imgs * s.H * s.W * s.C * elem_bytes(dtype) < ((int64_t)1 << 31);
+}
+
+template <int DT, bool RESID>
+hipError_t launch_tiled_tap(const ConvArgs& a, hipStream_t stream) {
+    constexpr int KT = KT_BYTES / DtTraits<DT>::E;
+    if (a.C > 0 && a.C % KT == 0) return launch_tiled_dt<DT, RESID, true>(a, stream);
+    return launch_tiled_dt<DT, RESID, false>(a, stream);
 }
 
 template <int DT, bool RESID>
@@ -383,6 +436,19 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
             default:
                 return resid ? launch_band_dt<DT_FP8, true>(a, bp, stream)
                              : launch_band_dt<DT_FP8, false>(a, bp, stream);
+        }
+    }
+    if (tiled_ok(s, dtype)) {
+        switch (dtype) {
+            case IGC_DTYPE_BF16:
+                return resid ? launch_tiled_tap<DT_BF16, true>(a, stream)
+                             : launch_tiled_tap<DT_BF16, false>(a, stream);
+            case IGC_DTYPE_FP16:
+                return resid ? launch_tiled_tap<DT_FP16, true>(a, stream)
+                             : launch_tiled_tap<DT_FP16, false>(a, stream);
+            default:
+                return resid ? launch_tiled_tap<DT_FP8, true>(a, stream)
+                             : launch_tiled_tap<DT_FP8, false>(a, stream);
         }
     }
     if (resident_ok(s, dtype)) {
