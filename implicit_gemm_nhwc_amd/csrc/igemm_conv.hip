@@ -83,7 +83,7 @@ int32_t check_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_
         return IGC_DECLINE_SIZE_LIMIT;
     s.kpad = round_up(s.K, KT_BYTES / eb);
     s.kpitch = s.kpad + 16 / eb;
-    if (s.kpitch >= lim) return IGC_DECLINE_SIZE_LIMIT;
+    if (s.kpitch >= lim || s.F * s.kpitch * eb >= lim) return IGC_DECLINE_SIZE_LIMIT;
     if (sh) *sh = s;
     return IGC_OK;
 }
@@ -366,6 +366,53 @@ hipError_t launch_tiled(ConvArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---- wide-layer kernel with direct-to-LDS staging ---------------------------
+template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK>
+hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
+    constexpr int BCO = WCO * TM * 32, BPX = WPX * TN * 32;
+    constexpr size_t lds = (size_t)NSTAGE * (BCO + BPX) * KTB;
+    static_assert(lds <= (size_t)kLdsBytes, "stages fit in LDS");
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    auto kern = igemm_fwd_wide_kernel<DT, TM, TN, WCO, WPX, KTB, NSTAGE, RESID, TAPK>;
+    std::call_once(once, [&] {
+        attr_err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    a.ktiles = a.ktiles * (KT_BYTES / KTB);   // NK rows hold whole 128-byte k-tiles
+    a.px_tiles = (a.M + BPX - 1) / BPX;
+    a.co_tiles = (a.F + BCO - 1) / BCO;
+    const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WCO * WPX * 64), lds, stream, a);
+    return hipGetLastError();
+}
+
+// Tile choice for C_out > 64, four waves (one per SIMD).  256 x 256 tiles
+// (128 x 128 per wave, 256 accumulator registers) whenever that still gives
+// a tile per CU, with 64-byte k-tiles in four stages (requests three k-tiles
+// ahead); else 256 x 128 (128 x 64 per wave) with 128-byte k-tiles in three
+// stages; 128 x 128 with four 128-byte stages for C_out <= 128.  TAPK when
+// C_in is a whole number of k-tiles.
+template <int DT, bool RESID>
+hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
+    constexpr int E = DtTraits<DT>::E;
+    const bool tap64 = a.C > 0 && (a.C * E) % 64 == 0;
+    const bool tap128 = a.C > 0 && (a.C * E) % 128 == 0;
+    const int64_t co_tiles256 = (a.F + 255) / 256;
+    const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
+    if (a.F > 128) {
+        if (px_tiles256 * co_tiles256 >= kNumCUs)
+            return tap64 ? launch_wide<DT, 4, 4, 2, 2, 64, 4, RESID, true>(a, stream)
+                         : launch_wide<DT, 4, 4, 2, 2, 64, 4, RESID, false>(a, stream);
+        return tap128 ? launch_wide<DT, 4, 2, 2, 2, 128, 3, RESID, true>(a, stream)
+                      : launch_wide<DT, 4, 2, 2, 2, 128, 3, RESID, false>(a, stream);
+    }
+    return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 4, RESID, true>(a, stream)
+                  : launch_wide<DT, 2, 2, 2, 2, 128, 4, RESID, false>(a, stream);
+}
+
 // Tile choice for C_out > 64, four waves (one per SIMD).  256 x 256 tiles
 // (128 x 128 per wave, 256 accumulator registers: LDS traffic ~11 bytes per
 // kFLOP) whenever that still gives a tile per CU; else 256 x 128 (128 x 64
@@ -395,8 +442,8 @@ bool tiled_ok(const Shape& s, int32_t dtype) {
 template <int DT, bool RESID>
 hipError_t launch_tiled_tap(const ConvArgs& a, hipStream_t stream) {
     constexpr int KT = KT_BYTES / DtTraits<DT>::E;
-    if (a.C > 0 && a.C % KT == 0) return launch_tiled_dt<DT, RESID, true>(a, stream);
-    return launch_tiled_dt<DT, RESID, false>(a, stream);
+    (void)KT;
+    return launch_wide_dt<DT, RESID>(a, stream);
 }
 
 template <int DT, bool RESID>

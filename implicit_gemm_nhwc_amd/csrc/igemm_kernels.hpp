@@ -1201,4 +1201,361 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_tiled_kernel(ConvArg
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Wide-layer implicit GEMM with direct-to-LDS staging.  Same tiling as the
+// kernel above (BCO x BPX workgroup tiles, WCO x WPX waves of TM x TN 32x32
+// blocks), but the k-tiles reach LDS through buffer-load-to-LDS: no staging
+// registers and no LDS-write instructions in the loop, which matters because
+// LDS writes run at about half the LDS read rate.
+//
+// Stage layout: BCO filter rows then BPX pixel rows of KTB bytes (64 or 128),
+// unpadded.  Chunk d (16 bytes) of row r sits at position d ^ swz(r), with
+// swz(r) = r & 7 for 128-byte rows and (r >> 1) & 3 for 64-byte rows, so the
+// 8 lanes of a fragment read that share a chunk index land in 8 different
+// 16-byte bank groups.  One wave DMA instruction fills 1 KB = 1024 / KTB
+// whole rows (lane t -> position t % CPR of row t / CPR), so each lane
+// fetches the chunk that belongs at its position.
+//
+// NSTAGE stages rotate.  Each k-tile requests k-tile kt + NSTAGE - 1 (a
+// fully masked request past the end keeps the wait counts uniform), runs
+// its MFMA steps with the next step's fragments read in between, and
+// before its last step waits for k-tile kt + 1, meets the other waves at a
+// barrier and reads the first fragments of k-tile kt + 1, so the last step
+// multiplies while they arrive.
+//
+// The epilogue goes through LDS per 32-pixel block: each wave writes its
+// fp32 block in [pixel][channel] order into a private region and reads it
+// back with consecutive lanes on consecutive channels of one pixel.  The
+// residual of block j + 1 is requested while block j is finished; stores
+// are 8 bytes per lane, contiguous over the wave's channels, and buffer
+// range checks drop pixels past the end.
+template <int DT>
+struct WideStep;
+template <>
+struct WideStep<DT_BF16> { static constexpr int KSB = 32; };
+template <>
+struct WideStep<DT_FP16> { static constexpr int KSB = 32; };
+template <>
+struct WideStep<DT_FP8> { static constexpr int KSB = 64; };
+
+template <int V>
+struct IntC { static constexpr int value = V; };
+
+template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK>
+__global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs a) {
+    constexpr int E = DtTraits<DT>::E;
+    constexpr int VEC = 16 / E;
+    constexpr int KTE = KTB / E;                      // k elements per k-tile
+    constexpr int CPR = KTB / 16;                     // chunks per staged row
+    constexpr int RPI = 64 / CPR;                     // rows per DMA instruction
+    constexpr int NW = WCO * WPX;
+    constexpr int BCO = WCO * TM * 32;
+    constexpr int BPX = WPX * TN * 32;
+    constexpr int AI = BCO / (RPI * NW), BI = BPX / (RPI * NW);   // DMA instrs per wave
+    constexpr int KSB = WideStep<DT>::KSB;            // k bytes per MFMA step
+    constexpr int FR = KSB / 32;                      // 16-byte chunks per fragment
+    constexpr int KS = KTB / KSB;                     // MFMA steps per k-tile
+    constexpr int STAGE = (BCO + BPX) * KTB;
+    constexpr int WAITN = (NSTAGE - 2) * (AI + BI);   // requests left in flight
+    static_assert(KTB == 64 || KTB == 128, "64- or 128-byte k-tiles");
+    static_assert(AI * RPI * NW == BCO && BI * RPI * NW == BPX, "whole DMA rows per wave");
+    static_assert(NSTAGE >= 2 && WAITN < 64, "stage count within the wait counter");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wco = wave / WPX, wpx = wave % WPX;
+
+    const int tile = xcd_remap(blockIdx.x, a.px_tiles * a.co_tiles);
+    const int co_tile = tile % a.co_tiles;
+    const int px_tile = tile / a.co_tiles;
+    const int co0 = co_tile * BCO;
+    const int m0 = px_tile * BPX;
+
+    auto swz = [](int r) { return CPR == 8 ? (r & 7) : ((r >> 1) & 3); };
+    // this lane's DMA slot: row `sub` of each RPI-row group, data chunk `dch`
+    const int sub = lane / CPR;
+    const int dch = (lane % CPR) ^ swz(sub);
+
+    // filter rows: the NK matrix (below 2^31 bytes), rows >= C_out out of range
+    const uint32_t nk_bytes = (uint32_t)a.F * (uint32_t)a.kpitch * (uint32_t)E;
+    const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, nk_bytes);
+    uint32_t aoff[AI];
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+        const int co = co0 + (wave * AI + i) * RPI + sub;
+        aoff[i] = co < a.F ? (uint32_t)co * (uint32_t)(a.kpitch * E) + dch * 16 : OOB_OFFSET;
+    }
+    // pixel rows: the buffer starts at the tile's first image
+    const int howo = a.Ho * a.Wo;
+    const int n0 = m0 / howo;
+    const int64_t img = (int64_t)a.H * a.W * a.C * E;   // bytes per image
+    const int64_t base = (int64_t)n0 * img;
+    const int64_t span = (int64_t)(a.M / howo) * img - base;
+    const __amdgpu_buffer_rsrc_t xrs =
+        make_rsrc(a.x + base, span > (int64_t)OOB_OFFSET ? OOB_OFFSET : (uint32_t)span);
+    int prel[BI], pih[BI], piw[BI];
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+        const int m = m0 + (wave * BI + i) * RPI + sub;
+        if (m < a.M) {
+            const int n = m / howo;
+            const int rem = m - n * howo;
+            const int oh = rem / a.Wo;
+            const int ow = rem - oh * a.Wo;
+            pih[i] = oh * a.stride - a.pad;
+            piw[i] = ow * a.stride - a.pad;
+            // TAPK: the lane's chunk offset rides here; otherwise the per-lane
+            // k walk below already starts at chunk dch
+            prel[i] = (int)((int64_t)(n - n0) * img + (int64_t)(pih[i] * a.W + piw[i]) * a.C * E) +
+                      (TAPK ? dch * 16 : 0);
+        } else {
+            pih[i] = -(1 << 28);
+            piw[i] = 0;
+            prel[i] = 0;
+        }
+    }
+    // k walk: uniform (TAPK) or per lane (this lane's chunk dch)
+    int t_ci = 0, t_r = 0, t_s = 0;
+    int kk = dch * VEC, ci = 0, fr = 0, fs = 0;
+    if constexpr (!TAPK) {
+        const int Cdiv = a.C > 0 ? a.C : 1;
+        const int tap = kk / Cdiv;
+        ci = kk - tap * Cdiv;
+        fr = tap / a.S;
+        fs = tap - fr * a.S;
+    }
+    auto dma = [](__amdgpu_buffer_rsrc_t rs, uint8_t* dst, uint32_t off) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+    };
+    const int nkt = a.ktiles;
+    // request the next k-tile into stage `st` (fully masked past the end)
+    int kt_next = 0;
+    auto issue = [&](int st) {
+        const int kt = kt_next++;
+        const uint32_t past = kt < nkt ? 0u : OOB_OFFSET;
+        uint8_t* sb = lds + st * STAGE;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            dma(frs, sb + (wave * AI + i) * 1024, (aoff[i] + (uint32_t)(kt * KTB)) | past);
+        uint8_t* pb = sb + BCO * KTB;
+        if constexpr (TAPK) {
+            const int koff = ((t_r * a.W + t_s) * a.C + t_ci) * E;
+#pragma unroll
+            for (int i = 0; i < BI; ++i) {
+                const bool ok = ((unsigned)(pih[i] + t_r) < (unsigned)a.H) &
+                                ((unsigned)(piw[i] + t_s) < (unsigned)a.W);
+                dma(xrs, pb + (wave * BI + i) * 1024,
+                    (uint32_t)(prel[i] + koff) | ((uint32_t)!ok << 31) | past);
+            }
+            t_ci += KTE;
+            const bool wrap = t_ci >= a.C;
+            t_ci = wrap ? 0 : t_ci;
+            t_s += wrap ? 1 : 0;
+            const bool wrap2 = t_s >= a.S;
+            t_s = wrap2 ? 0 : t_s;
+            t_r += wrap2 ? 1 : 0;
+        } else {
+            const bool kin = kk < a.K;
+            const int koff = ((fr * a.W + fs) * a.C + ci) * E;
+#pragma unroll
+            for (int i = 0; i < BI; ++i) {
+                const bool ok = kin & ((unsigned)(pih[i] + fr) < (unsigned)a.H) &
+                                ((unsigned)(piw[i] + fs) < (unsigned)a.W);
+                dma(xrs, pb + (wave * BI + i) * 1024,
+                    (uint32_t)(prel[i] + koff) | ((uint32_t)!ok << 31) | past);
+            }
+            kk += KTE;
+            ci += KTE;
+            while (ci >= a.C && a.C > 0) {
+                ci -= a.C;
+                if (++fs == a.S) { fs = 0; ++fr; }
+            }
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+    // fragment addresses: row (lane & 31) of each 32-row block, chunk
+    // ks*2*FR + half*FR + h at its swizzled position
+    const int frow = lane & 31, half = lane >> 5;
+    int xa[KS][FR], xb[KS][FR];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int h = 0; h < FR; ++h) {
+            const int x = frow * KTB + (((ks * 2 * FR + half * FR + h) ^ swz(frow)) << 4);
+            xa[ks][h] = x + wco * TM * 32 * KTB;
+            xb[ks][h] = x + (BCO + wpx * TN * 32) * KTB;
+        }
+    i32x4 af[2][TM][FR], bfr[2][TN][FR];
+    auto read_frags = [&](int st, int ks, int fb) {
+        const uint8_t* sb = lds + st * STAGE;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int h = 0; h < FR; ++h)
+                af[fb][i][h] = *reinterpret_cast<const i32x4*>(sb + xa[ks][h] + i * 32 * KTB);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int h = 0; h < FR; ++h)
+                bfr[fb][j][h] = *reinterpret_cast<const i32x4*>(sb + xb[ks][h] + j * 32 * KTB);
+    };
+    auto mma = [&](int fb) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int i = 0; i < TM; ++i) acc[i][j] = mfma32<DT>(af[fb][i], bfr[fb][j], acc[i][j]);
+    };
+    constexpr int MPG = (TM * TN + TM + TN - 1) / (TM + TN);
+    auto interleave = [&]() {
+#pragma unroll
+        for (int g = 0; g < TM + TN; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);   // DS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);  // MFMAs
+        }
+    };
+
+    int cur = 0;   // stage of the k-tile being multiplied
+    // one k-tile whose step-0 fragments are in buffer FB0
+    auto ktile = [&](auto fb0c) {
+        constexpr int FB0 = decltype(fb0c)::value;
+        issue(cur == 0 ? NSTAGE - 1 : cur - 1);
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+            read_frags(cur, ks + 1, (FB0 + ks + 1) & 1);
+            mma((FB0 + ks) & 1);
+            interleave();
+        }
+        // k-tile kt + 1 complete in this wave's part and this wave's reads of
+        // stage `cur` finished; then a bare barrier (__syncthreads would
+        // also drain the requests still in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(WAITN) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+        read_frags(cur, 0, (FB0 + KS) & 1);   // past the last k-tile: a harmless read
+        mma((FB0 + KS - 1) & 1);
+        interleave();
+    };
+
+    if (nkt > 0) {
+#pragma unroll
+        for (int st = 0; st < NSTAGE - 1; ++st) issue(st);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        read_frags(0, 0, 0);
+        if constexpr (KS % 2 == 0) {
+            for (int kt = 0; kt < nkt; ++kt) ktile(IntC<0>{});
+        } else {
+            // buffers alternate between k-tiles: two per iteration.  KS is
+            // odd only for 64-byte k-tiles, and NK rows hold whole 128-byte
+            // k-tiles, so nkt is even.
+            static_assert(KTB == 64, "odd step counts only with 64-byte k-tiles");
+            for (int kt = 0; kt < nkt; kt += 2) {
+                ktile(IntC<0>{});
+                ktile(IntC<1>{});
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // masked tail requests
+    __syncthreads();   // stages no longer read or written
+
+    // ---- epilogue through a private LDS region per wave
+    constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
+    constexpr int WCH = TM * 32;                 // channels per wave
+    constexpr int EP = WCH * 4 + 16;             // bytes per pixel row (padded)
+    constexpr int LPP = WCH / 4;                 // lanes per pixel on read-back
+    constexpr int PPI = 64 / LPP;                // pixels per read-back instruction
+    constexpr int NI = 32 / PPI;                 // read-back instructions per block
+    static_assert(NW * 32 * EP <= NSTAGE * STAGE, "epilogue region fits the stages");
+    uint8_t* ereg = lds + wave * 32 * EP;
+    const int c4 = lane % LPP, pl = lane / LPP;
+    const int co = co0 + wco * WCH + c4 * 4;     // this lane's first channel
+    auto stage_block = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 v4 = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                  acc[i][j][4 * g + 3]};
+                *reinterpret_cast<f32x4*>(ereg + frow * EP + (i * 32 + g * 8 + half * 4) * 4) = v4;
+            }
+    };
+    if ((a.F & 3) == 0) {
+        // block j's pixels [mb, mb + 32): buffers over pixels [mb, M)
+        auto blk = [&](const uint16_t* p, int mb) {
+            const int64_t bytes = mb < a.M ? (int64_t)(a.M - mb) * a.F * 2 : 0;
+            return make_rsrc(p + (int64_t)mb * a.F,
+                             bytes > (int64_t)OOB_OFFSET ? OOB_OFFSET : (uint32_t)bytes);
+        };
+        const uint32_t cmask = co < a.F ? 0u : OOB_OFFSET;
+        const int mw = m0 + wpx * TN * 32;      // this wave's first pixel
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 sv[2][NI];
+        auto load_src = [&](int j) {
+            const __amdgpu_buffer_rsrc_t srs = blk(a.src, mw + j * 32);
+#pragma unroll
+            for (int q = 0; q < NI; ++q)
+                sv[j & 1][q] = __builtin_amdgcn_raw_buffer_load_b64(
+                    srs, (uint32_t)(((q * PPI + pl) * a.F + co) * 2) | cmask, 0, 0);
+        };
+        if constexpr (RESID) load_src(0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (RESID) {
+                if (j + 1 < TN) load_src(j + 1);
+            }
+            stage_block(j);
+            const __amdgpu_buffer_rsrc_t yrs = blk(a.y, mw + j * 32);
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(ereg + (q * PPI + pl) * EP + c4 * 16);
+                float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+                if constexpr (RESID) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint16_t h = (uint16_t)(sv[j & 1][q][e >> 1] >> (16 * (e & 1)));
+                        v[e] = __builtin_fmaf(a.beta, out_to_f32(h, ODT), v[e]);
+                    }
+                }
+                u32x2 ov;
+                ov[0] = (uint32_t)f32_to_out(v[0], ODT) | ((uint32_t)f32_to_out(v[1], ODT) << 16);
+                ov[1] = (uint32_t)f32_to_out(v[2], ODT) | ((uint32_t)f32_to_out(v[3], ODT) << 16);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    ov, yrs, (uint32_t)(((q * PPI + pl) * a.F + co) * 2) | cmask, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            stage_block(j);
+            const int mb = m0 + wpx * TN * 32 + j * 32;
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                const int m = mb + q * PPI + pl;
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(ereg + (q * PPI + pl) * EP + c4 * 16);
+                if (m >= a.M) continue;
+                const int64_t o = (int64_t)m * a.F + co;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (co + e < a.F) {
+                        float d = v4[e];
+                        if constexpr (RESID) d = __builtin_fmaf(a.beta, out_to_f32(a.src[o + e], ODT), d);
+                        a.y[o + e] = f32_to_out(d, ODT);
+                    }
+                }
+            }
+        }
+    }
+}
+
 }  // namespace igc

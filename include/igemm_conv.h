@@ -92,7 +92,8 @@ const char* conv2d_reason_string(int32_t reason);
  * the page's dispatcher plus this library's limits.  Pointers are only
  * compared and tested for alignment, never dereferenced.  workspace may be
  * NULL (the library then allocates).  Returns IGC_OK or a decline reason.
- * Size limits: N*Ho*Wo, C_out, R*S*C_in, and (R*W + S)*C_in each below 2^31.
+ * Size limits: N*Ho*Wo, C_out, R*S*C_in, and (R*W + S)*C_in each below 2^31,
+ * and the NK matrix (conv2d_workspace_bytes) below 2^31 bytes.
  */
 int32_t conv2d_fwd_check(const void* input, const int64_t in_nhwc[4],
                          const void* filter, int32_t filter_is_fcrs,
