@@ -25,7 +25,7 @@ int elem_bytes(int32_t dtype) { return dtype == IGC_DTYPE_FP8_E4M3FN ? 1 : 2; }
 struct Shape {
     int64_t N, H, W, C, R, S, F, Ho, Wo, M, K;
     int64_t kpad;    // K rounded up to whole 128-byte k-tiles (elements)
-    int64_t kpitch;  // NK row stride: kpad plus a 16-byte zero pad (elements)
+    int64_t kpitch;  // NK row stride (elements), see nk_pitch
     int32_t st, pad;
 };
 
@@ -40,6 +40,15 @@ int64_t out_size(int64_t in, int64_t k, int64_t st, int64_t pad) {
 }
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// NK row stride in elements: K rounded up to whole 128-byte k-tiles; for
+// C_out <= 64 plus a 16-byte zero pad, since those kernels copy the rows
+// straight into LDS and read fragments across them (a pitch of 16 mod 128
+// bytes spreads the rows over the banks), while the wide-layer kernel
+// requests whole 128-byte row segments and wants them line aligned.
+int64_t nk_pitch(int64_t K, int64_t F, int64_t eb) {
+    return round_up(K, KT_BYTES / eb) + (F <= 64 ? 16 / eb : 0);
+}
 
 // Shape-only part of the gate: page rules, shape consistency, limits.
 int32_t check_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_dims[4],
@@ -82,7 +91,7 @@ int32_t check_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_
         (s.R * s.W + s.S) * s.C >= lim)
         return IGC_DECLINE_SIZE_LIMIT;
     s.kpad = round_up(s.K, KT_BYTES / eb);
-    s.kpitch = s.kpad + 16 / eb;
+    s.kpitch = nk_pitch(s.K, s.F, eb);
     if (s.kpitch >= lim || s.F * s.kpitch * eb >= lim) return IGC_DECLINE_SIZE_LIMIT;
     if (sh) *sh = s;
     return IGC_OK;
@@ -389,23 +398,21 @@ hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Tile choice for C_out > 64, four waves (one per SIMD).  256 x 256 tiles
-// (128 x 128 per wave, 256 accumulator registers) whenever that still gives
-// a tile per CU, with 64-byte k-tiles in four stages (requests three k-tiles
-// ahead); else 256 x 128 (128 x 64 per wave) with 128-byte k-tiles in three
-// stages; 128 x 128 with four 128-byte stages for C_out <= 128.  TAPK when
-// C_in is a whole number of k-tiles.
+// Tile choice for C_out > 64, four waves (one per SIMD), 128-byte k-tiles
+// (whole cache lines per request).  256 x 256 tiles (128 x 128 per wave,
+// 256 accumulator registers) in two stages whenever that still gives a tile
+// per CU; else 256 x 128 (128 x 64 per wave) in three stages; 128 x 128 in
+// four stages for C_out <= 128.  TAPK when C_in is a whole number of k-tiles.
 template <int DT, bool RESID>
 hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     constexpr int E = DtTraits<DT>::E;
-    const bool tap64 = a.C > 0 && (a.C * E) % 64 == 0;
     const bool tap128 = a.C > 0 && (a.C * E) % 128 == 0;
     const int64_t co_tiles256 = (a.F + 255) / 256;
     const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
     if (a.F > 128) {
         if (px_tiles256 * co_tiles256 >= kNumCUs)
-            return tap64 ? launch_wide<DT, 4, 4, 2, 2, 64, 4, RESID, true>(a, stream)
-                         : launch_wide<DT, 4, 4, 2, 2, 64, 4, RESID, false>(a, stream);
+            return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
+                          : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
         return tap128 ? launch_wide<DT, 4, 2, 2, 2, 128, 3, RESID, true>(a, stream)
                       : launch_wide<DT, 4, 2, 2, 2, 128, 3, RESID, false>(a, stream);
     }
@@ -574,7 +581,7 @@ int64_t conv2d_nk_row_pitch(const int64_t filt_dims[4], int32_t filter_is_fcrs, 
     int64_t R, S, C, F;
     filter_rscf(filt_dims, filter_is_fcrs, &R, &S, &C, &F);
     if (R < 0 || S < 0 || C < 0 || F < 0) return -1;
-    return round_up(R * S * C, KT_BYTES / elem_bytes(dtype)) + 16 / elem_bytes(dtype);
+    return nk_pitch(R * S * C, F, elem_bytes(dtype));
 }
 
 int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs, const int64_t filt_dims[4],
@@ -591,7 +598,7 @@ int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs, const in
     s.K = s.R * s.S * s.C;
     if (s.K >= lim) return 0;
     s.kpad = round_up(s.K, KT_BYTES / eb);
-    s.kpitch = s.kpad + 16 / eb;
+    s.kpitch = nk_pitch(s.K, s.F, eb);
     const size_t need = (size_t)(s.F * s.kpitch) * (size_t)eb;
     const size_t fbytes = (size_t)(s.K * s.F) * (size_t)eb;
     if (nk_bytes < need) return 0;

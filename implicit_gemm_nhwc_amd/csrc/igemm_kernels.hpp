@@ -53,7 +53,7 @@ struct ConvArgs {
     int S, stride, pad;
     int R;              // filter height
     int K;              // R*S*C elements
-    int kpitch;         // elements per NK row (stride; includes a 16-byte zero pad)
+    int kpitch;         // elements per NK row (stride; a 16-byte zero pad when C_out <= 64)
     int M;              // N*Ho*Wo
     int ktiles;         // 128-byte k-tiles covering K
     int px_tiles;       // ceil(M / BPX)
@@ -1217,12 +1217,13 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_tiled_kernel(ConvArg
 // whole rows (lane t -> position t % CPR of row t / CPR), so each lane
 // fetches the chunk that belongs at its position.
 //
-// NSTAGE stages rotate.  Each k-tile requests k-tile kt + NSTAGE - 1 (a
-// fully masked request past the end keeps the wait counts uniform), runs
-// its MFMA steps with the next step's fragments read in between, and
-// before its last step waits for k-tile kt + 1, meets the other waves at a
-// barrier and reads the first fragments of k-tile kt + 1, so the last step
-// multiplies while they arrive.
+// NSTAGE stages rotate.  A k-tile runs its MFMA steps with the next step's
+// fragments read in between; before its last step it waits for k-tile
+// kt + 1 and meets the other waves at a barrier, after which its own stage
+// is free: it requests k-tile kt + NSTAGE there (a fully masked request past
+// the end keeps the wait counts uniform) and reads the first fragments of
+// k-tile kt + 1 while the last step multiplies.  A request thus has
+// NSTAGE - 1 whole k-tiles to arrive.
 //
 // The epilogue goes through LDS per 32-pixel block: each wave writes its
 // fp32 block in [pixel][channel] order into a private region and reads it
@@ -1260,7 +1261,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
     constexpr int WAITN = (NSTAGE - 2) * (AI + BI);   // requests left in flight
     static_assert(KTB == 64 || KTB == 128, "64- or 128-byte k-tiles");
     static_assert(AI * RPI * NW == BCO && BI * RPI * NW == BPX, "whole DMA rows per wave");
-    static_assert(NSTAGE >= 2 && WAITN < 64, "stage count within the wait counter");
+    static_assert(NSTAGE >= 2 && (NSTAGE - 1) * (AI + BI) < 64, "stage count within the wait counter");
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -1428,7 +1429,6 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
     // one k-tile whose step-0 fragments are in buffer FB0
     auto ktile = [&](auto fb0c) {
         constexpr int FB0 = decltype(fb0c)::value;
-        issue(cur == 0 ? NSTAGE - 1 : cur - 1);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read_frags(cur, ks + 1, (FB0 + ks + 1) & 1);
@@ -1441,6 +1441,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(WAITN) : "memory");
         __builtin_amdgcn_sched_barrier(0);
+        issue(cur);   // stage `cur` is free in every wave: k-tile kt + NSTAGE
         cur = cur + 1 == NSTAGE ? 0 : cur + 1;
         read_frags(cur, 0, (FB0 + KS) & 1);   // past the last k-tile: a harmless read
         mma((FB0 + KS - 1) & 1);
@@ -1449,8 +1450,8 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
 
     if (nkt > 0) {
 #pragma unroll
-        for (int st = 0; st < NSTAGE - 1; ++st) issue(st);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int st = 0; st < NSTAGE; ++st) issue(st);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 1) * (AI + BI)) : "memory");
         __syncthreads();
         read_frags(0, 0, 0);
         if constexpr (KS % 2 == 0) {

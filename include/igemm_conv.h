@@ -139,9 +139,10 @@ size_t conv2d_workspace_bytes(const int64_t filt_dims[4],
 
 /*
  * Elements per NK row: K = R*S*C_in rounded up to a multiple of
- * 128 bytes' worth of elements (64 for bf16/fp16, 128 for fp8), plus
- * 16 bytes of zeros (8 or 16 elements) that keep LDS copies of the rows
- * free of bank conflicts.
+ * 128 bytes' worth of elements (64 for bf16/fp16, 128 for fp8); for
+ * C_out <= 64 plus 16 bytes of zeros (8 or 16 elements) that keep LDS
+ * copies of the rows free of bank conflicts.  Wider filters keep rows a
+ * whole number of 128-byte lines.
  */
 int64_t conv2d_nk_row_pitch(const int64_t filt_dims[4], int32_t filter_is_fcrs,
                             int32_t dtype);

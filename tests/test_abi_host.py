@@ -131,10 +131,11 @@ def test_workspace_and_pitch():
     # K rounded up to whole 128-byte k-tiles, plus a 16-byte zero pad per row
     assert igc.conv2d_nk_row_pitch((3, 3, 16, 16), False, 0) == 192 + 8     # 144 -> 3*64
     assert igc.conv2d_nk_row_pitch((64, 64, 3, 3), True, 0) == 576 + 8
-    assert igc.conv2d_nk_row_pitch((5, 5, 256, 256), False, 2) == 6400 + 16
+    assert igc.conv2d_nk_row_pitch((5, 5, 256, 256), False, 2) == 6400         # C_out > 64: no pad
+    assert igc.conv2d_nk_row_pitch((5, 5, 256, 64), False, 2) == 6400 + 16
     assert igc.conv2d_nk_row_pitch((3, 3, 16, 16), False, 2) == 256 + 16    # 144 -> 2*128
     assert igc.conv2d_workspace_bytes((3, 3, 128, 3), False, 0) == 3 * 1160 * 2
-    assert igc.conv2d_workspace_bytes((256, 128, 3, 3), True, 1) == 256 * 1160 * 2
+    assert igc.conv2d_workspace_bytes((256, 128, 3, 3), True, 1) == 256 * 1152 * 2
     assert igc.conv2d_workspace_bytes((3, 3, 16, 16), False, 9) == 0
 
 
