@@ -314,11 +314,11 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
     return found;
 }
 
-template <int DT, int TM, int TN, bool RESID>
+template <int DT, int TM, int TN, int U, bool RESID>
 hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
-    auto kern = igemm_fwd_band_kernel<DT, TM, TN, RESID>;
+    auto kern = igemm_fwd_band_kernel<DT, TM, TN, U, RESID>;
     std::call_once(once, [&] {
         attr_err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
@@ -338,13 +338,23 @@ hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// k-steps per unrolled block: the largest of 4, 2, 1 dividing the steps per tap
+template <int DT, int TM, int TN, bool RESID>
+hipError_t launch_band_u(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
+    constexpr int KSB = DT == DT_FP8 ? 64 : 32;
+    const int steps = a.C * DtTraits<DT>::E / KSB;
+    if (steps % 4 == 0) return launch_band<DT, TM, TN, 4, RESID>(a, bp, stream);
+    if (steps % 2 == 0) return launch_band<DT, TM, TN, 2, RESID>(a, bp, stream);
+    return launch_band<DT, TM, TN, 1, RESID>(a, bp, stream);
+}
+
 template <int DT, int TM, bool RESID>
 hipError_t launch_band_tm(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
     switch (bp.TN) {
-        case 1: return launch_band<DT, TM, 1, RESID>(a, bp, stream);
-        case 2: return launch_band<DT, TM, 2, RESID>(a, bp, stream);
-        case 3: return launch_band<DT, TM, 3, RESID>(a, bp, stream);
-        default: return launch_band<DT, TM, 4, RESID>(a, bp, stream);
+        case 1: return launch_band_u<DT, TM, 1, RESID>(a, bp, stream);
+        case 2: return launch_band_u<DT, TM, 2, RESID>(a, bp, stream);
+        case 3: return launch_band_u<DT, TM, 3, RESID>(a, bp, stream);
+        default: return launch_band_u<DT, TM, 4, RESID>(a, bp, stream);
     }
 }
 

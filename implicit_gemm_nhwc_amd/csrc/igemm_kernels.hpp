@@ -664,6 +664,9 @@ __device__ __forceinline__ int small_div(int n, int d, float inv_d) {
     return q;
 }
 
+template <int V>
+struct IntC { static constexpr int value = V; };
+
 constexpr int BAND_WAVES = 4;
 constexpr int BAND_MAX_TN = 4;   // 32-pixel blocks per wave at most (tile <= 512 px)
 
@@ -707,10 +710,11 @@ __device__ __forceinline__ f32x16 mfma32<DT_FP8>(const i32x4* a, const i32x4* b,
 // results go through LDS and leave with coalesced 16-byte stores; the
 // residual is added there, before the single rounding.
 //
-// TM: 32-row blocks of output channels; TN: 32-pixel blocks per wave.  The
-// input pixel size C_in * elem bytes is a power-of-two multiple of the MFMA
-// k-step (cpp_log2 = log2 of its 16-byte chunks).
-template <int DT, int TM, int TN, bool RESID>
+// TM: 32-row blocks of output channels; TN: 32-pixel blocks per wave; U:
+// MFMA k-steps per unrolled block (1, 2 or 4, dividing the steps per tap).
+// The input pixel size C_in * elem bytes is a power-of-two multiple of the
+// MFMA k-step (cpp_log2 = log2 of its 16-byte chunks).
+template <int DT, int TM, int TN, int U, bool RESID>
 __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArgs a) {
     constexpr int E = DtTraits<DT>::E;
     constexpr int KSB = (DT == DT_FP8) ? 64 : 32;   // K bytes per 32x32 MFMA
@@ -792,7 +796,11 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
 
     // ---- phase B: MFMAs from LDS.  Wave w owns pixel blocks w, w+4, ...,
     // always TN of them; blocks past the tile read patch pixel 0 and are
-    // never stored.  Fragments of step q+1 load while step q multiplies.
+    // never stored.  The k-steps run in blocks of U inside one filter tap:
+    // per block one scalar base per operand, the U steps at immediate LDS
+    // offsets, and the fragments of the next step read while this one
+    // multiplies (into the other of two register sets, fixed at compile
+    // time: step j of a block uses set j & 1).
     const int P = a.TH * a.TW;
     int pb[TN];
 #pragma unroll
@@ -802,47 +810,47 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         pb[t] = a.patch_off + half * 16 * FR +
                 ((p < P) ? (tp * a.stride * a.PW + tq * a.stride) * a.ppitch : 0);
     }
-    const uint8_t* frow = lds + frag_row * a.fpitch + half * 16 * FR;
+    int fr_off[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fr_off[i] = (i * 32 + frag_row) * a.fpitch + half * 16 * FR;
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t) acc[i][t] = f32x16{};
 
-    const int ksteps = cbytes / KSB;
-    const int Q = a.R * a.S * ksteps;
-    // uniform walk over k-steps: (r, s, kc) -> patch and filter byte offsets;
-    // past the last step it wraps to step 0 so the spare prefetch of the
-    // final iteration still reads valid LDS
-    int q_r = 0, q_s = 0, q_kc = 0;
-    auto offsets = [&](int& poff, int& foff) {
-        poff = (q_r * a.PW + q_s) * a.ppitch + q_kc * KSB;
-        foff = (q_r * a.S + q_s) * cbytes + q_kc * KSB;
-        if (++q_kc == ksteps) {
-            q_kc = 0;
-            if (++q_s == a.S) { q_s = 0; if (++q_r == a.R) q_r = 0; }
+    const int bpt = cbytes / (KSB * U);   // blocks per tap
+    const int NB = a.R * a.S * bpt;
+    // uniform walk over blocks: (r, s, b) -> patch and filter byte bases; past
+    // the last block it wraps to block 0, so the spare prefetch of the final
+    // block still reads valid LDS
+    int w_r = 0, w_s = 0, w_b = 0;
+    auto next_bases = [&](int& pbase, int& fbase) {
+        if (++w_b == bpt) {
+            w_b = 0;
+            if (++w_s == a.S) { w_s = 0; if (++w_r == a.R) w_r = 0; }
         }
+        pbase = (w_r * a.PW + w_s) * a.ppitch + w_b * U * KSB;
+        fbase = (w_r * a.S + w_s) * cbytes + w_b * U * KSB;
     };
     i32x4 fa[2][TM][FR], fb[2][TN][FR];
-    auto load = [&](int buf) {
-        int poff, foff;
-        offsets(poff, foff);
+    auto rd = [&](int set, int pbase, int fbase, int j) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int h = 0; h < FR; ++h)
-                fa[buf][i][h] = *reinterpret_cast<const i32x4*>(frow + i * 32 * a.fpitch + foff + h * 16);
+                fa[set][i][h] = *reinterpret_cast<const i32x4*>(lds + fr_off[i] + fbase + j * KSB + h * 16);
 #pragma unroll
         for (int t = 0; t < TN; ++t)
 #pragma unroll
             for (int h = 0; h < FR; ++h)
-                fb[buf][t][h] = *reinterpret_cast<const i32x4*>(lds + pb[t] + poff + h * 16);
+                fb[set][t][h] = *reinterpret_cast<const i32x4*>(lds + pb[t] + pbase + j * KSB + h * 16);
     };
-    auto mma = [&](int buf) {
+    auto mma = [&](int set) {
 #pragma unroll
         for (int t = 0; t < TN; ++t)
 #pragma unroll
-            for (int i = 0; i < TM; ++i) acc[i][t] = mfma32<DT>(fa[buf][i], fb[buf][t], acc[i][t]);
+            for (int i = 0; i < TM; ++i) acc[i][t] = mfma32<DT>(fa[set][i], fb[set][t], acc[i][t]);
     };
     // Interleave the next step's fragment reads with this step's MFMAs so
     // the LDS latency hides behind matrix work.
@@ -854,19 +862,39 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);  // MFMAs
         }
     };
-    // Two steps per iteration with no early exit, so every accumulator
-    // stays in place across the loop; an odd last step runs after it.
-    if (Q > 0) load(0);
-    int q = 0;
-    for (; q + 2 <= Q; q += 2) {
-        load(1);      // step q+1
-        mma(0);       // step q
-        interleave();
-        load(0);      // step q+2 (a harmless re-read past the end)
-        mma(1);       // step q+1
-        interleave();
+    // one block at bases (pb0, fb0) whose step 0 is in set S0; the next
+    // block's step 0 goes to set (S0 + U) & 1
+    int pb0 = 0, fb0 = 0;
+    auto block = [&](auto s0c) {
+        constexpr int S0 = decltype(s0c)::value;
+        int pbn, fbn;
+        next_bases(pbn, fbn);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if (j + 1 < U) rd((S0 + j + 1) & 1, pb0, fb0, j + 1);
+            else rd((S0 + U) & 1, pbn, fbn, 0);
+            mma((S0 + j) & 1);
+            interleave();
+            // fence: the scheduler must not pull the next step's MFMAs up
+            // next to their own reads
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pb0 = pbn;
+        fb0 = fbn;
+    };
+    if (NB > 0) rd(0, 0, 0, 0);
+    if constexpr (U % 2 == 0) {
+        for (int q = 0; q < NB; ++q) block(IntC<0>{});
+    } else {
+        // sets alternate between blocks: two per iteration with no early
+        // exit, so every accumulator stays in place; an odd last block after
+        int q = 0;
+        for (; q + 2 <= NB; q += 2) {
+            block(IntC<0>{});
+            block(IntC<1>{});
+        }
+        if (q < NB) block(IntC<0>{});
     }
-    if (q < Q) mma(0);
     __syncthreads();  // patch and filter no longer read
 
     // ---- epilogue: fp32 tile -> LDS [P][spitch floats] -> coalesced stores
@@ -1240,8 +1268,6 @@ struct WideStep<DT_FP16> { static constexpr int KSB = 32; };
 template <>
 struct WideStep<DT_FP8> { static constexpr int KSB = 64; };
 
-template <int V>
-struct IntC { static constexpr int value = V; };
 
 template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK>
 __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs a) {
