@@ -1,19 +1,23 @@
 """Benchmark: forward NHWC convolution as an implicit GEMM on one MI355X.
 
-One step = the whole path on one batch: the host gate, the filter transpose
-to NK (conv2d_filter_to_nk) and the implicit-GEMM kernel with its fused
-epilogue (conv2d_fwd_nk) -- exactly what conv2d_fwd enqueues, split in two
-calls so HIP events can bracket the GEMM kernel alone.
+One step = the whole path on one batch: the filter transpose to NK
+(conv2d_filter_to_nk) and the implicit-GEMM kernel with its fused epilogue
+(conv2d_fwd_nk) -- exactly what conv2d_fwd enqueues.  Each buffer set's step
+is captured once in a HIP graph (replays checked bit for bit against the
+eager step), and the timed loop replays them, so host-side launch overhead
+does not pace the GPU.
 
 Headline workload: the ResNet-style 3x3 body conv (N=32, 56x56, 64->64,
 stride 1, padding 1, bf16, FCRS filter).  value = 2*N*Ho*Wo*C_out*R*S*C_in /
 step time, in TFLOP/s.  Inputs are resident in HBM: each step uses the next
-of several identical buffer sets whose total size (>= 640 MB) exceeds the
-256 MB Infinity Cache and the L2s, so no step finds its operands in cache.
+of several identical buffer sets whose total size (>= 640 MB, at most 64
+sets) exceeds the 256 MB Infinity Cache and the L2s, so no step finds its
+operands in cache.
 
 Also reported on the same line:
   roofline      the GEMM kernel's algorithmic bytes (or FLOPs) per launch over
-                its mean duration from HIP events, against the MI355X peak;
+                its mean duration from HIP events around back-to-back launches
+                (queued behind a spin kernel), against the MI355X peak;
   cpu_baseline  the fp64 oracle timed on this host's cores on the same
                 workload (the full batch);
   shapes        the same measurement for each of the five named workloads.
@@ -36,6 +40,8 @@ PEAK = {"bf16_tflops": 2516.6, "fp16_tflops": 2516.6, "fp8_tflops": 5033.2,
         "hbm_gbs": 8000.0}
 RIDGE_BF16 = PEAK["bf16_tflops"] * 1e12 / (PEAK["hbm_gbs"] * 1e9)
 ROTATE_BYTES = 640 << 20   # default; --rotate-mib 0 = one set (warm caches, labelled)
+MAX_SETS = 64
+STEPS_PER_GRAPH = 5        # steps captured in one HIP graph (one replay = 5 steps)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "igemm_fwd_resnet_3x3_64c_n32_traffic.txt")
 
 
@@ -80,7 +86,9 @@ class Bufsets:
         nk_bytes = igc.conv2d_workspace_bytes(w.shape, self.fcrs, w.dtype)
         per_set = (x.numel() * x.element_size() + w.numel() * w.element_size() +
                    nk_bytes + n * ho * wo * f * 2 * (2 if src is not None else 1))
-        self.nsets = max(1, -(-rotate_bytes // per_set))
+        # enough sets to cover rotate_bytes, at most MAX_SETS (tiny layers
+        # fit in the caches whatever the count)
+        self.nsets = min(MAX_SETS, max(1, -(-rotate_bytes // per_set)))
         xd, wd = x.to(dev), w.to(dev)
         sd = None if src is None else src.to(dev)
         self.sets = []
@@ -92,24 +100,96 @@ class Bufsets:
                 src=None if sd is None else sd.clone()))
         torch.cuda.synchronize()
 
-    def step(self, igc, i, ev=None):
+    def step(self, igc, i):
+        """One step on set i: the filter transpose, then the GEMM kernel."""
         b = self.sets[i % self.nsets]
-        sp = self.spec
         rc = igc.conv2d_filter_to_nk(b["w"], b["nk"], filter_is_fcrs=self.fcrs)
         if rc != 1:
             raise RuntimeError(f"conv2d_filter_to_nk returned {rc}")
-        if ev is not None:
-            ev[0].record()
+        self.fwd_only(igc, i)
+
+    def fwd_only(self, igc, i):
+        """The GEMM kernel alone on set i (its NK matrix already made)."""
+        b = self.sets[i % self.nsets]
+        sp = self.spec
         rc = igc.conv2d_fwd_nk(b["x"], b["nk"], b["w"].shape, b["y"], filter_is_fcrs=self.fcrs,
                                stride=sp["stride"], padding=sp["pad"], source=b["src"],
                                beta=sp["beta"])
-        if ev is not None:
-            ev[1].record()
         if rc != 1:
             raise RuntimeError(f"conv2d_fwd_nk returned {rc}")
 
+    def capture(self, torch, igc, per_graph):
+        """HIP graphs of `per_graph` consecutive steps each (graph g runs the
+        steps on sets g*per_graph + u, u < per_graph, modulo the set count),
+        so the timed loop is not paced by host-side launch overhead.  Every
+        replay is checked bit for bit against the eager steps' outputs, with
+        eager work and synchronizations between the replays."""
+        self.per_graph = per_graph
+        ngraphs = -(-self.nsets // per_graph)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(self.nsets):
+                self.step(igc, i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        ref = []
+        for i in range(self.nsets):
+            self.step(igc, i)
+            torch.cuda.synchronize()
+            ref.append(self.sets[i]["y"].clone())
+        self.graphs = []
+        for g in range(ngraphs):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for u in range(per_graph):
+                    self.step(igc, g * per_graph + u)
+            self.graphs.append(graph)
+        torch.cuda.synchronize()
+        for rep in range(2):
+            for g in range(ngraphs):
+                sets = sorted({(g * per_graph + u) % self.nsets for u in range(per_graph)})
+                for i in sets:
+                    self.sets[i]["y"].zero_()
+                torch.cuda.synchronize()
+                self.graphs[g].replay()
+                torch.cuda.synchronize()
+                for i in sets:
+                    if not torch.equal(self.sets[i]["y"].view(torch.int16),
+                                       ref[i].view(torch.int16)):
+                        raise RuntimeError(f"graph {g} replay {rep}: set {i} differs from "
+                                           "the eager step")
+                self.step(igc, g)   # eager work between replays
+                torch.cuda.synchronize()
+
+    def replay(self, r):
+        """Replay r runs steps r*per_graph .. r*per_graph + per_graph - 1."""
+        self.graphs[r % len(self.graphs)].replay()
+
+
+def kernel_times(torch, igc, bufs, launches):
+    """Mean duration of conv2d_fwd_nk from HIP events on the launch stream
+    around `launches` back-to-back launches (rotating sets).  A spin kernel
+    holds the stream while the host enqueues them, so the GPU never waits on
+    the host inside the bracket (host-side launch latency would otherwise
+    count as kernel time); no event sits between the launches."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * (0.002 + 60e-6 * launches)))   # ~2 ms + 60 us per launch
+    e0.record(stream)
+    for i in range(launches):
+        bufs.fwd_only(igc, i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / launches
+
 
 def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES):
+    """Timed loop: `steps` steps as replays of the captured step graphs,
+    bracketed by synchronizations, after `warmup` eager steps and one
+    untimed round of replays; then the GEMM kernel's own duration from events
+    around `steps` back-to-back launches."""
     import datagen
 
     spec, x, w, src = datagen.make_workload(name)
@@ -117,24 +197,26 @@ def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES):
     for i in range(warmup):
         bufs.step(igc, i)
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+    per_graph = STEPS_PER_GRAPH if steps % STEPS_PER_GRAPH == 0 else 1
+    bufs.capture(torch, igc, per_graph)
+    for r in range(len(bufs.graphs)):
+        bufs.replay(r)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        bufs.step(igc, warmup + i, events[i])
+    for r in range(steps // per_graph):
+        bufs.replay(r)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kern_ms = sorted(e0.elapsed_time(e1) for e0, e1 in events)
+    kern_ms = kernel_times(torch, igc, bufs, steps)
     flops, nbytes = _algorithmic(spec)
     ms_step = (t1 - t0) * 1e3 / steps
-    kmean = sum(kern_ms) / len(kern_ms)
     bound, peak_t = _bound(spec, flops, nbytes)
     res = dict(workload=name, dtype=spec["dtype"], ms_per_step=ms_step,
                step_tflops=flops / (ms_step * 1e-3) / 1e12,
-               kernel_us_mean=kmean * 1e3, kernel_us_median=kern_ms[len(kern_ms) // 2] * 1e3,
-               kernel_tflops=flops / (kmean * 1e-3) / 1e12,
-               kernel_gbs=nbytes / (kmean * 1e-3) / 1e9, flops=flops, alg_bytes=nbytes,
-               bound=bound, rotating_sets=bufs.nsets)
+               kernel_us_mean=kern_ms * 1e3,
+               kernel_tflops=flops / (kern_ms * 1e-3) / 1e12,
+               kernel_gbs=nbytes / (kern_ms * 1e-3) / 1e9, flops=flops, alg_bytes=nbytes,
+               bound=bound, rotating_sets=bufs.nsets, steps_per_graph=per_graph)
     res["frac_mfma"] = res["kernel_tflops"] / peak_t
     res["frac_hbm"] = res["kernel_gbs"] / PEAK["hbm_gbs"]
     del bufs
@@ -245,7 +327,8 @@ def main():
     if not args.no_shapes:
         import datagen
         for name in datagen.WORKLOAD_ORDER:
-            r, _, _, _ = measure(torch, igc, name, max(10, args.steps // 2), args.warmup, rotate)
+            r, _, _, _ = measure(torch, igc, name, max(10, args.steps // 2 // 5 * 5), args.warmup,
+                                 rotate)
             shapes[name] = {k: (round(v, 4) if isinstance(v, float) else v)
                             for k, v in r.items() if k not in ("flops", "alg_bytes")}
             print(f"# {name}: step {r['ms_per_step'] * 1e3:.1f} us, kernel "
