@@ -895,9 +895,66 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         }
         if (q < NB) block(IntC<0>{});
     }
+    constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
+    const int th_n = min(a.TH, a.Ho - oh0);
+    const int tw_n = min(a.TW, a.Wo - ow0);
+    if ((a.F & 7) == 0) {
+        // ---- epilogue straight from the accumulators.  Lane l holds pixel
+        // (l & 31) and channels 8g + 4h + 0..3 (h = l >> 5) of each 32-channel
+        // block; swapping groups 2k and 2k+1 across the wave halves
+        // (v_permlane32_swap) leaves the lower half with all 8 channels of
+        // group 2k and the upper half with group 2k+1, so every lane stores
+        // 16 contiguous bytes and a store instruction writes 32 pixels x 32
+        // contiguous bytes.  No LDS, no barrier.
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            const int p = (wave + BAND_WAVES * t) * 32 + frag_row;
+            const int th = p / a.TW, tw = p - (p / a.TW) * a.TW;
+            const bool pix_ok = (p < P) & (th < th_n) & (tw < tw_n);
+            const int64_t obase = ((int64_t)(n * a.Ho + oh0 + th) * a.Wo + ow0 + tw) * a.F;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    float v[8];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        // copy the elements out first: a bit cast applied to
+                        // a vector subscript reads element 0
+                        const float lo = acc[i][t][8 * k + j];
+                        const float hi = acc[i][t][8 * k + 4 + j];
+                        const auto r = __builtin_amdgcn_permlane32_swap(
+                            __builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi),
+                            false, false);
+                        const unsigned r0 = r[0], r1 = r[1];
+                        v[j] = __builtin_bit_cast(float, r0);
+                        v[4 + j] = __builtin_bit_cast(float, r1);
+                    }
+                    const int co = i * 32 + 8 * (2 * k + half);
+                    if (pix_ok & (co < a.F)) {
+                        if constexpr (RESID) {
+                            const i32x4 sv = *reinterpret_cast<const i32x4*>(a.src + obase + co);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const uint16_t hb = (uint16_t)((unsigned)sv[e >> 1] >> (16 * (e & 1)));
+                                v[e] = __builtin_fmaf(a.beta, out_to_f32(hb, ODT), v[e]);
+                            }
+                        }
+                        i32x4 ov;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            ov[e] = (int)((unsigned)f32_to_out(v[2 * e], ODT) |
+                                          ((unsigned)f32_to_out(v[2 * e + 1], ODT) << 16));
+                        *reinterpret_cast<i32x4*>(a.y + obase + co) = ov;
+                    }
+                }
+        }
+        return;
+    }
     __syncthreads();  // patch and filter no longer read
 
-    // ---- epilogue: fp32 tile -> LDS [P][spitch floats] -> coalesced stores
+    // ---- epilogue for C_out not a multiple of 8: fp32 tile -> LDS
+    // [P][spitch floats] -> coalesced stores
     float* stage = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
@@ -914,34 +971,8 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         }
     }
     __syncthreads();
-    constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
-    const int th_n = min(a.TH, a.Ho - oh0);
-    const int tw_n = min(a.TW, a.Wo - ow0);
     const float inv_twn = 1.0f / (float)tw_n;
-    if ((a.F & 7) == 0) {
-        const int c8n = a.F / 8;
-        const float inv_c8n = 1.0f / (float)c8n;
-        const int items = th_n * tw_n * c8n;
-        for (int it = tid; it < items; it += NT) {
-            const int q = small_div(it, c8n, inv_c8n), c8 = it - q * c8n;
-            const int th = small_div(q, tw_n, inv_twn), tw = q - th * tw_n;
-            const float* sp = stage + (th * a.TW + tw) * a.spitch + c8 * 8;
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 4);
-            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const int64_t o = ((int64_t)(n * a.Ho + oh0 + th) * a.Wo + ow0 + tw) * a.F + c8 * 8;
-            if constexpr (RESID) {
-                const i32x4 sv = *reinterpret_cast<const i32x4*>(a.src + o);
-                const uint16_t* sh = reinterpret_cast<const uint16_t*>(&sv);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(a.beta, out_to_f32(sh[e], ODT), v[e]);
-            }
-            union { i32x4 v; uint16_t h[8]; } ov;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ov.h[e] = f32_to_out(v[e], ODT);
-            *reinterpret_cast<i32x4*>(a.y + o) = ov.v;
-        }
-    } else {
+    {
         const int items = th_n * tw_n * a.F;
         const float inv_f = 1.0f / (float)a.F;
         for (int it = tid; it < items; it += NT) {
