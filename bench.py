@@ -185,11 +185,11 @@ def kernel_times(torch, igc, bufs, launches):
     return e0.elapsed_time(e1) / launches
 
 
-def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES):
-    """Timed loop: `steps` steps as replays of the captured step graphs,
-    bracketed by synchronizations, after `warmup` eager steps and one
-    untimed round of replays; then the GEMM kernel's own duration from events
-    around `steps` back-to-back launches."""
+def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES, graphs=True):
+    """Timed loop: `steps` steps as replays of the captured step graphs
+    (eager steps with graphs=False), bracketed by synchronizations, after
+    `warmup` eager steps and one untimed round of replays; then the GEMM
+    kernel's own duration from events around `steps` back-to-back launches."""
     import datagen
 
     spec, x, w, src = datagen.make_workload(name)
@@ -198,13 +198,18 @@ def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES):
         bufs.step(igc, i)
     torch.cuda.synchronize()
     per_graph = STEPS_PER_GRAPH if steps % STEPS_PER_GRAPH == 0 else 1
-    bufs.capture(torch, igc, per_graph)
-    for r in range(len(bufs.graphs)):
-        bufs.replay(r)
-    torch.cuda.synchronize()
+    if graphs:
+        bufs.capture(torch, igc, per_graph)
+        for r in range(len(bufs.graphs)):
+            bufs.replay(r)
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for r in range(steps // per_graph):
-        bufs.replay(r)
+    if graphs:
+        for r in range(steps // per_graph):
+            bufs.replay(r)
+    else:
+        for i in range(steps):
+            bufs.step(igc, warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern_ms = kernel_times(torch, igc, bufs, steps)
@@ -216,7 +221,8 @@ def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES):
                kernel_us_mean=kern_ms * 1e3,
                kernel_tflops=flops / (kern_ms * 1e-3) / 1e12,
                kernel_gbs=nbytes / (kern_ms * 1e-3) / 1e9, flops=flops, alg_bytes=nbytes,
-               bound=bound, rotating_sets=bufs.nsets, steps_per_graph=per_graph)
+               bound=bound, rotating_sets=bufs.nsets,
+               steps_per_graph=per_graph if graphs else 0)
     res["frac_mfma"] = res["kernel_tflops"] / peak_t
     res["frac_hbm"] = res["kernel_gbs"] / PEAK["hbm_gbs"]
     del bufs
@@ -271,6 +277,9 @@ def main():
     ap.add_argument("--rotate-mib", type=int, default=ROTATE_BYTES >> 20,
                     help="total size of the rotated buffer sets; 0 keeps one set, so "
                          "operands stay in cache (warm figures, labelled as such)")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="time eager steps instead of graph replays (host-paced; used for "
+                         "counter runs, where every launch then works on cold buffers)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 3 times "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -306,7 +315,7 @@ def main():
 
     if args.only:
         res, _, _, _ = measure(torch, igc, args.only, args.steps, args.warmup,
-                               args.rotate_mib << 20)
+                               args.rotate_mib << 20, graphs=not args.no_graphs)
         res["caches"] = "cold" if args.rotate_mib else "warm"
         print(json.dumps(res), flush=True)
         return
