@@ -240,7 +240,7 @@ constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 constexpr int kNumCUs = 256;
 
 struct BandPlan {
-    int TH, TW, PH, PW, TN, fpitch, ppitch, spitch, lds, tiles_h, tiles_w;
+    int TH, TW, PH, PW, TN, fpitch, ppitch, prow, spitch, lds, tiles_h, tiles_w;
     int64_t tiles;
 };
 
@@ -289,8 +289,12 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
             const int tn = band_tn((NB + BAND_WAVES - 1) / BAND_WAVES);
             if (tn == 0) continue;
             const int64_t ph = (th - 1) * s.st + s.R, pw = (tw - 1) * s.st + s.S;
+            // row pad: (prow - tw * ppitch) % 128 == 0, so a fragment read
+            // whose pixels wrap to the next tile row keeps hitting distinct
+            // 16-byte bank groups
+            const int64_t prow = pw * ppitch + (((tw - pw) * ppitch) % 128 + 128) % 128;
             // filter and patch are each staged in whole 1 KB blocks
-            const int64_t patch = (ph * pw * ppitch + 1023) / 1024 * 1024;
+            const int64_t patch = (ph * prow + 1023) / 1024 * 1024;
             int64_t lds = (fbytes + 1023) / 1024 * 1024 + patch;
             const int64_t stage = P * spitch * 4;
             if (stage > lds) lds = stage;
@@ -307,7 +311,8 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
                 best = cost;
                 found = true;
                 *out = BandPlan{(int)th, (int)tw, (int)ph, (int)pw, tn, (int)fpitch, (int)ppitch,
-                                (int)spitch, (int)lds, (int)th_tiles, (int)tw_tiles, tiles};
+                                (int)prow, (int)spitch, (int)lds, (int)th_tiles, (int)tw_tiles,
+                                tiles};
             }
         }
     }
@@ -326,7 +331,7 @@ hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     if (attr_err != hipSuccess) return attr_err;
     a.TH = bp.TH; a.TW = bp.TW; a.PH = bp.PH; a.PW = bp.PW;
     a.tiles_h = bp.tiles_h; a.tiles_w = bp.tiles_w;
-    a.fpitch = bp.fpitch; a.ppitch = bp.ppitch; a.spitch = bp.spitch;
+    a.fpitch = bp.fpitch; a.ppitch = bp.ppitch; a.prow = bp.prow; a.spitch = bp.spitch;
     a.patch_off = (TM * 32 * bp.fpitch + 1023) / 1024 * 1024;
     {
         const int E = DtTraits<DT>::E;

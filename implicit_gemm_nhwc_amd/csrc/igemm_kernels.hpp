@@ -63,6 +63,7 @@ struct ConvArgs {
     int tiles_h, tiles_w;  // tiles per image along Ho / Wo
     int fpitch;            // LDS bytes per filter row
     int ppitch;            // LDS bytes per patch pixel (all C_in channels + 16)
+    int prow;              // LDS bytes per patch row (PW pixels + row pad)
     int patch_off;         // LDS byte offset of the patch
     int spitch;            // LDS floats per staged output pixel (epilogue)
     int cpp_log2;          // log2(16-byte chunks per input pixel)
@@ -740,15 +741,18 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     const int lg = a.cpp_log2;   // log2(chunks per input pixel)
 
     // ---- phase A: filter rows [TM*32][fpitch] and the input patch
-    // [PH][PW][ppitch] into LDS with direct-to-LDS buffer loads: no register
-    // round trip and no LDS-write instructions.  Each wave instruction fills
-    // one contiguous 1 KB block (lane t -> 16-byte slot t), so every lane
-    // picks the source chunk that belongs at its slot:
+    // [PH][prow bytes: PW pixels of ppitch bytes, then a row pad] into LDS
+    // with direct-to-LDS buffer loads: no register round trip and no
+    // LDS-write instructions.  Each wave instruction fills one contiguous
+    // 1 KB block (lane t -> 16-byte slot t), so every lane picks the source
+    // chunk that belongs at its slot:
     //  * filter: NK rows already carry their 16-byte zero pad, so slot s is
     //    NK byte 16 s (rows >= C_out are past the range: zero);
-    //  * patch: slot s is chunk s % (cpp+1) of patch pixel s / (cpp+1); the
-    //    last slot of each pixel is its pad, and padding pixels read out of
-    //    range (zero).
+    //  * patch: slot s is in patch row s / rs (rs = prow / 16 slots); within
+    //    the row, chunk r % (cpp+1) of pixel r / (cpp+1) for r = s % rs; the
+    //    last slot of each pixel, the row pad and padding pixels read out of
+    //    range (zero).  The row pad keeps a fragment read whose 32 pixels
+    //    wrap to the next tile row free of bank conflicts.
     // All loads go out back to back, then one wait.
     {
         const uint32_t fvalid = (uint32_t)(a.F * a.fpitch);
@@ -762,33 +766,30 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         }
         const int cpp = 1 << lg;                      // data chunks per input pixel
         const int spp = cpp + 1;                      // LDS slots per patch pixel
-        const int pslots = a.PH * a.PW * spp;
-        const int pblocks = (pslots + 63) >> 6;
+        const float inv_spp = 1.0f / (float)spp;
+        const int rs = a.prow >> 4;                   // LDS slots per patch row
+        const int pblocks = (a.PH * rs + 63) >> 6;
         const int64_t img = (int64_t)a.H * a.W * cbytes;
         const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (int64_t)n * img, (uint32_t)img);
         uint8_t* patch = lds + a.patch_off;
-        // slot of this lane in block `wave`, decomposed; advanced by 256 slots
-        // (one block per wave) per instruction with add-and-carry
-        int sl = wave * 64 + lane;
-        int pix = sl / spp, pos = sl - (sl / spp) * spp;
-        int ph = pix / a.PW, pw = pix - (pix / a.PW) * a.PW;
-        const int dpix = (BAND_WAVES * 64) / spp, dpos = (BAND_WAVES * 64) % spp;
-        const int dph = dpix / a.PW, dpw = dpix % a.PW;
+        // slot of this lane in block `wave` as (row, slot in row); advanced
+        // by 256 slots (one block per wave) per instruction with add-and-carry
+        const int sl = wave * 64 + lane;
+        int ph = sl / rs, rem = sl - (sl / rs) * rs;
+        const int dph = (BAND_WAVES * 64) / rs, drem = (BAND_WAVES * 64) % rs;
         for (int b = wave; b < pblocks; b += BAND_WAVES) {
+            const int pw = small_div(rem, spp, inv_spp), pos = rem - pw * spp;
             const int ih = ih0 + ph, iw = iw0 + pw;
-            const bool ok = (pos < cpp) & (ph < a.PH) & ((unsigned)ih < (unsigned)a.H) &
-                            ((unsigned)iw < (unsigned)a.W);
+            const bool ok = (pos < cpp) & (pw < a.PW) & (ph < a.PH) &
+                            ((unsigned)ih < (unsigned)a.H) & ((unsigned)iw < (unsigned)a.W);
             const uint32_t off = (uint32_t)((ih * a.W + iw) * cbytes + pos * 16);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xrs, (__attribute__((address_space(3))) void*)(patch + b * 1024), 16,
                 off | ((uint32_t)!ok << 31), 0, 0, 0);
-            pos += dpos;
-            const int pcar = pos >= spp ? 1 : 0;
-            pos -= pcar ? spp : 0;
-            pw += dpw + pcar;
-            const int wcar = pw >= a.PW ? 1 : 0;
-            pw -= wcar ? a.PW : 0;
-            ph += dph + wcar;
+            rem += drem;
+            const int car = rem >= rs ? 1 : 0;
+            rem -= car ? rs : 0;
+            ph += dph + car;
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -808,7 +809,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         const int p = (wave + BAND_WAVES * t) * 32 + frag_row;
         const int tp = p / a.TW, tq = p - tp * a.TW;
         pb[t] = a.patch_off + half * 16 * FR +
-                ((p < P) ? (tp * a.stride * a.PW + tq * a.stride) * a.ppitch : 0);
+                ((p < P) ? tp * a.stride * a.prow + tq * a.stride * a.ppitch : 0);
     }
     int fr_off[TM];
 #pragma unroll
@@ -830,7 +831,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             w_b = 0;
             if (++w_s == a.S) { w_s = 0; if (++w_r == a.R) w_r = 0; }
         }
-        pbase = (w_r * a.PW + w_s) * a.ppitch + w_b * U * KSB;
+        pbase = w_r * a.prow + w_s * a.ppitch + w_b * U * KSB;
         fbase = (w_r * a.S + w_s) * cbytes + w_b * U * KSB;
     };
     i32x4 fa[2][TM][FR], fb[2][TN][FR];
