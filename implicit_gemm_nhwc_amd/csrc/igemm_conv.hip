@@ -369,27 +369,6 @@ hipError_t launch_band_dt(const ConvArgs& a, const BandPlan& bp, hipStream_t str
     return launch_band_tm<DT, 2, RESID>(a, bp, stream);
 }
 
-// ---- wide-layer tiled kernel ----------------------------------------------
-template <int DT, int TM, int TN, int WCO, int WPX, bool RESID, bool TAPK, bool PIPE2>
-hipError_t launch_tiled(ConvArgs a, hipStream_t stream) {
-    constexpr int BCO = WCO * TM * 32, BPX = WPX * TN * 32;
-    constexpr size_t lds = 2 * (size_t)(BCO + BPX) * TILE_RP;
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    auto kern = igemm_fwd_tiled_kernel<DT, TM, TN, WCO, WPX, RESID, TAPK, PIPE2>;
-    std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    });
-    if (attr_err != hipSuccess) return attr_err;
-    a.px_tiles = (a.M + BPX - 1) / BPX;
-    a.co_tiles = (a.F + BCO - 1) / BCO;
-    const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WCO * WPX * 64), lds, stream, a);
-    return hipGetLastError();
-}
-
 // ---- wide-layer kernel with direct-to-LDS staging ---------------------------
 template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK>
 hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
@@ -435,25 +414,9 @@ hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
                   : launch_wide<DT, 2, 2, 2, 2, 128, 4, RESID, false>(a, stream);
 }
 
-// Tile choice for C_out > 64, four waves (one per SIMD).  256 x 256 tiles
-// (128 x 128 per wave, 256 accumulator registers: LDS traffic ~11 bytes per
-// kFLOP) whenever that still gives a tile per CU; else 256 x 128 (128 x 64
-// per wave, loads two k-tiles ahead); 128 x 128 for C_out <= 128.
-template <int DT, bool RESID, bool TAPK>
-hipError_t launch_tiled_dt(const ConvArgs& a, hipStream_t stream) {
-    const int64_t co_tiles256 = (a.F + 255) / 256;
-    const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
-    if (a.F > 128) {
-        if (px_tiles256 * co_tiles256 >= kNumCUs)
-            return launch_tiled<DT, 4, 4, 2, 2, RESID, TAPK, false>(a, stream);  // 256 x 256
-        return launch_tiled<DT, 4, 2, 2, 2, RESID, TAPK, true>(a, stream);       // 256 x 128
-    }
-    return launch_tiled<DT, 2, 2, 2, 2, RESID, TAPK, true>(a, stream);           // 128 x 128
-}
-
-// The tiled kernel bases each tile's pixel buffer at its first image; the
+// The wide kernel bases each tile's pixel buffer at its first image; the
 // images one tile's 256 pixels can touch must fit the 2^31-byte range.
-bool tiled_ok(const Shape& s, int32_t dtype) {
+bool wide_ok(const Shape& s, int32_t dtype) {
     if (s.F <= 64) return false;
     const int64_t howo = s.Ho * s.Wo;
     int64_t imgs = 255 / howo + 2;
@@ -461,12 +424,6 @@ bool tiled_ok(const Shape& s, int32_t dtype) {
     return imgs * s.H * s.W * s.C * elem_bytes(dtype) < ((int64_t)1 << 31);
 }
 
-template <int DT, bool RESID>
-hipError_t launch_tiled_tap(const ConvArgs& a, hipStream_t stream) {
-    constexpr int KT = KT_BYTES / DtTraits<DT>::E;
-    (void)KT;
-    return launch_wide_dt<DT, RESID>(a, stream);
-}
 
 template <int DT, bool RESID>
 hipError_t launch_dt(const ConvArgs& a, hipStream_t stream) {
@@ -507,17 +464,17 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
                              : launch_band_dt<DT_FP8, false>(a, bp, stream);
         }
     }
-    if (tiled_ok(s, dtype)) {
+    if (wide_ok(s, dtype)) {
         switch (dtype) {
             case IGC_DTYPE_BF16:
-                return resid ? launch_tiled_tap<DT_BF16, true>(a, stream)
-                             : launch_tiled_tap<DT_BF16, false>(a, stream);
+                return resid ? launch_wide_dt<DT_BF16, true>(a, stream)
+                             : launch_wide_dt<DT_BF16, false>(a, stream);
             case IGC_DTYPE_FP16:
-                return resid ? launch_tiled_tap<DT_FP16, true>(a, stream)
-                             : launch_tiled_tap<DT_FP16, false>(a, stream);
+                return resid ? launch_wide_dt<DT_FP16, true>(a, stream)
+                             : launch_wide_dt<DT_FP16, false>(a, stream);
             default:
-                return resid ? launch_tiled_tap<DT_FP8, true>(a, stream)
-                             : launch_tiled_tap<DT_FP8, false>(a, stream);
+                return resid ? launch_wide_dt<DT_FP8, true>(a, stream)
+                             : launch_wide_dt<DT_FP8, false>(a, stream);
         }
     }
     if (resident_ok(s, dtype)) {

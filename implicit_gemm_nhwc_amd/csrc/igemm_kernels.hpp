@@ -604,7 +604,7 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
         }
     }
 
-    // ---- epilogue (same lane mapping as the tiled kernel)
+    // ---- epilogue: lane owns pixel (lane & 15) of each 16-pixel block
     constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
     const bool vec_ok = (a.F & 3) == 0;
 #pragma unroll
@@ -988,286 +988,15 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
 }
 
 // ---------------------------------------------------------------------------
-// Wide-layer implicit GEMM: BCO x BPX workgroup tiles (BCO = WCO*TM*32 output
-// channels, BPX = WPX*TN*32 output pixels), WCO x WPX waves, each computing
-// TM x TN blocks of 32x32 with 32x32 MFMAs.  K streams in 128-byte k-tiles through a double-buffered
-// LDS stage whose rows are padded to 144 bytes (conflict-free fragment
-// reads); the next k-tile's 16-byte buffer loads are issued before the
-// current one multiplies.  Gather masks are buffer range checks: padding,
-// m >= M, k >= K and co >= C_out lanes load zero.  When C_in is a whole
-// number of k-tiles (TAPK) every k-tile lies inside one filter tap, so the
-// tap walk is uniform scalar work.
-constexpr int TILE_RP = KT_BYTES + 16;  // LDS bytes per staged row
-
-template <int DT, int TM, int TN, int WCO, int WPX, bool RESID, bool TAPK, bool PIPE2>
-__global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_tiled_kernel(ConvArgs a) {
-    constexpr int E = DtTraits<DT>::E;
-    constexpr int VEC = 16 / E;
-    constexpr int KT = KT_BYTES / E;
-    constexpr int NT = WCO * WPX * 64;                // threads
-    constexpr int RPP = NT / 8;                       // rows per staging pass
-    constexpr int BCO = WCO * TM * 32;
-    constexpr int BPX = WPX * TN * 32;
-    constexpr int AR = BCO / RPP, BR = BPX / RPP;     // staged rows per thread
-    constexpr int FR = (DT == DT_FP8) ? 2 : 1;        // 16-byte chunks per fragment
-    constexpr int KS = (DT == DT_FP8) ? 2 : 4;        // MFMA steps per k-tile
-    constexpr int STAGE = (BCO + BPX) * TILE_RP;
-    static_assert(BCO % RPP == 0 && BPX % RPP == 0, "whole staging passes");
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wco = wave / WPX, wpx = wave % WPX;
-
-    const int tile = xcd_remap(blockIdx.x, a.px_tiles * a.co_tiles);
-    const int co_tile = tile % a.co_tiles;
-    const int px_tile = tile / a.co_tiles;
-    const int co0 = co_tile * BCO;
-    const int m0 = px_tile * BPX;
-
-    // staging assignment: chunk c of rows lrow + RPP i
-    const int c = tid & 7;
-    const int lrow = tid >> 3;
-
-    // filter rows: NK buffer, rows >= C_out out of range
-    const uint32_t nk_bytes = (uint32_t)(a.F * a.kpitch * E);
-    const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, nk_bytes);
-    uint32_t aoff[AR];
-#pragma unroll
-    for (int i = 0; i < AR; ++i) {
-        const int co = co0 + lrow + RPP * i;
-        aoff[i] = co < a.F ? (uint32_t)(co * a.kpitch * E + c * 16) : OOB_OFFSET;
-    }
-    // pixel rows: the buffer starts at the tile's first image
-    const int howo = a.Ho * a.Wo;
-    const int n0 = m0 / howo;
-    const int64_t img = (int64_t)a.H * a.W * a.C * E;   // bytes per image
-    const int64_t base = (int64_t)n0 * img;
-    const int64_t span = (int64_t)(a.M / howo) * img - base;
-    const __amdgpu_buffer_rsrc_t xrs =
-        make_rsrc(a.x + base, span > (int64_t)OOB_OFFSET ? OOB_OFFSET : (uint32_t)span);
-    int prel[BR], pih[BR], piw[BR];
-#pragma unroll
-    for (int i = 0; i < BR; ++i) {
-        const int m = m0 + lrow + RPP * i;
-        if (m < a.M) {
-            const int n = m / howo;
-            const int rem = m - n * howo;
-            const int oh = rem / a.Wo;
-            const int ow = rem - oh * a.Wo;
-            pih[i] = oh * a.stride - a.pad;
-            piw[i] = ow * a.stride - a.pad;
-            prel[i] = (int)((int64_t)(n - n0) * img + (int64_t)(pih[i] * a.W + piw[i]) * a.C * E);
-        } else {
-            pih[i] = -(1 << 28);
-            piw[i] = 0;
-            prel[i] = 0;
-        }
-    }
-    // k walk: uniform (TAPK) or per thread (this thread's chunk c)
-    int t_ci = 0, t_r = 0, t_s = 0;             // TAPK: tap and first channel of the k-tile
-    int kk = c * VEC, ci = 0, fr = 0, fs = 0;   // general
-    if constexpr (!TAPK) {
-        const int Cdiv = a.C > 0 ? a.C : 1;
-        const int tap = kk / Cdiv;
-        ci = kk - tap * Cdiv;
-        fr = tap / a.S;
-        fs = tap - fr * a.S;
-    }
-
-    // register sets of staged rows.  PIPE2: k-tile kt+1 waits in one set
-    // while k-tile kt+2 loads into the other.  Otherwise (256-accumulator
-    // waves, where registers are scarce) one set: k-tile kt+1 loads while
-    // k-tile kt multiplies and is written to LDS after its MFMAs.
-    constexpr int NSET = PIPE2 ? 2 : 1;
-    i32x4 areg[NSET][AR], breg[NSET][BR];
-    int kt_next = 0;   // next k-tile to load (past the end loads are harmless)
-    auto load_tile = [&](int set) {
-        const int kt = kt_next++;
-#pragma unroll
-        for (int i = 0; i < AR; ++i)
-            areg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(frs, aoff[i] + (uint32_t)(kt * KT_BYTES), 0, 0);
-        if constexpr (TAPK) {
-            const int koff = ((t_r * a.W + t_s) * a.C + t_ci) * E + c * 16;
-#pragma unroll
-            for (int i = 0; i < BR; ++i) {
-                const bool ok = ((unsigned)(pih[i] + t_r) < (unsigned)a.H) &
-                                ((unsigned)(piw[i] + t_s) < (unsigned)a.W);
-                breg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    xrs, (uint32_t)(prel[i] + koff) | ((uint32_t)!ok << 31), 0, 0);
-            }
-            t_ci += KT;
-            const bool wrap = t_ci >= a.C;
-            t_ci = wrap ? 0 : t_ci;
-            t_s += wrap ? 1 : 0;
-            const bool wrap2 = t_s >= a.S;
-            t_s = wrap2 ? 0 : t_s;
-            t_r += wrap2 ? 1 : 0;
-        } else {
-            const bool kin = kk < a.K;
-            const int koff = ((fr * a.W + fs) * a.C + ci) * E;
-#pragma unroll
-            for (int i = 0; i < BR; ++i) {
-                const bool ok = kin & ((unsigned)(pih[i] + fr) < (unsigned)a.H) &
-                                ((unsigned)(piw[i] + fs) < (unsigned)a.W);
-                breg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    xrs, (uint32_t)(prel[i] + koff) | ((uint32_t)!ok << 31), 0, 0);
-            }
-            kk += KT;
-            ci += KT;
-            while (ci >= a.C && a.C > 0) {
-                ci -= a.C;
-                if (++fs == a.S) { fs = 0; ++fr; }
-            }
-        }
-    };
-    // store rows [lo, hi) of a register set (A rows first, then B rows)
-    auto store_rows = [&](int set, int stage, int lo, int hi) {
-        uint8_t* sb = lds + stage * STAGE;
-#pragma unroll
-        for (int i = 0; i < AR + BR; ++i) {
-            if (i < lo || i >= hi) continue;
-            if (i < AR)
-                *reinterpret_cast<i32x4*>(sb + (lrow + RPP * i) * TILE_RP + c * 16) = areg[set][i];
-            else
-                *reinterpret_cast<i32x4*>(sb + (BCO + lrow + RPP * (i - AR)) * TILE_RP + c * 16) =
-                    breg[set][i - AR];
-        }
-    };
-
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-
-    const int frow = lane & 31, half = lane >> 5;
-    const int arow0 = (wco * TM * 32 + frow) * TILE_RP;
-    const int brow0 = (BCO + wpx * TN * 32 + frow) * TILE_RP;
-    i32x4 af[2][TM][FR], bfr[2][TN][FR];
-    auto read_frags = [&](int stage, int ks, int fb) {
-        const uint8_t* sb = lds + stage * STAGE;
-        const int cb = (ks * 2 * FR + half * FR) * 16;   // this lane's chunk(s)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int h = 0; h < FR; ++h)
-                af[fb][i][h] = *reinterpret_cast<const i32x4*>(sb + arow0 + i * 32 * TILE_RP + cb + h * 16);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int h = 0; h < FR; ++h)
-                bfr[fb][j][h] = *reinterpret_cast<const i32x4*>(sb + brow0 + j * 32 * TILE_RP + cb + h * 16);
-    };
-    // One k-tile from LDS stage `cur`, with the rows of register set `set`
-    // written into the other stage between its MFMA steps and the fragments
-    // of step ks+1 read before step ks multiplies.
-    constexpr int SPS = (AR + BR + KS - 1) / KS;   // staged rows written per step
-    auto compute = [&](int cur, int set) {
-        read_frags(cur, 0, 0);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) read_frags(cur, ks + 1, (ks + 1) & 1);
-            if constexpr (PIPE2) store_rows(set, cur ^ 1, ks * SPS, (ks + 1) * SPS);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    acc[i][j] = mfma32<DT>(af[ks & 1][i], bfr[ks & 1][j], acc[i][j]);
-        }
-        if constexpr (!PIPE2) store_rows(set, cur ^ 1, 0, AR + BR);
-    };
-
-    const int nkt = a.ktiles;
-    if constexpr (PIPE2) {
-        // k-tile kt computes from stage kt&1 while k-tile kt+1 (in
-        // registers) is written to the other stage and k-tile kt+2 loads.
-        if (nkt > 0) {
-            load_tile(0);
-            load_tile(1);
-            store_rows(0, 0, 0, AR + BR);
-            __syncthreads();
-            int kt = 0;
-            for (; kt + 2 <= nkt; kt += 2) {
-                load_tile(0);        // k-tile kt+2
-                compute(0, 1);       // k-tile kt; k-tile kt+1 -> stage 1
-                __syncthreads();
-                load_tile(1);        // k-tile kt+3
-                compute(1, 0);       // k-tile kt+1; k-tile kt+2 -> stage 0
-                __syncthreads();
-            }
-            if (kt < nkt) compute(0, 1);
-        }
-    } else {
-        // k-tile kt computes from stage kt&1 while k-tile kt+1 loads into the
-        // one register set; it goes to the other stage after the MFMAs.
-        if (nkt > 0) {
-            load_tile(0);
-            store_rows(0, 0, 0, AR + BR);
-            __syncthreads();
-            int kt = 0;
-            for (; kt + 2 <= nkt; kt += 2) {
-                load_tile(0);        // k-tile kt+1
-                compute(0, 0);       // k-tile kt; then k-tile kt+1 -> stage 1
-                __syncthreads();
-                load_tile(0);        // k-tile kt+2
-                compute(1, 0);       // k-tile kt+1; then k-tile kt+2 -> stage 0
-                __syncthreads();
-            }
-            if (kt < nkt) compute(0, 0);
-        }
-    }
-
-    // ---- epilogue straight from the accumulators: lane owns pixel
-    // (lane & 31) of each 32-pixel block and channels 8g + 4*half + 0..3
-    constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
-    const bool vec_ok = (a.F & 3) == 0;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int m = m0 + wpx * TN * 32 + j * 32 + frow;
-        if (m >= a.M) continue;
-        const int64_t obase = (int64_t)m * a.F;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int co = co0 + wco * TM * 32 + i * 32 + g * 8 + half * 4;
-                if (co >= a.F) continue;
-                float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                              acc[i][j][4 * g + 3]};
-                if (vec_ok) {
-                    if constexpr (RESID) {
-                        const u16x4 sv = *reinterpret_cast<const u16x4*>(a.src + obase + co);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a.beta, out_to_f32(sv[q], ODT), v[q]);
-                    }
-                    u16x4 o;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) o[q] = f32_to_out(v[q], ODT);
-                    *reinterpret_cast<u16x4*>(a.y + obase + co) = o;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        if (co + q < a.F) {
-                            float d = v[q];
-                            if constexpr (RESID) d = __builtin_fmaf(a.beta, out_to_f32(a.src[obase + co + q], ODT), d);
-                            a.y[obase + co + q] = f32_to_out(d, ODT);
-                        }
-                    }
-                }
-            }
-        }
-    }
-}
-
-
-// ---------------------------------------------------------------------------
-// Wide-layer implicit GEMM with direct-to-LDS staging.  Same tiling as the
-// kernel above (BCO x BPX workgroup tiles, WCO x WPX waves of TM x TN 32x32
-// blocks), but the k-tiles reach LDS through buffer-load-to-LDS: no staging
-// registers and no LDS-write instructions in the loop, which matters because
-// LDS writes run at about half the LDS read rate.
+// Wide-layer implicit GEMM (C_out > 64) with direct-to-LDS staging: BCO x BPX
+// workgroup tiles (BCO = WCO*TM*32 output channels, BPX = WPX*TN*32 output
+// pixels), WCO x WPX waves, each computing TM x TN blocks of 32x32 with 32x32
+// MFMAs.  K streams through LDS in k-tiles that reach it by buffer-load-to-LDS:
+// no staging registers and no LDS-write instructions in the loop, which
+// matters because LDS writes run at about half the LDS read rate.  Gather
+// masks are buffer range checks: padding, m >= M, k >= K and co >= C_out lanes
+// load zero.  When C_in is a whole number of k-tiles (TAPK) every k-tile lies
+// inside one filter tap, so the tap walk is uniform scalar work.
 //
 // Stage layout: BCO filter rows then BPX pixel rows of KTB bytes (64 or 128),
 // unpadded.  Chunk d (16 bytes) of row r sits at position d ^ swz(r), with
