@@ -1204,6 +1204,12 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             for (int i = 0; i < TM; ++i) acc[i][j] = mfma32<DT>(af[fb][i], bfr[fb][j], acc[i][j]);
     };
     constexpr int MPG = (TM * TN + TM + TN - 1) / (TM + TN);
+    // last step of a k-tile: the first DMAM MFMAs carry the requests, the
+    // rest the next k-tile's first fragment reads
+    constexpr int DMAM = TM * TN / 2;
+    constexpr int DMAG = (AI + BI + DMAM - 1) / DMAM;                  // requests per MFMA
+    constexpr int VALUG = 6 * DMAG;                                    // their address math
+    constexpr int RDG = ((TM + TN) * FR + TM * TN - DMAM - 1) / (TM * TN - DMAM);   // reads per MFMA
     auto interleave = [&]() {
 #pragma unroll
         for (int g = 0; g < TM + TN; ++g) {
@@ -1228,11 +1234,25 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(WAITN) : "memory");
         __builtin_amdgcn_sched_barrier(0);
-        issue(cur);   // stage `cur` is free in every wave: k-tile kt + NSTAGE
+        const int freed = cur;   // free in every wave now: receives k-tile kt + NSTAGE
         cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+        issue(freed);
         read_frags(cur, 0, (FB0 + KS) & 1);   // past the last k-tile: a harmless read
         mma((FB0 + KS - 1) & 1);
-        interleave();
+        // Spread the requests, then the fragment reads, between this step's
+        // MFMAs so the matrix pipe is not idle while the wave issues them (the
+        // requests write LDS, so they stay ahead of the reads in program order).
+#pragma unroll
+        for (int g = 0; g < DMAM; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x010, DMAG, 0);       // buffer loads to LDS
+            __builtin_amdgcn_sched_group_barrier(0x002, VALUG, 0);      // their address math
+        }
+#pragma unroll
+        for (int g = DMAM; g < TM * TN; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, RDG, 0);        // DS reads
+        }
     };
 
     if (nkt > 0) {
