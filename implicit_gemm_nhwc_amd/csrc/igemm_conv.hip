@@ -289,10 +289,11 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
             const int tn = band_tn((NB + BAND_WAVES - 1) / BAND_WAVES);
             if (tn == 0) continue;
             const int64_t ph = (th - 1) * s.st + s.R, pw = (tw - 1) * s.st + s.S;
-            // row pad: (prow - tw * ppitch) % 128 == 0, so a fragment read
-            // whose pixels wrap to the next tile row keeps hitting distinct
-            // 16-byte bank groups
-            const int64_t prow = pw * ppitch + (((tw - pw) * ppitch) % 128 + 128) % 128;
+            // row pad: (prow - tw * ppitch) % 256 == 0, so the 16 lanes of a
+            // fragment read served together (64 banks, 256 bytes) keep hitting
+            // distinct 16-byte bank groups when their pixels wrap to the next
+            // tile row
+            const int64_t prow = pw * ppitch + (((tw - pw) * ppitch) % 256 + 256) % 256;
             // filter and patch are each staged in whole 1 KB blocks
             const int64_t patch = (ph * prow + 1023) / 1024 * 1024;
             int64_t lds = (fbytes + 1023) / 1024 * 1024 + patch;

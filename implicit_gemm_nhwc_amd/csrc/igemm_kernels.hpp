@@ -1000,9 +1000,9 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
 //
 // Stage layout: BCO filter rows then BPX pixel rows of KTB bytes (64 or 128),
 // unpadded.  Chunk d (16 bytes) of row r sits at position d ^ swz(r), with
-// swz(r) = r & 7 for 128-byte rows and (r >> 1) & 3 for 64-byte rows, so the
-// 8 lanes of a fragment read that share a chunk index land in 8 different
-// 16-byte bank groups.  One wave DMA instruction fills 1 KB = 1024 / KTB
+// swz(r) = (r >> 1) & 7 for 128-byte rows and (r >> 2) & 3 for 64-byte rows
+// (r's 256-byte window), so the 16 lanes of a fragment read served together
+// land in 16 different 16-byte bank groups.  One wave DMA instruction fills 1 KB = 1024 / KTB
 // whole rows (lane t -> position t % CPR of row t / CPR), so each lane
 // fetches the chunk that belongs at its position.
 //
@@ -1049,6 +1049,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
     static_assert(KTB == 64 || KTB == 128, "64- or 128-byte k-tiles");
     static_assert(AI * RPI * NW == BCO && BI * RPI * NW == BPX, "whole DMA rows per wave");
     static_assert(NSTAGE >= 2 && (NSTAGE - 1) * (AI + BI) < 64, "stage count within the wait counter");
+    static_assert(CPR == 4 || (AI % 2 == 0 && BI % 2 == 0), "request parity fixed per instruction index");
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -1062,10 +1063,17 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
     const int co0 = co_tile * BCO;
     const int m0 = px_tile * BPX;
 
-    auto swz = [](int r) { return CPR == 8 ? (r & 7) : ((r >> 1) & 3); };
-    // this lane's DMA slot: row `sub` of each RPI-row group, data chunk `dch`
+    // Bank groups: a 64-lane 16-byte read is served 16 lanes per clock from 64
+    // banks (256 bytes), so the 16 rows a fragment read touches at one chunk
+    // index must land on 16 different 16-byte groups of a 256-byte window:
+    // the position is XORed with the row's index among 256-byte windows.
+    auto swz = [](int r) { return CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
+    // this lane's DMA slot: row `sub` of each RPI-row group; the data chunk
+    // it fetches for request i is dch(i) (for 128-byte rows the row group's
+    // parity, which is i's parity since AI and BI are even, flips bit 2)
     const int sub = lane / CPR;
-    const int dch = (lane % CPR) ^ swz(sub);
+    const int dch0 = (lane % CPR) ^ swz(sub);
+    auto dch = [&](int i) { return CPR == 8 ? dch0 ^ ((i & 1) << 2) : dch0; };
 
     // filter rows: the NK matrix (below 2^31 bytes), rows >= C_out out of range
     const uint32_t nk_bytes = (uint32_t)a.F * (uint32_t)a.kpitch * (uint32_t)E;
@@ -1074,7 +1082,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
         const int co = co0 + (wave * AI + i) * RPI + sub;
-        aoff[i] = co < a.F ? (uint32_t)co * (uint32_t)(a.kpitch * E) + dch * 16 : OOB_OFFSET;
+        aoff[i] = co < a.F ? (uint32_t)co * (uint32_t)(a.kpitch * E) + dch(i) * 16 : OOB_OFFSET;
     }
     // pixel rows: the buffer starts at the tile's first image
     const int howo = a.Ho * a.Wo;
@@ -1096,24 +1104,31 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             pih[i] = oh * a.stride - a.pad;
             piw[i] = ow * a.stride - a.pad;
             // TAPK: the lane's chunk offset rides here; otherwise the per-lane
-            // k walk below already starts at chunk dch
+            // k walks below already start at chunk dch(i)
             prel[i] = (int)((int64_t)(n - n0) * img + (int64_t)(pih[i] * a.W + piw[i]) * a.C * E) +
-                      (TAPK ? dch * 16 : 0);
+                      (TAPK ? dch(i) * 16 : 0);
         } else {
             pih[i] = -(1 << 28);
             piw[i] = 0;
             prel[i] = 0;
         }
     }
-    // k walk: uniform (TAPK) or per lane (this lane's chunk dch)
+    // k walk: uniform (TAPK) or per lane, one per distinct chunk (walk w
+    // follows chunk dch(w))
+    constexpr int NWALK = CPR == 8 ? 2 : 1;
     int t_ci = 0, t_r = 0, t_s = 0;
-    int kk = dch * VEC, ci = 0, fr = 0, fs = 0;
-    if constexpr (!TAPK) {
-        const int Cdiv = a.C > 0 ? a.C : 1;
-        const int tap = kk / Cdiv;
-        ci = kk - tap * Cdiv;
-        fr = tap / a.S;
-        fs = tap - fr * a.S;
+    int kk[NWALK], ci[NWALK], fr[NWALK], fs[NWALK];
+#pragma unroll
+    for (int w = 0; w < NWALK; ++w) {
+        kk[w] = dch(w) * VEC;
+        ci[w] = fr[w] = fs[w] = 0;
+        if constexpr (!TAPK) {
+            const int Cdiv = a.C > 0 ? a.C : 1;
+            const int tap = kk[w] / Cdiv;
+            ci[w] = kk[w] - tap * Cdiv;
+            fr[w] = tap / a.S;
+            fs[w] = tap - fr[w] * a.S;
+        }
     }
     auto dma = [](__amdgpu_buffer_rsrc_t rs, uint8_t* dst, uint32_t off) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1147,20 +1162,29 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             t_s = wrap2 ? 0 : t_s;
             t_r += wrap2 ? 1 : 0;
         } else {
-            const bool kin = kk < a.K;
-            const int koff = ((fr * a.W + fs) * a.C + ci) * E;
+            bool kin[NWALK];
+            int koff[NWALK];
+#pragma unroll
+            for (int w = 0; w < NWALK; ++w) {
+                kin[w] = kk[w] < a.K;
+                koff[w] = ((fr[w] * a.W + fs[w]) * a.C + ci[w]) * E;
+            }
 #pragma unroll
             for (int i = 0; i < BI; ++i) {
-                const bool ok = kin & ((unsigned)(pih[i] + fr) < (unsigned)a.H) &
-                                ((unsigned)(piw[i] + fs) < (unsigned)a.W);
+                const int w = i % NWALK;
+                const bool ok = kin[w] & ((unsigned)(pih[i] + fr[w]) < (unsigned)a.H) &
+                                ((unsigned)(piw[i] + fs[w]) < (unsigned)a.W);
                 dma(xrs, pb + (wave * BI + i) * 1024,
-                    (uint32_t)(prel[i] + koff) | ((uint32_t)!ok << 31) | past);
+                    (uint32_t)(prel[i] + koff[w]) | ((uint32_t)!ok << 31) | past);
             }
-            kk += KTE;
-            ci += KTE;
-            while (ci >= a.C && a.C > 0) {
-                ci -= a.C;
-                if (++fs == a.S) { fs = 0; ++fr; }
+#pragma unroll
+            for (int w = 0; w < NWALK; ++w) {
+                kk[w] += KTE;
+                ci[w] += KTE;
+                while (ci[w] >= a.C && a.C > 0) {
+                    ci[w] -= a.C;
+                    if (++fs[w] == a.S) { fs[w] = 0; ++fr[w]; }
+                }
             }
         }
     };
