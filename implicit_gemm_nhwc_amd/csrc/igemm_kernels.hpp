@@ -753,17 +753,8 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     //    last slot of each pixel, the row pad and padding pixels read out of
     //    range (zero).  The row pad keeps a fragment read whose 32 pixels
     //    wrap to the next tile row free of bank conflicts.
-    // All loads go out back to back, then one wait.
+    // All loads go out back to back (patch first), then one wait.
     {
-        const uint32_t fvalid = (uint32_t)(a.F * a.fpitch);
-        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, fvalid);
-        const int fblocks = (TM * 32 * a.fpitch + 1023) >> 10;
-        for (int b = wave; b < fblocks; b += BAND_WAVES) {
-            const uint32_t off = (uint32_t)(b * 1024 + lane * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                frs, (__attribute__((address_space(3))) void*)(lds + b * 1024), 16,
-                off < fvalid ? off : OOB_OFFSET, 0, 0, 0);
-        }
         const int cpp = 1 << lg;                      // data chunks per input pixel
         const int spp = cpp + 1;                      // LDS slots per patch pixel
         const float inv_spp = 1.0f / (float)spp;
@@ -791,6 +782,17 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             rem -= car ? rs : 0;
             ph += dph + car;
         }
+        // the filter after the patch: its rows come from L2, the patch's
+        // mostly from HBM, so the longer requests go out first
+        const uint32_t fvalid = (uint32_t)(a.F * a.fpitch);
+        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, fvalid);
+        const int fblocks = (TM * 32 * a.fpitch + 1023) >> 10;
+        for (int b = wave; b < fblocks; b += BAND_WAVES) {
+            const uint32_t off = (uint32_t)(b * 1024 + lane * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                frs, (__attribute__((address_space(3))) void*)(lds + b * 1024), 16,
+                off < fvalid ? off : OOB_OFFSET, 0, 0, 0);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
@@ -799,9 +801,9 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     // always TN of them; blocks past the tile read patch pixel 0 and are
     // never stored.  The k-steps run in blocks of U inside one filter tap:
     // per block one scalar base per operand, the U steps at immediate LDS
-    // offsets, and the fragments of the next step read while this one
-    // multiplies (into the other of two register sets, fixed at compile
-    // time: step j of a block uses set j & 1).
+    // offsets, and the fragments of step g + LA read while step g multiplies
+    // (LA = 2 steps ahead when U >= 2, else 1), into NSET = 2 LA register
+    // sets fixed at compile time: step g uses set g % NSET.
     const int P = a.TH * a.TW;
     int pb[TN];
 #pragma unroll
@@ -834,7 +836,9 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         pbase = w_r * a.prow + w_s * a.ppitch + w_b * U * KSB;
         fbase = (w_r * a.S + w_s) * cbytes + w_b * U * KSB;
     };
-    i32x4 fa[2][TM][FR], fb[2][TN][FR];
+    constexpr int LA = U >= 2 ? 2 : 1;   // fragment lookahead in k-steps
+    constexpr int NSET = 2 * LA;
+    i32x4 fa[NSET][TM][FR], fb[NSET][TN][FR];
     auto rd = [&](int set, int pbase, int fbase, int j) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -863,8 +867,8 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);  // MFMAs
         }
     };
-    // one block at bases (pb0, fb0) whose step 0 is in set S0; the next
-    // block's step 0 goes to set (S0 + U) & 1
+    // one block at bases (pb0, fb0) whose step 0 is in set S0; step j + LA
+    // comes from this block or (past its end) from the next one
     int pb0 = 0, fb0 = 0;
     auto block = [&](auto s0c) {
         constexpr int S0 = decltype(s0c)::value;
@@ -872,9 +876,9 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         next_bases(pbn, fbn);
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            if (j + 1 < U) rd((S0 + j + 1) & 1, pb0, fb0, j + 1);
-            else rd((S0 + U) & 1, pbn, fbn, 0);
-            mma((S0 + j) & 1);
+            if (j + LA < U) rd((S0 + j + LA) % NSET, pb0, fb0, j + LA);
+            else rd((S0 + j + LA) % NSET, pbn, fbn, j + LA - U);
+            mma((S0 + j) % NSET);
             interleave();
             // fence: the scheduler must not pull the next step's MFMAs up
             // next to their own reads
@@ -883,16 +887,21 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         pb0 = pbn;
         fb0 = fbn;
     };
-    if (NB > 0) rd(0, 0, 0, 0);
-    if constexpr (U % 2 == 0) {
+    if (NB > 0) {
+#pragma unroll
+        for (int g = 0; g < LA; ++g) rd(g, 0, 0, g);   // LA <= U: all in block 0
+    }
+    if constexpr (U % NSET == 0) {
         for (int q = 0; q < NB; ++q) block(IntC<0>{});
     } else {
-        // sets alternate between blocks: two per iteration with no early
-        // exit, so every accumulator stays in place; an odd last block after
+        // sets rotate by U per block (U = NSET / 2): two blocks per iteration
+        // with no early exit, so every accumulator stays in place; an odd
+        // last block after
+        static_assert(2 * U == NSET, "two blocks cover the set rotation");
         int q = 0;
         for (; q + 2 <= NB; q += 2) {
             block(IntC<0>{});
-            block(IntC<1>{});
+            block(IntC<U>{});
         }
         if (q < NB) block(IntC<0>{});
     }
