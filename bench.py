@@ -236,7 +236,7 @@ def cpu_baseline(spec, x, w, budget_s=10.0):
 
     flops = _algorithmic(spec)[0]
     runs, t_total = 0, 0.0
-    while runs < 1 or (t_total < budget_s and runs < 5):
+    while runs < 1 or (t_total < budget_s and runs < 200):
         t0 = time.perf_counter()
         oracle.conv2d(x, w, filter_is_fcrs=spec["fcrs"], stride=spec["stride"],
                       padding=spec["pad"])
@@ -329,7 +329,12 @@ def main():
         achieved, peak, unit = head["kernel_tflops"], _bound(spec, flops, nbytes)[1], "TFLOP/s"
     roofline = {"bound": head["bound"], "achieved": round(achieved, 2), "peak": peak,
                 "unit": unit, "frac": round(achieved / peak, 4), "traffic": _traffic(head),
-                "kernel": "igemm_fwd_kernel", "kernel_us_mean": round(head["kernel_us_mean"], 3),
+                "kernel": igc.conv2d_fwd_kernel_name(
+                    (spec["N"], spec["H"], spec["W"], spec["C"]), w.shape,
+                    (spec["N"],) + tuple(spec["out_hw"]) + (spec["F"],),
+                    filter_is_fcrs=spec["fcrs"], dtype=w.dtype, stride=spec["stride"],
+                    padding=spec["pad"]),
+                "kernel_us_mean": round(head["kernel_us_mean"], 3),
                 "alg_bytes_per_launch": nbytes, "flops_per_launch": flops}
 
     shapes = {}

@@ -9,8 +9,8 @@ call is declined, these functions say so instead of computing anything.
 
 Names mirror the C entry points:
   conv2d_fwd, conv2d_fwd_check, conv2d_fwd_nk, conv2d_filter_to_nk,
-  conv2d_workspace_bytes, conv2d_nk_row_pitch, conv2d_reason_string,
-  conv2d_abi_version
+  conv2d_fwd_kernel_name, conv2d_workspace_bytes, conv2d_nk_row_pitch,
+  conv2d_reason_string, conv2d_abi_version
 plus conv2d(), which allocates the output and calls conv2d_fwd.
 """
 import ctypes
@@ -66,6 +66,8 @@ def lib():
     L.conv2d_workspace_bytes.argtypes, L.conv2d_workspace_bytes.restype = [i64p, i32, i32], sz
     L.conv2d_nk_row_pitch.argtypes = [i64p, i32, i32]
     L.conv2d_nk_row_pitch.restype = ctypes.c_int64
+    L.conv2d_fwd_kernel_name.argtypes = [i64p, i32, i64p, i64p, i32p, i32p, i32p, i32, i32]
+    L.conv2d_fwd_kernel_name.restype = ctypes.c_char_p
     L.conv2d_filter_to_nk.argtypes = [vp, i32, i64p, i32, vp, sz, vp]
     L.conv2d_filter_to_nk.restype = i32
     _lib = L
@@ -136,6 +138,19 @@ def conv2d_fwd_check(input, filter, output, *, filter_is_fcrs, stride=1, padding
     if isinstance(workspace, torch.Tensor) and not workspace_bytes:
         workspace_bytes = workspace.numel() * workspace.element_size()
     return lib().conv2d_fwd_check(*head, _ptr(workspace), int(workspace_bytes))
+
+
+def conv2d_fwd_kernel_name(in_shape, filt_shape, out_shape, *, filter_is_fcrs, dtype,
+                           stride=1, padding=0, dilation=1, groups=1):
+    """Name of the GEMM kernel the library would launch for these shapes
+    ("none" when the output is empty), or None when the call would be
+    declined.  Host-only; dtype is a torch dtype or a dtype code."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    name = lib().conv2d_fwd_kernel_name(_i64(in_shape), int(bool(filter_is_fcrs)),
+                                        _i64(filt_shape), _i64(out_shape), _pair(stride),
+                                        _pair(dilation), _pair(padding), int(groups),
+                                        int(code))
+    return None if name is None else name.decode()
 
 
 def conv2d_fwd(input, filter, output, *, filter_is_fcrs, stride=1, padding=0, dilation=1,

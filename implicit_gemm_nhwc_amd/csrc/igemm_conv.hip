@@ -436,6 +436,17 @@ hipError_t launch_dt(const ConvArgs& a, hipStream_t stream) {
     return launch_tile<DT, 128, 128, 2, 2, RESID>(a, stream);
 }
 
+// The kernel a problem goes to, in order of preference.
+enum KernelKind { K_NONE, K_BAND, K_WIDE, K_RESIDENT, K_TILED };
+
+KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp) {
+    if (s.M == 0 || s.F == 0) return K_NONE;
+    if (band_plan(s, dtype, bp)) return K_BAND;
+    if (wide_ok(s, dtype)) return K_WIDE;
+    if (resident_ok(s, dtype)) return K_RESIDENT;
+    return K_TILED;
+}
+
 hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
                         float beta, const Shape& s, int32_t dtype, hipStream_t stream) {
     ConvArgs a{};
@@ -449,10 +460,11 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
     a.R = (int)s.R; a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
     a.K = (int)s.K; a.kpitch = (int)s.kpitch; a.M = (int)s.M;
     a.ktiles = (int)(s.kpad / (KT_BYTES / elem_bytes(dtype)));
-    if (s.M == 0 || s.F == 0) return hipSuccess;
     const bool resid = source != nullptr;
     BandPlan bp;
-    if (band_plan(s, dtype, &bp)) {
+    const KernelKind kind = select_kernel(s, dtype, &bp);
+    if (kind == K_NONE) return hipSuccess;
+    if (kind == K_BAND) {
         switch (dtype) {
             case IGC_DTYPE_BF16:
                 return resid ? launch_band_dt<DT_BF16, true>(a, bp, stream)
@@ -465,7 +477,7 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
                              : launch_band_dt<DT_FP8, false>(a, bp, stream);
         }
     }
-    if (wide_ok(s, dtype)) {
+    if (kind == K_WIDE) {
         switch (dtype) {
             case IGC_DTYPE_BF16:
                 return resid ? launch_wide_dt<DT_BF16, true>(a, stream)
@@ -478,7 +490,7 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
                              : launch_wide_dt<DT_FP8, false>(a, stream);
         }
     }
-    if (resident_ok(s, dtype)) {
+    if (kind == K_RESIDENT) {
         switch (dtype) {
             case IGC_DTYPE_BF16:
                 return resid ? launch_resident_dt<DT_BF16, true>(a, stream)
@@ -537,6 +549,24 @@ int32_t conv2d_fwd_check(const void* input, const int64_t in_nhwc[4], const void
     return check_all(input, in_nhwc, filter, 0, filter_is_fcrs, filt_dims, output, out_nhwc,
                      stride, dilation, padding, groups, dtype, source, workspace,
                      workspace_bytes, nullptr);
+}
+
+const char* conv2d_fwd_kernel_name(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                   const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                                   const int32_t stride[2], const int32_t dilation[2],
+                                   const int32_t padding[2], int32_t groups, int32_t dtype) {
+    Shape s;
+    if (check_shapes(in_nhwc, filter_is_fcrs, filt_dims, out_nhwc, stride, dilation, padding,
+                     groups, dtype, &s) != IGC_OK)
+        return nullptr;
+    BandPlan bp;
+    switch (select_kernel(s, dtype, &bp)) {
+        case K_NONE: return "none";
+        case K_BAND: return "igemm_fwd_band_kernel";
+        case K_WIDE: return "igemm_fwd_wide_kernel";
+        case K_RESIDENT: return "igemm_fwd_resident_kernel";
+        default: return "igemm_fwd_kernel";
+    }
 }
 
 size_t conv2d_workspace_bytes(const int64_t filt_dims[4], int32_t filter_is_fcrs, int32_t dtype) {

@@ -131,6 +131,21 @@ int32_t conv2d_fwd(const void* input, const int64_t in_nhwc[4],
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Name of the GEMM kernel conv2d_fwd / conv2d_fwd_nk launch for this problem
+ * (a static string: "igemm_fwd_band_kernel", "igemm_fwd_wide_kernel",
+ * "igemm_fwd_resident_kernel", "igemm_fwd_kernel", or "none" when nothing is
+ * launched because the output is empty), or NULL when the shapes or
+ * parameters would be declined.  Host-only; pointers play no part (their
+ * checks come on top, see conv2d_fwd_check).  A selection rule of this
+ * library (page 1 names only its own 4-wave kernel), reported so that
+ * profiles and measurements can name what ran.
+ */
+const char* conv2d_fwd_kernel_name(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                   const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                                   const int32_t stride[2], const int32_t dilation[2],
+                                   const int32_t padding[2], int32_t groups, int32_t dtype);
+
+/*
  * Bytes of the NK filter matrix: C_out rows of conv2d_nk_row_pitch()
  * elements each.  0 for an invalid dtype or negative dims.
  */

@@ -12,6 +12,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import implicit_gemm_nhwc_amd as igc
 import oracle
@@ -165,3 +166,33 @@ def test_gate_matches_oracle_gate():
         assert (got == 0) == want, (dt, st, dil, pad, groups, h, k, c, f, fcrs, got)
         n += 1
     assert n > 1000
+
+
+def test_kernel_selection():
+    """The kernel each named workload goes to, the declined and empty cases."""
+    import datagen
+    want = {"tiny_3x3_16c": "igemm_fwd_band_kernel",
+            "resnet_3x3_64c_n32": "igemm_fwd_band_kernel",
+            "strided_3x3_s2_128to256_n32": "igemm_fwd_wide_kernel",
+            "fp8_5x5_256c_residual_n16": "igemm_fwd_wide_kernel",
+            "rgb_3x3_128to3_512px": "igemm_fwd_band_kernel"}
+    dts = {"bfloat16": torch.bfloat16, "float16": torch.float16,
+           "float8_e4m3fn": torch.float8_e4m3fn}
+    for name, spec in datagen.WORKLOADS.items():
+        r, s_, c, f = spec["R"], spec["S"], spec["C"], spec["F"]
+        w_shape = (f, c, r, s_) if spec["fcrs"] else (r, s_, c, f)
+        got = igc.conv2d_fwd_kernel_name(
+            (spec["N"], spec["H"], spec["W"], c), w_shape,
+            (spec["N"],) + tuple(spec["out_hw"]) + (f,), filter_is_fcrs=spec["fcrs"],
+            dtype=dts[spec["dtype"]], stride=spec["stride"], padding=spec["pad"])
+        assert got == want[name], (name, got)
+    # declined (stride 3), empty batch, and a wide layer with C_out = 65
+    assert igc.conv2d_fwd_kernel_name((1, 8, 8, 16), (3, 3, 16, 16), (1, 3, 3, 16),
+                                      filter_is_fcrs=False, dtype=torch.bfloat16, stride=3,
+                                      padding=1) is None
+    assert igc.conv2d_fwd_kernel_name((0, 8, 8, 16), (3, 3, 16, 16), (0, 8, 8, 16),
+                                      filter_is_fcrs=False, dtype=torch.bfloat16,
+                                      padding=1) == "none"
+    assert igc.conv2d_fwd_kernel_name((2, 8, 8, 64), (3, 3, 64, 65), (2, 8, 8, 65),
+                                      filter_is_fcrs=False, dtype=torch.float16,
+                                      padding=1) == "igemm_fwd_wide_kernel"
