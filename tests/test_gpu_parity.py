@@ -160,6 +160,57 @@ def test_fp8_workload_fcrs_variant_bitwise():
     assert torch.equal(_bits(a), _bits(b))
 
 
+# ------------------------------------------------------ kernel paths
+# One case per kernel variant the dispatcher can pick, each checked to go
+# where it is meant to (conv2d_fwd_kernel_name) and against the oracle
+# (sampled pixels for the 65536-pixel layers).
+PATH_CASES = [
+    # id, dtype, N, H, W, C, F, R, S, stride, pad, residual, kernel
+    ("wide256_bf16_tap", "bfloat16", 16, 64, 64, 64, 256, 3, 3, 1, 1, False, "wide"),
+    ("wide256_fp16_walk", "float16", 16, 64, 64, 48, 192, 3, 3, 1, 1, True, "wide"),
+    ("wide256_fp8_walk", "float8_e4m3fn", 16, 64, 64, 80, 256, 3, 3, 1, 1, False, "wide"),
+    ("wide256x128_bf16_walk_s2", "bfloat16", 4, 30, 30, 96, 160, 3, 3, 2, 1, True, "wide"),
+    ("wide128_fp8_tap", "float8_e4m3fn", 2, 20, 20, 128, 96, 3, 3, 1, 1, False, "wide"),
+    ("band_u1_bf16", "bfloat16", 2, 20, 20, 16, 48, 3, 3, 1, 1, False, "band"),
+    ("band_u2_fp16_tm1", "float16", 2, 20, 20, 32, 24, 5, 5, 1, 2, True, "band"),
+    ("band_u1_fp8", "float8_e4m3fn", 2, 20, 20, 64, 64, 3, 3, 1, 1, False, "band"),
+    ("band_u2_fp8_resid", "float8_e4m3fn", 2, 20, 20, 128, 32, 3, 3, 1, 1, True, "band"),
+    ("band_u4_bf16_s2", "bfloat16", 2, 28, 28, 64, 64, 3, 3, 2, 1, False, "band"),
+    ("band_lds_epilogue", "bfloat16", 2, 20, 20, 64, 20, 3, 3, 1, 1, True, "band"),
+    ("resident_c48", "bfloat16", 2, 20, 20, 48, 32, 3, 3, 1, 1, False, "resident"),
+    ("fallback_tiled", "bfloat16", 1, 12, 12, 96, 64, 5, 5, 1, 2, True, "tiled"),
+]
+_KERNEL = {"wide": "igemm_fwd_wide_kernel", "band": "igemm_fwd_band_kernel",
+           "resident": "igemm_fwd_resident_kernel", "tiled": "igemm_fwd_kernel"}
+
+
+@pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: c[0])
+def test_kernel_paths(case):
+    cid, dt, n, h, w, c, f, r, s, st, p, resid, kern = case
+    ho, wo = oracle.out_size(h, r, st, p), oracle.out_size(w, s, st, p)
+    _say(f"path {cid}: {dt} N{n} {h}x{w} C{c}->{f} {r}x{s} st{st} p{p} residual={resid}")
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype=dt, fcrs=False,
+                                   x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0) if resid else None,
+                                   out_hw=(ho, wo), seed=zlib.crc32(cid.encode()) % 1000)
+    got_kernel = igc.conv2d_fwd_kernel_name(x.shape, wt.shape, (n, ho, wo, f),
+                                            filter_is_fcrs=False, dtype=x.dtype, stride=st,
+                                            padding=p)
+    assert got_kernel == _KERNEL[kern], (cid, got_kernel)
+    beta = 0.5 if resid else 0.0
+    out = _run(x, wt, fcrs=False, stride=st, pad=p, src=src, beta=beta)
+    if n * ho * wo > 20000:
+        pix = _sample_pixels(n, ho, wo, 512, seed=11)
+        ref = oracle.conv2d_points(x, wt, pix, filter_is_fcrs=False, stride=st, padding=p,
+                                   source=src, beta=beta)
+        assert torch.isfinite(out.float()).all()
+        _assert_close(out.reshape(-1, f)[torch.as_tensor(pix, device=DEV)], ref, TOL[dt], cid)
+    else:
+        ref = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p, source=src,
+                            beta=beta)
+        _assert_close(out, ref, TOL[dt], cid)
+
+
 # ------------------------------------------------------ randomized sweep
 def _sweep_cases():
     rng = np.random.default_rng(2024)
