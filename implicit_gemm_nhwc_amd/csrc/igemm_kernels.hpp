@@ -79,11 +79,12 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return x * q + (x < rem ? x : rem) + j;
 }
 
-// LDS tiles: rows of 128 bytes, chunk c of row r stored at c ^ (r & 7) so
-// that eight consecutive rows read at one logical chunk hit eight
-// different 16-byte bank groups.
+// LDS tiles: rows of 128 bytes, chunk c of row r stored at c ^ ((r >> 1) & 7)
+// so that 16 consecutive rows read at one logical chunk (the 16 lanes a
+// 16-byte LDS read serves per clock from 64 banks) hit 16 different 16-byte
+// bank groups of a 256-byte window.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * KT_BYTES + ((chunk ^ (row & 7)) << 4);
+    return row * KT_BYTES + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 __device__ __forceinline__ uint16_t f32_to_out(float v, int dt) {
