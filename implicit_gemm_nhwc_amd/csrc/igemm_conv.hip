@@ -271,7 +271,11 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
     if (s.H * s.W * s.C * E >= ((int64_t)1 << 31)) return false;
     const int64_t tm = s.F <= 32 ? 1 : 2;
     const int64_t fpitch = s.kpitch * E;
-    const int64_t fbytes = tm * 32 * fpitch;
+    // filter rows kept in LDS: C_out real rows plus one zero row that the
+    // fragment reads of rows >= C_out all point at (up to the TM*32 rows the
+    // MFMAs span)
+    const int64_t frows = s.F + 1 < tm * 32 ? s.F + 1 : tm * 32;
+    const int64_t fbytes = frows * fpitch;
     const int64_t ppitch = s.C * E + 16;
     const int64_t spitch = tm * 32 + 4;
     const int64_t ksteps = s.R * s.S * (s.C * E / ksb);
@@ -333,7 +337,8 @@ hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     a.TH = bp.TH; a.TW = bp.TW; a.PH = bp.PH; a.PW = bp.PW;
     a.tiles_h = bp.tiles_h; a.tiles_w = bp.tiles_w;
     a.fpitch = bp.fpitch; a.ppitch = bp.ppitch; a.prow = bp.prow; a.spitch = bp.spitch;
-    a.patch_off = (TM * 32 * bp.fpitch + 1023) / 1024 * 1024;
+    a.frows = a.F + 1 < TM * 32 ? a.F + 1 : TM * 32;
+    a.patch_off = (a.frows * bp.fpitch + 1023) / 1024 * 1024;
     {
         const int E = DtTraits<DT>::E;
         a.cpp_log2 = log2_exact(a.C * E / 16);

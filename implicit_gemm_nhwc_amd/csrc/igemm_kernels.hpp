@@ -62,6 +62,7 @@ struct ConvArgs {
     int TH, TW, PH, PW;
     int tiles_h, tiles_w;  // tiles per image along Ho / Wo
     int fpitch;            // LDS bytes per filter row
+    int frows;             // filter rows in LDS: min(C_out + 1, TM*32), the last zero
     int ppitch;            // LDS bytes per patch pixel (all C_in channels + 16)
     int prow;              // LDS bytes per patch row (PW pixels + row pad)
     int patch_off;         // LDS byte offset of the patch
@@ -741,14 +742,14 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     const int cbytes = a.C * E;  // bytes of one input pixel
     const int lg = a.cpp_log2;   // log2(chunks per input pixel)
 
-    // ---- phase A: filter rows [TM*32][fpitch] and the input patch
+    // ---- phase A: filter rows [frows][fpitch] and the input patch
     // [PH][prow bytes: PW pixels of ppitch bytes, then a row pad] into LDS
     // with direct-to-LDS buffer loads: no register round trip and no
     // LDS-write instructions.  Each wave instruction fills one contiguous
     // 1 KB block (lane t -> 16-byte slot t), so every lane picks the source
     // chunk that belongs at its slot:
     //  * filter: NK rows already carry their 16-byte zero pad, so slot s is
-    //    NK byte 16 s (rows >= C_out are past the range: zero);
+    //    NK byte 16 s (row C_out, when staged, is past the range: zero);
     //  * patch: slot s is in patch row s / rs (rs = prow / 16 slots); within
     //    the row, chunk r % (cpp+1) of pixel r / (cpp+1) for r = s % rs; the
     //    last slot of each pixel, the row pad and padding pixels read out of
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         // mostly from HBM, so the longer requests go out first
         const uint32_t fvalid = (uint32_t)(a.F * a.fpitch);
         const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, fvalid);
-        const int fblocks = (TM * 32 * a.fpitch + 1023) >> 10;
+        const int fblocks = (a.frows * a.fpitch + 1023) >> 10;
         for (int b = wave; b < fblocks; b += BAND_WAVES) {
             const uint32_t off = (uint32_t)(b * 1024 + lane * 16);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -816,7 +817,8 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     }
     int fr_off[TM];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fr_off[i] = (i * 32 + frag_row) * a.fpitch + half * 16 * FR;
+    for (int i = 0; i < TM; ++i)   // rows >= C_out read the zero row (a broadcast)
+        fr_off[i] = min(i * 32 + frag_row, a.frows - 1) * a.fpitch + half * 16 * FR;
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
