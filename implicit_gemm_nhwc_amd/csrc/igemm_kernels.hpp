@@ -909,6 +909,15 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         if (q < NB) block(IntC<0>{});
     }
     constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
+    if constexpr (DT == DT_FP8) {
+        // The epilogue may read the last MFMA's accumulators first.  For the
+        // scaled fp8 MFMA the wait states the compiler inserts were measured
+        // (in a kernel that did so) to be too few: the last-written result
+        // rows read stale.  Extra independent wait states first.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
     const int th_n = min(a.TH, a.Ho - oh0);
     const int tw_n = min(a.TW, a.Wo - ow0);
     if ((a.F & 7) == 0) {

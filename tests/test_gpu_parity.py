@@ -177,6 +177,8 @@ PATH_CASES = [
     ("band_u2_fp8_resid", "float8_e4m3fn", 2, 20, 20, 128, 32, 3, 3, 1, 1, True, "band"),
     ("band_u4_bf16_s2", "bfloat16", 2, 28, 28, 64, 64, 3, 3, 2, 1, False, "band"),
     ("band_lds_epilogue", "bfloat16", 2, 20, 20, 64, 20, 3, 3, 1, 1, True, "band"),
+    # one accumulator block per wave: the epilogue reads the last MFMA first
+    ("band_fp8_single_block", "float8_e4m3fn", 1, 8, 8, 64, 16, 3, 3, 1, 1, False, "band"),
     ("resident_c48", "bfloat16", 2, 20, 20, 48, 32, 3, 3, 1, 1, False, "resident"),
     ("fallback_tiled", "bfloat16", 1, 12, 12, 96, 64, 5, 5, 1, 2, True, "tiled"),
 ]
