@@ -148,15 +148,20 @@ int32_t hip_fail(hipError_t e) { return e == hipSuccess ? 1 : -(int32_t)e; }
 hipError_t launch_transpose(const void* filter, int32_t fcrs, const Shape& s, int32_t dtype,
                             void* nk, hipStream_t stream) {
     const int eb = elem_bytes(dtype);
-    const int64_t chunks = s.F * (s.kpitch / (16 / eb));
-    if (chunks == 0) return hipSuccess;
-    const int blocks = (int)((chunks + 255) / 256);
+    const int64_t row_chunks = s.kpitch / (16 / eb);
+    if (s.F == 0 || row_chunks == 0) return hipSuccess;
+    // 64-thread workgroups along the stored layout's contiguous direction
+    // (FCRS: a row's chunks; RSCF: C_out), one grid row per NK row (FCRS)
+    // or chunk (RSCF), rows past 65535 looping; many small workgroups keep
+    // many CUs' loads in flight
+    const int64_t gx = fcrs ? row_chunks : s.F, gy = fcrs ? s.F : row_chunks;
+    const dim3 grid((unsigned)((gx + 63) / 64), (unsigned)(gy < 65535 ? gy : 65535));
     if (eb == 2)
-        hipLaunchKernelGGL(filter_to_nk_kernel<2>, dim3(blocks), dim3(256), 0, stream,
+        hipLaunchKernelGGL(filter_to_nk_kernel<2>, grid, dim3(64), 0, stream,
                            (const uint8_t*)filter, (uint8_t*)nk, fcrs, (int)s.R, (int)s.S,
                            (int)s.C, (int)s.F, (int)s.K, (int)s.kpitch);
     else
-        hipLaunchKernelGGL(filter_to_nk_kernel<1>, dim3(blocks), dim3(256), 0, stream,
+        hipLaunchKernelGGL(filter_to_nk_kernel<1>, grid, dim3(64), 0, stream,
                            (const uint8_t*)filter, (uint8_t*)nk, fcrs, (int)s.R, (int)s.S,
                            (int)s.C, (int)s.F, (int)s.K, (int)s.kpitch);
     return hipGetLastError();

@@ -134,31 +134,44 @@ __device__ __forceinline__ f32x4 mfma_step<DT_FP8>(const i32x4* a, const i32x4* 
 // VEC channels of one tap (C % VEC == 0), gathered from the stored layout:
 //   RSCF [R,S,C,F]: W(k, co) = w[k*F + co]              (k = (r*S+s)*C + ci)
 //   FCRS [F,C,R,S]: W(k, co) = w[((co*C + ci)*R + r)*S + s]
-// Chunks at or past K are zero.
+// Chunks at or past K are zero.  Consecutive lanes take the stored layout's
+// contiguous direction, so each of a wave's VEC loads touches few lines:
+//   RSCF: lanes along co (x), chunks along y;
+//   FCRS: lanes along the chunks of one row (x), rows along y.
+// Grid rows past 65535 loop.  Indices are 32-bit: the NK matrix is below
+// 2^31 bytes.
 template <int E>
-__global__ __launch_bounds__(256) void filter_to_nk_kernel(
+__global__ __launch_bounds__(64) void filter_to_nk_kernel(
     const uint8_t* __restrict__ w, uint8_t* __restrict__ nk, int fcrs, int R, int S,
     int C, int F, int K, int kpitch) {
     constexpr int VEC = 16 / E;
-    const int chunks_per_row = kpitch / VEC;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (int64_t)chunks_per_row * F) return;
-    const int co = (int)(gid / chunks_per_row);
-    const int k0 = (int)(gid % chunks_per_row) * VEC;
-    union { i32x4 v; uint8_t b[16]; uint16_t h[8]; } u;
-    u.v = i32x4{0, 0, 0, 0};
-    if (k0 < K) {
-        const int tap = k0 / C, ci0 = k0 - tap * C;
-        const int r = tap / S, s = tap - r * S;
-        for (int j = 0; j < VEC; ++j) {
-            int64_t idx;
-            if (fcrs) idx = ((int64_t)(co * C + ci0 + j) * R + r) * S + s;
-            else idx = (int64_t)(k0 + j) * F + co;
-            if (E == 2) u.h[j] = reinterpret_cast<const uint16_t*>(w)[idx];
-            else u.b[j] = w[idx];
+    const int row_chunks = kpitch / VEC;
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    auto chunk_out = [&](int co, int chunk) {
+        const int k0 = chunk * VEC;
+        union { i32x4 v; uint8_t b[16]; uint16_t h[8]; } u;
+        u.v = i32x4{0, 0, 0, 0};
+        if (k0 < K) {
+            const int tap = k0 / C, ci0 = k0 - tap * C;
+            const int r = tap / S, s = tap - r * S;
+            // VEC independent element loads at a fixed stride, all in flight
+            const int base = fcrs ? ((co * C + ci0) * R + r) * S + s : k0 * F + co;
+            const int step = fcrs ? R * S : F;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                if (E == 2) u.h[j] = reinterpret_cast<const uint16_t*>(w)[base + j * step];
+                else u.b[j] = w[base + j * step];
+            }
         }
+        *reinterpret_cast<i32x4*>(nk + ((int64_t)co * kpitch + k0) * E) = u.v;
+    };
+    if (fcrs) {
+        if (x >= row_chunks) return;
+        for (int co = blockIdx.y; co < F; co += gridDim.y) chunk_out(co, x);
+    } else {
+        if (x >= F) return;
+        for (int chunk = blockIdx.y; chunk < row_chunks; chunk += gridDim.y) chunk_out(x, chunk);
     }
-    *reinterpret_cast<i32x4*>(nk + ((int64_t)co * kpitch + k0) * E) = u.v;
 }
 
 // ---------------------------------------------------------------------------
