@@ -9,9 +9,10 @@ call is declined, these functions say so instead of computing anything.
 
 Names mirror the C entry points:
   conv2d_fwd, conv2d_fwd_check, conv2d_fwd_nk, conv2d_filter_to_nk,
+  conv2d_fwd_epilogue, conv2d_fwd_nk_epilogue, conv2d_epilogue_check,
   conv2d_fwd_kernel_name, conv2d_workspace_bytes, conv2d_nk_row_pitch,
   conv2d_reason_string, conv2d_abi_version
-plus conv2d(), which allocates the output and calls conv2d_fwd.
+plus conv2d(), which allocates the output and calls conv2d_fwd_epilogue.
 """
 import ctypes
 import os
@@ -28,7 +29,18 @@ OUT_DTYPES = {torch.bfloat16: torch.bfloat16, torch.float16: torch.float16,
 # decline reason codes (IGC_DECLINE_* in include/igemm_conv.h)
 REASONS = {0: "ok", 1: "dtype", 2: "stride", 3: "dilation", 4: "padding", 5: "groups",
            6: "shape", 7: "output_shape", 8: "vector_width", 9: "alignment",
-           10: "null_pointer", 11: "overlap", 12: "workspace", 13: "size_limit"}
+           10: "null_pointer", 11: "overlap", 12: "workspace", 13: "size_limit",
+           14: "epilogue"}
+
+# fused-epilogue activation codes (IGC_ACT_* in include/igemm_conv.h)
+ACTIVATIONS = {None: 0, "none": 0, "relu": 1, "silu": 2}
+
+
+class IgcEpilogue(ctypes.Structure):
+    """struct igc_epilogue: per-channel scale and bias (device float
+    arrays or NULL) and an activation code."""
+    _fields_ = [("scale", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("activation", ctypes.c_int32)]
 
 _lib = None
 
@@ -70,6 +82,13 @@ def lib():
     L.conv2d_fwd_kernel_name.restype = ctypes.c_char_p
     L.conv2d_filter_to_nk.argtypes = [vp, i32, i64p, i32, vp, sz, vp]
     L.conv2d_filter_to_nk.restype = i32
+    epip = ctypes.POINTER(IgcEpilogue)
+    L.conv2d_fwd_epilogue.argtypes = conv_head + [epip, vp, sz, vp]
+    L.conv2d_fwd_epilogue.restype = i32
+    L.conv2d_fwd_nk_epilogue.argtypes = conv_head + [epip, vp]
+    L.conv2d_fwd_nk_epilogue.restype = i32
+    L.conv2d_epilogue_check.argtypes = [epip, vp, i64p]
+    L.conv2d_epilogue_check.restype = i32
     _lib = L
     return L
 
@@ -176,6 +195,54 @@ def conv2d_fwd_nk(input, nk, filt_shape, output, *, filter_is_fcrs, stride=1, pa
     return lib().conv2d_fwd_nk(*head, _stream(stream, output))
 
 
+def make_epilogue(scale=None, bias=None, activation=None):
+    """An IgcEpilogue from tensors / raw pointers and an activation name or
+    code, or None when nothing is fused."""
+    if scale is None and bias is None and activation in (None, "none", 0):
+        return None
+    act = activation if isinstance(activation, int) else ACTIVATIONS.get(activation, -1)
+    return IgcEpilogue(_ptr(scale), _ptr(bias), int(act))
+
+
+def _epi_ref(epi):
+    return None if epi is None else ctypes.byref(epi)
+
+
+def conv2d_epilogue_check(output, *, scale=None, bias=None, activation=None,
+                          out_shape=None) -> int:
+    """Host-only check of a fused epilogue against the output: 0 or a code."""
+    out_shape = output.shape if out_shape is None else out_shape
+    return lib().conv2d_epilogue_check(_epi_ref(make_epilogue(scale, bias, activation)),
+                                       _ptr(output), _i64(out_shape))
+
+
+def conv2d_fwd_epilogue(input, filter, output, *, filter_is_fcrs, stride=1, padding=0,
+                        dilation=1, groups=1, source=None, beta=0.0, scale=None, bias=None,
+                        activation=None, workspace=None, workspace_bytes=0, stream=None,
+                        dtype=None, in_shape=None, filt_shape=None, out_shape=None) -> int:
+    """conv2d_fwd with the fused per-channel epilogue
+    act(scale[co] * conv + bias[co] + beta * source)."""
+    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
+                      groups, dtype, source, beta, in_shape, filt_shape, out_shape)
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    epi = make_epilogue(scale, bias, activation)
+    return lib().conv2d_fwd_epilogue(*head, _epi_ref(epi), _ptr(workspace),
+                                     int(workspace_bytes), _stream(stream, output))
+
+
+def conv2d_fwd_nk_epilogue(input, nk, filt_shape, output, *, filter_is_fcrs, stride=1,
+                           padding=0, dilation=1, groups=1, source=None, beta=0.0,
+                           scale=None, bias=None, activation=None, stream=None, dtype=None,
+                           in_shape=None, out_shape=None) -> int:
+    """conv2d_fwd_nk with the fused per-channel epilogue."""
+    head = _conv_head(input, nk, filter_is_fcrs, output, stride, dilation, padding, groups,
+                      dtype, source, beta, in_shape=in_shape, filt_shape=filt_shape,
+                      out_shape=out_shape)
+    epi = make_epilogue(scale, bias, activation)
+    return lib().conv2d_fwd_nk_epilogue(*head, _epi_ref(epi), _stream(stream, output))
+
+
 def conv2d_workspace_bytes(filt_shape, filter_is_fcrs, dtype) -> int:
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
     return int(lib().conv2d_workspace_bytes(_i64(filt_shape), int(bool(filter_is_fcrs)), code))
@@ -204,8 +271,9 @@ def out_hw(h, w, r, s, stride, padding):
 
 
 def conv2d(input, filter, *, filter_is_fcrs, stride=1, padding=0, source=None, beta=0.0,
-           stream=None):
-    """Allocate the NHWC output (torch memory) and run conv2d_fwd into it."""
+           scale=None, bias=None, activation=None, stream=None):
+    """Allocate the NHWC output (torch memory) and run conv2d_fwd_epilogue
+    into it (with no scale, bias or activation this is conv2d_fwd)."""
     if filter_is_fcrs:
         f, _, r, s = filter.shape
     else:
@@ -216,12 +284,17 @@ def conv2d(input, filter, *, filter_is_fcrs, stride=1, padding=0, source=None, b
                       device=input.device)
     ws_bytes = conv2d_workspace_bytes(filter.shape, filter_is_fcrs, input.dtype)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=input.device)
-    rc = conv2d_fwd(input, filter, out, filter_is_fcrs=filter_is_fcrs, stride=stride,
-                    padding=padding, source=source, beta=beta, workspace=ws, stream=stream)
+    rc = conv2d_fwd_epilogue(input, filter, out, filter_is_fcrs=filter_is_fcrs,
+                             stride=stride, padding=padding, source=source, beta=beta,
+                             scale=scale, bias=bias, activation=activation, workspace=ws,
+                             stream=stream)
     if rc == 0:
         reason = conv2d_fwd_check(input, filter, out, filter_is_fcrs=filter_is_fcrs,
                                   stride=stride, padding=padding, source=source, beta=beta,
                                   workspace=ws)
+        if reason == 0:
+            reason = conv2d_epilogue_check(out, scale=scale, bias=bias,
+                                           activation=activation)
         raise Declined(f"conv2d_fwd declined: {REASONS.get(reason, reason)}")
     if rc < 0:
         raise RuntimeError(f"conv2d_fwd failed with HIP error {-rc}")

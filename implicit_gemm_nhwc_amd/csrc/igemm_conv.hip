@@ -18,7 +18,7 @@ namespace {
 
 using namespace igc;
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 int elem_bytes(int32_t dtype) { return dtype == IGC_DTYPE_FP8_E4M3FN ? 1 : 2; }
 
@@ -142,6 +142,24 @@ int32_t check_all(const void* input, const int64_t in_nhwc[4], const void* filte
 }
 
 int32_t hip_fail(hipError_t e) { return e == hipSuccess ? 1 : -(int32_t)e; }
+
+// The fused epilogue's own gate: a known activation, 4-byte aligned
+// coefficient arrays, and none of them overlapping the output (every
+// workgroup reads them while others write the output).
+int32_t check_epilogue(const igc_epilogue* epi, const void* output, const Shape& s) {
+    if (!epi) return IGC_OK;
+    if (epi->activation != IGC_ACT_NONE && epi->activation != IGC_ACT_RELU &&
+        epi->activation != IGC_ACT_SILU)
+        return IGC_DECLINE_EPILOGUE;
+    const size_t out_bytes = (size_t)(s.M * s.F) * 2;
+    const size_t coef_bytes = (size_t)s.F * sizeof(float);
+    for (const float* c : {epi->scale, epi->bias}) {
+        if (!c) continue;
+        if (((uintptr_t)c & 3u) != 0) return IGC_DECLINE_EPILOGUE;
+        if (overlaps(c, coef_bytes, output, out_bytes)) return IGC_DECLINE_EPILOGUE;
+    }
+    return IGC_OK;
+}
 
 // ---- launches -----------------------------------------------------------
 
@@ -458,13 +476,20 @@ KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp) {
 }
 
 hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
-                        float beta, const Shape& s, int32_t dtype, hipStream_t stream) {
+                        float beta, const igc_epilogue* epi, const Shape& s, int32_t dtype,
+                        hipStream_t stream) {
     ConvArgs a{};
     a.x = (const uint8_t*)input;
     a.nk = (const uint8_t*)nk;
     a.y = (uint16_t*)output;
     a.src = (const uint16_t*)source;
     a.beta = beta;
+    if (epi) {
+        a.scale = epi->scale;
+        a.bias = epi->bias;
+        a.act = epi->activation;
+        a.epi = (a.scale || a.bias || a.act != IGC_ACT_NONE) ? 1 : 0;
+    }
     a.H = (int)s.H; a.W = (int)s.W; a.C = (int)s.C;
     a.Ho = (int)s.Ho; a.Wo = (int)s.Wo; a.F = (int)s.F;
     a.R = (int)s.R; a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
@@ -545,6 +570,7 @@ const char* conv2d_reason_string(int32_t reason) {
         case IGC_DECLINE_OVERLAP: return "overlap";
         case IGC_DECLINE_WORKSPACE: return "workspace";
         case IGC_DECLINE_SIZE_LIMIT: return "size_limit";
+        case IGC_DECLINE_EPILOGUE: return "epilogue";
         default: return "unknown";
     }
 }
@@ -621,30 +647,46 @@ int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs, const in
     return hip_fail(launch_transpose(filter, filter_is_fcrs, s, dtype, nk, (hipStream_t)stream));
 }
 
-int32_t conv2d_fwd_nk(const void* input, const int64_t in_nhwc[4], const void* nk,
-                      int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
-                      const int64_t out_nhwc[4], const int32_t stride[2],
-                      const int32_t dilation[2], const int32_t padding[2], int32_t groups,
-                      int32_t dtype, const void* source, float beta, void* stream) {
+int32_t conv2d_fwd_nk_epilogue(const void* input, const int64_t in_nhwc[4], const void* nk,
+                               int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
+                               const int64_t out_nhwc[4], const int32_t stride[2],
+                               const int32_t dilation[2], const int32_t padding[2],
+                               int32_t groups, int32_t dtype, const void* source, float beta,
+                               const igc_epilogue* epilogue, void* stream) {
     Shape s;
     size_t nk_bytes = conv2d_workspace_bytes(filt_dims, filter_is_fcrs, dtype);
     const int32_t rc = check_all(input, in_nhwc, nk, nk_bytes ? nk_bytes : 1, filter_is_fcrs,
                                  filt_dims, output, out_nhwc, stride, dilation, padding, groups,
                                  dtype, source, nullptr, 0, &s);
     if (rc != IGC_OK) return 0;
-    return hip_fail(launch_igemm(input, nk, output, source, beta, s, dtype, (hipStream_t)stream));
+    if (check_epilogue(epilogue, output, s) != IGC_OK) return 0;
+    return hip_fail(launch_igemm(input, nk, output, source, beta, epilogue, s, dtype,
+                                 (hipStream_t)stream));
 }
 
-int32_t conv2d_fwd(const void* input, const int64_t in_nhwc[4], const void* filter,
-                   int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
-                   const int64_t out_nhwc[4], const int32_t stride[2], const int32_t dilation[2],
-                   const int32_t padding[2], int32_t groups, int32_t dtype, const void* source,
-                   float beta, void* workspace, size_t workspace_bytes, void* stream) {
+int32_t conv2d_fwd_nk(const void* input, const int64_t in_nhwc[4], const void* nk,
+                      int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
+                      const int64_t out_nhwc[4], const int32_t stride[2],
+                      const int32_t dilation[2], const int32_t padding[2], int32_t groups,
+                      int32_t dtype, const void* source, float beta, void* stream) {
+    return conv2d_fwd_nk_epilogue(input, in_nhwc, nk, filter_is_fcrs, filt_dims, output,
+                                  out_nhwc, stride, dilation, padding, groups, dtype, source,
+                                  beta, nullptr, stream);
+}
+
+int32_t conv2d_fwd_epilogue(const void* input, const int64_t in_nhwc[4], const void* filter,
+                            int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
+                            const int64_t out_nhwc[4], const int32_t stride[2],
+                            const int32_t dilation[2], const int32_t padding[2], int32_t groups,
+                            int32_t dtype, const void* source, float beta,
+                            const igc_epilogue* epilogue, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     Shape s;
     const int32_t rc = check_all(input, in_nhwc, filter, 0, filter_is_fcrs, filt_dims, output,
                                  out_nhwc, stride, dilation, padding, groups, dtype, source,
                                  workspace, workspace_bytes, &s);
     if (rc != IGC_OK) return 0;
+    if (check_epilogue(epilogue, output, s) != IGC_OK) return 0;
     if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
     hipStream_t st = (hipStream_t)stream;
     const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
@@ -656,12 +698,33 @@ int32_t conv2d_fwd(const void* input, const int64_t in_nhwc[4], const void* filt
         owned = true;
     }
     hipError_t e = launch_transpose(filter, filter_is_fcrs, s, dtype, nk, st);
-    if (e == hipSuccess) e = launch_igemm(input, nk, output, source, beta, s, dtype, st);
+    if (e == hipSuccess) e = launch_igemm(input, nk, output, source, beta, epilogue, s, dtype, st);
     if (owned) {
         hipError_t f = hipFreeAsync(nk, st);
         if (e == hipSuccess) e = f;
     }
     return hip_fail(e);
+}
+
+int32_t conv2d_fwd(const void* input, const int64_t in_nhwc[4], const void* filter,
+                   int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
+                   const int64_t out_nhwc[4], const int32_t stride[2], const int32_t dilation[2],
+                   const int32_t padding[2], int32_t groups, int32_t dtype, const void* source,
+                   float beta, void* workspace, size_t workspace_bytes, void* stream) {
+    return conv2d_fwd_epilogue(input, in_nhwc, filter, filter_is_fcrs, filt_dims, output,
+                               out_nhwc, stride, dilation, padding, groups, dtype, source, beta,
+                               nullptr, workspace, workspace_bytes, stream);
+}
+
+int32_t conv2d_epilogue_check(const igc_epilogue* epilogue, const void* output,
+                              const int64_t out_nhwc[4]) {
+    if (!out_nhwc) return IGC_DECLINE_NULL_POINTER;
+    for (int i = 0; i < 4; ++i)
+        if (out_nhwc[i] < 0) return IGC_DECLINE_SHAPE;
+    Shape s{};
+    s.M = out_nhwc[0] * out_nhwc[1] * out_nhwc[2];
+    s.F = out_nhwc[3];
+    return check_epilogue(epilogue, output, s);
 }
 
 }  // extern "C"

@@ -48,6 +48,11 @@ struct ConvArgs {
     uint16_t* y;        // NHWC output (bf16 or fp16 bits)
     const uint16_t* src;  // residual source, same layout and type as y
     float beta;
+    // fused per-channel epilogue (all unused when epi == 0)
+    const float* scale;   // [C_out] multiplier of the convolution, or null (1)
+    const float* bias;    // [C_out] addend, or null (0)
+    int act;              // ACT_NONE, ACT_RELU or ACT_SILU
+    int epi;              // nonzero when scale, bias or act is present
     int H, W, C;        // input (N only enters through M)
     int Ho, Wo, F;      // output spatial size and C_out
     int S, stride, pad;
@@ -100,6 +105,31 @@ __device__ __forceinline__ uint16_t f32_to_out(float v, int dt) {
 __device__ __forceinline__ float out_to_f32(uint16_t bits, int dt) {
     if (dt == DT_FP16) return (float)__builtin_bit_cast(_Float16, bits);
     return __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+
+// Fused elementwise epilogue (page "dispatch_amd_4wave_conv2d", Parameters:
+// an optional elementwise function fused on each output element; page
+// "dispatch_fused_im2col_conv2d_apple", Parameters: the same in 4-D NHWC
+// coordinates).  A C ABI cannot carry a device closure, so the library
+// offers a fixed one, per output channel co:
+//   v = scale[co] * acc + bias[co];  v += beta * src;  v = act(v)
+// then the single rounding to the output type.  scale / bias may be null
+// (1 / 0).  Channels co >= C_out are never stored, so their coefficients are
+// not read.
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_SILU = 2 };
+
+__device__ __forceinline__ float epi_pre(const ConvArgs& a, int co, float v) {
+    const bool ok = co < a.F;
+    const float sc = (a.scale != nullptr && ok) ? a.scale[co] : 1.0f;
+    const float bi = (a.bias != nullptr && ok) ? a.bias[co] : 0.0f;
+    return __builtin_fmaf(sc, v, bi);
+}
+
+// ReLU keeps v when v > 0, else +0; SiLU is v * sigmoid(v) = v / (1 + e^-v).
+__device__ __forceinline__ float epi_act(const ConvArgs& a, float v) {
+    if (a.act == ACT_RELU) return v > 0.0f ? v : 0.0f;
+    if (a.act == ACT_SILU) return v / (1.0f + __expf(-v));
+    return v;
 }
 
 template <int DT>
@@ -380,10 +410,18 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
             if (co >= a.F) continue;
             float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
             if (vec_ok) {
+                if (a.epi) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = epi_pre(a, co + q, v[q]);
+                }
                 if constexpr (RESID) {
                     const u16x4 s = *reinterpret_cast<const u16x4*>(a.src + obase + co);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a.beta, out_to_f32(s[q], ODT), v[q]);
+                }
+                if (a.epi) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = epi_act(a, v[q]);
                 }
                 u16x4 o;
 #pragma unroll
@@ -394,7 +432,9 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
                 for (int q = 0; q < 4; ++q) {
                     if (co + q < a.F) {
                         float d = v[q];
+                        if (a.epi) d = epi_pre(a, co + q, d);
                         if constexpr (RESID) d = __builtin_fmaf(a.beta, out_to_f32(a.src[obase + co + q], ODT), d);
+                        if (a.epi) d = epi_act(a, d);
                         a.y[obase + co + q] = f32_to_out(d, ODT);
                     }
                 }
@@ -633,10 +673,18 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
             if (co >= a.F) continue;
             float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
             if (vec_ok) {
+                if (a.epi) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = epi_pre(a, co + q, v[q]);
+                }
                 if constexpr (RESID) {
                     const u16x4 s = *reinterpret_cast<const u16x4*>(a.src + obase + co);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a.beta, out_to_f32(s[q], ODT), v[q]);
+                }
+                if (a.epi) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = epi_act(a, v[q]);
                 }
                 u16x4 o;
 #pragma unroll
@@ -647,7 +695,9 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
                 for (int q = 0; q < 4; ++q) {
                     if (co + q < a.F) {
                         float d = v[q];
+                        if (a.epi) d = epi_pre(a, co + q, d);
                         if constexpr (RESID) d = __builtin_fmaf(a.beta, out_to_f32(a.src[obase + co + q], ODT), d);
+                        if (a.epi) d = epi_act(a, d);
                         a.y[obase + co + q] = f32_to_out(d, ODT);
                     }
                 }
@@ -967,6 +1017,10 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
                     }
                     const int co = i * 32 + 8 * (2 * k + half);
                     if (pix_ok & (co < a.F)) {
+                        if (a.epi) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] = epi_pre(a, co + e, v[e]);
+                        }
                         if constexpr (RESID) {
                             const i32x4 sv = *reinterpret_cast<const i32x4*>(a.src + obase + co);
 #pragma unroll
@@ -974,6 +1028,10 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
                                 const uint16_t hb = (uint16_t)((unsigned)sv[e >> 1] >> (16 * (e & 1)));
                                 v[e] = __builtin_fmaf(a.beta, out_to_f32(hb, ODT), v[e]);
                             }
+                        }
+                        if (a.epi) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] = epi_act(a, v[e]);
                         }
                         i32x4 ov;
 #pragma unroll
@@ -1015,7 +1073,9 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             const int th = small_div(q, tw_n, inv_twn), tw = q - th * tw_n;
             float v = stage[(th * a.TW + tw) * a.spitch + co];
             const int64_t o = ((int64_t)(n * a.Ho + oh0 + th) * a.Wo + ow0 + tw) * a.F + co;
+            if (a.epi) v = epi_pre(a, co, v);
             if constexpr (RESID) v = __builtin_fmaf(a.beta, out_to_f32(a.src[o], ODT), v);
+            if (a.epi) v = epi_act(a, v);
             a.y[o] = f32_to_out(v, ODT);
         }
     }
@@ -1386,12 +1446,20 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             for (int q = 0; q < NI; ++q) {
                 const f32x4 v4 = *reinterpret_cast<const f32x4*>(ereg + (q * PPI + pl) * EP + c4 * 16);
                 float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+                if (a.epi) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = epi_pre(a, co + e, v[e]);
+                }
                 if constexpr (RESID) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const uint16_t h = (uint16_t)(sv[j & 1][q][e >> 1] >> (16 * (e & 1)));
                         v[e] = __builtin_fmaf(a.beta, out_to_f32(h, ODT), v[e]);
                     }
+                }
+                if (a.epi) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = epi_act(a, v[e]);
                 }
                 u32x2 ov;
                 ov[0] = (uint32_t)f32_to_out(v[0], ODT) | ((uint32_t)f32_to_out(v[1], ODT) << 16);
@@ -1415,7 +1483,9 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 for (int e = 0; e < 4; ++e) {
                     if (co + e < a.F) {
                         float d = v4[e];
+                        if (a.epi) d = epi_pre(a, co + e, d);
                         if constexpr (RESID) d = __builtin_fmaf(a.beta, out_to_f32(a.src[o + e], ODT), d);
+                        if (a.epi) d = epi_act(a, d);
                         a.y[o + e] = f32_to_out(d, ODT);
                     }
                 }

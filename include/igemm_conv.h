@@ -77,9 +77,42 @@ enum {
                                       without being exactly the output       */
     IGC_DECLINE_WORKSPACE = 12,    /* workspace given but smaller than
                                       conv2d_workspace_bytes()               */
-    IGC_DECLINE_SIZE_LIMIT = 13    /* a size beyond the kernels' 32-bit index
+    IGC_DECLINE_SIZE_LIMIT = 13,   /* a size beyond the kernels' 32-bit index
                                       ranges (see conv2d_fwd_check)          */
+    IGC_DECLINE_EPILOGUE = 14      /* fused epilogue: unknown activation,
+                                      scale/bias not 4-byte aligned, or
+                                      scale/bias overlapping the output      */
 };
+
+/*
+ * Fused elementwise epilogue.  Page "dispatch_amd_4wave_conv2d" (Parameters:
+ * elementwise_lambda_fn) lets the caller fuse an elementwise function into
+ * the convolution's epilogue, called per output element with its (m, co)
+ * coordinates; page "dispatch_fused_im2col_conv2d_apple" (Parameters:
+ * maybe_epilogue_func) does the same in NHWC coordinates.  A C ABI cannot
+ * carry a device closure, so this library offers one fixed family, per
+ * output element (n, oh, ow, co), in fp32:
+ *   v = scale[co] * conv + bias[co]
+ *   v = v + beta * source          (when source != NULL)
+ *   v = act(v)                     relu: v if v > 0 else +0
+ *                                  silu: v / (1 + exp(-v))
+ *   output = round_to_nearest_even(v)
+ * scale and bias are device arrays of C_out floats (caller-owned, 4-byte
+ * aligned, not overlapping the output), either may be NULL (1 and 0).
+ * A NULL igc_epilogue pointer, or {NULL, NULL, IGC_ACT_NONE}, is exactly
+ * conv2d_fwd / conv2d_fwd_nk.
+ */
+enum {
+    IGC_ACT_NONE = 0,
+    IGC_ACT_RELU = 1,
+    IGC_ACT_SILU = 2
+};
+
+typedef struct igc_epilogue {
+    const float* scale;    /* [C_out] or NULL */
+    const float* bias;     /* [C_out] or NULL */
+    int32_t activation;    /* IGC_ACT_* */
+} igc_epilogue;
 
 /* Version of this ABI. */
 int32_t conv2d_abi_version(void);
@@ -191,6 +224,40 @@ int32_t conv2d_fwd_nk(const void* input, const int64_t in_nhwc[4],
                       const int32_t padding[2], int32_t groups,
                       int32_t dtype, const void* source, float beta,
                       void* stream);
+
+/*
+ * conv2d_fwd with the fused elementwise epilogue above (epilogue may be
+ * NULL).  Arguments and returns otherwise as conv2d_fwd; a call whose
+ * epilogue fails conv2d_epilogue_check is declined (0).
+ */
+int32_t conv2d_fwd_epilogue(const void* input, const int64_t in_nhwc[4],
+                            const void* filter, int32_t filter_is_fcrs,
+                            const int64_t filt_dims[4],
+                            void* output, const int64_t out_nhwc[4],
+                            const int32_t stride[2], const int32_t dilation[2],
+                            const int32_t padding[2], int32_t groups,
+                            int32_t dtype, const void* source, float beta,
+                            const igc_epilogue* epilogue,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* conv2d_fwd_nk with the fused elementwise epilogue (may be NULL). */
+int32_t conv2d_fwd_nk_epilogue(const void* input, const int64_t in_nhwc[4],
+                               const void* nk, int32_t filter_is_fcrs,
+                               const int64_t filt_dims[4],
+                               void* output, const int64_t out_nhwc[4],
+                               const int32_t stride[2], const int32_t dilation[2],
+                               const int32_t padding[2], int32_t groups,
+                               int32_t dtype, const void* source, float beta,
+                               const igc_epilogue* epilogue, void* stream);
+
+/*
+ * Host-only check of an epilogue against an output of shape out_nhwc
+ * (pointers compared, never dereferenced): IGC_OK, IGC_DECLINE_EPILOGUE,
+ * IGC_DECLINE_NULL_POINTER (out_nhwc NULL) or IGC_DECLINE_SHAPE (negative
+ * dims).  A NULL epilogue is IGC_OK.
+ */
+int32_t conv2d_epilogue_check(const igc_epilogue* epilogue, const void* output,
+                              const int64_t out_nhwc[4]);
 
 #ifdef __cplusplus
 }

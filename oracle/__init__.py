@@ -14,14 +14,23 @@ Parity status of each function (what pins it is in tests/test_oracle_pins.py):
                           closed form, delta filters, border counts,
                           stride subsampling, layout and bilinearity
                           invariants, residual identities.
+  conv2d_epilogue(_points) pinned: hand-worked golden values
+  activation              (tests/golden/epilogue_cases.txt), reduction to
+                          conv2d with no epilogue, bias as an extra
+                          constant-one input channel, scale folded into the
+                          filter, textbook sigmoid values, relu's sign split.
   filter_to_nk           pinned: element-wise brute force from the index
                           formula on small filters.
   gate_accepts           pinned: hand-written case table from page 1's
                           Parameters/Args rules (tests/golden/gate_cases.txt).
 """
 from .reference import (  # noqa: F401
+    ACTIVATIONS,
     DTYPES,
+    activation,
     conv2d,
+    conv2d_epilogue,
+    conv2d_epilogue_points,
     conv2d_points,
     filter_dims_rscf,
     filter_to_nk,

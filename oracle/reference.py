@@ -117,6 +117,65 @@ def conv2d(x, w, *, filter_is_fcrs: bool, stride=1, padding=0, source=None,
     return y
 
 
+ACTIVATIONS = ("none", "relu", "silu")
+
+
+def activation(v: np.ndarray, act: str) -> np.ndarray:
+    """The epilogue activations, in float64: relu keeps v where v > 0 and
+    gives +0 elsewhere; silu is v * sigmoid(v) = v / (1 + exp(-v))."""
+    if act in (None, "none"):
+        return v
+    if act == "relu":
+        return np.where(v > 0.0, v, 0.0)
+    if act == "silu":
+        with np.errstate(over="ignore"):
+            return v / (1.0 + np.exp(-v))
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def conv2d_epilogue(x, w, *, filter_is_fcrs: bool, stride=1, padding=0, source=None,
+                    beta: float = 0.0, scale=None, bias=None, act: str = "none") -> np.ndarray:
+    """The convolution with a fused per-channel elementwise epilogue, fp64.
+
+    Page 1 ("dispatch_amd_4wave_conv2d", Parameters: elementwise_lambda_fn)
+    and page 2 ("dispatch_fused_im2col_conv2d_apple", Parameters:
+    maybe_epilogue_func) fuse an elementwise function of each output element
+    and its coordinates into the convolution.  The pages leave the function
+    to the caller; this oracle follows the fixed family the library offers:
+        v = scale[co] * conv[n, oh, ow, co] + bias[co]
+        v = v + beta * source[n, oh, ow, co]     (when a source is given)
+        D = act(v)
+    scale and bias are per-output-channel vectors (None = 1 and 0).
+    Returns the unrounded float64 D, shape [N, Ho, Wo, C_out].
+    """
+    y = conv2d(x, w, filter_is_fcrs=filter_is_fcrs, stride=stride, padding=padding)
+    return _epilogue(y, None if source is None else _f64(source), beta, scale, bias, act)
+
+
+def _epilogue(y, src64, beta, scale, bias, act):
+    f = y.shape[-1]
+    sc = np.ones(f) if scale is None else _f64(scale).reshape(f)
+    bi = np.zeros(f) if bias is None else _f64(bias).reshape(f)
+    v = y * sc + bi
+    if src64 is not None:
+        v = v + beta * src64
+    return activation(v, act)
+
+
+def conv2d_epilogue_points(x, w, pix, *, filter_is_fcrs: bool, stride=1, padding=0,
+                           source=None, beta: float = 0.0, scale=None, bias=None,
+                           act: str = "none") -> np.ndarray:
+    """conv2d_epilogue evaluated only at the flattened output pixels pix
+    (as conv2d_points).  Returns [len(pix), C_out] float64."""
+    y = conv2d_points(x, w, pix, filter_is_fcrs=filter_is_fcrs, stride=stride,
+                      padding=padding)
+    src64 = None
+    if source is not None:
+        s64 = _f64(source)
+        src64 = s64.reshape(-1, s64.shape[-1])[np.asarray(pix, dtype=np.int64)]
+    return _epilogue(y, src64, beta, scale, bias, act)
+
+
 def conv2d_points(x, w, pix, *, filter_is_fcrs: bool, stride=1, padding=0,
                   source=None, beta: float = 0.0) -> np.ndarray:
     """The same definition as conv2d, evaluated only at the flattened output

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_reason_names():
-    assert igc.conv2d_abi_version() == 1
+    assert igc.conv2d_abi_version() == 2
     for code, name in igc.REASONS.items():
         assert igc.conv2d_reason_string(code) == name
     assert igc.conv2d_reason_string(999) == "unknown"
@@ -196,3 +196,43 @@ def test_kernel_selection():
     assert igc.conv2d_fwd_kernel_name((2, 8, 8, 64), (3, 3, 64, 65), (2, 8, 8, 65),
                                       filter_is_fcrs=False, dtype=torch.float16,
                                       padding=1) == "igemm_fwd_wide_kernel"
+
+
+# ------------------------------------------------------------ fused epilogue
+SC, BI = 0x60000000, 0x60001000
+OUT_BYTES = 2 * 9 * 9 * 48 * 2
+
+
+@pytest.mark.parametrize("kw,reason", [
+    (dict(), "ok"),
+    (dict(scale=SC, bias=BI, activation="relu"), "ok"),
+    (dict(activation="silu"), "ok"),
+    (dict(bias=BI), "ok"),
+    (dict(activation=3), "epilogue"),
+    (dict(activation=-1), "epilogue"),
+    (dict(scale=SC + 2), "epilogue"),
+    (dict(bias=BI + 1, activation="relu"), "epilogue"),
+    (dict(scale=Y + 64), "epilogue"),                      # inside the output
+    (dict(bias=Y + OUT_BYTES - 4), "epilogue"),            # last word overlaps
+    (dict(bias=Y - 48 * 4 + 4), "epilogue"),               # runs into the output
+    (dict(bias=Y - 48 * 4), "ok"),                         # ends where it starts
+])
+def test_epilogue_check(kw, reason):
+    code = igc.conv2d_epilogue_check(Y, out_shape=BASE["out_shape"], **kw)
+    assert igc.REASONS[code] == reason
+
+
+def test_epilogue_declined_call_enqueues_nothing():
+    # a bad epilogue declines before any HIP call, on both entry points; a
+    # bad convolution declines whatever the epilogue
+    assert igc.conv2d_fwd_epilogue(X, W, Y, activation=7, **BASE) == 0
+    assert igc.conv2d_fwd_epilogue(X, W, Y, scale=Y, **BASE) == 0
+    assert igc.conv2d_fwd_epilogue(X, W, Y, bias=SC, activation="relu",
+                                   **{**BASE, "stride": 3}) == 0
+    assert igc.conv2d_fwd_nk_epilogue(X, W, BASE["filt_shape"], Y, filter_is_fcrs=False,
+                                      stride=1, padding=1, dtype=0, bias=BI + 2,
+                                      in_shape=BASE["in_shape"],
+                                      out_shape=BASE["out_shape"]) == 0
+    # empty output with a valid epilogue: handled, nothing launched
+    args = dict(BASE, in_shape=(0, 9, 9, 32), out_shape=(0, 9, 9, 48))
+    assert igc.conv2d_fwd_epilogue(X, W, Y, scale=SC, activation="silu", **args) == 1

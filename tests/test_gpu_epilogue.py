@@ -1,0 +1,131 @@
+"""GPU parity of the fused per-channel epilogue
+    D = act(scale[co] * conv + bias[co] + beta * source)
+through conv2d_fwd_epilogue / conv2d_fwd_nk_epilogue, against the fp64
+oracle (oracle.conv2d_epilogue), on one case per kernel variant the
+dispatcher can pick.  Tolerances as for the plain convolution: the epilogue
+adds a few fp32 operations before the single rounding to the output type.
+"""
+import os
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import implicit_gemm_nhwc_amd as igc
+import oracle
+from test_gpu_parity import PATH_CASES, TOL, _KERNEL, _assert_close, _sample_pixels
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def setup_module(_):
+    if not os.path.exists(igc.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _coefs(f, seed):
+    g = torch.Generator().manual_seed(seed)
+    scale = (torch.rand(f, generator=g) * 3.0 - 1.5).to(torch.float32)
+    bias = torch.randn(f, generator=g).to(torch.float32)
+    return scale, bias
+
+
+def _out(x, f, ho, wo):
+    return torch.empty((x.shape[0], ho, wo, f), dtype=datagen.OUT_DTYPES[str(x.dtype)[6:]],
+                       device=DEV)
+
+
+@pytest.mark.parametrize("act", ["relu", "silu"])
+@pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: c[0])
+def test_epilogue_kernel_paths(case, act):
+    cid, dt, n, h, w, c, f, r, s, st, p, resid, kern = case
+    ho, wo = oracle.out_size(h, r, st, p), oracle.out_size(w, s, st, p)
+    _say(f"epilogue {act} {cid}: {dt} N{n} {h}x{w} C{c}->{f} {r}x{s} st{st} p{p} "
+         f"residual={resid}")
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype=dt, fcrs=False,
+                                   x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0) if resid else None,
+                                   out_hw=(ho, wo), seed=zlib.crc32(cid.encode()) % 1000)
+    assert igc.conv2d_fwd_kernel_name(x.shape, wt.shape, (n, ho, wo, f), filter_is_fcrs=False,
+                                      dtype=x.dtype, stride=st, padding=p) == _KERNEL[kern]
+    scale, bias = _coefs(f, zlib.crc32((cid + act).encode()) % 1000)
+    beta = 0.5 if resid else 0.0
+    out = _out(x, f, ho, wo)
+    rc = igc.conv2d_fwd_epilogue(x.to(DEV), wt.to(DEV), out, filter_is_fcrs=False, stride=st,
+                                 padding=p, source=None if src is None else src.to(DEV),
+                                 beta=beta, scale=scale.to(DEV), bias=bias.to(DEV),
+                                 activation=act)
+    assert rc == 1, rc
+    torch.cuda.synchronize()
+    kw = dict(filter_is_fcrs=False, stride=st, padding=p, source=src, beta=beta,
+              scale=scale, bias=bias, act=act)
+    if n * ho * wo > 20000:
+        pix = _sample_pixels(n, ho, wo, 512, seed=13)
+        ref = oracle.conv2d_epilogue_points(x, wt, pix, **kw)
+        assert torch.isfinite(out.float()).all()
+        _assert_close(out.reshape(-1, f)[torch.as_tensor(pix, device=DEV)], ref, TOL[dt], cid)
+    else:
+        ref = oracle.conv2d_epilogue(x, wt, **kw)
+        _assert_close(out, ref, TOL[dt], cid)
+
+
+@pytest.mark.parametrize("f", [3, 20, 64, 130])
+def test_epilogue_partial_forms(f):
+    # scale only, bias only, activation only, and the no-op epilogue (equal in
+    # value to conv2d_fwd: fma(1, v, 0) may turn -0 into +0, so values, not bits)
+    n, h, w, c = 2, 14, 13, 32
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=3, S=3, dtype="bfloat16",
+                                   fcrs=True, x_dist=("normal", 1.0), w_dist=("normal", 0.2),
+                                   src_dist=("normal", 1.0), out_hw=(h, w), seed=f)
+    scale, bias = _coefs(f, 100 + f)
+    xd, wd, sd = x.to(DEV), wt.to(DEV), src.to(DEV)
+    plain = _out(x, f, h, w)
+    assert igc.conv2d_fwd(xd, wd, plain, filter_is_fcrs=True, stride=1, padding=1,
+                          source=sd, beta=-0.25) == 1
+    forms = [dict(scale=scale), dict(bias=bias), dict(activation="relu"),
+             dict(activation="silu", bias=bias),
+             dict(scale=torch.ones(f), bias=torch.zeros(f), activation="none")]
+    for kw in forms:
+        _say(f"epilogue form C_out={f}: {sorted(kw)}")
+        out = _out(x, f, h, w)
+        dev_kw = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in kw.items()}
+        assert igc.conv2d_fwd_epilogue(xd, wd, out, filter_is_fcrs=True, stride=1, padding=1,
+                                       source=sd, beta=-0.25, **dev_kw) == 1
+        torch.cuda.synchronize()
+        ref = oracle.conv2d_epilogue(x, wt, filter_is_fcrs=True, stride=1, padding=1,
+                                     source=src, beta=-0.25, scale=kw.get("scale"),
+                                     bias=kw.get("bias"), act=kw.get("activation", "none"))
+        _assert_close(out, ref, TOL["bfloat16"], str(sorted(kw)))
+        if "activation" in kw and kw["activation"] == "none":
+            assert torch.equal(out.float(), plain.float())
+
+
+def test_epilogue_nk_entry_matches_fwd():
+    n, h, w, c, f = 2, 16, 16, 64, 96
+    x, wt, _ = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=3, S=3, dtype="float16",
+                                 fcrs=False, x_dist=("normal", 1.0), w_dist=("normal", 0.1),
+                                 seed=21)
+    scale, bias = _coefs(f, 22)
+    xd, wd, scd, bid = x.to(DEV), wt.to(DEV), scale.to(DEV), bias.to(DEV)
+    a = _out(x, f, h, w)
+    assert igc.conv2d_fwd_epilogue(xd, wd, a, filter_is_fcrs=False, stride=1, padding=1,
+                                   scale=scd, bias=bid, activation="silu") == 1
+    nk = torch.empty(igc.conv2d_workspace_bytes(wt.shape, False, wt.dtype), dtype=torch.uint8,
+                     device=DEV)
+    assert igc.conv2d_filter_to_nk(wd, nk, filter_is_fcrs=False) == 1
+    b = _out(x, f, h, w)
+    assert igc.conv2d_fwd_nk_epilogue(xd, nk, wt.shape, b, filter_is_fcrs=False, stride=1,
+                                      padding=1, scale=scd, bias=bid, activation="silu",
+                                      dtype=1, in_shape=x.shape) == 1
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

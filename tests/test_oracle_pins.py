@@ -363,3 +363,114 @@ def test_gate_shape_rules():
     assert g((2, 8, 8, 16), (4, 16, 3, 3), (2, 8, 8, 4), filter_is_fcrs=True)
     assert not g((1, 1, 1, 16), (5, 5, 16, 4), (1, 0, 0, 4))        # filter > padded input
     assert g((0, 8, 8, 16), (3, 3, 16, 4), (0, 8, 8, 4))            # empty batch
+
+
+# ------------------------------------------------------ fused epilogue pins
+def _read_epilogue_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "epilogue_cases.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tag, *vals = line.split()
+            if tag == "case":
+                cur = dict(name=vals[0], dims=[int(v) for v in vals[1:10]],
+                           beta=float(vals[10]), act=vals[11])
+                cases.append(cur)
+            elif vals == ["none"]:
+                cur[tag] = None
+            else:
+                cur[tag] = np.array([float(v) for v in vals])
+    return cases
+
+
+@pytest.mark.parametrize("case", _read_epilogue_cases(), ids=lambda c: c["name"])
+def test_epilogue_handworked(case):
+    n, h, w, c, r, s, f, st, p = case["dims"]
+    x = case["x"].reshape(n, h, w, c)
+    wt = case["w"].reshape(r, s, c, f)
+    ho = (h + 2 * p - r) // st + 1
+    wo = (w + 2 * p - s) // st + 1
+    src = None if case["src"] is None else case["src"].reshape(n, ho, wo, f)
+    y = oracle.conv2d_epilogue(x, wt, filter_is_fcrs=False, stride=st, padding=p,
+                               source=src, beta=case["beta"], scale=case["scale"],
+                               bias=case["bias"], act=case["act"])
+    np.testing.assert_allclose(y.reshape(-1), case["y"], rtol=1e-15, atol=1e-15)
+
+
+def _small_problem(seed, fcrs=False, n=2, h=6, w=5, c=3, f=4, r=3, s=3):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((n, h, w, c))
+    wt = g.standard_normal((f, c, r, s) if fcrs else (r, s, c, f))
+    return x, wt
+
+
+@pytest.mark.parametrize("st,p", [(1, 0), (1, 1), (2, 1), (2, 2)])
+def test_epilogue_none_is_conv2d(st, p):
+    x, wt = _small_problem(1)
+    ho = (6 + 2 * p - 3) // st + 1
+    wo = (5 + 2 * p - 3) // st + 1
+    src = np.random.default_rng(2).standard_normal((2, ho, wo, 4))
+    for source, beta in ((None, 0.0), (src, -0.75)):
+        a = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p,
+                          source=source, beta=beta)
+        b = oracle.conv2d_epilogue(x, wt, filter_is_fcrs=False, stride=st, padding=p,
+                                   source=source, beta=beta)
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("st", [1, 2])
+def test_epilogue_bias_is_a_constant_input_channel(st):
+    # an extra input channel of ones whose only weight b[co] sits on the
+    # centre tap of a 3x3 filter at padding 1 (always inside the image) adds
+    # exactly b[co] to every output
+    x, wt = _small_problem(3)
+    bias = np.array([0.5, -1.25, 3.0, 0.0])
+    x1 = np.concatenate([x, np.ones(x.shape[:3] + (1,))], axis=3)
+    w1 = np.concatenate([wt, np.zeros((3, 3, 1, 4))], axis=2)
+    w1[1, 1, 3, :] = bias
+    want = oracle.conv2d(x1, w1, filter_is_fcrs=False, stride=st, padding=1)
+    got = oracle.conv2d_epilogue(x, wt, filter_is_fcrs=False, stride=st, padding=1,
+                                 bias=bias)
+    assert _rel(got, want) < 1e-13
+
+
+@pytest.mark.parametrize("fcrs", [False, True])
+def test_epilogue_scale_folds_into_filter(fcrs):
+    # scale[co] * conv(x, w) == conv(x, w with output channel co scaled)
+    x, wt = _small_problem(4, fcrs=fcrs)
+    scale = np.array([2.0, -0.5, 0.0, 1.5])
+    wf = wt * (scale[:, None, None, None] if fcrs else scale[None, None, None, :])
+    want = oracle.conv2d(x, wf, filter_is_fcrs=fcrs, stride=1, padding=1)
+    got = oracle.conv2d_epilogue(x, wt, filter_is_fcrs=fcrs, stride=1, padding=1,
+                                 scale=scale)
+    assert _rel(got, want) < 1e-13
+
+
+def test_activation_identities():
+    v = np.random.default_rng(5).standard_normal(1000) * 8
+    r = oracle.activation(v, "relu")
+    assert np.all(r >= 0)
+    np.testing.assert_array_equal(r - oracle.activation(-v, "relu"), v)
+    si = oracle.activation(v, "silu")
+    # sigmoid(v) + sigmoid(-v) = 1, so silu(v) - silu(-v) = v
+    assert np.max(np.abs(si - oracle.activation(-v, "silu") - v)) < 1e-12 * np.max(np.abs(v))
+    big = oracle.activation(np.array([-800.0, -40.0, 40.0]), "silu")
+    assert big[0] == 0.0 and abs(big[1]) < 1e-15 and abs(big[2] - 40.0) < 1e-15
+    np.testing.assert_array_equal(oracle.activation(v, "none"), v)
+    with pytest.raises(ValueError):
+        oracle.activation(v, "gelu")
+
+
+def test_epilogue_points_equal_full():
+    x, wt = _small_problem(6)
+    src = np.random.default_rng(7).standard_normal((2, 6, 5, 4))
+    sc, bi = np.array([1.5, -2.0, 0.25, 1.0]), np.array([0.0, 1.0, -1.0, 0.5])
+    full = oracle.conv2d_epilogue(x, wt, filter_is_fcrs=False, stride=1, padding=1,
+                                  source=src, beta=0.5, scale=sc, bias=bi, act="silu")
+    pix = [0, 7, 29, 59, 31]
+    pts = oracle.conv2d_epilogue_points(x, wt, pix, filter_is_fcrs=False, stride=1,
+                                        padding=1, source=src, beta=0.5, scale=sc, bias=bi,
+                                        act="silu")
+    np.testing.assert_array_equal(pts, full.reshape(-1, 4)[pix])
