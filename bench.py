@@ -20,7 +20,10 @@ Also reported on the same line:
                 (queued behind a spin kernel), against the MI355X peak;
   cpu_baseline  the fp64 oracle timed on this host's cores on the same
                 workload (the full batch);
-  shapes        the same measurement for each of the five named workloads.
+  shapes        the same measurement for each of the five named workloads;
+  next          the fused per-channel epilogue's cost on the headline layer,
+                and the materialised im2col + GEMM route against the fused
+                kernel on the two memory-bound layers.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -185,6 +188,112 @@ def kernel_times(torch, igc, bufs, launches):
     return e0.elapsed_time(e1) / launches
 
 
+def event_time(torch, fn, launches):
+    """Mean duration of fn(i) (launches on the current stream) from HIP events
+    around `launches` back-to-back calls, queued behind a spin kernel as in
+    kernel_times."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * (0.002 + 80e-6 * launches)))
+    e0.record(stream)
+    for i in range(launches):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / launches * 1e3   # us
+
+
+def _ok(rc, what):
+    if rc != 1:
+        raise RuntimeError(f"{what} returned {rc}")
+
+
+def measure_next(torch, igc, launches, rotate_bytes=ROTATE_BYTES):
+    """The rows past the core path, on cold rotating buffer sets:
+      epilogue  the headline layer's GEMM kernel with the fused per-channel
+                scale, bias and ReLU, against the same kernel without them;
+      im2col    the write-then-GEMM route on the two memory-bound layers: the
+                im2col kernel, the GEMM on the materialised matrix (a 1x1
+                convolution), and both back to back, against the fused kernel.
+    Times in us from HIP events around back-to-back launches."""
+    import datagen
+
+    out = {}
+    spec, x, w, src = datagen.make_workload(HEADLINE)
+    bufs = Bufsets(torch, igc, spec, x, w, src, rotate_bytes)
+    for i in range(bufs.nsets):
+        bufs.step(igc, i)
+    f = spec["F"]
+    g = torch.Generator().manual_seed(0)
+    scale = (torch.rand(f, generator=g) + 0.5).to("cuda:0")
+    bias = torch.randn(f, generator=g).to("cuda:0")
+
+    def epi(i):
+        b = bufs.sets[i % bufs.nsets]
+        _ok(igc.conv2d_fwd_nk_epilogue(b["x"], b["nk"], b["w"].shape, b["y"],
+                                       filter_is_fcrs=bufs.fcrs, stride=spec["stride"],
+                                       padding=spec["pad"], scale=scale, bias=bias,
+                                       activation="relu"), "conv2d_fwd_nk_epilogue")
+    for i in range(3):
+        epi(i)
+    plain = kernel_times(torch, igc, bufs, launches) * 1e3
+    fused = event_time(torch, epi, launches)
+    out["epilogue"] = {"workload": HEADLINE, "fused": "scale, bias, relu",
+                       "kernel_us": round(fused, 3), "plain_kernel_us": round(plain, 3),
+                       "extra_us": round(fused - plain, 3)}
+    del bufs
+    torch.cuda.empty_cache()
+
+    abl = {}
+    for name in ("resnet_3x3_64c_n32", "rgb_3x3_128to3_512px"):
+        spec, x, w, src = datagen.make_workload(name)
+        bufs = Bufsets(torch, igc, spec, x, w, src, rotate_bytes)
+        for i in range(bufs.nsets):
+            bufs.step(igc, i)
+        r, s_, c = spec["R"], spec["S"], spec["C"]
+        kp = igc.im2col_row_elems(r, s_, c, x.dtype)
+        nbytes = igc.conv2d_im2col_bytes(x.shape, r, s_, stride=spec["stride"],
+                                         padding=spec["pad"], dtype=x.dtype)
+        a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        n, (ho, wo) = spec["N"], spec["out_hw"]
+
+        def im2col(i):
+            b = bufs.sets[i % bufs.nsets]
+            _ok(igc.conv2d_im2col(b["x"], r, s_, a, stride=spec["stride"],
+                                  padding=spec["pad"]), "conv2d_im2col")
+
+        def gemm(i):
+            b = bufs.sets[i % bufs.nsets]
+            _ok(igc.conv2d_fwd_nk(a, b["nk"], (spec["F"], kp, 1, 1), b["y"],
+                                  filter_is_fcrs=True, stride=1, padding=0, source=b["src"],
+                                  beta=spec["beta"], dtype=igc.dtype_code(x.dtype),
+                                  in_shape=(n, ho, wo, kp)), "conv2d_fwd_nk (1x1 view)")
+
+        def route(i):
+            im2col(i)
+            gemm(i)
+        route(0)
+        torch.cuda.synchronize()
+        fused = kernel_times(torch, igc, bufs, launches) * 1e3
+        t_i = event_time(torch, im2col, launches)
+        t_g = event_time(torch, gemm, launches)
+        t_r = event_time(torch, route, launches)
+        in_bytes = x.numel() * x.element_size()
+        abl[name] = {"fused_kernel_us": round(fused, 3), "im2col_us": round(t_i, 3),
+                     "gemm_on_matrix_us": round(t_g, 3), "route_us": round(t_r, 3),
+                     "route_over_fused": round(t_r / fused, 3),
+                     "matrix_bytes": nbytes,
+                     "im2col_gbs": round((nbytes + in_bytes) / (t_i * 1e-6) / 1e9, 1),
+                     "gemm_kernel": igc.conv2d_fwd_kernel_name(
+                         (n, ho, wo, kp), (spec["F"], kp, 1, 1), (n, ho, wo, spec["F"]),
+                         filter_is_fcrs=True, dtype=x.dtype, stride=1, padding=0)}
+        del bufs, a
+        torch.cuda.empty_cache()
+    out["im2col_ablation"] = abl
+    return out
+
+
 def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES, graphs=True):
     """Timed loop: `steps` steps as replays of the captured step graphs
     (eager steps with graphs=False), bracketed by synchronizations, after
@@ -272,6 +381,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-workload table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the fused-epilogue and im2col-ablation measurements")
     ap.add_argument("--only", default=None,
                     help="run only this workload's timed loop (for profiling); prints one line")
     ap.add_argument("--rotate-mib", type=int, default=ROTATE_BYTES >> 20,
@@ -351,6 +462,10 @@ def main():
                   f"({100 * r['frac_hbm']:.1f}% HBM), bound {r['bound']}",
                   file=sys.stderr, flush=True)
 
+    nxt = None
+    if not args.no_next:
+        nxt = measure_next(torch, igc, max(10, args.steps // 2), rotate)
+        print(f"# next rows: {json.dumps(nxt)}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(spec, x, w)
     line = {
         "metric": "conv2d fwd TFLOP/s per shape + % of MFMA peak (or % HBM BW if memory-bound)",
@@ -374,6 +489,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "shapes": shapes,
+        "next": nxt,
     }
     print(json.dumps(line), flush=True)
 

@@ -10,9 +10,13 @@ call is declined, these functions say so instead of computing anything.
 Names mirror the C entry points:
   conv2d_fwd, conv2d_fwd_check, conv2d_fwd_nk, conv2d_filter_to_nk,
   conv2d_fwd_epilogue, conv2d_fwd_nk_epilogue, conv2d_epilogue_check,
+  conv2d_im2col, conv2d_im2col_bytes,
   conv2d_fwd_kernel_name, conv2d_workspace_bytes, conv2d_nk_row_pitch,
   conv2d_reason_string, conv2d_abi_version
-plus conv2d(), which allocates the output and calls conv2d_fwd_epilogue.
+plus conv2d(), which allocates the output and calls conv2d_fwd_epilogue, and
+conv2d_materialized(), the write-then-GEMM route (conv2d_filter_to_nk,
+conv2d_im2col, conv2d_fwd_nk on the 1x1 view) kept for measuring what the
+fused gather saves.
 """
 import ctypes
 import os
@@ -89,6 +93,11 @@ def lib():
     L.conv2d_fwd_nk_epilogue.restype = i32
     L.conv2d_epilogue_check.argtypes = [epip, vp, i64p]
     L.conv2d_epilogue_check.restype = i32
+    i64p2 = ctypes.POINTER(ctypes.c_int64)
+    L.conv2d_im2col.argtypes = [vp, i64p, i64p2, i32p, i32p, i32, vp, sz, vp]
+    L.conv2d_im2col.restype = i32
+    L.conv2d_im2col_bytes.argtypes = [i64p, i64p2, i32p, i32p, i32]
+    L.conv2d_im2col_bytes.restype = sz
     _lib = L
     return L
 
@@ -263,6 +272,60 @@ def conv2d_filter_to_nk(filter, nk, *, filter_is_fcrs, stream=None, dtype=None,
     return lib().conv2d_filter_to_nk(_ptr(filter), int(bool(filter_is_fcrs)),
                                      _i64(filt_shape), int(code), _ptr(nk), int(nk_bytes),
                                      _stream(stream, nk))
+
+
+def _rs(r, s):
+    return (ctypes.c_int64 * 2)(int(r), int(s))
+
+
+def conv2d_im2col_bytes(in_shape, r, s, *, stride=1, padding=0, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(lib().conv2d_im2col_bytes(_i64(in_shape), _rs(r, s), _pair(stride),
+                                         _pair(padding), int(code)))
+
+
+def conv2d_im2col(input, r, s, a_out, *, stride=1, padding=0, stream=None, dtype=None,
+                  in_shape=None, a_bytes=None) -> int:
+    """Enqueue the materialised im2col of input into a_out (rows of Kp
+    elements).  1 enqueued, 0 declined, < 0 HIP error."""
+    in_shape = input.shape if in_shape is None else in_shape
+    code = dtype_code(input.dtype) if dtype is None else dtype
+    if a_bytes is None:
+        a_bytes = a_out.numel() * a_out.element_size()
+    return lib().conv2d_im2col(_ptr(input), _i64(in_shape), _rs(r, s), _pair(stride),
+                               _pair(padding), int(code), _ptr(a_out), int(a_bytes),
+                               _stream(stream, a_out))
+
+
+def im2col_row_elems(r, s, c, dtype) -> int:
+    """Kp: K = R*S*C_in rounded up to a multiple of 128 bytes."""
+    per = 128 // (1 if dtype == torch.float8_e4m3fn else 2)
+    k = r * s * c
+    return (k + per - 1) // per * per
+
+
+def conv2d_materialized(input, filter, output, nk, a_buf, *, filter_is_fcrs, stride=1,
+                        padding=0, source=None, beta=0.0, stream=None, transpose=True):
+    """The write-then-GEMM route: filter -> NK (unless transpose=False and nk
+    already holds it), input -> im2col matrix a_buf, then the 1x1 stride-1
+    convolution of a_buf viewed as [N, Ho, Wo, Kp] with the same NK matrix.
+    Returns the first nonzero-but-not-1 code, or 1."""
+    if filter_is_fcrs:
+        f, c, r, s = filter.shape
+    else:
+        r, s, c, f = filter.shape
+    n, ho, wo, _ = output.shape
+    kp = im2col_row_elems(r, s, c, input.dtype)
+    if transpose:
+        rc = conv2d_filter_to_nk(filter, nk, filter_is_fcrs=filter_is_fcrs, stream=stream)
+        if rc != 1:
+            return rc
+    rc = conv2d_im2col(input, r, s, a_buf, stride=stride, padding=padding, stream=stream)
+    if rc != 1:
+        return rc
+    return conv2d_fwd_nk(a_buf, nk, (f, kp, 1, 1), output, filter_is_fcrs=True, stride=1,
+                         padding=0, source=source, beta=beta, stream=stream,
+                         dtype=dtype_code(input.dtype), in_shape=(n, ho, wo, kp))
 
 
 def out_hw(h, w, r, s, stride, padding):

@@ -548,9 +548,87 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
     }
 }
 
+FastDiv make_fastdiv(uint32_t d) {
+    uint32_t sh = 0;
+    while (sh < 31 && ((uint64_t)1 << sh) < d) ++sh;
+    const uint64_t m = (((uint64_t)1 << (32 + sh)) + d - 1) / d;
+    return FastDiv{(uint32_t)(m - ((uint64_t)1 << 32)), sh};
+}
+
+// Shapes of the materialised im2col: the convolution gate applied to a
+// filter of R x S taps (C_out plays no part), plus the 16-byte vector count
+// below 2^31.  Row pitch Kp: K rounded up to whole 128-byte k-tiles.
+int32_t im2col_shape(const int64_t in_nhwc[4], const int64_t filt_rs[2],
+                     const int32_t stride[2], const int32_t padding[2], int32_t dtype,
+                     Shape* sh, int64_t* kp) {
+    if (!in_nhwc || !filt_rs) return IGC_DECLINE_NULL_POINTER;
+    const int64_t fd[4] = {filt_rs[0], filt_rs[1], in_nhwc[3], 1};
+    const int32_t dil[2] = {1, 1};
+    const int64_t eb = elem_bytes(dtype);
+    // Ho, Wo as the gate computes them (a first pass fills the shape)
+    Shape s{};
+    int64_t od[4] = {in_nhwc[0], 1, 1, 1};
+    if (stride && padding && filt_rs[0] >= 1 && filt_rs[1] >= 1 && stride[0] >= 1 &&
+        stride[1] >= 1) {
+        od[1] = out_size(in_nhwc[1], filt_rs[0], stride[0], padding[0]);
+        od[2] = out_size(in_nhwc[2], filt_rs[1], stride[1], padding[1]);
+    }
+    const int32_t rc = check_shapes(in_nhwc, 0, fd, od, stride, dil, padding, 1, dtype, &s);
+    if (rc != IGC_OK) return rc;
+    if ((s.M * s.kpad * eb) / 16 >= ((int64_t)1 << 31)) return IGC_DECLINE_SIZE_LIMIT;
+    *sh = s;
+    *kp = s.kpad;
+    return IGC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t conv2d_im2col_bytes(const int64_t in_nhwc[4], const int64_t filt_rs[2],
+                           const int32_t stride[2], const int32_t padding[2], int32_t dtype) {
+    Shape s;
+    int64_t kp;
+    if (im2col_shape(in_nhwc, filt_rs, stride, padding, dtype, &s, &kp) != IGC_OK) return 0;
+    return (size_t)(s.M * kp * elem_bytes(dtype));
+}
+
+int32_t conv2d_im2col(const void* input, const int64_t in_nhwc[4], const int64_t filt_rs[2],
+                      const int32_t stride[2], const int32_t padding[2], int32_t dtype,
+                      void* a_out, size_t a_bytes, void* stream) {
+    Shape s;
+    int64_t kp;
+    if (im2col_shape(in_nhwc, filt_rs, stride, padding, dtype, &s, &kp) != IGC_OK) return 0;
+    const int64_t eb = elem_bytes(dtype);
+    const size_t need = (size_t)(s.M * kp * eb);
+    const size_t in_bytes = (size_t)(s.N * s.H * s.W * s.C * eb);
+    if (a_bytes < need) return 0;
+    if ((need && !a_out) || (in_bytes && !input)) return 0;
+    if (!aligned16(input) || !aligned16(a_out)) return 0;
+    if (overlaps(a_out, need, input, in_bytes)) return 0;
+    if (need == 0) return 1;
+    Im2colArgs a{};
+    a.x = (const uint8_t*)input;
+    a.a = (uint8_t*)a_out;
+    a.H = (int)s.H; a.W = (int)s.W; a.Ho = (int)s.Ho; a.Wo = (int)s.Wo;
+    a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
+    a.RS = (int)(s.R * s.S);
+    a.CB = (int)(s.C * eb);
+    a.VPR = (uint32_t)(kp * eb / 16);
+    a.CV = (uint32_t)(s.C * eb / 16);
+    a.total = (uint32_t)(s.M * a.VPR);
+    a.HoWo = (uint32_t)(s.Ho * s.Wo);
+    // need > 0, so M, C_in and hence VPR and CV are at least 1
+    a.d_vpr = make_fastdiv(a.VPR);
+    a.d_cv = make_fastdiv(a.CV);
+    a.d_s = make_fastdiv((uint32_t)s.S);
+    a.d_howo = make_fastdiv(a.HoWo);
+    a.d_wo = make_fastdiv((uint32_t)s.Wo);
+    const uint32_t blocks = (a.total + 255) / 256 < 4096u ? (a.total + 255) / 256 : 4096u;
+    hipLaunchKernelGGL(im2col_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, a);
+    return hip_fail(hipGetLastError());
+}
+
 
 int32_t conv2d_abi_version(void) { return kAbiVersion; }
 

@@ -114,22 +114,48 @@ __device__ __forceinline__ float out_to_f32(uint16_t bits, int dt) {
 // offers a fixed one, per output channel co:
 //   v = scale[co] * acc + bias[co];  v += beta * src;  v = act(v)
 // then the single rounding to the output type.  scale / bias may be null
-// (1 / 0).  Channels co >= C_out are never stored, so their coefficients are
-// not read.
+// (1 / 0).
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_SILU = 2 };
 
+// The coefficients are read through buffer descriptors: a null array gets
+// an empty range and channels co >= C_out fall outside it, and such loads
+// return 0 without touching memory, so no load needs a branch.
 __device__ __forceinline__ float epi_pre(const ConvArgs& a, int co, float v) {
-    const bool ok = co < a.F;
-    const float sc = (a.scale != nullptr && ok) ? a.scale[co] : 1.0f;
-    const float bi = (a.bias != nullptr && ok) ? a.bias[co] : 0.0f;
-    return __builtin_fmaf(sc, v, bi);
+    const int nb = a.F * 4;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.scale), (short)0, a.scale ? nb : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.bias), (short)0, a.bias ? nb : 0, 0x00020000);
+    const float sc = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(srs, (unsigned)co * 4u, 0, 0));
+    const float bi = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(brs, (unsigned)co * 4u, 0, 0));
+    return __builtin_fmaf(a.scale ? sc : 1.0f, v, bi);
 }
 
-// ReLU keeps v when v > 0, else +0; SiLU is v * sigmoid(v) = v / (1 + e^-v).
+// The scale and bias of channel co (1 and 0 when absent), for hoisting out
+// of unrolled loops; v = fma(sc, acc, bi) is then epi_pre's value.
+__device__ __forceinline__ void epi_coef(const ConvArgs& a, int co, float* sc, float* bi) {
+    const int nb = a.F * 4;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.scale), (short)0, a.scale ? nb : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.bias), (short)0, a.bias ? nb : 0, 0x00020000);
+    const float s = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(srs, (unsigned)co * 4u, 0, 0));
+    *sc = a.scale ? s : 1.0f;
+    *bi = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(brs, (unsigned)co * 4u, 0, 0));
+}
+
+// ReLU keeps v when v > 0, else +0; SiLU is v * sigmoid(v) = v / (1 + e^-v),
+// here v times the hardware reciprocal (about 1 ulp) of 1 + e^-v: a few
+// instructions instead of an IEEE division, far below the output rounding.
+// Selects, not branches.
 __device__ __forceinline__ float epi_act(const ConvArgs& a, float v) {
-    if (a.act == ACT_RELU) return v > 0.0f ? v : 0.0f;
-    if (a.act == ACT_SILU) return v / (1.0f + __expf(-v));
-    return v;
+    const float relu = v > 0.0f ? v : 0.0f;
+    const float silu = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+    return a.act == ACT_RELU ? relu : (a.act == ACT_SILU ? silu : v);
 }
 
 template <int DT>
@@ -1406,6 +1432,10 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
     uint8_t* ereg = lds + wave * 32 * EP;
     const int c4 = lane % LPP, pl = lane / LPP;
     const int co = co0 + wco * WCH + c4 * 4;     // this lane's first channel
+    // the fused epilogue's coefficients of this lane's four channels
+    float esc[4], ebi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) epi_coef(a, co + e, &esc[e], &ebi[e]);
     auto stage_block = [&](int j) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -1448,7 +1478,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 float v[4] = {v4[0], v4[1], v4[2], v4[3]};
                 if (a.epi) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = epi_pre(a, co + e, v[e]);
+                    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(esc[e], v[e], ebi[e]);
                 }
                 if constexpr (RESID) {
 #pragma unroll
@@ -1483,7 +1513,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 for (int e = 0; e < 4; ++e) {
                     if (co + e < a.F) {
                         float d = v4[e];
-                        if (a.epi) d = epi_pre(a, co + e, d);
+                        if (a.epi) d = __builtin_fmaf(esc[e], d, ebi[e]);
                         if constexpr (RESID) d = __builtin_fmaf(a.beta, out_to_f32(a.src[o + e], ODT), d);
                         if (a.epi) d = epi_act(a, d);
                         a.y[o + e] = f32_to_out(d, ODT);
@@ -1491,6 +1521,63 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 }
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Materialised im2col (page "dispatch_fused_im2col_conv2d_apple", summary:
+// the [M, K] patch matrix the fused path never writes), for comparing the
+// fused gather against the write-then-GEMM route on the same MFMA kernels:
+//   A[m][k] = x[n, oh*st - p + r, ow*st - p + s, ci]   (0 in the padding)
+//   m = (n*Ho + oh)*Wo + ow,  k = (r*S + s)*C_in + ci,  rows of Kp elements
+// (K rounded up to whole 128-byte k-tiles, zero past K).  Read as an NHWC
+// tensor [N, Ho, Wo, Kp], A is the input of a 1x1, stride-1 convolution
+// whose NK matrix is the original filter's.
+//
+// One thread per 16-byte vector of A, grid-stride; a vector is VEC channels
+// of one tap (C_in * E % 16 == 0).  Stores are fully coalesced; loads are
+// contiguous within a tap's channels.  Divisions by runtime constants use
+// multiply-high magic numbers made on the host.
+struct FastDiv {
+    uint32_t mul;    // ceil(2^(32+shift) / d) - 2^32
+    uint32_t shift;  // ceil(log2(d))
+};
+
+// floor(n / d) for 0 <= n < 2^31: with m = ceil(2^(32+s) / d), s = ceil(log2 d),
+// n * m / 2^(32+s) exceeds n / d by less than n / 2^(32+s) < 1/d, which never
+// reaches the next integer.
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv d) {
+    return (__umulhi(n, d.mul) + n) >> d.shift;
+}
+
+struct Im2colArgs {
+    const uint8_t* x;
+    uint8_t* a;
+    int H, W, Ho, Wo, S, stride, pad;
+    int RS;             // taps
+    int CB;             // bytes per input pixel (C_in * E)
+    uint32_t total;     // 16-byte vectors of A: M * VPR
+    uint32_t VPR, CV;   // vectors per A row; per tap
+    uint32_t HoWo;
+    FastDiv d_vpr, d_cv, d_s, d_howo, d_wo;
+};
+
+__global__ __launch_bounds__(256) void im2col_kernel(Im2colArgs a) {
+    const uint32_t step = gridDim.x * 256u;
+    for (uint32_t g = blockIdx.x * 256u + threadIdx.x; g < a.total; g += step) {
+        const uint32_t m = fast_div(g, a.d_vpr), j = g - m * a.VPR;
+        const uint32_t tap = fast_div(j, a.d_cv), cv = j - tap * a.CV;
+        i32x4 v = {0, 0, 0, 0};
+        if (tap < (uint32_t)a.RS) {
+            const int r = (int)fast_div(tap, a.d_s), s = (int)tap - r * a.S;
+            const uint32_t n = fast_div(m, a.d_howo), rem = m - n * a.HoWo;
+            const int oh = (int)fast_div(rem, a.d_wo), ow = (int)rem - oh * a.Wo;
+            const int ih = oh * a.stride - a.pad + r, iw = ow * a.stride - a.pad + s;
+            if ((unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W)
+                v = *reinterpret_cast<const i32x4*>(
+                    a.x + (((int64_t)n * a.H + ih) * a.W + iw) * a.CB + cv * 16);
+        }
+        *reinterpret_cast<i32x4*>(a.a + (int64_t)g * 16) = v;
     }
 }
 

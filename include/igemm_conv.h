@@ -259,6 +259,34 @@ int32_t conv2d_fwd_nk_epilogue(const void* input, const int64_t in_nhwc[4],
 int32_t conv2d_epilogue_check(const igc_epilogue* epilogue, const void* output,
                               const int64_t out_nhwc[4]);
 
+/*
+ * Materialised im2col, for measuring what the fused gather saves (page
+ * "dispatch_fused_im2col_conv2d_apple", summary: the fused kernel gathers
+ * the [M, K] patch matrix on the fly instead of writing it to memory and
+ * running a GEMM over it).  Writes
+ *   A[m][k] = x[n, oh*st - p + r, ow*st - p + s, ci]   (0 in the padding)
+ * with m = (n*Ho + oh)*Wo + ow and k = (r*S + s)*C_in + ci, in rows of Kp
+ * elements: K = R*S*C_in rounded up to a multiple of 128 bytes, zero past K.
+ * A bit copy of the input's elements.  filt_rs = {R, S}; the shape rules
+ * (dtype, stride, padding, Ho/Wo >= 1, C_in * element bytes % 16 == 0) are
+ * conv2d_fwd's.  a_out: device memory of at least conv2d_im2col_bytes(),
+ * 16-byte aligned, not overlapping the input.
+ * Read as an NHWC tensor [N, Ho, Wo, Kp], A is the input of a 1x1, stride-1,
+ * padding-0 convolution whose NK matrix is the one conv2d_filter_to_nk makes
+ * from the original filter: conv2d_fwd_nk with in_nhwc = {N, Ho, Wo, Kp} and
+ * FCRS filt_dims = {C_out, Kp, 1, 1} then computes the same convolution.
+ * Returns 1 = enqueued (or nothing to do), 0 = declined, or -(hipError_t).
+ */
+int32_t conv2d_im2col(const void* input, const int64_t in_nhwc[4],
+                      const int64_t filt_rs[2], const int32_t stride[2],
+                      const int32_t padding[2], int32_t dtype,
+                      void* a_out, size_t a_bytes, void* stream);
+
+/* Bytes of the im2col matrix: N*Ho*Wo*Kp elements; 0 if declined. */
+size_t conv2d_im2col_bytes(const int64_t in_nhwc[4], const int64_t filt_rs[2],
+                           const int32_t stride[2], const int32_t padding[2],
+                           int32_t dtype);
+
 #ifdef __cplusplus
 }
 #endif

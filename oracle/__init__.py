@@ -21,6 +21,9 @@ Parity status of each function (what pins it is in tests/test_oracle_pins.py):
                           filter, textbook sigmoid values, relu's sign split.
   filter_to_nk           pinned: element-wise brute force from the index
                           formula on small filters.
+  im2col                 pinned: pure-Python brute force on tiny shapes,
+                          im2col(x) @ filter_to_nk(w)^T equals conv2d,
+                          zero columns past K.
   gate_accepts           pinned: hand-written case table from page 1's
                           Parameters/Args rules (tests/golden/gate_cases.txt).
 """
@@ -35,6 +38,7 @@ from .reference import (  # noqa: F401
     filter_dims_rscf,
     filter_to_nk,
     gate_accepts,
+    im2col,
     num_threads,
     out_size,
 )

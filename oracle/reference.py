@@ -216,6 +216,36 @@ def filter_to_nk(w: torch.Tensor, filter_is_fcrs: bool, k_pad: int = None) -> to
     return nk.contiguous().view(w.dtype)
 
 
+def im2col(x, r: int, s: int, *, stride=1, padding=0, k_pad: int = None) -> torch.Tensor:
+    """The [M, K] patch matrix of page 2 ("dispatch_fused_im2col_conv2d_apple",
+    summary: the matrix the fused kernel gathers on the fly instead of
+    materialising), as a bit copy of the input's elements:
+        A[(n*Ho + oh)*Wo + ow, (rr*S + ss)*C_in + ci]
+            = x[n, oh*st - p + rr, ow*st - p + ss, ci],  0 outside the image
+    k ordered (r, s, ci) with ci fastest, the order of filter_to_nk.
+    Columns K..k_pad-1 (when k_pad > K) are zero.  Returns a CPU tensor
+    [M, max(K, k_pad)] of x's dtype.
+    """
+    sh, sw = (stride, stride) if isinstance(stride, int) else stride
+    ph, pw = (padding, padding) if isinstance(padding, int) else padding
+    bits = x.detach().cpu().contiguous()
+    bits = bits.view(torch.int16) if bits.element_size() == 2 else bits.view(torch.uint8)
+    n, h, w, c = bits.shape
+    ho, wo = out_size(h, r, sh, ph), out_size(w, s, sw, pw)
+    padded = torch.zeros((n, h + 2 * ph, w + 2 * pw, c), dtype=bits.dtype)
+    padded[:, ph:ph + h, pw:pw + w, :] = bits
+    cols = []
+    for rr in range(r):
+        for ss in range(s):
+            win = padded[:, rr:rr + sh * (ho - 1) + 1:sh, ss:ss + sw * (wo - 1) + 1:sw, :]
+            cols.append(win.reshape(n * ho * wo, c))
+    a = torch.cat(cols, dim=1) if cols else torch.zeros((n * ho * wo, 0), dtype=bits.dtype)
+    k = r * s * c
+    if k_pad is not None and k_pad > k:
+        a = torch.cat([a, torch.zeros((a.shape[0], k_pad - k), dtype=a.dtype)], dim=1)
+    return a.contiguous().view(x.dtype)
+
+
 def gate_accepts(dtype: str, filter_dtype: str, out_dtype: str, in_nhwc,
                  filt_dims, filter_is_fcrs: bool, out_nhwc, stride, dilation,
                  padding, groups) -> bool:

@@ -236,3 +236,29 @@ def test_epilogue_declined_call_enqueues_nothing():
     # empty output with a valid epilogue: handled, nothing launched
     args = dict(BASE, in_shape=(0, 9, 9, 32), out_shape=(0, 9, 9, 48))
     assert igc.conv2d_fwd_epilogue(X, W, Y, scale=SC, activation="silu", **args) == 1
+
+
+# --------------------------------------------------------- im2col ablation
+def test_im2col_bytes_and_declines():
+    # 2 x 9 x 9 x 32 bf16, 3x3 stride 1 pad 1: M = 162, K = 288 -> Kp = 320
+    assert igc.conv2d_im2col_bytes((2, 9, 9, 32), 3, 3, stride=1, padding=1,
+                                   dtype=torch.bfloat16) == 162 * 320 * 2
+    # fp8, 5x5 stride 2 pad 2 on 16 x 16 x 16: Ho = 8, K = 400 -> Kp = 512
+    assert igc.conv2d_im2col_bytes((1, 16, 16, 16), 5, 5, stride=2, padding=2,
+                                   dtype=torch.float8_e4m3fn) == 64 * 512
+    for kw in (dict(stride=3), dict(padding=3), dict(dtype=7)):
+        args = dict(stride=1, padding=1, dtype=torch.bfloat16)
+        args.update(kw)
+        assert igc.conv2d_im2col_bytes((2, 9, 9, 32), 3, 3, **args) == 0
+    assert igc.conv2d_im2col_bytes((2, 9, 9, 12), 3, 3, stride=1, padding=1,
+                                   dtype=torch.bfloat16) == 0        # vector width
+    lib = igc.lib()
+    call = lambda x, a, nb, st=1: lib.conv2d_im2col(  # noqa: E731
+        x, igc._i64((2, 9, 9, 32)), igc._rs(3, 3), igc._pair(st), igc._pair(1), 0, a, nb, None)
+    need = 162 * 320 * 2
+    assert call(X, WS, need - 1) == 0          # too small
+    assert call(X + 8, WS, need) == 0          # misaligned input
+    assert call(X, WS + 4, need) == 0          # misaligned output
+    assert call(X, X + 4096, need) == 0        # overlaps the input
+    assert call(X, 0, need) == 0               # null output
+    assert call(X, WS, need, st=3) == 0        # stride

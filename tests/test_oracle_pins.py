@@ -474,3 +474,43 @@ def test_epilogue_points_equal_full():
                                         padding=1, source=src, beta=0.5, scale=sc, bias=bi,
                                         act="silu")
     np.testing.assert_array_equal(pts, full.reshape(-1, 4)[pix])
+
+
+# ------------------------------------------------------------ im2col pins
+@pytest.mark.parametrize("n,h,w,c,r,s,st,p", [
+    (1, 4, 5, 2, 3, 3, 1, 1), (2, 5, 4, 1, 2, 3, 2, 0), (1, 6, 6, 3, 5, 5, 2, 2),
+    (1, 3, 3, 2, 1, 1, 1, 0), (2, 4, 4, 2, 3, 2, 1, 2)])
+def test_im2col_brute_force(n, h, w, c, r, s, st, p):
+    x = torch.randn(n, h, w, c, generator=torch.Generator().manual_seed(h * 7 + c),
+                    dtype=torch.float32).to(torch.bfloat16)
+    ho, wo = (h + 2 * p - r) // st + 1, (w + 2 * p - s) // st + 1
+    a = oracle.im2col(x, r, s, stride=st, padding=p, k_pad=r * s * c + 3)
+    assert tuple(a.shape) == (n * ho * wo, r * s * c + 3)
+    xv = x.float().tolist()
+    av = a.float().tolist()
+    for nn in range(n):
+        for oh in range(ho):
+            for ow in range(wo):
+                row = av[(nn * ho + oh) * wo + ow]
+                for rr in range(r):
+                    for ss in range(s):
+                        for ci in range(c):
+                            ih, iw = oh * st - p + rr, ow * st - p + ss
+                            want = xv[nn][ih][iw][ci] if 0 <= ih < h and 0 <= iw < w else 0.0
+                            assert row[(rr * s + ss) * c + ci] == want
+                assert row[r * s * c:] == [0.0, 0.0, 0.0]
+
+
+@pytest.mark.parametrize("fcrs", [False, True])
+@pytest.mark.parametrize("st,p", [(1, 1), (2, 1), (2, 2), (1, 0)])
+def test_im2col_times_nk_is_conv(fcrs, st, p):
+    # A (M x K) @ NK^T (K x C_out) is the convolution: the closed form the
+    # fused method computes without writing A
+    g = torch.Generator().manual_seed(31)
+    x = (torch.rand(2, 7, 6, 4, generator=g) * 2 - 1).to(torch.float16)
+    w = (torch.rand(*((5, 4, 3, 3) if fcrs else (3, 3, 4, 5)), generator=g) * 2 - 1).to(
+        torch.float16)
+    a = oracle.im2col(x, 3, 3, stride=st, padding=p).to(torch.float64).numpy()
+    nk = oracle.filter_to_nk(w, fcrs).to(torch.float64).numpy()
+    y = oracle.conv2d(x, w, filter_is_fcrs=fcrs, stride=st, padding=p)
+    np.testing.assert_allclose(a @ nk.T, y.reshape(-1, 5), rtol=1e-12, atol=1e-12)
