@@ -151,11 +151,22 @@ __device__ __forceinline__ void epi_coef(const ConvArgs& a, int co, float* sc, f
 // ReLU keeps v when v > 0, else +0; SiLU is v * sigmoid(v) = v / (1 + e^-v),
 // here v times the hardware reciprocal (about 1 ulp) of 1 + e^-v: a few
 // instructions instead of an IEEE division, far below the output rounding.
-// Selects, not branches.
+// The activation is uniform, so the branches are scalar, and the two
+// quarter-rate transcendentals run only for SiLU.
+template <int NV>
+__device__ __forceinline__ void epi_act_n(const ConvArgs& a, float* v) {
+    if (a.act == ACT_SILU) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) v[e] = v[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-v[e]));
+    } else if (a.act == ACT_RELU) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) v[e] = v[e] > 0.0f ? v[e] : 0.0f;
+    }
+}
+
 __device__ __forceinline__ float epi_act(const ConvArgs& a, float v) {
-    const float relu = v > 0.0f ? v : 0.0f;
-    const float silu = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
-    return a.act == ACT_RELU ? relu : (a.act == ACT_SILU ? silu : v);
+    epi_act_n<1>(a, &v);
+    return v;
 }
 
 template <int DT>
@@ -445,10 +456,7 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a.beta, out_to_f32(s[q], ODT), v[q]);
                 }
-                if (a.epi) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = epi_act(a, v[q]);
-                }
+                if (a.epi) epi_act_n<4>(a, v);
                 u16x4 o;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) o[q] = f32_to_out(v[q], ODT);
@@ -708,10 +716,7 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a.beta, out_to_f32(s[q], ODT), v[q]);
                 }
-                if (a.epi) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = epi_act(a, v[q]);
-                }
+                if (a.epi) epi_act_n<4>(a, v);
                 u16x4 o;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) o[q] = f32_to_out(v[q], ODT);
@@ -1010,6 +1015,30 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     const int th_n = min(a.TH, a.Ho - oh0);
     const int tw_n = min(a.TW, a.Wo - ow0);
     if ((a.F & 7) == 0) {
+        // the fused epilogue's coefficients of this lane's channels
+        // i*32 + 8*(2k + half) + 0..7, loaded once (16-byte buffer loads; the
+        // whole 8-channel group is inside C_out or outside it)
+        f32x4 esc[TM][2][2], ebi[TM][2][2];
+        if (a.epi) {
+            const int nb = a.F * 4;
+            const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.scale), (short)0, a.scale ? nb : 0, 0x00020000);
+            const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.bias), (short)0, a.bias ? nb : 0, 0x00020000);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const unsigned off = (unsigned)(i * 32 + 8 * (2 * k + half) + 4 * h) * 4u;
+                        const f32x4 sv = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0));
+                        esc[i][k][h] = a.scale ? sv : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+                        ebi[i][k][h] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
+                    }
+        }
         // ---- epilogue straight from the accumulators.  Lane l holds pixel
         // (l & 31) and channels 8g + 4h + 0..3 (h = l >> 5) of each 32-channel
         // block; swapping groups 2k and 2k+1 across the wave halves
@@ -1045,7 +1074,11 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
                     if (pix_ok & (co < a.F)) {
                         if (a.epi) {
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] = epi_pre(a, co + e, v[e]);
+                            for (int e = 0; e < 8; ++e) {
+                                const float sc = esc[i][k][e >> 2][e & 3];
+                                const float bi = ebi[i][k][e >> 2][e & 3];
+                                v[e] = __builtin_fmaf(sc, v[e], bi);
+                            }
                         }
                         if constexpr (RESID) {
                             const i32x4 sv = *reinterpret_cast<const i32x4*>(a.src + obase + co);
@@ -1055,10 +1088,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
                                 v[e] = __builtin_fmaf(a.beta, out_to_f32(hb, ODT), v[e]);
                             }
                         }
-                        if (a.epi) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] = epi_act(a, v[e]);
-                        }
+                        if (a.epi) epi_act_n<8>(a, v);
                         i32x4 ov;
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -1487,10 +1517,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                         v[e] = __builtin_fmaf(a.beta, out_to_f32(h, ODT), v[e]);
                     }
                 }
-                if (a.epi) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = epi_act(a, v[e]);
-                }
+                if (a.epi) epi_act_n<4>(a, v);
                 u32x2 ov;
                 ov[0] = (uint32_t)f32_to_out(v[0], ODT) | ((uint32_t)f32_to_out(v[1], ODT) << 16);
                 ov[1] = (uint32_t)f32_to_out(v[2], ODT) | ((uint32_t)f32_to_out(v[3], ODT) << 16);
