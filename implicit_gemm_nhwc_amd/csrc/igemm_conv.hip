@@ -421,26 +421,30 @@ hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Tile choice for C_out > 64, four waves (one per SIMD), 128-byte k-tiles
-// (whole cache lines per request).  256 x 256 tiles (128 x 128 per wave,
-// 256 accumulator registers) in two stages whenever that still gives a tile
-// per CU; else 256 x 128 (128 x 64 per wave) in three stages; 128 x 128 in
-// four stages for C_out <= 128.  TAPK when C_in is a whole number of k-tiles.
+// Tile choice for C_out > 64, four waves, 128-byte k-tiles (whole cache
+// lines per request).  256 x 256 tiles (128 x 128 per wave, 256 accumulator
+// registers) in two stages (128 KB of LDS, one workgroup per CU) whenever
+// that still gives a tile per CU; otherwise 128 x 128 tiles (64 x 64 per
+// wave) in two stages, 64 KB, so two workgroups share a CU and one's
+// prologue, epilogue and waits overlap the other's MFMAs.  Measured on the
+// strided 3x3 128->256 layer (N=32, 56x56, fp16; kernel time, cold operands):
+// 128x128 in 2 stages 27.9 us, 256x128 in 3 stages 30.4 us, 256x128 in 2
+// stages 31.0 us, 128x256 in 3 stages 30.7 us, 128x128 in 4 stages (one
+// workgroup per CU) 35.1 us, 256x256 in 2 stages (98 tiles) 42.7 us.  On the
+// fp8 5x5 256->256 layer (256 tiles of 256x256): 256x256 in 2 stages 105 us,
+// 128x128 in 2 stages 115 us, 256x128 in 3 stages 125 us.  TAPK when C_in is
+// a whole number of k-tiles.
 template <int DT, bool RESID>
 hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     constexpr int E = DtTraits<DT>::E;
     const bool tap128 = a.C > 0 && (a.C * E) % 128 == 0;
     const int64_t co_tiles256 = (a.F + 255) / 256;
     const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
-    if (a.F > 128) {
-        if (px_tiles256 * co_tiles256 >= kNumCUs)
-            return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
-                          : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
-        return tap128 ? launch_wide<DT, 4, 2, 2, 2, 128, 3, RESID, true>(a, stream)
-                      : launch_wide<DT, 4, 2, 2, 2, 128, 3, RESID, false>(a, stream);
-    }
-    return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 4, RESID, true>(a, stream)
-                  : launch_wide<DT, 2, 2, 2, 2, 128, 4, RESID, false>(a, stream);
+    if (a.F > 128 && px_tiles256 * co_tiles256 >= kNumCUs)
+        return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
+                      : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
+    return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, true>(a, stream)
+                  : launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, false>(a, stream);
 }
 
 // The wide kernel bases each tile's pixel buffer at its first image; the

@@ -169,7 +169,7 @@ PATH_CASES = [
     ("wide256_bf16_tap", "bfloat16", 16, 64, 64, 64, 256, 3, 3, 1, 1, False, "wide"),
     ("wide256_fp16_walk", "float16", 16, 64, 64, 48, 192, 3, 3, 1, 1, True, "wide"),
     ("wide256_fp8_walk", "float8_e4m3fn", 16, 64, 64, 80, 256, 3, 3, 1, 1, False, "wide"),
-    ("wide256x128_bf16_walk_s2", "bfloat16", 4, 30, 30, 96, 160, 3, 3, 2, 1, True, "wide"),
+    ("wide128_bf16_walk_s2_f160", "bfloat16", 4, 30, 30, 96, 160, 3, 3, 2, 1, True, "wide"),
     ("wide128_fp8_tap", "float8_e4m3fn", 2, 20, 20, 128, 96, 3, 3, 1, 1, False, "wide"),
     ("band_u1_bf16", "bfloat16", 2, 20, 20, 16, 48, 3, 3, 1, 1, False, "band"),
     ("band_u2_fp16_tm1", "float16", 2, 20, 20, 32, 24, 5, 5, 1, 2, True, "band"),
