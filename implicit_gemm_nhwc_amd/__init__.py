@@ -11,9 +11,11 @@ Names mirror the C entry points:
   conv2d_fwd, conv2d_fwd_check, conv2d_fwd_nk, conv2d_filter_to_nk,
   conv2d_fwd_epilogue, conv2d_fwd_nk_epilogue, conv2d_epilogue_check,
   conv2d_im2col, conv2d_im2col_bytes,
+  conv2d_transposed_fwd, conv2d_transposed_check, conv2d_transposed_workspace_bytes,
   conv2d_fwd_kernel_name, conv2d_workspace_bytes, conv2d_nk_row_pitch,
   conv2d_reason_string, conv2d_abi_version
-plus conv2d(), which allocates the output and calls conv2d_fwd_epilogue, and
+plus conv2d() and conv2d_transposed(), which allocate the output and call
+conv2d_fwd_epilogue / conv2d_transposed_fwd, and
 conv2d_materialized(), the write-then-GEMM route (conv2d_filter_to_nk,
 conv2d_im2col, conv2d_fwd_nk on the 1x1 view) kept for measuring what the
 fused gather saves.
@@ -98,6 +100,13 @@ def lib():
     L.conv2d_im2col.restype = i32
     L.conv2d_im2col_bytes.argtypes = [i64p, i64p2, i32p, i32p, i32]
     L.conv2d_im2col_bytes.restype = sz
+    tr_head = [vp, i64p, vp, i64p, vp, i64p, i32p, i32p, i32p, i32, vp, f32, epip]
+    L.conv2d_transposed_fwd.argtypes = tr_head + [vp, sz, vp]
+    L.conv2d_transposed_fwd.restype = i32
+    L.conv2d_transposed_check.argtypes = tr_head + [vp, sz]
+    L.conv2d_transposed_check.restype = i32
+    L.conv2d_transposed_workspace_bytes.argtypes = [i64p, i32]
+    L.conv2d_transposed_workspace_bytes.restype = sz
     _lib = L
     return L
 
@@ -326,6 +335,71 @@ def conv2d_materialized(input, filter, output, nk, a_buf, *, filter_is_fcrs, str
     return conv2d_fwd_nk(a_buf, nk, (f, kp, 1, 1), output, filter_is_fcrs=True, stride=1,
                          padding=0, source=source, beta=beta, stream=stream,
                          dtype=dtype_code(input.dtype), in_shape=(n, ho, wo, kp))
+
+
+def conv2d_transposed_workspace_bytes(filt_rsfc, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(lib().conv2d_transposed_workspace_bytes(_i64(filt_rsfc), code))
+
+
+def _tr_head(input, filter, output, stride, dilation, padding, dtype, source, beta, scale,
+             bias, activation, in_shape, filt_shape, out_shape):
+    in_shape = input.shape if in_shape is None else in_shape
+    filt_shape = filter.shape if filt_shape is None else filt_shape
+    out_shape = output.shape if out_shape is None else out_shape
+    if dtype is None:
+        dtype = dtype_code(input.dtype)
+    return [_ptr(input), _i64(in_shape), _ptr(filter), _i64(filt_shape), _ptr(output),
+            _i64(out_shape), _pair(stride), _pair(dilation), _pair(padding), int(dtype),
+            _ptr(source), float(beta), _epi_ref(make_epilogue(scale, bias, activation))]
+
+
+def conv2d_transposed_check(input, filter, output, *, stride=1, padding=0, dilation=1,
+                            source=None, beta=0.0, scale=None, bias=None, activation=None,
+                            workspace=None, workspace_bytes=0, dtype=None, in_shape=None,
+                            filt_shape=None, out_shape=None) -> int:
+    """Host-only gate of the transposed convolution: 0 or a decline code."""
+    head = _tr_head(input, filter, output, stride, dilation, padding, dtype, source, beta,
+                    scale, bias, activation, in_shape, filt_shape, out_shape)
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return lib().conv2d_transposed_check(*head, _ptr(workspace), int(workspace_bytes))
+
+
+def conv2d_transposed_fwd(input, filter, output, *, stride=1, padding=0, dilation=1,
+                          source=None, beta=0.0, scale=None, bias=None, activation=None,
+                          workspace=None, workspace_bytes=0, stream=None, dtype=None,
+                          in_shape=None, filt_shape=None, out_shape=None) -> int:
+    """Enqueue the transposed convolution (RSFC filter).  1 handled, 0
+    declined, < 0 HIP error."""
+    head = _tr_head(input, filter, output, stride, dilation, padding, dtype, source, beta,
+                    scale, bias, activation, in_shape, filt_shape, out_shape)
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return lib().conv2d_transposed_fwd(*head, _ptr(workspace), int(workspace_bytes),
+                                       _stream(stream, output))
+
+
+def conv2d_transposed(input, filter, *, stride=1, padding=0, source=None, beta=0.0,
+                      scale=None, bias=None, activation=None, stream=None):
+    """Allocate the NHWC output and run conv2d_transposed_fwd into it
+    (filter RSFC [R, S, F, C])."""
+    r, s, f, _ = filter.shape
+    n, h, w, _ = input.shape
+    ho, wo = (h - 1) * stride - 2 * padding + r, (w - 1) * stride - 2 * padding + s
+    out = torch.empty((n, ho, wo, f), dtype=OUT_DTYPES.get(input.dtype, input.dtype),
+                      device=input.device)
+    ws = torch.empty(max(conv2d_transposed_workspace_bytes(filter.shape, input.dtype), 16),
+                     dtype=torch.uint8, device=input.device)
+    kw = dict(stride=stride, padding=padding, source=source, beta=beta, scale=scale,
+              bias=bias, activation=activation, workspace=ws)
+    rc = conv2d_transposed_fwd(input, filter, out, stream=stream, **kw)
+    if rc == 0:
+        reason = conv2d_transposed_check(input, filter, out, **kw)
+        raise Declined(f"conv2d_transposed_fwd declined: {REASONS.get(reason, reason)}")
+    if rc < 0:
+        raise RuntimeError(f"conv2d_transposed_fwd failed with HIP error {-rc}")
+    return out
 
 
 def out_hw(h, w, r, s, stride, padding):

@@ -585,9 +585,111 @@ int32_t im2col_shape(const int64_t in_nhwc[4], const int64_t filt_rs[2],
     return IGC_OK;
 }
 
+// Transposed convolution (page "conv_transposed_gpu") as the equivalent
+// forward convolution: stride 1 and dilation 1 only, a square filter
+// (R == S, so the equivalent padding R - 1 - p is the same on both axes) and
+// R - 1 - p in {0, 1, 2}.  Fills the forward shape, whose filter dims are
+// the RSCF {R, S, C, F} of the flipped filter.
+int32_t transposed_shape(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
+                         const int64_t out_nhwc[4], const int32_t stride[2],
+                         const int32_t dilation[2], const int32_t padding[2], int32_t dtype,
+                         Shape* sh) {
+    if (!in_nhwc || !filt_rsfc || !out_nhwc || !stride || !dilation || !padding)
+        return IGC_DECLINE_NULL_POINTER;
+    if (stride[0] != 1 || stride[1] != 1) return IGC_DECLINE_STRIDE;
+    if (dilation[0] != 1 || dilation[1] != 1) return IGC_DECLINE_DILATION;
+    if (padding[0] != padding[1] || padding[0] < 0) return IGC_DECLINE_PADDING;
+    const int64_t R = filt_rsfc[0], S = filt_rsfc[1], F = filt_rsfc[2], C = filt_rsfc[3];
+    if (R < 1 || S < 1 || F < 0 || C < 0 || C != in_nhwc[3]) return IGC_DECLINE_SHAPE;
+    if (R != S) return IGC_DECLINE_PADDING;
+    const int64_t fpad = R - 1 - padding[0];
+    if (fpad < 0 || fpad > 2) return IGC_DECLINE_PADDING;
+    const int64_t fdims[4] = {R, S, C, F};
+    const int32_t one[2] = {1, 1};
+    const int32_t fp[2] = {(int32_t)fpad, (int32_t)fpad};
+    return check_shapes(in_nhwc, 0, fdims, out_nhwc, one, one, fp, 1, dtype, sh);
+}
+
+hipError_t launch_transpose_flipped(const void* filter, const Shape& s, int32_t dtype, void* nk,
+                                    hipStream_t stream) {
+    const int eb = elem_bytes(dtype);
+    const int64_t chunks = s.F * (s.kpitch / (16 / eb));
+    if (chunks == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096);
+    if (eb == 2)
+        hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<2>, dim3(blocks), dim3(256), 0, stream,
+                           (const uint8_t*)filter, (uint8_t*)nk, (int)s.R, (int)s.S, (int)s.F,
+                           (int)s.C, (int)s.K, (int)s.kpitch);
+    else
+        hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<1>, dim3(blocks), dim3(256), 0, stream,
+                           (const uint8_t*)filter, (uint8_t*)nk, (int)s.R, (int)s.S, (int)s.F,
+                           (int)s.C, (int)s.K, (int)s.kpitch);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t conv2d_transposed_workspace_bytes(const int64_t filt_rsfc[4], int32_t dtype) {
+    if (!filt_rsfc) return 0;
+    const int64_t fdims[4] = {filt_rsfc[0], filt_rsfc[1], filt_rsfc[3], filt_rsfc[2]};
+    return conv2d_workspace_bytes(fdims, 0, dtype);
+}
+
+int32_t conv2d_transposed_check(const void* input, const int64_t in_nhwc[4], const void* filter,
+                                const int64_t filt_rsfc[4], const void* output,
+                                const int64_t out_nhwc[4], const int32_t stride[2],
+                                const int32_t dilation[2], const int32_t padding[2],
+                                int32_t dtype, const void* source, float beta,
+                                const igc_epilogue* epilogue, const void* workspace,
+                                size_t workspace_bytes) {
+    (void)beta;
+    Shape s;
+    int32_t rc = transposed_shape(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding,
+                                  dtype, &s);
+    if (rc != IGC_OK) return rc;
+    const int64_t fdims[4] = {s.R, s.S, s.C, s.F};
+    const int32_t one[2] = {1, 1};
+    const int32_t fp[2] = {s.pad, s.pad};
+    rc = check_all(input, in_nhwc, filter, 0, 0, fdims, output, out_nhwc, one, one, fp, 1, dtype,
+                   source, workspace, workspace_bytes, &s);
+    if (rc != IGC_OK) return rc;
+    return check_epilogue(epilogue, output, s);
+}
+
+int32_t conv2d_transposed_fwd(const void* input, const int64_t in_nhwc[4], const void* filter,
+                              const int64_t filt_rsfc[4], void* output,
+                              const int64_t out_nhwc[4], const int32_t stride[2],
+                              const int32_t dilation[2], const int32_t padding[2],
+                              int32_t dtype, const void* source, float beta,
+                              const igc_epilogue* epilogue, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (conv2d_transposed_check(input, in_nhwc, filter, filt_rsfc, output, out_nhwc, stride,
+                                dilation, padding, dtype, source, beta, epilogue, workspace,
+                                workspace_bytes) != IGC_OK)
+        return 0;
+    Shape s;
+    transposed_shape(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding, dtype, &s);
+    if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
+    hipStream_t st = (hipStream_t)stream;
+    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
+    void* nk = workspace;
+    bool owned = false;
+    if (!nk && nk_bytes) {
+        hipError_t e = hipMallocAsync(&nk, nk_bytes, st);
+        if (e != hipSuccess) return -(int32_t)e;
+        owned = true;
+    }
+    hipError_t e = launch_transpose_flipped(filter, s, dtype, nk, st);
+    if (e == hipSuccess) e = launch_igemm(input, nk, output, source, beta, epilogue, s, dtype, st);
+    if (owned) {
+        hipError_t f = hipFreeAsync(nk, st);
+        if (e == hipSuccess) e = f;
+    }
+    return hip_fail(e);
+}
+
 
 size_t conv2d_im2col_bytes(const int64_t in_nhwc[4], const int64_t filt_rs[2],
                            const int32_t stride[2], const int32_t padding[2], int32_t dtype) {

@@ -1552,6 +1552,38 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
 }
 
 // ---------------------------------------------------------------------------
+// Transposed convolution (page "conv_transposed_gpu": NHWC input, RSFC
+// filter [R][S][F][C], F output and C input channels).  With stride 1,
+//   out[n, oh, ow, f] = sum_{r, s, c} in[n, oh + p - r, ow + p - s, c] * W[r][s][f][c]
+// is the forward convolution of `in` with padding R - 1 - p and the filter
+// flipped in both taps and with its channel roles swapped,
+//   W'(r', s', c, f) = W[R-1-r'][S-1-s'][f][c],
+// whose NK matrix is NK'[f][(r'*S + s')*C + c] = W[R-1-r'][S-1-s'][f][c]: for
+// each (f, r', s') a contiguous run of C elements of W.  One thread copies one
+// 16-byte chunk (C * E % 16 == 0); chunks at or past K are zero.
+template <int E>
+__global__ __launch_bounds__(256) void filter_rsfc_to_nk_flipped_kernel(
+    const uint8_t* __restrict__ w, uint8_t* __restrict__ nk, int R, int S, int F, int C,
+    int K, int kpitch) {
+    constexpr int VEC = 16 / E;
+    const int row_chunks = kpitch / VEC;
+    const int64_t total = (int64_t)F * row_chunks;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total;
+         g += (int64_t)gridDim.x * 256) {
+        const int f = (int)(g / row_chunks), chunk = (int)(g - (int64_t)f * row_chunks);
+        const int k0 = chunk * VEC;
+        i32x4 v = {0, 0, 0, 0};
+        if (k0 < K) {
+            const int tap = k0 / C, c0 = k0 - tap * C;
+            const int r = tap / S, s = tap - r * S;
+            const int64_t src = ((((int64_t)(R - 1 - r) * S + (S - 1 - s)) * F + f) * C + c0) * E;
+            v = *reinterpret_cast<const i32x4*>(w + src);
+        }
+        *reinterpret_cast<i32x4*>(nk + ((int64_t)f * kpitch + k0) * E) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Materialised im2col (page "dispatch_fused_im2col_conv2d_apple", summary:
 // the [M, K] patch matrix the fused path never writes), for comparing the
 // fused gather against the write-then-GEMM route on the same MFMA kernels:

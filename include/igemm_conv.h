@@ -287,6 +287,53 @@ size_t conv2d_im2col_bytes(const int64_t in_nhwc[4], const int64_t filt_rs[2],
                            const int32_t stride[2], const int32_t padding[2],
                            int32_t dtype);
 
+/*
+ * Transposed convolution (page "conv_transposed_gpu": NHWC input, filter in
+ * RSFC layout [R][S][F][C] with F output and C input channels; the page runs
+ * it through cuDNN's backward-data path and applies an elementwise epilogue
+ * as a separate pass).  Definition, cross-correlation form:
+ *   out[n, oh, ow, f] = sum over (ih, iw, r, s, c) with
+ *                         oh = ih*st - p + r,  ow = iw*st - p + s
+ *                       of in[n, ih, iw, c] * W[r][s][f][c]
+ *   Ho = (H - 1)*st - 2p + R,  Wo = (W - 1)*st - 2p + S
+ * i.e. the adjoint of the forward convolution whose RSCF filter is W.  Then
+ * the same fused epilogue as conv2d_fwd_epilogue (scale, bias, residual
+ * source, activation; all optional) and one rounding.
+ * Supported here: stride (1,1), dilation (1,1), a square filter (R == S) and
+ * symmetric padding p with R - 1 - p in {0, 1, 2}: the call is then the
+ * forward convolution of the input with the filter flipped in both taps and
+ * its channel roles swapped, at padding R - 1 - p, which runs on the same
+ * implicit-GEMM kernels (the flip is a 16-byte chunk permutation done by the
+ * NK transpose).  Other shapes are declined (stride, dilation or padding
+ * codes); dtypes, layouts, alignment and overlap rules as conv2d_fwd.
+ *   in_nhwc = {N, H, W, C}, filt_rsfc = {R, S, F, C}, out_nhwc = {N, Ho, Wo, F}
+ *   workspace: at least conv2d_transposed_workspace_bytes(), or NULL
+ *   (stream-ordered allocation as in conv2d_fwd).
+ * Returns 1 = handled, 0 = declined (conv2d_transposed_check gives the
+ * reason), or -(hipError_t).
+ */
+int32_t conv2d_transposed_fwd(const void* input, const int64_t in_nhwc[4],
+                              const void* filter, const int64_t filt_rsfc[4],
+                              void* output, const int64_t out_nhwc[4],
+                              const int32_t stride[2], const int32_t dilation[2],
+                              const int32_t padding[2], int32_t dtype,
+                              const void* source, float beta,
+                              const igc_epilogue* epilogue,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only gate of conv2d_transposed_fwd: IGC_OK or a decline reason. */
+int32_t conv2d_transposed_check(const void* input, const int64_t in_nhwc[4],
+                                const void* filter, const int64_t filt_rsfc[4],
+                                const void* output, const int64_t out_nhwc[4],
+                                const int32_t stride[2], const int32_t dilation[2],
+                                const int32_t padding[2], int32_t dtype,
+                                const void* source, float beta,
+                                const igc_epilogue* epilogue,
+                                const void* workspace, size_t workspace_bytes);
+
+/* Bytes of the flipped NK matrix conv2d_transposed_fwd needs. */
+size_t conv2d_transposed_workspace_bytes(const int64_t filt_rsfc[4], int32_t dtype);
+
 #ifdef __cplusplus
 }
 #endif

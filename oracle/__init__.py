@@ -21,6 +21,11 @@ Parity status of each function (what pins it is in tests/test_oracle_pins.py):
                           filter, textbook sigmoid values, relu's sign split.
   filter_to_nk           pinned: element-wise brute force from the index
                           formula on small filters.
+  conv2d_transposed      pinned: hand-worked golden values
+                          (tests/golden/transposed_cases.txt), pure-Python
+                          brute force with strides, dilations and padding,
+                          the adjoint identity <conv2d(a, W), b> =
+                          <a, conv2d_transposed(b, W)> against conv2d.
   im2col                 pinned: pure-Python brute force on tiny shapes,
                           im2col(x) @ filter_to_nk(w)^T equals conv2d,
                           zero columns past K.
@@ -35,6 +40,7 @@ from .reference import (  # noqa: F401
     conv2d_epilogue,
     conv2d_epilogue_points,
     conv2d_points,
+    conv2d_transposed,
     filter_dims_rscf,
     filter_to_nk,
     gate_accepts,

@@ -216,6 +216,43 @@ def filter_to_nk(w: torch.Tensor, filter_is_fcrs: bool, k_pad: int = None) -> to
     return nk.contiguous().view(w.dtype)
 
 
+def conv2d_transposed(x, w_rsfc, *, stride=1, padding=0, dilation=1, source=None,
+                      beta: float = 0.0, scale=None, bias=None, act: str = "none") -> np.ndarray:
+    """Transposed convolution, fp64 (page 3, "conv_transposed_gpu": NHWC input,
+    RSFC filter [R, S, F, C] with F output and C input channels, stride,
+    dilation and padding per spatial axis; an optional elementwise epilogue
+    after it).  Scatter form of the definition: every input pixel (ih, iw)
+    adds in[n, ih, iw, :] . W[r, s, f, :] to output pixel
+        (ih*sh - ph + r*dh,  iw*sw - pw + s*dw)
+    when that lies inside the output of size
+        Ho = (H - 1)*sh - 2*ph + dh*(R - 1) + 1  (and likewise Wo).
+    Then the fused-epilogue family of conv2d_epilogue.  Returns the
+    unrounded float64 result [N, Ho, Wo, F].
+    """
+    sh, sw = (stride, stride) if isinstance(stride, int) else stride
+    ph, pw = (padding, padding) if isinstance(padding, int) else padding
+    dh, dw = (dilation, dilation) if isinstance(dilation, int) else dilation
+    x64, w64 = _f64(x), _f64(w_rsfc)
+    n, h, wd, c = x64.shape
+    r, s, f, cw = w64.shape
+    if cw != c:
+        raise ValueError(f"filter C {cw} != input C {c}")
+    fh = (h - 1) * sh + dh * (r - 1) + 1     # output extent before the padding is cut
+    fw = (wd - 1) * sw + dw * (s - 1) + 1
+    ho, wo = fh - 2 * ph, fw - 2 * pw
+    if ho < 1 or wo < 1:
+        raise ValueError("empty transposed-convolution output")
+    full = np.zeros((n, fh, fw, f))
+    for rr in range(r):
+        for ss in range(s):
+            contrib = x64 @ w64[rr, ss].T                      # [N, H, W, F]
+            full[:, rr * dh:rr * dh + (h - 1) * sh + 1:sh,
+                 ss * dw:ss * dw + (wd - 1) * sw + 1:sw, :] += contrib
+    y = np.ascontiguousarray(full[:, ph:ph + ho, pw:pw + wo, :])
+    src64 = None if source is None else _f64(source)
+    return _epilogue(y, src64, beta, scale, bias, act)
+
+
 def im2col(x, r: int, s: int, *, stride=1, padding=0, k_pad: int = None) -> torch.Tensor:
     """The [M, K] patch matrix of page 2 ("dispatch_fused_im2col_conv2d_apple",
     summary: the matrix the fused kernel gathers on the fly instead of

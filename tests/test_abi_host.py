@@ -262,3 +262,51 @@ def test_im2col_bytes_and_declines():
     assert call(X, X + 4096, need) == 0        # overlaps the input
     assert call(X, 0, need) == 0               # null output
     assert call(X, WS, need, st=3) == 0        # stride
+
+
+# ----------------------------------------------------- transposed convolution
+TBASE = dict(in_shape=(2, 9, 9, 32), filt_shape=(3, 3, 48, 32), out_shape=(2, 9, 9, 48),
+             stride=1, padding=1, dilation=1, dtype=0)
+
+
+def _tcheck(**kw):
+    args = {**TBASE, **kw}
+    return igc.conv2d_transposed_check(args.pop("input", X), args.pop("filter", W),
+                                       args.pop("output", Y), **args)
+
+
+def test_transposed_workspace_bytes():
+    # equivalent forward filter RSCF {3, 3, 32, 48}: K = 288 -> 320 (+8 for C_out <= 64)
+    assert igc.conv2d_transposed_workspace_bytes((3, 3, 48, 32), torch.bfloat16) == 48 * 328 * 2
+    assert igc.conv2d_transposed_workspace_bytes((3, 3, 48, 32), 9) == 0
+
+
+@pytest.mark.parametrize("kw,reason", [
+    (dict(), "ok"),
+    (dict(source=SRC, beta=0.5, scale=SC, activation="silu"), "ok"),
+    (dict(padding=0, out_shape=(2, 11, 11, 48)), "ok"),          # R - 1 - p = 2
+    (dict(filt_shape=(5, 5, 48, 32), padding=2), "ok"),
+    (dict(filt_shape=(4, 4, 48, 32), padding=1, out_shape=(2, 10, 10, 48)), "ok"),
+    (dict(stride=2, out_shape=(2, 17, 17, 48)), "stride"),
+    (dict(dilation=2), "dilation"),
+    (dict(padding=3), "padding"),                                # R - 1 - p < 0
+    (dict(filt_shape=(5, 5, 48, 32), padding=1, out_shape=(2, 11, 11, 48)), "padding"),
+    (dict(filt_shape=(3, 5, 48, 32)), "padding"),                # R != S
+    (dict(padding=(1, 0)), "padding"),
+    (dict(filt_shape=(3, 3, 48, 16)), "shape"),
+    (dict(out_shape=(2, 9, 9, 47)), "output_shape"),
+    (dict(out_shape=(2, 10, 10, 48)), "output_shape"),
+    (dict(dtype=5), "dtype"),
+    (dict(output=X + 64), "overlap"),
+    (dict(activation=9), "epilogue"),
+])
+def test_transposed_decline_paths(kw, reason):
+    assert igc.REASONS[_tcheck(**kw)] == reason
+
+
+def test_transposed_declined_call_enqueues_nothing():
+    assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "stride": 2,
+                                                 "out_shape": (2, 17, 17, 48)}) == 0
+    assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "dilation": 2}) == 0
+    args = dict(TBASE, in_shape=(0, 9, 9, 32), out_shape=(0, 9, 9, 48))
+    assert igc.conv2d_transposed_fwd(X, W, Y, **args) == 1

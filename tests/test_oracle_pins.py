@@ -514,3 +514,72 @@ def test_im2col_times_nk_is_conv(fcrs, st, p):
     nk = oracle.filter_to_nk(w, fcrs).to(torch.float64).numpy()
     y = oracle.conv2d(x, w, filter_is_fcrs=fcrs, stride=st, padding=p)
     np.testing.assert_allclose(a @ nk.T, y.reshape(-1, 5), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------ transposed convolution pins
+def _read_transposed():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "transposed_cases.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tag, *vals = line.split()
+            if tag == "case":
+                cur = dict(name=vals[0], dims=[int(v) for v in vals[1:10]])
+                cases.append(cur)
+            else:
+                cur[tag] = np.array([float(v) for v in vals])
+    return cases
+
+
+@pytest.mark.parametrize("case", _read_transposed(), ids=lambda c: c["name"])
+def test_transposed_handworked(case):
+    n, h, w, c, r, s, f, st, p = case["dims"]
+    y = oracle.conv2d_transposed(case["x"].reshape(n, h, w, c), case["w"].reshape(r, s, f, c),
+                                 stride=st, padding=p)
+    np.testing.assert_array_equal(y.reshape(-1), case["y"])
+
+
+@pytest.mark.parametrize("n,h,w,c,f,r,s,st,p,d", [
+    (1, 3, 2, 2, 3, 3, 3, 1, 1, 1), (2, 2, 3, 1, 2, 2, 3, 2, 0, 1), (1, 3, 3, 2, 1, 3, 2, 2, 1, 1),
+    (1, 2, 2, 1, 2, 3, 3, 1, 0, 2), (1, 3, 2, 2, 2, 4, 4, 2, 1, 1), (1, 2, 3, 3, 2, 1, 1, 3, 0, 1)])
+def test_transposed_brute_force(n, h, w, c, f, r, s, st, p, d):
+    g = np.random.default_rng(h * 31 + r)
+    x = g.standard_normal((n, h, w, c))
+    wt = g.standard_normal((r, s, f, c))
+    y = oracle.conv2d_transposed(x, wt, stride=st, padding=p, dilation=d)
+    ho, wo = (h - 1) * st - 2 * p + d * (r - 1) + 1, (w - 1) * st - 2 * p + d * (s - 1) + 1
+    assert y.shape == (n, ho, wo, f)
+    want = [[[[[] for _ in range(f)] for _ in range(wo)] for _ in range(ho)] for _ in range(n)]
+    for b in range(n):
+        for ih in range(h):
+            for iw in range(w):
+                for rr in range(r):
+                    for ss in range(s):
+                        oh, ow = ih * st - p + rr * d, iw * st - p + ss * d
+                        if 0 <= oh < ho and 0 <= ow < wo:
+                            for ff in range(f):
+                                for cc in range(c):
+                                    want[b][oh][ow][ff].append(x[b, ih, iw, cc] * wt[rr, ss, ff, cc])
+    ref = np.array([[[[math.fsum(v) for v in px] for px in row] for row in img] for img in want])
+    assert _rel(y, ref) < 1e-13
+
+
+@pytest.mark.parametrize("h,w,r,st,p", [(6, 5, 3, 1, 1), (7, 7, 3, 2, 1), (5, 6, 5, 1, 2),
+                                        (8, 8, 4, 2, 1), (5, 5, 1, 1, 0), (7, 5, 3, 2, 0)])
+def test_transposed_is_adjoint_of_conv2d(h, w, r, st, p):
+    # <conv2d(a, W), b> = <a, conv2d_transposed(b, W)>: the RSCF filter of the
+    # forward convolution is the RSFC filter of its adjoint
+    if (h + 2 * p - r) % st or (w + 2 * p - r) % st:
+        pytest.skip("output extent must map back onto the input exactly")
+    g = np.random.default_rng(h * 100 + w * 10 + r)
+    cin, cout = 3, 4
+    a = g.standard_normal((2, h, w, cin))
+    wt = g.standard_normal((r, r, cin, cout))
+    y = oracle.conv2d(a, wt, filter_is_fcrs=False, stride=st, padding=p)
+    b = g.standard_normal(y.shape)
+    at = oracle.conv2d_transposed(b, wt, stride=st, padding=p)
+    assert at.shape == a.shape
+    lhs, rhs = float(np.sum(y * b)), float(np.sum(a * at))
+    assert abs(lhs - rhs) <= 1e-12 * max(abs(lhs), 1.0) * a.size
