@@ -22,8 +22,9 @@ Also reported on the same line:
                 workload (the full batch);
   shapes        the same measurement for each of the five named workloads;
   next          the fused per-channel epilogue's cost on the headline layer,
-                and the materialised im2col + GEMM route against the fused
-                kernel on the two memory-bound layers.
+                the materialised im2col + GEMM route against the fused
+                kernel on the two memory-bound layers, and a stride-1
+                transposed convolution (both of its launches).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -291,6 +292,39 @@ def measure_next(torch, igc, launches, rotate_bytes=ROTATE_BYTES):
         del bufs, a
         torch.cuda.empty_cache()
     out["im2col_ablation"] = abl
+
+    # transposed convolution, stride 1 (a decoder-style 3x3 layer): the flipped
+    # NK transpose and the GEMM, timed together over rotating buffer sets
+    n, h, w, c, f, r, p = 8, 64, 64, 256, 128, 3, 1
+    x, wf, _ = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=r, dtype="bfloat16",
+                                 fcrs=False, x_dist=("normal", 1.0),
+                                 w_dist=("normal", 1.0 / (r * r * c) ** 0.5), seed=0)
+    wt = wf.permute(0, 1, 3, 2).contiguous()          # RSFC [R, S, F, C]
+    ho, wo = h - 1 - 2 * p + r, w - 1 - 2 * p + r
+    per = x.numel() * 2 + n * ho * wo * f * 2
+    nsets = min(MAX_SETS, max(1, -(-rotate_bytes // per)))
+    sets = [dict(x=x.to("cuda:0"), w=wt.to("cuda:0"),
+                 y=torch.empty((n, ho, wo, f), dtype=torch.bfloat16, device="cuda:0"),
+                 ws=torch.empty(igc.conv2d_transposed_workspace_bytes(wt.shape, wt.dtype),
+                                dtype=torch.uint8, device="cuda:0")) for _ in range(nsets)]
+
+    def tconv(i):
+        b = sets[i % nsets]
+        _ok(igc.conv2d_transposed_fwd(b["x"], b["w"], b["y"], stride=1, padding=p,
+                                      workspace=b["ws"]), "conv2d_transposed_fwd")
+    for i in range(nsets):
+        tconv(i)
+    t = event_time(torch, tconv, launches)
+    flops = 2 * n * ho * wo * f * r * r * c
+    out["transposed"] = {"shape": f"N={n} {h}x{w} C={c} -> F={f}, {r}x{r}, stride 1, pad {p}, bf16",
+                         "call_us": round(t, 3),
+                         "tflops": round(flops / (t * 1e-6) / 1e12, 1),
+                         "frac_mfma": round(flops / (t * 1e-6) / 1e12 / PEAK["bf16_tflops"], 4),
+                         "gemm_kernel": igc.conv2d_fwd_kernel_name(
+                             (n, h, w, c), (r, r, c, f), (n, ho, wo, f), filter_is_fcrs=False,
+                             dtype=torch.bfloat16, stride=1, padding=r - 1 - p)}
+    del sets
+    torch.cuda.empty_cache()
     return out
 
 
