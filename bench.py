@@ -293,38 +293,43 @@ def measure_next(torch, igc, launches, rotate_bytes=ROTATE_BYTES):
         torch.cuda.empty_cache()
     out["im2col_ablation"] = abl
 
-    # transposed convolution, stride 1 (a decoder-style 3x3 layer): the flipped
-    # NK transpose and the GEMM, timed together over rotating buffer sets
-    n, h, w, c, f, r, p = 8, 64, 64, 256, 128, 3, 1
-    x, wf, _ = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=r, dtype="bfloat16",
-                                 fcrs=False, x_dist=("normal", 1.0),
-                                 w_dist=("normal", 1.0 / (r * r * c) ** 0.5), seed=0)
-    wt = wf.permute(0, 1, 3, 2).contiguous()          # RSFC [R, S, F, C]
-    ho, wo = h - 1 - 2 * p + r, w - 1 - 2 * p + r
-    per = x.numel() * 2 + n * ho * wo * f * 2
-    nsets = min(MAX_SETS, max(1, -(-rotate_bytes // per)))
-    sets = [dict(x=x.to("cuda:0"), w=wt.to("cuda:0"),
-                 y=torch.empty((n, ho, wo, f), dtype=torch.bfloat16, device="cuda:0"),
-                 ws=torch.empty(igc.conv2d_transposed_workspace_bytes(wt.shape, wt.dtype),
-                                dtype=torch.uint8, device="cuda:0")) for _ in range(nsets)]
+    # transposed convolutions: a decoder-style 3x3 stride-1 layer and the 4x4
+    # stride-2 2x upsampler, each call timed whole (filter flip, GEMMs and,
+    # for stride 2, the phase interleave) over rotating buffer sets
+    out["transposed"] = {}
+    for tag, (n, h, w, c, f, r, st, p) in {
+            "3x3_s1": (8, 64, 64, 256, 128, 3, 1, 1),
+            "4x4_s2_upsample": (8, 32, 32, 256, 128, 4, 2, 1)}.items():
+        x, wf, _ = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=r, dtype="bfloat16",
+                                     fcrs=False, x_dist=("normal", 1.0),
+                                     w_dist=("normal", 1.0 / (r * r * c) ** 0.5), seed=0)
+        wt = wf.permute(0, 1, 3, 2).contiguous()          # RSFC [R, S, F, C]
+        ho, wo = (h - 1) * st - 2 * p + r, (w - 1) * st - 2 * p + r
+        per = x.numel() * 2 + n * ho * wo * f * 2
+        nsets = min(MAX_SETS, max(1, -(-rotate_bytes // per)))
+        wsb = igc.conv2d_transposed_workspace_bytes(x.shape, wt.shape, stride=st, padding=p,
+                                                    dtype=wt.dtype)
+        sets = [dict(x=x.to("cuda:0"), w=wt.to("cuda:0"),
+                     y=torch.empty((n, ho, wo, f), dtype=torch.bfloat16, device="cuda:0"),
+                     ws=torch.empty(wsb, dtype=torch.uint8, device="cuda:0"))
+                for _ in range(nsets)]
 
-    def tconv(i):
-        b = sets[i % nsets]
-        _ok(igc.conv2d_transposed_fwd(b["x"], b["w"], b["y"], stride=1, padding=p,
-                                      workspace=b["ws"]), "conv2d_transposed_fwd")
-    for i in range(nsets):
-        tconv(i)
-    t = event_time(torch, tconv, launches)
-    flops = 2 * n * ho * wo * f * r * r * c
-    out["transposed"] = {"shape": f"N={n} {h}x{w} C={c} -> F={f}, {r}x{r}, stride 1, pad {p}, bf16",
-                         "call_us": round(t, 3),
-                         "tflops": round(flops / (t * 1e-6) / 1e12, 1),
-                         "frac_mfma": round(flops / (t * 1e-6) / 1e12 / PEAK["bf16_tflops"], 4),
-                         "gemm_kernel": igc.conv2d_fwd_kernel_name(
-                             (n, h, w, c), (r, r, c, f), (n, ho, wo, f), filter_is_fcrs=False,
-                             dtype=torch.bfloat16, stride=1, padding=r - 1 - p)}
-    del sets
-    torch.cuda.empty_cache()
+        def tconv(i):
+            b = sets[i % nsets]
+            _ok(igc.conv2d_transposed_fwd(b["x"], b["w"], b["y"], stride=st, padding=p,
+                                          workspace=b["ws"]), "conv2d_transposed_fwd")
+        for i in range(nsets):
+            tconv(i)
+        t = event_time(torch, tconv, launches)
+        # useful FLOPs: every input pixel meets every tap once
+        flops = 2 * n * h * w * f * r * r * c
+        out["transposed"][tag] = {
+            "shape": f"N={n} {h}x{w} C={c} -> F={f}, {r}x{r}, stride {st}, pad {p} -> "
+                     f"{ho}x{wo}, bf16",
+            "call_us": round(t, 3), "tflops": round(flops / (t * 1e-6) / 1e12, 1),
+            "frac_mfma": round(flops / (t * 1e-6) / 1e12 / PEAK["bf16_tflops"], 4)}
+        del sets
+        torch.cuda.empty_cache()
     return out
 
 

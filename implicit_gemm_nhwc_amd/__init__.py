@@ -105,7 +105,7 @@ def lib():
     L.conv2d_transposed_fwd.restype = i32
     L.conv2d_transposed_check.argtypes = tr_head + [vp, sz]
     L.conv2d_transposed_check.restype = i32
-    L.conv2d_transposed_workspace_bytes.argtypes = [i64p, i32]
+    L.conv2d_transposed_workspace_bytes.argtypes = [i64p, i64p, i32p, i32p, i32, i32]
     L.conv2d_transposed_workspace_bytes.restype = sz
     _lib = L
     return L
@@ -337,9 +337,12 @@ def conv2d_materialized(input, filter, output, nk, a_buf, *, filter_is_fcrs, str
                          dtype=dtype_code(input.dtype), in_shape=(n, ho, wo, kp))
 
 
-def conv2d_transposed_workspace_bytes(filt_rsfc, dtype) -> int:
+def conv2d_transposed_workspace_bytes(in_shape, filt_rsfc, *, stride=1, padding=0, dtype,
+                                      with_source=False) -> int:
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
-    return int(lib().conv2d_transposed_workspace_bytes(_i64(filt_rsfc), code))
+    return int(lib().conv2d_transposed_workspace_bytes(_i64(in_shape), _i64(filt_rsfc),
+                                                       _pair(stride), _pair(padding), code,
+                                                       int(bool(with_source))))
 
 
 def _tr_head(input, filter, output, stride, dilation, padding, dtype, source, beta, scale,
@@ -389,8 +392,9 @@ def conv2d_transposed(input, filter, *, stride=1, padding=0, source=None, beta=0
     ho, wo = (h - 1) * stride - 2 * padding + r, (w - 1) * stride - 2 * padding + s
     out = torch.empty((n, ho, wo, f), dtype=OUT_DTYPES.get(input.dtype, input.dtype),
                       device=input.device)
-    ws = torch.empty(max(conv2d_transposed_workspace_bytes(filter.shape, input.dtype), 16),
-                     dtype=torch.uint8, device=input.device)
+    ws = torch.empty(max(conv2d_transposed_workspace_bytes(
+        input.shape, filter.shape, stride=stride, padding=padding, dtype=input.dtype,
+        with_source=source is not None), 16), dtype=torch.uint8, device=input.device)
     kw = dict(stride=stride, padding=padding, source=source, beta=beta, scale=scale,
               bias=bias, activation=activation, workspace=ws)
     rc = conv2d_transposed_fwd(input, filter, out, stream=stream, **kw)

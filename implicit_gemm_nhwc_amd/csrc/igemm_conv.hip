@@ -585,56 +585,243 @@ int32_t im2col_shape(const int64_t in_nhwc[4], const int64_t filt_rs[2],
     return IGC_OK;
 }
 
-// Transposed convolution (page "conv_transposed_gpu") as the equivalent
-// forward convolution: stride 1 and dilation 1 only, a square filter
-// (R == S, so the equivalent padding R - 1 - p is the same on both axes) and
-// R - 1 - p in {0, 1, 2}.  Fills the forward shape, whose filter dims are
-// the RSCF {R, S, C, F} of the flipped filter.
-int32_t transposed_shape(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
-                         const int64_t out_nhwc[4], const int32_t stride[2],
-                         const int32_t dilation[2], const int32_t padding[2], int32_t dtype,
-                         Shape* sh) {
+// ---- transposed convolution (page "conv_transposed_gpu") -----------------
+// Planned as stride-1 forward implicit GEMMs over the input (the phases of
+// filter_rsfc_to_nk_flipped_kernel's comment):
+//   stride 1: one phase, all taps, padding R - 1 - p, written straight to the
+//             output;
+//   stride 2: four phases (output row and column parities), each with the
+//             taps of one parity per axis, all at one padding P, written to
+//             phase buffers that phase_interleave_kernel merges; a residual
+//             source is first split into phase buffers the same way, so the
+//             fused epilogue and its single rounding stay in the GEMMs.
+// Limits: dilation 1, a square filter (R == S) and symmetric padding, so one
+// padding serves both axes; stride 2 needs R >= 2 (every parity has a tap).
+struct TPlan {
+    int32_t st = 1;
+    int64_t N = 0, H = 0, W = 0, C = 0, R = 0, F = 0, Ho = 0, Wo = 0;
+    int32_t P = 0;
+    int nph = 1;
+    int J[2] = {0, 0}, B[2] = {0, 0}, OH[2] = {0, 0}, OW[2] = {0, 0};
+    int64_t YH[2] = {0, 0}, YW[2] = {0, 0};
+    Shape ph[4];
+    size_t nk_off[4] = {}, y_off[4] = {}, s_off[4] = {};
+    size_t ws_bytes = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+int32_t transposed_plan(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
+                        const int64_t out_nhwc[4], const int32_t stride[2],
+                        const int32_t dilation[2], const int32_t padding[2], int32_t dtype,
+                        bool with_source, TPlan* tp) {
     if (!in_nhwc || !filt_rsfc || !out_nhwc || !stride || !dilation || !padding)
         return IGC_DECLINE_NULL_POINTER;
-    if (stride[0] != 1 || stride[1] != 1) return IGC_DECLINE_STRIDE;
+    if (dtype != IGC_DTYPE_BF16 && dtype != IGC_DTYPE_FP16 && dtype != IGC_DTYPE_FP8_E4M3FN)
+        return IGC_DECLINE_DTYPE;
+    if (!((stride[0] == 1 && stride[1] == 1) || (stride[0] == 2 && stride[1] == 2)))
+        return IGC_DECLINE_STRIDE;
     if (dilation[0] != 1 || dilation[1] != 1) return IGC_DECLINE_DILATION;
     if (padding[0] != padding[1] || padding[0] < 0) return IGC_DECLINE_PADDING;
-    const int64_t R = filt_rsfc[0], S = filt_rsfc[1], F = filt_rsfc[2], C = filt_rsfc[3];
-    if (R < 1 || S < 1 || F < 0 || C < 0 || C != in_nhwc[3]) return IGC_DECLINE_SHAPE;
-    if (R != S) return IGC_DECLINE_PADDING;
-    const int64_t fpad = R - 1 - padding[0];
-    if (fpad < 0 || fpad > 2) return IGC_DECLINE_PADDING;
-    const int64_t fdims[4] = {R, S, C, F};
+    TPlan t;
+    t.st = stride[0];
+    t.N = in_nhwc[0]; t.H = in_nhwc[1]; t.W = in_nhwc[2]; t.C = in_nhwc[3];
+    t.R = filt_rsfc[0]; t.F = filt_rsfc[2];
+    const int64_t S = filt_rsfc[1], p = padding[0];
+    if (t.R < 1 || S < 1 || t.F < 0 || t.C < 0 || filt_rsfc[3] != t.C || t.N < 0 || t.H < 1 ||
+        t.W < 1)
+        return IGC_DECLINE_SHAPE;
+    if (t.R != S) return IGC_DECLINE_PADDING;
+    t.Ho = (t.H - 1) * t.st - 2 * p + t.R;
+    t.Wo = (t.W - 1) * t.st - 2 * p + t.R;
+    const bool out_ok = t.Ho >= 1 && t.Wo >= 1 && out_nhwc[0] == t.N && out_nhwc[1] == t.Ho &&
+                        out_nhwc[2] == t.Wo && out_nhwc[3] == t.F;
+    const int64_t eb = elem_bytes(dtype);
     const int32_t one[2] = {1, 1};
-    const int32_t fp[2] = {(int32_t)fpad, (int32_t)fpad};
-    return check_shapes(in_nhwc, 0, fdims, out_nhwc, one, one, fp, 1, dtype, sh);
+    if (t.st == 1) {
+        t.nph = 1;
+        t.P = (int32_t)(t.R - 1 - p);
+        if (t.P < 0 || t.P > 2) return IGC_DECLINE_PADDING;
+        if (!out_ok) return IGC_DECLINE_OUTPUT_SHAPE;
+        t.J[0] = (int)t.R;
+        const int64_t fd[4] = {t.R, t.R, t.C, t.F};
+        const int32_t fp[2] = {t.P, t.P};
+        const int32_t rc = check_shapes(in_nhwc, 0, fd, out_nhwc, one, one, fp, 1, dtype, &t.ph[0]);
+        if (rc != IGC_OK) return rc;
+        t.nk_off[0] = 0;
+        t.ws_bytes = (size_t)(t.F * t.ph[0].kpitch * eb);
+        *tp = t;
+        return IGC_OK;
+    }
+    if (t.R < 2) return IGC_DECLINE_SHAPE;
+    t.nph = 4;
+    int64_t c[2];
+    int64_t P = 0;
+    for (int a = 0; a < 2; ++a) {
+        t.B[a] = (int)((a + p) % 2);
+        t.J[a] = (int)((t.R - t.B[a] + 1) / 2);
+        c[a] = (a + p - t.B[a]) / 2;
+        const int64_t need = t.J[a] - 1 - c[a];
+        if (need > P) P = need;
+    }
+    if (P > 2) return IGC_DECLINE_PADDING;
+    if (!out_ok) return IGC_DECLINE_OUTPUT_SHAPE;
+    t.P = (int32_t)P;
+    for (int a = 0; a < 2; ++a) {
+        const int64_t o = c[a] - (t.J[a] - 1) + P;
+        t.OH[a] = t.OW[a] = (int)o;
+        t.YH[a] = t.H + 2 * P - t.J[a] + 1;
+        t.YW[a] = t.W + 2 * P - t.J[a] + 1;
+        const int64_t qh = (t.Ho - a + 1) / 2, qw = (t.Wo - a + 1) / 2;
+        if (o < 0 || o + qh > t.YH[a] || o + qw > t.YW[a]) return IGC_DECLINE_PADDING;
+    }
+    size_t off = 0;
+    for (int ph = 0; ph < 4; ++ph) {
+        const int ah = ph >> 1, aw = ph & 1;
+        const int64_t fd[4] = {t.J[ah], t.J[aw], t.C, t.F};
+        const int64_t od[4] = {t.N, t.YH[ah], t.YW[aw], t.F};
+        const int32_t fp[2] = {t.P, t.P};
+        const int32_t rc = check_shapes(in_nhwc, 0, fd, od, one, one, fp, 1, dtype, &t.ph[ph]);
+        if (rc != IGC_OK) return rc;
+        const size_t ybytes = (size_t)(t.N * t.YH[ah] * t.YW[aw] * t.F) * 2;
+        t.nk_off[ph] = off;
+        off += align256((size_t)(t.F * t.ph[ph].kpitch * eb));
+        t.y_off[ph] = off;
+        off += align256(ybytes);
+        if (with_source) {
+            t.s_off[ph] = off;
+            off += align256(ybytes);
+        }
+    }
+    t.ws_bytes = off;
+    *tp = t;
+    return IGC_OK;
 }
 
-hipError_t launch_transpose_flipped(const void* filter, const Shape& s, int32_t dtype, void* nk,
-                                    hipStream_t stream) {
+// Pointer rules of the transposed convolution (as conv2d_fwd's, plus the
+// coefficient arrays of the epilogue against the workspace).
+int32_t transposed_pointers(const TPlan& t, int32_t dtype, const void* input, const void* filter,
+                            const void* output, const void* source, const igc_epilogue* epi,
+                            const void* workspace, size_t workspace_bytes) {
+    const size_t eb = (size_t)elem_bytes(dtype);
+    const size_t in_bytes = (size_t)(t.N * t.H * t.W * t.C) * eb;
+    const size_t f_bytes = (size_t)(t.R * t.R * t.F * t.C) * eb;
+    const size_t out_bytes = (size_t)(t.N * t.Ho * t.Wo * t.F) * 2;
+    if ((in_bytes && !input) || (f_bytes && !filter) || (out_bytes && !output))
+        return IGC_DECLINE_NULL_POINTER;
+    if (!aligned16(input) || !aligned16(filter) || !aligned16(output) || !aligned16(source) ||
+        !aligned16(workspace))
+        return IGC_DECLINE_ALIGNMENT;
+    if (overlaps(output, out_bytes, input, in_bytes) || overlaps(output, out_bytes, filter, f_bytes))
+        return IGC_DECLINE_OVERLAP;
+    if (source && source != output && overlaps(source, out_bytes, output, out_bytes))
+        return IGC_DECLINE_OVERLAP;
+    if (workspace) {
+        const size_t w = t.ws_bytes;
+        if (overlaps(workspace, w, output, out_bytes) || overlaps(workspace, w, input, in_bytes) ||
+            overlaps(workspace, w, filter, f_bytes) ||
+            (source && overlaps(workspace, w, source, out_bytes)))
+            return IGC_DECLINE_OVERLAP;
+        if (workspace_bytes < w) return IGC_DECLINE_WORKSPACE;
+        if (epi) {
+            for (const float* c : {epi->scale, epi->bias})
+                if (c && overlaps(c, (size_t)t.F * sizeof(float), workspace, w))
+                    return IGC_DECLINE_EPILOGUE;
+        }
+    }
+    Shape so{};
+    so.M = t.N * t.Ho * t.Wo;
+    so.F = t.F;
+    return check_epilogue(epi, output, so);
+}
+
+hipError_t launch_transpose_flipped(const void* filter, const TPlan& t, int ph, int32_t dtype,
+                                    void* nk, hipStream_t stream) {
     const int eb = elem_bytes(dtype);
+    const Shape& s = t.ph[ph];
     const int64_t chunks = s.F * (s.kpitch / (16 / eb));
     if (chunks == 0) return hipSuccess;
+    TapSel sel{};
+    sel.R = (int)t.R; sel.S = (int)t.R; sel.F = (int)t.F; sel.C = (int)t.C;
+    sel.st = t.st;
+    if (t.st == 1) {
+        sel.BH = sel.BW = 0;
+        sel.JH = sel.JW = (int)t.R;
+    } else {
+        sel.BH = t.B[ph >> 1]; sel.BW = t.B[ph & 1];
+        sel.JH = t.J[ph >> 1]; sel.JW = t.J[ph & 1];
+    }
+    sel.K = (int)s.K;
+    sel.kpitch = (int)s.kpitch;
     const unsigned blocks = (unsigned)((chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096);
     if (eb == 2)
         hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<2>, dim3(blocks), dim3(256), 0, stream,
-                           (const uint8_t*)filter, (uint8_t*)nk, (int)s.R, (int)s.S, (int)s.F,
-                           (int)s.C, (int)s.K, (int)s.kpitch);
+                           (const uint8_t*)filter, (uint8_t*)nk, sel);
     else
         hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<1>, dim3(blocks), dim3(256), 0, stream,
-                           (const uint8_t*)filter, (uint8_t*)nk, (int)s.R, (int)s.S, (int)s.F,
-                           (int)s.C, (int)s.K, (int)s.kpitch);
+                           (const uint8_t*)filter, (uint8_t*)nk, sel);
     return hipGetLastError();
+}
+
+hipError_t launch_interleave(const TPlan& t, uint8_t* ws, const void* src, void* dst, size_t* offs,
+                             int to_phase, hipStream_t stream) {
+    PhaseMap m{};
+    m.src = (const uint16_t*)src;
+    m.dst = (uint16_t*)dst;
+    for (int ph = 0; ph < 4; ++ph) m.phase[ph] = (uint16_t*)(ws + offs[ph]);
+    m.N = (int)t.N; m.Ho = (int)t.Ho; m.Wo = (int)t.Wo; m.F = (int)t.F;
+    for (int a = 0; a < 2; ++a) {
+        m.HY[a] = (int)t.YH[a]; m.WY[a] = (int)t.YW[a];
+        m.OH[a] = t.OH[a]; m.OW[a] = t.OW[a];
+    }
+    m.to_phase = to_phase;
+    const int64_t groups = (t.F % 8 == 0) ? t.F / 8 : t.F;
+    const int64_t total = t.N * t.Ho * t.Wo * groups;
+    if (total == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
+    hipLaunchKernelGGL(phase_interleave_kernel, dim3(blocks), dim3(256), 0, stream, m);
+    return hipGetLastError();
+}
+
+hipError_t run_transposed(const TPlan& t, const void* input, const void* filter, void* output,
+                          const void* source, float beta, const igc_epilogue* epi, int32_t dtype,
+                          uint8_t* ws, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    if (t.st == 1) {
+        e = launch_transpose_flipped(filter, t, 0, dtype, ws, stream);
+        if (e == hipSuccess) e = launch_igemm(input, ws, output, source, beta, epi, t.ph[0], dtype, stream);
+        return e;
+    }
+    size_t yoffs[4], soffs[4];
+    for (int ph = 0; ph < 4; ++ph) { yoffs[ph] = t.y_off[ph]; soffs[ph] = t.s_off[ph]; }
+    for (int ph = 0; ph < 4 && e == hipSuccess; ++ph)
+        e = launch_transpose_flipped(filter, t, ph, dtype, ws + t.nk_off[ph], stream);
+    if (e == hipSuccess && source) e = launch_interleave(t, ws, source, nullptr, soffs, 1, stream);
+    for (int ph = 0; ph < 4 && e == hipSuccess; ++ph)
+        e = launch_igemm(input, ws + t.nk_off[ph], ws + t.y_off[ph],
+                         source ? (const void*)(ws + t.s_off[ph]) : nullptr, beta, epi, t.ph[ph],
+                         dtype, stream);
+    if (e == hipSuccess) e = launch_interleave(t, ws, nullptr, output, yoffs, 0, stream);
+    return e;
 }
 
 }  // namespace
 
 extern "C" {
 
-size_t conv2d_transposed_workspace_bytes(const int64_t filt_rsfc[4], int32_t dtype) {
-    if (!filt_rsfc) return 0;
-    const int64_t fdims[4] = {filt_rsfc[0], filt_rsfc[1], filt_rsfc[3], filt_rsfc[2]};
-    return conv2d_workspace_bytes(fdims, 0, dtype);
+size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
+                                         const int32_t stride[2], const int32_t padding[2],
+                                         int32_t dtype, int32_t with_source) {
+    if (!in_nhwc || !filt_rsfc || !stride || !padding) return 0;
+    const int32_t dil[2] = {1, 1};
+    const int64_t R = filt_rsfc[0], p = padding[0], st = stride[0];
+    const int64_t od[4] = {in_nhwc[0], (in_nhwc[1] - 1) * st - 2 * p + R,
+                           (in_nhwc[2] - 1) * st - 2 * p + filt_rsfc[1], filt_rsfc[2]};
+    TPlan t;
+    if (transposed_plan(in_nhwc, filt_rsfc, od, stride, dil, padding, dtype, with_source != 0,
+                        &t) != IGC_OK)
+        return 0;
+    return t.ws_bytes;
 }
 
 int32_t conv2d_transposed_check(const void* input, const int64_t in_nhwc[4], const void* filter,
@@ -645,17 +832,12 @@ int32_t conv2d_transposed_check(const void* input, const int64_t in_nhwc[4], con
                                 const igc_epilogue* epilogue, const void* workspace,
                                 size_t workspace_bytes) {
     (void)beta;
-    Shape s;
-    int32_t rc = transposed_shape(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding,
-                                  dtype, &s);
+    TPlan t;
+    const int32_t rc = transposed_plan(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding,
+                                       dtype, source != nullptr, &t);
     if (rc != IGC_OK) return rc;
-    const int64_t fdims[4] = {s.R, s.S, s.C, s.F};
-    const int32_t one[2] = {1, 1};
-    const int32_t fp[2] = {s.pad, s.pad};
-    rc = check_all(input, in_nhwc, filter, 0, 0, fdims, output, out_nhwc, one, one, fp, 1, dtype,
-                   source, workspace, workspace_bytes, &s);
-    if (rc != IGC_OK) return rc;
-    return check_epilogue(epilogue, output, s);
+    return transposed_pointers(t, dtype, input, filter, output, source, epilogue, workspace,
+                               workspace_bytes);
 }
 
 int32_t conv2d_transposed_fwd(const void* input, const int64_t in_nhwc[4], const void* filter,
@@ -669,27 +851,26 @@ int32_t conv2d_transposed_fwd(const void* input, const int64_t in_nhwc[4], const
                                 dilation, padding, dtype, source, beta, epilogue, workspace,
                                 workspace_bytes) != IGC_OK)
         return 0;
-    Shape s;
-    transposed_shape(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding, dtype, &s);
-    if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
+    TPlan t;
+    transposed_plan(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding, dtype,
+                    source != nullptr, &t);
+    if (t.N == 0 || t.F == 0) return 1;  // empty output: nothing to compute
     hipStream_t st = (hipStream_t)stream;
-    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
-    void* nk = workspace;
+    void* ws = workspace;
     bool owned = false;
-    if (!nk && nk_bytes) {
-        hipError_t e = hipMallocAsync(&nk, nk_bytes, st);
+    if (!ws && t.ws_bytes) {
+        hipError_t e = hipMallocAsync(&ws, t.ws_bytes, st);
         if (e != hipSuccess) return -(int32_t)e;
         owned = true;
     }
-    hipError_t e = launch_transpose_flipped(filter, s, dtype, nk, st);
-    if (e == hipSuccess) e = launch_igemm(input, nk, output, source, beta, epilogue, s, dtype, st);
+    hipError_t e = run_transposed(t, input, filter, output, source, beta, epilogue, dtype,
+                                  (uint8_t*)ws, st);
     if (owned) {
-        hipError_t f = hipFreeAsync(nk, st);
+        hipError_t f = hipFreeAsync(ws, st);
         if (e == hipSuccess) e = f;
     }
     return hip_fail(e);
 }
-
 
 size_t conv2d_im2col_bytes(const int64_t in_nhwc[4], const int64_t filt_rs[2],
                            const int32_t stride[2], const int32_t padding[2], int32_t dtype) {

@@ -299,16 +299,26 @@ size_t conv2d_im2col_bytes(const int64_t in_nhwc[4], const int64_t filt_rs[2],
  * i.e. the adjoint of the forward convolution whose RSCF filter is W.  Then
  * the same fused epilogue as conv2d_fwd_epilogue (scale, bias, residual
  * source, activation; all optional) and one rounding.
- * Supported here: stride (1,1), dilation (1,1), a square filter (R == S) and
- * symmetric padding p with R - 1 - p in {0, 1, 2}: the call is then the
- * forward convolution of the input with the filter flipped in both taps and
- * its channel roles swapped, at padding R - 1 - p, which runs on the same
- * implicit-GEMM kernels (the flip is a 16-byte chunk permutation done by the
- * NK transpose).  Other shapes are declined (stride, dilation or padding
- * codes); dtypes, layouts, alignment and overlap rules as conv2d_fwd.
+ * Supported here: stride (1,1) or (2,2), dilation (1,1), a square filter
+ * (R == S) and symmetric padding p.  Every case runs on the forward
+ * implicit-GEMM kernels over the input:
+ *   stride 1: one forward convolution with the filter flipped in both taps
+ *     and its channel roles swapped, at padding R - 1 - p (needs
+ *     R - 1 - p in {0, 1, 2});
+ *   stride 2 (R >= 2): the output rows and columns of each parity take the
+ *     filter taps of one parity; each of the four (row, column) parities is
+ *     a forward convolution with that tap subset, flipped, at one padding P
+ *     in {0, 1, 2}, into a phase buffer of the workspace, and a final pass
+ *     interleaves the phases into the output.  A residual source is split
+ *     into phase buffers first, so every output element still gets the
+ *     fused epilogue and one rounding in the GEMM.
+ * (The flips are 16-byte chunk permutations done by the NK transpose.)
+ * Other shapes are declined (stride, dilation, padding or shape codes);
+ * dtypes, layouts, alignment and overlap rules as conv2d_fwd.
  *   in_nhwc = {N, H, W, C}, filt_rsfc = {R, S, F, C}, out_nhwc = {N, Ho, Wo, F}
  *   workspace: at least conv2d_transposed_workspace_bytes(), or NULL
- *   (stream-ordered allocation as in conv2d_fwd).
+ *   (stream-ordered allocation as in conv2d_fwd); source == output is
+ *   allowed.
  * Returns 1 = handled, 0 = declined (conv2d_transposed_check gives the
  * reason), or -(hipError_t).
  */
@@ -331,8 +341,12 @@ int32_t conv2d_transposed_check(const void* input, const int64_t in_nhwc[4],
                                 const igc_epilogue* epilogue,
                                 const void* workspace, size_t workspace_bytes);
 
-/* Bytes of the flipped NK matrix conv2d_transposed_fwd needs. */
-size_t conv2d_transposed_workspace_bytes(const int64_t filt_rsfc[4], int32_t dtype);
+/* Workspace conv2d_transposed_fwd needs for this problem (NK matrices, and
+ * for stride 2 the phase buffers; with_source = the call passes a source);
+ * 0 if the problem would be declined. */
+size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
+                                         const int32_t stride[2], const int32_t padding[2],
+                                         int32_t dtype, int32_t with_source);
 
 #ifdef __cplusplus
 }

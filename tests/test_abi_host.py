@@ -277,8 +277,26 @@ def _tcheck(**kw):
 
 def test_transposed_workspace_bytes():
     # equivalent forward filter RSCF {3, 3, 32, 48}: K = 288 -> 320 (+8 for C_out <= 64)
-    assert igc.conv2d_transposed_workspace_bytes((3, 3, 48, 32), torch.bfloat16) == 48 * 328 * 2
-    assert igc.conv2d_transposed_workspace_bytes((3, 3, 48, 32), 9) == 0
+    ws = igc.conv2d_transposed_workspace_bytes
+    assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=1, padding=1,
+              dtype=torch.bfloat16) == 48 * 328 * 2
+    assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=1, padding=1, dtype=9) == 0
+    # stride 2, R = 3, p = 1: phases of 1 and 2 taps per axis at padding 0,
+    # phase outputs 9 or 8 rows/columns; NK rows of K = 32, 64, 64, 128
+    # elements (+8 pad) and bf16 phase buffers, each 256-byte aligned
+    def al(v):
+        return (v + 255) // 256 * 256
+    want = 0
+    for jh, jw in ((1, 1), (1, 2), (2, 1), (2, 2)):
+        k = jh * jw * 32
+        kp = (k + 63) // 64 * 64 + 8
+        y = 2 * (10 - jh) * (10 - jw) * 48 * 2
+        want += al(48 * kp * 2) + al(y)
+    assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=2, padding=1,
+              dtype=torch.bfloat16) == want
+    assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=2, padding=1, dtype=torch.bfloat16,
+              with_source=True) > want
+    assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=3, padding=1, dtype=torch.bfloat16) == 0
 
 
 @pytest.mark.parametrize("kw,reason", [
@@ -287,7 +305,13 @@ def test_transposed_workspace_bytes():
     (dict(padding=0, out_shape=(2, 11, 11, 48)), "ok"),          # R - 1 - p = 2
     (dict(filt_shape=(5, 5, 48, 32), padding=2), "ok"),
     (dict(filt_shape=(4, 4, 48, 32), padding=1, out_shape=(2, 10, 10, 48)), "ok"),
-    (dict(stride=2, out_shape=(2, 17, 17, 48)), "stride"),
+    (dict(stride=2, out_shape=(2, 17, 17, 48)), "ok"),
+    (dict(stride=2, padding=2, filt_shape=(4, 4, 48, 32), out_shape=(2, 16, 16, 48)), "ok"),
+    (dict(stride=3, out_shape=(2, 25, 25, 48)), "stride"),
+    (dict(stride=(2, 1), out_shape=(2, 17, 9, 48)), "stride"),
+    (dict(stride=2, filt_shape=(1, 1, 48, 32), padding=0, out_shape=(2, 17, 17, 48)), "shape"),
+    (dict(stride=2, out_shape=(2, 18, 18, 48)), "output_shape"),
+    (dict(stride=2, out_shape=(2, 17, 17, 48), workspace=WS, workspace_bytes=1024), "workspace"),
     (dict(dilation=2), "dilation"),
     (dict(padding=3), "padding"),                                # R - 1 - p < 0
     (dict(filt_shape=(5, 5, 48, 32), padding=1, out_shape=(2, 11, 11, 48)), "padding"),
@@ -305,8 +329,8 @@ def test_transposed_decline_paths(kw, reason):
 
 
 def test_transposed_declined_call_enqueues_nothing():
-    assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "stride": 2,
-                                                 "out_shape": (2, 17, 17, 48)}) == 0
+    assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "stride": 3,
+                                                 "out_shape": (2, 25, 25, 48)}) == 0
     assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "dilation": 2}) == 0
     args = dict(TBASE, in_shape=(0, 9, 9, 32), out_shape=(0, 9, 9, 48))
     assert igc.conv2d_transposed_fwd(X, W, Y, **args) == 1

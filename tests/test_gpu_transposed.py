@@ -32,21 +32,28 @@ def _say(msg):
 
 
 CASES = [
-    # dtype, N, H, W, C, F, R, pad, residual/epilogue, kernel it lands on
-    ("bfloat16", 2, 20, 18, 32, 48, 3, 1, False, "band"),
-    ("float16", 2, 16, 16, 64, 96, 3, 0, True, "wide"),
-    ("float8_e4m3fn", 2, 14, 15, 64, 32, 5, 2, True, "band"),
-    ("bfloat16", 1, 12, 12, 128, 130, 1, 0, False, "wide"),
-    ("bfloat16", 2, 17, 9, 32, 16, 2, 0, True, "band"),
-    ("float16", 1, 24, 24, 64, 64, 4, 1, False, "band"),
-    ("bfloat16", 8, 32, 32, 256, 128, 3, 1, True, "wide"),
+    # dtype, N, H, W, C, F, R, stride, pad, residual/epilogue
+    ("bfloat16", 2, 20, 18, 32, 48, 3, 1, 1, False),
+    ("float16", 2, 16, 16, 64, 96, 3, 1, 0, True),
+    ("float8_e4m3fn", 2, 14, 15, 64, 32, 5, 1, 2, True),
+    ("bfloat16", 1, 12, 12, 128, 130, 1, 1, 0, False),
+    ("bfloat16", 2, 17, 9, 32, 16, 2, 1, 0, True),
+    ("float16", 1, 24, 24, 64, 64, 4, 1, 1, False),
+    ("bfloat16", 8, 32, 32, 256, 128, 3, 1, 1, True),
+    # stride 2: four phase convolutions and the interleave
+    ("bfloat16", 2, 16, 12, 32, 48, 4, 2, 1, False),     # the 2x upsampler
+    ("float16", 2, 11, 13, 64, 96, 3, 2, 1, True),
+    ("float8_e4m3fn", 1, 10, 9, 64, 32, 2, 2, 0, True),
+    ("bfloat16", 1, 9, 10, 32, 20, 5, 2, 2, True),       # C_out not a multiple of 8
+    ("bfloat16", 2, 8, 8, 64, 130, 3, 2, 0, False),
+    ("float16", 1, 12, 12, 32, 16, 6, 2, 2, True),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_transposed_matches_oracle(case):
-    dt, n, h, w, c, f, r, p, fused, kern = case
-    ho, wo = h - 1 - 2 * p + r, w - 1 - 2 * p + r
+    dt, n, h, w, c, f, r, st, p, fused = case
+    ho, wo = (h - 1) * st - 2 * p + r, (w - 1) * st - 2 * p + r
     _say(f"transposed {case} -> out {n}x{ho}x{wo}x{f}")
     seed = zlib.crc32(repr(case).encode()) % 1000
     x, wfwd, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=r, dtype=dt, fcrs=False,
@@ -55,13 +62,7 @@ def test_transposed_matches_oracle(case):
                                      out_hw=(ho, wo), seed=seed)
     # an RSFC filter [R, S, F, C]: the seeded RSCF draw [R, S, C, F] re-laid out
     wt = wfwd.permute(0, 1, 3, 2).contiguous()
-    # the equivalent forward problem is what decides the kernel
-    assert igc.conv2d_fwd_kernel_name((n, h, w, c), (r, r, c, f), (n, ho, wo, f),
-                                      filter_is_fcrs=False, dtype=x.dtype, stride=1,
-                                      padding=r - 1 - p).endswith(
-        {"band": "band_kernel", "wide": "wide_kernel"}[kern])
-    kw = {}
-    okw = {}
+    kw, okw = {}, {}
     if fused:
         g = torch.Generator().manual_seed(seed + 1)
         scale = (torch.rand(f, generator=g) + 0.5).float()
@@ -69,8 +70,36 @@ def test_transposed_matches_oracle(case):
         kw = dict(source=src.to(DEV), beta=0.5, scale=scale.to(DEV), bias=bias.to(DEV),
                   activation="silu")
         okw = dict(source=src, beta=0.5, scale=scale, bias=bias, act="silu")
-    out = igc.conv2d_transposed(x.to(DEV), wt.to(DEV), stride=1, padding=p, **kw)
+    out = igc.conv2d_transposed(x.to(DEV), wt.to(DEV), stride=st, padding=p, **kw)
     torch.cuda.synchronize()
     assert tuple(out.shape) == (n, ho, wo, f)
-    ref = oracle.conv2d_transposed(x, wt, stride=1, padding=p, **okw)
+    ref = oracle.conv2d_transposed(x, wt, stride=st, padding=p, **okw)
     _assert_close(out, ref, TOL[dt], str(case))
+
+
+def test_transposed_stride2_in_place_and_workspace():
+    # source == output (in place) with a caller workspace, against the
+    # library-allocated, separate-source call: bitwise equal
+    n, h, w, c, f, r, st, p = 2, 12, 10, 64, 64, 4, 2, 1
+    ho, wo = (h - 1) * st - 2 * p + r, (w - 1) * st - 2 * p + r
+    x, wfwd, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=r, dtype="bfloat16",
+                                     fcrs=False, x_dist=("normal", 1.0),
+                                     w_dist=("normal", 0.1), src_dist=("normal", 1.0),
+                                     out_hw=(ho, wo), seed=5)
+    wt = wfwd.permute(0, 1, 3, 2).contiguous().to(DEV)
+    xd, sd = x.to(DEV), src.to(DEV)
+    a = torch.empty((n, ho, wo, f), dtype=torch.bfloat16, device=DEV)
+    assert igc.conv2d_transposed_fwd(xd, wt, a, stride=st, padding=p, source=sd, beta=-1.5,
+                                     activation="relu") == 1
+    b = sd.clone()
+    ws = torch.empty(igc.conv2d_transposed_workspace_bytes(x.shape, wt.shape, stride=st,
+                                                           padding=p, dtype=x.dtype,
+                                                           with_source=True),
+                     dtype=torch.uint8, device=DEV)
+    assert igc.conv2d_transposed_fwd(xd, wt, b, stride=st, padding=p, source=b, beta=-1.5,
+                                     activation="relu", workspace=ws) == 1
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.conv2d_transposed(x, wt.cpu(), stride=st, padding=p, source=src, beta=-1.5,
+                                   act="relu")
+    _assert_close(a, ref, TOL["bfloat16"], "in place")
