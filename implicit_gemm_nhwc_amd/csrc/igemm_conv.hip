@@ -200,7 +200,8 @@ hipError_t launch_tile(ConvArgs a, hipStream_t stream) {
     a.co_tiles = (a.F + BCO - 1) / BCO;
     const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NTHREADS), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
+                       dim3(NTHREADS), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -224,7 +225,8 @@ hipError_t launch_resident(ConvArgs a, hipStream_t stream) {
     const int64_t wtiles = ((int64_t)a.M + kResidentTN * 16 - 1) / (kResidentTN * 16);
     const int64_t blocks = (wtiles + RES_WAVES - 1) / RES_WAVES;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(RES_WAVES * 64), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
+                       dim3(RES_WAVES * 64), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -367,7 +369,8 @@ hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
         a.cpp_log2 = log2_exact(a.C * E / 16);
     }
     if (bp.tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)bp.tiles), dim3(BAND_WAVES * 64), (size_t)bp.lds,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(bp.tiles * (a.groups > 1 ? a.groups : 1))),
+                       dim3(BAND_WAVES * 64), (size_t)bp.lds,
                        stream, a);
     return hipGetLastError();
 }
@@ -399,14 +402,15 @@ hipError_t launch_band_dt(const ConvArgs& a, const BandPlan& bp, hipStream_t str
 }
 
 // ---- wide-layer kernel with direct-to-LDS staging ---------------------------
-template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK>
+template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK,
+          bool GROUPED = false>
 hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
     constexpr int BCO = WCO * TM * 32, BPX = WPX * TN * 32;
     constexpr size_t lds = (size_t)NSTAGE * (BCO + BPX) * KTB;
     static_assert(lds <= (size_t)kLdsBytes, "stages fit in LDS");
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
-    auto kern = igemm_fwd_wide_kernel<DT, TM, TN, WCO, WPX, KTB, NSTAGE, RESID, TAPK>;
+    auto kern = igemm_fwd_wide_kernel<DT, TM, TN, WCO, WPX, KTB, NSTAGE, RESID, TAPK, GROUPED>;
     std::call_once(once, [&] {
         attr_err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -417,7 +421,8 @@ hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
     a.co_tiles = (a.F + BCO - 1) / BCO;
     const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WCO * WPX * 64), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
+                       dim3(WCO * WPX * 64), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -440,6 +445,9 @@ hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     const bool tap128 = a.C > 0 && (a.C * E) % 128 == 0;
     const int64_t co_tiles256 = (a.F + 255) / 256;
     const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
+    if (a.groups > 1)   // grouped launches: 128 x 128 tiles only
+        return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, true, true>(a, stream)
+                      : launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, false, true>(a, stream);
     if (a.F > 128 && px_tiles256 * co_tiles256 >= kNumCUs)
         return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
                       : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
@@ -479,10 +487,24 @@ KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp) {
     return K_TILED;
 }
 
+// Several problems of one shape in one launch (the phases of a stride-2
+// transposed convolution): NK matrices, outputs and sources a fixed byte
+// stride apart.
+struct Group {
+    int n;
+    int64_t nk, y, src;
+};
+
 hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
                         float beta, const igc_epilogue* epi, const Shape& s, int32_t dtype,
-                        hipStream_t stream) {
+                        hipStream_t stream, const Group* grp = nullptr) {
     ConvArgs a{};
+    if (grp && grp->n > 1) {
+        a.groups = grp->n;
+        a.g_nk = grp->nk;
+        a.g_y = grp->y;
+        a.g_src = grp->src;
+    }
     a.x = (const uint8_t*)input;
     a.nk = (const uint8_t*)nk;
     a.y = (uint16_t*)output;
@@ -797,10 +819,21 @@ hipError_t run_transposed(const TPlan& t, const void* input, const void* filter,
     for (int ph = 0; ph < 4 && e == hipSuccess; ++ph)
         e = launch_transpose_flipped(filter, t, ph, dtype, ws + t.nk_off[ph], stream);
     if (e == hipSuccess && source) e = launch_interleave(t, ws, source, nullptr, soffs, 1, stream);
-    for (int ph = 0; ph < 4 && e == hipSuccess; ++ph)
-        e = launch_igemm(input, ws + t.nk_off[ph], ws + t.y_off[ph],
-                         source ? (const void*)(ws + t.s_off[ph]) : nullptr, beta, epi, t.ph[ph],
-                         dtype, stream);
+    if (t.J[0] == t.J[1]) {
+        // every phase has the same shape (even R): one grouped launch, the
+        // phases' buffers a fixed stride apart in the workspace
+        const Group g{4, (int64_t)(t.nk_off[1] - t.nk_off[0]), (int64_t)(t.y_off[1] - t.y_off[0]),
+                      source ? (int64_t)(t.s_off[1] - t.s_off[0]) : 0};
+        if (e == hipSuccess)
+            e = launch_igemm(input, ws + t.nk_off[0], ws + t.y_off[0],
+                             source ? (const void*)(ws + t.s_off[0]) : nullptr, beta, epi,
+                             t.ph[0], dtype, stream, &g);
+    } else {
+        for (int ph = 0; ph < 4 && e == hipSuccess; ++ph)
+            e = launch_igemm(input, ws + t.nk_off[ph], ws + t.y_off[ph],
+                             source ? (const void*)(ws + t.s_off[ph]) : nullptr, beta, epi,
+                             t.ph[ph], dtype, stream);
+    }
     if (e == hipSuccess) e = launch_interleave(t, ws, nullptr, output, yoffs, 0, stream);
     return e;
 }

@@ -53,6 +53,10 @@ struct ConvArgs {
     const float* bias;    // [C_out] addend, or null (0)
     int act;              // ACT_NONE, ACT_RELU or ACT_SILU
     int epi;              // nonzero when scale, bias or act is present
+    // grouped launch: `groups` problems of the same shape whose NK matrix,
+    // output and source lie g_nk, g_y and g_src bytes apart (0 or 1 = one)
+    int groups;
+    int64_t g_nk, g_y, g_src;
     int H, W, C;        // input (N only enters through M)
     int Ho, Wo, F;      // output spatial size and C_out
     int S, stride, pad;
@@ -83,6 +87,23 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     const int q = n / X, rem = n % X;
     const int x = b % X, j = b / X;
     return x * q + (x < rem ? x : rem) + j;
+}
+
+// The block index within this workgroup's problem of a grouped launch
+// (gridDim.x = groups * per), after moving the NK, output and source
+// pointers to that problem.  A launch of one problem returns blockIdx.x.
+__device__ __forceinline__ int group_block(ConvArgs& a, int per) {
+    int b = blockIdx.x;
+    if (a.groups > 1) {
+        const int gi = b / per;
+        b -= gi * per;
+        a.nk += gi * a.g_nk;
+        a.y = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.y) + gi * a.g_y);
+        if (a.src)
+            a.src = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.src) +
+                                                      gi * a.g_src);
+    }
+    return b;
 }
 
 // LDS tiles: rows of 128 bytes, chunk c of row r stored at c ^ ((r >> 1) & 7)
@@ -274,7 +295,7 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
     const int wave = tid >> 6;
     const int wco = wave / WPX, wpx = wave % WPX;
 
-    const int tile = xcd_remap(blockIdx.x, a.px_tiles * a.co_tiles);
+    const int tile = xcd_remap(group_block(a, a.px_tiles * a.co_tiles), a.px_tiles * a.co_tiles);
     const int co_tile = tile % a.co_tiles;
     const int px_tile = tile / a.co_tiles;
     const int co0 = co_tile * BCO;
@@ -517,6 +538,9 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
     // buffer descriptors derived from it in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lpitch = a.kpitch * E;  // includes the 16-byte pad: conflict-free fragment reads
+    // this workgroup's problem of a grouped launch (before any pointer use)
+    const int per = a.groups > 1 ? (int)gridDim.x / a.groups : (int)gridDim.x;
+    const int gblock = group_block(a, per);
 
     // ---- stage the filter (all of K) in LDS, rows >= C_out as zeros.
     // NK rows already carry their 16-byte zero pad, so the LDS image is the
@@ -538,7 +562,7 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
     __syncthreads();
 
     const int n_wtiles = (a.M + TN * 16 - 1) / (TN * 16);
-    const int wtile = xcd_remap(blockIdx.x, gridDim.x) * RES_WAVES + wave;
+    const int wtile = xcd_remap(gblock, per) * RES_WAVES + wave;
     if (wtile >= n_wtiles) return;  // no barrier follows
     const int m0 = wtile * TN * 16;
 
@@ -826,7 +850,8 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     const int half = lane >> 5;
 
     const int per_img = a.tiles_h * a.tiles_w;
-    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int per = a.groups > 1 ? (int)gridDim.x / a.groups : (int)gridDim.x;
+    const int tile = xcd_remap(group_block(a, per), per);
     const int n = tile / per_img;
     const int trem = tile - n * per_img;
     const int oh0 = (trem / a.tiles_w) * a.TH;
@@ -1180,7 +1205,11 @@ template <>
 struct WideStep<DT_FP8> { static constexpr int KSB = 64; };
 
 
-template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK>
+// GROUPED: a grouped launch (group_block); a compile-time choice here, since
+// the runtime pointer selection costs the single-problem 256x256 fp8 kernel
+// twelve VGPRs and a quarter of its speed.
+template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK,
+          bool GROUPED = false>
 __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs a) {
     constexpr int E = DtTraits<DT>::E;
     constexpr int VEC = 16 / E;
@@ -1207,7 +1236,8 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wco = wave / WPX, wpx = wave % WPX;
 
-    const int tile = xcd_remap(blockIdx.x, a.px_tiles * a.co_tiles);
+    const int ntile = a.px_tiles * a.co_tiles;
+    const int tile = xcd_remap(GROUPED ? group_block(a, ntile) : (int)blockIdx.x, ntile);
     const int co_tile = tile % a.co_tiles;
     const int px_tile = tile / a.co_tiles;
     const int co0 = co_tile * BCO;

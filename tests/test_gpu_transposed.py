@@ -47,6 +47,10 @@ CASES = [
     ("bfloat16", 1, 9, 10, 32, 20, 5, 2, 2, True),       # C_out not a multiple of 8
     ("bfloat16", 2, 8, 8, 64, 130, 3, 2, 0, False),
     ("float16", 1, 12, 12, 32, 16, 6, 2, 2, True),
+    # even R: the four phases share one shape and run as one grouped launch
+    # (band kernel above for R = 4, 2, 6; wide kernel here)
+    ("bfloat16", 2, 10, 12, 64, 96, 4, 2, 1, True),
+    ("float8_e4m3fn", 1, 8, 8, 128, 256, 2, 2, 0, False),
 ]
 
 
