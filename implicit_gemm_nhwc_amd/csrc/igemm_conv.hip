@@ -143,6 +143,28 @@ int32_t check_all(const void* input, const int64_t in_nhwc[4], const void* filte
 
 int32_t hip_fail(hipError_t e) { return e == hipSuccess ? 1 : -(int32_t)e; }
 
+// hipFuncSetAttribute acts on the current device, so the dynamic-LDS limit
+// of each kernel is raised once per device (the first launch there).
+constexpr int kMaxDevices = 64;
+struct LdsAttr {
+    std::mutex mu;
+    bool done[kMaxDevices] = {};
+    hipError_t err[kMaxDevices] = {};
+};
+
+hipError_t ensure_lds(LdsAttr& at, const void* kern, size_t lds) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(at.mu);
+    if (!at.done[dev]) {
+        at.err[dev] = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        at.done[dev] = true;
+    }
+    return at.err[dev];
+}
+
 // The fused epilogue's own gate: a known activation, 4-byte aligned
 // coefficient arrays, and none of them overlapping the output (every
 // workgroup reads them while others write the output).
@@ -188,13 +210,9 @@ hipError_t launch_transpose(const void* filter, int32_t fcrs, const Shape& s, in
 template <int DT, int BCO, int BPX, int WCO, int WPX, bool RESID>
 hipError_t launch_tile(ConvArgs a, hipStream_t stream) {
     constexpr size_t lds = 2 * (size_t)(BCO + BPX) * KT_BYTES;
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
     auto kern = igemm_fwd_kernel<DT, BCO, BPX, WCO, WPX, RESID>;
-    std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    });
+    static LdsAttr attr;
+    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)(lds));
     if (attr_err != hipSuccess) return attr_err;
     a.px_tiles = (a.M + BPX - 1) / BPX;
     a.co_tiles = (a.F + BCO - 1) / BCO;
@@ -211,14 +229,9 @@ constexpr int kResidentTN = 4;                   // 64 pixels per wave
 template <int DT, int TM, bool RESID, bool ALIGNED>
 hipError_t launch_resident(ConvArgs a, hipStream_t stream) {
     constexpr int E = DtTraits<DT>::E;
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
     auto kern = igemm_fwd_resident_kernel<DT, TM, kResidentTN, RESID, ALIGNED>;
-    std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kResidentLdsMax);
-    });
+    static LdsAttr attr;
+    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, kResidentLdsMax);
     if (attr_err != hipSuccess) return attr_err;
     // the filter is staged in whole 1 KB blocks: round the allocation up
     const size_t lds = ((size_t)TM * 16 * ((size_t)a.kpitch * E) + 1023) / 1024 * 1024;
@@ -351,13 +364,9 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
 
 template <int DT, int TM, int TN, int U, bool RESID>
 hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
     auto kern = igemm_fwd_band_kernel<DT, TM, TN, U, RESID>;
-    std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    });
+    static LdsAttr attr;
+    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, kLdsBytes);
     if (attr_err != hipSuccess) return attr_err;
     a.TH = bp.TH; a.TW = bp.TW; a.PH = bp.PH; a.PW = bp.PW;
     a.tiles_h = bp.tiles_h; a.tiles_w = bp.tiles_w;
@@ -408,13 +417,9 @@ hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
     constexpr int BCO = WCO * TM * 32, BPX = WPX * TN * 32;
     constexpr size_t lds = (size_t)NSTAGE * (BCO + BPX) * KTB;
     static_assert(lds <= (size_t)kLdsBytes, "stages fit in LDS");
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
     auto kern = igemm_fwd_wide_kernel<DT, TM, TN, WCO, WPX, KTB, NSTAGE, RESID, TAPK, GROUPED>;
-    std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    });
+    static LdsAttr attr;
+    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)(lds));
     if (attr_err != hipSuccess) return attr_err;
     a.ktiles = a.ktiles * (KT_BYTES / KTB);   // NK rows hold whole 128-byte k-tiles
     a.px_tiles = (a.M + BPX - 1) / BPX;
