@@ -106,11 +106,15 @@ class Bufsets:
 
     def step(self, igc, i):
         """One step on set i: the filter transpose, then the GEMM kernel."""
+        self.transpose(igc, i)
+        self.fwd_only(igc, i)
+
+    def transpose(self, igc, i):
+        """The filter transpose of set i into its NK matrix."""
         b = self.sets[i % self.nsets]
         rc = igc.conv2d_filter_to_nk(b["w"], b["nk"], filter_is_fcrs=self.fcrs)
         if rc != 1:
             raise RuntimeError(f"conv2d_filter_to_nk returned {rc}")
-        self.fwd_only(igc, i)
 
     def fwd_only(self, igc, i):
         """The GEMM kernel alone on set i (its NK matrix already made)."""
@@ -361,12 +365,13 @@ def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES, graphs=T
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern_ms = kernel_times(torch, igc, bufs, steps)
+    transpose_us = event_time(torch, lambda i: bufs.transpose(igc, i), steps)
     flops, nbytes = _algorithmic(spec)
     ms_step = (t1 - t0) * 1e3 / steps
     bound, peak_t = _bound(spec, flops, nbytes)
     res = dict(workload=name, dtype=spec["dtype"], ms_per_step=ms_step,
                step_tflops=flops / (ms_step * 1e-3) / 1e12,
-               kernel_us_mean=kern_ms * 1e3,
+               kernel_us_mean=kern_ms * 1e3, transpose_us_mean=transpose_us,
                kernel_tflops=flops / (kern_ms * 1e-3) / 1e12,
                kernel_gbs=nbytes / (kern_ms * 1e-3) / 1e9, flops=flops, alg_bytes=nbytes,
                bound=bound, rotating_sets=bufs.nsets,
@@ -495,7 +500,8 @@ def main():
                                  rotate)
             shapes[name] = {k: (round(v, 4) if isinstance(v, float) else v)
                             for k, v in r.items() if k not in ("flops", "alg_bytes")}
-            print(f"# {name}: step {r['ms_per_step'] * 1e3:.1f} us, kernel "
+            print(f"# {name}: step {r['ms_per_step'] * 1e3:.1f} us, transpose "
+                  f"{r['transpose_us_mean']:.1f} us, kernel "
                   f"{r['kernel_us_mean']:.1f} us = {r['kernel_tflops']:.1f} TFLOP/s "
                   f"({100 * r['frac_mfma']:.1f}% MFMA peak), {r['kernel_gbs']:.0f} GB/s "
                   f"({100 * r['frac_hbm']:.1f}% HBM), bound {r['bound']}",
