@@ -5,6 +5,7 @@ oracle (oracle.conv2d_epilogue), on one case per kernel variant the
 dispatcher can pick.  Tolerances as for the plain convolution: the epilogue
 adds a few fp32 operations before the single rounding to the output type.
 """
+import itertools
 import os
 import sys
 import zlib
@@ -129,3 +130,38 @@ def test_epilogue_nk_entry_matches_fwd():
                                       dtype=1, in_shape=x.shape) == 1
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _epi_sweep():
+    rng = np.random.default_rng(77)
+    cases = []
+    for i, (dt, fcrs, st, act) in enumerate(itertools.product(
+            ["bfloat16", "float16", "float8_e4m3fn"], [False, True], [1, 2],
+            ["relu", "silu"])):
+        f = int(rng.choice([1, 3, 8, 17, 40, 64, 72, 130]))
+        c = int(rng.choice([16, 32, 64] if dt != "float8_e4m3fn" else [16, 32, 64, 128]))
+        r = int(rng.choice([1, 3, 5]))
+        p = int(rng.integers(0, 3)) if r > 1 else 0
+        h, w = int(rng.integers(max(r, 4), 20)), int(rng.integers(max(r, 4), 20))
+        cases.append((dt, fcrs, st, act, bool(i % 2), int(rng.integers(1, 3)), h, w, c, f, r, p))
+    return cases
+
+
+@pytest.mark.parametrize("case", _epi_sweep(), ids=lambda c: "-".join(map(str, c)))
+def test_epilogue_random_sweep(case):
+    dt, fcrs, st, act, resid, n, h, w, c, f, r, p = case
+    ho, wo = oracle.out_size(h, r, st, p), oracle.out_size(w, r, st, p)
+    _say(f"epilogue sweep {case} -> out {n}x{ho}x{wo}x{f}")
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=r, dtype=dt, fcrs=fcrs,
+                                   x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0) if resid else None,
+                                   out_hw=(ho, wo), seed=zlib.crc32(repr(case).encode()) % 1000)
+    scale, bias = _coefs(f, zlib.crc32(repr(case).encode()) % 997)
+    beta = 0.75 if resid else 0.0
+    out = igc.conv2d(x.to(DEV), wt.to(DEV), filter_is_fcrs=fcrs, stride=st, padding=p,
+                     source=None if src is None else src.to(DEV), beta=beta,
+                     scale=scale.to(DEV), bias=bias.to(DEV), activation=act)
+    torch.cuda.synchronize()
+    ref = oracle.conv2d_epilogue(x, wt, filter_is_fcrs=fcrs, stride=st, padding=p, source=src,
+                                 beta=beta, scale=scale, bias=bias, act=act)
+    _assert_close(out, ref, TOL[dt], str(case))

@@ -4,10 +4,12 @@ oracle (oracle.conv2d_transposed, a scatter-form implementation pinned by
 hand-worked cases, brute force and the adjoint identity with conv2d).
 Tolerances as for the forward convolution.
 """
+import itertools
 import os
 import sys
 import zlib
 
+import numpy as np
 import pytest
 import torch
 
@@ -107,3 +109,48 @@ def test_transposed_stride2_in_place_and_workspace():
     ref = oracle.conv2d_transposed(x, wt.cpu(), stride=st, padding=p, source=src, beta=-1.5,
                                    act="relu")
     _assert_close(a, ref, TOL["bfloat16"], "in place")
+
+
+def _tr_sweep():
+    rng = np.random.default_rng(91)
+    cases = []
+    for i, (dt, st, r) in enumerate(itertools.product(
+            ["bfloat16", "float16", "float8_e4m3fn"], [1, 2], [2, 3, 4, 5])):
+        # paddings the library takes: stride 1 needs R - 1 - p in {0, 1, 2}
+        ps = [p for p in range(0, r) if (st == 2 or 0 <= r - 1 - p <= 2)]
+        p = int(rng.choice(ps))
+        f = int(rng.choice([3, 8, 24, 64, 96, 136]))
+        c = int(rng.choice([16, 32, 64] if dt != "float8_e4m3fn" else [16, 64, 128]))
+        h, w = int(rng.integers(3, 14)), int(rng.integers(3, 14))
+        cases.append((dt, int(rng.integers(1, 3)), h, w, c, f, r, st, p, bool(i % 2)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _tr_sweep(), ids=lambda c: "-".join(map(str, c)))
+def test_transposed_random_sweep(case):
+    dt, n, h, w, c, f, r, st, p, fused = case
+    ho, wo = (h - 1) * st - 2 * p + r, (w - 1) * st - 2 * p + r
+    if ho < 1 or wo < 1:
+        pytest.skip("empty output")
+    code = igc.conv2d_transposed_check(0x10000000, 0x20000000, 0x30000000, stride=st, padding=p,
+                                       dtype=igc.dtype_code(getattr(torch, dt)),
+                                       in_shape=(n, h, w, c), filt_shape=(r, r, f, c),
+                                       out_shape=(n, ho, wo, f))
+    if igc.REASONS[code] == "padding":
+        pytest.skip("padding outside what the phase convolutions take")
+    assert code == 0, igc.REASONS[code]
+    _say(f"transposed sweep {case} -> out {n}x{ho}x{wo}x{f}")
+    seed = zlib.crc32(repr(case).encode()) % 1000
+    x, wfwd, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=r, dtype=dt, fcrs=False,
+                                     x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                     src_dist=("normal", 1.0) if fused else None,
+                                     out_hw=(ho, wo), seed=seed)
+    wt = wfwd.permute(0, 1, 3, 2).contiguous()
+    kw, okw = {}, {}
+    if fused:
+        kw = dict(source=src.to(DEV), beta=-0.5, activation="relu")
+        okw = dict(source=src, beta=-0.5, act="relu")
+    out = igc.conv2d_transposed(x.to(DEV), wt.to(DEV), stride=st, padding=p, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.conv2d_transposed(x, wt, stride=st, padding=p, **okw)
+    _assert_close(out, ref, TOL[dt], str(case))
