@@ -762,31 +762,40 @@ int32_t transposed_pointers(const TPlan& t, int32_t dtype, const void* input, co
     return check_epilogue(epi, output, so);
 }
 
-hipError_t launch_transpose_flipped(const void* filter, const TPlan& t, int ph, int32_t dtype,
-                                    void* nk, hipStream_t stream) {
+// The flipped NK matrices of every phase, in one launch (grid rows =
+// phases); ws + nk_off[ph] receives phase ph's.
+hipError_t launch_transpose_flipped(const void* filter, const TPlan& t, int32_t dtype, uint8_t* ws,
+                                    hipStream_t stream) {
     const int eb = elem_bytes(dtype);
-    const Shape& s = t.ph[ph];
-    const int64_t chunks = s.F * (s.kpitch / (16 / eb));
-    if (chunks == 0) return hipSuccess;
-    TapSel sel{};
-    sel.R = (int)t.R; sel.S = (int)t.R; sel.F = (int)t.F; sel.C = (int)t.C;
-    sel.st = t.st;
-    if (t.st == 1) {
-        sel.BH = sel.BW = 0;
-        sel.JH = sel.JW = (int)t.R;
-    } else {
-        sel.BH = t.B[ph >> 1]; sel.BW = t.B[ph & 1];
-        sel.JH = t.J[ph >> 1]; sel.JW = t.J[ph & 1];
+    TapSels ts{};
+    int64_t most = 0;
+    for (int ph = 0; ph < t.nph; ++ph) {
+        const Shape& s = t.ph[ph];
+        TapSel& sel = ts.t[ph];
+        sel.R = (int)t.R; sel.S = (int)t.R; sel.F = (int)t.F; sel.C = (int)t.C;
+        sel.st = t.st;
+        if (t.st == 1) {
+            sel.BH = sel.BW = 0;
+            sel.JH = sel.JW = (int)t.R;
+        } else {
+            sel.BH = t.B[ph >> 1]; sel.BW = t.B[ph & 1];
+            sel.JH = t.J[ph >> 1]; sel.JW = t.J[ph & 1];
+        }
+        sel.K = (int)s.K;
+        sel.kpitch = (int)s.kpitch;
+        ts.nk[ph] = ws + t.nk_off[ph];
+        const int64_t chunks = s.F * (s.kpitch / (16 / eb));
+        if (chunks > most) most = chunks;
     }
-    sel.K = (int)s.K;
-    sel.kpitch = (int)s.kpitch;
-    const unsigned blocks = (unsigned)((chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096);
+    if (most == 0) return hipSuccess;
+    const dim3 grid((unsigned)((most + 255) / 256 < 4096 ? (most + 255) / 256 : 4096),
+                    (unsigned)t.nph);
     if (eb == 2)
-        hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<2>, dim3(blocks), dim3(256), 0, stream,
-                           (const uint8_t*)filter, (uint8_t*)nk, sel);
+        hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<2>, grid, dim3(256), 0, stream,
+                           (const uint8_t*)filter, ts);
     else
-        hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<1>, dim3(blocks), dim3(256), 0, stream,
-                           (const uint8_t*)filter, (uint8_t*)nk, sel);
+        hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<1>, grid, dim3(256), 0, stream,
+                           (const uint8_t*)filter, ts);
     return hipGetLastError();
 }
 
@@ -814,15 +823,13 @@ hipError_t run_transposed(const TPlan& t, const void* input, const void* filter,
                           const void* source, float beta, const igc_epilogue* epi, int32_t dtype,
                           uint8_t* ws, hipStream_t stream) {
     hipError_t e = hipSuccess;
+    e = launch_transpose_flipped(filter, t, dtype, ws, stream);
     if (t.st == 1) {
-        e = launch_transpose_flipped(filter, t, 0, dtype, ws, stream);
         if (e == hipSuccess) e = launch_igemm(input, ws, output, source, beta, epi, t.ph[0], dtype, stream);
         return e;
     }
     size_t yoffs[4], soffs[4];
     for (int ph = 0; ph < 4; ++ph) { yoffs[ph] = t.y_off[ph]; soffs[ph] = t.s_off[ph]; }
-    for (int ph = 0; ph < 4 && e == hipSuccess; ++ph)
-        e = launch_transpose_flipped(filter, t, ph, dtype, ws + t.nk_off[ph], stream);
     if (e == hipSuccess && source) e = launch_interleave(t, ws, source, nullptr, soffs, 1, stream);
     if (t.J[0] == t.J[1]) {
         // every phase has the same shape (even R): one grouped launch, the

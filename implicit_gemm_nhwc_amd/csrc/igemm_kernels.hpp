@@ -1607,10 +1607,18 @@ struct TapSel {
     int K, kpitch;     // K = JH*JW*C; NK row pitch (elements)
 };
 
+// Up to four phases in one launch: blockIdx.y selects the phase.
+struct TapSels {
+    TapSel t[4];
+    uint8_t* nk[4];
+};
+
 template <int E>
 __global__ __launch_bounds__(256) void filter_rsfc_to_nk_flipped_kernel(
-    const uint8_t* __restrict__ w, uint8_t* __restrict__ nk, TapSel t) {
+    const uint8_t* __restrict__ w, TapSels ts) {
     constexpr int VEC = 16 / E;
+    const TapSel& t = ts.t[blockIdx.y];
+    uint8_t* __restrict__ nk = ts.nk[blockIdx.y];
     const int row_chunks = t.kpitch / VEC;
     const int64_t total = (int64_t)t.F * row_chunks;
     for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total;
