@@ -1551,8 +1551,13 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 u32x2 ov;
                 ov[0] = (uint32_t)f32_to_out(v[0], ODT) | ((uint32_t)f32_to_out(v[1], ODT) << 16);
                 ov[1] = (uint32_t)f32_to_out(v[2], ODT) | ((uint32_t)f32_to_out(v[3], ODT) << 16);
+                // non-temporal (cache policy NT): the output is written once
+                // and not read again by this kernel; each instruction writes
+                // 128 or 256 contiguous bytes per pixel (measured with C_out
+                // = 256: fp8 5x5 layer 105.6 -> 103.3 us, strided 3x3 layer
+                // 28.1 -> 26.8 us)
                 __builtin_amdgcn_raw_buffer_store_b64(
-                    ov, yrs, (uint32_t)(((q * PPI + pl) * a.F + co) * 2) | cmask, 0, 0);
+                    ov, yrs, (uint32_t)(((q * PPI + pl) * a.F + co) * 2) | cmask, 0, 2);
             }
         }
     } else {
