@@ -1521,8 +1521,10 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             const __amdgpu_buffer_rsrc_t srs = blk(a.src, mw + j * 32);
 #pragma unroll
             for (int q = 0; q < NI; ++q)
+                // non-temporal: the source is read exactly once (measured
+                // on the fp8 5x5 layer: 101.5 -> 97 us)
                 sv[j & 1][q] = __builtin_amdgcn_raw_buffer_load_b64(
-                    srs, (uint32_t)(((q * PPI + pl) * a.F + co) * 2) | cmask, 0, 0);
+                    srs, (uint32_t)(((q * PPI + pl) * a.F + co) * 2) | cmask, 0, 2);
         };
         if constexpr (RESID) load_src(0);
 #pragma unroll
