@@ -895,9 +895,14 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             const bool ok = (pos < cpp) & (pw < a.PW) & (ph < a.PH) &
                             ((unsigned)ih < (unsigned)a.H) & ((unsigned)iw < (unsigned)a.W);
             const uint32_t off = (uint32_t)((ih * a.W + iw) * cbytes + pos * 16);
+            // non-temporal: each input line is wanted by this tile and at
+            // most its neighbours, which run at the same time, so the patch
+            // should not push the filter (read by every workgroup) out of
+            // L2 (measured: ResNet 3x3 layer 17.0 -> 15.9 us, RGB layer
+            // 32.1 -> 30.6 us)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xrs, (__attribute__((address_space(3))) void*)(patch + b * 1024), 16,
-                off | ((uint32_t)!ok << 31), 0, 0, 0);
+                off | ((uint32_t)!ok << 31), 0, 0, 2);
             rem += drem;
             const int car = rem >= rs ? 1 : 0;
             rem -= car ? rs : 0;
