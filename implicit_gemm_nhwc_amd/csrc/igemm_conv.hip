@@ -12,7 +12,8 @@
 #include <string.h>
 
 #include "igemm_conv.h"
-#include "igemm_kernels.hpp"
+#include "igemm_host.hpp"
+#include "igemm_aux_kernels.hpp"
 
 namespace {
 
@@ -143,27 +144,6 @@ int32_t check_all(const void* input, const int64_t in_nhwc[4], const void* filte
 
 int32_t hip_fail(hipError_t e) { return e == hipSuccess ? 1 : -(int32_t)e; }
 
-// hipFuncSetAttribute acts on the current device, so the dynamic-LDS limit
-// of each kernel is raised once per device (the first launch there).
-constexpr int kMaxDevices = 64;
-struct LdsAttr {
-    std::mutex mu;
-    bool done[kMaxDevices] = {};
-    hipError_t err[kMaxDevices] = {};
-};
-
-hipError_t ensure_lds(LdsAttr& at, const void* kern, size_t lds) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> g(at.mu);
-    if (!at.done[dev]) {
-        at.err[dev] = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        at.done[dev] = true;
-    }
-    return at.err[dev];
-}
 
 // The fused epilogue's own gate: a known activation, 4-byte aligned
 // coefficient arrays, and none of them overlapping the output (every
@@ -207,44 +187,6 @@ hipError_t launch_transpose(const void* filter, int32_t fcrs, const Shape& s, in
     return hipGetLastError();
 }
 
-template <int DT, int BCO, int BPX, int WCO, int WPX, bool RESID>
-hipError_t launch_tile(ConvArgs a, hipStream_t stream) {
-    constexpr size_t lds = 2 * (size_t)(BCO + BPX) * KT_BYTES;
-    auto kern = igemm_fwd_kernel<DT, BCO, BPX, WCO, WPX, RESID>;
-    static LdsAttr attr;
-    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)(lds));
-    if (attr_err != hipSuccess) return attr_err;
-    a.px_tiles = (a.M + BPX - 1) / BPX;
-    a.co_tiles = (a.F + BCO - 1) / BCO;
-    const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
-                       dim3(NTHREADS), lds, stream, a);
-    return hipGetLastError();
-}
-
-constexpr size_t kResidentLdsMax = 80 * 1024;  // two workgroups per CU
-constexpr int kResidentTN = 4;                   // 64 pixels per wave
-
-template <int DT, int TM, bool RESID, bool ALIGNED>
-hipError_t launch_resident(ConvArgs a, hipStream_t stream) {
-    constexpr int E = DtTraits<DT>::E;
-    auto kern = igemm_fwd_resident_kernel<DT, TM, kResidentTN, RESID, ALIGNED>;
-    static LdsAttr attr;
-    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, kResidentLdsMax);
-    if (attr_err != hipSuccess) return attr_err;
-    // the filter is staged in whole 1 KB blocks: round the allocation up
-    const size_t lds = ((size_t)TM * 16 * ((size_t)a.kpitch * E) + 1023) / 1024 * 1024;
-    const int64_t wtiles = ((int64_t)a.M + kResidentTN * 16 - 1) / (kResidentTN * 16);
-    const int64_t blocks = (wtiles + RES_WAVES - 1) / RES_WAVES;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
-                       dim3(RES_WAVES * 64), lds, stream, a);
-    return hipGetLastError();
-}
-
-// The filter-resident kernel applies when the padded NK matrix fits its LDS
-// budget and every wave's gather window (the images its 64 pixels touch)
 // stays below the 2^31-byte buffer range.
 bool resident_ok(const Shape& s, int32_t dtype) {
     if (s.F > 64) return false;
@@ -257,42 +199,14 @@ bool resident_ok(const Shape& s, int32_t dtype) {
     return imgs * s.H * s.W * s.C * eb < ((int64_t)1 << 31);
 }
 
-template <int DT, bool RESID, bool ALIGNED>
-hipError_t launch_resident_tm(const ConvArgs& a, hipStream_t stream) {
-    if (a.F <= 16) return launch_resident<DT, 1, RESID, ALIGNED>(a, stream);
-    if (a.F <= 32) return launch_resident<DT, 2, RESID, ALIGNED>(a, stream);
-    if (a.F <= 48) return launch_resident<DT, 3, RESID, ALIGNED>(a, stream);
-    return launch_resident<DT, 4, RESID, ALIGNED>(a, stream);
-}
-
-// C_in a multiple of the 128-byte k-tile: each k-tile sits inside one tap.
-template <int DT, bool RESID>
-hipError_t launch_resident_dt(const ConvArgs& a, hipStream_t stream) {
-    constexpr int KT = KT_BYTES / DtTraits<DT>::E;
-    if (a.C > 0 && a.C % KT == 0) return launch_resident_tm<DT, RESID, true>(a, stream);
-    return launch_resident_tm<DT, RESID, false>(a, stream);
-}
 
 // ---- band kernel planning ------------------------------------------------
-constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
-constexpr int kNumCUs = 256;
-
-struct BandPlan {
-    int TH, TW, PH, PW, TN, fpitch, ppitch, prow, spitch, lds, tiles_h, tiles_w;
-    int64_t tiles;
-};
 
 // 32-pixel blocks per wave the band kernel is built for.
 int band_tn(int64_t blocks_per_wave) {
     for (int tn : {1, 2, 3, 4})
         if (blocks_per_wave <= tn) return tn;
     return 0;
-}
-
-int log2_exact(int64_t v) {
-    int l = 0;
-    while (((int64_t)1 << l) < v) ++l;
-    return ((int64_t)1 << l) == v ? l : -1;
 }
 
 // Pick the output tile (TH x TW) for the band kernel, or return false when
@@ -362,103 +276,6 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
     return found;
 }
 
-template <int DT, int TM, int TN, int U, bool RESID>
-hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
-    auto kern = igemm_fwd_band_kernel<DT, TM, TN, U, RESID>;
-    static LdsAttr attr;
-    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, kLdsBytes);
-    if (attr_err != hipSuccess) return attr_err;
-    a.TH = bp.TH; a.TW = bp.TW; a.PH = bp.PH; a.PW = bp.PW;
-    a.tiles_h = bp.tiles_h; a.tiles_w = bp.tiles_w;
-    a.fpitch = bp.fpitch; a.ppitch = bp.ppitch; a.prow = bp.prow; a.spitch = bp.spitch;
-    a.frows = a.F + 1 < TM * 32 ? a.F + 1 : TM * 32;
-    a.patch_off = (a.frows * bp.fpitch + 1023) / 1024 * 1024;
-    {
-        const int E = DtTraits<DT>::E;
-        a.cpp_log2 = log2_exact(a.C * E / 16);
-    }
-    if (bp.tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(bp.tiles * (a.groups > 1 ? a.groups : 1))),
-                       dim3(BAND_WAVES * 64), (size_t)bp.lds,
-                       stream, a);
-    return hipGetLastError();
-}
-
-// k-steps per unrolled block: the largest of 4, 2, 1 dividing the steps per tap
-template <int DT, int TM, int TN, bool RESID>
-hipError_t launch_band_u(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
-    constexpr int KSB = DT == DT_FP8 ? 64 : 32;
-    const int steps = a.C * DtTraits<DT>::E / KSB;
-    if (steps % 4 == 0) return launch_band<DT, TM, TN, 4, RESID>(a, bp, stream);
-    if (steps % 2 == 0) return launch_band<DT, TM, TN, 2, RESID>(a, bp, stream);
-    return launch_band<DT, TM, TN, 1, RESID>(a, bp, stream);
-}
-
-template <int DT, int TM, bool RESID>
-hipError_t launch_band_tm(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
-    switch (bp.TN) {
-        case 1: return launch_band_u<DT, TM, 1, RESID>(a, bp, stream);
-        case 2: return launch_band_u<DT, TM, 2, RESID>(a, bp, stream);
-        case 3: return launch_band_u<DT, TM, 3, RESID>(a, bp, stream);
-        default: return launch_band_u<DT, TM, 4, RESID>(a, bp, stream);
-    }
-}
-
-template <int DT, bool RESID>
-hipError_t launch_band_dt(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
-    if (a.F <= 32) return launch_band_tm<DT, 1, RESID>(a, bp, stream);
-    return launch_band_tm<DT, 2, RESID>(a, bp, stream);
-}
-
-// ---- wide-layer kernel with direct-to-LDS staging ---------------------------
-template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK,
-          bool GROUPED = false>
-hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
-    constexpr int BCO = WCO * TM * 32, BPX = WPX * TN * 32;
-    constexpr size_t lds = (size_t)NSTAGE * (BCO + BPX) * KTB;
-    static_assert(lds <= (size_t)kLdsBytes, "stages fit in LDS");
-    auto kern = igemm_fwd_wide_kernel<DT, TM, TN, WCO, WPX, KTB, NSTAGE, RESID, TAPK, GROUPED>;
-    static LdsAttr attr;
-    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)(lds));
-    if (attr_err != hipSuccess) return attr_err;
-    a.ktiles = a.ktiles * (KT_BYTES / KTB);   // NK rows hold whole 128-byte k-tiles
-    a.px_tiles = (a.M + BPX - 1) / BPX;
-    a.co_tiles = (a.F + BCO - 1) / BCO;
-    const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
-                       dim3(WCO * WPX * 64), lds, stream, a);
-    return hipGetLastError();
-}
-
-// Tile choice for C_out > 64, four waves, 128-byte k-tiles (whole cache
-// lines per request).  256 x 256 tiles (128 x 128 per wave, 256 accumulator
-// registers) in two stages (128 KB of LDS, one workgroup per CU) whenever
-// that still gives a tile per CU; otherwise 128 x 128 tiles (64 x 64 per
-// wave) in two stages, 64 KB, so two workgroups share a CU and one's
-// prologue, epilogue and waits overlap the other's MFMAs.  Measured on the
-// strided 3x3 128->256 layer (N=32, 56x56, fp16; kernel time, cold operands):
-// 128x128 in 2 stages 27.9 us, 256x128 in 3 stages 30.4 us, 256x128 in 2
-// stages 31.0 us, 128x256 in 3 stages 30.7 us, 128x128 in 4 stages (one
-// workgroup per CU) 35.1 us, 256x256 in 2 stages (98 tiles) 42.7 us.  On the
-// fp8 5x5 256->256 layer (256 tiles of 256x256): 256x256 in 2 stages 105 us,
-// 128x128 in 2 stages 115 us, 256x128 in 3 stages 125 us.  TAPK when C_in is
-// a whole number of k-tiles.
-template <int DT, bool RESID>
-hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
-    constexpr int E = DtTraits<DT>::E;
-    const bool tap128 = a.C > 0 && (a.C * E) % 128 == 0;
-    const int64_t co_tiles256 = (a.F + 255) / 256;
-    const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
-    if (a.groups > 1)   // grouped launches: 128 x 128 tiles only
-        return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, true, true>(a, stream)
-                      : launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, false, true>(a, stream);
-    if (a.F > 128 && px_tiles256 * co_tiles256 >= kNumCUs)
-        return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
-                      : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
-    return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, true>(a, stream)
-                  : launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, false>(a, stream);
-}
 
 // The wide kernel bases each tile's pixel buffer at its first image; the
 // images one tile's 256 pixels can touch must fit the 2^31-byte range.
@@ -470,16 +287,6 @@ bool wide_ok(const Shape& s, int32_t dtype) {
     return imgs * s.H * s.W * s.C * elem_bytes(dtype) < ((int64_t)1 << 31);
 }
 
-
-template <int DT, bool RESID>
-hipError_t launch_dt(const ConvArgs& a, hipStream_t stream) {
-    // Tile by C_out: one 16x16 MFMA row block per wave for tiny C_out, up to
-    // 128 x 128 workgroup tiles (64 x 64 per wave) for wide layers.
-    if (a.F <= 16) return launch_tile<DT, 16, 256, 1, 4, RESID>(a, stream);
-    if (a.F <= 32) return launch_tile<DT, 32, 256, 1, 4, RESID>(a, stream);
-    if (a.F <= 64) return launch_tile<DT, 64, 256, 1, 4, RESID>(a, stream);
-    return launch_tile<DT, 128, 128, 2, 2, RESID>(a, stream);
-}
 
 // The kernel a problem goes to, in order of preference.
 enum KernelKind { K_NONE, K_BAND, K_WIDE, K_RESIDENT, K_TILED };
@@ -499,6 +306,17 @@ struct Group {
     int n;
     int64_t nk, y, src;
 };
+
+template <int DT>
+hipError_t launch_kind(KernelKind kind, bool resid, const ConvArgs& a, const BandPlan& bp,
+                       hipStream_t stream) {
+    switch (kind) {
+        case K_BAND: return launch_band_any<DT>(resid, a, bp, stream);
+        case K_WIDE: return launch_wide_any<DT>(resid, a, stream);
+        case K_RESIDENT: return launch_resident_any<DT>(resid, a, stream);
+        default: return launch_tiled_any<DT>(resid, a, stream);
+    }
+}
 
 hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
                         float beta, const igc_epilogue* epi, const Shape& s, int32_t dtype,
@@ -530,52 +348,10 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
     BandPlan bp;
     const KernelKind kind = select_kernel(s, dtype, &bp);
     if (kind == K_NONE) return hipSuccess;
-    if (kind == K_BAND) {
-        switch (dtype) {
-            case IGC_DTYPE_BF16:
-                return resid ? launch_band_dt<DT_BF16, true>(a, bp, stream)
-                             : launch_band_dt<DT_BF16, false>(a, bp, stream);
-            case IGC_DTYPE_FP16:
-                return resid ? launch_band_dt<DT_FP16, true>(a, bp, stream)
-                             : launch_band_dt<DT_FP16, false>(a, bp, stream);
-            default:
-                return resid ? launch_band_dt<DT_FP8, true>(a, bp, stream)
-                             : launch_band_dt<DT_FP8, false>(a, bp, stream);
-        }
-    }
-    if (kind == K_WIDE) {
-        switch (dtype) {
-            case IGC_DTYPE_BF16:
-                return resid ? launch_wide_dt<DT_BF16, true>(a, stream)
-                             : launch_wide_dt<DT_BF16, false>(a, stream);
-            case IGC_DTYPE_FP16:
-                return resid ? launch_wide_dt<DT_FP16, true>(a, stream)
-                             : launch_wide_dt<DT_FP16, false>(a, stream);
-            default:
-                return resid ? launch_wide_dt<DT_FP8, true>(a, stream)
-                             : launch_wide_dt<DT_FP8, false>(a, stream);
-        }
-    }
-    if (kind == K_RESIDENT) {
-        switch (dtype) {
-            case IGC_DTYPE_BF16:
-                return resid ? launch_resident_dt<DT_BF16, true>(a, stream)
-                             : launch_resident_dt<DT_BF16, false>(a, stream);
-            case IGC_DTYPE_FP16:
-                return resid ? launch_resident_dt<DT_FP16, true>(a, stream)
-                             : launch_resident_dt<DT_FP16, false>(a, stream);
-            default:
-                return resid ? launch_resident_dt<DT_FP8, true>(a, stream)
-                             : launch_resident_dt<DT_FP8, false>(a, stream);
-        }
-    }
     switch (dtype) {
-        case IGC_DTYPE_BF16:
-            return resid ? launch_dt<DT_BF16, true>(a, stream) : launch_dt<DT_BF16, false>(a, stream);
-        case IGC_DTYPE_FP16:
-            return resid ? launch_dt<DT_FP16, true>(a, stream) : launch_dt<DT_FP16, false>(a, stream);
-        default:
-            return resid ? launch_dt<DT_FP8, true>(a, stream) : launch_dt<DT_FP8, false>(a, stream);
+        case IGC_DTYPE_BF16: return launch_kind<DT_BF16>(kind, resid, a, bp, stream);
+        case IGC_DTYPE_FP16: return launch_kind<DT_FP16>(kind, resid, a, bp, stream);
+        default: return launch_kind<DT_FP8>(kind, resid, a, bp, stream);
     }
 }
 

@@ -217,52 +217,6 @@ __device__ __forceinline__ f32x4 mfma_step<DT_FP8>(const i32x4* a, const i32x4* 
 }
 
 // ---------------------------------------------------------------------------
-// Filter transpose to NK (page "dispatch_fused_im2col_conv2d_apple", summary).
-// One thread writes one 16-byte chunk of an NK row; the chunk's elements are
-// VEC channels of one tap (C % VEC == 0), gathered from the stored layout:
-//   RSCF [R,S,C,F]: W(k, co) = w[k*F + co]              (k = (r*S+s)*C + ci)
-//   FCRS [F,C,R,S]: W(k, co) = w[((co*C + ci)*R + r)*S + s]
-// Chunks at or past K are zero.  Consecutive lanes take the stored layout's
-// contiguous direction, so each of a wave's VEC loads touches few lines:
-//   RSCF: lanes along co (x), chunks along y;
-//   FCRS: lanes along the chunks of one row (x), rows along y.
-// Grid rows past 65535 loop.  Indices are 32-bit: the NK matrix is below
-// 2^31 bytes.
-template <int E>
-__global__ __launch_bounds__(64) void filter_to_nk_kernel(
-    const uint8_t* __restrict__ w, uint8_t* __restrict__ nk, int fcrs, int R, int S,
-    int C, int F, int K, int kpitch) {
-    constexpr int VEC = 16 / E;
-    const int row_chunks = kpitch / VEC;
-    const int x = blockIdx.x * blockDim.x + threadIdx.x;
-    auto chunk_out = [&](int co, int chunk) {
-        const int k0 = chunk * VEC;
-        union { i32x4 v; uint8_t b[16]; uint16_t h[8]; } u;
-        u.v = i32x4{0, 0, 0, 0};
-        if (k0 < K) {
-            const int tap = k0 / C, ci0 = k0 - tap * C;
-            const int r = tap / S, s = tap - r * S;
-            // VEC independent element loads at a fixed stride, all in flight
-            const int base = fcrs ? ((co * C + ci0) * R + r) * S + s : k0 * F + co;
-            const int step = fcrs ? R * S : F;
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                if (E == 2) u.h[j] = reinterpret_cast<const uint16_t*>(w)[base + j * step];
-                else u.b[j] = w[base + j * step];
-            }
-        }
-        *reinterpret_cast<i32x4*>(nk + ((int64_t)co * kpitch + k0) * E) = u.v;
-    };
-    if (fcrs) {
-        if (x >= row_chunks) return;
-        for (int co = blockIdx.y; co < F; co += gridDim.y) chunk_out(co, x);
-    } else {
-        if (x >= F) return;
-        for (int chunk = blockIdx.y; chunk < row_chunks; chunk += gridDim.y) chunk_out(x, chunk);
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Implicit-GEMM forward convolution.
 //   BCO x BPX  workgroup tile (output channels x output pixels)
 //   WCO x WPX  arrangement of the 4 waves; each wave owns a
@@ -1590,165 +1544,6 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 }
             }
         }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Transposed convolution (page "conv_transposed_gpu": NHWC input, RSFC
-// filter [R][S][F][C], F output and C input channels):
-//   out[n, oh, ow, f] = sum over ih*st - p + r = oh, iw*st - p + s = ow
-//                       of in[n, ih, iw, c] * W[r][s][f][c]
-// Along one axis, the output rows of parity a (oh = st*q + a) take only the
-// taps r = b, b + st, ... (b = (a + p) mod st), at input rows
-// ih = q + c_a - j for r = b + st*j (c_a = (a + p - b) / st).  Read with the
-// taps in increasing input order that is a stride-1 forward correlation of
-// the input with the J taps W[b + st*(J-1-t)], t < J: the forward implicit
-// GEMM at some padding P, whose output row q + c_a - (J-1) + P is output
-// row st*q + a.  With stride 1 there is one phase (b = 0, J = R) and the
-// forward output is the result itself, at padding R - 1 - p.
-//
-// The NK matrix of one phase (taps t_h < JH, t_w < JW):
-//   NK'[f][(t_h*JW + t_w)*C + c] = W[BH + st*(JH-1-t_h)][BW + st*(JW-1-t_w)][f][c]
-// for each (f, t_h, t_w) a contiguous run of C elements of W.  One thread
-// copies one 16-byte chunk (C * E % 16 == 0); chunks at or past K are zero.
-struct TapSel {
-    int R, S, F, C;    // stored filter
-    int BH, BW;        // first tap of the phase along each axis
-    int JH, JW;        // taps of the phase along each axis
-    int st;            // tap step (the stride)
-    int K, kpitch;     // K = JH*JW*C; NK row pitch (elements)
-};
-
-// Up to four phases in one launch: blockIdx.y selects the phase.
-struct TapSels {
-    TapSel t[4];
-    uint8_t* nk[4];
-};
-
-template <int E>
-__global__ __launch_bounds__(256) void filter_rsfc_to_nk_flipped_kernel(
-    const uint8_t* __restrict__ w, TapSels ts) {
-    constexpr int VEC = 16 / E;
-    const TapSel& t = ts.t[blockIdx.y];
-    uint8_t* __restrict__ nk = ts.nk[blockIdx.y];
-    const int row_chunks = t.kpitch / VEC;
-    const int64_t total = (int64_t)t.F * row_chunks;
-    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total;
-         g += (int64_t)gridDim.x * 256) {
-        const int f = (int)(g / row_chunks), chunk = (int)(g - (int64_t)f * row_chunks);
-        const int k0 = chunk * VEC;
-        i32x4 v = {0, 0, 0, 0};
-        if (k0 < t.K) {
-            const int tap = k0 / t.C, c0 = k0 - tap * t.C;
-            const int th = tap / t.JW, tw = tap - th * t.JW;
-            const int r = t.BH + t.st * (t.JH - 1 - th), sx = t.BW + t.st * (t.JW - 1 - tw);
-            const int64_t src = ((((int64_t)r * t.S + sx) * t.F + f) * t.C + c0) * E;
-            v = *reinterpret_cast<const i32x4*>(w + src);
-        }
-        *reinterpret_cast<i32x4*>(nk + ((int64_t)f * t.kpitch + k0) * E) = v;
-    }
-}
-
-// Moves 2-byte output elements between the interleaved output [N, Ho, Wo, F]
-// and the four phase buffers [N, HY[ah], WY[aw], F] of a stride-2 transposed
-// convolution: output pixel (2*qh + ah, 2*qw + aw) is phase (ah, aw) pixel
-// (qh + OH[ah], qw + OW[aw]).  to_phase = 0 fills the output from the phases,
-// 1 fills the phases from an output-shaped tensor (the residual source; phase
-// pixels no output pixel maps to are left as they are).  One thread per
-// output pixel and 16-byte channel group (F % 8 == 0) or channel.
-struct PhaseMap {
-    const uint16_t* src;
-    uint16_t* dst;
-    uint16_t* phase[4];   // index 2*ah + aw
-    int N, Ho, Wo, F;
-    int HY[2], WY[2], OH[2], OW[2];
-    int to_phase;
-};
-
-__global__ __launch_bounds__(256) void phase_interleave_kernel(PhaseMap m) {
-    const bool vec = (m.F & 7) == 0;
-    const int groups = vec ? m.F / 8 : m.F;
-    const int64_t total = (int64_t)m.N * m.Ho * m.Wo * groups;
-    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total;
-         g += (int64_t)gridDim.x * 256) {
-        const int64_t pix = g / groups;
-        const int cg = (int)(g - pix * groups);
-        const int ow = (int)(pix % m.Wo);
-        const int64_t t = pix / m.Wo;
-        const int oh = (int)(t % m.Ho);
-        const int n = (int)(t / m.Ho);
-        const int ah = oh & 1, aw = ow & 1;
-        const int qh = (oh >> 1) + m.OH[ah], qw = (ow >> 1) + m.OW[aw];
-        const int64_t po = (((int64_t)n * m.HY[ah] + qh) * m.WY[aw] + qw) * m.F;
-        const int64_t oo = pix * m.F;
-        uint16_t* ph = m.phase[2 * ah + aw];
-        if (vec) {
-            const int c = cg * 8;
-            if (m.to_phase)
-                *reinterpret_cast<i32x4*>(ph + po + c) = *reinterpret_cast<const i32x4*>(m.src + oo + c);
-            else
-                *reinterpret_cast<i32x4*>(m.dst + oo + c) = *reinterpret_cast<const i32x4*>(ph + po + c);
-        } else {
-            if (m.to_phase) ph[po + cg] = m.src[oo + cg];
-            else m.dst[oo + cg] = ph[po + cg];
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Materialised im2col (page "dispatch_fused_im2col_conv2d_apple", summary:
-// the [M, K] patch matrix the fused path never writes), for comparing the
-// fused gather against the write-then-GEMM route on the same MFMA kernels:
-//   A[m][k] = x[n, oh*st - p + r, ow*st - p + s, ci]   (0 in the padding)
-//   m = (n*Ho + oh)*Wo + ow,  k = (r*S + s)*C_in + ci,  rows of Kp elements
-// (K rounded up to whole 128-byte k-tiles, zero past K).  Read as an NHWC
-// tensor [N, Ho, Wo, Kp], A is the input of a 1x1, stride-1 convolution
-// whose NK matrix is the original filter's.
-//
-// One thread per 16-byte vector of A, grid-stride; a vector is VEC channels
-// of one tap (C_in * E % 16 == 0).  Stores are fully coalesced; loads are
-// contiguous within a tap's channels.  Divisions by runtime constants use
-// multiply-high magic numbers made on the host.
-struct FastDiv {
-    uint32_t mul;    // ceil(2^(32+shift) / d) - 2^32
-    uint32_t shift;  // ceil(log2(d))
-};
-
-// floor(n / d) for 0 <= n < 2^31: with m = ceil(2^(32+s) / d), s = ceil(log2 d),
-// n * m / 2^(32+s) exceeds n / d by less than n / 2^(32+s) < 1/d, which never
-// reaches the next integer.
-__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv d) {
-    return (__umulhi(n, d.mul) + n) >> d.shift;
-}
-
-struct Im2colArgs {
-    const uint8_t* x;
-    uint8_t* a;
-    int H, W, Ho, Wo, S, stride, pad;
-    int RS;             // taps
-    int CB;             // bytes per input pixel (C_in * E)
-    uint32_t total;     // 16-byte vectors of A: M * VPR
-    uint32_t VPR, CV;   // vectors per A row; per tap
-    uint32_t HoWo;
-    FastDiv d_vpr, d_cv, d_s, d_howo, d_wo;
-};
-
-__global__ __launch_bounds__(256) void im2col_kernel(Im2colArgs a) {
-    const uint32_t step = gridDim.x * 256u;
-    for (uint32_t g = blockIdx.x * 256u + threadIdx.x; g < a.total; g += step) {
-        const uint32_t m = fast_div(g, a.d_vpr), j = g - m * a.VPR;
-        const uint32_t tap = fast_div(j, a.d_cv), cv = j - tap * a.CV;
-        i32x4 v = {0, 0, 0, 0};
-        if (tap < (uint32_t)a.RS) {
-            const int r = (int)fast_div(tap, a.d_s), s = (int)tap - r * a.S;
-            const uint32_t n = fast_div(m, a.d_howo), rem = m - n * a.HoWo;
-            const int oh = (int)fast_div(rem, a.d_wo), ow = (int)rem - oh * a.Wo;
-            const int ih = oh * a.stride - a.pad + r, iw = ow * a.stride - a.pad + s;
-            if ((unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W)
-                v = *reinterpret_cast<const i32x4*>(
-                    a.x + (((int64_t)n * a.H + ih) * a.W + iw) * a.CB + cv * 16);
-        }
-        *reinterpret_cast<i32x4*>(a.a + (int64_t)g * 16) = v;
     }
 }
 
