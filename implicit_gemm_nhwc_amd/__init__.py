@@ -6,10 +6,14 @@ gather, MFMA contraction, masks, residual epilogue) runs in the HIP kernels
 behind the C ABI declared in include/igemm_conv.h; torch supplies device
 memory and streams.  There is no fallback: if the library is not built, or a
 call is declined, these functions say so instead of computing anything.
+Tensor arguments of calls that enqueue work are checked first (contiguous,
+on one GPU, of the types and sizes their shape arguments describe):
+InvalidArgument is raised before anything is launched.
 
 Names mirror the C entry points:
-  conv2d_fwd, conv2d_fwd_check, conv2d_fwd_nk, conv2d_filter_to_nk,
-  conv2d_fwd_epilogue, conv2d_fwd_nk_epilogue, conv2d_epilogue_check,
+  conv2d_fwd, conv2d_fwd_check, conv2d_fwd_query, conv2d_fwd_nk, conv2d_filter_to_nk,
+  conv2d_fwd_epilogue, conv2d_fwd_epilogue_check, conv2d_fwd_nk_epilogue,
+  conv2d_epilogue_check,
   conv2d_im2col, conv2d_im2col_bytes,
   conv2d_transposed_fwd, conv2d_transposed_check, conv2d_transposed_workspace_bytes,
   conv2d_fwd_kernel_name, conv2d_workspace_bytes, conv2d_nk_row_pitch,
@@ -77,6 +81,8 @@ def lib():
     L.conv2d_reason_string.argtypes, L.conv2d_reason_string.restype = [i32], ctypes.c_char_p
     L.conv2d_fwd_check.argtypes = conv_head + [vp, sz]
     L.conv2d_fwd_check.restype = i32
+    L.conv2d_fwd_query.argtypes = [i64p, i32, i64p, i64p, i32p, i32p, i32p, i32, i32]
+    L.conv2d_fwd_query.restype = i32
     L.conv2d_fwd.argtypes = conv_head + [vp, sz, vp]
     L.conv2d_fwd.restype = i32
     L.conv2d_fwd_nk.argtypes = conv_head + [vp]
@@ -91,6 +97,8 @@ def lib():
     epip = ctypes.POINTER(IgcEpilogue)
     L.conv2d_fwd_epilogue.argtypes = conv_head + [epip, vp, sz, vp]
     L.conv2d_fwd_epilogue.restype = i32
+    L.conv2d_fwd_epilogue_check.argtypes = conv_head + [epip, vp, sz]
+    L.conv2d_fwd_epilogue_check.restype = i32
     L.conv2d_fwd_nk_epilogue.argtypes = conv_head + [epip, vp]
     L.conv2d_fwd_nk_epilogue.restype = i32
     L.conv2d_epilogue_check.argtypes = [epip, vp, i64p]
@@ -109,6 +117,101 @@ def lib():
     L.conv2d_transposed_workspace_bytes.restype = sz
     _lib = L
     return L
+
+
+class InvalidArgument(ValueError):
+    """A tensor argument the C ABI cannot describe: not a contiguous tensor on
+    the GPU, on another device than the others, or of the wrong type or
+    shape.  Raised before anything is enqueued."""
+
+
+def _check_tensors(named, device=None):
+    """Every torch tensor among named (name -> tensor, raw int or None) must
+    be a contiguous CUDA tensor, all on one device.  Returns that device."""
+    for name, t in named.items():
+        if not isinstance(t, torch.Tensor):
+            continue
+        if not t.is_cuda:
+            raise InvalidArgument(f"{name} must be a GPU tensor (got device {t.device})")
+        if not t.is_contiguous():
+            raise InvalidArgument(f"{name} must be contiguous (densely packed, row-major)")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise InvalidArgument(f"{name} is on {t.device}, the other tensors on {device}")
+    return device
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _prod(shape):
+    n = 1
+    for v in shape:
+        n *= int(v)
+    return n
+
+
+def _check_fwd(input, filter, output, source, dtype, in_shape, filt_shape, out_shape,
+               filter_is_fcrs, *, scale=None, bias=None, workspace=None, workspace_bytes=0,
+               nk=False):
+    """The binding's own checks of a forward call's tensor arguments, before
+    anything is enqueued (the C gate sees only pointers and shapes, so it
+    cannot tell a host tensor, a strided view or a short buffer).  Every torch
+    tensor must be a contiguous GPU tensor, all on one device, and hold at
+    least the bytes its shape argument describes.  When the element type comes
+    from the input tensor (dtype None), the filter must have the input's type,
+    the output the type page 1 pairs with it, and a source the output's shape
+    and type; an explicit dtype code marks the tensors as raw byte buffers.
+    scale / bias must be float32 with at least C_out values.  Raw integer
+    pointers pass unchecked."""
+    _check_tensors(dict(input=input, filter=filter, output=output, source=source,
+                        scale=scale, bias=bias, workspace=workspace))
+    if dtype is None and isinstance(input, torch.Tensor):
+        if input.dtype not in DTYPE_CODES:
+            raise InvalidArgument(f"input dtype {input.dtype} is not bf16, fp16 or fp8 e4m3fn")
+        if isinstance(filter, torch.Tensor) and not nk and filter.dtype != input.dtype:
+            raise InvalidArgument(f"filter dtype {filter.dtype} differs from input {input.dtype}")
+        if isinstance(output, torch.Tensor) and output.dtype != OUT_DTYPES[input.dtype]:
+            raise InvalidArgument(f"output dtype must be {OUT_DTYPES[input.dtype]} for "
+                                  f"{input.dtype} inputs (got {output.dtype})")
+        if isinstance(source, torch.Tensor) and isinstance(output, torch.Tensor) and (
+                source.shape != output.shape or source.dtype != output.dtype):
+            raise InvalidArgument(f"source must have the output's shape and dtype "
+                                  f"({tuple(output.shape)}, {output.dtype}); got "
+                                  f"({tuple(source.shape)}, {source.dtype})")
+    code = dtype if dtype is not None else (
+        dtype_code(input.dtype) if isinstance(input, torch.Tensor) else None)
+    if code not in (0, 1, 2):
+        return   # the C gate declines the element type
+    eb = 1 if code == 2 else 2
+    if any(int(v) < 0 for v in (*in_shape, *filt_shape, *out_shape)):
+        return   # the C gate declines negative dims
+    if isinstance(input, torch.Tensor) and _nbytes(input) < _prod(in_shape) * eb:
+        raise InvalidArgument(f"input holds {_nbytes(input)} bytes, the shape "
+                              f"{tuple(in_shape)} needs {_prod(in_shape) * eb}")
+    if isinstance(filter, torch.Tensor):
+        need = (conv2d_workspace_bytes(filt_shape, filter_is_fcrs, code) if nk
+                else _prod(filt_shape) * eb)
+        if _nbytes(filter) < need:
+            raise InvalidArgument(f"{'NK matrix' if nk else 'filter'} holds "
+                                  f"{_nbytes(filter)} bytes, needs {need}")
+    out_need = _prod(out_shape) * 2
+    for name, t in (("output", output), ("source", source)):
+        if isinstance(t, torch.Tensor) and _nbytes(t) < out_need:
+            raise InvalidArgument(f"{name} holds {_nbytes(t)} bytes, the output shape "
+                                  f"{tuple(out_shape)} needs {out_need}")
+    c_out = int(out_shape[3]) if len(out_shape) == 4 else None
+    for name, t in (("scale", scale), ("bias", bias)):
+        if isinstance(t, torch.Tensor):
+            if t.dtype != torch.float32:
+                raise InvalidArgument(f"{name} must be float32 (got {t.dtype})")
+            if c_out is not None and t.numel() < c_out:
+                raise InvalidArgument(f"{name} holds {t.numel()} values, C_out is {c_out}")
+    if isinstance(workspace, torch.Tensor) and _nbytes(workspace) < int(workspace_bytes):
+        raise InvalidArgument(f"workspace holds {_nbytes(workspace)} bytes, "
+                              f"workspace_bytes says {workspace_bytes}")
 
 
 def _i64(vals):
@@ -146,10 +249,19 @@ def dtype_code(dtype):
 
 
 def _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding, groups,
-               dtype, source, beta, in_shape=None, filt_shape=None, out_shape=None):
+               dtype, source, beta, in_shape=None, filt_shape=None, out_shape=None, *,
+               launch=False, nk=False, scale=None, bias=None, workspace=None,
+               workspace_bytes=0):
+    """The common leading arguments of the forward entry points; for a call
+    that enqueues work (launch=True) the tensors are checked first
+    (_check_fwd)."""
     in_shape = input.shape if in_shape is None else in_shape
     filt_shape = filter.shape if filt_shape is None else filt_shape
     out_shape = output.shape if out_shape is None else out_shape
+    if launch:
+        _check_fwd(input, filter, output, source, dtype, in_shape, filt_shape, out_shape,
+                   filter_is_fcrs, scale=scale, bias=bias, workspace=workspace,
+                   workspace_bytes=workspace_bytes, nk=nk)
     if dtype is None:
         dtype = dtype_code(input.dtype)
     return [_ptr(input), _i64(in_shape), _ptr(filter), int(bool(filter_is_fcrs)),
@@ -195,10 +307,11 @@ def conv2d_fwd(input, filter, output, *, filter_is_fcrs, stride=1, padding=0, di
                stream=None, dtype=None, in_shape=None, filt_shape=None,
                out_shape=None) -> int:
     """Enqueue the forward convolution.  1 handled, 0 declined, < 0 HIP error."""
-    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
-                      groups, dtype, source, beta, in_shape, filt_shape, out_shape)
     if isinstance(workspace, torch.Tensor) and not workspace_bytes:
         workspace_bytes = workspace.numel() * workspace.element_size()
+    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
+                      groups, dtype, source, beta, in_shape, filt_shape, out_shape,
+                      launch=True, workspace=workspace, workspace_bytes=workspace_bytes)
     return lib().conv2d_fwd(*head, _ptr(workspace), int(workspace_bytes),
                             _stream(stream, output))
 
@@ -209,7 +322,7 @@ def conv2d_fwd_nk(input, nk, filt_shape, output, *, filter_is_fcrs, stride=1, pa
     """Enqueue the implicit-GEMM kernel on an NK matrix from conv2d_filter_to_nk."""
     head = _conv_head(input, nk, filter_is_fcrs, output, stride, dilation, padding, groups,
                       dtype, source, beta, in_shape=in_shape, filt_shape=filt_shape,
-                      out_shape=out_shape)
+                      out_shape=out_shape, launch=True, nk=True)
     return lib().conv2d_fwd_nk(*head, _stream(stream, output))
 
 
@@ -234,16 +347,43 @@ def conv2d_epilogue_check(output, *, scale=None, bias=None, activation=None,
                                        _ptr(output), _i64(out_shape))
 
 
+def conv2d_fwd_epilogue_check(input, filter, output, *, filter_is_fcrs, stride=1, padding=0,
+                              dilation=1, groups=1, source=None, beta=0.0, scale=None,
+                              bias=None, activation=None, workspace=None, workspace_bytes=0,
+                              dtype=None, in_shape=None, filt_shape=None,
+                              out_shape=None) -> int:
+    """Host-only gate of conv2d_fwd_epilogue: 0 or a decline reason code."""
+    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
+                      groups, dtype, source, beta, in_shape, filt_shape, out_shape)
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    epi = make_epilogue(scale, bias, activation)
+    return lib().conv2d_fwd_epilogue_check(*head, _epi_ref(epi), _ptr(workspace),
+                                           int(workspace_bytes))
+
+
+def conv2d_fwd_query(in_shape, filt_shape, out_shape, *, filter_is_fcrs, dtype, stride=1,
+                     padding=0, dilation=1, groups=1) -> int:
+    """Pointer-free gate of the problem's shapes and parameters: 0 or a
+    decline reason code.  dtype is a torch dtype or a dtype code."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return lib().conv2d_fwd_query(_i64(in_shape), int(bool(filter_is_fcrs)), _i64(filt_shape),
+                                  _i64(out_shape), _pair(stride), _pair(dilation),
+                                  _pair(padding), int(groups), int(code))
+
+
 def conv2d_fwd_epilogue(input, filter, output, *, filter_is_fcrs, stride=1, padding=0,
                         dilation=1, groups=1, source=None, beta=0.0, scale=None, bias=None,
                         activation=None, workspace=None, workspace_bytes=0, stream=None,
                         dtype=None, in_shape=None, filt_shape=None, out_shape=None) -> int:
     """conv2d_fwd with the fused per-channel epilogue
     act(scale[co] * conv + bias[co] + beta * source)."""
-    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
-                      groups, dtype, source, beta, in_shape, filt_shape, out_shape)
     if isinstance(workspace, torch.Tensor) and not workspace_bytes:
         workspace_bytes = workspace.numel() * workspace.element_size()
+    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
+                      groups, dtype, source, beta, in_shape, filt_shape, out_shape,
+                      launch=True, scale=scale, bias=bias, workspace=workspace,
+                      workspace_bytes=workspace_bytes)
     epi = make_epilogue(scale, bias, activation)
     return lib().conv2d_fwd_epilogue(*head, _epi_ref(epi), _ptr(workspace),
                                      int(workspace_bytes), _stream(stream, output))
@@ -256,7 +396,7 @@ def conv2d_fwd_nk_epilogue(input, nk, filt_shape, output, *, filter_is_fcrs, str
     """conv2d_fwd_nk with the fused per-channel epilogue."""
     head = _conv_head(input, nk, filter_is_fcrs, output, stride, dilation, padding, groups,
                       dtype, source, beta, in_shape=in_shape, filt_shape=filt_shape,
-                      out_shape=out_shape)
+                      out_shape=out_shape, launch=True, nk=True, scale=scale, bias=bias)
     epi = make_epilogue(scale, bias, activation)
     return lib().conv2d_fwd_nk_epilogue(*head, _epi_ref(epi), _stream(stream, output))
 
@@ -273,11 +413,21 @@ def conv2d_nk_row_pitch(filt_shape, filter_is_fcrs, dtype) -> int:
 
 def conv2d_filter_to_nk(filter, nk, *, filter_is_fcrs, stream=None, dtype=None,
                         filt_shape=None, nk_bytes=None) -> int:
-    """Enqueue the filter transpose into nk.  1 enqueued, 0 declined, < 0 error."""
+    """Enqueue the filter transpose into nk.  1 enqueued, 0 declined, < 0 error.
+    Tensors must be contiguous GPU tensors on one device, nk holding at least
+    nk_bytes."""
+    _check_tensors(dict(filter=filter, nk=nk))
     filt_shape = filter.shape if filt_shape is None else filt_shape
     code = dtype_code(filter.dtype) if dtype is None else dtype
     if nk_bytes is None:
         nk_bytes = nk.numel() * nk.element_size()
+    elif isinstance(nk, torch.Tensor) and _nbytes(nk) < int(nk_bytes):
+        raise InvalidArgument(f"nk holds {_nbytes(nk)} bytes, nk_bytes says {nk_bytes}")
+    if (isinstance(filter, torch.Tensor) and code in (0, 1, 2)
+            and min(int(v) for v in filt_shape) >= 0
+            and _nbytes(filter) < _prod(filt_shape) * (1 if code == 2 else 2)):
+        raise InvalidArgument(f"filter holds {_nbytes(filter)} bytes, the shape "
+                              f"{tuple(filt_shape)} needs more")
     return lib().conv2d_filter_to_nk(_ptr(filter), int(bool(filter_is_fcrs)),
                                      _i64(filt_shape), int(code), _ptr(nk), int(nk_bytes),
                                      _stream(stream, nk))
@@ -296,11 +446,20 @@ def conv2d_im2col_bytes(in_shape, r, s, *, stride=1, padding=0, dtype) -> int:
 def conv2d_im2col(input, r, s, a_out, *, stride=1, padding=0, stream=None, dtype=None,
                   in_shape=None, a_bytes=None) -> int:
     """Enqueue the materialised im2col of input into a_out (rows of Kp
-    elements).  1 enqueued, 0 declined, < 0 HIP error."""
+    elements).  1 enqueued, 0 declined, < 0 HIP error.  Tensors must be
+    contiguous GPU tensors on one device, a_out holding at least a_bytes."""
+    _check_tensors(dict(input=input, a_out=a_out))
     in_shape = input.shape if in_shape is None else in_shape
     code = dtype_code(input.dtype) if dtype is None else dtype
     if a_bytes is None:
         a_bytes = a_out.numel() * a_out.element_size()
+    elif isinstance(a_out, torch.Tensor) and _nbytes(a_out) < int(a_bytes):
+        raise InvalidArgument(f"a_out holds {_nbytes(a_out)} bytes, a_bytes says {a_bytes}")
+    if (isinstance(input, torch.Tensor) and code in (0, 1, 2)
+            and min(int(v) for v in in_shape) >= 0
+            and _nbytes(input) < _prod(in_shape) * (1 if code == 2 else 2)):
+        raise InvalidArgument(f"input holds {_nbytes(input)} bytes, the shape "
+                              f"{tuple(in_shape)} needs more")
     return lib().conv2d_im2col(_ptr(input), _i64(in_shape), _rs(r, s), _pair(stride),
                                _pair(padding), int(code), _ptr(a_out), int(a_bytes),
                                _stream(stream, a_out))
@@ -346,10 +505,16 @@ def conv2d_transposed_workspace_bytes(in_shape, filt_rsfc, *, stride=1, padding=
 
 
 def _tr_head(input, filter, output, stride, dilation, padding, dtype, source, beta, scale,
-             bias, activation, in_shape, filt_shape, out_shape):
+             bias, activation, in_shape, filt_shape, out_shape, *, launch=False,
+             workspace=None, workspace_bytes=0):
     in_shape = input.shape if in_shape is None else in_shape
     filt_shape = filter.shape if filt_shape is None else filt_shape
     out_shape = output.shape if out_shape is None else out_shape
+    if launch:
+        # the RSFC filter [R, S, F, C] holds as many elements as an RSCF one
+        _check_fwd(input, filter, output, source, dtype, in_shape, filt_shape, out_shape,
+                   False, scale=scale, bias=bias, workspace=workspace,
+                   workspace_bytes=workspace_bytes)
     if dtype is None:
         dtype = dtype_code(input.dtype)
     return [_ptr(input), _i64(in_shape), _ptr(filter), _i64(filt_shape), _ptr(output),
@@ -375,10 +540,11 @@ def conv2d_transposed_fwd(input, filter, output, *, stride=1, padding=0, dilatio
                           in_shape=None, filt_shape=None, out_shape=None) -> int:
     """Enqueue the transposed convolution (RSFC filter).  1 handled, 0
     declined, < 0 HIP error."""
-    head = _tr_head(input, filter, output, stride, dilation, padding, dtype, source, beta,
-                    scale, bias, activation, in_shape, filt_shape, out_shape)
     if isinstance(workspace, torch.Tensor) and not workspace_bytes:
         workspace_bytes = workspace.numel() * workspace.element_size()
+    head = _tr_head(input, filter, output, stride, dilation, padding, dtype, source, beta,
+                    scale, bias, activation, in_shape, filt_shape, out_shape, launch=True,
+                    workspace=workspace, workspace_bytes=workspace_bytes)
     return lib().conv2d_transposed_fwd(*head, _ptr(workspace), int(workspace_bytes),
                                        _stream(stream, output))
 
@@ -430,12 +596,10 @@ def conv2d(input, filter, *, filter_is_fcrs, stride=1, padding=0, source=None, b
                              scale=scale, bias=bias, activation=activation, workspace=ws,
                              stream=stream)
     if rc == 0:
-        reason = conv2d_fwd_check(input, filter, out, filter_is_fcrs=filter_is_fcrs,
-                                  stride=stride, padding=padding, source=source, beta=beta,
-                                  workspace=ws)
-        if reason == 0:
-            reason = conv2d_epilogue_check(out, scale=scale, bias=bias,
-                                           activation=activation)
+        reason = conv2d_fwd_epilogue_check(input, filter, out, filter_is_fcrs=filter_is_fcrs,
+                                           stride=stride, padding=padding, source=source,
+                                           beta=beta, scale=scale, bias=bias,
+                                           activation=activation, workspace=ws)
         raise Declined(f"conv2d_fwd declined: {REASONS.get(reason, reason)}")
     if rc < 0:
         raise RuntimeError(f"conv2d_fwd failed with HIP error {-rc}")

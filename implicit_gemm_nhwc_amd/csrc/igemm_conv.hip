@@ -19,7 +19,7 @@ namespace {
 
 using namespace igc;
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 int elem_bytes(int32_t dtype) { return dtype == IGC_DTYPE_FP8_E4M3FN ? 1 : 2; }
 
@@ -132,8 +132,11 @@ int32_t check_all(const void* input, const int64_t in_nhwc[4], const void* filte
     if (overlaps(output, out_bytes, input, in_bytes) || overlaps(output, out_bytes, filter, f_bytes))
         return IGC_DECLINE_OVERLAP;
     if (workspace && overlaps(output, out_bytes, workspace, nk_bytes)) return IGC_DECLINE_OVERLAP;
+    // the NK transpose writes the workspace before the GEMM reads the
+    // input, the filter and the residual source
     if (workspace && (overlaps(workspace, nk_bytes, input, in_bytes) ||
-                      overlaps(workspace, nk_bytes, filter, f_bytes)))
+                      overlaps(workspace, nk_bytes, filter, f_bytes) ||
+                      (source && overlaps(workspace, nk_bytes, source, out_bytes))))
         return IGC_DECLINE_OVERLAP;
     if (source && source != output && overlaps(source, out_bytes, output, out_bytes))
         return IGC_DECLINE_OVERLAP;
@@ -147,8 +150,10 @@ int32_t hip_fail(hipError_t e) { return e == hipSuccess ? 1 : -(int32_t)e; }
 
 // The fused epilogue's own gate: a known activation, 4-byte aligned
 // coefficient arrays, and none of them overlapping the output (every
-// workgroup reads them while others write the output).
-int32_t check_epilogue(const igc_epilogue* epi, const void* output, const Shape& s) {
+// workgroup reads them while others write the output) or the workspace
+// (written by the filter transpose before the GEMM reads them).
+int32_t check_epilogue(const igc_epilogue* epi, const void* output, const Shape& s,
+                       const void* workspace = nullptr, size_t workspace_used = 0) {
     if (!epi) return IGC_OK;
     if (epi->activation != IGC_ACT_NONE && epi->activation != IGC_ACT_RELU &&
         epi->activation != IGC_ACT_SILU)
@@ -159,6 +164,8 @@ int32_t check_epilogue(const igc_epilogue* epi, const void* output, const Shape&
         if (!c) continue;
         if (((uintptr_t)c & 3u) != 0) return IGC_DECLINE_EPILOGUE;
         if (overlaps(c, coef_bytes, output, out_bytes)) return IGC_DECLINE_EPILOGUE;
+        if (workspace && overlaps(c, coef_bytes, workspace, workspace_used))
+            return IGC_DECLINE_EPILOGUE;
     }
     return IGC_OK;
 }
@@ -761,6 +768,32 @@ const char* conv2d_reason_string(int32_t reason) {
     }
 }
 
+int32_t conv2d_fwd_query(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                         const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                         const int32_t stride[2], const int32_t dilation[2],
+                         const int32_t padding[2], int32_t groups, int32_t dtype) {
+    return check_shapes(in_nhwc, filter_is_fcrs, filt_dims, out_nhwc, stride, dilation, padding,
+                        groups, dtype, nullptr);
+}
+
+int32_t conv2d_fwd_epilogue_check(const void* input, const int64_t in_nhwc[4],
+                                  const void* filter, int32_t filter_is_fcrs,
+                                  const int64_t filt_dims[4], const void* output,
+                                  const int64_t out_nhwc[4], const int32_t stride[2],
+                                  const int32_t dilation[2], const int32_t padding[2],
+                                  int32_t groups, int32_t dtype, const void* source, float beta,
+                                  const igc_epilogue* epilogue, const void* workspace,
+                                  size_t workspace_bytes) {
+    (void)beta;
+    Shape s;
+    const int32_t rc = check_all(input, in_nhwc, filter, 0, filter_is_fcrs, filt_dims, output,
+                                 out_nhwc, stride, dilation, padding, groups, dtype, source,
+                                 workspace, workspace_bytes, &s);
+    if (rc != IGC_OK) return rc;
+    return check_epilogue(epilogue, output, s, workspace,
+                          (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype));
+}
+
 int32_t conv2d_fwd_check(const void* input, const int64_t in_nhwc[4], const void* filter,
                          int32_t filter_is_fcrs, const int64_t filt_dims[4], const void* output,
                          const int64_t out_nhwc[4], const int32_t stride[2],
@@ -824,6 +857,8 @@ int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs, const in
     if (s.K >= lim) return 0;
     s.kpad = round_up(s.K, KT_BYTES / eb);
     s.kpitch = nk_pitch(s.K, s.F, eb);
+    // the transpose kernel indexes both matrices with 32-bit integers
+    if (s.kpitch >= lim || s.F * s.kpitch * eb >= lim) return 0;
     const size_t need = (size_t)(s.F * s.kpitch) * (size_t)eb;
     const size_t fbytes = (size_t)(s.K * s.F) * (size_t)eb;
     if (nk_bytes < need) return 0;
@@ -872,10 +907,10 @@ int32_t conv2d_fwd_epilogue(const void* input, const int64_t in_nhwc[4], const v
                                  out_nhwc, stride, dilation, padding, groups, dtype, source,
                                  workspace, workspace_bytes, &s);
     if (rc != IGC_OK) return 0;
-    if (check_epilogue(epilogue, output, s) != IGC_OK) return 0;
+    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
+    if (check_epilogue(epilogue, output, s, workspace, nk_bytes) != IGC_OK) return 0;
     if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
     hipStream_t st = (hipStream_t)stream;
-    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
     void* nk = workspace;
     bool owned = false;
     if (!nk && nk_bytes) {

@@ -190,6 +190,22 @@ __device__ __forceinline__ float epi_act(const ConvArgs& a, float v) {
     return v;
 }
 
+// Wait states between the last scaled fp8 MFMA and an epilogue that may read
+// its accumulators at once.  For the scaled fp8 MFMAs the wait states the
+// compiler inserts before such a read were measured (in a kernel whose
+// epilogue read the final MFMA's result first) to be too few: the
+// last-written result rows read stale.  Every fp8 kernel therefore puts 24
+// extra independent wait states between its last MFMA and its epilogue; the
+// scheduling fences keep the compiler from moving either across them.
+template <int DT>
+__device__ __forceinline__ void fp8_accumulator_margin() {
+    if constexpr (DT == DT_FP8) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ f32x4 mfma_step(const i32x4* a, const i32x4* b, f32x4 acc);
 
@@ -407,6 +423,7 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
         __syncthreads();
     }
 
+    fp8_accumulator_margin<DT>();
     // ---- epilogue: lane owns pixel (lane & 15) and channels 4*(lane>>4)+0..3
     // of each 16x16 block.  D = acc (+ beta * src), one rounding, NHWC store.
     constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
@@ -671,6 +688,7 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
         }
     }
 
+    fp8_accumulator_margin<DT>();
     // ---- epilogue: lane owns pixel (lane & 15) of each 16-pixel block
     constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
     const bool vec_ok = (a.F & 3) == 0;
@@ -987,15 +1005,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         if (q < NB) block(IntC<0>{});
     }
     constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
-    if constexpr (DT == DT_FP8) {
-        // The epilogue may read the last MFMA's accumulators first.  For the
-        // scaled fp8 MFMA the wait states the compiler inserts were measured
-        // (in a kernel that did so) to be too few: the last-written result
-        // rows read stale.  Extra independent wait states first.
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    fp8_accumulator_margin<DT>();   // the epilogue may read the last MFMA first
     const int th_n = min(a.TH, a.Ho - oh0);
     const int tw_n = min(a.TW, a.Wo - ow0);
     if ((a.F & 7) == 0) {
@@ -1437,6 +1447,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             }
         }
     }
+    fp8_accumulator_margin<DT>();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // masked tail requests
     __syncthreads();   // stages no longer read or written
 

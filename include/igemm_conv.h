@@ -73,15 +73,17 @@ enum {
     IGC_DECLINE_NULL_POINTER = 10, /* NULL pointer for a non-empty tensor,
                                       or NULL shape/parameter array          */
     IGC_DECLINE_OVERLAP = 11,      /* output overlaps input, filter or
-                                      workspace; or source overlaps output
-                                      without being exactly the output       */
+                                      workspace; workspace overlaps input,
+                                      filter or source; or source overlaps
+                                      output without being exactly it        */
     IGC_DECLINE_WORKSPACE = 12,    /* workspace given but smaller than
                                       conv2d_workspace_bytes()               */
     IGC_DECLINE_SIZE_LIMIT = 13,   /* a size beyond the kernels' 32-bit index
                                       ranges (see conv2d_fwd_check)          */
     IGC_DECLINE_EPILOGUE = 14      /* fused epilogue: unknown activation,
                                       scale/bias not 4-byte aligned, or
-                                      scale/bias overlapping the output      */
+                                      scale/bias overlapping the output or
+                                      the workspace                          */
 };
 
 /*
@@ -119,6 +121,20 @@ int32_t conv2d_abi_version(void);
 
 /* Human-readable name of a decline reason code (static string). */
 const char* conv2d_reason_string(int32_t reason);
+
+/*
+ * Pointer-free acceptance check of a problem's shapes and parameters (no
+ * HIP call): page "dispatch_amd_4wave_conv2d" (Parameters and Args: element
+ * types, stride, dilation, symmetric padding, groups, NHWC output shape) plus
+ * this library's shape limits (IGC_DECLINE_VECTOR_WIDTH,
+ * IGC_DECLINE_SIZE_LIMIT).  Returns IGC_OK or the decline reason; a call
+ * with these shapes is then accepted unless its pointers fail the rules of
+ * conv2d_fwd_check (alignment, NULL, overlap, workspace size).
+ */
+int32_t conv2d_fwd_query(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                         const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                         const int32_t stride[2], const int32_t dilation[2],
+                         const int32_t padding[2], int32_t groups, int32_t dtype);
 
 /*
  * Host-only acceptance check (no HIP call, no memory access): the gate of
@@ -202,8 +218,8 @@ int64_t conv2d_nk_row_pitch(const int64_t filt_dims[4], int32_t filter_is_fcrs,
  *   nk[co * pitch + k] = 0                                     for K <= k < pitch
  * with pitch = conv2d_nk_row_pitch().  A bit copy: values are not converted.
  * nk must be 16-byte aligned and hold nk_bytes >= conv2d_workspace_bytes().
- * Returns 1 = enqueued, 0 = declined (bad dtype/dims/pointers, too small),
- * or -(hipError_t).
+ * Returns 1 = enqueued, 0 = declined (bad dtype/dims/pointers, too small,
+ * or an NK matrix of 2^31 bytes or more), or -(hipError_t).
  */
 int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs,
                             const int64_t filt_dims[4], int32_t dtype,
@@ -249,6 +265,22 @@ int32_t conv2d_fwd_nk_epilogue(const void* input, const int64_t in_nhwc[4],
                                const int32_t padding[2], int32_t groups,
                                int32_t dtype, const void* source, float beta,
                                const igc_epilogue* epilogue, void* stream);
+
+/*
+ * Host-only gate of conv2d_fwd_epilogue (no HIP call, no memory access):
+ * conv2d_fwd_check's rules, then the epilogue's (conv2d_epilogue_check),
+ * and scale / bias must not overlap the workspace (the filter transpose
+ * writes it before the GEMM reads them).  Returns IGC_OK or a decline
+ * reason; conv2d_fwd_epilogue declines exactly when this is not IGC_OK.
+ */
+int32_t conv2d_fwd_epilogue_check(const void* input, const int64_t in_nhwc[4],
+                                  const void* filter, int32_t filter_is_fcrs,
+                                  const int64_t filt_dims[4], const void* output,
+                                  const int64_t out_nhwc[4], const int32_t stride[2],
+                                  const int32_t dilation[2], const int32_t padding[2],
+                                  int32_t groups, int32_t dtype, const void* source, float beta,
+                                  const igc_epilogue* epilogue, const void* workspace,
+                                  size_t workspace_bytes);
 
 /*
  * Host-only check of an epilogue against an output of shape out_nhwc

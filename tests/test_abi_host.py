@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_reason_names():
-    assert igc.conv2d_abi_version() == 2
+    assert igc.conv2d_abi_version() == 3
     for code, name in igc.REASONS.items():
         assert igc.conv2d_reason_string(code) == name
     assert igc.conv2d_reason_string(999) == "unknown"
@@ -101,6 +101,12 @@ def test_base_case_accepted():
     (dict(source=Y + 64), "overlap"),
     (dict(workspace=Y + 256, workspace_bytes=1 << 20), "overlap"),
     (dict(workspace=WS, workspace_bytes=100), "workspace"),
+    # the transpose writes the workspace before the GEMM reads the source
+    (dict(source=SRC, beta=0.5, workspace=SRC + 256, workspace_bytes=1 << 20), "overlap"),
+    (dict(source=SRC, beta=0.5, workspace=SRC - 48 * 328 * 2 + 16,
+          workspace_bytes=48 * 328 * 2), "overlap"),
+    (dict(workspace=X + 4096, workspace_bytes=1 << 20), "overlap"),
+    (dict(workspace=W + 64, workspace_bytes=1 << 20), "overlap"),
     (dict(in_shape=(300000, 100, 100, 32), out_shape=(300000, 100, 100, 48)), "size_limit"),
 ])
 def test_decline_paths(kw, reason):
@@ -334,3 +340,150 @@ def test_transposed_declined_call_enqueues_nothing():
     assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "dilation": 2}) == 0
     args = dict(TBASE, in_shape=(0, 9, 9, 32), out_shape=(0, 9, 9, 48))
     assert igc.conv2d_transposed_fwd(X, W, Y, **args) == 1
+
+
+def test_workspace_beside_source_accepted():
+    # a workspace that ends exactly where the source starts does not overlap it
+    nk = 48 * 328 * 2
+    assert _check(source=SRC, beta=0.5, workspace=SRC - nk, workspace_bytes=nk) == 0
+
+
+# ------------------------------------------------------ pointer-free query
+def test_query_matches_pointer_gate():
+    """conv2d_fwd_query gives the shape/parameter reason conv2d_fwd_check
+    gives for well-formed pointers, for accepted and declined problems."""
+    cases = [dict(), dict(stride=3), dict(dilation=2), dict(padding=(0, 1)), dict(groups=2),
+             dict(dtype=7), dict(filt_shape=(3, 3, 16, 48)), dict(out_shape=(2, 9, 9, 47)),
+             dict(in_shape=(2, 9, 9, 12), filt_shape=(3, 3, 12, 48)),
+             dict(in_shape=(300000, 100, 100, 32), out_shape=(300000, 100, 100, 48)),
+             dict(in_shape=(0, 9, 9, 32), out_shape=(0, 9, 9, 48))]
+    for kw in cases:
+        args = {**BASE, **kw}
+        q = igc.conv2d_fwd_query(args["in_shape"], args["filt_shape"], args["out_shape"],
+                                 filter_is_fcrs=args["filter_is_fcrs"], dtype=args["dtype"],
+                                 stride=args["stride"], padding=args["padding"],
+                                 dilation=args["dilation"], groups=args["groups"])
+        assert q == _check(**kw), kw
+    # pointer rules are not the query's: a misaligned input passes it
+    assert igc.conv2d_fwd_query(BASE["in_shape"], BASE["filt_shape"], BASE["out_shape"],
+                                filter_is_fcrs=False, dtype=0, padding=1) == 0
+    assert igc.REASONS[_check(input=X + 8)] == "alignment"
+
+
+# --------------------------------------------- epilogue against the workspace
+NK_BYTES = 48 * 328 * 2
+
+
+@pytest.mark.parametrize("kw,reason", [
+    (dict(scale=SC, bias=BI), "ok"),
+    (dict(scale=WS + 64), "epilogue"),                     # inside the workspace
+    (dict(bias=WS + NK_BYTES - 4, activation="relu"), "epilogue"),
+    (dict(bias=WS + NK_BYTES), "ok"),                       # just past its end
+    (dict(scale=WS - 48 * 4), "ok"),                        # ends where it starts
+    (dict(scale=WS - 48 * 4 + 4), "epilogue"),
+])
+def test_epilogue_against_workspace(kw, reason):
+    code = igc.conv2d_fwd_epilogue_check(X, W, Y, workspace=WS, workspace_bytes=NK_BYTES,
+                                         **BASE, **kw)
+    assert igc.REASONS[code] == reason
+    if reason != "ok":
+        assert igc.conv2d_fwd_epilogue(X, W, Y, workspace=WS, workspace_bytes=NK_BYTES,
+                                       **BASE, **kw) == 0
+
+
+def test_filter_to_nk_declines_nk_of_2gib():
+    # NK matrix of 2^31 bytes or more: the transpose's 32-bit indices would
+    # overflow, so the call is declined (no GPU here: it must not launch)
+    lib = igc.lib()
+    big = (1, 1, 1 << 16, 1 << 15)            # K = 65536, C_out = 32768 -> 2^32 bytes bf16
+    assert lib.conv2d_filter_to_nk(W, 0, igc._i64(big), 0, WS, 1 << 40, None) == 0
+    just = (1, 1, 1 << 14, 1 << 16)           # 2^30 elements -> 2^31 bytes
+    assert lib.conv2d_filter_to_nk(W, 0, igc._i64(just), 0, WS, 1 << 40, None) == 0
+
+
+# ------------------------------------------------------- binding checks
+def _cpu(shape, dt=torch.bfloat16):
+    return torch.zeros(shape, dtype=dt)
+
+
+def test_binding_rejects_host_tensors():
+    x, w, y = _cpu((1, 4, 4, 16)), _cpu((3, 3, 16, 8)), _cpu((1, 4, 4, 8))
+    with pytest.raises(igc.InvalidArgument, match="GPU tensor"):
+        igc.conv2d_fwd(x, w, y, filter_is_fcrs=False, padding=1)
+    with pytest.raises(igc.InvalidArgument, match="GPU tensor"):
+        igc.conv2d_fwd_nk(x, _cpu(1000, torch.uint8), w.shape, y, filter_is_fcrs=False,
+                          padding=1)
+    with pytest.raises(igc.InvalidArgument, match="GPU tensor"):
+        igc.conv2d_filter_to_nk(w, _cpu(1000, torch.uint8), filter_is_fcrs=False)
+    with pytest.raises(igc.InvalidArgument, match="GPU tensor"):
+        igc.conv2d_im2col(x, 3, 3, _cpu(100000, torch.uint8), padding=1)
+    with pytest.raises(igc.InvalidArgument, match="GPU tensor"):
+        igc.conv2d_transposed_fwd(x, _cpu((3, 3, 8, 16)), y, padding=1)
+    # a host tensor mixed with raw device pointers is caught too
+    with pytest.raises(igc.InvalidArgument, match="GPU tensor"):
+        igc.conv2d_fwd(X, W, Y, source=_cpu((2, 9, 9, 48)), beta=1.0, **BASE)
+
+
+class _FakeCuda:
+    """Stands in for a GPU tensor in the binding's checks on a machine
+    without a GPU: the binding only reads these attributes before calling
+    into the library."""
+
+    def __init__(self, shape, dtype, contiguous=True, device="cuda:0", ptr=0x70000000):
+        self.shape = torch.Size(shape)
+        self.dtype = dtype
+        self.is_cuda = True
+        self.device = torch.device(device)
+        self._contig = contiguous
+        self._ptr = ptr
+
+    def is_contiguous(self):
+        return self._contig
+
+    def numel(self):
+        n = 1
+        for v in self.shape:
+            n *= v
+        return n
+
+    def element_size(self):
+        return torch.empty((), dtype=self.dtype).element_size()
+
+    def data_ptr(self):
+        return self._ptr
+
+
+def test_binding_checks_tensor_properties(monkeypatch):
+    monkeypatch.setattr(igc.torch, "Tensor", _FakeCuda)
+    ok = dict(input=_FakeCuda((1, 4, 4, 16), torch.bfloat16, ptr=X),
+              filter=_FakeCuda((3, 3, 16, 8), torch.bfloat16, ptr=W),
+              output=_FakeCuda((1, 4, 4, 8), torch.bfloat16, ptr=Y))
+
+    def call(**kw):
+        args = {**ok, **kw}
+        return igc.conv2d_fwd_epilogue(args.pop("input"), args.pop("filter"),
+                                       args.pop("output"), filter_is_fcrs=False, padding=1,
+                                       stream=0, **args)
+    bad = [
+        (dict(input=_FakeCuda((1, 4, 4, 16), torch.bfloat16, contiguous=False)), "contiguous"),
+        (dict(filter=_FakeCuda((3, 3, 16, 8), torch.float16)), "filter dtype"),
+        (dict(output=_FakeCuda((1, 4, 4, 8), torch.float16)), "output dtype"),
+        (dict(input=_FakeCuda((1, 4, 4, 16), torch.float32)), "input dtype"),
+        (dict(source=_FakeCuda((1, 4, 4, 4), torch.bfloat16, ptr=SRC)), "source"),
+        (dict(source=_FakeCuda((1, 4, 4, 8), torch.float16, ptr=SRC)), "source"),
+        (dict(output=_FakeCuda((1, 4, 4, 8), torch.bfloat16, device="cuda:1")), "on cuda:1"),
+        (dict(scale=_FakeCuda((8,), torch.float16, ptr=SC)), "float32"),
+        (dict(bias=_FakeCuda((7,), torch.float32, ptr=BI)), "C_out"),
+        (dict(workspace=_FakeCuda((10,), torch.uint8, ptr=WS), workspace_bytes=4096),
+         "workspace"),
+    ]
+    for kw, msg in bad:
+        with pytest.raises(igc.InvalidArgument, match=msg):
+            call(**kw)
+    # explicit shapes larger than the buffers they describe
+    with pytest.raises(igc.InvalidArgument, match="input holds"):
+        igc.conv2d_fwd(ok["input"], ok["filter"], ok["output"], filter_is_fcrs=False,
+                       padding=1, in_shape=(2, 4, 4, 16), out_shape=(2, 4, 4, 8), stream=0)
+    with pytest.raises(igc.InvalidArgument, match="NK matrix holds"):
+        igc.conv2d_fwd_nk(ok["input"], _FakeCuda((100,), torch.uint8, ptr=WS), (3, 3, 16, 8),
+                          ok["output"], filter_is_fcrs=False, padding=1, stream=0)

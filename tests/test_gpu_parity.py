@@ -4,9 +4,8 @@ Tolerance (from the arithmetic: fp32 accumulation of exactly-rounded inputs,
 one final rounding to bf16/fp16 with a relative error of at most 2^-9 / 2^-11):
   max|gpu - ref| <= 1e-2 * max|ref|  for bf16 / fp16 inputs,
   max|gpu - ref| <= 4e-2 * max|ref|  for fp8 e4m3fn inputs (bf16 output),
-over the whole tensor (or over the sampled pixels for the largest workload),
-with every output finite.  Where the exact result is representable in the
-output type (delta filters, all-ones border counts) the test asks for exact
+over the whole tensor, with every output finite.  Where the exact result is
+representable in the output type (delta filters, all-ones border counts) the test asks for exact
 bits.  Bitwise checks compare two GPU calls (layouts, residual forms,
 in-place, determinism).
 """
@@ -108,23 +107,6 @@ def test_filter_to_nk_bit_exact(dtype, fcrs, r, s, c, f):
 
 
 # ----------------------------------------------------- named workloads
-SAMPLED = {"fp8_5x5_256c_residual_n16"}
-
-
-def _sample_pixels(n, ho, wo, count, seed):
-    rng = np.random.default_rng(seed)
-    pix = set(rng.integers(0, n * ho * wo, size=count).tolist())
-    for b in (0, n - 1):
-        for oh in range(ho):
-            for ow in (0, 1, wo - 2, wo - 1):
-                pix.add((b * ho + oh) * wo + ow)
-        for ow in range(wo):
-            for oh in (0, 1, ho - 2, ho - 1):
-                pix.add((b * ho + oh) * wo + ow)
-    pix.add(n * ho * wo - 1)
-    return np.array(sorted(pix), dtype=np.int64)
-
-
 @pytest.mark.parametrize("name", datagen.WORKLOAD_ORDER)
 def test_workload_parity(name):
     spec, x, w, src = datagen.make_workload(name)
@@ -134,19 +116,11 @@ def test_workload_parity(name):
     out = _run(x, w, fcrs=spec["fcrs"], stride=spec["stride"], pad=spec["pad"], src=src,
                beta=spec["beta"])
     tol = TOL[spec["dtype"]]
-    if name in SAMPLED:
-        n, ho, wo, f = out.shape
-        pix = _sample_pixels(n, ho, wo, 768, seed=5)
-        ref = oracle.conv2d_points(x, w, pix, filter_is_fcrs=spec["fcrs"],
-                                   stride=spec["stride"], padding=spec["pad"], source=src,
-                                   beta=spec["beta"])
-        got = out.reshape(-1, f)[torch.as_tensor(pix, device=DEV)]
-        assert torch.isfinite(out.float()).all()
-        err, scale = _assert_close(got, ref, tol, name)
-    else:
-        ref = oracle.conv2d(x, w, filter_is_fcrs=spec["fcrs"], stride=spec["stride"],
-                            padding=spec["pad"], source=src, beta=spec["beta"])
-        err, scale = _assert_close(out, ref, tol, name)
+    # the whole output tensor against the oracle (the fp8 5x5 workload's
+    # 214.7 GFLOP take the oracle a few seconds on the host's cores)
+    ref = oracle.conv2d(x, w, filter_is_fcrs=spec["fcrs"], stride=spec["stride"],
+                        padding=spec["pad"], source=src, beta=spec["beta"])
+    err, scale = _assert_close(out, ref, tol, name)
     _say(f"  max|err|/max|ref| = {err / max(scale, 1e-300):.3e}")
 
 
@@ -162,8 +136,9 @@ def test_fp8_workload_fcrs_variant_bitwise():
 
 # ------------------------------------------------------ kernel paths
 # One case per kernel variant the dispatcher can pick, each checked to go
-# where it is meant to (conv2d_fwd_kernel_name) and against the oracle
-# (sampled pixels for the 65536-pixel layers).
+# where it is meant to (conv2d_fwd_kernel_name) and against the oracle over
+# the whole output.  The "single" cases give a wave a single block of output
+# pixels, so the epilogue may read the final MFMA's accumulators first.
 PATH_CASES = [
     # id, dtype, N, H, W, C, F, R, S, stride, pad, residual, kernel
     ("wide256_bf16_tap", "bfloat16", 16, 64, 64, 64, 256, 3, 3, 1, 1, False, "wide"),
@@ -180,7 +155,14 @@ PATH_CASES = [
     # one accumulator block per wave: the epilogue reads the last MFMA first
     ("band_fp8_single_block", "float8_e4m3fn", 1, 8, 8, 64, 16, 3, 3, 1, 1, False, "band"),
     ("resident_c48", "bfloat16", 2, 20, 20, 48, 32, 3, 3, 1, 1, False, "resident"),
+    ("resident_fp16_c48", "float16", 2, 10, 10, 48, 24, 3, 3, 1, 1, True, "resident"),
+    ("resident_fp8_single", "float8_e4m3fn", 1, 4, 4, 48, 16, 3, 3, 1, 1, True, "resident"),
     ("fallback_tiled", "bfloat16", 1, 12, 12, 96, 64, 5, 5, 1, 2, True, "tiled"),
+    ("fallback_tiled_fp16", "float16", 1, 12, 12, 96, 64, 5, 5, 1, 2, True, "tiled"),
+    ("fallback_tiled_fp8", "float8_e4m3fn", 1, 12, 12, 48, 64, 5, 5, 1, 2, False, "tiled"),
+    ("fallback_tiled_fp8_single", "float8_e4m3fn", 1, 4, 4, 208, 16, 5, 5, 1, 2, True, "tiled"),
+    ("wide_fp8_single", "float8_e4m3fn", 1, 4, 4, 64, 96, 3, 3, 1, 1, True, "wide"),
+    ("wide256_fp8_resid", "float8_e4m3fn", 16, 64, 64, 64, 256, 3, 3, 1, 1, True, "wide"),
 ]
 _KERNEL = {"wide": "igemm_fwd_wide_kernel", "band": "igemm_fwd_band_kernel",
            "resident": "igemm_fwd_resident_kernel", "tiled": "igemm_fwd_kernel"}
@@ -201,16 +183,9 @@ def test_kernel_paths(case):
     assert got_kernel == _KERNEL[kern], (cid, got_kernel)
     beta = 0.5 if resid else 0.0
     out = _run(x, wt, fcrs=False, stride=st, pad=p, src=src, beta=beta)
-    if n * ho * wo > 20000:
-        pix = _sample_pixels(n, ho, wo, 512, seed=11)
-        ref = oracle.conv2d_points(x, wt, pix, filter_is_fcrs=False, stride=st, padding=p,
-                                   source=src, beta=beta)
-        assert torch.isfinite(out.float()).all()
-        _assert_close(out.reshape(-1, f)[torch.as_tensor(pix, device=DEV)], ref, TOL[dt], cid)
-    else:
-        ref = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p, source=src,
-                            beta=beta)
-        _assert_close(out, ref, TOL[dt], cid)
+    ref = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p, source=src,
+                        beta=beta)
+    _assert_close(out, ref, TOL[dt], cid)
 
 
 # ------------------------------------------------------ randomized sweep
