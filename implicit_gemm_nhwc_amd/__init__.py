@@ -11,7 +11,8 @@ on one GPU, of the types and sizes their shape arguments describe):
 InvalidArgument is raised before anything is launched.
 
 Names mirror the C entry points:
-  conv2d_fwd, conv2d_fwd_check, conv2d_fwd_query, conv2d_fwd_nk, conv2d_filter_to_nk,
+  conv2d_fwd, conv2d_fwd_check, conv2d_fwd_query, conv2d_fwd_noalloc, conv2d_fwd_nk,
+  conv2d_filter_to_nk,
   conv2d_fwd_epilogue, conv2d_fwd_epilogue_check, conv2d_fwd_nk_epilogue,
   conv2d_epilogue_check,
   conv2d_im2col, conv2d_im2col_bytes,
@@ -85,6 +86,8 @@ def lib():
     L.conv2d_fwd_query.restype = i32
     L.conv2d_fwd.argtypes = conv_head + [vp, sz, vp]
     L.conv2d_fwd.restype = i32
+    L.conv2d_fwd_noalloc.argtypes = conv_head + [vp]
+    L.conv2d_fwd_noalloc.restype = i32
     L.conv2d_fwd_nk.argtypes = conv_head + [vp]
     L.conv2d_fwd_nk.restype = i32
     L.conv2d_workspace_bytes.argtypes, L.conv2d_workspace_bytes.restype = [i64p, i32, i32], sz
@@ -314,6 +317,20 @@ def conv2d_fwd(input, filter, output, *, filter_is_fcrs, stride=1, padding=0, di
                       launch=True, workspace=workspace, workspace_bytes=workspace_bytes)
     return lib().conv2d_fwd(*head, _ptr(workspace), int(workspace_bytes),
                             _stream(stream, output))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # IGC_NOALLOC_SCRATCH_BYTES in include/igemm_conv.h
+
+
+def conv2d_fwd_noalloc(input, filter, output, *, filter_is_fcrs, stride=1, padding=0,
+                       dilation=1, groups=1, source=None, beta=0.0, stream=None, dtype=None,
+                       in_shape=None, filt_shape=None, out_shape=None) -> int:
+    """conv2d_fwd with the NK matrix in the library's static device scratch
+    (no allocation).  1 handled, 0 declined, < 0 HIP error."""
+    head = _conv_head(input, filter, filter_is_fcrs, output, stride, dilation, padding,
+                      groups, dtype, source, beta, in_shape, filt_shape, out_shape,
+                      launch=True)
+    return lib().conv2d_fwd_noalloc(*head, _stream(stream, output))
 
 
 def conv2d_fwd_nk(input, nk, filt_shape, output, *, filter_is_fcrs, stride=1, padding=0,

@@ -633,9 +633,66 @@ hipError_t run_transposed(const TPlan& t, const void* input, const void* filter,
     return e;
 }
 
+// ---- the allocation-free entry point's scratch ----------------------------
+// The NK matrix of conv2d_fwd_noalloc lives in this file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in, not a device
+// address): on the first call on each device, with that device current, the
+// device address is looked up once and kept per device.
+constexpr size_t kScratchBytes = IGC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchPtrs {
+    std::mutex mu;
+    bool done[kMaxDevices] = {};
+    hipError_t err[kMaxDevices] = {};
+    void* ptr[kMaxDevices] = {};
+};
+ScratchPtrs g_scratch;
+
+hipError_t scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(g_scratch.mu);
+    if (!g_scratch.done[dev]) {
+        void* p = nullptr;
+        g_scratch.err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch.ptr[dev] = p;
+        g_scratch.done[dev] = true;
+    }
+    *out = g_scratch.ptr[dev];
+    return g_scratch.err[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t conv2d_fwd_noalloc(const void* input, const int64_t in_nhwc[4], const void* filter,
+                           int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
+                           const int64_t out_nhwc[4], const int32_t stride[2],
+                           const int32_t dilation[2], const int32_t padding[2], int32_t groups,
+                           int32_t dtype, const void* source, float beta, void* stream) {
+    Shape s;
+    // the gate of conv2d_fwd with no caller workspace (the scratch is the
+    // library's own, so no caller buffer can overlap it)
+    const int32_t rc = check_all(input, in_nhwc, filter, 0, filter_is_fcrs, filt_dims, output,
+                                 out_nhwc, stride, dilation, padding, groups, dtype, source,
+                                 nullptr, 0, &s);
+    if (rc != IGC_OK) return 0;
+    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
+    if (nk_bytes > kScratchBytes) return 0;   // beyond the static scratch: declined
+    if (s.M == 0 || s.F == 0) return 1;       // empty output: nothing to compute
+    void* nk = nullptr;
+    hipError_t e = scratch_ptr(&nk);
+    if (e != hipSuccess) return -(int32_t)e;
+    hipStream_t st = (hipStream_t)stream;
+    e = launch_transpose(filter, filter_is_fcrs, s, dtype, nk, st);
+    if (e == hipSuccess) e = launch_igemm(input, nk, output, source, beta, nullptr, s, dtype, st);
+    return hip_fail(e);
+}
 
 size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
                                          const int32_t stride[2], const int32_t padding[2],

@@ -180,6 +180,29 @@ int32_t conv2d_fwd(const void* input, const int64_t in_nhwc[4],
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * conv2d_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * NK filter matrix goes to a static device scratch array of the library,
+ * IGC_NOALLOC_SCRATCH_BYTES bytes per GPU, held until the process ends; no
+ * hipMalloc, hipFree or other allocating call is made.  Arguments as
+ * conv2d_fwd without the workspace.  Returns 1 = handled, 0 = declined
+ * (conv2d_fwd_check with a NULL workspace gives the reason, or the NK
+ * matrix, conv2d_workspace_bytes(), exceeds IGC_NOALLOC_SCRATCH_BYTES), or
+ * -(hipError_t).  The first call on each device looks up the scratch's
+ * device address (make it outside graph capture).  Every call on one GPU
+ * shares its scratch: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be ordered by the caller.
+ */
+#define IGC_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int32_t conv2d_fwd_noalloc(const void* input, const int64_t in_nhwc[4],
+                           const void* filter, int32_t filter_is_fcrs,
+                           const int64_t filt_dims[4],
+                           void* output, const int64_t out_nhwc[4],
+                           const int32_t stride[2], const int32_t dilation[2],
+                           const int32_t padding[2], int32_t groups,
+                           int32_t dtype, const void* source, float beta, void* stream);
+
+/*
  * Name of the GEMM kernel conv2d_fwd / conv2d_fwd_nk launch for this problem
  * (a static string: "igemm_fwd_band_kernel", "igemm_fwd_wide_kernel",
  * "igemm_fwd_resident_kernel", "igemm_fwd_kernel", or "none" when nothing is
