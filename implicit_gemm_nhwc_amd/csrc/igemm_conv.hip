@@ -276,7 +276,7 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
                 found = true;
                 *out = BandPlan{(int)th, (int)tw, (int)ph, (int)pw, tn, (int)fpitch, (int)ppitch,
                                 (int)prow, (int)spitch, (int)lds, (int)th_tiles, (int)tw_tiles,
-                                tiles};
+                                tiles, 0};
             }
         }
     }
@@ -295,11 +295,82 @@ bool wide_ok(const Shape& s, int32_t dtype) {
 }
 
 
+// Plan of the tap-fold kernel (igemm_tapfold.hpp), or false when the layer
+// does not fit it: C_out * R * S <= 32 (the (channel, tap) pairs of one
+// 32-row MFMA block) with R * S >= 2, C_in a whole number of 1, 2, 4, 8 or
+// 16 MFMA k-steps, and an image below 2^31 bytes.  The workgroup streams a
+// strip of output columns whose input row (PW = (TW - 1)*st + S pixels) is
+// one to four 32-pixel blocks, over TH output rows; strips times row
+// segments are chosen near one round of resident workgroups (as many per CU
+// as their LDS allows), the estimate charging each
+// workgroup its input bytes (at ~16 B/clk), a fixed start and ~400 clocks
+// per input row (more with fewer than four ring slots).  LDS: coefficients,
+// the NK rows, a ring of up to four input rows and R + 1 rows of fp32 partial
+// products.  The plan fields carry the kernel's geometry: TW/TH, PW/PH,
+// ppitch (bytes per staged pixel), prow (bytes per ring slot), spitch
+// (floats per partial-product pixel), fpitch (LDS offset of the ring),
+// groups (ring slots).
+bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out) {
+    const int64_t E = elem_bytes(dtype);
+    const int64_t ksb = dtype == IGC_DTYPE_FP8_E4M3FN ? 64 : 32;
+    const int64_t rs = s.R * s.S;
+    if (s.F < 1 || rs < 2 || s.F * rs > 32 || s.C < 1 || (s.C * E) % ksb != 0) return false;
+    const int64_t ks = s.C * E / ksb;
+    if (ks != 1 && ks != 2 && ks != 4 && ks != 8 && ks != 16) return false;
+    if (s.H * s.W * s.C * E >= ((int64_t)1 << 31)) return false;
+    const int64_t ppitch = s.C * E;   // unpadded, swizzled staging
+    const int64_t spitch = 33;
+    const int64_t nk_bytes = s.F * s.kpitch * E;
+    const int64_t ring_off = 256;   // past the coefficients; the NK rows are staged in the ring
+    double best = 1e300;
+    bool found = false;
+    for (int64_t blocks = 1; blocks <= 4; ++blocks) {
+        int64_t tw = (32 * blocks - s.S) / s.st + 1;
+        if (tw < 1) continue;
+        if (tw > s.Wo) tw = s.Wo;
+        const int64_t pw = (tw - 1) * s.st + s.S;
+        const int64_t prow = (pw * ppitch + 1023) / 1024 * 1024;
+        const int64_t pslot = (pw * spitch * 4 + 15) / 16 * 16;
+        const int64_t fixed = ring_off + (s.R + 1) * pslot;
+        // two slots (one row in flight per workgroup): small workgroups, so
+        // several share a CU and one's row work overlaps another's waits
+        // (measured on the RGB layer: 29.0 us at two per CU with four slots,
+        // 24.4 us at three per CU with three slots)
+        int64_t nslot = 2;
+        if (fixed + nslot * prow > kLdsBytes || nk_bytes > nslot * prow) continue;
+        const int64_t strips = (s.Wo + tw - 1) / tw;
+        const int64_t per = s.N * strips;
+        const int64_t per_cu = kLdsBytes / (fixed + nslot * prow);   // workgroups per CU
+        for (int64_t want : {(int64_t)kNumCUs * per_cu, (int64_t)kNumCUs * per_cu * 2}) {
+            int64_t segs = want / per;
+            if (segs < 1) segs = 1;
+            if (segs > s.Ho) segs = s.Ho;
+            const int64_t th = (s.Ho + segs - 1) / segs;
+            const int64_t tiles_h = (s.Ho + th - 1) / th;
+            const int64_t ph = (th - 1) * s.st + s.R;
+            const int64_t tiles = per * tiles_h;
+            const int64_t rounds = (tiles + kNumCUs * per_cu - 1) / (kNumCUs * per_cu);
+            // fewer than four ring slots leave too few rows in flight
+            const double cost =
+                rounds * ((double)(ph * prow) / 16.0 + 2500.0 + (nslot < 4 ? 1000.0 : 400.0) * ph);
+            if (cost < best) {
+                best = cost;
+                found = true;
+                *out = BandPlan{(int)th, (int)tw, (int)ph, (int)pw, 0, (int)ring_off, (int)ppitch,
+                                (int)prow, (int)spitch, (int)(fixed + nslot * prow),
+                                (int)tiles_h, (int)strips, tiles, (int)nslot};
+            }
+        }
+    }
+    return found;
+}
+
 // The kernel a problem goes to, in order of preference.
-enum KernelKind { K_NONE, K_BAND, K_WIDE, K_RESIDENT, K_TILED };
+enum KernelKind { K_NONE, K_TAPFOLD, K_BAND, K_WIDE, K_RESIDENT, K_TILED };
 
 KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp) {
     if (s.M == 0 || s.F == 0) return K_NONE;
+    if (tapfold_plan(s, dtype, bp)) return K_TAPFOLD;
     if (band_plan(s, dtype, bp)) return K_BAND;
     if (wide_ok(s, dtype)) return K_WIDE;
     if (resident_ok(s, dtype)) return K_RESIDENT;
@@ -318,6 +389,7 @@ template <int DT>
 hipError_t launch_kind(KernelKind kind, bool resid, const ConvArgs& a, const BandPlan& bp,
                        hipStream_t stream) {
     switch (kind) {
+        case K_TAPFOLD: return launch_tapfold_any<DT>(resid, a, bp, stream);
         case K_BAND: return launch_band_any<DT>(resid, a, bp, stream);
         case K_WIDE: return launch_wide_any<DT>(resid, a, stream);
         case K_RESIDENT: return launch_resident_any<DT>(resid, a, stream);
@@ -874,6 +946,7 @@ const char* conv2d_fwd_kernel_name(const int64_t in_nhwc[4], int32_t filter_is_f
     BandPlan bp;
     switch (select_kernel(s, dtype, &bp)) {
         case K_NONE: return "none";
+        case K_TAPFOLD: return "igemm_fwd_tapfold_kernel";
         case K_BAND: return "igemm_fwd_band_kernel";
         case K_WIDE: return "igemm_fwd_wide_kernel";
         case K_RESIDENT: return "igemm_fwd_resident_kernel";

@@ -49,6 +49,7 @@ inline int log2_exact(int64_t v) {
 struct BandPlan {
     int TH, TW, PH, PW, TN, fpitch, ppitch, prow, spitch, lds, tiles_h, tiles_w;
     int64_t tiles;
+    int groups;   // tap-fold kernel: input rows in the LDS ring
 };
 
 // Launchers of each kernel family, per element type DT (DT_BF16, DT_FP16 or
@@ -56,6 +57,9 @@ struct BandPlan {
 // enqueue one launch on the stream.
 template <int DT>
 hipError_t launch_band_any(bool resid, const ConvArgs& a, const BandPlan& bp, hipStream_t stream);
+template <int DT>
+hipError_t launch_tapfold_any(bool resid, const ConvArgs& a, const BandPlan& bp,
+                              hipStream_t stream);
 template <int DT>
 hipError_t launch_wide_any(bool resid, const ConvArgs& a, hipStream_t stream);
 template <int DT>

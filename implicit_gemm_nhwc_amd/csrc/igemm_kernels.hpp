@@ -77,6 +77,7 @@ struct ConvArgs {
     int patch_off;         // LDS byte offset of the patch
     int spitch;            // LDS floats per staged output pixel (epilogue)
     int cpp_log2;          // log2(16-byte chunks per input pixel)
+    int nslot;             // tap-fold kernel: input rows in the LDS ring
 };
 
 // Workgroup b is placed on XCD b % 8 by the hardware's round-robin
@@ -756,6 +757,35 @@ __device__ __forceinline__ int small_div(int n, int d, float inv_d) {
     q -= (r < 0) ? 1 : 0;
     return q;
 }
+
+#define IGC_VMCNT_CASE(n) \
+    case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
+
+// s_waitcnt vmcnt(n) for a wave-uniform n known only at run time: a scalar
+// jump over the counter's 64 immediate forms.  n is clamped to [0, 63]; at
+// most 63 requests are ever counted, so a larger n means no wait.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+    switch (n < 0 ? 0 : (n > 63 ? 63 : n)) {
+        IGC_VMCNT_CASE(0) IGC_VMCNT_CASE(1) IGC_VMCNT_CASE(2) IGC_VMCNT_CASE(3)
+        IGC_VMCNT_CASE(4) IGC_VMCNT_CASE(5) IGC_VMCNT_CASE(6) IGC_VMCNT_CASE(7)
+        IGC_VMCNT_CASE(8) IGC_VMCNT_CASE(9) IGC_VMCNT_CASE(10) IGC_VMCNT_CASE(11)
+        IGC_VMCNT_CASE(12) IGC_VMCNT_CASE(13) IGC_VMCNT_CASE(14) IGC_VMCNT_CASE(15)
+        IGC_VMCNT_CASE(16) IGC_VMCNT_CASE(17) IGC_VMCNT_CASE(18) IGC_VMCNT_CASE(19)
+        IGC_VMCNT_CASE(20) IGC_VMCNT_CASE(21) IGC_VMCNT_CASE(22) IGC_VMCNT_CASE(23)
+        IGC_VMCNT_CASE(24) IGC_VMCNT_CASE(25) IGC_VMCNT_CASE(26) IGC_VMCNT_CASE(27)
+        IGC_VMCNT_CASE(28) IGC_VMCNT_CASE(29) IGC_VMCNT_CASE(30) IGC_VMCNT_CASE(31)
+        IGC_VMCNT_CASE(32) IGC_VMCNT_CASE(33) IGC_VMCNT_CASE(34) IGC_VMCNT_CASE(35)
+        IGC_VMCNT_CASE(36) IGC_VMCNT_CASE(37) IGC_VMCNT_CASE(38) IGC_VMCNT_CASE(39)
+        IGC_VMCNT_CASE(40) IGC_VMCNT_CASE(41) IGC_VMCNT_CASE(42) IGC_VMCNT_CASE(43)
+        IGC_VMCNT_CASE(44) IGC_VMCNT_CASE(45) IGC_VMCNT_CASE(46) IGC_VMCNT_CASE(47)
+        IGC_VMCNT_CASE(48) IGC_VMCNT_CASE(49) IGC_VMCNT_CASE(50) IGC_VMCNT_CASE(51)
+        IGC_VMCNT_CASE(52) IGC_VMCNT_CASE(53) IGC_VMCNT_CASE(54) IGC_VMCNT_CASE(55)
+        IGC_VMCNT_CASE(56) IGC_VMCNT_CASE(57) IGC_VMCNT_CASE(58) IGC_VMCNT_CASE(59)
+        IGC_VMCNT_CASE(60) IGC_VMCNT_CASE(61) IGC_VMCNT_CASE(62)
+        default: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
+    }
+}
+#undef IGC_VMCNT_CASE
 
 template <int V>
 struct IntC { static constexpr int value = V; };

@@ -181,7 +181,7 @@ def test_kernel_selection():
             "resnet_3x3_64c_n32": "igemm_fwd_band_kernel",
             "strided_3x3_s2_128to256_n32": "igemm_fwd_wide_kernel",
             "fp8_5x5_256c_residual_n16": "igemm_fwd_wide_kernel",
-            "rgb_3x3_128to3_512px": "igemm_fwd_band_kernel"}
+            "rgb_3x3_128to3_512px": "igemm_fwd_tapfold_kernel"}
     dts = {"bfloat16": torch.bfloat16, "float16": torch.float16,
            "float8_e4m3fn": torch.float8_e4m3fn}
     for name, spec in datagen.WORKLOADS.items():

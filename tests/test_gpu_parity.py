@@ -154,6 +154,16 @@ PATH_CASES = [
     ("band_lds_epilogue", "bfloat16", 2, 20, 20, 64, 20, 3, 3, 1, 1, True, "band"),
     # one accumulator block per wave: the epilogue reads the last MFMA first
     ("band_fp8_single_block", "float8_e4m3fn", 1, 8, 8, 64, 16, 3, 3, 1, 1, False, "band"),
+    # tap-fold kernel: C_out * R * S <= 32 (3x3 up to 3 channels, 5x5 one,
+    # 1x3 eight), strides 1 and 2, paddings 0..2, several strips and row
+    # segments, partial last strip and segment
+    ("tapfold_bf16_rgb", "bfloat16", 2, 40, 70, 128, 3, 3, 3, 1, 1, False, "tapfold"),
+    ("tapfold_fp16_s2_resid", "float16", 2, 33, 41, 64, 2, 3, 3, 2, 1, True, "tapfold"),
+    ("tapfold_fp8_p0", "float8_e4m3fn", 1, 30, 50, 64, 3, 3, 3, 1, 0, False, "tapfold"),
+    ("tapfold_bf16_5x5_f1", "bfloat16", 2, 20, 20, 32, 1, 5, 5, 1, 2, True, "tapfold"),
+    ("tapfold_bf16_1x3_f8", "bfloat16", 1, 17, 300, 32, 8, 1, 3, 1, 0, False, "tapfold"),
+    ("tapfold_fp8_s2_p2_resid", "float8_e4m3fn", 2, 19, 23, 128, 3, 3, 3, 2, 2, True, "tapfold"),
+    ("tapfold_fp16_c256", "float16", 1, 9, 9, 256, 1, 3, 3, 1, 1, False, "tapfold"),
     ("resident_c48", "bfloat16", 2, 20, 20, 48, 32, 3, 3, 1, 1, False, "resident"),
     ("resident_fp16_c48", "float16", 2, 10, 10, 48, 24, 3, 3, 1, 1, True, "resident"),
     ("resident_fp8_single", "float8_e4m3fn", 1, 4, 4, 48, 16, 3, 3, 1, 1, True, "resident"),
@@ -165,6 +175,7 @@ PATH_CASES = [
     ("wide256_fp8_resid", "float8_e4m3fn", 16, 64, 64, 64, 256, 3, 3, 1, 1, True, "wide"),
 ]
 _KERNEL = {"wide": "igemm_fwd_wide_kernel", "band": "igemm_fwd_band_kernel",
+           "tapfold": "igemm_fwd_tapfold_kernel",
            "resident": "igemm_fwd_resident_kernel", "tiled": "igemm_fwd_kernel"}
 
 
