@@ -19,6 +19,15 @@ Parity status of each function (what pins it is in tests/test_oracle_pins.py):
                           conv2d with no epilogue, bias as an extra
                           constant-one input channel, scale folded into the
                           filter, textbook sigmoid values, relu's sign split.
+  conv2d_general         pinned: hand-worked golden values
+                          (tests/golden/general_cases.txt), pure-Python
+                          brute force with dilation, groups, per-axis
+                          strides and asymmetric padding, torch conv2d in
+                          fp64, reduction to conv2d, groups as the
+                          concatenation of per-group convolutions,
+                          dilation as a zero-inserted filter, asymmetric
+                          padding as an explicitly padded input, stride as
+                          subsampling of stride 1.
   filter_to_nk           pinned: element-wise brute force from the index
                           formula on small filters.
   conv2d_transposed      pinned: hand-worked golden values
@@ -39,6 +48,7 @@ from .reference import (  # noqa: F401
     conv2d,
     conv2d_epilogue,
     conv2d_epilogue_points,
+    conv2d_general,
     conv2d_points,
     conv2d_transposed,
     filter_dims_rscf,
@@ -47,4 +57,5 @@ from .reference import (  # noqa: F401
     im2col,
     num_threads,
     out_size,
+    out_size_general,
 )

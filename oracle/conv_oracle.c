@@ -145,3 +145,79 @@ int oracle_conv2d_points_f64(const double* x, int64_t N, int64_t H, int64_t W,
     }
     return 0;
 }
+
+/*
+ * The general forward convolution: per-axis stride (sh, sw), dilation
+ * (dh, dw), padding before (pt, pl) and after (pb, pr) each spatial axis,
+ * and `groups` channel groups.  The parameters are the ones page
+ * "dispatch_amd_4wave_conv2d" (Args: stride, dilation, symmetric_padding,
+ * num_groups) lists and its dispatcher restricts; their meaning is the
+ * standard one (this oracle's reading, as in every deep-learning framework):
+ *
+ *   y[n,oh,ow,co] = sum_{r<R} sum_{s<S} sum_{c<Cg}
+ *                     X(n, oh*sh - pt + r*dh, ow*sw - pl + s*dw, g*Cg + c)
+ *                     * Wt(r, s, c, co),     g = co / (F / groups)
+ *
+ *   Cg = C / groups input channels per group (the filter's C_in), F output
+ *   channels in all, F / groups per group; X as in oracle_conv2d_f64 (zero
+ *   outside the image); Wt(r,s,c,co) = w[((r*S + s)*Cg + c)*F + co] (RSCF)
+ *   or w[((co*Cg + c)*R + r)*S + s] (FCRS);
+ *   Ho = floor((H + pt + pb - dh*(R - 1) - 1) / sh) + 1, likewise Wo.
+ *
+ * With pt = pb = ph, pl = pr = pw, unit dilation and one group this is
+ * exactly oracle_conv2d_f64.  Each element is one straight (r, s, c) loop
+ * accumulating in double; OpenMP over (n, oh) rows only.
+ * Returns 0, or -1 for arguments that describe no convolution.
+ */
+int64_t oracle_out_size_general(int64_t in, int64_t k, int64_t stride, int64_t dil,
+                                int64_t pad_before, int64_t pad_after) {
+    if (stride <= 0 || dil <= 0 || k <= 0) return -1;
+    const int64_t span = in + pad_before + pad_after - dil * (k - 1) - 1;
+    if (span < 0) return 0;
+    return span / stride + 1;
+}
+
+int oracle_conv2d_general_f64(const double* x, int64_t N, int64_t H, int64_t W,
+                              int64_t C, const double* w, int fcrs, int64_t R,
+                              int64_t S, int64_t Cg, int64_t F, int64_t sh,
+                              int64_t sw, int64_t dh, int64_t dw, int64_t pt,
+                              int64_t pb, int64_t pl, int64_t pr, int64_t groups,
+                              const double* src, double beta, double* y,
+                              int64_t Ho, int64_t Wo) {
+    if (N < 0 || H < 0 || W < 0 || C < 0 || R <= 0 || S <= 0 || F < 0 ||
+        pt < 0 || pb < 0 || pl < 0 || pr < 0 || groups <= 0)
+        return -1;
+    if (C != Cg * groups || F % groups != 0) return -1;
+    if (Ho != oracle_out_size_general(H, R, sh, dh, pt, pb) ||
+        Wo != oracle_out_size_general(W, S, sw, dw, pl, pr))
+        return -1;
+    const int64_t Fg = groups ? F / groups : 0;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t oh = 0; oh < Ho; ++oh) {
+            for (int64_t ow = 0; ow < Wo; ++ow) {
+                for (int64_t co = 0; co < F; ++co) {
+                    const int64_t g = co / Fg;
+                    double acc = 0.0;
+                    for (int64_t r = 0; r < R; ++r) {
+                        const int64_t ih = oh * sh - pt + r * dh;
+                        for (int64_t s = 0; s < S; ++s) {
+                            const int64_t iw = ow * sw - pl + s * dw;
+                            for (int64_t c = 0; c < Cg; ++c) {
+                                double xv = 0.0;
+                                if (ih >= 0 && ih < H && iw >= 0 && iw < W)
+                                    xv = x[((n * H + ih) * W + iw) * C + g * Cg + c];
+                                acc += xv * filter_tap(w, fcrs, R, S, Cg, F, r, s, c, co);
+                            }
+                        }
+                    }
+                    const int64_t o = ((n * Ho + oh) * Wo + ow) * F + co;
+                    if (src) acc = acc + beta * src[o];
+                    y[o] = acc;
+                }
+            }
+        }
+    }
+    return 0;
+}
+

@@ -42,6 +42,12 @@ def _lib():
         lib.oracle_conv2d_points_f64.restype = ctypes.c_int
         lib.oracle_out_size.argtypes = [i64, i64, i64, i64]
         lib.oracle_out_size.restype = i64
+        lib.oracle_out_size_general.argtypes = [i64, i64, i64, i64, i64, i64]
+        lib.oracle_out_size_general.restype = i64
+        lib.oracle_conv2d_general_f64.argtypes = [
+            dp, i64, i64, i64, i64, dp, ip, i64, i64, i64, i64, i64, i64, i64, i64,
+            i64, i64, i64, i64, i64, dp, ctypes.c_double, dp, i64, i64]
+        lib.oracle_conv2d_general_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _LIB = lib
@@ -320,3 +326,48 @@ def gate_accepts(dtype: str, filter_dtype: str, out_dtype: str, in_nhwc,
     if ho < 1 or wo < 1:
         return False
     return tuple(out_nhwc) == (n, ho, wo, f)
+
+
+def _pair2(v):
+    return (int(v), int(v)) if isinstance(v, (int, np.integer)) else (int(v[0]), int(v[1]))
+
+
+def out_size_general(n_in: int, k: int, stride: int, dilation: int, pad_before: int,
+                     pad_after: int) -> int:
+    """floor((n + pad_before + pad_after - dilation*(k - 1) - 1) / stride) + 1,
+    or 0 when the padded input is shorter than the dilated filter."""
+    return int(_lib().oracle_out_size_general(n_in, k, stride, dilation, pad_before,
+                                              pad_after))
+
+
+def conv2d_general(x, w, *, filter_is_fcrs: bool, stride=1, dilation=1, pad_begin=0,
+                   pad_end=0, groups: int = 1, source=None, beta: float = 0.0, scale=None,
+                   bias=None, act: str = "none") -> np.ndarray:
+    """The forward convolution with the parameters page 1
+    ("dispatch_amd_4wave_conv2d", Args: stride, dilation, symmetric_padding,
+    num_groups) names and its dispatcher restricts, in their standard
+    meaning: per-axis stride [sh, sw] and dilation [dh, dw], padding
+    pad_begin = [top, left] and pad_end = [bottom, right], and `groups`
+    channel groups (output channel co reads input channels
+    g*Cg .. g*Cg + Cg - 1, g = co // (C_out / groups), Cg = C_in / groups,
+    the filter's C_in being Cg).  Then the fused-epilogue family of
+    conv2d_epilogue.  fp64; returns [N, Ho, Wo, C_out]."""
+    sh, sw = _pair2(stride)
+    dh, dw = _pair2(dilation)
+    pt, pl = _pair2(pad_begin)
+    pb, pr = _pair2(pad_end)
+    x64, w64 = _f64(x), _f64(w)
+    n, h, wd, c = x64.shape
+    r, s, cg, f = filter_dims_rscf(w64.shape, filter_is_fcrs)
+    if groups < 1 or cg * groups != c or f % groups:
+        raise ValueError("channels do not split into the groups")
+    ho = out_size_general(h, r, sh, dh, pt, pb)
+    wo = out_size_general(wd, s, sw, dw, pl, pr)
+    y = np.zeros((n, max(ho, 0), max(wo, 0), f), dtype=np.float64)
+    rc = _lib().oracle_conv2d_general_f64(
+        _ptr(x64), n, h, wd, c, _ptr(w64), int(bool(filter_is_fcrs)), r, s, cg, f,
+        sh, sw, dh, dw, pt, pb, pl, pr, int(groups), None, 0.0, _ptr(y), ho, wo)
+    if rc != 0:
+        raise ValueError("oracle rejected the convolution arguments")
+    src64 = None if source is None else _f64(source)
+    return _epilogue(y, src64, beta, scale, bias, act)

@@ -583,3 +583,147 @@ def test_transposed_is_adjoint_of_conv2d(h, w, r, st, p):
     assert at.shape == a.shape
     lhs, rhs = float(np.sum(y * b)), float(np.sum(a * at))
     assert abs(lhs - rhs) <= 1e-12 * max(abs(lhs), 1.0) * a.size
+
+
+# ------------------------------------------------- general convolution
+def _read_general():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "general_cases.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tag, *vals = line.split()
+            if tag == "case":
+                cur = dict(name=vals[0], dims=[int(v) for v in vals[1:17]],
+                           beta=float(vals[17]))
+                cases.append(cur)
+            elif vals == ["none"]:
+                cur[tag] = None
+            else:
+                cur[tag] = np.array([float(v) for v in vals])
+    return cases
+
+
+@pytest.mark.parametrize("case", _read_general(), ids=lambda c: c["name"])
+def test_general_handworked(case):
+    n, h, w, c, r, s, f, sh, sw, dh, dw, pt, pl, pb, pr, g = case["dims"]
+    x = case["x"].reshape(n, h, w, c)
+    wt = case["w"].reshape(r, s, c // g, f)
+    ho = oracle.out_size_general(h, r, sh, dh, pt, pb)
+    wo = oracle.out_size_general(w, s, sw, dw, pl, pr)
+    src = None if case["src"] is None else case["src"].reshape(n, ho, wo, f)
+    kw = dict(stride=(sh, sw), dilation=(dh, dw), pad_begin=(pt, pl), pad_end=(pb, pr),
+              groups=g, source=src, beta=case["beta"])
+    y = oracle.conv2d_general(x, wt, filter_is_fcrs=False, **kw)
+    np.testing.assert_array_equal(y.reshape(-1), case["y"])
+    y2 = oracle.conv2d_general(x, wt.transpose(3, 2, 0, 1).copy(), filter_is_fcrs=True, **kw)
+    np.testing.assert_array_equal(y2, y)
+
+
+def _brute_general(x, w, st, dil, pb_, pe_, groups):
+    """Pure-Python general convolution over an explicitly (asymmetrically)
+    zero-padded copy, RSCF filter [R, S, Cg, F], each sum by math.fsum."""
+    (sh, sw), (dh, dw), (pt, pl), (pb, pr) = st, dil, pb_, pe_
+    n_, h, wd, c = x.shape
+    r_, s_, cg, f = w.shape
+    fg = f // groups
+    xp = np.zeros((n_, h + pt + pb, wd + pl + pr, c))
+    xp[:, pt:pt + h, pl:pl + wd, :] = x
+    ho = (h + pt + pb - dh * (r_ - 1) - 1) // sh + 1
+    wo = (wd + pl + pr - dw * (s_ - 1) - 1) // sw + 1
+    y = np.zeros((n_, ho, wo, f))
+    for n, oh, ow, co in itertools.product(range(n_), range(ho), range(wo), range(f)):
+        g = co // fg
+        y[n, oh, ow, co] = math.fsum(
+            xp[n, oh * sh + rr * dh, ow * sw + ss * dw, g * cg + ci] * w[rr, ss, ci, co]
+            for rr in range(r_) for ss in range(s_) for ci in range(cg))
+    return y
+
+
+GENERAL_CASES = [
+    # N H W C F R S (sh, sw) (dh, dw) (pt, pl) (pb, pr) groups
+    (1, 7, 8, 2, 2, 3, 3, (1, 1), (2, 2), (2, 2), (2, 2), 1),
+    (2, 9, 7, 4, 6, 3, 2, (3, 2), (1, 3), (1, 0), (2, 3), 2),
+    (1, 8, 8, 6, 3, 2, 2, (4, 4), (1, 1), (0, 0), (0, 0), 3),
+    (1, 6, 9, 4, 4, 3, 3, (2, 1), (2, 1), (0, 3), (1, 0), 4),
+    (2, 5, 5, 2, 4, 1, 3, (1, 2), (1, 2), (0, 2), (0, 2), 2),
+    (1, 10, 6, 3, 3, 2, 3, (5, 3), (3, 1), (4, 1), (0, 1), 3),
+]
+
+
+@pytest.mark.parametrize("case", GENERAL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_general_brute_force(case):
+    n, h, w, c, f, r, s, st, dil, pb_, pe_, g = case
+    x = _rand((n, h, w, c))
+    wt = _rand((r, s, c // g, f))
+    y = oracle.conv2d_general(x, wt, filter_is_fcrs=False, stride=st, dilation=dil,
+                              pad_begin=pb_, pad_end=pe_, groups=g)
+    ref = _brute_general(x, wt, st, dil, pb_, pe_, g)
+    assert y.shape == ref.shape
+    assert _rel(y, ref) < 1e-12
+
+
+@pytest.mark.parametrize("case", GENERAL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_general_matches_torch_f64(case):
+    n, h, w, c, f, r, s, st, dil, pb_, pe_, g = case
+    x = torch.from_numpy(_rand((n, h, w, c)))
+    wf = torch.from_numpy(_rand((f, c // g, r, s)))      # FCRS is torch's layout
+    y = oracle.conv2d_general(x, wf, filter_is_fcrs=True, stride=st, dilation=dil,
+                              pad_begin=pb_, pad_end=pe_, groups=g)
+    xp = torch.nn.functional.pad(x.permute(0, 3, 1, 2), (pb_[1], pe_[1], pb_[0], pe_[0]))
+    ref = torch.nn.functional.conv2d(xp, wf, stride=st, dilation=dil, groups=g)
+    np.testing.assert_allclose(y, ref.permute(0, 2, 3, 1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("st,p", [(1, 0), (1, 1), (2, 2), (2, 1)])
+def test_general_reduces_to_conv2d(st, p):
+    x, wt = _rand((2, 9, 8, 3)), _rand((3, 3, 3, 4))
+    a = oracle.conv2d_general(x, wt, filter_is_fcrs=False, stride=st, pad_begin=p, pad_end=p)
+    b = oracle.conv2d(x, wt, filter_is_fcrs=False, stride=st, padding=p)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_general_groups_are_independent_convolutions():
+    g, cg, fg = 3, 2, 2
+    x, wt = _rand((2, 7, 6, g * cg)), _rand((3, 2, cg, g * fg))
+    y = oracle.conv2d_general(x, wt, filter_is_fcrs=False, stride=(1, 2), pad_begin=(1, 0),
+                              pad_end=(1, 1), groups=g)
+    for k in range(g):
+        part = oracle.conv2d_general(x[..., k * cg:(k + 1) * cg], wt[..., k * fg:(k + 1) * fg],
+                                     filter_is_fcrs=False, stride=(1, 2), pad_begin=(1, 0),
+                                     pad_end=(1, 1))
+        np.testing.assert_array_equal(y[..., k * fg:(k + 1) * fg], part)
+
+
+def test_general_dilation_is_a_zero_inserted_filter():
+    x, wt = _rand((1, 11, 10, 2)), _rand((3, 2, 2, 3))
+    dh, dw = 3, 2
+    wz = np.zeros((dh * 2 + 1, dw * 1 + 1, 2, 3))
+    wz[::dh, ::dw] = wt
+    a = oracle.conv2d_general(x, wt, filter_is_fcrs=False, dilation=(dh, dw), pad_begin=(1, 2),
+                              pad_end=(0, 1))
+    b = oracle.conv2d_general(x, wz, filter_is_fcrs=False, pad_begin=(1, 2), pad_end=(0, 1))
+    assert a.shape == b.shape
+    assert _rel(a, b) < 1e-12
+
+
+def test_general_asymmetric_padding_is_a_padded_input():
+    x, wt = _rand((2, 6, 7, 2)), _rand((3, 3, 2, 2))
+    pt, pl, pb, pr = 2, 0, 1, 3
+    xp = np.zeros((2, 6 + pt + pb, 7 + pl + pr, 2))
+    xp[:, pt:pt + 6, pl:pl + 7] = x
+    a = oracle.conv2d_general(x, wt, filter_is_fcrs=False, stride=(2, 1),
+                              pad_begin=(pt, pl), pad_end=(pb, pr))
+    b = oracle.conv2d_general(xp, wt, filter_is_fcrs=False, stride=(2, 1))
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("sh,sw", [(3, 3), (4, 2), (5, 7)])
+def test_general_stride_subsamples_stride1(sh, sw):
+    x, wt = _rand((1, 16, 17, 2)), _rand((2, 3, 2, 2))
+    a = oracle.conv2d_general(x, wt, filter_is_fcrs=False, stride=(sh, sw), dilation=(2, 1),
+                              pad_begin=(1, 1), pad_end=(0, 2))
+    b = oracle.conv2d_general(x, wt, filter_is_fcrs=False, dilation=(2, 1), pad_begin=(1, 1),
+                              pad_end=(0, 2))
+    np.testing.assert_array_equal(a, b[:, ::sh, ::sw][:, :a.shape[1], :a.shape[2]])
