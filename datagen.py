@@ -81,12 +81,15 @@ def filter_shape(R, S, C, F, fcrs):
 
 
 def make_case(*, N, H, W, C, F, R, S, dtype, fcrs, x_dist, w_dist,
-              src_dist=None, out_hw=None, seed=0):
+              src_dist=None, out_hw=None, seed=0, filt_c=None):
     """Draws (x, w, src) as CPU tensors in their stored dtypes.  src is None
-    unless src_dist is given, in which case out_hw = (Ho, Wo) is required."""
+    unless src_dist is given, in which case out_hw = (Ho, Wo) is required.
+    filt_c: the filter's input channels when they differ from the input's
+    (a grouped convolution's per-group count)."""
     gen = torch.Generator().manual_seed(seed)
     x = _round(_draw(gen, (N, H, W, C), x_dist), dtype)
-    w = _round(_draw(gen, filter_shape(R, S, C, F, fcrs), w_dist), dtype)
+    w = _round(_draw(gen, filter_shape(R, S, C if filt_c is None else filt_c, F, fcrs), w_dist),
+               dtype)
     src = None
     if src_dist is not None:
         ho, wo = out_hw

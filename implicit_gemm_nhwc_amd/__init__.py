@@ -53,6 +53,13 @@ class IgcEpilogue(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("activation", ctypes.c_int32)]
 
+class IgcConvParams(ctypes.Structure):
+    """igc_conv_params of include/igemm_conv.h."""
+    _fields_ = [("stride", ctypes.c_int32 * 2), ("dilation", ctypes.c_int32 * 2),
+                ("pad_begin", ctypes.c_int32 * 2), ("pad_end", ctypes.c_int32 * 2),
+                ("groups", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -118,6 +125,16 @@ def lib():
     L.conv2d_transposed_check.restype = i32
     L.conv2d_transposed_workspace_bytes.argtypes = [i64p, i64p, i32p, i32p, i32, i32]
     L.conv2d_transposed_workspace_bytes.restype = sz
+    prm = ctypes.POINTER(IgcConvParams)
+    gen_head = [vp, i64p, vp, i32, i64p, vp, i64p, prm, i32, vp, f32, epip]
+    L.conv2d_fwd_general.argtypes = gen_head + [vp, sz, vp]
+    L.conv2d_fwd_general.restype = i32
+    L.conv2d_fwd_general_check.argtypes = gen_head + [vp, sz]
+    L.conv2d_fwd_general_check.restype = i32
+    L.conv2d_fwd_general_query.argtypes = [i64p, i32, i64p, i64p, prm, i32]
+    L.conv2d_fwd_general_query.restype = i32
+    L.conv2d_fwd_general_kernel_name.argtypes = [i64p, i32, i64p, i64p, prm, i32]
+    L.conv2d_fwd_general_kernel_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -620,4 +637,116 @@ def conv2d(input, filter, *, filter_is_fcrs, stride=1, padding=0, source=None, b
         raise Declined(f"conv2d_fwd declined: {REASONS.get(reason, reason)}")
     if rc < 0:
         raise RuntimeError(f"conv2d_fwd failed with HIP error {-rc}")
+    return out
+
+
+# ------------------------------------------------ general convolution
+def conv_params(*, stride=1, dilation=1, pad_begin=0, pad_end=None, groups=1):
+    """An IgcConvParams; each of stride, dilation, pad_begin (top, left) and
+    pad_end (bottom, right; None = pad_begin) is an int or a pair."""
+    def two(v):
+        return (int(v), int(v)) if isinstance(v, int) else (int(v[0]), int(v[1]))
+    pe = pad_begin if pad_end is None else pad_end
+    return IgcConvParams((ctypes.c_int32 * 2)(*two(stride)), (ctypes.c_int32 * 2)(*two(dilation)),
+                         (ctypes.c_int32 * 2)(*two(pad_begin)), (ctypes.c_int32 * 2)(*two(pe)),
+                         int(groups))
+
+
+def out_hw_general(h, w, r, s, params):
+    """Ho, Wo of the general convolution (floor rounding; 0 when empty)."""
+    def one(n, k, st, d, a, b):
+        span = n + a + b - d * (k - 1) - 1
+        return 0 if span < 0 else span // st + 1
+    return (one(h, r, params.stride[0], params.dilation[0], params.pad_begin[0],
+                params.pad_end[0]),
+            one(w, s, params.stride[1], params.dilation[1], params.pad_begin[1],
+                params.pad_end[1]))
+
+
+def _gen_head(input, filter, filter_is_fcrs, output, params, dtype, source, beta, scale, bias,
+              activation, in_shape, filt_shape, out_shape, *, launch=False, workspace=None,
+              workspace_bytes=0):
+    in_shape = input.shape if in_shape is None else in_shape
+    filt_shape = filter.shape if filt_shape is None else filt_shape
+    out_shape = output.shape if out_shape is None else out_shape
+    if launch:
+        _check_fwd(input, filter, output, source, dtype, in_shape, filt_shape, out_shape,
+                   filter_is_fcrs, scale=scale, bias=bias, workspace=workspace,
+                   workspace_bytes=workspace_bytes)
+    if dtype is None:
+        dtype = dtype_code(input.dtype)
+    return [_ptr(input), _i64(in_shape), _ptr(filter), int(bool(filter_is_fcrs)),
+            _i64(filt_shape), _ptr(output), _i64(out_shape), ctypes.byref(params), int(dtype),
+            _ptr(source), float(beta), _epi_ref(make_epilogue(scale, bias, activation))]
+
+
+def conv2d_fwd_general_query(in_shape, filt_shape, out_shape, params, *, filter_is_fcrs,
+                             dtype) -> int:
+    """Pointer-free gate of the general convolution: 0 or a decline code."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return lib().conv2d_fwd_general_query(_i64(in_shape), int(bool(filter_is_fcrs)),
+                                          _i64(filt_shape), _i64(out_shape),
+                                          ctypes.byref(params), int(code))
+
+
+def conv2d_fwd_general_kernel_name(in_shape, filt_shape, out_shape, params, *, filter_is_fcrs,
+                                   dtype):
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    name = lib().conv2d_fwd_general_kernel_name(_i64(in_shape), int(bool(filter_is_fcrs)),
+                                                _i64(filt_shape), _i64(out_shape),
+                                                ctypes.byref(params), int(code))
+    return None if name is None else name.decode()
+
+
+def conv2d_fwd_general_check(input, filter, output, params, *, filter_is_fcrs, source=None,
+                             beta=0.0, scale=None, bias=None, activation=None, workspace=None,
+                             workspace_bytes=0, dtype=None, in_shape=None, filt_shape=None,
+                             out_shape=None) -> int:
+    """Host-only gate of conv2d_fwd_general: 0 or a decline code."""
+    head = _gen_head(input, filter, filter_is_fcrs, output, params, dtype, source, beta, scale,
+                     bias, activation, in_shape, filt_shape, out_shape)
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return lib().conv2d_fwd_general_check(*head, _ptr(workspace), int(workspace_bytes))
+
+
+def conv2d_fwd_general(input, filter, output, params, *, filter_is_fcrs, source=None, beta=0.0,
+                       scale=None, bias=None, activation=None, workspace=None,
+                       workspace_bytes=0, stream=None, dtype=None, in_shape=None,
+                       filt_shape=None, out_shape=None) -> int:
+    """Enqueue the general forward convolution.  1 handled, 0 declined, < 0
+    HIP error."""
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    head = _gen_head(input, filter, filter_is_fcrs, output, params, dtype, source, beta, scale,
+                     bias, activation, in_shape, filt_shape, out_shape, launch=True,
+                     workspace=workspace, workspace_bytes=workspace_bytes)
+    return lib().conv2d_fwd_general(*head, _ptr(workspace), int(workspace_bytes),
+                                    _stream(stream, output))
+
+
+def conv2d_general(input, filter, *, filter_is_fcrs, stride=1, dilation=1, pad_begin=0,
+                   pad_end=None, groups=1, source=None, beta=0.0, scale=None, bias=None,
+                   activation=None, stream=None):
+    """Allocate the NHWC output and run conv2d_fwd_general into it."""
+    params = conv_params(stride=stride, dilation=dilation, pad_begin=pad_begin,
+                         pad_end=pad_end, groups=groups)
+    if filter_is_fcrs:
+        f, _, r, s = filter.shape
+    else:
+        r, s, _, f = filter.shape
+    n, h, w, _ = input.shape
+    ho, wo = out_hw_general(h, w, r, s, params)
+    out = torch.empty((n, ho, wo, f), dtype=OUT_DTYPES.get(input.dtype, input.dtype),
+                      device=input.device)
+    ws = torch.empty(max(conv2d_workspace_bytes(filter.shape, filter_is_fcrs, input.dtype), 16),
+                     dtype=torch.uint8, device=input.device)
+    kw = dict(filter_is_fcrs=filter_is_fcrs, source=source, beta=beta, scale=scale, bias=bias,
+              activation=activation, workspace=ws)
+    rc = conv2d_fwd_general(input, filter, out, params, stream=stream, **kw)
+    if rc == 0:
+        reason = conv2d_fwd_general_check(input, filter, out, params, **kw)
+        raise Declined(f"conv2d_fwd_general declined: {REASONS.get(reason, reason)}")
+    if rc < 0:
+        raise RuntimeError(f"conv2d_fwd_general failed with HIP error {-rc}")
     return out

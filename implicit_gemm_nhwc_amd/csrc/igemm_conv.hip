@@ -19,7 +19,7 @@ namespace {
 
 using namespace igc;
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 
 int elem_bytes(int32_t dtype) { return dtype == IGC_DTYPE_FP8_E4M3FN ? 1 : 2; }
 
@@ -106,6 +106,31 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Pointer rules of a forward call, given the byte sizes of its tensors
+// (nk_bytes: what the filter transpose writes into the workspace).
+int32_t check_pointers(const void* input, size_t in_bytes, const void* filter, size_t f_bytes,
+                       const void* output, size_t out_bytes, const void* source,
+                       const void* workspace, size_t nk_bytes, size_t workspace_bytes) {
+    if ((in_bytes && !input) || (f_bytes && !filter) || (out_bytes && !output))
+        return IGC_DECLINE_NULL_POINTER;
+    if (!aligned16(input) || !aligned16(filter) || !aligned16(output) || !aligned16(source) ||
+        !aligned16(workspace))
+        return IGC_DECLINE_ALIGNMENT;
+    if (overlaps(output, out_bytes, input, in_bytes) || overlaps(output, out_bytes, filter, f_bytes))
+        return IGC_DECLINE_OVERLAP;
+    if (workspace && overlaps(output, out_bytes, workspace, nk_bytes)) return IGC_DECLINE_OVERLAP;
+    // the NK transpose writes the workspace before the GEMM reads the
+    // input, the filter and the residual source
+    if (workspace && (overlaps(workspace, nk_bytes, input, in_bytes) ||
+                      overlaps(workspace, nk_bytes, filter, f_bytes) ||
+                      (source && overlaps(workspace, nk_bytes, source, out_bytes))))
+        return IGC_DECLINE_OVERLAP;
+    if (source && source != output && overlaps(source, out_bytes, output, out_bytes))
+        return IGC_DECLINE_OVERLAP;
+    if (workspace && workspace_bytes < nk_bytes) return IGC_DECLINE_WORKSPACE;
+    return IGC_OK;
+}
+
 // Full gate: shapes plus pointers.  filter may be the NK matrix (nk_bytes
 // then gives its size); workspace is NULL for conv2d_fwd_nk.
 int32_t check_all(const void* input, const int64_t in_nhwc[4], const void* filter,
@@ -124,23 +149,9 @@ int32_t check_all(const void* input, const int64_t in_nhwc[4], const void* filte
                                                  : (size_t)(s.R * s.S * s.C * s.F) * eb;
     const size_t out_bytes = (size_t)(s.M * s.F) * 2;
     const size_t nk_bytes = (size_t)(s.F * s.kpitch) * eb;
-    if ((in_bytes && !input) || (f_bytes && !filter) || (out_bytes && !output))
-        return IGC_DECLINE_NULL_POINTER;
-    if (!aligned16(input) || !aligned16(filter) || !aligned16(output) || !aligned16(source) ||
-        !aligned16(workspace))
-        return IGC_DECLINE_ALIGNMENT;
-    if (overlaps(output, out_bytes, input, in_bytes) || overlaps(output, out_bytes, filter, f_bytes))
-        return IGC_DECLINE_OVERLAP;
-    if (workspace && overlaps(output, out_bytes, workspace, nk_bytes)) return IGC_DECLINE_OVERLAP;
-    // the NK transpose writes the workspace before the GEMM reads the
-    // input, the filter and the residual source
-    if (workspace && (overlaps(workspace, nk_bytes, input, in_bytes) ||
-                      overlaps(workspace, nk_bytes, filter, f_bytes) ||
-                      (source && overlaps(workspace, nk_bytes, source, out_bytes))))
-        return IGC_DECLINE_OVERLAP;
-    if (source && source != output && overlaps(source, out_bytes, output, out_bytes))
-        return IGC_DECLINE_OVERLAP;
-    if (workspace && workspace_bytes < nk_bytes) return IGC_DECLINE_WORKSPACE;
+    rc = check_pointers(input, in_bytes, filter, f_bytes, output, out_bytes, source, workspace,
+                        nk_bytes, workspace_bytes);
+    if (rc != IGC_OK) return rc;
     if (out_shape) *out_shape = s;
     return IGC_OK;
 }
@@ -397,16 +408,12 @@ hipError_t launch_kind(KernelKind kind, bool resid, const ConvArgs& a, const Ban
     }
 }
 
-hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
-                        float beta, const igc_epilogue* epi, const Shape& s, int32_t dtype,
-                        hipStream_t stream, const Group* grp = nullptr) {
+// The kernel arguments every family reads, for problem s (one group's
+// shape); the tiled kernel's general geometry is set to the page form
+// (square stride, symmetric padding, unit dilation, dense pixels).
+ConvArgs base_args(const void* input, const void* nk, void* output, const void* source,
+                   float beta, const igc_epilogue* epi, const Shape& s, int32_t dtype) {
     ConvArgs a{};
-    if (grp && grp->n > 1) {
-        a.groups = grp->n;
-        a.g_nk = grp->nk;
-        a.g_y = grp->y;
-        a.g_src = grp->src;
-    }
     a.x = (const uint8_t*)input;
     a.nk = (const uint8_t*)nk;
     a.y = (uint16_t*)output;
@@ -423,6 +430,24 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
     a.R = (int)s.R; a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
     a.K = (int)s.K; a.kpitch = (int)s.kpitch; a.M = (int)s.M;
     a.ktiles = (int)(s.kpad / (KT_BYTES / elem_bytes(dtype)));
+    a.sh = a.sw = s.st;
+    a.pt = a.pl = s.pad;
+    a.dh = a.dw = 1;
+    a.xpitch = (int)s.C;
+    a.ypitch = (int)s.F;
+    return a;
+}
+
+hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
+                        float beta, const igc_epilogue* epi, const Shape& s, int32_t dtype,
+                        hipStream_t stream, const Group* grp = nullptr) {
+    ConvArgs a = base_args(input, nk, output, source, beta, epi, s, dtype);
+    if (grp && grp->n > 1) {
+        a.groups = grp->n;
+        a.g_nk = grp->nk;
+        a.g_y = grp->y;
+        a.g_src = grp->src;
+    }
     const bool resid = source != nullptr;
     BandPlan bp;
     const KernelKind kind = select_kernel(s, dtype, &bp);
@@ -703,6 +728,148 @@ hipError_t run_transposed(const TPlan& t, const void* input, const void* filter,
     }
     if (e == hipSuccess) e = launch_interleave(t, ws, nullptr, output, yoffs, 0, stream);
     return e;
+}
+
+// ---- general forward convolution -----------------------------------------
+// The parameters page "dispatch_amd_4wave_conv2d" (Args) lists and its
+// dispatcher restricts, widened: per-axis stride, dilation, padding before
+// and after each axis, and channel groups.  A problem inside the page's gate
+// runs exactly as conv2d_fwd; any other runs on the tiled kernel with its
+// general geometry, the groups as one grouped launch (group g reads input
+// channels g*Cg.., NK rows, output channels, source channels and scale /
+// bias entries g*Fg..).
+struct GShape {
+    Shape s;          // C = C_in per group (Cg), F = all output channels
+    int64_t cin;      // input channels, groups * Cg
+    int32_t sh, sw, dh, dw, pt, pl, pb, pr, groups;
+    bool page;        // inside the page's gate: conv2d_fwd's kernels run it
+};
+
+int64_t out_size_general(int64_t in, int64_t k, int64_t st, int64_t dil, int64_t pb, int64_t pe) {
+    const int64_t span = in + pb + pe - dil * (k - 1) - 1;
+    return span < 0 ? 0 : span / st + 1;
+}
+
+int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_dims[4],
+                             const int64_t out_nhwc[4], const igc_conv_params* p, int32_t dtype,
+                             GShape* g) {
+    if (!in_nhwc || !filt_dims || !out_nhwc || !p) return IGC_DECLINE_NULL_POINTER;
+    if (dtype != IGC_DTYPE_BF16 && dtype != IGC_DTYPE_FP16 && dtype != IGC_DTYPE_FP8_E4M3FN)
+        return IGC_DECLINE_DTYPE;
+    if (p->stride[0] < 1 || p->stride[1] < 1) return IGC_DECLINE_STRIDE;
+    if (p->dilation[0] < 1 || p->dilation[1] < 1) return IGC_DECLINE_DILATION;
+    if (p->pad_begin[0] < 0 || p->pad_begin[1] < 0 || p->pad_end[0] < 0 || p->pad_end[1] < 0)
+        return IGC_DECLINE_PADDING;
+    if (p->groups < 1) return IGC_DECLINE_GROUPS;
+    GShape t{};
+    Shape& s = t.s;
+    s.N = in_nhwc[0]; s.H = in_nhwc[1]; s.W = in_nhwc[2];
+    t.cin = in_nhwc[3];
+    filter_rscf(filt_dims, fcrs, &s.R, &s.S, &s.C, &s.F);
+    if (s.N < 0 || s.H < 0 || s.W < 0 || t.cin < 0 || s.F < 0 || s.C < 0 || s.R < 1 || s.S < 1)
+        return IGC_DECLINE_SHAPE;
+    const int64_t lim = (int64_t)1 << 31;
+    if (s.H >= lim || s.W >= lim || s.R >= lim || s.S >= lim || s.C >= lim || s.F >= lim ||
+        t.cin >= lim)
+        return IGC_DECLINE_SIZE_LIMIT;
+    t.groups = p->groups;
+    if (s.C * t.groups != t.cin) return IGC_DECLINE_SHAPE;
+    if (s.F % t.groups != 0) return IGC_DECLINE_GROUPS;
+    t.sh = p->stride[0]; t.sw = p->stride[1];
+    t.dh = p->dilation[0]; t.dw = p->dilation[1];
+    t.pt = p->pad_begin[0]; t.pl = p->pad_begin[1];
+    t.pb = p->pad_end[0]; t.pr = p->pad_end[1];
+    s.Ho = out_size_general(s.H, s.R, t.sh, t.dh, t.pt, t.pb);
+    s.Wo = out_size_general(s.W, s.S, t.sw, t.dw, t.pl, t.pr);
+    if (s.Ho < 1 || s.Wo < 1) return IGC_DECLINE_OUTPUT_SHAPE;
+    if (out_nhwc[0] != s.N || out_nhwc[1] != s.Ho || out_nhwc[2] != s.Wo || out_nhwc[3] != s.F)
+        return IGC_DECLINE_OUTPUT_SHAPE;
+    const int64_t eb = elem_bytes(dtype);
+    if ((s.C * eb) % 16 != 0) return IGC_DECLINE_VECTOR_WIDTH;
+    // the tiled kernel's 32-bit coordinates: padded extents and dilated
+    // filter spans below 2^30 keep every tap's row and column in range
+    const int64_t l30 = (int64_t)1 << 30;
+    if (s.H + t.pt + t.pb >= l30 || s.W + t.pl + t.pr >= l30 || (int64_t)t.dh * (s.R - 1) >= l30 ||
+        (int64_t)t.dw * (s.S - 1) >= l30)
+        return IGC_DECLINE_SIZE_LIMIT;
+    if (s.Ho > lim / s.Wo) return IGC_DECLINE_SIZE_LIMIT;
+    s.M = s.N * s.Ho * s.Wo;
+    s.K = s.R * s.S * s.C;
+    if (s.M >= lim || s.K >= lim) return IGC_DECLINE_SIZE_LIMIT;
+    s.kpad = round_up(s.K, KT_BYTES / eb);
+    s.kpitch = nk_pitch(s.K, s.F, eb);
+    if (s.kpitch >= lim || s.F * s.kpitch * eb >= lim) return IGC_DECLINE_SIZE_LIMIT;
+    // the grouped launch's grid: at most (M / 128) x (C_out per group / 16)
+    // tiles per group
+    if ((s.M + 127) / 128 * ((s.F / t.groups + 15) / 16) * t.groups >= lim)
+        return IGC_DECLINE_SIZE_LIMIT;
+    t.page = t.groups == 1 && t.dh == 1 && t.dw == 1 && t.sh == t.sw && t.sh <= 2 &&
+             t.pt == t.pb && t.pt == t.pl && t.pt == t.pr && t.pt <= 2;
+    if (t.page) {
+        // the page form: conv2d_fwd's own gate, limits included
+        const int32_t st[2] = {t.sh, t.sw}, dil[2] = {1, 1}, pad[2] = {t.pt, t.pl};
+        const int32_t rc = check_shapes(in_nhwc, fcrs, filt_dims, out_nhwc, st, dil, pad, 1,
+                                        dtype, &t.s);
+        if (rc != IGC_OK) return rc;
+    }
+    if (g) *g = t;
+    return IGC_OK;
+}
+
+int32_t check_general(const void* input, const int64_t in_nhwc[4], const void* filter,
+                      int32_t fcrs, const int64_t filt_dims[4], const void* output,
+                      const int64_t out_nhwc[4], const igc_conv_params* p, int32_t dtype,
+                      const void* source, const igc_epilogue* epi, const void* workspace,
+                      size_t workspace_bytes, GShape* out) {
+    GShape g;
+    int32_t rc = check_general_shapes(in_nhwc, fcrs, filt_dims, out_nhwc, p, dtype, &g);
+    if (rc != IGC_OK) return rc;
+    const Shape& s = g.s;
+    const size_t eb = (size_t)elem_bytes(dtype);
+    const size_t in_bytes = (size_t)(s.N * s.H * s.W * g.cin) * eb;
+    const size_t f_bytes = (size_t)(s.R * s.S * s.C * s.F) * eb;
+    const size_t out_bytes = (size_t)(s.M * s.F) * 2;
+    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * eb;
+    rc = check_pointers(input, in_bytes, filter, f_bytes, output, out_bytes, source, workspace,
+                        nk_bytes, workspace_bytes);
+    if (rc != IGC_OK) return rc;
+    rc = check_epilogue(epi, output, s, workspace, nk_bytes);
+    if (rc != IGC_OK) return rc;
+    if (out) *out = g;
+    return IGC_OK;
+}
+
+// The GEMM of a general problem whose NK matrix is in nk (all groups' rows,
+// group g's Fg rows starting at row g*Fg).
+hipError_t launch_general(const void* input, const void* nk, void* output, const void* source,
+                          float beta, const igc_epilogue* epi, const GShape& g, int32_t dtype,
+                          hipStream_t stream) {
+    if (g.page) return launch_igemm(input, nk, output, source, beta, epi, g.s, dtype, stream);
+    const Shape& s = g.s;
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t fg = s.F / g.groups;
+    if (s.M == 0 || fg == 0) return hipSuccess;
+    ConvArgs a = base_args(input, nk, output, source, beta, epi, s, dtype);
+    a.F = (int)fg;
+    a.sh = g.sh; a.sw = g.sw;
+    a.pt = g.pt; a.pl = g.pl;
+    a.dh = g.dh; a.dw = g.dw;
+    a.xpitch = (int)g.cin;
+    a.ypitch = (int)s.F;
+    if (g.groups > 1) {
+        a.groups = g.groups;
+        a.g_x = s.C * eb;
+        a.g_nk = fg * s.kpitch * eb;
+        a.g_y = fg * 2;
+        a.g_src = source ? fg * 2 : 0;
+        a.g_c = (int)fg;
+    }
+    const bool resid = source != nullptr;
+    switch (dtype) {
+        case IGC_DTYPE_BF16: return launch_tiled_any<DT_BF16>(resid, a, stream);
+        case IGC_DTYPE_FP16: return launch_tiled_any<DT_FP16>(resid, a, stream);
+        default: return launch_tiled_any<DT_FP8>(resid, a, stream);
+    }
 }
 
 // ---- the allocation-free entry point's scratch ----------------------------
@@ -1076,6 +1243,78 @@ int32_t conv2d_epilogue_check(const igc_epilogue* epilogue, const void* output,
     s.M = out_nhwc[0] * out_nhwc[1] * out_nhwc[2];
     s.F = out_nhwc[3];
     return check_epilogue(epilogue, output, s);
+}
+
+const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                           const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                                           const igc_conv_params* params, int32_t dtype) {
+    GShape g;
+    if (check_general_shapes(in_nhwc, filter_is_fcrs, filt_dims, out_nhwc, params, dtype, &g) !=
+        IGC_OK)
+        return nullptr;
+    if (g.page) {
+        BandPlan bp;
+        switch (select_kernel(g.s, dtype, &bp)) {
+            case K_NONE: return "none";
+            case K_TAPFOLD: return "igemm_fwd_tapfold_kernel";
+            case K_BAND: return "igemm_fwd_band_kernel";
+            case K_WIDE: return "igemm_fwd_wide_kernel";
+            case K_RESIDENT: return "igemm_fwd_resident_kernel";
+            default: return "igemm_fwd_kernel";
+        }
+    }
+    return (g.s.M == 0 || g.s.F == 0) ? "none" : "igemm_fwd_kernel";
+}
+
+int32_t conv2d_fwd_general_query(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                 const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                                 const igc_conv_params* params, int32_t dtype) {
+    return check_general_shapes(in_nhwc, filter_is_fcrs, filt_dims, out_nhwc, params, dtype,
+                                nullptr);
+}
+
+int32_t conv2d_fwd_general_check(const void* input, const int64_t in_nhwc[4],
+                                 const void* filter, int32_t filter_is_fcrs,
+                                 const int64_t filt_dims[4], const void* output,
+                                 const int64_t out_nhwc[4], const igc_conv_params* params,
+                                 int32_t dtype, const void* source, float beta,
+                                 const igc_epilogue* epilogue, const void* workspace,
+                                 size_t workspace_bytes) {
+    (void)beta;
+    return check_general(input, in_nhwc, filter, filter_is_fcrs, filt_dims, output, out_nhwc,
+                         params, dtype, source, epilogue, workspace, workspace_bytes, nullptr);
+}
+
+int32_t conv2d_fwd_general(const void* input, const int64_t in_nhwc[4], const void* filter,
+                           int32_t filter_is_fcrs, const int64_t filt_dims[4], void* output,
+                           const int64_t out_nhwc[4], const igc_conv_params* params,
+                           int32_t dtype, const void* source, float beta,
+                           const igc_epilogue* epilogue, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    GShape g;
+    if (check_general(input, in_nhwc, filter, filter_is_fcrs, filt_dims, output, out_nhwc,
+                      params, dtype, source, epilogue, workspace, workspace_bytes,
+                      &g) != IGC_OK)
+        return 0;
+    const Shape& s = g.s;
+    if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
+    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
+    hipStream_t st = (hipStream_t)stream;
+    void* nk = workspace;
+    bool owned = false;
+    if (!nk && nk_bytes) {
+        hipError_t e = hipMallocAsync(&nk, nk_bytes, st);
+        if (e != hipSuccess) return -(int32_t)e;
+        owned = true;
+    }
+    hipError_t e = launch_transpose(filter, filter_is_fcrs, s, dtype, nk, st);
+    if (e == hipSuccess)
+        e = launch_general(input, nk, output, source, beta, epilogue, g, dtype, st);
+    if (owned) {
+        hipError_t f = hipFreeAsync(nk, st);
+        if (e == hipSuccess) e = f;
+    }
+    return hip_fail(e);
 }
 
 }  // extern "C"

@@ -78,6 +78,15 @@ struct ConvArgs {
     int spitch;            // LDS floats per staged output pixel (epilogue)
     int cpp_log2;          // log2(16-byte chunks per input pixel)
     int nslot;             // tap-fold kernel: input rows in the LDS ring
+    // general geometry, read by the tiled kernel only: per-axis stride,
+    // padding before each axis, dilation, and elements per input / output
+    // pixel (the whole tensors' C_in / C_out when a grouped launch runs the
+    // channel groups of one convolution; C and F above are one group's)
+    int sh, sw, pt, pl, dh, dw;
+    int xpitch, ypitch;
+    // grouped launch: input bytes and scale / bias entries between problems
+    int64_t g_x;
+    int g_c;
 };
 
 // Workgroup b is placed on XCD b % 8 by the hardware's round-robin
@@ -91,13 +100,17 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 }
 
 // The block index within this workgroup's problem of a grouped launch
-// (gridDim.x = groups * per), after moving the NK, output and source
-// pointers to that problem.  A launch of one problem returns blockIdx.x.
+// (gridDim.x = groups * per), after moving the input, NK, output, source
+// and scale / bias pointers to that problem.  A launch of one problem
+// returns blockIdx.x.
 __device__ __forceinline__ int group_block(ConvArgs& a, int per) {
     int b = blockIdx.x;
     if (a.groups > 1) {
         const int gi = b / per;
         b -= gi * per;
+        a.x += gi * a.g_x;
+        if (a.scale) a.scale += (int64_t)gi * a.g_c;
+        if (a.bias) a.bias += (int64_t)gi * a.g_c;
         a.nk += gi * a.g_nk;
         a.y = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.y) + gi * a.g_y);
         if (a.src)
@@ -243,6 +256,10 @@ __device__ __forceinline__ f32x4 mfma_step<DT_FP8>(const i32x4* a, const i32x4* 
 // Masks (in registers): gathered pixels outside the input (padding), pixel
 // rows m >= M and k >= K load zero; filter rows co >= C_out load zero;
 // the epilogue stores only m < M, co < C_out.
+// Geometry is general: tap (r, s) of output pixel (oh, ow) reads input pixel
+// (oh*sh - pt + r*dh, ow*sw - pl + s*dw), input pixels lie xpitch elements
+// apart and output pixels ypitch apart, so one launch per channel group (or
+// one grouped launch) covers a grouped convolution.
 template <int DT, int BCO, int BPX, int WCO, int WPX, bool RESID>
 __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
     constexpr int E = DtTraits<DT>::E;
@@ -297,9 +314,9 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
             const int rem = m - n * howo;
             const int oh = rem / a.Wo;
             const int ow = rem - oh * a.Wo;
-            pih[i] = oh * a.stride - a.pad;
-            piw[i] = ow * a.stride - a.pad;
-            pbase[i] = (((int64_t)n * a.H + pih[i]) * a.W + piw[i]) * a.C;
+            pih[i] = oh * a.sh - a.pt;
+            piw[i] = ow * a.sw - a.pl;
+            pbase[i] = (((int64_t)n * a.H + pih[i]) * a.W + piw[i]) * a.xpitch;
         } else {
             pih[i] = -(1 << 30);
             piw[i] = 0;
@@ -321,11 +338,12 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
 
     auto load_tile = [&](int kt) {
         const bool kin = kk < a.K;
-        const int64_t koff = ((int64_t)fr * a.W + fs) * a.C + ci;
+        const int tr = fr * a.dh, ts = fs * a.dw;
+        const int64_t koff = ((int64_t)tr * a.W + ts) * a.xpitch + ci;
 #pragma unroll
         for (int i = 0; i < PX_ROWS; ++i) {
-            const bool ok = kin && (unsigned)(pih[i] + fr) < (unsigned)a.H &&
-                            (unsigned)(piw[i] + fs) < (unsigned)a.W;
+            const bool ok = kin && (unsigned)(pih[i] + tr) < (unsigned)a.H &&
+                            (unsigned)(piw[i] + ts) < (unsigned)a.W;
             i32x4 v = {0, 0, 0, 0};
             if (ok) v = *reinterpret_cast<const i32x4*>(a.x + (pbase[i] + koff) * E);
             px_reg[i] = v;
@@ -433,7 +451,7 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
     for (int j = 0; j < TN; ++j) {
         const int m = m0 + wrow_px + j * 16 + frag_row;
         if (m >= a.M) continue;
-        const int64_t obase = (int64_t)m * a.F;
+        const int64_t obase = (int64_t)m * a.ypitch;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int co = co0 + wrow_co + i * 16 + frag_grp * 4;

@@ -403,6 +403,80 @@ size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t
                                          const int32_t stride[2], const int32_t padding[2],
                                          int32_t dtype, int32_t with_source);
 
+/*
+ * General forward convolution: the parameters that page
+ * "dispatch_amd_4wave_conv2d" (Args: stride, dilation, symmetric_padding,
+ * num_groups) names and its dispatcher restricts, here all accepted within
+ * the limits below.  Definition (cross-correlation, zero padding):
+ *   y[n,oh,ow,co] = sum_{r<R, s<S, c<Cg}
+ *                     x[n, oh*sh - pt + r*dh, ow*sw - pl + s*dw, g*Cg + c] * W(r, s, c, co)
+ *   g  = co / (C_out / groups),  Cg = C_in / groups
+ *   Ho = floor((H + pt + pb - dh*(R-1) - 1) / sh) + 1, likewise Wo with
+ *        (W, pl, pr, dw, S, sw)
+ * then the fused epilogue of conv2d_fwd_epilogue (scale, bias, residual
+ * source, activation; all optional; scale / bias indexed by co over all
+ * C_out channels) and one rounding.
+ *   filter     RSCF {R, S, Cg, C_out} or FCRS {C_out, Cg, R, S} (the filter's
+ *              C_in is the per-group count, as in every framework's grouped
+ *              convolution); filt_dims is that stored shape.
+ *   params     stride >= 1, dilation >= 1, padding >= 0 before (top, left)
+ *              and after (bottom, right) each axis, groups >= 1 dividing
+ *              C_in and C_out.
+ *   workspace  conv2d_workspace_bytes(filt_dims, filter_is_fcrs, dtype)
+ *              bytes (the NK matrix of all groups, group g's rows at
+ *              g*C_out/groups), or NULL for a stream-ordered allocation.
+ * A problem inside the page's gate (one group, unit dilation, stride (1,1)
+ * or (2,2), equal padding 0, 1 or 2 on every side) runs exactly as
+ * conv2d_fwd_epilogue; any other runs on the tiled implicit-GEMM kernel,
+ * all groups in one launch.  Library limits: Cg * element bytes a multiple
+ * of 16 (IGC_DECLINE_VECTOR_WIDTH); H + pt + pb, W + pl + pr, dh*(R-1) and
+ * dw*(S-1) below 2^30, and conv2d_fwd_check's size limits with Cg for C_in
+ * (IGC_DECLINE_SIZE_LIMIT).  Decline codes: STRIDE, DILATION, PADDING,
+ * GROUPS (groups < 1 or not dividing C_out), SHAPE (C_in != groups * Cg),
+ * and the pointer rules of conv2d_fwd_epilogue_check.
+ * Returns 1 = handled, 0 = declined (conv2d_fwd_general_check gives the
+ * reason), or -(hipError_t).
+ */
+typedef struct igc_conv_params {
+    int32_t stride[2];      /* {sh, sw} */
+    int32_t dilation[2];    /* {dh, dw} */
+    int32_t pad_begin[2];   /* {pt, pl}: zero rows above, columns left */
+    int32_t pad_end[2];     /* {pb, pr}: zero rows below, columns right */
+    int32_t groups;
+} igc_conv_params;
+
+int32_t conv2d_fwd_general(const void* input, const int64_t in_nhwc[4],
+                           const void* filter, int32_t filter_is_fcrs,
+                           const int64_t filt_dims[4],
+                           void* output, const int64_t out_nhwc[4],
+                           const igc_conv_params* params, int32_t dtype,
+                           const void* source, float beta,
+                           const igc_epilogue* epilogue,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only gate of conv2d_fwd_general (pointers compared, never
+ * dereferenced): IGC_OK or a decline reason. */
+int32_t conv2d_fwd_general_check(const void* input, const int64_t in_nhwc[4],
+                                 const void* filter, int32_t filter_is_fcrs,
+                                 const int64_t filt_dims[4],
+                                 const void* output, const int64_t out_nhwc[4],
+                                 const igc_conv_params* params, int32_t dtype,
+                                 const void* source, float beta,
+                                 const igc_epilogue* epilogue,
+                                 const void* workspace, size_t workspace_bytes);
+
+/* Pointer-free gate of conv2d_fwd_general's shapes and parameters. */
+int32_t conv2d_fwd_general_query(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                 const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                                 const igc_conv_params* params, int32_t dtype);
+
+/* Name of the GEMM kernel conv2d_fwd_general launches for this problem
+ * (as conv2d_fwd_kernel_name), or NULL when it would be declined. */
+const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                           const int64_t filt_dims[4],
+                                           const int64_t out_nhwc[4],
+                                           const igc_conv_params* params, int32_t dtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_reason_names():
-    assert igc.conv2d_abi_version() == 3
+    assert igc.conv2d_abi_version() == 4
     for code, name in igc.REASONS.items():
         assert igc.conv2d_reason_string(code) == name
     assert igc.conv2d_reason_string(999) == "unknown"
@@ -487,3 +487,161 @@ def test_binding_checks_tensor_properties(monkeypatch):
     with pytest.raises(igc.InvalidArgument, match="NK matrix holds"):
         igc.conv2d_fwd_nk(ok["input"], _FakeCuda((100,), torch.uint8, ptr=WS), (3, 3, 16, 8),
                           ok["output"], filter_is_fcrs=False, padding=1, stream=0)
+
+
+# ------------------------------------------------ general convolution
+GBASE = dict(in_shape=(2, 20, 21, 32), filt_shape=(3, 3, 16, 8), filter_is_fcrs=False,
+             stride=(3, 2), dilation=(2, 1), pad_begin=(1, 0), pad_end=(2, 3), groups=2,
+             dtype=0)
+
+
+def _gen(**kw):
+    """(in_shape, filt_shape, out_shape, params, fcrs, dtype) with the output
+    shape from the oracle's size rule unless given."""
+    a = {**GBASE, **kw}
+    fcrs = a["filter_is_fcrs"]
+    if fcrs:
+        f, _, r, s = a["filt_shape"]
+    else:
+        r, s, _, f = a["filt_shape"]
+    st = a["stride"] if isinstance(a["stride"], tuple) else (a["stride"],) * 2
+    dl = a["dilation"] if isinstance(a["dilation"], tuple) else (a["dilation"],) * 2
+    pb = a["pad_begin"] if isinstance(a["pad_begin"], tuple) else (a["pad_begin"],) * 2
+    pe = a["pad_end"] if isinstance(a["pad_end"], tuple) else (a["pad_end"],) * 2
+    n, h, w, _ = a["in_shape"]
+    ho = oracle.out_size_general(h, r, st[0], dl[0], pb[0], pe[0]) if min(st + dl) > 0 else 1
+    wo = oracle.out_size_general(w, s, st[1], dl[1], pb[1], pe[1]) if min(st + dl) > 0 else 1
+    out = a.get("out_shape", (n, max(ho, 0), max(wo, 0), f))
+    p = igc.conv_params(stride=st, dilation=dl, pad_begin=pb, pad_end=pe, groups=a["groups"])
+    return a["in_shape"], a["filt_shape"], out, p, fcrs, a["dtype"]
+
+
+def _gcheck(input=X, filter=W, output=Y, source=None, workspace=None, workspace_bytes=0,
+            scale=None, bias=None, activation=None, **kw):
+    i, f, o, p, fcrs, dt = _gen(**kw)
+    return igc.conv2d_fwd_general_check(input, filter, output, p, filter_is_fcrs=fcrs,
+                                        source=source, scale=scale, bias=bias,
+                                        activation=activation, workspace=workspace,
+                                        workspace_bytes=workspace_bytes, dtype=dt, in_shape=i,
+                                        filt_shape=f, out_shape=o)
+
+
+def test_general_base_case_accepted_and_kernel():
+    assert _gcheck() == 0
+    i, f, o, p, fcrs, dt = _gen()
+    assert o == (2, 7, 11, 8)      # (20+1+2-2*2-1)//3+1, (21+0+3-1*2-1)//2+1
+    assert igc.conv2d_fwd_general_query(i, f, o, p, filter_is_fcrs=fcrs, dtype=dt) == 0
+    assert igc.conv2d_fwd_general_kernel_name(i, f, o, p, filter_is_fcrs=fcrs,
+                                              dtype=dt) == "igemm_fwd_kernel"
+    assert _gcheck(source=SRC, workspace=WS, workspace_bytes=1 << 20, scale=0x60000000,
+                   bias=0x60001000, activation="silu") == 0
+    assert _gcheck(source=Y) == 0                                   # in place
+
+
+@pytest.mark.parametrize("kw", [
+    dict(stride=1, dilation=1, pad_begin=1, pad_end=1, groups=1, filt_shape=(3, 3, 32, 48)),
+    dict(stride=2, dilation=1, pad_begin=2, pad_end=2, groups=1, filt_shape=(5, 5, 32, 3)),
+    dict(stride=1, dilation=1, pad_begin=0, pad_end=0, groups=1, filt_shape=(1, 1, 32, 128)),
+])
+def test_general_page_problems_take_conv2d_fwd_kernels(kw):
+    """Inside the page's gate the general entry runs what conv2d_fwd runs."""
+    i, f, o, p, fcrs, dt = _gen(**kw)
+    st, pad = p.stride[0], p.pad_begin[0]
+    name = igc.conv2d_fwd_general_kernel_name(i, f, o, p, filter_is_fcrs=fcrs, dtype=dt)
+    assert name is not None and name == igc.conv2d_fwd_kernel_name(
+        i, f, o, filter_is_fcrs=fcrs, dtype=dt, stride=st, padding=pad)
+
+
+@pytest.mark.parametrize("kw,reason", [
+    (dict(dtype=3), "dtype"),
+    (dict(stride=(0, 1)), "stride"),
+    (dict(dilation=(1, 0)), "dilation"),
+    (dict(pad_begin=(-1, 0)), "padding"),
+    (dict(pad_end=(0, -2)), "padding"),
+    (dict(groups=0), "groups"),
+    (dict(groups=3, in_shape=(2, 20, 21, 48), filt_shape=(3, 3, 16, 8)), "groups"),
+    (dict(groups=4), "shape"),                      # 4 * 16 != 32 input channels
+    (dict(filt_shape=(0, 3, 16, 8)), "shape"),
+    (dict(in_shape=(2, 20, 21, -32)), "shape"),
+    (dict(out_shape=(2, 7, 11, 9)), "output_shape"),
+    (dict(out_shape=(2, 8, 11, 8)), "output_shape"),
+    (dict(in_shape=(1, 2, 2, 32), dilation=4, pad_begin=0, pad_end=0,
+          out_shape=(1, 0, 0, 8)), "output_shape"),
+    (dict(in_shape=(2, 20, 21, 8), filt_shape=(3, 3, 4, 8)), "vector_width"),
+    (dict(dtype=2, in_shape=(2, 20, 21, 16), filt_shape=(3, 3, 8, 8)), "vector_width"),
+    (dict(input=X + 8), "alignment"),
+    (dict(input=0), "null_pointer"),
+    (dict(output=X + 1024), "overlap"),
+    (dict(source=Y + 64), "overlap"),
+    (dict(workspace=WS, workspace_bytes=100), "workspace"),
+    (dict(workspace=X + 64, workspace_bytes=1 << 20), "overlap"),
+    (dict(activation="gelu"), "epilogue"),
+    (dict(scale=Y + 4), "epilogue"),
+    (dict(scale=WS + 64, workspace=WS, workspace_bytes=1 << 20), "epilogue"),
+])
+def test_general_decline_paths(kw, reason):
+    assert igc.REASONS[_gcheck(**kw)] == reason
+
+
+@pytest.mark.parametrize("kw,reason", [
+    (dict(dilation=(1 << 29, 1), in_shape=(1, 1 << 29, 4, 32), pad_begin=0, pad_end=0,
+          filt_shape=(1, 3, 16, 8)), "ok"),
+    (dict(dilation=(1 << 28, 1), in_shape=(1, (1 << 29) + 5, 4, 32), pad_begin=0,
+          pad_end=0, filt_shape=(3, 3, 16, 8)), "ok"),
+    (dict(dilation=(1 << 29, 1), in_shape=(1, (1 << 30) + 5, 4, 32), pad_begin=0,
+          pad_end=0, filt_shape=(3, 3, 16, 8)), "size_limit"),    # H >= 2^30
+    # H + pt + pb = 20 + pt + 2 against 2^30 (a large stride keeps M small)
+    (dict(pad_begin=((1 << 30) - 22, 0), stride=(1 << 20, 2)), "size_limit"),
+    (dict(pad_begin=((1 << 30) - 23, 0), stride=(1 << 20, 2)), "ok"),
+])
+def test_general_coordinate_limits(kw, reason):
+    i, f, o, p, fcrs, dt = _gen(**kw)
+    assert igc.REASONS[igc.conv2d_fwd_general_query(i, f, o, p, filter_is_fcrs=fcrs,
+                                                    dtype=dt)] == reason
+
+
+def test_general_input_bytes_use_all_channels():
+    # the input holds N*H*W*C_in elements (all groups): an output right after
+    # a 2x20x21x16 input would still overlap the 32-channel one
+    assert igc.REASONS[_gcheck(output=X + 2 * 20 * 21 * 16 * 2)] == "overlap"
+    assert _gcheck(output=X + 2 * 20 * 21 * 32 * 2) == 0
+
+
+def test_general_declined_call_enqueues_nothing():
+    i, f, o, p, fcrs, dt = _gen(groups=4)
+    assert igc.conv2d_fwd_general(X, W, Y, p, filter_is_fcrs=fcrs, dtype=dt, in_shape=i,
+                                  filt_shape=f, out_shape=o) == 0
+    i, f, o, p, fcrs, dt = _gen(in_shape=(0, 20, 21, 32), out_shape=(0, 7, 11, 8))
+    assert igc.conv2d_fwd_general(X, W, Y, p, filter_is_fcrs=fcrs, dtype=dt, in_shape=i,
+                                  filt_shape=f, out_shape=o) == 1   # empty: nothing to do
+
+
+def test_general_gate_against_oracle_sizes():
+    """Over a grid of parameters the general gate accepts exactly the
+    problems whose oracle output is non-empty (vector width and limits not
+    binding), and the page gate accepts the subset the page allows."""
+    n = 0
+    for (sh, sw), (dh, dw), (pt, pl, pb, pr), g, fcrs in itertools.product(
+            [(1, 1), (2, 2), (3, 1), (1, 4)], [(1, 1), (2, 3)],
+            [(0, 0, 0, 0), (1, 1, 1, 1), (2, 0, 1, 3), (3, 3, 3, 3)], [1, 2, 4],
+            [False, True]):
+        cg, f, r, s = 16, 8, 3, 2
+        in_shape = (1, 9, 7, cg * g)
+        filt = (f, cg, r, s) if fcrs else (r, s, cg, f)
+        ho = oracle.out_size_general(9, r, sh, dh, pt, pb)
+        wo = oracle.out_size_general(7, s, sw, dw, pl, pr)
+        out = (1, max(ho, 0), max(wo, 0), f)
+        p = igc.conv_params(stride=(sh, sw), dilation=(dh, dw), pad_begin=(pt, pl),
+                            pad_end=(pb, pr), groups=g)
+        got = igc.conv2d_fwd_general_query(in_shape, filt, out, p, filter_is_fcrs=fcrs,
+                                           dtype=0)
+        assert (got == 0) == (ho >= 1 and wo >= 1), (sh, sw, dh, dw, pt, pl, pb, pr, g)
+        page = oracle.gate_accepts("bfloat16", "bfloat16", "bfloat16", in_shape, filt, fcrs,
+                                   out, (sh, sw), (dh, dw), (pt, pl), g) and pt == pb and \
+            pl == pr
+        name = igc.conv2d_fwd_general_kernel_name(in_shape, filt, out, p, filter_is_fcrs=fcrs,
+                                                  dtype=0)
+        if got == 0 and not page:
+            assert name == "igemm_fwd_kernel"
+        n += 1
+    assert n == 192

@@ -1,0 +1,186 @@
+"""GPU parity of the general forward convolution (conv2d_fwd_general: per-axis
+stride, dilation, padding before / after each axis, channel groups) through
+the C ABI, against the fp64 oracle (oracle.conv2d_general) over the whole
+output tensor.  Tolerances as for conv2d_fwd: fp32 accumulation of exactly
+rounded inputs and one rounding to the output type.  Each widened parameter
+has its own sweep; a problem inside the page's gate must give conv2d_fwd's
+bits."""
+import os
+import sys
+import zlib
+
+import pytest
+import torch
+
+import datagen
+import implicit_gemm_nhwc_amd as igc
+import oracle
+from test_gpu_parity import TOL, _assert_close, _bits
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def setup_module(_):
+    if not os.path.exists(igc.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# name, dtype, N, H, W, C_in, C_out, R, S, stride, dilation, pad_begin, pad_end, groups
+CASES = [
+    # dilation
+    ("dil2_same_bf16", "bfloat16", 2, 17, 19, 64, 64, 3, 3, 1, 2, 2, 2, 1),
+    ("dil3x1_fp16", "float16", 1, 23, 15, 32, 48, 3, 3, 1, (3, 1), (3, 1), (3, 1), 1),
+    ("dil2_s2_fp8", "float8_e4m3fn", 2, 21, 20, 64, 40, 3, 3, 2, 2, 2, 1, 1),
+    ("dil4_5x5_bf16", "bfloat16", 1, 30, 33, 16, 24, 5, 5, 1, 4, 8, 8, 1),
+    # stride beyond 2 and per-axis strides
+    ("s4_patchify_bf16", "bfloat16", 2, 32, 36, 16, 96, 4, 4, 4, 1, 0, 0, 1),
+    ("s3_3x3_fp16", "float16", 2, 25, 26, 32, 32, 3, 3, 3, 1, 1, 1, 1),
+    ("s1x2_fp8", "float8_e4m3fn", 1, 14, 31, 32, 24, 3, 3, (1, 2), 1, 1, 1, 1),
+    ("s5x3_7x7_bf16", "bfloat16", 1, 40, 29, 16, 8, 7, 7, (5, 3), 1, 3, 3, 1),
+    # asymmetric padding
+    ("same_s2_even_bf16", "bfloat16", 2, 16, 16, 32, 64, 3, 3, 2, 1, 0, 1, 1),
+    ("pad_tlbr_fp16", "float16", 1, 13, 17, 32, 20, 3, 2, 1, 1, (2, 0), (0, 3), 1),
+    ("pad3_fp8", "float8_e4m3fn", 1, 15, 15, 16, 16, 7, 7, 2, 1, 3, 3, 1),
+    # channel groups
+    ("g2_bf16", "bfloat16", 2, 15, 14, 64, 64, 3, 3, 1, 1, 1, 1, 2),
+    ("g32_resnext_bf16", "bfloat16", 2, 14, 14, 256, 256, 3, 3, 1, 1, 1, 1, 32),
+    ("g4_s2_fp16", "float16", 1, 19, 17, 64, 32, 3, 3, 2, 1, 1, 1, 4),
+    ("g2_fp8", "float8_e4m3fn", 1, 12, 13, 64, 48, 3, 3, 1, 1, 1, 1, 2),
+    ("g2_fg3_bf16", "bfloat16", 1, 9, 11, 32, 6, 3, 3, 1, 1, 1, 1, 2),
+    ("g2_wide_bf16", "bfloat16", 1, 10, 12, 128, 256, 1, 1, 1, 1, 0, 0, 2),
+    ("g8_cg8_ragged_k_bf16", "bfloat16", 3, 23, 29, 64, 64, 3, 3, 1, 1, 1, 1, 8),
+    # everything at once
+    ("all_fp16", "float16", 2, 27, 22, 96, 48, 3, 2, (3, 2), (2, 3), (1, 0), (2, 3), 3),
+    ("all_fp8", "float8_e4m3fn", 1, 26, 31, 64, 32, 5, 3, (2, 3), (2, 1), (4, 0), (1, 2), 2),
+]
+
+
+def _pair(v):
+    return (v, v) if isinstance(v, int) else tuple(v)
+
+
+def _draw(case, fcrs=False, resid=False):
+    cid, dt, n, h, w, c, f, r, s, st, dil, pb, pe, g = case
+    p = igc.conv_params(stride=st, dilation=dil, pad_begin=pb, pad_end=pe, groups=g)
+    ho, wo = igc.out_hw_general(h, w, r, s, p)
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype=dt, fcrs=fcrs,
+                                   x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0) if resid else None,
+                                   out_hw=(ho, wo), seed=zlib.crc32(cid.encode()) % 1000,
+                                   filt_c=c // g)
+    return p, (n, ho, wo, f), x, wt, src
+
+
+def _oracle(case, x, wt, fcrs, **kw):
+    _, _, _, _, _, _, _, _, _, st, dil, pb, pe, g = case
+    return oracle.conv2d_general(x, wt, filter_is_fcrs=fcrs, stride=_pair(st),
+                                 dilation=_pair(dil), pad_begin=_pair(pb), pad_end=_pair(pe),
+                                 groups=g, **kw)
+
+
+def _run(x, wt, out_shape, p, fcrs, **kw):
+    out = torch.empty(out_shape, dtype=datagen.OUT_DTYPES[str(x.dtype)[6:]], device=DEV)
+    nb = igc.conv2d_workspace_bytes(wt.shape, fcrs, x.dtype)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    rc = igc.conv2d_fwd_general(x.to(DEV), wt.to(DEV), out, p, filter_is_fcrs=fcrs,
+                                workspace=ws, **kw)
+    assert rc == 1, f"conv2d_fwd_general returned {rc}"
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_general_parity(case):
+    cid, dt = case[0], case[1]
+    _say(f"general {cid}: {case[2:]}")
+    p, oshape, x, wt, _ = _draw(case)
+    assert igc.conv2d_fwd_general_kernel_name(x.shape, wt.shape, oshape, p,
+                                              filter_is_fcrs=False,
+                                              dtype=x.dtype) == "igemm_fwd_kernel"
+    out = _run(x, wt, oshape, p, False)
+    ref = _oracle(case, x, wt, False)
+    err, scale = _assert_close(out, ref, TOL[dt], cid)
+    _say(f"  max|err|/max|ref| = {err / max(scale, 1e-300):.3e}")
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] in (
+    "dil2_s2_fp8", "g32_resnext_bf16", "g2_fg3_bf16", "all_fp16", "pad_tlbr_fp16",
+    "g2_wide_bf16")], ids=lambda c: c[0])
+def test_general_fcrs_residual_epilogue(case):
+    """FCRS filter, a residual source and the fused scale / bias / SiLU, with
+    groups offsetting the coefficients; FCRS bits equal RSCF bits."""
+    cid, dt = case[0], case[1]
+    _say(f"general epilogue {cid}")
+    p, oshape, x, wt, src = _draw(case, fcrs=True, resid=True)
+    f = oshape[3]
+    gen = torch.Generator().manual_seed(zlib.crc32(cid.encode()) % 977)
+    scale = (torch.rand(f, generator=gen) * 3.0 - 1.5).to(torch.float32)
+    bias = torch.randn(f, generator=gen).to(torch.float32)
+    kw = dict(source=src.to(DEV), beta=-0.75, scale=scale.to(DEV), bias=bias.to(DEV),
+              activation="silu")
+    out = _run(x, wt, oshape, p, True, **kw)
+    ref = _oracle(case, x, wt, True, source=src, beta=-0.75, scale=scale, bias=bias,
+                  act="silu")
+    _assert_close(out, ref, TOL[dt], cid)
+    # the same filter stored RSCF: identical bits
+    w_rscf = wt.view(torch.uint8).permute(2, 3, 1, 0).contiguous().view(wt.dtype) \
+        if wt.element_size() == 1 else wt.permute(2, 3, 1, 0).contiguous()
+    out2 = _run(x, w_rscf, oshape, p, False, **kw)
+    assert torch.equal(_bits(out), _bits(out2))
+
+
+def test_general_groups_equal_separate_convolutions():
+    """A grouped call gives, bit for bit, the concatenation of one ungrouped
+    call per group on that group's channels."""
+    case = ("g4_split", "bfloat16", 2, 13, 15, 64, 32, 3, 3, (2, 1), (1, 2), (1, 2), (0, 2), 4)
+    _say("general groups vs per-group calls")
+    p, oshape, x, wt, _ = _draw(case)
+    out = _run(x, wt, oshape, p, False)
+    g, cg, fg = 4, 16, 8
+    p1 = igc.conv_params(stride=(2, 1), dilation=(1, 2), pad_begin=(1, 2), pad_end=(0, 2))
+    for k in range(g):
+        xs = x[..., k * cg:(k + 1) * cg].contiguous()
+        ws_ = wt[..., k * fg:(k + 1) * fg].contiguous()
+        part = _run(xs, ws_, oshape[:3] + (fg,), p1, False)
+        assert torch.equal(_bits(out[..., k * fg:(k + 1) * fg].contiguous()), _bits(part)), k
+
+
+@pytest.mark.parametrize("st,pad", [(1, 1), (2, 0), (2, 2), (1, 0)])
+def test_general_page_problems_match_conv2d_fwd(st, pad):
+    """Inside the page's gate conv2d_fwd_general runs conv2d_fwd's kernel:
+    the same bits."""
+    _say(f"general page problem st{st} p{pad}")
+    x, wt, _ = datagen.make_case(N=2, H=19, W=21, C=64, F=48, R=3, S=3, dtype="bfloat16",
+                                 fcrs=False, x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                 seed=11)
+    p = igc.conv_params(stride=st, pad_begin=pad)
+    ho, wo = igc.out_hw_general(19, 21, 3, 3, p)
+    assert (ho, wo) == igc.out_hw(19, 21, 3, 3, st, pad)
+    a = _run(x, wt, (2, ho, wo, 48), p, False)
+    b = igc.conv2d(x.to(DEV), wt.to(DEV), filter_is_fcrs=False, stride=st, padding=pad)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a), _bits(b))
+
+
+def test_general_dilated_equals_zero_inserted_filter():
+    """Dilation d equals the undilated convolution with d - 1 zero taps
+    between the filter's taps: both calls within tolerance of the oracle of
+    the dilated problem (their summation orders differ)."""
+    _say("general dilation vs zero-inserted filter")
+    case = ("dilz", "bfloat16", 1, 20, 22, 32, 16, 3, 3, 1, (2, 3), (2, 3), (2, 3), 1)
+    p, oshape, x, wt, _ = _draw(case)
+    a = _run(x, wt, oshape, p, False)
+    wz = torch.zeros((5, 7, 32, 16), dtype=wt.dtype)
+    wz[::2, ::3] = wt
+    p2 = igc.conv_params(pad_begin=(2, 3))
+    b = _run(x, wz, oshape, p2, False)
+    ref = _oracle(case, x, wt, False)
+    _assert_close(a, ref, TOL["bfloat16"], "dilated")
+    _assert_close(b, ref, TOL["bfloat16"], "zero-inserted")
