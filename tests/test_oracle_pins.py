@@ -727,3 +727,29 @@ def test_general_stride_subsamples_stride1(sh, sw):
     b = oracle.conv2d_general(x, wt, filter_is_fcrs=False, dilation=(2, 1), pad_begin=(1, 1),
                               pad_end=(0, 2))
     np.testing.assert_array_equal(a, b[:, ::sh, ::sw][:, :a.shape[1], :a.shape[2]])
+
+
+@pytest.mark.parametrize("case", GENERAL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_general_off_centre_delta(case):
+    """A filter that is one 1 at an off-centre tap (r0, s0) and one input
+    channel per output channel copies that channel of the input pixel the
+    tap lands on, oh*sh - pt + r0*dh and ow*sw - pl + s0*dw (zero where it
+    lands in the padding): the output is known exactly, element by element."""
+    n, h, w, c, f, r, s, (sh, sw), (dh, dw), (pt, pl), (pb, pr), g = case
+    cg, fg = c // g, f // g
+    r0, s0 = r - 1, s // 2
+    csel = [(co * 7 + 3) % cg for co in range(f)]
+    wt = np.zeros((r, s, cg, f))
+    for co in range(f):
+        wt[r0, s0, csel[co], co] = 1.0
+    x = _rand((n, h, w, c))
+    y = oracle.conv2d_general(x, wt, filter_is_fcrs=False, stride=(sh, sw), dilation=(dh, dw),
+                              pad_begin=(pt, pl), pad_end=(pb, pr), groups=g)
+    ho = oracle.out_size_general(h, r, sh, dh, pt, pb)
+    wo = oracle.out_size_general(w, s, sw, dw, pl, pr)
+    want = np.zeros((n, ho, wo, f))
+    for b, oh, ow, co in itertools.product(range(n), range(ho), range(wo), range(f)):
+        ih, iw = oh * sh - pt + r0 * dh, ow * sw - pl + s0 * dw
+        if 0 <= ih < h and 0 <= iw < w:
+            want[b, oh, ow, co] = x[b, ih, iw, (co // fg) * cg + csel[co]]
+    np.testing.assert_array_equal(y, want)
