@@ -21,10 +21,13 @@ Also reported on the same line:
   cpu_baseline  the fp64 oracle timed on this host's cores on the same
                 workload (the full batch);
   shapes        the same measurement for each of the five named workloads;
+  launch_floor_us  an empty kernel's time per launch, back to back (the
+                floor under the tiny layer's kernel time);
   next          the fused per-channel epilogue's cost on the headline layer,
                 the materialised im2col + GEMM route against the fused
-                kernel on the two memory-bound layers, and a stride-1
-                transposed convolution (both of its launches).
+                kernel on the two memory-bound layers, transposed
+                convolutions (whole calls), and layers outside page 1's gate
+                through conv2d_fwd_general (whole calls).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -334,7 +337,77 @@ def measure_next(torch, igc, launches, rotate_bytes=ROTATE_BYTES):
             "frac_mfma": round(flops / (t * 1e-6) / 1e12 / PEAK["bf16_tflops"], 4)}
         del sets
         torch.cuda.empty_cache()
+    out["general"] = measure_general(torch, igc, launches, rotate_bytes)
     return out
+
+
+# Layers outside page 1's gate, run through conv2d_fwd_general (the tiled
+# kernel with its general gather): a dilated 3x3 on the headline layer's
+# shape, a ResNeXt-style grouped 3x3 (32 groups of 8 channels) and a 4x4
+# stride-4 patchify stem (8 input channels).
+GENERAL_LAYERS = {
+    "dilated2_3x3_64c_n32": dict(N=32, H=56, W=56, C=64, F=64, R=3, S=3, stride=1,
+                                 dilation=2, pad=2, groups=1),
+    "grouped32_3x3_256c_n32": dict(N=32, H=28, W=28, C=256, F=256, R=3, S=3, stride=1,
+                                   dilation=1, pad=1, groups=32),
+    "patchify_4x4_s4_8to96_n32": dict(N=32, H=224, W=224, C=8, F=96, R=4, S=4, stride=4,
+                                      dilation=1, pad=0, groups=1),
+}
+
+
+def measure_general(torch, igc, launches, rotate_bytes=ROTATE_BYTES):
+    """Each general layer's whole conv2d_fwd_general call (filter transpose
+    and GEMM), bf16, on rotating buffer sets; TFLOP/s from the useful FLOPs
+    (2 * N * Ho * Wo * C_out * R * S * C_in / groups)."""
+    import datagen
+
+    res = {}
+    for tag, L in GENERAL_LAYERS.items():
+        n, h, w, c, f, r, s = (L[k] for k in ("N", "H", "W", "C", "F", "R", "S"))
+        g = L["groups"]
+        p = igc.conv_params(stride=L["stride"], dilation=L["dilation"], pad_begin=L["pad"],
+                            groups=g)
+        ho, wo = igc.out_hw_general(h, w, r, s, p)
+        x, wt, _ = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype="bfloat16",
+                                     fcrs=False, x_dist=("normal", 1.0),
+                                     w_dist=("normal", 1.0 / (r * s * c / g) ** 0.5), seed=0,
+                                     filt_c=c // g)
+        per = x.numel() * 2 + n * ho * wo * f * 2
+        nsets = min(MAX_SETS, max(1, -(-rotate_bytes // per)))
+        wsb = max(igc.conv2d_workspace_bytes(wt.shape, False, wt.dtype), 16)
+        sets = [dict(x=x.to("cuda:0"), w=wt.to("cuda:0"),
+                     y=torch.empty((n, ho, wo, f), dtype=torch.bfloat16, device="cuda:0"),
+                     ws=torch.empty(wsb, dtype=torch.uint8, device="cuda:0"))
+                for _ in range(nsets)]
+
+        def call(i):
+            b = sets[i % nsets]
+            _ok(igc.conv2d_fwd_general(b["x"], b["w"], b["y"], p, filter_is_fcrs=False,
+                                       workspace=b["ws"]), "conv2d_fwd_general")
+        for i in range(nsets):
+            call(i)
+        t = event_time(torch, call, launches)
+        flops = 2 * n * ho * wo * f * r * s * (c // g)
+        nbytes = x.numel() * 2 + wt.numel() * 2 + n * ho * wo * f * 2
+        res[tag] = {
+            "shape": f"N={n} {h}x{w} C={c} -> F={f}, {r}x{s}, stride {L['stride']}, "
+                     f"dilation {L['dilation']}, pad {L['pad']}, groups {g} -> {ho}x{wo}, bf16",
+            "kernel": igc.conv2d_fwd_general_kernel_name(x.shape, wt.shape, (n, ho, wo, f), p,
+                                                         filter_is_fcrs=False, dtype=x.dtype),
+            "call_us": round(t, 3), "tflops": round(flops / (t * 1e-6) / 1e12, 1),
+            "frac_mfma": round(flops / (t * 1e-6) / 1e12 / PEAK["bf16_tflops"], 4),
+            "gbs": round(nbytes / (t * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nbytes / (t * 1e-6) / 1e9 / PEAK["hbm_gbs"], 4)}
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
+def launch_floor(torch, launches=200):
+    """Mean time per launch of an empty kernel (torch's spin kernel with a
+    zero count) back to back behind a spin kernel: the per-launch floor under
+    every kernel time above."""
+    return event_time(torch, lambda i: torch.cuda._sleep(0), launches)
 
 
 def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES, graphs=True):
@@ -507,6 +580,9 @@ def main():
                   f"({100 * r['frac_hbm']:.1f}% HBM), bound {r['bound']}",
                   file=sys.stderr, flush=True)
 
+    floor_us = launch_floor(torch)
+    print(f"# empty-kernel launch floor: {floor_us:.2f} us per launch", file=sys.stderr,
+          flush=True)
     nxt = None
     if not args.no_next:
         nxt = measure_next(torch, igc, max(10, args.steps // 2), rotate)
@@ -532,6 +608,7 @@ def main():
                    "filter_layout": "FCRS" if spec["fcrs"] else "RSCF",
                    "residual": spec["src"] is not None, "parallelism": "single_gpu"},
         "roofline": roofline,
+        "launch_floor_us": round(floor_us, 3),
         "cpu_baseline": cpu,
         "shapes": shapes,
         "next": nxt,
