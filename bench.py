@@ -301,8 +301,8 @@ def measure_next(torch, igc, launches, rotate_bytes=ROTATE_BYTES):
     out["im2col_ablation"] = abl
 
     # transposed convolutions: a decoder-style 3x3 stride-1 layer and the 4x4
-    # stride-2 2x upsampler, each call timed whole (filter flip, GEMMs and,
-    # for stride 2, the phase interleave) over rotating buffer sets
+    # stride-2 2x upsampler, each call timed whole (the phases' filter flips
+    # and GEMMs) over rotating buffer sets
     out["transposed"] = {}
     for tag, (n, h, w, c, f, r, st, p) in {
             "3x3_s1": (8, 64, 64, 256, 128, 3, 1, 1),

@@ -123,7 +123,7 @@ def lib():
     L.conv2d_transposed_fwd.restype = i32
     L.conv2d_transposed_check.argtypes = tr_head + [vp, sz]
     L.conv2d_transposed_check.restype = i32
-    L.conv2d_transposed_workspace_bytes.argtypes = [i64p, i64p, i32p, i32p, i32, i32]
+    L.conv2d_transposed_workspace_bytes.argtypes = [i64p, i64p, i32p, i32p, i32p, i32]
     L.conv2d_transposed_workspace_bytes.restype = sz
     prm = ctypes.POINTER(IgcConvParams)
     gen_head = [vp, i64p, vp, i32, i64p, vp, i64p, prm, i32, vp, f32, epip]
@@ -530,12 +530,12 @@ def conv2d_materialized(input, filter, output, nk, a_buf, *, filter_is_fcrs, str
                          dtype=dtype_code(input.dtype), in_shape=(n, ho, wo, kp))
 
 
-def conv2d_transposed_workspace_bytes(in_shape, filt_rsfc, *, stride=1, padding=0, dtype,
-                                      with_source=False) -> int:
+def conv2d_transposed_workspace_bytes(in_shape, filt_rsfc, *, stride=1, padding=0, dilation=1,
+                                      dtype) -> int:
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
     return int(lib().conv2d_transposed_workspace_bytes(_i64(in_shape), _i64(filt_rsfc),
-                                                       _pair(stride), _pair(padding), code,
-                                                       int(bool(with_source))))
+                                                       _pair(stride), _pair(dilation),
+                                                       _pair(padding), code))
 
 
 def _tr_head(input, filter, output, stride, dilation, padding, dtype, source, beta, scale,
@@ -583,20 +583,31 @@ def conv2d_transposed_fwd(input, filter, output, *, stride=1, padding=0, dilatio
                                        _stream(stream, output))
 
 
-def conv2d_transposed(input, filter, *, stride=1, padding=0, source=None, beta=0.0,
-                      scale=None, bias=None, activation=None, stream=None):
+def transposed_out_hw(h, w, r, s, *, stride=1, padding=0, dilation=1):
+    """Ho, Wo of the transposed convolution: (H-1)*st - 2p + d*(R-1) + 1."""
+    st, p, d = (_two(v) for v in (stride, padding, dilation))
+    return ((h - 1) * st[0] - 2 * p[0] + d[0] * (r - 1) + 1,
+            (w - 1) * st[1] - 2 * p[1] + d[1] * (s - 1) + 1)
+
+
+def _two(v):
+    return (int(v), int(v)) if isinstance(v, int) else (int(v[0]), int(v[1]))
+
+
+def conv2d_transposed(input, filter, *, stride=1, padding=0, dilation=1, source=None,
+                      beta=0.0, scale=None, bias=None, activation=None, stream=None):
     """Allocate the NHWC output and run conv2d_transposed_fwd into it
     (filter RSFC [R, S, F, C])."""
     r, s, f, _ = filter.shape
     n, h, w, _ = input.shape
-    ho, wo = (h - 1) * stride - 2 * padding + r, (w - 1) * stride - 2 * padding + s
+    ho, wo = transposed_out_hw(h, w, r, s, stride=stride, padding=padding, dilation=dilation)
     out = torch.empty((n, ho, wo, f), dtype=OUT_DTYPES.get(input.dtype, input.dtype),
                       device=input.device)
     ws = torch.empty(max(conv2d_transposed_workspace_bytes(
-        input.shape, filter.shape, stride=stride, padding=padding, dtype=input.dtype,
-        with_source=source is not None), 16), dtype=torch.uint8, device=input.device)
-    kw = dict(stride=stride, padding=padding, source=source, beta=beta, scale=scale,
-              bias=bias, activation=activation, workspace=ws)
+        input.shape, filter.shape, stride=stride, padding=padding, dilation=dilation,
+        dtype=input.dtype), 16), dtype=torch.uint8, device=input.device)
+    kw = dict(stride=stride, padding=padding, dilation=dilation, source=source, beta=beta,
+              scale=scale, bias=bias, activation=activation, workspace=ws)
     rc = conv2d_transposed_fwd(input, filter, out, stream=stream, **kw)
     if rc == 0:
         reason = conv2d_transposed_check(input, filter, out, **kw)

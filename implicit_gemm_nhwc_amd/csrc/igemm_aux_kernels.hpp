@@ -1,6 +1,5 @@
 // Kernels besides the implicit GEMMs: the filter transposes into NK
-// matrices, the phase interleave of the stride-2 transposed convolution and
-// the materialised im2col.  Included only by the translation unit of the C
+// matrices and the materialised im2col.  Included only by the translation unit of the C
 // entry points.
 #pragma once
 
@@ -55,28 +54,19 @@ __global__ __launch_bounds__(64) void filter_to_nk_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Transposed convolution (page "conv_transposed_gpu": NHWC input, RSFC
-// filter [R][S][F][C], F output and C input channels):
-//   out[n, oh, ow, f] = sum over ih*st - p + r = oh, iw*st - p + s = ow
-//                       of in[n, ih, iw, c] * W[r][s][f][c]
-// Along one axis, the output rows of parity a (oh = st*q + a) take only the
-// taps r = b, b + st, ... (b = (a + p) mod st), at input rows
-// ih = q + c_a - j for r = b + st*j (c_a = (a + p - b) / st).  Read with the
-// taps in increasing input order that is a stride-1 forward correlation of
-// the input with the J taps W[b + st*(J-1-t)], t < J: the forward implicit
-// GEMM at some padding P, whose output row q + c_a - (J-1) + P is output
-// row st*q + a.  With stride 1 there is one phase (b = 0, J = R) and the
-// forward output is the result itself, at padding R - 1 - p.
-//
-// The NK matrix of one phase (taps t_h < JH, t_w < JW):
-//   NK'[f][(t_h*JW + t_w)*C + c] = W[BH + st*(JH-1-t_h)][BW + st*(JW-1-t_w)][f][c]
+// NK matrices of a transposed convolution's phases (page "conv_transposed_gpu":
+// RSFC filter [R][S][F][C], F output and C input channels).  A phase takes the
+// taps BH + LH*j (j < JH) along the height and BW + LW*j (j < JW) along the
+// width and reads them in reverse order (see the phase decomposition in the
+// host code), so its NK matrix is
+//   NK'[f][(t_h*JW + t_w)*C + c] = W[BH + LH*(JH-1-t_h)][BW + LW*(JW-1-t_w)][f][c]
 // for each (f, t_h, t_w) a contiguous run of C elements of W.  One thread
 // copies one 16-byte chunk (C * E % 16 == 0); chunks at or past K are zero.
 struct TapSel {
     int R, S, F, C;    // stored filter
     int BH, BW;        // first tap of the phase along each axis
     int JH, JW;        // taps of the phase along each axis
-    int st;            // tap step (the stride)
+    int LH, LW;        // tap step along each axis
     int K, kpitch;     // K = JH*JW*C; NK row pitch (elements)
 };
 
@@ -102,57 +92,11 @@ __global__ __launch_bounds__(256) void filter_rsfc_to_nk_flipped_kernel(
         if (k0 < t.K) {
             const int tap = k0 / t.C, c0 = k0 - tap * t.C;
             const int th = tap / t.JW, tw = tap - th * t.JW;
-            const int r = t.BH + t.st * (t.JH - 1 - th), sx = t.BW + t.st * (t.JW - 1 - tw);
+            const int r = t.BH + t.LH * (t.JH - 1 - th), sx = t.BW + t.LW * (t.JW - 1 - tw);
             const int64_t src = ((((int64_t)r * t.S + sx) * t.F + f) * t.C + c0) * E;
             v = *reinterpret_cast<const i32x4*>(w + src);
         }
         *reinterpret_cast<i32x4*>(nk + ((int64_t)f * t.kpitch + k0) * E) = v;
-    }
-}
-
-// Moves 2-byte output elements between the interleaved output [N, Ho, Wo, F]
-// and the four phase buffers [N, HY[ah], WY[aw], F] of a stride-2 transposed
-// convolution: output pixel (2*qh + ah, 2*qw + aw) is phase (ah, aw) pixel
-// (qh + OH[ah], qw + OW[aw]).  to_phase = 0 fills the output from the phases,
-// 1 fills the phases from an output-shaped tensor (the residual source; phase
-// pixels no output pixel maps to are left as they are).  One thread per
-// output pixel and 16-byte channel group (F % 8 == 0) or channel.
-struct PhaseMap {
-    const uint16_t* src;
-    uint16_t* dst;
-    uint16_t* phase[4];   // index 2*ah + aw
-    int N, Ho, Wo, F;
-    int HY[2], WY[2], OH[2], OW[2];
-    int to_phase;
-};
-
-__global__ __launch_bounds__(256) void phase_interleave_kernel(PhaseMap m) {
-    const bool vec = (m.F & 7) == 0;
-    const int groups = vec ? m.F / 8 : m.F;
-    const int64_t total = (int64_t)m.N * m.Ho * m.Wo * groups;
-    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total;
-         g += (int64_t)gridDim.x * 256) {
-        const int64_t pix = g / groups;
-        const int cg = (int)(g - pix * groups);
-        const int ow = (int)(pix % m.Wo);
-        const int64_t t = pix / m.Wo;
-        const int oh = (int)(t % m.Ho);
-        const int n = (int)(t / m.Ho);
-        const int ah = oh & 1, aw = ow & 1;
-        const int qh = (oh >> 1) + m.OH[ah], qw = (ow >> 1) + m.OW[aw];
-        const int64_t po = (((int64_t)n * m.HY[ah] + qh) * m.WY[aw] + qw) * m.F;
-        const int64_t oo = pix * m.F;
-        uint16_t* ph = m.phase[2 * ah + aw];
-        if (vec) {
-            const int c = cg * 8;
-            if (m.to_phase)
-                *reinterpret_cast<i32x4*>(ph + po + c) = *reinterpret_cast<const i32x4*>(m.src + oo + c);
-            else
-                *reinterpret_cast<i32x4*>(m.dst + oo + c) = *reinterpret_cast<const i32x4*>(ph + po + c);
-        } else {
-            if (m.to_phase) ph[po + cg] = m.src[oo + cg];
-            else m.dst[oo + cg] = ph[po + cg];
-        }
     }
 }
 

@@ -10,6 +10,7 @@
 #include <mutex>
 #include <stdint.h>
 #include <string.h>
+#include <vector>
 
 #include "igemm_conv.h"
 #include "igemm_host.hpp"
@@ -28,6 +29,7 @@ struct Shape {
     int64_t kpad;    // K rounded up to whole 128-byte k-tiles (elements)
     int64_t kpitch;  // NK row stride (elements), see nk_pitch
     int32_t st, pad;
+    int32_t pt, pl;  // padding before each axis (pad, or the general or phase problem's own)
 };
 
 void filter_rscf(const int64_t* fd, int32_t fcrs, int64_t* R, int64_t* S, int64_t* C, int64_t* F) {
@@ -75,6 +77,7 @@ int32_t check_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_
     if (s.C != cin) return IGC_DECLINE_SHAPE;
     s.st = stride[0];
     s.pad = padding[0];
+    s.pt = s.pl = s.pad;
     s.Ho = out_size(s.H, s.R, s.st, s.pad);
     s.Wo = out_size(s.W, s.S, s.st, s.pad);
     if (s.Ho < 1 || s.Wo < 1) return IGC_DECLINE_OUTPUT_SHAPE;
@@ -379,21 +382,34 @@ bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out) {
 // The kernel a problem goes to, in order of preference.
 enum KernelKind { K_NONE, K_TAPFOLD, K_BAND, K_WIDE, K_RESIDENT, K_TILED };
 
-KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp) {
+// tapfold_ok: the tap-fold kernel may be chosen (it has no output map and
+// is only exercised on the page's symmetric paddings).
+KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp, bool tapfold_ok = true) {
     if (s.M == 0 || s.F == 0) return K_NONE;
-    if (tapfold_plan(s, dtype, bp)) return K_TAPFOLD;
+    if (tapfold_ok && tapfold_plan(s, dtype, bp)) return K_TAPFOLD;
     if (band_plan(s, dtype, bp)) return K_BAND;
     if (wide_ok(s, dtype)) return K_WIDE;
     if (resident_ok(s, dtype)) return K_RESIDENT;
     return K_TILED;
 }
 
-// Several problems of one shape in one launch (the phases of a stride-2
-// transposed convolution): NK matrices, outputs and sources a fixed byte
-// stride apart.
+// Several problems of one shape in one launch (the phases of a strided
+// transposed convolution): NK matrices a fixed byte stride apart; problem
+// gi = gh*split + gw (split = 0: gh = 0, gw = gi) writes its output at
+// gw*y + gh*y2 bytes and reads its source at gw*src + gh*src2 bytes past
+// the first's, and has its padding lowered by gh*dpt (top), gw*dpl (left).
 struct Group {
     int n;
     int64_t nk, y, src;
+    int split = 0;
+    int64_t y2 = 0, src2 = 0;
+    int dpt = 0, dpl = 0;
+};
+
+// An output map (ConvArgs::ymap): GEMM pixel (n, oh, ow) to output pixel
+// (n, oh*ysh, ow*ysw) of images of Hy x Wy pixels.
+struct OutMap {
+    int Hy, Wy, ysh, ysw;
 };
 
 template <int DT>
@@ -427,30 +443,49 @@ ConvArgs base_args(const void* input, const void* nk, void* output, const void* 
     }
     a.H = (int)s.H; a.W = (int)s.W; a.C = (int)s.C;
     a.Ho = (int)s.Ho; a.Wo = (int)s.Wo; a.F = (int)s.F;
-    a.R = (int)s.R; a.S = (int)s.S; a.stride = s.st; a.pad = s.pad;
+    a.R = (int)s.R; a.S = (int)s.S; a.stride = s.st;
     a.K = (int)s.K; a.kpitch = (int)s.kpitch; a.M = (int)s.M;
     a.ktiles = (int)(s.kpad / (KT_BYTES / elem_bytes(dtype)));
+    a.pt = s.pt;
+    a.pl = s.pl;
     a.sh = a.sw = s.st;
-    a.pt = a.pl = s.pad;
     a.dh = a.dw = 1;
     a.xpitch = (int)s.C;
     a.ypitch = (int)s.F;
+    a.ymap = 0;
+    a.Hy = (int)s.Ho;
+    a.Wy = (int)s.Wo;
+    a.ysh = a.ysw = 1;
     return a;
 }
 
 hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
                         float beta, const igc_epilogue* epi, const Shape& s, int32_t dtype,
-                        hipStream_t stream, const Group* grp = nullptr) {
+                        hipStream_t stream, const Group* grp = nullptr, bool tapfold_ok = true,
+                        const OutMap* map = nullptr) {
     ConvArgs a = base_args(input, nk, output, source, beta, epi, s, dtype);
     if (grp && grp->n > 1) {
         a.groups = grp->n;
         a.g_nk = grp->nk;
         a.g_y = grp->y;
         a.g_src = grp->src;
+        a.gsplit = grp->split;
+        a.g_y2 = grp->y2;
+        a.g_src2 = grp->src2;
+        a.g_pt = grp->dpt;
+        a.g_pl = grp->dpl;
+    }
+    if (map) {
+        a.ymap = 1;
+        a.Hy = map->Hy;
+        a.Wy = map->Wy;
+        a.ysh = map->ysh;
+        a.ysw = map->ysw;
+        tapfold_ok = false;
     }
     const bool resid = source != nullptr;
     BandPlan bp;
-    const KernelKind kind = select_kernel(s, dtype, &bp);
+    const KernelKind kind = select_kernel(s, dtype, &bp, tapfold_ok);
     if (kind == K_NONE) return hipSuccess;
     switch (dtype) {
         case IGC_DTYPE_BF16: return launch_kind<DT_BF16>(kind, resid, a, bp, stream);
@@ -493,114 +528,171 @@ int32_t im2col_shape(const int64_t in_nhwc[4], const int64_t filt_rs[2],
 }
 
 // ---- transposed convolution (page "conv_transposed_gpu") -----------------
-// Planned as stride-1 forward implicit GEMMs over the input (the phases of
-// filter_rsfc_to_nk_flipped_kernel's comment):
-//   stride 1: one phase, all taps, padding R - 1 - p, written straight to the
-//             output;
-//   stride 2: four phases (output row and column parities), each with the
-//             taps of one parity per axis, all at one padding P, written to
-//             phase buffers that phase_interleave_kernel merges; a residual
-//             source is first split into phase buffers the same way, so the
-//             fused epilogue and its single rounding stay in the GEMMs.
-// Limits: dilation 1, a square filter (R == S) and symmetric padding, so one
-// padding serves both axes; stride 2 needs R >= 2 (every parity has a tap).
+// Definition (cross-correlation form; per axis stride st, dilation d and
+// padding p cut from both ends):
+//   out[n, oh, ow, f] = sum over oh = ih*st - p + r*d, ow = iw*st - p + s*d
+//                       of in[n, ih, iw, c] * W[r][s][f][c]
+// Along one axis, the output rows of phase a (oh = st*q + a, 0 <= a < st)
+// take the taps r with r*d = a + p (mod st).  With g = gcd(st, d) these are
+// r = B + L*j, j < J (L = st/g, B the smallest such tap, J = 0 when there is
+// none below R), at input row ih = q + c - j*e with e = d/g and
+// c = (a + p - B*d)/st.  Read with the taps in increasing input order
+// (j' = J - 1 - j) that is a stride-1 forward correlation with J taps at
+// dilation e and padding P = (J - 1)*e - c before the axis (negative P: the
+// window starts inside the image), whose output row q is output row
+// st*q + a.  Each (row phase, column phase) pair is thus one forward
+// implicit GEMM over the whole input, with its tap subset flipped and the
+// channel roles swapped as NK matrix, that stores through an output map
+// straight into every st-th row and column of the output from (a_h, a_w),
+// reading the residual source at the same places: no phase buffers, and the
+// fused epilogue with its single rounding stays in the GEMMs.  A phase with
+// no tap gets the epilogue alone (a GEMM with K = 0).
+struct TAxis {
+    int J = 0, B = 0, L = 1, e = 1, P = 0;
+    int64_t Q = 0;   // output rows (columns) of the phase
+};
+
+struct TPhase {
+    int ah = 0, aw = 0;
+    Shape s{};        // the phase's forward problem (R = JH, S = JW, Ho = QH, Wo = QW)
+    TAxis h, w;
+    size_t nk_off = 0;
+};
+
 struct TPlan {
-    int32_t st = 1;
-    int64_t N = 0, H = 0, W = 0, C = 0, R = 0, F = 0, Ho = 0, Wo = 0;
-    int32_t P = 0;
-    int nph = 1;
-    int J[2] = {0, 0}, B[2] = {0, 0}, OH[2] = {0, 0}, OW[2] = {0, 0};
-    int64_t YH[2] = {0, 0}, YW[2] = {0, 0};
-    Shape ph[4];
-    size_t nk_off[4] = {}, y_off[4] = {}, s_off[4] = {};
+    int64_t N = 0, H = 0, W = 0, C = 0, R = 0, S = 0, F = 0, Ho = 0, Wo = 0;
+    int32_t sh = 1, sw = 1;
+    std::vector<TPhase> ph;
     size_t ws_bytes = 0;
+    bool grouped = false;   // every phase one shape: one grouped launch
+    int dpt = 0, dpl = 0;   // padding step between phase rows / columns (grouped)
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+TAxis axis_phase(int64_t a, int64_t st, int64_t d, int64_t p, int64_t R, int64_t out) {
+    TAxis x;
+    const int64_t g = gcd64(st, d);
+    x.L = (int)(st / g);
+    x.e = (int)(d / g);
+    x.Q = a < out ? (out - a + st - 1) / st : 0;
+    for (int64_t r = 0; r < x.L && r < R; ++r) {
+        if (((a + p - r * d) % st + st) % st == 0) {
+            x.B = (int)r;
+            x.J = (int)((R - 1 - r) / x.L + 1);
+            const int64_t c = (a + p - r * d) / st;   // exact
+            x.P = (int)((x.J - 1) * (int64_t)x.e - c);
+            break;
+        }
+    }
+    return x;
+}
+
+// The phase's forward problem within the forward kernels' limits (those of
+// check_shapes), or false.
+bool phase_shape(const TPlan& t, const TAxis& h, const TAxis& w, int64_t eb, Shape* out) {
+    Shape s{};
+    s.N = t.N; s.H = t.H; s.W = t.W; s.C = t.C; s.F = t.F;
+    s.R = h.J; s.S = w.J;
+    s.Ho = h.Q; s.Wo = w.Q;
+    s.st = 1;
+    s.pad = 0;
+    s.pt = h.P;
+    s.pl = w.P;
+    const int64_t lim = (int64_t)1 << 31;
+    s.M = s.N * s.Ho * s.Wo;
+    s.K = s.R * s.S * s.C;
+    if (s.M >= lim || s.K >= lim || (s.R * s.W + s.S) * s.C >= lim) return false;
+    s.kpad = round_up(s.K, KT_BYTES / eb);
+    s.kpitch = nk_pitch(s.K, s.F, eb);
+    if (s.kpitch >= lim || s.F * s.kpitch * eb >= lim) return false;
+    *out = s;
+    return true;
+}
+
 int32_t transposed_plan(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
                         const int64_t out_nhwc[4], const int32_t stride[2],
                         const int32_t dilation[2], const int32_t padding[2], int32_t dtype,
-                        bool with_source, TPlan* tp) {
+                        TPlan* tp) {
     if (!in_nhwc || !filt_rsfc || !out_nhwc || !stride || !dilation || !padding)
         return IGC_DECLINE_NULL_POINTER;
     if (dtype != IGC_DTYPE_BF16 && dtype != IGC_DTYPE_FP16 && dtype != IGC_DTYPE_FP8_E4M3FN)
         return IGC_DECLINE_DTYPE;
-    if (!((stride[0] == 1 && stride[1] == 1) || (stride[0] == 2 && stride[1] == 2)))
-        return IGC_DECLINE_STRIDE;
-    if (dilation[0] != 1 || dilation[1] != 1) return IGC_DECLINE_DILATION;
-    if (padding[0] != padding[1] || padding[0] < 0) return IGC_DECLINE_PADDING;
+    if (stride[0] < 1 || stride[1] < 1) return IGC_DECLINE_STRIDE;
+    if (dilation[0] < 1 || dilation[1] < 1) return IGC_DECLINE_DILATION;
+    if (padding[0] < 0 || padding[1] < 0) return IGC_DECLINE_PADDING;
     TPlan t;
-    t.st = stride[0];
+    t.sh = stride[0];
+    t.sw = stride[1];
     t.N = in_nhwc[0]; t.H = in_nhwc[1]; t.W = in_nhwc[2]; t.C = in_nhwc[3];
-    t.R = filt_rsfc[0]; t.F = filt_rsfc[2];
-    const int64_t S = filt_rsfc[1], p = padding[0];
-    if (t.R < 1 || S < 1 || t.F < 0 || t.C < 0 || filt_rsfc[3] != t.C || t.N < 0 || t.H < 1 ||
+    t.R = filt_rsfc[0]; t.S = filt_rsfc[1]; t.F = filt_rsfc[2];
+    if (t.R < 1 || t.S < 1 || t.F < 0 || t.C < 0 || filt_rsfc[3] != t.C || t.N < 0 || t.H < 1 ||
         t.W < 1)
         return IGC_DECLINE_SHAPE;
-    if (t.R != S) return IGC_DECLINE_PADDING;
-    t.Ho = (t.H - 1) * t.st - 2 * p + t.R;
-    t.Wo = (t.W - 1) * t.st - 2 * p + t.R;
-    const bool out_ok = t.Ho >= 1 && t.Wo >= 1 && out_nhwc[0] == t.N && out_nhwc[1] == t.Ho &&
-                        out_nhwc[2] == t.Wo && out_nhwc[3] == t.F;
+    const int64_t lim = (int64_t)1 << 31, l30 = (int64_t)1 << 30;
+    if (t.N >= lim || t.H >= lim || t.W >= lim || t.C >= lim || t.F >= lim || t.R >= lim ||
+        t.S >= lim)
+        return IGC_DECLINE_SIZE_LIMIT;
+    // output extents before the padding is cut, and the padding, below 2^30:
+    // every phase coordinate then fits the kernels' 32-bit arithmetic
+    const int64_t fh = (t.H - 1) * t.sh + (int64_t)dilation[0] * (t.R - 1) + 1;
+    const int64_t fw = (t.W - 1) * t.sw + (int64_t)dilation[1] * (t.S - 1) + 1;
+    if (fh >= l30 || fw >= l30 || padding[0] >= l30 || padding[1] >= l30)
+        return IGC_DECLINE_SIZE_LIMIT;
+    t.Ho = fh - 2 * (int64_t)padding[0];
+    t.Wo = fw - 2 * (int64_t)padding[1];
+    if (t.Ho < 1 || t.Wo < 1 || out_nhwc[0] != t.N || out_nhwc[1] != t.Ho ||
+        out_nhwc[2] != t.Wo || out_nhwc[3] != t.F)
+        return IGC_DECLINE_OUTPUT_SHAPE;
     const int64_t eb = elem_bytes(dtype);
-    const int32_t one[2] = {1, 1};
-    if (t.st == 1) {
-        t.nph = 1;
-        t.P = (int32_t)(t.R - 1 - p);
-        if (t.P < 0 || t.P > 2) return IGC_DECLINE_PADDING;
-        if (!out_ok) return IGC_DECLINE_OUTPUT_SHAPE;
-        t.J[0] = (int)t.R;
-        const int64_t fd[4] = {t.R, t.R, t.C, t.F};
-        const int32_t fp[2] = {t.P, t.P};
-        const int32_t rc = check_shapes(in_nhwc, 0, fd, out_nhwc, one, one, fp, 1, dtype, &t.ph[0]);
-        if (rc != IGC_OK) return rc;
-        t.nk_off[0] = 0;
-        t.ws_bytes = (size_t)(t.F * t.ph[0].kpitch * eb);
-        *tp = t;
-        return IGC_OK;
-    }
-    if (t.R < 2) return IGC_DECLINE_SHAPE;
-    t.nph = 4;
-    int64_t c[2];
-    int64_t P = 0;
-    for (int a = 0; a < 2; ++a) {
-        t.B[a] = (int)((a + p) % 2);
-        t.J[a] = (int)((t.R - t.B[a] + 1) / 2);
-        c[a] = (a + p - t.B[a]) / 2;
-        const int64_t need = t.J[a] - 1 - c[a];
-        if (need > P) P = need;
-    }
-    if (P > 2) return IGC_DECLINE_PADDING;
-    if (!out_ok) return IGC_DECLINE_OUTPUT_SHAPE;
-    t.P = (int32_t)P;
-    for (int a = 0; a < 2; ++a) {
-        const int64_t o = c[a] - (t.J[a] - 1) + P;
-        t.OH[a] = t.OW[a] = (int)o;
-        t.YH[a] = t.H + 2 * P - t.J[a] + 1;
-        t.YW[a] = t.W + 2 * P - t.J[a] + 1;
-        const int64_t qh = (t.Ho - a + 1) / 2, qw = (t.Wo - a + 1) / 2;
-        if (o < 0 || o + qh > t.YH[a] || o + qw > t.YW[a]) return IGC_DECLINE_PADDING;
-    }
+    if ((t.C * eb) % 16 != 0) return IGC_DECLINE_VECTOR_WIDTH;
+    // the wide kernel places a 32-pixel block's mapped pixels at 32-bit byte
+    // offsets from its first one
+    if ((33 * t.sh * t.Wo + 32 * (int64_t)t.sw) * t.F * 2 >= lim) return IGC_DECLINE_SIZE_LIMIT;
+    if (t.sh * (int64_t)t.sw > 4096) return IGC_DECLINE_SIZE_LIMIT;
     size_t off = 0;
-    for (int ph = 0; ph < 4; ++ph) {
-        const int ah = ph >> 1, aw = ph & 1;
-        const int64_t fd[4] = {t.J[ah], t.J[aw], t.C, t.F};
-        const int64_t od[4] = {t.N, t.YH[ah], t.YW[aw], t.F};
-        const int32_t fp[2] = {t.P, t.P};
-        const int32_t rc = check_shapes(in_nhwc, 0, fd, od, one, one, fp, 1, dtype, &t.ph[ph]);
-        if (rc != IGC_OK) return rc;
-        const size_t ybytes = (size_t)(t.N * t.YH[ah] * t.YW[aw] * t.F) * 2;
-        t.nk_off[ph] = off;
-        off += align256((size_t)(t.F * t.ph[ph].kpitch * eb));
-        t.y_off[ph] = off;
-        off += align256(ybytes);
-        if (with_source) {
-            t.s_off[ph] = off;
-            off += align256(ybytes);
+    for (int ah = 0; ah < t.sh; ++ah) {
+        const TAxis h = axis_phase(ah, t.sh, dilation[0], padding[0], t.R, t.Ho);
+        for (int aw = 0; aw < t.sw; ++aw) {
+            const TAxis w = axis_phase(aw, t.sw, dilation[1], padding[1], t.S, t.Wo);
+            TPhase p;
+            p.ah = ah;
+            p.aw = aw;
+            p.h = h;
+            p.w = w;
+            if (h.Q == 0 || w.Q == 0) continue;   // no output pixel of this phase
+            if (!phase_shape(t, h, w, eb, &p.s)) return IGC_DECLINE_SIZE_LIMIT;
+            p.nk_off = off;
+            off += align256((size_t)(p.s.F * p.s.kpitch * eb));
+            t.ph.push_back(p);
         }
     }
     t.ws_bytes = off;
+    // one grouped launch when every phase has one shape and the paddings step
+    // evenly from phase to phase (always so for strides of 1 and 2)
+    const size_t nph = t.ph.size();
+    t.grouped = nph == (size_t)t.sh * t.sw && nph > 1;
+    if (t.grouped) {
+        const TPhase& p0 = t.ph[0];
+        const TPhase& p1 = t.ph[nph - 1];
+        t.dpt = t.sh > 1 ? (p0.h.P - p1.h.P) / (t.sh - 1) : 0;
+        t.dpl = t.sw > 1 ? (p0.w.P - p1.w.P) / (t.sw - 1) : 0;
+        for (const TPhase& p : t.ph) {
+            if (p.h.J != p0.h.J || p.w.J != p0.w.J || p.h.Q != p0.h.Q || p.w.Q != p0.w.Q ||
+                p.h.e != p0.h.e || p.w.e != p0.w.e || p.h.P != p0.h.P - p.ah * t.dpt ||
+                p.w.P != p0.w.P - p.aw * t.dpl)
+                t.grouped = false;
+        }
+    }
     *tp = t;
     return IGC_OK;
 }
@@ -612,7 +704,7 @@ int32_t transposed_pointers(const TPlan& t, int32_t dtype, const void* input, co
                             const void* workspace, size_t workspace_bytes) {
     const size_t eb = (size_t)elem_bytes(dtype);
     const size_t in_bytes = (size_t)(t.N * t.H * t.W * t.C) * eb;
-    const size_t f_bytes = (size_t)(t.R * t.R * t.F * t.C) * eb;
+    const size_t f_bytes = (size_t)(t.R * t.S * t.F * t.C) * eb;
     const size_t out_bytes = (size_t)(t.N * t.Ho * t.Wo * t.F) * 2;
     if ((in_bytes && !input) || (f_bytes && !filter) || (out_bytes && !output))
         return IGC_DECLINE_NULL_POINTER;
@@ -642,91 +734,101 @@ int32_t transposed_pointers(const TPlan& t, int32_t dtype, const void* input, co
     return check_epilogue(epi, output, so);
 }
 
-// The flipped NK matrices of every phase, in one launch (grid rows =
-// phases); ws + nk_off[ph] receives phase ph's.
+// The flipped NK matrices of every phase, four phases per launch (grid rows
+// = phases); ws + nk_off receives each phase's.
 hipError_t launch_transpose_flipped(const void* filter, const TPlan& t, int32_t dtype, uint8_t* ws,
                                     hipStream_t stream) {
     const int eb = elem_bytes(dtype);
-    TapSels ts{};
-    int64_t most = 0;
-    for (int ph = 0; ph < t.nph; ++ph) {
-        const Shape& s = t.ph[ph];
-        TapSel& sel = ts.t[ph];
-        sel.R = (int)t.R; sel.S = (int)t.R; sel.F = (int)t.F; sel.C = (int)t.C;
-        sel.st = t.st;
-        if (t.st == 1) {
-            sel.BH = sel.BW = 0;
-            sel.JH = sel.JW = (int)t.R;
-        } else {
-            sel.BH = t.B[ph >> 1]; sel.BW = t.B[ph & 1];
-            sel.JH = t.J[ph >> 1]; sel.JW = t.J[ph & 1];
+    for (size_t b = 0; b < t.ph.size(); b += 4) {
+        TapSels ts{};
+        int64_t most = 0;
+        const int cnt = (int)(t.ph.size() - b < 4 ? t.ph.size() - b : 4);
+        for (int i = 0; i < cnt; ++i) {
+            const TPhase& p = t.ph[b + i];
+            TapSel& sel = ts.t[i];
+            sel.R = (int)t.R; sel.S = (int)t.S; sel.F = (int)t.F; sel.C = (int)t.C;
+            sel.BH = p.h.B; sel.BW = p.w.B;
+            sel.JH = p.h.J; sel.JW = p.w.J;
+            sel.LH = p.h.L; sel.LW = p.w.L;
+            sel.K = (int)p.s.K;
+            sel.kpitch = (int)p.s.kpitch;
+            ts.nk[i] = ws + p.nk_off;
+            const int64_t chunks = p.s.F * (p.s.kpitch / (16 / eb));
+            if (chunks > most) most = chunks;
         }
-        sel.K = (int)s.K;
-        sel.kpitch = (int)s.kpitch;
-        ts.nk[ph] = ws + t.nk_off[ph];
-        const int64_t chunks = s.F * (s.kpitch / (16 / eb));
-        if (chunks > most) most = chunks;
+        if (most == 0) continue;
+        const dim3 grid((unsigned)((most + 255) / 256 < 4096 ? (most + 255) / 256 : 4096),
+                        (unsigned)cnt);
+        if (eb == 2)
+            hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<2>, grid, dim3(256), 0, stream,
+                               (const uint8_t*)filter, ts);
+        else
+            hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<1>, grid, dim3(256), 0, stream,
+                               (const uint8_t*)filter, ts);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    if (most == 0) return hipSuccess;
-    const dim3 grid((unsigned)((most + 255) / 256 < 4096 ? (most + 255) / 256 : 4096),
-                    (unsigned)t.nph);
-    if (eb == 2)
-        hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<2>, grid, dim3(256), 0, stream,
-                           (const uint8_t*)filter, ts);
-    else
-        hipLaunchKernelGGL(filter_rsfc_to_nk_flipped_kernel<1>, grid, dim3(256), 0, stream,
-                           (const uint8_t*)filter, ts);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
-hipError_t launch_interleave(const TPlan& t, uint8_t* ws, const void* src, void* dst, size_t* offs,
-                             int to_phase, hipStream_t stream) {
-    PhaseMap m{};
-    m.src = (const uint16_t*)src;
-    m.dst = (uint16_t*)dst;
-    for (int ph = 0; ph < 4; ++ph) m.phase[ph] = (uint16_t*)(ws + offs[ph]);
-    m.N = (int)t.N; m.Ho = (int)t.Ho; m.Wo = (int)t.Wo; m.F = (int)t.F;
-    for (int a = 0; a < 2; ++a) {
-        m.HY[a] = (int)t.YH[a]; m.WY[a] = (int)t.YW[a];
-        m.OH[a] = t.OH[a]; m.OW[a] = t.OW[a];
+// One phase GEMM (or all of them, grouped): the forward kernels when the
+// phase has unit dilation and at least one tap, else the tiled kernel with
+// the phase's dilation (and K = 0 for a phase without taps).
+hipError_t launch_phase(const TPlan& t, const TPhase& p, const void* input, const uint8_t* nk,
+                        void* out, const void* src, float beta, const igc_epilogue* epi,
+                        int32_t dtype, hipStream_t stream, const Group* grp) {
+    const OutMap map{(int)t.Ho, (int)t.Wo, t.sh, t.sw};
+    const bool ident = t.sh == 1 && t.sw == 1;
+    if (p.h.e == 1 && p.w.e == 1 && p.s.K > 0)
+        return launch_igemm(input, nk, out, src, beta, epi, p.s, dtype, stream, grp, false,
+                            ident ? nullptr : &map);
+    ConvArgs a = base_args(input, nk, out, src, beta, epi, p.s, dtype);
+    a.dh = p.h.e;
+    a.dw = p.w.e;
+    if (!ident) {
+        a.ymap = 1;
+        a.Hy = map.Hy; a.Wy = map.Wy; a.ysh = map.ysh; a.ysw = map.ysw;
     }
-    m.to_phase = to_phase;
-    const int64_t groups = (t.F % 8 == 0) ? t.F / 8 : t.F;
-    const int64_t total = t.N * t.Ho * t.Wo * groups;
-    if (total == 0) return hipSuccess;
-    const unsigned blocks = (unsigned)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
-    hipLaunchKernelGGL(phase_interleave_kernel, dim3(blocks), dim3(256), 0, stream, m);
-    return hipGetLastError();
+    if (grp && grp->n > 1) {
+        a.groups = grp->n;
+        a.g_nk = grp->nk; a.g_y = grp->y; a.g_src = grp->src;
+        a.gsplit = grp->split; a.g_y2 = grp->y2; a.g_src2 = grp->src2;
+        a.g_pt = grp->dpt; a.g_pl = grp->dpl;
+    }
+    const bool resid = src != nullptr;
+    switch (dtype) {
+        case IGC_DTYPE_BF16: return launch_tiled_any<DT_BF16>(resid, a, stream);
+        case IGC_DTYPE_FP16: return launch_tiled_any<DT_FP16>(resid, a, stream);
+        default: return launch_tiled_any<DT_FP8>(resid, a, stream);
+    }
 }
 
 hipError_t run_transposed(const TPlan& t, const void* input, const void* filter, void* output,
                           const void* source, float beta, const igc_epilogue* epi, int32_t dtype,
                           uint8_t* ws, hipStream_t stream) {
-    hipError_t e = hipSuccess;
-    e = launch_transpose_flipped(filter, t, dtype, ws, stream);
-    if (t.st == 1) {
-        if (e == hipSuccess) e = launch_igemm(input, ws, output, source, beta, epi, t.ph[0], dtype, stream);
+    hipError_t e = launch_transpose_flipped(filter, t, dtype, ws, stream);
+    const int64_t px = t.F * 2;   // bytes per output pixel
+    if (t.grouped) {
+        // phase gi = ah*sw + aw starts at output pixel (ah, aw)
+        Group g{(int)t.ph.size(), (int64_t)(t.ph[1].nk_off - t.ph[0].nk_off), px,
+                source ? px : 0};
+        g.split = t.sw;
+        g.y2 = t.Wo * px;
+        g.src2 = source ? t.Wo * px : 0;
+        g.dpt = t.dpt;
+        g.dpl = t.dpl;
+        if (e == hipSuccess)
+            e = launch_phase(t, t.ph[0], input, ws + t.ph[0].nk_off, output, source, beta, epi,
+                             dtype, stream, &g);
         return e;
     }
-    size_t yoffs[4], soffs[4];
-    for (int ph = 0; ph < 4; ++ph) { yoffs[ph] = t.y_off[ph]; soffs[ph] = t.s_off[ph]; }
-    if (e == hipSuccess && source) e = launch_interleave(t, ws, source, nullptr, soffs, 1, stream);
-    if (t.J[0] == t.J[1]) {
-        // every phase has the same shape (even R): one grouped launch, the
-        // phases' buffers a fixed stride apart in the workspace
-        const Group g{4, (int64_t)(t.nk_off[1] - t.nk_off[0]), (int64_t)(t.y_off[1] - t.y_off[0]),
-                      source ? (int64_t)(t.s_off[1] - t.s_off[0]) : 0};
-        if (e == hipSuccess)
-            e = launch_igemm(input, ws + t.nk_off[0], ws + t.y_off[0],
-                             source ? (const void*)(ws + t.s_off[0]) : nullptr, beta, epi,
-                             t.ph[0], dtype, stream, &g);
-    } else {
-        for (int ph = 0; ph < 4 && e == hipSuccess; ++ph)
-            e = launch_igemm(input, ws + t.nk_off[ph], ws + t.y_off[ph],
-                             source ? (const void*)(ws + t.s_off[ph]) : nullptr, beta, epi,
-                             t.ph[ph], dtype, stream);
+    for (const TPhase& p : t.ph) {
+        if (e != hipSuccess) break;
+        const int64_t o = (p.ah * t.Wo + p.aw) * px;
+        e = launch_phase(t, p, input, ws + p.nk_off, (uint8_t*)output + o,
+                         source ? (const void*)((const uint8_t*)source + o) : nullptr, beta, epi,
+                         dtype, stream, nullptr);
     }
-    if (e == hipSuccess) e = launch_interleave(t, ws, nullptr, output, yoffs, 0, stream);
     return e;
 }
 
@@ -734,7 +836,10 @@ hipError_t run_transposed(const TPlan& t, const void* input, const void* filter,
 // The parameters page "dispatch_amd_4wave_conv2d" (Args) lists and its
 // dispatcher restricts, widened: per-axis stride, dilation, padding before
 // and after each axis, and channel groups.  A problem inside the page's gate
-// runs exactly as conv2d_fwd; any other runs on the tiled kernel with its
+// runs exactly as conv2d_fwd.  One group at unit dilation and stride (1,1)
+// or (2,2) with any other padding runs on the same forward kernels (each
+// takes the padding before each axis; the tap-fold kernel is left to the
+// page's paddings).  Any other problem runs on the tiled kernel with its
 // general geometry, the groups as one grouped launch (group g reads input
 // channels g*Cg.., NK rows, output channels, source channels and scale /
 // bias entries g*Fg..).
@@ -743,6 +848,8 @@ struct GShape {
     int64_t cin;      // input channels, groups * Cg
     int32_t sh, sw, dh, dw, pt, pl, pb, pr, groups;
     bool page;        // inside the page's gate: conv2d_fwd's kernels run it
+    bool fast;        // one group, unit dilation, stride (1,1) or (2,2), any
+                      // padding: the forward kernels (but the tap-fold one) run it
 };
 
 int64_t out_size_general(int64_t in, int64_t k, int64_t st, int64_t dil, int64_t pb, int64_t pe) {
@@ -795,7 +902,7 @@ int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64
     if (s.Ho > lim / s.Wo) return IGC_DECLINE_SIZE_LIMIT;
     s.M = s.N * s.Ho * s.Wo;
     s.K = s.R * s.S * s.C;
-    if (s.M >= lim || s.K >= lim) return IGC_DECLINE_SIZE_LIMIT;
+    if (s.M >= lim || s.K >= lim || (s.R * s.W + s.S) * s.C >= lim) return IGC_DECLINE_SIZE_LIMIT;
     s.kpad = round_up(s.K, KT_BYTES / eb);
     s.kpitch = nk_pitch(s.K, s.F, eb);
     if (s.kpitch >= lim || s.F * s.kpitch * eb >= lim) return IGC_DECLINE_SIZE_LIMIT;
@@ -803,8 +910,12 @@ int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64
     // tiles per group
     if ((s.M + 127) / 128 * ((s.F / t.groups + 15) / 16) * t.groups >= lim)
         return IGC_DECLINE_SIZE_LIMIT;
-    t.page = t.groups == 1 && t.dh == 1 && t.dw == 1 && t.sh == t.sw && t.sh <= 2 &&
-             t.pt == t.pb && t.pt == t.pl && t.pt == t.pr && t.pt <= 2;
+    t.fast = t.groups == 1 && t.dh == 1 && t.dw == 1 && t.sh == t.sw && t.sh <= 2;
+    t.page = t.fast && t.pt == t.pb && t.pt == t.pl && t.pt == t.pr && t.pt <= 2;
+    s.st = t.sh;
+    s.pad = 0;
+    s.pt = t.pt;
+    s.pl = t.pl;
     if (t.page) {
         // the page form: conv2d_fwd's own gate, limits included
         const int32_t st[2] = {t.sh, t.sw}, dil[2] = {1, 1}, pad[2] = {t.pt, t.pl};
@@ -844,7 +955,9 @@ int32_t check_general(const void* input, const int64_t in_nhwc[4], const void* f
 hipError_t launch_general(const void* input, const void* nk, void* output, const void* source,
                           float beta, const igc_epilogue* epi, const GShape& g, int32_t dtype,
                           hipStream_t stream) {
-    if (g.page) return launch_igemm(input, nk, output, source, beta, epi, g.s, dtype, stream);
+    if (g.fast)
+        return launch_igemm(input, nk, output, source, beta, epi, g.s, dtype, stream, nullptr,
+                             g.page);
     const Shape& s = g.s;
     const int64_t eb = elem_bytes(dtype);
     const int64_t fg = s.F / g.groups;
@@ -934,16 +1047,15 @@ int32_t conv2d_fwd_noalloc(const void* input, const int64_t in_nhwc[4], const vo
 }
 
 size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
-                                         const int32_t stride[2], const int32_t padding[2],
-                                         int32_t dtype, int32_t with_source) {
-    if (!in_nhwc || !filt_rsfc || !stride || !padding) return 0;
-    const int32_t dil[2] = {1, 1};
-    const int64_t R = filt_rsfc[0], p = padding[0], st = stride[0];
-    const int64_t od[4] = {in_nhwc[0], (in_nhwc[1] - 1) * st - 2 * p + R,
-                           (in_nhwc[2] - 1) * st - 2 * p + filt_rsfc[1], filt_rsfc[2]};
+                                         const int32_t stride[2], const int32_t dilation[2],
+                                         const int32_t padding[2], int32_t dtype) {
+    if (!in_nhwc || !filt_rsfc || !stride || !dilation || !padding) return 0;
+    int64_t od[4] = {in_nhwc[0], 0, 0, filt_rsfc[2]};
+    for (int i = 0; i < 2; ++i)
+        od[1 + i] = (in_nhwc[1 + i] - 1) * stride[i] - 2 * (int64_t)padding[i] +
+                    (int64_t)dilation[i] * (filt_rsfc[i] - 1) + 1;
     TPlan t;
-    if (transposed_plan(in_nhwc, filt_rsfc, od, stride, dil, padding, dtype, with_source != 0,
-                        &t) != IGC_OK)
+    if (transposed_plan(in_nhwc, filt_rsfc, od, stride, dilation, padding, dtype, &t) != IGC_OK)
         return 0;
     return t.ws_bytes;
 }
@@ -958,7 +1070,7 @@ int32_t conv2d_transposed_check(const void* input, const int64_t in_nhwc[4], con
     (void)beta;
     TPlan t;
     const int32_t rc = transposed_plan(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding,
-                                       dtype, source != nullptr, &t);
+                                       dtype, &t);
     if (rc != IGC_OK) return rc;
     return transposed_pointers(t, dtype, input, filter, output, source, epilogue, workspace,
                                workspace_bytes);
@@ -976,8 +1088,7 @@ int32_t conv2d_transposed_fwd(const void* input, const int64_t in_nhwc[4], const
                                 workspace_bytes) != IGC_OK)
         return 0;
     TPlan t;
-    transposed_plan(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding, dtype,
-                    source != nullptr, &t);
+    transposed_plan(in_nhwc, filt_rsfc, out_nhwc, stride, dilation, padding, dtype, &t);
     if (t.N == 0 || t.F == 0) return 1;  // empty output: nothing to compute
     hipStream_t st = (hipStream_t)stream;
     void* ws = workspace;
@@ -1252,9 +1363,9 @@ const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t fil
     if (check_general_shapes(in_nhwc, filter_is_fcrs, filt_dims, out_nhwc, params, dtype, &g) !=
         IGC_OK)
         return nullptr;
-    if (g.page) {
+    if (g.fast) {
         BandPlan bp;
-        switch (select_kernel(g.s, dtype, &bp)) {
+        switch (select_kernel(g.s, dtype, &bp, g.page)) {
             case K_NONE: return "none";
             case K_TAPFOLD: return "igemm_fwd_tapfold_kernel";
             case K_BAND: return "igemm_fwd_band_kernel";

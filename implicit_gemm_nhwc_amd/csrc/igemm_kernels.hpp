@@ -59,7 +59,7 @@ struct ConvArgs {
     int64_t g_nk, g_y, g_src;
     int H, W, C;        // input (N only enters through M)
     int Ho, Wo, F;      // output spatial size and C_out
-    int S, stride, pad;
+    int S, stride;      // filter width; stride of both axes (all kernels but the tiled one)
     int R;              // filter height
     int K;              // R*S*C elements
     int kpitch;         // elements per NK row (stride; a 16-byte zero pad when C_out <= 64)
@@ -78,15 +78,30 @@ struct ConvArgs {
     int spitch;            // LDS floats per staged output pixel (epilogue)
     int cpp_log2;          // log2(16-byte chunks per input pixel)
     int nslot;             // tap-fold kernel: input rows in the LDS ring
+    // padding before each axis (top, left), read by every kernel; it may be
+    // negative (the output window then starts inside the image)
+    int pt, pl;
     // general geometry, read by the tiled kernel only: per-axis stride,
-    // padding before each axis, dilation, and elements per input / output
-    // pixel (the whole tensors' C_in / C_out when a grouped launch runs the
-    // channel groups of one convolution; C and F above are one group's)
-    int sh, sw, pt, pl, dh, dw;
+    // dilation, and elements per input / output pixel (the whole tensors'
+    // C_in / C_out when a grouped launch runs the channel groups of one
+    // convolution; C and F above are one group's)
+    int sh, sw, dh, dw;
     int xpitch, ypitch;
+    // output map (every kernel but the tap-fold one): GEMM pixel (n, oh, ow)
+    // is output pixel (n, oh*ysh, ow*ysw) of an image of Hy x Wy pixels, the
+    // residual source read at the same place (identity: ysh = ysw = 1,
+    // Hy = Ho, Wy = Wo; ymap = 0 then).  A constant pixel offset rides in
+    // the y and src pointers.
+    int ymap, Hy, Wy, ysh, ysw;
     // grouped launch: input bytes and scale / bias entries between problems
     int64_t g_x;
     int g_c;
+    // grouped launch on a grid of gsplit columns (gsplit > 1): problem
+    // gi = gh*gsplit + gw moves the output by gw*g_y + gh*g_y2 bytes, the
+    // source by gw*g_src + gh*g_src2, and its padding by -gh*g_pt, -gw*g_pl
+    int gsplit;
+    int64_t g_y2, g_src2;
+    int g_pt, g_pl;
 };
 
 // Workgroup b is placed on XCD b % 8 by the hardware's round-robin
@@ -112,12 +127,33 @@ __device__ __forceinline__ int group_block(ConvArgs& a, int per) {
         if (a.scale) a.scale += (int64_t)gi * a.g_c;
         if (a.bias) a.bias += (int64_t)gi * a.g_c;
         a.nk += gi * a.g_nk;
-        a.y = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.y) + gi * a.g_y);
+        const int gh = a.gsplit > 1 ? gi / a.gsplit : 0;
+        const int gw = gi - gh * (a.gsplit > 1 ? a.gsplit : 0);
+        a.y = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.y) + gw * a.g_y +
+                                          gh * a.g_y2);
         if (a.src)
             a.src = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.src) +
-                                                      gi * a.g_src);
+                                                      gw * a.g_src + gh * a.g_src2);
+        a.pt -= gh * a.g_pt;
+        a.pl -= gw * a.g_pl;
     }
     return b;
+}
+
+// Output pixel index of GEMM pixel (n, oh, ow) under the output map.
+__device__ __forceinline__ int64_t out_pixel3(const ConvArgs& a, int n, int oh, int ow) {
+    return ((int64_t)n * a.Hy + (int64_t)oh * a.ysh) * a.Wy + (int64_t)ow * a.ysw;
+}
+
+// Output pixel index of GEMM pixel m = (n*Ho + oh)*Wo + ow: m itself
+// without a map.
+__device__ __forceinline__ int64_t out_pixel(const ConvArgs& a, int m) {
+    if (!a.ymap) return m;
+    const int howo = a.Ho * a.Wo;
+    const int n = m / howo;
+    const int rem = m - n * howo;
+    const int oh = rem / a.Wo;
+    return out_pixel3(a, n, oh, rem - oh * a.Wo);
 }
 
 // LDS tiles: rows of 128 bytes, chunk c of row r stored at c ^ ((r >> 1) & 7)
@@ -451,7 +487,7 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
     for (int j = 0; j < TN; ++j) {
         const int m = m0 + wrow_px + j * 16 + frag_row;
         if (m >= a.M) continue;
-        const int64_t obase = (int64_t)m * a.ypitch;
+        const int64_t obase = out_pixel(a, m) * a.ypitch;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int co = co0 + wrow_co + i * 16 + frag_grp * 4;
@@ -577,8 +613,8 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
             const int rem = m - n * howo;
             const int oh = rem / a.Wo;
             const int ow = rem - oh * a.Wo;
-            pih[j] = oh * a.stride - a.pad;
-            piw[j] = ow * a.stride - a.pad;
+            pih[j] = oh * a.stride - a.pt;
+            piw[j] = ow * a.stride - a.pl;
             prel[j] = (int)((int64_t)(n - n0) * img + ((int64_t)pih[j] * a.W + piw[j]) * a.C);
         } else {
             pih[j] = -(1 << 30);
@@ -715,7 +751,7 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
     for (int j = 0; j < TN; ++j) {
         const int m = m0 + j * 16 + frag_row;
         if (m >= a.M) continue;
-        const int64_t obase = (int64_t)m * a.F;
+        const int64_t obase = out_pixel(a, m) * a.F;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int co = i * 16 + grp * 4;
@@ -753,18 +789,6 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
 }
 
 // ---------------------------------------------------------------------------
-// Band kernel: narrow layers (C_out <= 64) whose whole NK filter and one
-// tile's input patch fit in LDS together.
-//
-// A workgroup owns a TH x TW rectangle of output pixels of one image and all
-// output channels.  Phase A copies the padded filter and the tile's input
-// patch (the (TH-1)*st + R rows and (TW-1)*st + S columns it reads, padding
-// as zeros) into LDS with coalesced 16-byte loads, so every input line is
-// fetched once per tile instead of once per filter tap.  After one barrier
-// each wave runs its MFMAs from LDS alone: for every tap (r, s) the B operand
-// of output pixel (th, tw) is patch pixel (th*st + r, tw*st + s).  The fp32
-// results go through LDS and leave with coalesced 16-byte stores; the
-// residual is added there, before the single rounding.
 // Exact n / d for 0 <= n < 2^22 and d >= 1 via a float reciprocal and one
 // correction step (|n * (1/d) - n/d| < 1 there); a handful of full-rate
 // VALU ops instead of a ~30-instruction integer division.
@@ -876,8 +900,8 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     const int trem = tile - n * per_img;
     const int oh0 = (trem / a.tiles_w) * a.TH;
     const int ow0 = (trem % a.tiles_w) * a.TW;
-    const int ih0 = oh0 * a.stride - a.pad;
-    const int iw0 = ow0 * a.stride - a.pad;
+    const int ih0 = oh0 * a.stride - a.pt;
+    const int iw0 = ow0 * a.stride - a.pl;
     const int cbytes = a.C * E;  // bytes of one input pixel
     const int lg = a.cpp_log2;   // log2(chunks per input pixel)
 
@@ -1093,7 +1117,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             const int p = (wave + BAND_WAVES * t) * 32 + frag_row;
             const int th = p / a.TW, tw = p - (p / a.TW) * a.TW;
             const bool pix_ok = (p < P) & (th < th_n) & (tw < tw_n);
-            const int64_t obase = ((int64_t)(n * a.Ho + oh0 + th) * a.Wo + ow0 + tw) * a.F;
+            const int64_t obase = out_pixel3(a, n, oh0 + th, ow0 + tw) * a.F;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1170,7 +1194,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             const int q = small_div(it, a.F, inv_f), co = it - q * a.F;
             const int th = small_div(q, tw_n, inv_twn), tw = q - th * tw_n;
             float v = stage[(th * a.TW + tw) * a.spitch + co];
-            const int64_t o = ((int64_t)(n * a.Ho + oh0 + th) * a.Wo + ow0 + tw) * a.F + co;
+            const int64_t o = out_pixel3(a, n, oh0 + th, ow0 + tw) * a.F + co;
             if (a.epi) v = epi_pre(a, co, v);
             if constexpr (RESID) v = __builtin_fmaf(a.beta, out_to_f32(a.src[o], ODT), v);
             if (a.epi) v = epi_act(a, v);
@@ -1222,9 +1246,10 @@ template <>
 struct WideStep<DT_FP8> { static constexpr int KSB = 64; };
 
 
-// GROUPED: a grouped launch (group_block); a compile-time choice here, since
-// the runtime pointer selection costs the single-problem 256x256 fp8 kernel
-// twelve VGPRs and a quarter of its speed.
+// GROUPED: a grouped launch (group_block) or an output map (ymap); a
+// compile-time choice here, since the runtime pointer selection costs the
+// single-problem 256x256 fp8 kernel twelve VGPRs and a quarter of its speed,
+// and the map's per-pixel placement as much again (measured: 91 -> 122 us).
 template <int DT, int TM, int TN, int WCO, int WPX, int KTB, int NSTAGE, bool RESID, bool TAPK,
           bool GROUPED = false>
 __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs a) {
@@ -1298,8 +1323,8 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             const int rem = m - n * howo;
             const int oh = rem / a.Wo;
             const int ow = rem - oh * a.Wo;
-            pih[i] = oh * a.stride - a.pad;
-            piw[i] = ow * a.stride - a.pad;
+            pih[i] = oh * a.stride - a.pt;
+            piw[i] = ow * a.stride - a.pl;
             // TAPK: the lane's chunk offset rides here; otherwise the per-lane
             // k walks below already start at chunk dch(i)
             prel[i] = (int)((int64_t)(n - n0) * img + (int64_t)(pih[i] * a.W + piw[i]) * a.C * E) +
@@ -1525,24 +1550,47 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             }
     };
     if ((a.F & 3) == 0) {
-        // block j's pixels [mb, mb + 32): buffers over pixels [mb, M)
-        auto blk = [&](const uint16_t* p, int mb) {
-            const int64_t bytes = mb < a.M ? (int64_t)(a.M - mb) * a.F * 2 : 0;
-            return make_rsrc(p + (int64_t)mb * a.F,
+        // Block j's pixels [mb, mb + 32) go through buffers based at the
+        // block's first output pixel bpx(mb), reaching to one past the last
+        // output pixel: without an output map that is pixel mb and [mb, M)
+        // (pixels past M fall outside); with one, each lane's pixel is placed
+        // by the map and pixels past M are masked.
+        const bool mapped = GROUPED && a.ymap;
+        const int64_t last_px = mapped ? out_pixel(a, a.M - 1) + 1 : (int64_t)a.M;
+        auto bpx = [&](int mb) -> int64_t {
+            return mapped ? (mb < a.M ? out_pixel(a, mb) : last_px) : (int64_t)mb;
+        };
+        auto blk = [&](const uint16_t* p, int64_t b0) {
+            const int64_t bytes = b0 < last_px ? (last_px - b0) * a.F * 2 : 0;
+            return make_rsrc(p + b0 * a.F,
                              bytes > (int64_t)OOB_OFFSET ? OOB_OFFSET : (uint32_t)bytes);
+        };
+        // pixel offsets of this lane's NI pixels from the block's base
+        auto rel_px = [&](int mb, int64_t b0, uint32_t (&rel)[NI]) {
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                const int m = mb + q * PPI + pl;
+                rel[q] = !mapped ? (uint32_t)(q * PPI + pl)
+                                 : (m < a.M ? (uint32_t)(out_pixel(a, m) - b0) : OOB_OFFSET);
+            }
         };
         const uint32_t cmask = co < a.F ? 0u : OOB_OFFSET;
         const int mw = m0 + wpx * TN * 32;      // this wave's first pixel
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         u32x2 sv[2][NI];
         auto load_src = [&](int j) {
-            const __amdgpu_buffer_rsrc_t srs = blk(a.src, mw + j * 32);
+            const int mb = mw + j * 32;
+            const int64_t b0 = bpx(mb);
+            uint32_t rel[NI];
+            rel_px(mb, b0, rel);
+            const __amdgpu_buffer_rsrc_t srs = blk(a.src, b0);
 #pragma unroll
             for (int q = 0; q < NI; ++q)
                 // non-temporal: the source is read exactly once (measured
                 // on the fp8 5x5 layer: 101.5 -> 97 us)
                 sv[j & 1][q] = __builtin_amdgcn_raw_buffer_load_b64(
-                    srs, (uint32_t)(((q * PPI + pl) * a.F + co) * 2) | cmask, 0, 2);
+                    srs, ((rel[q] * (uint32_t)a.F + co) * 2) | (rel[q] & OOB_OFFSET) | cmask, 0,
+                    2);
         };
         if constexpr (RESID) load_src(0);
 #pragma unroll
@@ -1551,7 +1599,11 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 if (j + 1 < TN) load_src(j + 1);
             }
             stage_block(j);
-            const __amdgpu_buffer_rsrc_t yrs = blk(a.y, mw + j * 32);
+            const int mb = mw + j * 32;
+            const int64_t b0 = bpx(mb);
+            uint32_t rel[NI];
+            rel_px(mb, b0, rel);
+            const __amdgpu_buffer_rsrc_t yrs = blk(a.y, b0);
 #pragma unroll
             for (int q = 0; q < NI; ++q) {
                 const f32x4 v4 = *reinterpret_cast<const f32x4*>(ereg + (q * PPI + pl) * EP + c4 * 16);
@@ -1577,7 +1629,8 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 // = 256: fp8 5x5 layer 105.6 -> 103.3 us, strided 3x3 layer
                 // 28.1 -> 26.8 us)
                 __builtin_amdgcn_raw_buffer_store_b64(
-                    ov, yrs, (uint32_t)(((q * PPI + pl) * a.F + co) * 2) | cmask, 0, 2);
+                    ov, yrs, ((rel[q] * (uint32_t)a.F + co) * 2) | (rel[q] & OOB_OFFSET) | cmask,
+                    0, 2);
             }
         }
     } else {
@@ -1590,7 +1643,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                 const int m = mb + q * PPI + pl;
                 const f32x4 v4 = *reinterpret_cast<const f32x4*>(ereg + (q * PPI + pl) * EP + c4 * 16);
                 if (m >= a.M) continue;
-                const int64_t o = (int64_t)m * a.F + co;
+                const int64_t o = (GROUPED ? out_pixel(a, m) : (int64_t)m) * a.F + co;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if (co + e < a.F) {

@@ -75,8 +75,8 @@ __global__ __launch_bounds__(TF_WAVES * 64) void igemm_fwd_tapfold_kernel(ConvAr
     const int trem = tile - n * per_img;
     const int oh0 = (trem / a.tiles_w) * a.TH;
     const int ow0 = (trem % a.tiles_w) * a.TW;
-    const int ih0 = oh0 * a.stride - a.pad;
-    const int iw0 = ow0 * a.stride - a.pad;
+    const int ih0 = oh0 * a.stride - a.pt;
+    const int iw0 = ow0 * a.stride - a.pl;
 
     // ---- LDS: [coefficients: scale[32], bias[32]] [input row ring: NSLOT
     // slots of prow bytes] [P ring: R + 1 rows of PW pixels x spitch floats].

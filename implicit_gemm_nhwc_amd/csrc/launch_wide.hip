@@ -50,7 +50,7 @@ hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     const bool tap128 = a.C > 0 && (a.C * E) % 128 == 0;
     const int64_t co_tiles256 = (a.F + 255) / 256;
     const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
-    if (a.groups > 1)   // grouped launches: 128 x 128 tiles only
+    if (a.groups > 1 || a.ymap)   // grouped or mapped launches: 128 x 128 tiles only
         return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, true, true>(a, stream)
                       : launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, false, true>(a, stream);
     if (a.F > 128 && px_tiles256 * co_tiles256 >= kNumCUs)

@@ -344,36 +344,37 @@ size_t conv2d_im2col_bytes(const int64_t in_nhwc[4], const int64_t filt_rs[2],
 
 /*
  * Transposed convolution (page "conv_transposed_gpu": NHWC input, filter in
- * RSFC layout [R][S][F][C] with F output and C input channels; the page runs
- * it through cuDNN's backward-data path and applies an elementwise epilogue
- * as a separate pass).  Definition, cross-correlation form:
+ * RSFC layout [R][S][F][C] with F output and C input channels, stride,
+ * dilation and padding per spatial axis; the page runs it through cuDNN's
+ * backward-data path and applies an elementwise epilogue as a separate
+ * pass).  Definition, cross-correlation form, per axis stride st, dilation
+ * d and padding p cut from both ends:
  *   out[n, oh, ow, f] = sum over (ih, iw, r, s, c) with
- *                         oh = ih*st - p + r,  ow = iw*st - p + s
+ *                         oh = ih*sh - ph + r*dh,  ow = iw*sw - pw + s*dw
  *                       of in[n, ih, iw, c] * W[r][s][f][c]
- *   Ho = (H - 1)*st - 2p + R,  Wo = (W - 1)*st - 2p + S
+ *   Ho = (H - 1)*sh - 2ph + dh*(R - 1) + 1, likewise Wo
  * i.e. the adjoint of the forward convolution whose RSCF filter is W.  Then
  * the same fused epilogue as conv2d_fwd_epilogue (scale, bias, residual
  * source, activation; all optional) and one rounding.
- * Supported here: stride (1,1) or (2,2), dilation (1,1), a square filter
- * (R == S) and symmetric padding p.  Every case runs on the forward
- * implicit-GEMM kernels over the input:
- *   stride 1: one forward convolution with the filter flipped in both taps
- *     and its channel roles swapped, at padding R - 1 - p (needs
- *     R - 1 - p in {0, 1, 2});
- *   stride 2 (R >= 2): the output rows and columns of each parity take the
- *     filter taps of one parity; each of the four (row, column) parities is
- *     a forward convolution with that tap subset, flipped, at one padding P
- *     in {0, 1, 2}, into a phase buffer of the workspace, and a final pass
- *     interleaves the phases into the output.  A residual source is split
- *     into phase buffers first, so every output element still gets the
- *     fused epilogue and one rounding in the GEMM.
- * (The flips are 16-byte chunk permutations done by the NK transpose.)
- * Other shapes are declined (stride, dilation, padding or shape codes);
- * dtypes, layouts, alignment and overlap rules as conv2d_fwd.
+ * Any stride, dilation and padding (each >= 1, >= 1, >= 0) and any R, S.
+ * Along each axis the output rows of phase a (oh = st*q + a) take the taps
+ * r with r*d = a + p (mod st); each (row phase, column phase) pair is one
+ * forward implicit GEMM over the input with that tap subset flipped and the
+ * channel roles swapped (the NK transpose does both), which stores through
+ * an output map straight into its rows and columns of the output and reads
+ * the residual source there: no intermediate buffers, every output element
+ * gets the fused epilogue and one rounding in a GEMM.  A phase without taps
+ * gets the epilogue alone.  When all phases have one shape (strides 1 and 2
+ * among others) they run as one launch.
+ * Library limits: C * element bytes a multiple of 16; (H-1)*sh + dh*(R-1)
+ * + 1, the same along W, and the padding below 2^30; sh*sw <= 4096 phases;
+ * (33*sh*Wo + 32*sw) * F * 2 below 2^31 bytes; each phase's forward problem
+ * within conv2d_fwd_check's size limits (IGC_DECLINE_SIZE_LIMIT).  Dtypes,
+ * alignment and overlap rules as conv2d_fwd.
  *   in_nhwc = {N, H, W, C}, filt_rsfc = {R, S, F, C}, out_nhwc = {N, Ho, Wo, F}
- *   workspace: at least conv2d_transposed_workspace_bytes(), or NULL
- *   (stream-ordered allocation as in conv2d_fwd); source == output is
- *   allowed.
+ *   workspace: at least conv2d_transposed_workspace_bytes() (the phases' NK
+ *   matrices), or NULL (stream-ordered allocation as in conv2d_fwd);
+ *   source == output is allowed.
  * Returns 1 = handled, 0 = declined (conv2d_transposed_check gives the
  * reason), or -(hipError_t).
  */
@@ -396,12 +397,11 @@ int32_t conv2d_transposed_check(const void* input, const int64_t in_nhwc[4],
                                 const igc_epilogue* epilogue,
                                 const void* workspace, size_t workspace_bytes);
 
-/* Workspace conv2d_transposed_fwd needs for this problem (NK matrices, and
- * for stride 2 the phase buffers; with_source = the call passes a source);
- * 0 if the problem would be declined. */
+/* Workspace conv2d_transposed_fwd needs for this problem (the phases' NK
+ * matrices); 0 if the problem would be declined. */
 size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
-                                         const int32_t stride[2], const int32_t padding[2],
-                                         int32_t dtype, int32_t with_source);
+                                         const int32_t stride[2], const int32_t dilation[2],
+                                         const int32_t padding[2], int32_t dtype);
 
 /*
  * General forward convolution: the parameters that page
@@ -427,8 +427,9 @@ size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t
  *              g*C_out/groups), or NULL for a stream-ordered allocation.
  * A problem inside the page's gate (one group, unit dilation, stride (1,1)
  * or (2,2), equal padding 0, 1 or 2 on every side) runs exactly as
- * conv2d_fwd_epilogue; any other runs on the tiled implicit-GEMM kernel,
- * all groups in one launch.  Library limits: Cg * element bytes a multiple
+ * conv2d_fwd_epilogue; one group at unit dilation and stride (1,1) or (2,2)
+ * with other paddings runs on the same forward kernels; any other problem
+ * runs on the tiled implicit-GEMM kernel, all groups in one launch.  Library limits: Cg * element bytes a multiple
  * of 16 (IGC_DECLINE_VECTOR_WIDTH); H + pt + pb, W + pl + pr, dh*(R-1) and
  * dw*(S-1) below 2^30, and conv2d_fwd_check's size limits with Cg for C_in
  * (IGC_DECLINE_SIZE_LIMIT).  Decline codes: STRIDE, DILATION, PADDING,

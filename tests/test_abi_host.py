@@ -287,43 +287,59 @@ def test_transposed_workspace_bytes():
     assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=1, padding=1,
               dtype=torch.bfloat16) == 48 * 328 * 2
     assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=1, padding=1, dtype=9) == 0
-    # stride 2, R = 3, p = 1: phases of 1 and 2 taps per axis at padding 0,
-    # phase outputs 9 or 8 rows/columns; NK rows of K = 32, 64, 64, 128
-    # elements (+8 pad) and bf16 phase buffers, each 256-byte aligned
+
     def al(v):
         return (v + 255) // 256 * 256
+    # stride 2, R = 3, p = 1: row / column phase 0 takes tap 1, phase 1 taps
+    # 0 and 2; NK rows of K = 32, 64, 64, 128 elements (+8 pad), each matrix
+    # 256-byte aligned, and nothing else (no phase buffers)
     want = 0
     for jh, jw in ((1, 1), (1, 2), (2, 1), (2, 2)):
         k = jh * jw * 32
-        kp = (k + 63) // 64 * 64 + 8
-        y = 2 * (10 - jh) * (10 - jw) * 48 * 2
-        want += al(48 * kp * 2) + al(y)
+        want += al(48 * ((k + 63) // 64 * 64 + 8) * 2)
     assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=2, padding=1,
               dtype=torch.bfloat16) == want
-    assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=2, padding=1, dtype=torch.bfloat16,
-              with_source=True) > want
-    assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=3, padding=1, dtype=torch.bfloat16) == 0
+    # stride 3, R = 2, p = 0: phase 2 of each axis has no tap (K = 0: rows of
+    # the 8-element pad alone)
+    want = 0
+    for jh, jw in itertools.product((1, 1, 0), (1, 1, 0)):
+        k = jh * jw * 32
+        want += al(48 * ((k + 63) // 64 * 64 + 8) * 2)
+    assert ws((2, 9, 9, 32), (2, 2, 48, 32), stride=3, padding=0,
+              dtype=torch.bfloat16) == want
+    # dilation 2 at stride 1: one phase, all 9 taps
+    assert ws((2, 9, 9, 32), (3, 3, 48, 32), stride=1, dilation=2, padding=1,
+              dtype=torch.bfloat16) == 48 * 328 * 2
 
 
 @pytest.mark.parametrize("kw,reason", [
     (dict(), "ok"),
     (dict(source=SRC, beta=0.5, scale=SC, activation="silu"), "ok"),
-    (dict(padding=0, out_shape=(2, 11, 11, 48)), "ok"),          # R - 1 - p = 2
+    (dict(padding=0, out_shape=(2, 11, 11, 48)), "ok"),
     (dict(filt_shape=(5, 5, 48, 32), padding=2), "ok"),
     (dict(filt_shape=(4, 4, 48, 32), padding=1, out_shape=(2, 10, 10, 48)), "ok"),
     (dict(stride=2, out_shape=(2, 17, 17, 48)), "ok"),
     (dict(stride=2, padding=2, filt_shape=(4, 4, 48, 32), out_shape=(2, 16, 16, 48)), "ok"),
-    (dict(stride=3, out_shape=(2, 25, 25, 48)), "stride"),
-    (dict(stride=(2, 1), out_shape=(2, 17, 9, 48)), "stride"),
-    (dict(stride=2, filt_shape=(1, 1, 48, 32), padding=0, out_shape=(2, 17, 17, 48)), "shape"),
+    (dict(stride=3, out_shape=(2, 25, 25, 48)), "ok"),
+    (dict(stride=(2, 1), out_shape=(2, 17, 9, 48)), "ok"),
+    (dict(stride=2, filt_shape=(1, 1, 48, 32), padding=0, out_shape=(2, 17, 17, 48)), "ok"),
+    (dict(dilation=2, out_shape=(2, 11, 11, 48)), "ok"),
+    (dict(dilation=(3, 1), stride=2, out_shape=(2, 21, 17, 48)), "ok"),
+    (dict(padding=3, out_shape=(2, 5, 5, 48)), "ok"),
+    (dict(filt_shape=(5, 5, 48, 32), padding=1, out_shape=(2, 11, 11, 48)), "ok"),
+    (dict(filt_shape=(3, 5, 48, 32), out_shape=(2, 9, 11, 48)), "ok"),
+    (dict(padding=(1, 0), out_shape=(2, 9, 11, 48)), "ok"),
     (dict(stride=2, out_shape=(2, 18, 18, 48)), "output_shape"),
     (dict(stride=2, out_shape=(2, 17, 17, 48), workspace=WS, workspace_bytes=1024), "workspace"),
-    (dict(dilation=2), "dilation"),
-    (dict(padding=3), "padding"),                                # R - 1 - p < 0
-    (dict(filt_shape=(5, 5, 48, 32), padding=1, out_shape=(2, 11, 11, 48)), "padding"),
-    (dict(filt_shape=(3, 5, 48, 32)), "padding"),                # R != S
-    (dict(padding=(1, 0)), "padding"),
+    (dict(stride=(0, 1)), "stride"),
+    (dict(dilation=(1, 0)), "dilation"),
+    (dict(padding=(-1, 1)), "padding"),
+    (dict(padding=6), "output_shape"),                           # Ho = 11 - 12 < 1
+    (dict(dilation=2), "output_shape"),                          # Ho is 11
     (dict(filt_shape=(3, 3, 48, 16)), "shape"),
+    (dict(in_shape=(2, 9, 9, 12), filt_shape=(3, 3, 48, 12)), "vector_width"),
+    (dict(in_shape=(1, 1 << 29, 2, 32), stride=(2, 1),
+          out_shape=(1, (1 << 30) - 1, 2, 48)), "size_limit"),  # extent 2^30
     (dict(out_shape=(2, 9, 9, 47)), "output_shape"),
     (dict(out_shape=(2, 10, 10, 48)), "output_shape"),
     (dict(dtype=5), "dtype"),
@@ -334,10 +350,15 @@ def test_transposed_decline_paths(kw, reason):
     assert igc.REASONS[_tcheck(**kw)] == reason
 
 
+def test_transposed_out_hw_matches_oracle_rule():
+    for h, r, st, p, d in itertools.product([1, 5, 9], [1, 2, 3, 5], [1, 2, 3], [0, 1, 2], [1, 2]):
+        ho, _ = igc.transposed_out_hw(h, h, r, r, stride=st, padding=p, dilation=d)
+        assert ho == (h - 1) * st + d * (r - 1) + 1 - 2 * p
+
+
 def test_transposed_declined_call_enqueues_nothing():
-    assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "stride": 3,
-                                                 "out_shape": (2, 25, 25, 48)}) == 0
-    assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "dilation": 2}) == 0
+    assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "stride": (0, 1)}) == 0
+    assert igc.conv2d_transposed_fwd(X, W, Y, **{**TBASE, "dilation": 2}) == 0   # output shape
     args = dict(TBASE, in_shape=(0, 9, 9, 32), out_shape=(0, 9, 9, 48))
     assert igc.conv2d_transposed_fwd(X, W, Y, **args) == 1
 
@@ -641,7 +662,12 @@ def test_general_gate_against_oracle_sizes():
             pl == pr
         name = igc.conv2d_fwd_general_kernel_name(in_shape, filt, out, p, filter_is_fcrs=fcrs,
                                                   dtype=0)
+        fast = g == 1 and (dh, dw) == (1, 1) and sh == sw and sh <= 2
         if got == 0 and not page:
-            assert name == "igemm_fwd_kernel"
+            if fast:   # the forward kernels with per-side padding, never the tap-fold one
+                assert name in ("igemm_fwd_band_kernel", "igemm_fwd_wide_kernel",
+                                "igemm_fwd_resident_kernel", "igemm_fwd_kernel"), name
+            else:
+                assert name == "igemm_fwd_kernel"
         n += 1
     assert n == 192

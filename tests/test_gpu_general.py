@@ -59,7 +59,20 @@ CASES = [
     # everything at once
     ("all_fp16", "float16", 2, 27, 22, 96, 48, 3, 2, (3, 2), (2, 3), (1, 0), (2, 3), 3),
     ("all_fp8", "float8_e4m3fn", 1, 26, 31, 64, 32, 5, 3, (2, 3), (2, 1), (4, 0), (1, 2), 2),
+    # one group, unit dilation, stride 1 or 2, other paddings: the forward
+    # kernels with per-side padding (band, wide, resident)
+    ("fast_band_pad3_bf16", "bfloat16", 2, 20, 22, 64, 64, 3, 3, 1, 1, 3, 3, 1),
+    ("fast_band_tl_fp8", "float8_e4m3fn", 2, 19, 17, 64, 40, 5, 5, 2, 1, (0, 4), (3, 1), 1),
+    ("fast_wide_asym_fp16", "float16", 2, 15, 16, 128, 256, 3, 3, 2, 1, (0, 1), (2, 0), 1),
+    ("fast_wide_big_pad_bf16", "bfloat16", 1, 12, 13, 64, 96, 3, 3, 1, 1, (5, 0), (0, 6), 1),
+    ("fast_resident_bf16", "bfloat16", 2, 9, 11, 96, 16, 3, 3, 1, 1, (1, 0), (0, 2), 1),
 ]
+
+
+def _fast(case):
+    _, _, _, _, _, _, _, _, _, st, dil, _, _, g = case
+    st, dil = _pair(st), _pair(dil)
+    return g == 1 and dil == (1, 1) and st[0] == st[1] and st[0] <= 2
 
 
 def _pair(v):
@@ -101,9 +114,20 @@ def test_general_parity(case):
     cid, dt = case[0], case[1]
     _say(f"general {cid}: {case[2:]}")
     p, oshape, x, wt, _ = _draw(case)
-    assert igc.conv2d_fwd_general_kernel_name(x.shape, wt.shape, oshape, p,
-                                              filter_is_fcrs=False,
-                                              dtype=x.dtype) == "igemm_fwd_kernel"
+    name = igc.conv2d_fwd_general_kernel_name(x.shape, wt.shape, oshape, p, filter_is_fcrs=False,
+                                              dtype=x.dtype)
+    if _fast(case):
+        want = {"fast_band_pad3_bf16": "igemm_fwd_band_kernel",
+                "fast_band_tl_fp8": "igemm_fwd_band_kernel",
+                "fast_wide_asym_fp16": "igemm_fwd_wide_kernel",
+                "fast_wide_big_pad_bf16": "igemm_fwd_wide_kernel",
+                "fast_resident_bf16": "igemm_fwd_resident_kernel"}.get(cid)
+        assert name != "igemm_fwd_tapfold_kernel"
+        if want:
+            assert name == want, name
+    else:
+        assert name == "igemm_fwd_kernel", name
+    _say(f"  kernel {name}")
     out = _run(x, wt, oshape, p, False)
     ref = _oracle(case, x, wt, False)
     err, scale = _assert_close(out, ref, TOL[dt], cid)
@@ -112,7 +136,7 @@ def test_general_parity(case):
 
 @pytest.mark.parametrize("case", [c for c in CASES if c[0] in (
     "dil2_s2_fp8", "g32_resnext_bf16", "g2_fg3_bf16", "all_fp16", "pad_tlbr_fp16",
-    "g2_wide_bf16")], ids=lambda c: c[0])
+    "g2_wide_bf16", "fast_band_tl_fp8", "fast_wide_asym_fp16")], ids=lambda c: c[0])
 def test_general_fcrs_residual_epilogue(case):
     """FCRS filter, a residual source and the fused scale / bias / SiLU, with
     groups offsetting the coefficients; FCRS bits equal RSCF bits."""

@@ -99,8 +99,7 @@ def test_transposed_stride2_in_place_and_workspace():
                                      activation="relu") == 1
     b = sd.clone()
     ws = torch.empty(igc.conv2d_transposed_workspace_bytes(x.shape, wt.shape, stride=st,
-                                                           padding=p, dtype=x.dtype,
-                                                           with_source=True),
+                                                           padding=p, dtype=x.dtype),
                      dtype=torch.uint8, device=DEV)
     assert igc.conv2d_transposed_fwd(xd, wt, b, stride=st, padding=p, source=b, beta=-1.5,
                                      activation="relu", workspace=ws) == 1
@@ -116,9 +115,7 @@ def _tr_sweep():
     cases = []
     for i, (dt, st, r) in enumerate(itertools.product(
             ["bfloat16", "float16", "float8_e4m3fn"], [1, 2], [2, 3, 4, 5])):
-        # paddings the library takes: stride 1 needs R - 1 - p in {0, 1, 2}
-        ps = [p for p in range(0, r) if (st == 2 or 0 <= r - 1 - p <= 2)]
-        p = int(rng.choice(ps))
+        p = int(rng.integers(0, r))
         f = int(rng.choice([3, 8, 24, 64, 96, 136]))
         c = int(rng.choice([16, 32, 64] if dt != "float8_e4m3fn" else [16, 64, 128]))
         h, w = int(rng.integers(3, 14)), int(rng.integers(3, 14))
@@ -136,8 +133,6 @@ def test_transposed_random_sweep(case):
                                        dtype=igc.dtype_code(getattr(torch, dt)),
                                        in_shape=(n, h, w, c), filt_shape=(r, r, f, c),
                                        out_shape=(n, ho, wo, f))
-    if igc.REASONS[code] == "padding":
-        pytest.skip("padding outside what the phase convolutions take")
     assert code == 0, igc.REASONS[code]
     _say(f"transposed sweep {case} -> out {n}x{ho}x{wo}x{f}")
     seed = zlib.crc32(repr(case).encode()) % 1000
@@ -154,3 +149,65 @@ def test_transposed_random_sweep(case):
     torch.cuda.synchronize()
     ref = oracle.conv2d_transposed(x, wt, stride=st, padding=p, **okw)
     _assert_close(out, ref, TOL[dt], str(case))
+
+
+# Strides, dilations, paddings and filter shapes per axis: phases of
+# different shapes (one launch each), phases without taps (epilogue only),
+# dilated phases (the tiled kernel), negative phase paddings (large p).
+# dtype, N, H, W, C, F, (R, S), stride, dilation, padding, fused
+GENERAL = [
+    ("bfloat16", 2, 9, 11, 32, 48, (3, 3), 1, 2, 1, True),          # dilation, stride 1
+    ("float16", 1, 10, 8, 64, 24, (3, 2), 2, (2, 1), (1, 0), True),  # dilated phases
+    ("bfloat16", 2, 7, 6, 32, 40, (3, 3), 3, 1, 1, False),           # stride 3
+    ("float8_e4m3fn", 1, 6, 7, 64, 32, (2, 2), 3, 1, 0, True),       # phases without taps
+    ("bfloat16", 1, 8, 9, 32, 72, (4, 3), (2, 3), 1, (1, 0), True),  # per-axis stride, R != S
+    ("float16", 2, 12, 10, 32, 16, (3, 3), 1, 1, 3, False),          # p > R - 1: cropping
+    ("bfloat16", 1, 9, 9, 64, 96, (5, 5), 2, 1, 4, True),            # negative phase padding
+    ("bfloat16", 2, 10, 10, 32, 8, (1, 1), 2, 1, 0, True),           # 1x1 stride 2: zeros + epilogue
+    ("float8_e4m3fn", 2, 8, 8, 128, 136, (2, 2), 2, 1, 0, True),     # wide kernel, grouped phases
+    ("float16", 1, 7, 9, 64, 64, (3, 5), (3, 2), (2, 1), (2, 1), False),
+]
+
+
+@pytest.mark.parametrize("case", GENERAL, ids=lambda c: "-".join(map(str, c)))
+def test_transposed_general_matches_oracle(case):
+    dt, n, h, w, c, f, (r, s), st, dil, p, fused = case
+    ho, wo = igc.transposed_out_hw(h, w, r, s, stride=st, padding=p, dilation=dil)
+    _say(f"transposed general {case} -> out {n}x{ho}x{wo}x{f}")
+    seed = zlib.crc32(repr(case).encode()) % 1000
+    x, wfwd, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype=dt, fcrs=False,
+                                     x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                     src_dist=("normal", 1.0) if fused else None,
+                                     out_hw=(ho, wo), seed=seed)
+    wt = wfwd.permute(0, 1, 3, 2).contiguous()       # RSFC [R, S, F, C]
+    kw, okw = {}, {}
+    if fused:
+        g = torch.Generator().manual_seed(seed + 1)
+        scale = (torch.rand(f, generator=g) + 0.5).float()
+        bias = torch.randn(f, generator=g).float()
+        kw = dict(source=src.to(DEV), beta=0.75, scale=scale.to(DEV), bias=bias.to(DEV),
+                  activation="relu")
+        okw = dict(source=src, beta=0.75, scale=scale, bias=bias, act="relu")
+    out = igc.conv2d_transposed(x.to(DEV), wt.to(DEV), stride=st, padding=p, dilation=dil, **kw)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (n, ho, wo, f)
+    ref = oracle.conv2d_transposed(x, wt, stride=st, padding=p, dilation=dil, **okw)
+    _assert_close(out, ref, TOL[dt], str(case))
+
+
+def test_transposed_in_place_general():
+    """source == output through the output map (stride 3, phases launched
+    one by one): equal bits to a separate source."""
+    n, h, w, c, f, r, st, p = 1, 7, 8, 32, 24, 4, 3, 1
+    ho, wo = igc.transposed_out_hw(h, w, r, r, stride=st, padding=p)
+    x, wfwd, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=r, dtype="bfloat16",
+                                     fcrs=False, x_dist=("normal", 1.0),
+                                     w_dist=("normal", 0.1), src_dist=("normal", 1.0),
+                                     out_hw=(ho, wo), seed=8)
+    wt = wfwd.permute(0, 1, 3, 2).contiguous().to(DEV)
+    xd, sd = x.to(DEV), src.to(DEV)
+    a = igc.conv2d_transposed(xd, wt, stride=st, padding=p, source=sd, beta=-1.0)
+    b = sd.clone()
+    assert igc.conv2d_transposed_fwd(xd, wt, b, stride=st, padding=p, source=b, beta=-1.0) == 1
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
