@@ -16,6 +16,31 @@
 #include "igemm_host.hpp"
 #include "igemm_aux_kernels.hpp"
 
+namespace igc {
+
+DevInfo device_info() {
+    static std::mutex mu;
+    static bool done[kMaxDevices] = {};
+    static DevInfo info[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DevInfo{};
+    std::lock_guard<std::mutex> g(mu);
+    if (!done[dev]) {
+        int cus = 0, lds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0)
+            info[dev].cus = cus;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) ==
+                hipSuccess &&
+            lds > 0)
+            info[dev].lds = lds < kLdsBytes ? lds : kLdsBytes;
+        done[dev] = true;
+    }
+    return info[dev];
+}
+
+}  // namespace igc
+
 namespace {
 
 using namespace igc;
@@ -208,6 +233,8 @@ hipError_t launch_transpose(const void* filter, int32_t fcrs, const Shape& s, in
     return hipGetLastError();
 }
 
+// The filter-resident kernel applies when the padded NK matrix fits its LDS
+// budget and every wave's gather window (the images its 64 pixels touch)
 // stays below the 2^31-byte buffer range.
 bool resident_ok(const Shape& s, int32_t dtype) {
     if (s.F > 64) return false;
@@ -236,7 +263,7 @@ int band_tn(int64_t blocks_per_wave) {
 // each round of resident workgroups its load time (filter + patch at
 // ~48 B/clk/CU plus a fixed latency) and its MFMA time (32 clk per 32x32
 // block step, one wave per SIMD, TN blocks per wave including padding).
-bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
+bool band_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev) {
     const int64_t E = elem_bytes(dtype);
     const int64_t ksb = dtype == IGC_DTYPE_FP8_E4M3FN ? 64 : 32;
     if (s.F > 64 || s.F < 1 || s.C < 1 || (s.C * E) % ksb != 0) return false;
@@ -252,7 +279,7 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
     const int64_t ppitch = s.C * E + 16;
     const int64_t spitch = tm * 32 + 4;
     const int64_t ksteps = s.R * s.S * (s.C * E / ksb);
-    if (fbytes >= kLdsBytes) return false;
+    if (fbytes >= dev.lds) return false;
     int tws[6], ntw = 0;
     if (s.Wo <= 128) tws[ntw++] = (int)s.Wo;
     for (int c : {128, 64, 32})
@@ -276,12 +303,12 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out) {
             int64_t lds = (fbytes + 1023) / 1024 * 1024 + patch;
             const int64_t stage = P * spitch * 4;
             if (stage > lds) lds = stage;
-            if (lds > kLdsBytes) continue;
+            if (lds > dev.lds) continue;
             const int64_t th_tiles = (s.Ho + th - 1) / th, tw_tiles = (s.Wo + tw - 1) / tw;
             const int64_t tiles = s.N * th_tiles * tw_tiles;
-            const int64_t per_cu = kLdsBytes / lds;
-            const int64_t rounds = (tiles + kNumCUs * per_cu - 1) / (kNumCUs * per_cu);
-            const int64_t conc = tiles < kNumCUs * per_cu ? (tiles + kNumCUs - 1) / kNumCUs : per_cu;
+            const int64_t per_cu = dev.lds / lds;
+            const int64_t rounds = (tiles + dev.cus * per_cu - 1) / (dev.cus * per_cu);
+            const int64_t conc = tiles < dev.cus * per_cu ? (tiles + dev.cus - 1) / dev.cus : per_cu;
             const double load = (double)(fbytes + patch) / 48.0 + 2500.0;
             const double mfma = (double)tn * tm * ksteps * 32.0;
             const double cost = rounds * (load + mfma * (double)conc);
@@ -324,7 +351,7 @@ bool wide_ok(const Shape& s, int32_t dtype) {
 // ppitch (bytes per staged pixel), prow (bytes per ring slot), spitch
 // (floats per partial-product pixel), fpitch (LDS offset of the ring),
 // groups (ring slots).
-bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out) {
+bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev) {
     const int64_t E = elem_bytes(dtype);
     const int64_t ksb = dtype == IGC_DTYPE_FP8_E4M3FN ? 64 : 32;
     const int64_t rs = s.R * s.S;
@@ -351,11 +378,11 @@ bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out) {
         // (measured on the RGB layer: 29.0 us at two per CU with four slots,
         // 24.4 us at three per CU with three slots)
         int64_t nslot = 2;
-        if (fixed + nslot * prow > kLdsBytes || nk_bytes > nslot * prow) continue;
+        if (fixed + nslot * prow > dev.lds || nk_bytes > nslot * prow) continue;
         const int64_t strips = (s.Wo + tw - 1) / tw;
         const int64_t per = s.N * strips;
-        const int64_t per_cu = kLdsBytes / (fixed + nslot * prow);   // workgroups per CU
-        for (int64_t want : {(int64_t)kNumCUs * per_cu, (int64_t)kNumCUs * per_cu * 2}) {
+        const int64_t per_cu = dev.lds / (fixed + nslot * prow);   // workgroups per CU
+        for (int64_t want : {(int64_t)dev.cus * per_cu, (int64_t)dev.cus * per_cu * 2}) {
             int64_t segs = want / per;
             if (segs < 1) segs = 1;
             if (segs > s.Ho) segs = s.Ho;
@@ -363,7 +390,7 @@ bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out) {
             const int64_t tiles_h = (s.Ho + th - 1) / th;
             const int64_t ph = (th - 1) * s.st + s.R;
             const int64_t tiles = per * tiles_h;
-            const int64_t rounds = (tiles + kNumCUs * per_cu - 1) / (kNumCUs * per_cu);
+            const int64_t rounds = (tiles + dev.cus * per_cu - 1) / (dev.cus * per_cu);
             // fewer than four ring slots leave too few rows in flight
             const double cost =
                 rounds * ((double)(ph * prow) / 16.0 + 2500.0 + (nslot < 4 ? 1000.0 : 400.0) * ph);
@@ -384,10 +411,11 @@ enum KernelKind { K_NONE, K_TAPFOLD, K_BAND, K_WIDE, K_RESIDENT, K_TILED };
 
 // tapfold_ok: the tap-fold kernel may be chosen (it has no output map and
 // is only exercised on the page's symmetric paddings).
-KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp, bool tapfold_ok = true) {
+KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp, bool tapfold_ok = true,
+                         const DevInfo& dev = DevInfo{}) {
     if (s.M == 0 || s.F == 0) return K_NONE;
-    if (tapfold_ok && tapfold_plan(s, dtype, bp)) return K_TAPFOLD;
-    if (band_plan(s, dtype, bp)) return K_BAND;
+    if (tapfold_ok && tapfold_plan(s, dtype, bp, dev)) return K_TAPFOLD;
+    if (band_plan(s, dtype, bp, dev)) return K_BAND;
     if (wide_ok(s, dtype)) return K_WIDE;
     if (resident_ok(s, dtype)) return K_RESIDENT;
     return K_TILED;
@@ -485,7 +513,7 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
     }
     const bool resid = source != nullptr;
     BandPlan bp;
-    const KernelKind kind = select_kernel(s, dtype, &bp, tapfold_ok);
+    const KernelKind kind = select_kernel(s, dtype, &bp, tapfold_ok, device_info());
     if (kind == K_NONE) return hipSuccess;
     switch (dtype) {
         case IGC_DTYPE_BF16: return launch_kind<DT_BF16>(kind, resid, a, bp, stream);

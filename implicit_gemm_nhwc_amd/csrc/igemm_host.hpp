@@ -46,6 +46,16 @@ inline int log2_exact(int64_t v) {
     return ((int64_t)1 << l) == v ? l : -1;
 }
 
+// Planning figures of the device a launch runs on: compute units and LDS
+// bytes per CU, looked up once per device (hipDeviceGetAttribute); MI355X's
+// (kNumCUs, kLdsBytes) when the lookup fails, and for host-only queries
+// that make no HIP call (kernel names).
+struct DevInfo {
+    int cus = kNumCUs;
+    int lds = kLdsBytes;
+};
+DevInfo device_info();
+
 struct BandPlan {
     int TH, TW, PH, PW, TN, fpitch, ppitch, prow, spitch, lds, tiles_h, tiles_w;
     int64_t tiles;

@@ -15,7 +15,7 @@ template <int DT, int TM, int TN, int U, bool RESID>
 hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     auto kern = igemm_fwd_band_kernel<DT, TM, TN, U, RESID>;
     static LdsAttr attr;
-    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, kLdsBytes);
+    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)device_info().lds);
     if (attr_err != hipSuccess) return attr_err;
     a.TH = bp.TH; a.TW = bp.TW; a.PH = bp.PH; a.PW = bp.PW;
     a.tiles_h = bp.tiles_h; a.tiles_w = bp.tiles_w;

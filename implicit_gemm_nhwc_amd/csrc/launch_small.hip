@@ -44,9 +44,6 @@ hipError_t launch_resident(ConvArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// The filter-resident kernel applies when the padded NK matrix fits its LDS
-// budget and every wave's gather window (the images its 64 pixels touch)
-
 template <int DT, bool RESID, bool ALIGNED>
 hipError_t launch_resident_tm(const ConvArgs& a, hipStream_t stream) {
     if (a.F <= 16) return launch_resident<DT, 1, RESID, ALIGNED>(a, stream);

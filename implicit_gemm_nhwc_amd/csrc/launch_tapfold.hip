@@ -16,7 +16,7 @@ template <int DT, int KS, bool T3, bool RESID>
 hipError_t launch_tf(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     auto kern = igemm_fwd_tapfold_kernel<DT, KS, T3, RESID>;
     static LdsAttr attr;
-    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, kLdsBytes);
+    const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)device_info().lds);
     if (attr_err != hipSuccess) return attr_err;
     a.TH = bp.TH; a.TW = bp.TW; a.PH = bp.PH; a.PW = bp.PW;
     a.tiles_h = bp.tiles_h; a.tiles_w = bp.tiles_w;

@@ -53,7 +53,7 @@ hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     if (a.groups > 1 || a.ymap)   // grouped or mapped launches: 128 x 128 tiles only
         return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, true, true>(a, stream)
                       : launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, false, true>(a, stream);
-    if (a.F > 128 && px_tiles256 * co_tiles256 >= kNumCUs)
+    if (a.F > 128 && px_tiles256 * co_tiles256 >= device_info().cus)
         return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
                       : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
     return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, true>(a, stream)

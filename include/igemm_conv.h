@@ -210,7 +210,9 @@ int32_t conv2d_fwd_noalloc(const void* input, const int64_t in_nhwc[4],
  * parameters would be declined.  Host-only; pointers play no part (their
  * checks come on top, see conv2d_fwd_check).  A selection rule of this
  * library (page 1 names only its own 4-wave kernel), reported so that
- * profiles and measurements can name what ran.
+ * profiles and measurements can name what ran.  The name is the one for an
+ * MI355X (256 CUs, 160 KB of LDS per CU); a launch plans with the figures
+ * of the device it runs on.
  */
 const char* conv2d_fwd_kernel_name(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
                                    const int64_t filt_dims[4], const int64_t out_nhwc[4],
