@@ -25,6 +25,7 @@ conv2d_materialized(), the write-then-GEMM route (conv2d_filter_to_nk,
 conv2d_im2col, conv2d_fwd_nk on the 1x1 view) kept for measuring what the
 fused gather saves.
 """
+import contextlib
 import ctypes
 import os
 
@@ -32,6 +33,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libigemmconv.so")
+# debug build whose kernels fill their LDS with NaN bytes first (tests only)
+POISON_LIB_PATH = os.path.join(_PKG, "libigemmconv_ldspoison.so")
 
 DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1, torch.float8_e4m3fn: 2}
 OUT_DTYPES = {torch.bfloat16: torch.bfloat16, torch.float16: torch.float16,
@@ -71,21 +74,45 @@ class Declined(RuntimeError):
     pass
 
 
+_libs = {}
+
+
 def lib():
     """The loaded C library with argument types set.  Raises if not built."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Run the binding's calls inside the with-block on another build of the
+    library (the LDS-poison debug build in the tests)."""
+    global _lib
+    prev = lib()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def _load(path):
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
         raise LibraryNotBuilt(
-            f"{LIB_PATH} is missing: build it with "
+            f"{path} is missing: build it with "
             "`python -c 'import __graft_entry__ as g; g.build()'` "
             "(or python implicit_gemm_nhwc_amd/_build.py)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i32, i64p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)
     i32p, f32, sz = ctypes.POINTER(ctypes.c_int32), ctypes.c_float, ctypes.c_size_t
     conv_head = [vp, i64p, vp, i32, i64p, vp, i64p, i32p, i32p, i32p, i32, i32, vp, f32]
     L.conv2d_abi_version.argtypes, L.conv2d_abi_version.restype = [], i32
+    L.conv2d_build_flags.argtypes, L.conv2d_build_flags.restype = [], i32
     L.conv2d_reason_string.argtypes, L.conv2d_reason_string.restype = [i32], ctypes.c_char_p
     L.conv2d_fwd_check.argtypes = conv_head + [vp, sz]
     L.conv2d_fwd_check.restype = i32
@@ -135,7 +162,7 @@ def lib():
     L.conv2d_fwd_general_query.restype = i32
     L.conv2d_fwd_general_kernel_name.argtypes = [i64p, i32, i64p, i64p, prm, i32]
     L.conv2d_fwd_general_kernel_name.restype = ctypes.c_char_p
-    _lib = L
+    _libs[path] = L
     return L
 
 

@@ -1182,6 +1182,14 @@ int32_t conv2d_im2col(const void* input, const int64_t in_nhwc[4], const int64_t
 
 int32_t conv2d_abi_version(void) { return kAbiVersion; }
 
+int32_t conv2d_build_flags(void) {
+#ifdef IGC_LDS_POISON
+    return 1;
+#else
+    return 0;
+#endif
+}
+
 const char* conv2d_reason_string(int32_t reason) {
     switch (reason) {
         case IGC_OK: return "ok";

@@ -102,6 +102,7 @@ struct ConvArgs {
     int gsplit;
     int64_t g_y2, g_src2;
     int g_pt, g_pl;
+    int lds_bytes;      // dynamic LDS of the launch (the poison fill below)
 };
 
 // Workgroup b is placed on XCD b % 8 by the hardware's round-robin
@@ -138,6 +139,23 @@ __device__ __forceinline__ int group_block(ConvArgs& a, int per) {
         a.pl -= gw * a.g_pl;
     }
     return b;
+}
+
+// Debug build (IGC_LDS_POISON): every workgroup first fills its dynamic LDS
+// with 0xFF bytes, a NaN in every element type it holds (bf16, fp16, fp8
+// e4m3fn, fp32), so a read that runs ahead of its data (a missing wait or
+// barrier) shows up as NaN outputs instead of plausible stale values.  The
+// normal build compiles this to nothing.
+template <int NT>
+__device__ __forceinline__ void lds_poison(uint8_t* lds, int bytes) {
+#ifdef IGC_LDS_POISON
+    for (int i = (int)threadIdx.x * 16; i < bytes; i += NT * 16)
+        *reinterpret_cast<i32x4*>(lds + i) = i32x4{-1, -1, -1, -1};
+    __syncthreads();
+#else
+    (void)lds;
+    (void)bytes;
+#endif
 }
 
 // Output pixel index of GEMM pixel (n, oh, ow) under the output map.
@@ -313,6 +331,7 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
     constexpr int STAGE = (BCO + BPX) * KT_BYTES;
 
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    lds_poison<NTHREADS>(lds, a.lds_bytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -557,6 +576,7 @@ __global__ __launch_bounds__(RES_WAVES * 64) void igemm_fwd_resident_kernel(Conv
     constexpr int KT = KT_BYTES / E;
     constexpr int ROWS = TM * 16;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    lds_poison<RES_WAVES * 64>(lds, a.lds_bytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -886,6 +906,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     constexpr int FR = (DT == DT_FP8) ? 2 : 1;      // 16-byte chunks per fragment
     constexpr int NT = BAND_WAVES * 64;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    lds_poison<BAND_WAVES * 64>(lds, a.lds_bytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1272,6 +1293,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
     static_assert(NSTAGE >= 2 && (NSTAGE - 1) * (AI + BI) < 64, "stage count within the wait counter");
     static_assert(CPR == 4 || (AI % 2 == 0 && BI % 2 == 0), "request parity fixed per instruction index");
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    lds_poison<WCO * WPX * 64>(lds, a.lds_bytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;

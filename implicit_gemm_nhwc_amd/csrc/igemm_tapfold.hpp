@@ -60,6 +60,7 @@ __global__ __launch_bounds__(TF_WAVES * 64) void igemm_fwd_tapfold_kernel(ConvAr
     constexpr int FR = (DT == DT_FP8) ? 2 : 1;      // 16-byte chunks per fragment
     constexpr int ODT = (DT == DT_FP16) ? DT_FP16 : DT_BF16;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    lds_poison<TF_WAVES * 64>(lds, a.lds_bytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;

@@ -22,6 +22,7 @@ hipError_t launch_tile(ConvArgs a, hipStream_t stream) {
     a.co_tiles = (a.F + BCO - 1) / BCO;
     const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
     if (blocks == 0) return hipSuccess;
+    a.lds_bytes = (int)lds;
     hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
                        dim3(NTHREADS), lds, stream, a);
     return hipGetLastError();
@@ -39,6 +40,7 @@ hipError_t launch_resident(ConvArgs a, hipStream_t stream) {
     const int64_t wtiles = ((int64_t)a.M + kResidentTN * 16 - 1) / (kResidentTN * 16);
     const int64_t blocks = (wtiles + RES_WAVES - 1) / RES_WAVES;
     if (blocks == 0) return hipSuccess;
+    a.lds_bytes = (int)lds;
     hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
                        dim3(RES_WAVES * 64), lds, stream, a);
     return hipGetLastError();

@@ -24,6 +24,7 @@ hipError_t launch_tf(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     a.patch_off = bp.fpitch;   // the ring starts past the coefficients and NK rows
     a.nslot = bp.groups;
     if (bp.tiles == 0) return hipSuccess;
+    a.lds_bytes = bp.lds;
     hipLaunchKernelGGL(kern, dim3((unsigned)(bp.tiles * (a.groups > 1 ? a.groups : 1))),
                        dim3(TF_WAVES * 64), (size_t)bp.lds, stream, a);
     return hipGetLastError();

@@ -26,6 +26,7 @@ hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
     a.co_tiles = (a.F + BCO - 1) / BCO;
     const int64_t blocks = (int64_t)a.px_tiles * a.co_tiles;
     if (blocks == 0) return hipSuccess;
+    a.lds_bytes = (int)lds;
     hipLaunchKernelGGL(kern, dim3((unsigned)(blocks * (a.groups > 1 ? a.groups : 1))),
                        dim3(WCO * WPX * 64), lds, stream, a);
     return hipGetLastError();

@@ -119,6 +119,12 @@ typedef struct igc_epilogue {
 /* Version of this ABI. */
 int32_t conv2d_abi_version(void);
 
+/* Build flags of this library: bit 0 set in the LDS-poison debug build
+ * (libigemmconv_ldspoison.so), whose kernels first fill their LDS with 0xFF
+ * bytes (NaN in every element type) so that a read running ahead of its data
+ * shows up as NaN outputs; 0 in the normal build. */
+int32_t conv2d_build_flags(void);
+
 /* Human-readable name of a decline reason code (static string). */
 const char* conv2d_reason_string(int32_t reason);
 
