@@ -9,12 +9,15 @@ namespace igc {
 
 // ---------------------------------------------------------------------------
 // Filter transpose to NK (page "dispatch_fused_im2col_conv2d_apple", summary).
-// One thread writes one 16-byte chunk of an NK row; the chunk's elements are
-// VEC channels of one tap (C % VEC == 0), gathered from the stored layout:
+// One thread writes one 16-byte chunk of an NK row, gathered element by
+// element from the stored layout:
 //   RSCF [R,S,C,F]: W(k, co) = w[k*F + co]              (k = (r*S+s)*C + ci)
 //   FCRS [F,C,R,S]: W(k, co) = w[((co*C + ci)*R + r)*S + s]
-// Chunks at or past K are zero.  Consecutive lanes take the stored layout's
-// contiguous direction, so each of a wave's VEC loads touches few lines:
+// When C % VEC == 0 a chunk's VEC elements are channels of one tap, at a
+// fixed stride in the source; otherwise each element finds its own tap.
+// Elements at or past K are zero.  Consecutive lanes take the stored
+// layout's contiguous direction, so each of a wave's VEC loads touches few
+// lines:
 //   RSCF: lanes along co (x), chunks along y;
 //   FCRS: lanes along the chunks of one row (x), rows along y.
 // Grid rows past 65535 loop.  Indices are 32-bit: the NK matrix is below
@@ -30,7 +33,7 @@ __global__ __launch_bounds__(64) void filter_to_nk_kernel(
         const int k0 = chunk * VEC;
         union { i32x4 v; uint8_t b[16]; uint16_t h[8]; } u;
         u.v = i32x4{0, 0, 0, 0};
-        if (k0 < K) {
+        if (k0 < K && C % VEC == 0) {
             const int tap = k0 / C, ci0 = k0 - tap * C;
             const int r = tap / S, s = tap - r * S;
             // VEC independent element loads at a fixed stride, all in flight
@@ -40,6 +43,16 @@ __global__ __launch_bounds__(64) void filter_to_nk_kernel(
             for (int j = 0; j < VEC; ++j) {
                 if (E == 2) u.h[j] = reinterpret_cast<const uint16_t*>(w)[base + j * step];
                 else u.b[j] = w[base + j * step];
+            }
+        } else if (k0 < K) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const int k = k0 + j;
+                const int tap = k / C, ci = k - tap * C;
+                const int r = tap / S, s = tap - r * S;
+                const int idx = k < K ? (fcrs ? ((co * C + ci) * R + r) * S + s : k * F + co) : 0;
+                if (E == 2) u.h[j] = k < K ? reinterpret_cast<const uint16_t*>(w)[idx] : 0;
+                else u.b[j] = k < K ? w[idx] : 0;
             }
         }
         *reinterpret_cast<i32x4*>(nk + ((int64_t)co * kpitch + k0) * E) = u.v;

@@ -109,7 +109,6 @@ int32_t check_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_
     if (out_nhwc[0] != s.N || out_nhwc[1] != s.Ho || out_nhwc[2] != s.Wo || out_nhwc[3] != s.F)
         return IGC_DECLINE_OUTPUT_SHAPE;
     const int64_t eb = elem_bytes(dtype);
-    if ((s.C * eb) % 16 != 0) return IGC_DECLINE_VECTOR_WIDTH;
 
     const int64_t lim = (int64_t)1 << 31;
     if (s.H >= lim || s.W >= lim || s.R >= lim || s.S >= lim || s.C >= lim || s.F >= lim)
@@ -414,6 +413,9 @@ enum KernelKind { K_NONE, K_TAPFOLD, K_BAND, K_WIDE, K_RESIDENT, K_TILED };
 KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp, bool tapfold_ok = true,
                          const DevInfo& dev = DevInfo{}) {
     if (s.M == 0 || s.F == 0) return K_NONE;
+    // C_in not a whole number of 16-byte vectors: only the tiled kernel's
+    // element gather takes it
+    if ((s.C * elem_bytes(dtype)) % 16 != 0) return K_TILED;
     if (tapfold_ok && tapfold_plan(s, dtype, bp, dev)) return K_TAPFOLD;
     if (band_plan(s, dtype, bp, dev)) return K_BAND;
     if (wide_ok(s, dtype)) return K_WIDE;
@@ -549,6 +551,8 @@ int32_t im2col_shape(const int64_t in_nhwc[4], const int64_t filt_rs[2],
     }
     const int32_t rc = check_shapes(in_nhwc, 0, fd, od, stride, dil, padding, 1, dtype, &s);
     if (rc != IGC_OK) return rc;
+    // the im2col kernel moves 16-byte vectors of one tap
+    if ((s.C * eb) % 16 != 0) return IGC_DECLINE_VECTOR_WIDTH;
     if ((s.M * s.kpad * eb) / 16 >= ((int64_t)1 << 31)) return IGC_DECLINE_SIZE_LIMIT;
     *sh = s;
     *kp = s.kpad;
@@ -920,7 +924,6 @@ int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64
     if (out_nhwc[0] != s.N || out_nhwc[1] != s.Ho || out_nhwc[2] != s.Wo || out_nhwc[3] != s.F)
         return IGC_DECLINE_OUTPUT_SHAPE;
     const int64_t eb = elem_bytes(dtype);
-    if ((s.C * eb) % 16 != 0) return IGC_DECLINE_VECTOR_WIDTH;
     // the tiled kernel's 32-bit coordinates: padded extents and dilated
     // filter spans below 2^30 keep every tap's row and column in range
     const int64_t l30 = (int64_t)1 << 30;
@@ -1295,7 +1298,7 @@ int32_t conv2d_filter_to_nk(const void* filter, int32_t filter_is_fcrs, const in
     filter_rscf(filt_dims, filter_is_fcrs, &s.R, &s.S, &s.C, &s.F);
     const int64_t eb = elem_bytes(dtype);
     const int64_t lim = (int64_t)1 << 31;
-    if (s.R < 1 || s.S < 1 || s.C < 0 || s.F < 0 || (s.C * eb) % 16 != 0) return 0;
+    if (s.R < 1 || s.S < 1 || s.C < 0 || s.F < 0) return 0;
     if (s.R >= lim || s.S >= lim || s.C >= lim || s.F >= lim) return 0;
     s.K = s.R * s.S * s.C;
     if (s.K >= lim) return 0;

@@ -314,7 +314,9 @@ __device__ __forceinline__ f32x4 mfma_step<DT_FP8>(const i32x4* a, const i32x4* 
 // (oh*sh - pt + r*dh, ow*sw - pl + s*dw), input pixels lie xpitch elements
 // apart and output pixels ypitch apart, so one launch per channel group (or
 // one grouped launch) covers a grouped convolution.
-template <int DT, int BCO, int BPX, int WCO, int WPX, bool RESID>
+// EG (element gather): C_in * E is not a multiple of 16, so a 16-byte chunk
+// of k can span taps; each of its VEC elements is then gathered on its own.
+template <int DT, int BCO, int BPX, int WCO, int WPX, bool RESID, bool EG = false>
 __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
     constexpr int E = DtTraits<DT>::E;
     constexpr int VEC = 16 / E;            // elements per 16-byte chunk
@@ -392,16 +394,51 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
     i32x4 co_reg[CO_ROWS];
 
     auto load_tile = [&](int kt) {
-        const bool kin = kk < a.K;
-        const int tr = fr * a.dh, ts = fs * a.dw;
-        const int64_t koff = ((int64_t)tr * a.W + ts) * a.xpitch + ci;
+        if constexpr (EG) {
+            // each element k = kk + e of the chunk: its own tap and channel
+            int64_t eoff[VEC];
+            int etr[VEC], ets[VEC];
+            bool ekin[VEC];
 #pragma unroll
-        for (int i = 0; i < PX_ROWS; ++i) {
-            const bool ok = kin && (unsigned)(pih[i] + tr) < (unsigned)a.H &&
-                            (unsigned)(piw[i] + ts) < (unsigned)a.W;
-            i32x4 v = {0, 0, 0, 0};
-            if (ok) v = *reinterpret_cast<const i32x4*>(a.x + (pbase[i] + koff) * E);
-            px_reg[i] = v;
+            for (int e = 0; e < VEC; ++e) {
+                const int k = kk + e;
+                ekin[e] = k < a.K;
+                const int tap = ekin[e] ? k / Cdiv : 0;
+                const int c = ekin[e] ? k - tap * Cdiv : 0;
+                const int r = tap / a.S, sx = tap - r * a.S;
+                etr[e] = r * a.dh;
+                ets[e] = sx * a.dw;
+                eoff[e] = ((int64_t)etr[e] * a.W + ets[e]) * a.xpitch + c;
+            }
+#pragma unroll
+            for (int i = 0; i < PX_ROWS; ++i) {
+                union { i32x4 v; uint16_t h[8]; uint8_t b[16]; } u;
+                u.v = i32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const bool ok = ekin[e] && (unsigned)(pih[i] + etr[e]) < (unsigned)a.H &&
+                                    (unsigned)(piw[i] + ets[e]) < (unsigned)a.W;
+                    if (ok) {
+                        if constexpr (E == 2)
+                            u.h[e] = reinterpret_cast<const uint16_t*>(a.x)[pbase[i] + eoff[e]];
+                        else
+                            u.b[e] = a.x[pbase[i] + eoff[e]];
+                    }
+                }
+                px_reg[i] = u.v;
+            }
+        } else {
+            const bool kin = kk < a.K;
+            const int tr = fr * a.dh, ts = fs * a.dw;
+            const int64_t koff = ((int64_t)tr * a.W + ts) * a.xpitch + ci;
+#pragma unroll
+            for (int i = 0; i < PX_ROWS; ++i) {
+                const bool ok = kin && (unsigned)(pih[i] + tr) < (unsigned)a.H &&
+                                (unsigned)(piw[i] + ts) < (unsigned)a.W;
+                i32x4 v = {0, 0, 0, 0};
+                if (ok) v = *reinterpret_cast<const i32x4*>(a.x + (pbase[i] + koff) * E);
+                px_reg[i] = v;
+            }
         }
 #pragma unroll
         for (int i = 0; i < CO_ROWS; ++i) {
@@ -411,10 +448,12 @@ __global__ __launch_bounds__(NTHREADS) void igemm_fwd_kernel(ConvArgs a) {
         }
         // advance this thread's k decomposition to the next k-tile
         kk += KT;
-        ci += KT;
-        while (ci >= a.C && a.C > 0) {
-            ci -= a.C;
-            if (++fs == a.S) { fs = 0; ++fr; }
+        if constexpr (!EG) {
+            ci += KT;
+            while (ci >= a.C && a.C > 0) {
+                ci -= a.C;
+                if (++fs == a.S) { fs = 0; ++fr; }
+            }
         }
     };
     auto store_tile = [&](int stage) {

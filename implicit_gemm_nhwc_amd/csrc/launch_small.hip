@@ -11,10 +11,10 @@
 namespace igc {
 namespace {
 
-template <int DT, int BCO, int BPX, int WCO, int WPX, bool RESID>
+template <int DT, int BCO, int BPX, int WCO, int WPX, bool RESID, bool EG>
 hipError_t launch_tile(ConvArgs a, hipStream_t stream) {
     constexpr size_t lds = 2 * (size_t)(BCO + BPX) * KT_BYTES;
-    auto kern = igemm_fwd_kernel<DT, BCO, BPX, WCO, WPX, RESID>;
+    auto kern = igemm_fwd_kernel<DT, BCO, BPX, WCO, WPX, RESID, EG>;
     static LdsAttr attr;
     const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)(lds));
     if (attr_err != hipSuccess) return attr_err;
@@ -62,14 +62,21 @@ hipError_t launch_resident_dt(const ConvArgs& a, hipStream_t stream) {
     return launch_resident_tm<DT, RESID, false>(a, stream);
 }
 
-template <int DT, bool RESID>
-hipError_t launch_dt(const ConvArgs& a, hipStream_t stream) {
+template <int DT, bool RESID, bool EG>
+hipError_t launch_dt_eg(const ConvArgs& a, hipStream_t stream) {
     // Tile by C_out: one 16x16 MFMA row block per wave for tiny C_out, up to
     // 128 x 128 workgroup tiles (64 x 64 per wave) for wide layers.
-    if (a.F <= 16) return launch_tile<DT, 16, 256, 1, 4, RESID>(a, stream);
-    if (a.F <= 32) return launch_tile<DT, 32, 256, 1, 4, RESID>(a, stream);
-    if (a.F <= 64) return launch_tile<DT, 64, 256, 1, 4, RESID>(a, stream);
-    return launch_tile<DT, 128, 128, 2, 2, RESID>(a, stream);
+    if (a.F <= 16) return launch_tile<DT, 16, 256, 1, 4, RESID, EG>(a, stream);
+    if (a.F <= 32) return launch_tile<DT, 32, 256, 1, 4, RESID, EG>(a, stream);
+    if (a.F <= 64) return launch_tile<DT, 64, 256, 1, 4, RESID, EG>(a, stream);
+    return launch_tile<DT, 128, 128, 2, 2, RESID, EG>(a, stream);
+}
+
+// C_in (per group) * E not a multiple of 16: the element gather.
+template <int DT, bool RESID>
+hipError_t launch_dt(const ConvArgs& a, hipStream_t stream) {
+    if ((a.C * DtTraits<DT>::E) % 16 != 0) return launch_dt_eg<DT, RESID, true>(a, stream);
+    return launch_dt_eg<DT, RESID, false>(a, stream);
 }
 
 }  // namespace

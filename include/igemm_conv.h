@@ -68,7 +68,10 @@ enum {
     IGC_DECLINE_OUTPUT_SHAPE = 7,  /* Ho or Wo < 1, or out_nhwc is not
                                       {N, Ho, Wo, C_out}                     */
     IGC_DECLINE_VECTOR_WIDTH = 8,  /* C_in * element bytes not a multiple of
-                                      16 (the gather moves 16-byte vectors)  */
+                                      16: im2col and the transposed
+                                      convolution only (they move 16-byte
+                                      vectors); the forward entry points take
+                                      any C_in (an element-wise gather)     */
     IGC_DECLINE_ALIGNMENT = 9,     /* a tensor pointer not 16-byte aligned   */
     IGC_DECLINE_NULL_POINTER = 10, /* NULL pointer for a non-empty tensor,
                                       or NULL shape/parameter array          */
@@ -132,8 +135,8 @@ const char* conv2d_reason_string(int32_t reason);
  * Pointer-free acceptance check of a problem's shapes and parameters (no
  * HIP call): page "dispatch_amd_4wave_conv2d" (Parameters and Args: element
  * types, stride, dilation, symmetric padding, groups, NHWC output shape) plus
- * this library's shape limits (IGC_DECLINE_VECTOR_WIDTH,
- * IGC_DECLINE_SIZE_LIMIT).  Returns IGC_OK or the decline reason; a call
+ * this library's size limits (IGC_DECLINE_SIZE_LIMIT).  Returns IGC_OK or
+ * the decline reason; a call
  * with these shapes is then accepted unless its pointers fail the rules of
  * conv2d_fwd_check (alignment, NULL, overlap, workspace size).
  */
@@ -437,8 +440,10 @@ size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t
  * or (2,2), equal padding 0, 1 or 2 on every side) runs exactly as
  * conv2d_fwd_epilogue; one group at unit dilation and stride (1,1) or (2,2)
  * with other paddings runs on the same forward kernels; any other problem
- * runs on the tiled implicit-GEMM kernel, all groups in one launch.  Library limits: Cg * element bytes a multiple
- * of 16 (IGC_DECLINE_VECTOR_WIDTH); H + pt + pb, W + pl + pr, dh*(R-1) and
+ * runs on the tiled implicit-GEMM kernel, all groups in one launch (as does
+ * any problem whose Cg * element bytes is not a multiple of 16: the tiled
+ * kernel then gathers element by element).  Library limits: H + pt + pb,
+ * W + pl + pr, dh*(R-1) and
  * dw*(S-1) below 2^30, and conv2d_fwd_check's size limits with Cg for C_in
  * (IGC_DECLINE_SIZE_LIMIT).  Decline codes: STRIDE, DILATION, PADDING,
  * GROUPS (groups < 1 or not dividing C_out), SHAPE (C_in != groups * Cg),

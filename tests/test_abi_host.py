@@ -56,6 +56,17 @@ BASE = dict(in_shape=(2, 9, 9, 32), filt_shape=(3, 3, 32, 48), out_shape=(2, 9, 
             filter_is_fcrs=False, stride=1, padding=1, dilation=1, groups=1, dtype=0)
 
 
+def test_element_gather_goes_to_tiled_kernel():
+    """C_in * element bytes not a multiple of 16: accepted, on the tiled
+    kernel's element gather whatever C_out (the vector kernels need whole
+    16-byte channel vectors)."""
+    for c, f, dt in ((3, 64, 0), (12, 16, 1), (8, 256, 2), (1, 3, 0)):
+        name = igc.conv2d_fwd_kernel_name((1, 32, 32, c), (3, 3, c, f), (1, 32, 32, f),
+                                          filter_is_fcrs=False, dtype=dt, stride=1, padding=1)
+        assert name == "igemm_fwd_kernel", (c, f, dt, name)
+    assert igc.conv2d_workspace_bytes((3, 3, 3, 64), False, 0) == 64 * (64 + 8) * 2
+
+
 def _check(**kw):
     args = {**BASE, **kw}
     inp = args.pop("input", X)
@@ -89,8 +100,10 @@ def test_base_case_accepted():
     (dict(out_shape=(2, 8, 9, 48)), "output_shape"),
     (dict(in_shape=(1, 1, 1, 32), filt_shape=(5, 5, 32, 48), padding=1,
           out_shape=(1, 0, 0, 48)), "output_shape"),
-    (dict(in_shape=(2, 9, 9, 12), filt_shape=(3, 3, 12, 48)), "vector_width"),
-    (dict(dtype=2, in_shape=(2, 9, 9, 8), filt_shape=(3, 3, 8, 48)), "vector_width"),
+    # any C_in: the tiled kernel's element gather takes C_in * E % 16 != 0
+    (dict(in_shape=(2, 9, 9, 12), filt_shape=(3, 3, 12, 48)), "ok"),
+    (dict(dtype=2, in_shape=(2, 9, 9, 8), filt_shape=(3, 3, 8, 48)), "ok"),
+    (dict(in_shape=(2, 9, 9, 3), filt_shape=(3, 3, 3, 48)), "ok"),
     (dict(input=X + 8), "alignment"),
     (dict(output=Y + 2), "alignment"),
     (dict(source=SRC + 4), "alignment"),
@@ -588,8 +601,9 @@ def test_general_page_problems_take_conv2d_fwd_kernels(kw):
     (dict(out_shape=(2, 8, 11, 8)), "output_shape"),
     (dict(in_shape=(1, 2, 2, 32), dilation=4, pad_begin=0, pad_end=0,
           out_shape=(1, 0, 0, 8)), "output_shape"),
-    (dict(in_shape=(2, 20, 21, 8), filt_shape=(3, 3, 4, 8)), "vector_width"),
-    (dict(dtype=2, in_shape=(2, 20, 21, 16), filt_shape=(3, 3, 8, 8)), "vector_width"),
+    (dict(in_shape=(2, 20, 21, 8), filt_shape=(3, 3, 4, 8)), "ok"),       # Cg = 4
+    (dict(dtype=2, in_shape=(2, 20, 21, 16), filt_shape=(3, 3, 8, 8)), "ok"),
+    (dict(groups=32, in_shape=(2, 20, 21, 32), filt_shape=(3, 3, 1, 32)), "ok"),   # depthwise
     (dict(input=X + 8), "alignment"),
     (dict(input=0), "null_pointer"),
     (dict(output=X + 1024), "overlap"),

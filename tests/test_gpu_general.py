@@ -59,6 +59,12 @@ CASES = [
     # everything at once
     ("all_fp16", "float16", 2, 27, 22, 96, 48, 3, 2, (3, 2), (2, 3), (1, 0), (2, 3), 3),
     ("all_fp8", "float8_e4m3fn", 1, 26, 31, 64, 32, 5, 3, (2, 3), (2, 1), (4, 0), (1, 2), 2),
+    # channel counts that are not whole 16-byte vectors: element gather
+    ("stem_7x7_s2_p3_c3_bf16", "bfloat16", 2, 37, 41, 3, 64, 7, 7, 2, 1, 3, 3, 1),
+    ("resnext_cg4_fp16", "float16", 2, 14, 15, 128, 128, 3, 3, 1, 1, 1, 1, 32),
+    ("depthwise_bf16", "bfloat16", 2, 19, 18, 32, 32, 3, 3, 1, 1, 1, 1, 32),
+    ("depthwise_x2_s2_fp8", "float8_e4m3fn", 1, 21, 22, 16, 32, 5, 5, 2, 1, 2, 2, 16),
+    ("dil2_c12_fp16", "float16", 1, 16, 17, 12, 20, 3, 3, 1, 2, (2, 1), (2, 3), 1),
     # one group, unit dilation, stride 1 or 2, other paddings: the forward
     # kernels with per-side padding (band, wide, resident)
     ("fast_band_pad3_bf16", "bfloat16", 2, 20, 22, 64, 64, 3, 3, 1, 1, 3, 3, 1),

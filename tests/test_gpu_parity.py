@@ -89,10 +89,9 @@ def _name(dtype):
 @pytest.mark.parametrize("dtype", ["bfloat16", "float16", "float8_e4m3fn"])
 @pytest.mark.parametrize("fcrs", [False, True])
 @pytest.mark.parametrize("r,s,c,f", [(3, 3, 16, 16), (3, 3, 64, 64), (5, 5, 32, 3),
-                                     (1, 1, 48, 17), (3, 2, 128, 5)])
+                                     (1, 1, 48, 17), (3, 2, 128, 5), (3, 3, 3, 16),
+                                     (7, 7, 3, 64), (1, 3, 12, 5), (3, 3, 1, 1)])
 def test_filter_to_nk_bit_exact(dtype, fcrs, r, s, c, f):
-    if dtype == "float8_e4m3fn" and c % 16:
-        pytest.skip("fp8 needs C_in % 16 == 0")
     _say(f"NK transpose {dtype} fcrs={fcrs} R{r} S{s} C{c} F{f}")
     _, w, _ = datagen.make_case(N=1, H=1, W=1, C=c, F=f, R=r, S=s, dtype=dtype, fcrs=fcrs,
                                 x_dist=("normal", 1.0), w_dist=("normal", 1.0), seed=3)
@@ -172,6 +171,14 @@ PATH_CASES = [
     ("fallback_tiled_fp8", "float8_e4m3fn", 1, 12, 12, 48, 64, 5, 5, 1, 2, False, "tiled"),
     ("fallback_tiled_fp8_single", "float8_e4m3fn", 1, 4, 4, 208, 16, 5, 5, 1, 2, True, "tiled"),
     ("wide_fp8_single", "float8_e4m3fn", 1, 4, 4, 64, 96, 3, 3, 1, 1, True, "wide"),
+    # C_in * E not a multiple of 16: the tiled kernel's element gather (taps
+    # spanning a 16-byte chunk of k), any C_out
+    ("eg_bf16_c3", "bfloat16", 2, 20, 22, 3, 64, 3, 3, 1, 1, False, "tiled"),
+    ("eg_fp16_c12_s2", "float16", 1, 17, 19, 12, 24, 3, 3, 2, 1, True, "tiled"),
+    ("eg_fp8_c8", "float8_e4m3fn", 2, 15, 15, 8, 96, 3, 3, 1, 1, True, "tiled"),
+    ("eg_bf16_c1_f3_5x5", "bfloat16", 1, 30, 31, 1, 3, 5, 5, 1, 2, False, "tiled"),
+    ("eg_bf16_c20_f130", "bfloat16", 1, 14, 13, 20, 130, 3, 3, 1, 0, True, "tiled"),
+    ("eg_fp8_c3_s2", "float8_e4m3fn", 1, 33, 31, 3, 16, 3, 3, 2, 2, False, "tiled"),
     ("wide256_fp8_resid", "float8_e4m3fn", 16, 64, 64, 64, 256, 3, 3, 1, 1, True, "wide"),
 ]
 _KERNEL = {"wide": "igemm_fwd_wide_kernel", "band": "igemm_fwd_band_kernel",
