@@ -74,7 +74,9 @@ __global__ __launch_bounds__(64) void filter_to_nk_kernel(
 // host code), so its NK matrix is
 //   NK'[f][(t_h*JW + t_w)*C + c] = W[BH + LH*(JH-1-t_h)][BW + LW*(JW-1-t_w)][f][c]
 // for each (f, t_h, t_w) a contiguous run of C elements of W.  One thread
-// copies one 16-byte chunk (C * E % 16 == 0); chunks at or past K are zero.
+// writes one 16-byte chunk: a single 16-byte copy when C * E % 16 == 0,
+// else element by element (each finding its own tap); elements at or past K
+// are zero.
 struct TapSel {
     int R, S, F, C;    // stored filter
     int BH, BW;        // first tap of the phase along each axis
@@ -101,15 +103,28 @@ __global__ __launch_bounds__(256) void filter_rsfc_to_nk_flipped_kernel(
          g += (int64_t)gridDim.x * 256) {
         const int f = (int)(g / row_chunks), chunk = (int)(g - (int64_t)f * row_chunks);
         const int k0 = chunk * VEC;
-        i32x4 v = {0, 0, 0, 0};
-        if (k0 < t.K) {
-            const int tap = k0 / t.C, c0 = k0 - tap * t.C;
+        auto src_of = [&](int k) {
+            const int tap = k / t.C, c = k - tap * t.C;
             const int th = tap / t.JW, tw = tap - th * t.JW;
             const int r = t.BH + t.LH * (t.JH - 1 - th), sx = t.BW + t.LW * (t.JW - 1 - tw);
-            const int64_t src = ((((int64_t)r * t.S + sx) * t.F + f) * t.C + c0) * E;
-            v = *reinterpret_cast<const i32x4*>(w + src);
+            return (((int64_t)r * t.S + sx) * t.F + f) * t.C + c;   // element index
+        };
+        union { i32x4 v; uint16_t h[8]; uint8_t b[16]; } u;
+        u.v = i32x4{0, 0, 0, 0};
+        if (k0 < t.K && (t.C * E) % 16 == 0) {
+            u.v = *reinterpret_cast<const i32x4*>(w + src_of(k0) * E);
+        } else if (k0 < t.K) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                if (k0 + j < t.K) {
+                    if constexpr (E == 2)
+                        u.h[j] = reinterpret_cast<const uint16_t*>(w)[src_of(k0 + j)];
+                    else
+                        u.b[j] = w[src_of(k0 + j)];
+                }
+            }
         }
-        *reinterpret_cast<i32x4*>(nk + ((int64_t)f * t.kpitch + k0) * E) = v;
+        *reinterpret_cast<i32x4*>(nk + ((int64_t)f * t.kpitch + k0) * E) = u.v;
     }
 }
 

@@ -686,7 +686,6 @@ int32_t transposed_plan(const int64_t in_nhwc[4], const int64_t filt_rsfc[4],
         out_nhwc[2] != t.Wo || out_nhwc[3] != t.F)
         return IGC_DECLINE_OUTPUT_SHAPE;
     const int64_t eb = elem_bytes(dtype);
-    if ((t.C * eb) % 16 != 0) return IGC_DECLINE_VECTOR_WIDTH;
     // the wide kernel places a 32-pixel block's mapped pixels at 32-bit byte
     // offsets from its first one
     if ((33 * t.sh * t.Wo + 32 * (int64_t)t.sw) * t.F * 2 >= lim) return IGC_DECLINE_SIZE_LIMIT;

@@ -68,10 +68,9 @@ enum {
     IGC_DECLINE_OUTPUT_SHAPE = 7,  /* Ho or Wo < 1, or out_nhwc is not
                                       {N, Ho, Wo, C_out}                     */
     IGC_DECLINE_VECTOR_WIDTH = 8,  /* C_in * element bytes not a multiple of
-                                      16: im2col and the transposed
-                                      convolution only (they move 16-byte
-                                      vectors); the forward entry points take
-                                      any C_in (an element-wise gather)     */
+                                      16: conv2d_im2col only (it moves
+                                      16-byte vectors); the convolutions
+                                      take any C_in (an element-wise gather) */
     IGC_DECLINE_ALIGNMENT = 9,     /* a tensor pointer not 16-byte aligned   */
     IGC_DECLINE_NULL_POINTER = 10, /* NULL pointer for a non-empty tensor,
                                       or NULL shape/parameter array          */
@@ -377,7 +376,8 @@ size_t conv2d_im2col_bytes(const int64_t in_nhwc[4], const int64_t filt_rs[2],
  * gets the fused epilogue and one rounding in a GEMM.  A phase without taps
  * gets the epilogue alone.  When all phases have one shape (strides 1 and 2
  * among others) they run as one launch.
- * Library limits: C * element bytes a multiple of 16; (H-1)*sh + dh*(R-1)
+ * Any C (C * element bytes not a multiple of 16: the phases run on the
+ * tiled kernel's element gather).  Library limits: (H-1)*sh + dh*(R-1)
  * + 1, the same along W, and the padding below 2^30; sh*sw <= 4096 phases;
  * (33*sh*Wo + 32*sw) * F * 2 below 2^31 bytes; each phase's forward problem
  * within conv2d_fwd_check's size limits (IGC_DECLINE_SIZE_LIMIT).  Dtypes,

@@ -166,6 +166,10 @@ GENERAL = [
     ("bfloat16", 2, 10, 10, 32, 8, (1, 1), 2, 1, 0, True),           # 1x1 stride 2: zeros + epilogue
     ("float8_e4m3fn", 2, 8, 8, 128, 136, (2, 2), 2, 1, 0, True),     # wide kernel, grouped phases
     ("float16", 1, 7, 9, 64, 64, (3, 5), (3, 2), (2, 1), (2, 1), False),
+    # C * E not a multiple of 16: element-wise flip, phases on the element gather
+    ("bfloat16", 2, 9, 8, 12, 40, (4, 4), 2, 1, 1, True),                # grouped phases
+    ("float8_e4m3fn", 1, 7, 7, 3, 16, (3, 3), 1, 1, 1, False),
+    ("float16", 1, 6, 7, 20, 96, (3, 3), 3, 1, 0, True),
 ]
 
 
