@@ -374,7 +374,9 @@ def measure_general(torch, igc, launches, rotate_bytes=ROTATE_BYTES):
                                      filt_c=c // g)
         per = x.numel() * 2 + n * ho * wo * f * 2
         nsets = min(MAX_SETS, max(1, -(-rotate_bytes // per)))
-        wsb = max(igc.conv2d_workspace_bytes(wt.shape, False, wt.dtype), 16)
+        wsb = max(igc.conv2d_fwd_general_workspace_bytes(x.shape, wt.shape, (n, ho, wo, f), p,
+                                                         filter_is_fcrs=False, dtype=wt.dtype),
+                  16)
         sets = [dict(x=x.to("cuda:0"), w=wt.to("cuda:0"),
                      y=torch.empty((n, ho, wo, f), dtype=torch.bfloat16, device="cuda:0"),
                      ws=torch.empty(wsb, dtype=torch.uint8, device="cuda:0"))

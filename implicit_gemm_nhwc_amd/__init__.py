@@ -17,10 +17,13 @@ Names mirror the C entry points:
   conv2d_epilogue_check,
   conv2d_im2col, conv2d_im2col_bytes,
   conv2d_transposed_fwd, conv2d_transposed_check, conv2d_transposed_workspace_bytes,
+  conv2d_fwd_general, conv2d_fwd_general_check, conv2d_fwd_general_query,
+  conv2d_fwd_general_kernel_name, conv2d_fwd_general_workspace_bytes,
   conv2d_fwd_kernel_name, conv2d_workspace_bytes, conv2d_nk_row_pitch,
-  conv2d_reason_string, conv2d_abi_version
-plus conv2d() and conv2d_transposed(), which allocate the output and call
-conv2d_fwd_epilogue / conv2d_transposed_fwd, and
+  conv2d_build_flags, conv2d_reason_string, conv2d_abi_version
+plus conv2d(), conv2d_general() and conv2d_transposed(), which allocate the
+output and call conv2d_fwd_epilogue / conv2d_fwd_general /
+conv2d_transposed_fwd, and
 conv2d_materialized(), the write-then-GEMM route (conv2d_filter_to_nk,
 conv2d_im2col, conv2d_fwd_nk on the 1x1 view) kept for measuring what the
 fused gather saves.
@@ -162,6 +165,8 @@ def _load(path):
     L.conv2d_fwd_general_query.restype = i32
     L.conv2d_fwd_general_kernel_name.argtypes = [i64p, i32, i64p, i64p, prm, i32]
     L.conv2d_fwd_general_kernel_name.restype = ctypes.c_char_p
+    L.conv2d_fwd_general_workspace_bytes.argtypes = [i64p, i32, i64p, i64p, prm, i32]
+    L.conv2d_fwd_general_workspace_bytes.restype = sz
     _libs[path] = L
     return L
 
@@ -736,6 +741,16 @@ def conv2d_fwd_general_kernel_name(in_shape, filt_shape, out_shape, params, *, f
     return None if name is None else name.decode()
 
 
+def conv2d_fwd_general_workspace_bytes(in_shape, filt_shape, out_shape, params, *,
+                                       filter_is_fcrs, dtype) -> int:
+    """Workspace bytes conv2d_fwd_general needs for this problem (0 when
+    declined)."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(lib().conv2d_fwd_general_workspace_bytes(
+        _i64(in_shape), int(bool(filter_is_fcrs)), _i64(filt_shape), _i64(out_shape),
+        ctypes.byref(params), int(code)))
+
+
 def conv2d_fwd_general_check(input, filter, output, params, *, filter_is_fcrs, source=None,
                              beta=0.0, scale=None, bias=None, activation=None, workspace=None,
                              workspace_bytes=0, dtype=None, in_shape=None, filt_shape=None,
@@ -777,8 +792,9 @@ def conv2d_general(input, filter, *, filter_is_fcrs, stride=1, dilation=1, pad_b
     ho, wo = out_hw_general(h, w, r, s, params)
     out = torch.empty((n, ho, wo, f), dtype=OUT_DTYPES.get(input.dtype, input.dtype),
                       device=input.device)
-    ws = torch.empty(max(conv2d_workspace_bytes(filter.shape, filter_is_fcrs, input.dtype), 16),
-                     dtype=torch.uint8, device=input.device)
+    wsb = conv2d_fwd_general_workspace_bytes(input.shape, filter.shape, out.shape, params,
+                                             filter_is_fcrs=filter_is_fcrs, dtype=input.dtype)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=input.device)
     kw = dict(filter_is_fcrs=filter_is_fcrs, source=source, beta=beta, scale=scale, bias=bias,
               activation=activation, workspace=ws)
     rc = conv2d_fwd_general(input, filter, out, params, stream=stream, **kw)

@@ -67,6 +67,46 @@ __global__ __launch_bounds__(64) void filter_to_nk_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// NK matrix of a grouped convolution run as super-groups: q consecutive
+// channel groups (Cg input, Fg output channels each) form one problem of
+// q*Cg input and q*Fg output channels whose filter is block diagonal:
+//   NK'[co][tap*qCg + c'] = W(tap, c' - j*Cg, co)  if c' / Cg == j,
+//                           0                       otherwise,
+// j = (co % qFg) / Fg the group of co inside its super-group, W the stored
+// filter (RSCF [R][S][Cg][F] or FCRS [F][Cg][R][S]); zero at or past
+// K' = R*S*qCg.  One thread per 16-byte chunk, element by element; grid
+// rows past 65535 loop; 32-bit indices (below 2^31 bytes).
+template <int E>
+__global__ __launch_bounds__(64) void filter_to_nk_blockdiag_kernel(
+    const uint8_t* __restrict__ w, uint8_t* __restrict__ nk, int fcrs, int R, int S, int Cg,
+    int F, int Fg, int q, int kpitch) {
+    constexpr int VEC = 16 / E;
+    const int row_chunks = kpitch / VEC;
+    const int qcg = q * Cg, qfg = q * Fg;
+    const int Kp = R * S * qcg;
+    const int chunk = blockIdx.x * blockDim.x + threadIdx.x;
+    if (chunk >= row_chunks) return;
+    for (int co = blockIdx.y; co < F; co += gridDim.y) {
+        const int j = (co % qfg) / Fg;
+        union { i32x4 v; uint16_t h[8]; uint8_t b[16]; } u;
+        u.v = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int k = chunk * VEC + e;
+            const int tap = k / qcg, cp = k - tap * qcg;
+            const int c = cp - j * Cg;
+            if (k < Kp && c >= 0 && c < Cg) {
+                const int r = tap / S, sx = tap - r * S;
+                const int idx = fcrs ? ((co * Cg + c) * R + r) * S + sx : (tap * Cg + c) * F + co;
+                if constexpr (E == 2) u.h[e] = reinterpret_cast<const uint16_t*>(w)[idx];
+                else u.b[e] = w[idx];
+            }
+        }
+        *reinterpret_cast<i32x4*>(nk + ((int64_t)co * kpitch + chunk * VEC) * E) = u.v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // NK matrices of a transposed convolution's phases (page "conv_transposed_gpu":
 // RSFC filter [R][S][F][C], F output and C input channels).  A phase takes the
 // taps BH + LH*j (j < JH) along the height and BW + LW*j (j < JW) along the

@@ -45,7 +45,7 @@ namespace {
 
 using namespace igc;
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 
 int elem_bytes(int32_t dtype) { return dtype == IGC_DTYPE_FP8_E4M3FN ? 1 : 2; }
 
@@ -262,7 +262,8 @@ int band_tn(int64_t blocks_per_wave) {
 // each round of resident workgroups its load time (filter + patch at
 // ~48 B/clk/CU plus a fixed latency) and its MFMA time (32 clk per 32x32
 // block step, one wave per SIMD, TN blocks per wave including padding).
-bool band_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev) {
+bool band_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev,
+               double* cost_out = nullptr) {
     const int64_t E = elem_bytes(dtype);
     const int64_t ksb = dtype == IGC_DTYPE_FP8_E4M3FN ? 64 : 32;
     if (s.F > 64 || s.F < 1 || s.C < 1 || (s.C * E) % ksb != 0) return false;
@@ -314,6 +315,7 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev)
             if (cost < best) {
                 best = cost;
                 found = true;
+                if (cost_out) *cost_out = cost;
                 *out = BandPlan{(int)th, (int)tw, (int)ph, (int)pw, tn, (int)fpitch, (int)ppitch,
                                 (int)prow, (int)spitch, (int)lds, (int)th_tiles, (int)tw_tiles,
                                 tiles, 0};
@@ -870,10 +872,12 @@ hipError_t run_transposed(const TPlan& t, const void* input, const void* filter,
 // runs exactly as conv2d_fwd.  One group at unit dilation and stride (1,1)
 // or (2,2) with any other padding runs on the same forward kernels (each
 // takes the padding before each axis; the tap-fold kernel is left to the
-// page's paddings).  Any other problem runs on the tiled kernel with its
-// general geometry, the groups as one grouped launch (group g reads input
-// channels g*Cg.., NK rows, output channels, source channels and scale /
-// bias entries g*Fg..).
+// page's paddings).  Several groups at unit dilation and stride (1,1) or
+// (2,2) run as super-groups on the band kernel when its gate admits them
+// (see supergroup_plan).  Any other problem runs on the tiled kernel with
+// its general geometry, the groups as one grouped launch (group g reads
+// input channels g*Cg.., NK rows, output channels, source channels and
+// scale / bias entries g*Fg..).
 struct GShape {
     Shape s;          // C = C_in per group (Cg), F = all output channels
     int64_t cin;      // input channels, groups * Cg
@@ -881,11 +885,62 @@ struct GShape {
     bool page;        // inside the page's gate: conv2d_fwd's kernels run it
     bool fast;        // one group, unit dilation, stride (1,1) or (2,2), any
                       // padding: the forward kernels (but the tap-fold one) run it
+    int32_t q;        // > 0: groups run as super-groups of q (sg below)
+    Shape sg;         // one super-group's problem (C = q*Cg, F = q*Fg, its K,
+                      // kpad and kpitch); N, H, W, Ho, Wo, R, S as s
+    int64_t nk_bytes; // the NK matrix's bytes (all output channels' rows)
 };
 
 int64_t out_size_general(int64_t in, int64_t k, int64_t st, int64_t dil, int64_t pb, int64_t pe) {
     const int64_t span = in + pb + pe - dil * (k - 1) - 1;
     return span < 0 ? 0 : span / st + 1;
+}
+
+// Super-groups: q consecutive channel groups form one problem of q*Cg input
+// and q*Fg output channels whose NK matrix is block diagonal (zero where an
+// input channel's group differs from the output channel's), and the G/q
+// problems run as one grouped launch of the band kernel: each reads its
+// input channels at pixel pitch C_in and writes its output channels at
+// pixel pitch C_out.  The zero blocks cost MFMA work (q times the useful
+// products) but the gathers become whole 16-byte chunks of q*Cg channels,
+// where the tiled kernel's grouped launch gathers Cg channels per pixel.
+// The band kernel's gate applies to the super-group: q*Fg <= 64, q*Cg
+// elements a power-of-two multiple of the MFMA k-step, one image below
+// 2^31 bytes.  q is the divisor of G with the lowest band-kernel cost
+// estimate over the whole grouped launch.
+void supergroup_plan(GShape& t, int32_t dtype, const DevInfo& dev) {
+    const Shape& s = t.s;
+    if (t.groups < 2 || t.dh != 1 || t.dw != 1 || t.sh != t.sw || t.sh > 2) return;
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t fg = s.F / t.groups;
+    if (fg < 1 || s.M == 0 || s.C < 1) return;
+    if (s.H * s.W * t.cin * eb >= lim) return;
+    double best = 1e300;
+    for (int64_t q = 1; q <= t.groups && q * fg <= 64; ++q) {
+        if (t.groups % q) continue;
+        Shape u = s;
+        u.C = q * s.C;
+        u.F = q * fg;
+        u.K = s.R * s.S * u.C;
+        if (u.K >= lim) continue;
+        u.kpad = round_up(u.K, KT_BYTES / eb);
+        u.kpitch = nk_pitch(u.K, u.F, eb);
+        if (u.kpitch >= lim || s.F * u.kpitch * eb >= lim) continue;
+        // plan over the whole grouped launch: G/q times the images
+        Shape pl = u;
+        pl.N = s.N * (t.groups / q);
+        BandPlan bp;
+        double cost = 0;
+        if (!band_plan(pl, dtype, &bp, dev, &cost)) continue;
+        if (bp.tiles >= lim) continue;
+        if (cost < best) {
+            best = cost;
+            t.q = (int32_t)q;
+            t.sg = u;
+        }
+    }
+    if (t.q > 0) t.nk_bytes = s.F * t.sg.kpitch * eb;
 }
 
 int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_dims[4],
@@ -953,6 +1008,9 @@ int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64
                                         dtype, &t.s);
         if (rc != IGC_OK) return rc;
     }
+    t.q = 0;
+    t.nk_bytes = s.F * s.kpitch * eb;
+    if (!t.fast) supergroup_plan(t, dtype, device_info());
     if (g) *g = t;
     return IGC_OK;
 }
@@ -970,7 +1028,7 @@ int32_t check_general(const void* input, const int64_t in_nhwc[4], const void* f
     const size_t in_bytes = (size_t)(s.N * s.H * s.W * g.cin) * eb;
     const size_t f_bytes = (size_t)(s.R * s.S * s.C * s.F) * eb;
     const size_t out_bytes = (size_t)(s.M * s.F) * 2;
-    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * eb;
+    const size_t nk_bytes = (size_t)g.nk_bytes;
     rc = check_pointers(input, in_bytes, filter, f_bytes, output, out_bytes, source, workspace,
                         nk_bytes, workspace_bytes);
     if (rc != IGC_OK) return rc;
@@ -980,8 +1038,63 @@ int32_t check_general(const void* input, const int64_t in_nhwc[4], const void* f
     return IGC_OK;
 }
 
+// The NK matrix of a general problem: the plain transpose (group g's Fg rows
+// from row g*Fg), or the super-groups' block-diagonal one.
+hipError_t launch_general_nk(const void* filter, int32_t fcrs, const GShape& g, int32_t dtype,
+                             void* nk, hipStream_t stream) {
+    if (g.q == 0) return launch_transpose(filter, fcrs, g.s, dtype, nk, stream);
+    const Shape& u = g.sg;
+    const int eb = elem_bytes(dtype);
+    const int64_t row_chunks = u.kpitch / (16 / eb);
+    const int64_t F = g.s.F;
+    if (F == 0 || row_chunks == 0) return hipSuccess;
+    const dim3 grid((unsigned)((row_chunks + 63) / 64), (unsigned)(F < 65535 ? F : 65535));
+    const int fg = (int)(F / g.groups);
+    if (eb == 2)
+        hipLaunchKernelGGL(filter_to_nk_blockdiag_kernel<2>, grid, dim3(64), 0, stream,
+                           (const uint8_t*)filter, (uint8_t*)nk, fcrs, (int)u.R, (int)u.S,
+                           (int)g.s.C, (int)F, fg, (int)g.q, (int)u.kpitch);
+    else
+        hipLaunchKernelGGL(filter_to_nk_blockdiag_kernel<1>, grid, dim3(64), 0, stream,
+                           (const uint8_t*)filter, (uint8_t*)nk, fcrs, (int)u.R, (int)u.S,
+                           (int)g.s.C, (int)F, fg, (int)g.q, (int)u.kpitch);
+    return hipGetLastError();
+}
+
+// The super-groups' grouped launch of the band kernel.
+hipError_t launch_supergroups(const void* input, const void* nk, void* output,
+                              const void* source, float beta, const igc_epilogue* epi,
+                              const GShape& g, int32_t dtype, hipStream_t stream) {
+    const Shape& u = g.sg;
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t ng = g.groups / g.q;
+    Shape pl = u;
+    pl.N = u.N * ng;
+    BandPlan bp;
+    if (!band_plan(pl, dtype, &bp, device_info())) return hipErrorInvalidValue;
+    bp.tiles = u.N * bp.tiles_h * bp.tiles_w;   // per super-group
+    ConvArgs a = base_args(input, nk, output, source, beta, epi, u, dtype);
+    a.xpitch = (int)g.cin;
+    a.ypitch = (int)g.s.F;
+    if (ng > 1) {
+        a.groups = (int)ng;
+        a.g_x = u.C * eb;
+        a.g_nk = u.F * u.kpitch * eb;
+        a.g_y = u.F * 2;
+        a.g_src = source ? u.F * 2 : 0;
+        a.g_c = (int)u.F;
+    }
+    const bool resid = source != nullptr;
+    switch (dtype) {
+        case IGC_DTYPE_BF16: return launch_band_any<DT_BF16>(resid, a, bp, stream);
+        case IGC_DTYPE_FP16: return launch_band_any<DT_FP16>(resid, a, bp, stream);
+        default: return launch_band_any<DT_FP8>(resid, a, bp, stream);
+    }
+}
+
 // The GEMM of a general problem whose NK matrix is in nk (all groups' rows,
-// group g's Fg rows starting at row g*Fg).
+// group g's Fg rows starting at row g*Fg; super-group j's q*Fg rows starting
+// at row j*q*Fg).
 hipError_t launch_general(const void* input, const void* nk, void* output, const void* source,
                           float beta, const igc_epilogue* epi, const GShape& g, int32_t dtype,
                           hipStream_t stream) {
@@ -992,6 +1105,7 @@ hipError_t launch_general(const void* input, const void* nk, void* output, const
     const int64_t eb = elem_bytes(dtype);
     const int64_t fg = s.F / g.groups;
     if (s.M == 0 || fg == 0) return hipSuccess;
+    if (g.q > 0) return launch_supergroups(input, nk, output, source, beta, epi, g, dtype, stream);
     ConvArgs a = base_args(input, nk, output, source, beta, epi, s, dtype);
     a.F = (int)fg;
     a.sh = g.sh; a.sw = g.sw;
@@ -1412,7 +1526,18 @@ const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t fil
             default: return "igemm_fwd_kernel";
         }
     }
-    return (g.s.M == 0 || g.s.F == 0) ? "none" : "igemm_fwd_kernel";
+    if (g.s.M == 0 || g.s.F == 0) return "none";
+    return g.q > 0 ? "igemm_fwd_band_kernel" : "igemm_fwd_kernel";
+}
+
+size_t conv2d_fwd_general_workspace_bytes(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                          const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                                          const igc_conv_params* params, int32_t dtype) {
+    GShape g;
+    if (check_general_shapes(in_nhwc, filter_is_fcrs, filt_dims, out_nhwc, params, dtype, &g) !=
+        IGC_OK)
+        return 0;
+    return (size_t)g.nk_bytes;
 }
 
 int32_t conv2d_fwd_general_query(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
@@ -1447,7 +1572,7 @@ int32_t conv2d_fwd_general(const void* input, const int64_t in_nhwc[4], const vo
         return 0;
     const Shape& s = g.s;
     if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
-    const size_t nk_bytes = (size_t)(s.F * s.kpitch) * (size_t)elem_bytes(dtype);
+    const size_t nk_bytes = (size_t)g.nk_bytes;
     hipStream_t st = (hipStream_t)stream;
     void* nk = workspace;
     bool owned = false;
@@ -1456,7 +1581,7 @@ int32_t conv2d_fwd_general(const void* input, const int64_t in_nhwc[4], const vo
         if (e != hipSuccess) return -(int32_t)e;
         owned = true;
     }
-    hipError_t e = launch_transpose(filter, filter_is_fcrs, s, dtype, nk, st);
+    hipError_t e = launch_general_nk(filter, filter_is_fcrs, g, dtype, nk, st);
     if (e == hipSuccess)
         e = launch_general(input, nk, output, source, beta, epilogue, g, dtype, st);
     if (owned) {

@@ -81,11 +81,12 @@ struct ConvArgs {
     // padding before each axis (top, left), read by every kernel; it may be
     // negative (the output window then starts inside the image)
     int pt, pl;
-    // general geometry, read by the tiled kernel only: per-axis stride,
-    // dilation, and elements per input / output pixel (the whole tensors'
-    // C_in / C_out when a grouped launch runs the channel groups of one
-    // convolution; C and F above are one group's)
+    // general geometry, read by the tiled kernel only: per-axis stride and
+    // dilation
     int sh, sw, dh, dw;
+    // elements per input / output pixel (the whole tensors' C_in / C_out
+    // when a grouped launch runs the channel groups of one convolution; C
+    // and F above are one group's), read by the tiled and band kernels
     int xpitch, ypitch;
     // output map (every kernel but the tap-fold one): GEMM pixel (n, oh, ow)
     // is output pixel (n, oh*ysh, ow*ysw) of an image of Hy x Wy pixels, the
@@ -962,8 +963,9 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     const int ow0 = (trem % a.tiles_w) * a.TW;
     const int ih0 = oh0 * a.stride - a.pt;
     const int iw0 = ow0 * a.stride - a.pl;
-    const int cbytes = a.C * E;  // bytes of one input pixel
-    const int lg = a.cpp_log2;   // log2(chunks per input pixel)
+    const int cbytes = a.C * E;       // bytes of one input pixel's channels (one group's)
+    const int xbytes = a.xpitch * E;  // bytes between input pixels (all groups)
+    const int lg = a.cpp_log2;        // log2(chunks per input pixel)
 
     // ---- phase A: filter rows [frows][fpitch] and the input patch
     // [PH][prow bytes: PW pixels of ppitch bytes, then a row pad] into LDS
@@ -985,7 +987,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         const float inv_spp = 1.0f / (float)spp;
         const int rs = a.prow >> 4;                   // LDS slots per patch row
         const int pblocks = (a.PH * rs + 63) >> 6;
-        const int64_t img = (int64_t)a.H * a.W * cbytes;
+        const int64_t img = (int64_t)a.H * a.W * xbytes;
         const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (int64_t)n * img, (uint32_t)img);
         uint8_t* patch = lds + a.patch_off;
         // slot of this lane in block `wave` as (row, slot in row); advanced
@@ -998,7 +1000,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             const int ih = ih0 + ph, iw = iw0 + pw;
             const bool ok = (pos < cpp) & (pw < a.PW) & (ph < a.PH) &
                             ((unsigned)ih < (unsigned)a.H) & ((unsigned)iw < (unsigned)a.W);
-            const uint32_t off = (uint32_t)((ih * a.W + iw) * cbytes + pos * 16);
+            const uint32_t off = (uint32_t)((ih * a.W + iw) * xbytes + pos * 16);
             // non-temporal: each input line is wanted by this tile and at
             // most its neighbours, which run at the same time, so the patch
             // should not push the filter (read by every workgroup) out of
@@ -1140,7 +1142,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
     fp8_accumulator_margin<DT>();   // the epilogue may read the last MFMA first
     const int th_n = min(a.TH, a.Ho - oh0);
     const int tw_n = min(a.TW, a.Wo - ow0);
-    if ((a.F & 7) == 0) {
+    if (((a.F | a.ypitch) & 7) == 0) {
         // the fused epilogue's coefficients of this lane's channels
         // i*32 + 8*(2k + half) + 0..7, loaded once (16-byte buffer loads; the
         // whole 8-channel group is inside C_out or outside it)
@@ -1177,7 +1179,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             const int p = (wave + BAND_WAVES * t) * 32 + frag_row;
             const int th = p / a.TW, tw = p - (p / a.TW) * a.TW;
             const bool pix_ok = (p < P) & (th < th_n) & (tw < tw_n);
-            const int64_t obase = out_pixel3(a, n, oh0 + th, ow0 + tw) * a.F;
+            const int64_t obase = out_pixel3(a, n, oh0 + th, ow0 + tw) * a.ypitch;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1254,7 +1256,7 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
             const int q = small_div(it, a.F, inv_f), co = it - q * a.F;
             const int th = small_div(q, tw_n, inv_twn), tw = q - th * tw_n;
             float v = stage[(th * a.TW + tw) * a.spitch + co];
-            const int64_t o = out_pixel3(a, n, oh0 + th, ow0 + tw) * a.F + co;
+            const int64_t o = out_pixel3(a, n, oh0 + th, ow0 + tw) * a.ypitch + co;
             if (a.epi) v = epi_pre(a, co, v);
             if constexpr (RESID) v = __builtin_fmaf(a.beta, out_to_f32(a.src[o], ODT), v);
             if (a.epi) v = epi_act(a, v);

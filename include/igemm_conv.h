@@ -433,16 +433,21 @@ size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t
  *   params     stride >= 1, dilation >= 1, padding >= 0 before (top, left)
  *              and after (bottom, right) each axis, groups >= 1 dividing
  *              C_in and C_out.
- *   workspace  conv2d_workspace_bytes(filt_dims, filter_is_fcrs, dtype)
- *              bytes (the NK matrix of all groups, group g's rows at
- *              g*C_out/groups), or NULL for a stream-ordered allocation.
+ *   workspace  conv2d_fwd_general_workspace_bytes(...) bytes for this
+ *              problem (its NK matrix), or NULL for a stream-ordered
+ *              allocation.
  * A problem inside the page's gate (one group, unit dilation, stride (1,1)
  * or (2,2), equal padding 0, 1 or 2 on every side) runs exactly as
  * conv2d_fwd_epilogue; one group at unit dilation and stride (1,1) or (2,2)
- * with other paddings runs on the same forward kernels; any other problem
- * runs on the tiled implicit-GEMM kernel, all groups in one launch (as does
- * any problem whose Cg * element bytes is not a multiple of 16: the tiled
- * kernel then gathers element by element).  Library limits: H + pt + pb,
+ * with other paddings runs on the same forward kernels.  Several groups at
+ * unit dilation and stride (1,1) or (2,2) run as super-groups on the band
+ * kernel where it admits them: q consecutive groups become one problem of
+ * q*Cg input and q*Fg output channels with a block-diagonal NK matrix
+ * (zeros between different groups' channels), q*Fg <= 64 and q*Cg *
+ * element bytes a power-of-two multiple of 32 (64 for fp8).  Any other
+ * problem runs on the tiled implicit-GEMM kernel, all groups in one launch
+ * (as does any problem whose Cg * element bytes is not a multiple of 16:
+ * the tiled kernel then gathers element by element).  Library limits: H + pt + pb,
  * W + pl + pr, dh*(R-1) and
  * dw*(S-1) below 2^30, and conv2d_fwd_check's size limits with Cg for C_in
  * (IGC_DECLINE_SIZE_LIMIT).  Decline codes: STRIDE, DILATION, PADDING,
@@ -490,6 +495,14 @@ const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t fil
                                            const int64_t filt_dims[4],
                                            const int64_t out_nhwc[4],
                                            const igc_conv_params* params, int32_t dtype);
+
+/* Workspace conv2d_fwd_general needs for this problem: the NK matrix, C_out
+ * rows of conv2d_nk_row_pitch's pitch for a K of R*S*Cg (plain groups) or
+ * R*S*q*Cg (super-groups of q); 0 when the problem would be declined. */
+size_t conv2d_fwd_general_workspace_bytes(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                          const int64_t filt_dims[4],
+                                          const int64_t out_nhwc[4],
+                                          const igc_conv_params* params, int32_t dtype);
 
 #ifdef __cplusplus
 }

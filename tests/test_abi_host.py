@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_reason_names():
-    assert igc.conv2d_abi_version() == 4
+    assert igc.conv2d_abi_version() == 5
     for code, name in igc.REASONS.items():
         assert igc.conv2d_reason_string(code) == name
     assert igc.conv2d_reason_string(999) == "unknown"
@@ -677,11 +677,69 @@ def test_general_gate_against_oracle_sizes():
         name = igc.conv2d_fwd_general_kernel_name(in_shape, filt, out, p, filter_is_fcrs=fcrs,
                                                   dtype=0)
         fast = g == 1 and (dh, dw) == (1, 1) and sh == sw and sh <= 2
+        # several groups of 16 bf16 channels (32 bytes, one MFMA k-step):
+        # super-groups on the band kernel
+        sgroups = g > 1 and (dh, dw) == (1, 1) and sh == sw and sh <= 2
         if got == 0 and not page:
             if fast:   # the forward kernels with per-side padding, never the tap-fold one
                 assert name in ("igemm_fwd_band_kernel", "igemm_fwd_wide_kernel",
                                 "igemm_fwd_resident_kernel", "igemm_fwd_kernel"), name
+            elif sgroups:
+                assert name == "igemm_fwd_band_kernel"
             else:
                 assert name == "igemm_fwd_kernel"
         n += 1
     assert n == 192
+
+
+def _nk_bytes(r, s, c, f, dt):
+    return f * igc.conv2d_nk_row_pitch((r, s, c, f), False, dt) * (1 if dt == 2 else 2)
+
+
+@pytest.mark.parametrize("dt", [0, 1, 2])
+def test_general_workspace_bytes(dt):
+    """The general entry's workspace: the plain NK matrix (C_out rows of
+    R*S*Cg) on the tiled path, and C_out rows of R*S*q*Cg (block-diagonal
+    super-groups of q) on the super-group path, with q a divisor of the
+    groups, q * Fg <= 64 and q * Cg * element bytes a power-of-two multiple
+    of 32 (64 for fp8); a smaller workspace is declined."""
+    e = 1 if dt == 2 else 2
+    # tiled path (dilation 2): the plain matrix
+    i, f, o, p, fcrs, _ = _gen(dtype=dt)
+    assert igc.conv2d_fwd_general_workspace_bytes(i, f, o, p, filter_is_fcrs=fcrs,
+                                                  dtype=dt) == _nk_bytes(3, 3, 16, 8, dt)
+    # 32 groups of 8 -> 8 channels, 3x3, 28x28: super-groups
+    i, f, o, p, fcrs, _ = _gen(dtype=dt, in_shape=(4, 28, 28, 256), filt_shape=(3, 3, 8, 256),
+                               stride=1, dilation=1, pad_begin=1, pad_end=1, groups=32)
+    assert igc.conv2d_fwd_general_kernel_name(i, f, o, p, filter_is_fcrs=fcrs,
+                                              dtype=dt) == "igemm_fwd_band_kernel"
+    got = igc.conv2d_fwd_general_workspace_bytes(i, f, o, p, filter_is_fcrs=fcrs, dtype=dt)
+    ksb = 64 if dt == 2 else 32
+    allowed = {_nk_bytes(3, 3, q * 8, q * 8, dt) // (q * 8) * 256
+               for q in (1, 2, 4, 8) if (q * 8 * e) % ksb == 0}
+    assert got in allowed, (got, allowed)
+    assert _gcheck(workspace=WS, workspace_bytes=got, dtype=dt, in_shape=i, filt_shape=f,
+                   out_shape=o, stride=1, dilation=1, pad_begin=1, pad_end=1, groups=32) == 0
+    assert igc.REASONS[_gcheck(workspace=WS, workspace_bytes=got - 16, dtype=dt, in_shape=i,
+                               filt_shape=f, out_shape=o, stride=1, dilation=1, pad_begin=1,
+                               pad_end=1, groups=32)] == "workspace"
+    # declined problem: 0
+    i, f, o, p, fcrs, _ = _gen(dtype=dt, groups=4)
+    assert igc.conv2d_fwd_general_workspace_bytes(i, f, o, p, filter_is_fcrs=fcrs,
+                                                  dtype=dt) == 0
+
+
+@pytest.mark.parametrize("g,cg,fg,dt,want", [
+    (32, 8, 8, 0, "igemm_fwd_band_kernel"),        # ResNeXt-like
+    (64, 1, 2, 0, "igemm_fwd_band_kernel"),        # depthwise, multiplier 2
+    (16, 1, 2, 2, "igemm_fwd_kernel"),             # fp8 depthwise: 16 * 1 byte < 64
+    (2, 64, 128, 0, "igemm_fwd_kernel"),           # Fg > 64
+    (4, 24, 16, 0, "igemm_fwd_kernel"),            # q * 48 bytes never a power of two
+    (8, 16, 16, 2, "igemm_fwd_band_kernel"),       # fp8: q = 4 -> 64 bytes, 64 channels
+])
+def test_general_supergroup_selection(g, cg, fg, dt, want):
+    i, f, o, p, fcrs, _ = _gen(dtype=dt, in_shape=(2, 20, 21, g * cg),
+                               filt_shape=(3, 3, cg, g * fg), stride=1, dilation=1,
+                               pad_begin=1, pad_end=1, groups=g)
+    assert igc.conv2d_fwd_general_kernel_name(i, f, o, p, filter_is_fcrs=fcrs,
+                                              dtype=dt) == want

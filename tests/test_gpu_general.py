@@ -72,7 +72,35 @@ CASES = [
     ("fast_wide_asym_fp16", "float16", 2, 15, 16, 128, 256, 3, 3, 2, 1, (0, 1), (2, 0), 1),
     ("fast_wide_big_pad_bf16", "bfloat16", 1, 12, 13, 64, 96, 3, 3, 1, 1, (5, 0), (0, 6), 1),
     ("fast_resident_bf16", "bfloat16", 2, 9, 11, 96, 16, 3, 3, 1, 1, (1, 0), (0, 2), 1),
+    # several groups, unit dilation, stride 1 or 2: super-groups on the band
+    # kernel (block-diagonal NK matrix, pixel pitch C_in / C_out)
+    ("sg_g32_many_tiles_bf16", "bfloat16", 3, 28, 30, 256, 256, 3, 3, 1, 1, 1, 1, 32),
+    ("sg_g16_fp8", "float8_e4m3fn", 2, 17, 19, 256, 256, 3, 3, 1, 1, 1, 1, 16),
+    ("sg_g4_asym_pad_fp16", "float16", 2, 21, 18, 128, 64, 3, 3, 2, 1, (0, 1), (2, 0), 4),
+    ("sg_depthwise_x2_s2_bf16", "bfloat16", 2, 23, 20, 64, 128, 3, 3, 2, 1, 1, 1, 64),
+    ("sg_depthwise_5x5_fp16", "float16", 1, 19, 33, 96, 96, 5, 5, 1, 1, 2, 2, 96),
+    ("sg_g8_fg6_bf16", "bfloat16", 1, 15, 16, 128, 48, 3, 1, 1, 1, (1, 0), (1, 0), 8),
 ]
+
+ELEM = {"bfloat16": 2, "float16": 2, "float8_e4m3fn": 1}
+
+
+def _supergroup(case):
+    """Whether conv2d_fwd_general runs the case as super-groups on the band
+    kernel: several groups, unit dilation, equal strides of 1 or 2, and some
+    q dividing the groups with q * Fg <= 64 and q * Cg * element bytes a
+    power-of-two multiple of the MFMA k-step (32 bytes, 64 for fp8)."""
+    _, dt, _, _, _, c, f, _, _, st, dil, _, _, g = case
+    st, dil = _pair(st), _pair(dil)
+    if g == 1 or dil != (1, 1) or st[0] != st[1] or st[0] > 2:
+        return False
+    cg, fg, e = c // g, f // g, ELEM[dt]
+    ksb = 64 if e == 1 else 32
+    for q in range(1, g + 1):
+        b = q * cg * e
+        if g % q == 0 and q * fg <= 64 and b % ksb == 0 and (b // 16) & (b // 16 - 1) == 0:
+            return True
+    return False
 
 
 def _fast(case):
@@ -106,7 +134,8 @@ def _oracle(case, x, wt, fcrs, **kw):
 
 def _run(x, wt, out_shape, p, fcrs, **kw):
     out = torch.empty(out_shape, dtype=datagen.OUT_DTYPES[str(x.dtype)[6:]], device=DEV)
-    nb = igc.conv2d_workspace_bytes(wt.shape, fcrs, x.dtype)
+    nb = igc.conv2d_fwd_general_workspace_bytes(x.shape, wt.shape, out_shape, p,
+                                                filter_is_fcrs=fcrs, dtype=x.dtype)
     ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
     rc = igc.conv2d_fwd_general(x.to(DEV), wt.to(DEV), out, p, filter_is_fcrs=fcrs,
                                 workspace=ws, **kw)
@@ -131,6 +160,8 @@ def test_general_parity(case):
         assert name != "igemm_fwd_tapfold_kernel"
         if want:
             assert name == want, name
+    elif _supergroup(case):
+        assert name == "igemm_fwd_band_kernel", name
     else:
         assert name == "igemm_fwd_kernel", name
     _say(f"  kernel {name}")
@@ -142,7 +173,8 @@ def test_general_parity(case):
 
 @pytest.mark.parametrize("case", [c for c in CASES if c[0] in (
     "dil2_s2_fp8", "g32_resnext_bf16", "g2_fg3_bf16", "all_fp16", "pad_tlbr_fp16",
-    "g2_wide_bf16", "fast_band_tl_fp8", "fast_wide_asym_fp16")], ids=lambda c: c[0])
+    "g2_wide_bf16", "fast_band_tl_fp8", "fast_wide_asym_fp16", "sg_g16_fp8",
+    "sg_depthwise_x2_s2_bf16", "sg_g8_fg6_bf16", "depthwise_bf16")], ids=lambda c: c[0])
 def test_general_fcrs_residual_epilogue(case):
     """FCRS filter, a residual source and the fused scale / bias / SiLU, with
     groups offsetting the coefficients; FCRS bits equal RSCF bits."""
@@ -214,3 +246,45 @@ def test_general_dilated_equals_zero_inserted_filter():
     ref = _oracle(case, x, wt, False)
     _assert_close(a, ref, TOL["bfloat16"], "dilated")
     _assert_close(b, ref, TOL["bfloat16"], "zero-inserted")
+
+
+def test_supergroups_in_place_residual_and_repeat():
+    """Super-groups with the output as its own residual source (each output
+    element read once, by the lane that writes it), twice in a row on the
+    same buffers: both calls match the oracle."""
+    case = ("sg_inplace", "bfloat16", 2, 14, 13, 64, 64, 3, 3, 1, 1, 1, 1, 8)
+    assert _supergroup(case)
+    _say("general super-groups in place")
+    p, oshape, x, wt, src = _draw(case, resid=True)
+    y = src.to(DEV).clone()
+    nb = igc.conv2d_fwd_general_workspace_bytes(x.shape, wt.shape, oshape, p,
+                                                filter_is_fcrs=False, dtype=x.dtype)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    xd, wd = x.to(DEV), wt.to(DEV)
+    ref = _oracle(case, x, wt, False, source=src, beta=1.0)
+    for it in range(2):
+        assert igc.conv2d_fwd_general(xd, wd, y, p, filter_is_fcrs=False, source=y, beta=1.0,
+                                      workspace=ws) == 1
+        torch.cuda.synchronize()
+        _assert_close(y, ref, TOL["bfloat16"], f"in place {it}")
+        ref = _oracle(case, x, wt, False, source=y.cpu(), beta=1.0)
+
+
+GENERAL_FULL = [
+    # the general layers the benchmark times, at their full sizes, compared
+    # with the oracle over every output element
+    ("dilated2_3x3_64c_n32", "bfloat16", 32, 56, 56, 64, 64, 3, 3, 1, 2, 2, 2, 1),
+    ("grouped32_3x3_256c_n32", "bfloat16", 32, 28, 28, 256, 256, 3, 3, 1, 1, 1, 1, 32),
+    ("patchify_4x4_s4_8to96_n32", "bfloat16", 32, 224, 224, 8, 96, 4, 4, 4, 1, 0, 0, 1),
+]
+
+
+@pytest.mark.parametrize("case", GENERAL_FULL, ids=lambda c: c[0])
+def test_general_benchmark_layers_full_size(case):
+    cid, dt = case[0], case[1]
+    _say(f"general full size {cid}: {case[2:]}")
+    p, oshape, x, wt, _ = _draw(case)
+    out = _run(x, wt, oshape, p, False)
+    ref = _oracle(case, x, wt, False)
+    err, scale = _assert_close(out, ref, TOL[dt], cid)
+    _say(f"  max|err|/max|ref| = {err / max(scale, 1e-300):.3e}")

@@ -106,3 +106,23 @@ def test_general_and_epilogue_poisoned():
     ref = oracle.conv2d_general(x, wt, filter_is_fcrs=False, source=src, beta=0.25,
                                 scale=scale, bias=bias, act="silu", **kw)
     _assert_close(out, ref, TOL["float16"], "general")
+
+
+def test_supergroups_poisoned():
+    """Grouped channels run as block-diagonal super-groups on the band
+    kernel, with a residual source."""
+    _say("poison super-groups")
+    x, wt, src = datagen.make_case(N=2, H=16, W=15, C=128, F=128, R=3, S=3, dtype="bfloat16",
+                                   fcrs=False, x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0), out_hw=(16, 15), seed=33, filt_c=8)
+    kw = dict(stride=1, dilation=1, pad_begin=1, pad_end=1, groups=16)
+    p = igc.conv_params(**kw)
+    assert igc.conv2d_fwd_general_kernel_name(x.shape, wt.shape, (2, 16, 15, 128), p,
+                                              filter_is_fcrs=False,
+                                              dtype=x.dtype) == "igemm_fwd_band_kernel"
+    with igc.using_library(igc.POISON_LIB_PATH):
+        out = igc.conv2d_general(x.to(DEV), wt.to(DEV), filter_is_fcrs=False, source=src.to(DEV),
+                                 beta=0.5, **kw)
+        torch.cuda.synchronize()
+    ref = oracle.conv2d_general(x, wt, filter_is_fcrs=False, source=src, beta=0.5, **kw)
+    _assert_close(out, ref, TOL["bfloat16"], "super-groups")
