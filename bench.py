@@ -1,8 +1,9 @@
 """Benchmark: forward NHWC convolution as an implicit GEMM on one MI355X.
 
-One step = the whole path on one batch: the filter transpose to NK
-(conv2d_filter_to_nk) and the implicit-GEMM kernel with its fused epilogue
-(conv2d_fwd_nk) -- exactly what conv2d_fwd enqueues.  Each buffer set's step
+One step = the whole path on one batch: one conv2d_fwd call, i.e. the filter
+transpose to NK and the implicit-GEMM kernel with its fused epilogue, or, on
+the band kernel, the one kernel that transposes the stored filter into its
+LDS itself (conv2d_fwd_filter_in_kernel tells which).  Each buffer set's step
 is captured once in a HIP graph (replays checked bit for bit against the
 eager step), and the timed loop replays them, so host-side launch overhead
 does not pace the GPU.
@@ -15,7 +16,8 @@ sets) exceeds the 256 MB Infinity Cache and the L2s, so no step finds its
 operands in cache.
 
 Also reported on the same line:
-  roofline      the GEMM kernel's algorithmic bytes (or FLOPs) per launch over
+  roofline      the GEMM kernel's (on the band kernel: the whole call's one
+                kernel's) algorithmic bytes (or FLOPs) per launch over
                 its mean duration from HIP events around back-to-back launches
                 (queued behind a spin kernel), against the MI355X peak;
   cpu_baseline  the fp64 oracle timed on this host's cores on the same
@@ -105,12 +107,28 @@ class Bufsets:
                 nk=torch.empty(max(nk_bytes, 16), dtype=torch.uint8, device=dev),
                 y=torch.empty((n, ho, wo, f), dtype=out_dt, device=dev),
                 src=None if sd is None else sd.clone()))
+        # whether conv2d_fwd is one kernel that transposes the filter itself
+        # (the band kernel) or a transpose launch followed by the GEMM kernel
+        self.fused = igc.conv2d_fwd_filter_in_kernel(
+            x.shape, w.shape, (n, ho, wo, f), filter_is_fcrs=self.fcrs, dtype=w.dtype,
+            stride=spec["stride"], padding=spec["pad"])
+        # every set's NK matrix, made once, for the rows that run on a given
+        # NK matrix (conv2d_fwd_nk; the fused path leaves it untouched)
+        for i in range(self.nsets):
+            self.transpose(igc, i)
         torch.cuda.synchronize()
 
     def step(self, igc, i):
-        """One step on set i: the filter transpose, then the GEMM kernel."""
-        self.transpose(igc, i)
-        self.fwd_only(igc, i)
+        """One step on set i: the whole conv2d_fwd call (the filter transpose
+        into the set's workspace and the GEMM kernel, or the one kernel that
+        transposes the filter itself)."""
+        b = self.sets[i % self.nsets]
+        sp = self.spec
+        rc = igc.conv2d_fwd(b["x"], b["w"], b["y"], filter_is_fcrs=self.fcrs,
+                            stride=sp["stride"], padding=sp["pad"], source=b["src"],
+                            beta=sp["beta"], workspace=b["nk"])
+        if rc != 1:
+            raise RuntimeError(f"conv2d_fwd returned {rc}")
 
     def transpose(self, igc, i):
         """The filter transpose of set i into its NK matrix."""
@@ -120,7 +138,11 @@ class Bufsets:
             raise RuntimeError(f"conv2d_filter_to_nk returned {rc}")
 
     def fwd_only(self, igc, i):
-        """The GEMM kernel alone on set i (its NK matrix already made)."""
+        """The GEMM kernel alone on set i: conv2d_fwd when that is one kernel,
+        else conv2d_fwd_nk on the set's NK matrix."""
+        if self.fused:
+            self.step(igc, i)
+            return
         b = self.sets[i % self.nsets]
         sp = self.spec
         rc = igc.conv2d_fwd_nk(b["x"], b["nk"], b["w"].shape, b["y"], filter_is_fcrs=self.fcrs,
@@ -179,8 +201,9 @@ class Bufsets:
 
 
 def kernel_times(torch, igc, bufs, launches):
-    """Mean duration of conv2d_fwd_nk from HIP events on the launch stream
-    around `launches` back-to-back launches (rotating sets).  A spin kernel
+    """Mean duration of the GEMM kernel (Bufsets.fwd_only: conv2d_fwd_nk, or
+    conv2d_fwd when that is the one kernel) from HIP events on the launch
+    stream around `launches` back-to-back launches (rotating sets).  A spin kernel
     holds the stream while the host enqueues them, so the GPU never waits on
     the host inside the bracket (host-side launch latency would otherwise
     count as kernel time); no event sits between the launches."""
@@ -239,6 +262,12 @@ def measure_next(torch, igc, launches, rotate_bytes=ROTATE_BYTES):
 
     def epi(i):
         b = bufs.sets[i % bufs.nsets]
+        if bufs.fused:   # the same one kernel as the plain call, with the epilogue
+            _ok(igc.conv2d_fwd_epilogue(b["x"], b["w"], b["y"], filter_is_fcrs=bufs.fcrs,
+                                        stride=spec["stride"], padding=spec["pad"],
+                                        scale=scale, bias=bias, activation="relu",
+                                        workspace=b["nk"]), "conv2d_fwd_epilogue")
+            return
         _ok(igc.conv2d_fwd_nk_epilogue(b["x"], b["nk"], b["w"].shape, b["y"],
                                        filter_is_fcrs=bufs.fcrs, stride=spec["stride"],
                                        padding=spec["pad"], scale=scale, bias=bias,
@@ -440,7 +469,10 @@ def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES, graphs=T
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern_ms = kernel_times(torch, igc, bufs, steps)
-    transpose_us = event_time(torch, lambda i: bufs.transpose(igc, i), steps)
+    # the transpose launch a step makes (none when the kernel transposes the
+    # filter itself)
+    transpose_us = 0.0 if bufs.fused else event_time(torch, lambda i: bufs.transpose(igc, i),
+                                                     steps)
     flops, nbytes = _algorithmic(spec)
     ms_step = (t1 - t0) * 1e3 / steps
     bound, peak_t = _bound(spec, flops, nbytes)
@@ -449,7 +481,7 @@ def measure(torch, igc, name, steps, warmup, rotate_bytes=ROTATE_BYTES, graphs=T
                kernel_us_mean=kern_ms * 1e3, transpose_us_mean=transpose_us,
                kernel_tflops=flops / (kern_ms * 1e-3) / 1e12,
                kernel_gbs=nbytes / (kern_ms * 1e-3) / 1e9, flops=flops, alg_bytes=nbytes,
-               bound=bound, rotating_sets=bufs.nsets,
+               bound=bound, rotating_sets=bufs.nsets, filter_in_kernel=bufs.fused,
                steps_per_graph=per_graph if graphs else 0)
     res["frac_mfma"] = res["kernel_tflops"] / peak_t
     res["frac_hbm"] = res["kernel_gbs"] / PEAK["hbm_gbs"]

@@ -19,8 +19,8 @@ Names mirror the C entry points:
   conv2d_transposed_fwd, conv2d_transposed_check, conv2d_transposed_workspace_bytes,
   conv2d_fwd_general, conv2d_fwd_general_check, conv2d_fwd_general_query,
   conv2d_fwd_general_kernel_name, conv2d_fwd_general_workspace_bytes,
-  conv2d_fwd_kernel_name, conv2d_workspace_bytes, conv2d_nk_row_pitch,
-  conv2d_build_flags, conv2d_reason_string, conv2d_abi_version
+  conv2d_fwd_kernel_name, conv2d_fwd_filter_in_kernel, conv2d_workspace_bytes,
+  conv2d_nk_row_pitch, conv2d_build_flags, conv2d_reason_string, conv2d_abi_version
 plus conv2d(), conv2d_general() and conv2d_transposed(), which allocate the
 output and call conv2d_fwd_epilogue / conv2d_fwd_general /
 conv2d_transposed_fwd, and
@@ -132,6 +132,9 @@ def _load(path):
     L.conv2d_nk_row_pitch.restype = ctypes.c_int64
     L.conv2d_fwd_kernel_name.argtypes = [i64p, i32, i64p, i64p, i32p, i32p, i32p, i32, i32]
     L.conv2d_fwd_kernel_name.restype = ctypes.c_char_p
+    L.conv2d_fwd_filter_in_kernel.argtypes = [i64p, i32, i64p, i64p, i32p, i32p, i32p, i32,
+                                              i32]
+    L.conv2d_fwd_filter_in_kernel.restype = i32
     L.conv2d_filter_to_nk.argtypes = [vp, i32, i64p, i32, vp, sz, vp]
     L.conv2d_filter_to_nk.restype = i32
     epip = ctypes.POINTER(IgcEpilogue)
@@ -352,6 +355,18 @@ def conv2d_fwd_kernel_name(in_shape, filt_shape, out_shape, *, filter_is_fcrs, d
                                         _pair(dilation), _pair(padding), int(groups),
                                         int(code))
     return None if name is None else name.decode()
+
+
+def conv2d_fwd_filter_in_kernel(in_shape, filt_shape, out_shape, *, filter_is_fcrs, dtype,
+                                stride=1, padding=0, dilation=1, groups=1) -> bool:
+    """Whether conv2d_fwd runs these shapes as one kernel launch that
+    transposes the stored filter itself (no NK matrix, workspace untouched).
+    Host-only."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return bool(lib().conv2d_fwd_filter_in_kernel(_i64(in_shape), int(bool(filter_is_fcrs)),
+                                                  _i64(filt_shape), _i64(out_shape),
+                                                  _pair(stride), _pair(dilation),
+                                                  _pair(padding), int(groups), int(code)))
 
 
 def conv2d_fwd(input, filter, output, *, filter_is_fcrs, stride=1, padding=0, dilation=1,

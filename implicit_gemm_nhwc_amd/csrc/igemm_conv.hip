@@ -261,7 +261,8 @@ int band_tn(int64_t blocks_per_wave) {
 // C_in not a power-of-two number of MFMA k-steps).  The estimate charges
 // each round of resident workgroups its load time (filter + patch at
 // ~48 B/clk/CU plus a fixed latency) and its MFMA time (32 clk per 32x32
-// block step, one wave per SIMD, TN blocks per wave including padding).
+// block step, band_waves / 4 waves per SIMD with TN blocks each, padding
+// included).
 bool band_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev,
                double* cost_out = nullptr) {
     const int64_t E = elem_bytes(dtype);
@@ -270,6 +271,7 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev,
     if (log2_exact(s.C * E / 16) < 0) return false;
     if (s.H * s.W * s.C * E >= ((int64_t)1 << 31)) return false;
     const int64_t tm = s.F <= 32 ? 1 : 2;
+    const int64_t waves = band_waves(dtype == IGC_DTYPE_FP8_E4M3FN ? DT_FP8 : DT_BF16);
     const int64_t fpitch = s.kpitch * E;
     // filter rows kept in LDS: C_out real rows plus one zero row that the
     // fragment reads of rows >= C_out all point at (up to the TM*32 rows the
@@ -288,9 +290,9 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev,
     bool found = false;
     for (int k = 0; k < ntw; ++k) {
         const int64_t tw = tws[k];
-        for (int64_t th = 1; th <= s.Ho && th * tw <= 32 * BAND_MAX_TN * BAND_WAVES; ++th) {
+        for (int64_t th = 1; th <= s.Ho && th * tw <= 32 * BAND_MAX_TN * waves; ++th) {
             const int64_t P = th * tw, NB = (P + 31) / 32;
-            const int tn = band_tn((NB + BAND_WAVES - 1) / BAND_WAVES);
+            const int tn = band_tn((NB + waves - 1) / waves);
             if (tn == 0) continue;
             const int64_t ph = (th - 1) * s.st + s.R, pw = (tw - 1) * s.st + s.S;
             // row pad: (prow - tw * ppitch) % 256 == 0, so the 16 lanes of a
@@ -310,7 +312,7 @@ bool band_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& dev,
             const int64_t rounds = (tiles + dev.cus * per_cu - 1) / (dev.cus * per_cu);
             const int64_t conc = tiles < dev.cus * per_cu ? (tiles + dev.cus - 1) / dev.cus : per_cu;
             const double load = (double)(fbytes + patch) / 48.0 + 2500.0;
-            const double mfma = (double)tn * tm * ksteps * 32.0;
+            const double mfma = (double)tn * (waves / 4) * tm * ksteps * 32.0;
             const double cost = rounds * (load + mfma * (double)conc);
             if (cost < best) {
                 best = cost;
@@ -491,11 +493,16 @@ ConvArgs base_args(const void* input, const void* nk, void* output, const void* 
     return a;
 }
 
+// wraw: the stored filter (RSCF, or FCRS when wfcrs), passed instead of an
+// NK matrix to a problem for which filter_in_kernel holds.
 hipError_t launch_igemm(const void* input, const void* nk, void* output, const void* source,
                         float beta, const igc_epilogue* epi, const Shape& s, int32_t dtype,
                         hipStream_t stream, const Group* grp = nullptr, bool tapfold_ok = true,
-                        const OutMap* map = nullptr) {
+                        const OutMap* map = nullptr, const void* wraw = nullptr,
+                        int32_t wfcrs = 0) {
     ConvArgs a = base_args(input, nk, output, source, beta, epi, s, dtype);
+    a.wraw = (const uint8_t*)wraw;
+    a.wrs = wfcrs ? (int)(s.R * s.S) : 0;
     if (grp && grp->n > 1) {
         a.groups = grp->n;
         a.g_nk = grp->nk;
@@ -519,11 +526,27 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
     BandPlan bp;
     const KernelKind kind = select_kernel(s, dtype, &bp, tapfold_ok, device_info());
     if (kind == K_NONE) return hipSuccess;
+    if (wraw && kind != K_BAND) return hipErrorInvalidValue;
     switch (dtype) {
         case IGC_DTYPE_BF16: return launch_kind<DT_BF16>(kind, resid, a, bp, stream);
         case IGC_DTYPE_FP16: return launch_kind<DT_FP16>(kind, resid, a, bp, stream);
         default: return launch_kind<DT_FP8>(kind, resid, a, bp, stream);
     }
+}
+
+// One launch instead of two: the band kernel transposes the stored filter
+// into its LDS itself, so no NK matrix and no transpose launch are needed.
+// Its register transposes take whole 16-byte loads of 2-byte elements
+// (bf16, fp16): an RSCF filter needs C_out a multiple of 8, an FCRS filter
+// R*S of 1, 9 or 25 (the register transposes are built for those tap
+// counts: 1x1, 3x3, 5x5 filters).
+bool filter_in_kernel(const Shape& s, int32_t dtype, int32_t fcrs, bool tapfold_ok = true) {
+    const int64_t vec = 16 / elem_bytes(dtype);
+    if (s.M == 0 || s.F == 0 || dtype == IGC_DTYPE_FP8_E4M3FN) return false;
+    if (fcrs ? !(s.R * s.S == 1 || s.R * s.S == 9 || s.R * s.S == 25) : s.F % vec != 0)
+        return false;
+    BandPlan bp;
+    return select_kernel(s, dtype, &bp, tapfold_ok, device_info()) == K_BAND;
 }
 
 FastDiv make_fastdiv(uint32_t d) {
@@ -1471,6 +1494,9 @@ int32_t conv2d_fwd_epilogue(const void* input, const int64_t in_nhwc[4], const v
     if (check_epilogue(epilogue, output, s, workspace, nk_bytes) != IGC_OK) return 0;
     if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
     hipStream_t st = (hipStream_t)stream;
+    if (filter_in_kernel(s, dtype, filter_is_fcrs))
+        return hip_fail(launch_igemm(input, nullptr, output, source, beta, epilogue, s, dtype, st,
+                                     nullptr, true, nullptr, filter, filter_is_fcrs));
     void* nk = workspace;
     bool owned = false;
     if (!nk && nk_bytes) {
@@ -1530,6 +1556,17 @@ const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t fil
     return g.q > 0 ? "igemm_fwd_band_kernel" : "igemm_fwd_kernel";
 }
 
+int32_t conv2d_fwd_filter_in_kernel(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                    const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                                    const int32_t stride[2], const int32_t dilation[2],
+                                    const int32_t padding[2], int32_t groups, int32_t dtype) {
+    Shape s;
+    if (check_shapes(in_nhwc, filter_is_fcrs, filt_dims, out_nhwc, stride, dilation, padding,
+                     groups, dtype, &s) != IGC_OK)
+        return 0;
+    return filter_in_kernel(s, dtype, filter_is_fcrs) ? 1 : 0;
+}
+
 size_t conv2d_fwd_general_workspace_bytes(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
                                           const int64_t filt_dims[4], const int64_t out_nhwc[4],
                                           const igc_conv_params* params, int32_t dtype) {
@@ -1574,6 +1611,9 @@ int32_t conv2d_fwd_general(const void* input, const int64_t in_nhwc[4], const vo
     if (s.M == 0 || s.F == 0) return 1;  // empty output: nothing to compute
     const size_t nk_bytes = (size_t)g.nk_bytes;
     hipStream_t st = (hipStream_t)stream;
+    if (g.fast && filter_in_kernel(s, dtype, filter_is_fcrs, g.page))
+        return hip_fail(launch_igemm(input, nullptr, output, source, beta, epilogue, s, dtype, st,
+                                     nullptr, g.page, nullptr, filter, filter_is_fcrs));
     void* nk = workspace;
     bool owned = false;
     if (!nk && nk_bytes) {

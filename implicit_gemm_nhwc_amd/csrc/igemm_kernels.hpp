@@ -45,6 +45,11 @@ template <> struct DtTraits<DT_FP8> { static constexpr int E = 1; };
 struct ConvArgs {
     const uint8_t* x;   // NHWC input
     const uint8_t* nk;  // [C_out][kpitch] transposed filter, zero past K
+    // band kernel only: when set, the stored filter that the kernel
+    // transposes into its LDS itself (nk is then unused): RSCF [R][S][C][F]
+    // when wrs == 0, else FCRS [F][C][R][S] with R*S == wrs (1, 9 or 25)
+    const uint8_t* wraw;
+    int wrs;
     uint16_t* y;        // NHWC output (bf16 or fp16 bits)
     const uint16_t* src;  // residual source, same layout and type as y
     float beta;
@@ -892,8 +897,13 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 template <int V>
 struct IntC { static constexpr int value = V; };
 
-constexpr int BAND_WAVES = 4;
-constexpr int BAND_MAX_TN = 4;   // 32-pixel blocks per wave at most (tile <= 512 px)
+// Band kernel waves: eight for bf16 / fp16, two per SIMD, so while one
+// waits on its LDS fragment reads the other multiplies (measured on the
+// ResNet 3x3 layer: 16.3 -> 14.9 us against four waves with the same
+// tiles, identical bits); four for fp8, whose twice-as-wide fragments need
+// more than the 256 registers a wave has at two waves per SIMD.
+constexpr int band_waves(int dt) { return dt == DT_FP8 ? 4 : 8; }
+constexpr int BAND_MAX_TN = 4;   // 32-pixel blocks per wave at most
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -922,6 +932,107 @@ __device__ __forceinline__ f32x16 mfma32<DT_FP8>(const i32x4* a, const i32x4* b,
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
 }
 
+// The band kernel's filter rows made from the stored filter in the kernel,
+// instead of by a separate transpose launch: NK row co at LDS byte
+// co*fpitch, k = (r*S + s)*C_in + c at byte k*E (VEC = 16 / E elements per
+// 16-byte chunk).  The stored filter is read in whole 16-byte loads and
+// transposed in registers:
+//  * RSCF [K][F] (RS == 0): block (kb, cb) = VEC x VEC elements, rows
+//    k = kb*VEC.. of VEC output channels cb*VEC..; its VEC loads (one per
+//    k) become the VEC output channels' chunks at k = kb*VEC (needs C_out a
+//    multiple of VEC);
+//  * FCRS [F][C][R][S] with R*S == RS: block (co, cb) = the RS taps of VEC
+//    input channels cb*VEC.. of output channel co, RS contiguous loads in
+//    (c, tap) order; tap t's chunk holds elements j*RS + t, j < VEC.
+// K is a whole number of VEC (the band kernel's C_in * E is a multiple of
+// 32).  Consecutive threads take consecutive blocks (adjacent addresses).
+// load issues one round's loads (NB blocks per thread); store writes them
+// once they have arrived.  The pad k >= K of each row is left as it is (the
+// MFMA loop never reads it).
+template <int E, int NT, int RS>
+struct FilterGather {
+    static constexpr int VEC = 16 / E;
+    static constexpr int NL = RS == 0 ? VEC : RS;              // loads per block
+    static constexpr int NB = (RS == 0 && E == 2) ? 2 : 1;     // blocks per thread per round
+    union Block {
+        i32x4 w[NL];
+        uint16_t h[NL * 8];
+        uint8_t b[NL * 16];
+    };
+    int nblk, ncb;
+    float inv_ncb;
+    __amdgpu_buffer_rsrc_t rs;
+    Block v[NB];
+
+    __device__ __forceinline__ void init(const ConvArgs& a) {
+        ncb = (RS == 0 ? a.F : a.C) / VEC;
+        nblk = RS == 0 ? (a.K / VEC) * ncb : a.F * ncb;
+        inv_ncb = 1.0f / (float)ncb;
+        rs = make_rsrc(a.wraw, (uint32_t)(a.F * a.K * E));
+    }
+    __device__ __forceinline__ void load(const ConvArgs& a, int b0) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            const int b = b0 + n * NT;
+            if (b < nblk) {
+                const int hi = small_div(b, ncb, inv_ncb), lo = b - hi * ncb;
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    const unsigned off = RS == 0
+                        ? (unsigned)(((hi * VEC + i) * a.F + lo * VEC) * E)
+                        : (unsigned)((hi * a.C + lo * VEC) * RS * E + i * 16);
+                    v[n].w[i] = __builtin_bit_cast(
+                        i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(const ConvArgs& a, uint8_t* lds, int b0) const {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            const int b = b0 + n * NT;
+            if (b >= nblk) continue;
+            const int hi = small_div(b, ncb, inv_ncb), lo = b - hi * ncb;
+            constexpr int NOUT = RS == 0 ? VEC : RS;     // chunks per block
+#pragma unroll
+            for (int t = 0; t < NOUT; ++t) {
+                Block c;   // only c.w[0] used
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    // RSCF: chunk of channel lo*VEC + t holds k = hi*VEC + j
+                    // (load j, element t); FCRS: chunk of tap t holds input
+                    // channel lo*VEC + j (block element j*RS + t)
+                    const int src = RS == 0 ? j * VEC + t : j * RS + t;
+                    if constexpr (E == 2) c.h[j] = v[n].h[src];
+                    else c.b[j] = v[n].b[src];
+                }
+                const int off = RS == 0 ? (lo * VEC + t) * a.fpitch + hi * VEC * E
+                                        : hi * a.fpitch + (t * a.C + lo * VEC) * E;
+                *reinterpret_cast<i32x4*>(lds + off) = c.w[0];
+            }
+        }
+    }
+};
+
+// Phase A's filter rows from the stored filter (FilterGather), after the
+// patch DMA (issue_patch): the patch's requests, mostly to HBM, go out
+// first, the filter's L2 reads behind them, as on the NK path (measured on
+// the ResNet 3x3 layer: 16.3 -> 15.5 us against the filter loads first).
+template <int E, int NT, int RS, class PatchFn>
+__device__ __forceinline__ void gather_filter(const ConvArgs& a, uint8_t* lds, int tid,
+                                              PatchFn issue_patch) {
+    FilterGather<E, NT, RS> g;
+    g.init(a);
+    issue_patch();
+    g.load(a, tid);
+    g.store(a, lds, tid);
+    constexpr int STEP = NT * FilterGather<E, NT, RS>::NB;
+    for (int b0 = tid + STEP; b0 < g.nblk; b0 += STEP) {
+        g.load(a, b0);
+        g.store(a, lds, b0);
+    }
+}
+
 // Band kernel: narrow layers (C_out <= 64) whose whole NK filter and one
 // tile's input patch fit in LDS together.
 //
@@ -931,16 +1042,18 @@ __device__ __forceinline__ f32x16 mfma32<DT_FP8>(const i32x4* a, const i32x4* b,
 // as zeros) into LDS with coalesced 16-byte loads, so every input line is
 // fetched once per tile instead of once per filter tap.  After one barrier
 // each wave runs its MFMAs from LDS alone: for every tap (r, s) the B operand
-// of output pixel (th, tw) is patch pixel (th*st + r, tw*st + s).  The fp32
-// results go through LDS and leave with coalesced 16-byte stores; the
-// residual is added there, before the single rounding.
+// of output pixel (th, tw) is patch pixel (th*st + r, tw*st + s).  The
+// epilogue (fused coefficients, residual, one rounding) stores 16 bytes per
+// lane straight from the accumulators when C_out and the output pixel pitch
+// are multiples of 8, else through an fp32 LDS stage.
 //
 // TM: 32-row blocks of output channels; TN: 32-pixel blocks per wave; U:
 // MFMA k-steps per unrolled block (1, 2 or 4, dividing the steps per tap).
 // The input pixel size C_in * elem bytes is a power-of-two multiple of the
 // MFMA k-step (cpp_log2 = log2 of its 16-byte chunks).
 template <int DT, int TM, int TN, int U, bool RESID>
-__global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArgs a) {
+__global__ __launch_bounds__(band_waves(DT) * 64) void igemm_fwd_band_kernel(ConvArgs a) {
+    constexpr int BAND_WAVES = band_waves(DT);
     constexpr int E = DtTraits<DT>::E;
     constexpr int KSB = (DT == DT_FP8) ? 64 : 32;   // K bytes per 32x32 MFMA
     constexpr int FR = (DT == DT_FP8) ? 2 : 1;      // 16-byte chunks per fragment
@@ -990,48 +1103,74 @@ __global__ __launch_bounds__(BAND_WAVES * 64) void igemm_fwd_band_kernel(ConvArg
         const int64_t img = (int64_t)a.H * a.W * xbytes;
         const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (int64_t)n * img, (uint32_t)img);
         uint8_t* patch = lds + a.patch_off;
-        // slot of this lane in block `wave` as (row, slot in row); advanced
-        // by 256 slots (one block per wave) per instruction with add-and-carry
-        const int sl = wave * 64 + lane;
-        int ph = sl / rs, rem = sl - (sl / rs) * rs;
-        const int dph = (BAND_WAVES * 64) / rs, drem = (BAND_WAVES * 64) % rs;
-        for (int b = wave; b < pblocks; b += BAND_WAVES) {
-            const int pw = small_div(rem, spp, inv_spp), pos = rem - pw * spp;
-            const int ih = ih0 + ph, iw = iw0 + pw;
-            const bool ok = (pos < cpp) & (pw < a.PW) & (ph < a.PH) &
-                            ((unsigned)ih < (unsigned)a.H) & ((unsigned)iw < (unsigned)a.W);
-            const uint32_t off = (uint32_t)((ih * a.W + iw) * xbytes + pos * 16);
-            // non-temporal: each input line is wanted by this tile and at
-            // most its neighbours, which run at the same time, so the patch
-            // should not push the filter (read by every workgroup) out of
-            // L2 (measured: ResNet 3x3 layer 17.0 -> 15.9 us, RGB layer
-            // 32.1 -> 30.6 us)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xrs, (__attribute__((address_space(3))) void*)(patch + b * 1024), 16,
-                off | ((uint32_t)!ok << 31), 0, 0, 2);
-            rem += drem;
-            const int car = rem >= rs ? 1 : 0;
-            rem -= car ? rs : 0;
-            ph += dph + car;
+        auto issue_patch = [&]() {
+            // slot of this lane in block `wave` as (row, slot in row),
+            // advanced by one block per wave per instruction with
+            // add-and-carry
+            const int sl = wave * 64 + lane;
+            int ph = sl / rs, rem = sl - (sl / rs) * rs;
+            const int dph = (BAND_WAVES * 64) / rs, drem = (BAND_WAVES * 64) % rs;
+            for (int b = wave; b < pblocks; b += BAND_WAVES) {
+                const int pw = small_div(rem, spp, inv_spp), pos = rem - pw * spp;
+                const int ih = ih0 + ph, iw = iw0 + pw;
+                const bool ok = (pos < cpp) & (pw < a.PW) & (ph < a.PH) &
+                                ((unsigned)ih < (unsigned)a.H) &
+                                ((unsigned)iw < (unsigned)a.W);
+                const uint32_t off = (uint32_t)((ih * a.W + iw) * xbytes + pos * 16);
+                // non-temporal: each input line is wanted by this tile and
+                // at most its neighbours, which run at the same time, so the
+                // patch should not push the filter (read by every workgroup)
+                // out of L2 (measured: ResNet 3x3 layer 17.0 -> 15.9 us, RGB
+                // layer 32.1 -> 30.6 us)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xrs, (__attribute__((address_space(3))) void*)(patch + b * 1024), 16,
+                    off | ((uint32_t)!ok << 31), 0, 0, 2);
+                rem += drem;
+                const int car = rem >= rs ? 1 : 0;
+                rem -= car ? rs : 0;
+                ph += dph + car;
+            }
+        };
+        bool filter_done = false;
+        if constexpr (E == 2) {   // (fp8 filters always come as NK matrices)
+            if (a.wraw) {
+                // the stored filter, transposed here, then the zero row
+                // (row C_out) cleared when it is staged
+                switch (a.wrs) {
+                    case 0: gather_filter<E, NT, 0>(a, lds, tid, issue_patch); break;
+                    case 1: gather_filter<E, NT, 1>(a, lds, tid, issue_patch); break;
+                    case 9: gather_filter<E, NT, 9>(a, lds, tid, issue_patch); break;
+                    default: gather_filter<E, NT, 25>(a, lds, tid, issue_patch); break;
+                }
+                if (a.frows > a.F)
+                    for (int i = tid; i < a.fpitch / 16; i += NT)
+                        *reinterpret_cast<i32x4*>(lds + a.F * a.fpitch + i * 16) =
+                            i32x4{0, 0, 0, 0};
+                filter_done = true;
+            }
         }
-        // the filter after the patch: its rows come from L2, the patch's
-        // mostly from HBM, so the longer requests go out first
-        const uint32_t fvalid = (uint32_t)(a.F * a.fpitch);
-        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, fvalid);
-        const int fblocks = (a.frows * a.fpitch + 1023) >> 10;
-        for (int b = wave; b < fblocks; b += BAND_WAVES) {
-            const uint32_t off = (uint32_t)(b * 1024 + lane * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                frs, (__attribute__((address_space(3))) void*)(lds + b * 1024), 16,
-                off < fvalid ? off : OOB_OFFSET, 0, 0, 0);
+        if (!filter_done) {
+            issue_patch();
+            // the filter after the patch: its rows come from L2, the patch's
+            // mostly from HBM, so the longer requests go out first
+            const uint32_t fvalid = (uint32_t)(a.F * a.fpitch);
+            const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, fvalid);
+            const int fblocks = (a.frows * a.fpitch + 1023) >> 10;
+            for (int b = wave; b < fblocks; b += BAND_WAVES) {
+                const uint32_t off = (uint32_t)(b * 1024 + lane * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    frs, (__attribute__((address_space(3))) void*)(lds + b * 1024), 16,
+                    off < fvalid ? off : OOB_OFFSET, 0, 0, 0);
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
 
-    // ---- phase B: MFMAs from LDS.  Wave w owns pixel blocks w, w+4, ...,
-    // always TN of them; blocks past the tile read patch pixel 0 and are
-    // never stored.  The k-steps run in blocks of U inside one filter tap:
+    // ---- phase B: MFMAs from LDS.  Wave w owns pixel blocks w,
+    // w + BAND_WAVES, ..., always TN of them; blocks past the tile read
+    // patch pixel 0 and are never stored.  The k-steps run in blocks of U
+    // inside one filter tap:
     // per block one scalar base per operand, the U steps at immediate LDS
     // offsets, and the fragments of step g + LA read while step g multiplies
     // (LA = 2 steps ahead when U >= 2, else 1), into NSET = 2 LA register

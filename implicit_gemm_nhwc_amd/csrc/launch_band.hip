@@ -29,7 +29,7 @@ hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     if (bp.tiles == 0) return hipSuccess;
     a.lds_bytes = bp.lds;
     hipLaunchKernelGGL(kern, dim3((unsigned)(bp.tiles * (a.groups > 1 ? a.groups : 1))),
-                       dim3(BAND_WAVES * 64), (size_t)bp.lds,
+                       dim3(band_waves(DT) * 64), (size_t)bp.lds,
                        stream, a);
     return hipGetLastError();
 }

@@ -496,6 +496,21 @@ const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t fil
                                            const int64_t out_nhwc[4],
                                            const igc_conv_params* params, int32_t dtype);
 
+/* 1 when conv2d_fwd / conv2d_fwd_epilogue run this problem as one kernel
+ * launch that transposes the stored filter into its LDS itself (no NK
+ * matrix, the workspace is not touched): problems on the band kernel in
+ * bf16 or fp16 with an RSCF filter of C_out a multiple of 8, or an FCRS
+ * filter of R*S 1, 9 or 25.  0 when a filter transpose launch into the
+ * workspace precedes the GEMM kernel, or when the problem would be
+ * declined.  conv2d_fwd_general does the same for its problems of one
+ * group on the band kernel.  A library choice (page
+ * "dispatch_fused_im2col_conv2d_apple", summary, transposes the filter once
+ * ahead of the GEMM); the results are the same bits either way. */
+int32_t conv2d_fwd_filter_in_kernel(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
+                                    const int64_t filt_dims[4], const int64_t out_nhwc[4],
+                                    const int32_t stride[2], const int32_t dilation[2],
+                                    const int32_t padding[2], int32_t groups, int32_t dtype);
+
 /* Workspace conv2d_fwd_general needs for this problem: the NK matrix, C_out
  * rows of conv2d_nk_row_pitch's pitch for a K of R*S*Cg (plain groups) or
  * R*S*q*Cg (super-groups of q); 0 when the problem would be declined. */

@@ -743,3 +743,30 @@ def test_general_supergroup_selection(g, cg, fg, dt, want):
                                pad_begin=1, pad_end=1, groups=g)
     assert igc.conv2d_fwd_general_kernel_name(i, f, o, p, filter_is_fcrs=fcrs,
                                               dtype=dt) == want
+
+
+@pytest.mark.parametrize("shape,want", [
+    (dict(in_shape=(32, 56, 56, 64), filt=(3, 3, 64, 64), st=1, p=1, dt=0), True),    # band
+    (dict(in_shape=(2, 16, 16, 16), filt=(3, 3, 16, 16), st=1, p=1, dt=0), True),     # band
+    (dict(in_shape=(32, 56, 56, 128), filt=(3, 3, 128, 256), st=2, p=1, dt=1), False),  # wide
+    (dict(in_shape=(1, 64, 64, 128), filt=(3, 3, 128, 3), st=1, p=1, dt=0), False),   # tap-fold
+    (dict(in_shape=(32, 56, 56, 64), filt=(3, 3, 64, 64), st=3, p=1, dt=0), False),   # declined
+    (dict(in_shape=(2, 16, 16, 64), filt=(3, 3, 64, 64), st=1, p=1, dt=2), False),    # fp8
+    (dict(in_shape=(2, 16, 16, 16), filt=(3, 3, 16, 12), st=1, p=1, dt=0), False),    # F % 8
+])
+def test_filter_in_kernel_query(shape, want):
+    """The band kernel transposes a bf16 / fp16 stored filter itself (RSCF:
+    C_out a multiple of 8); every other problem reads an NK matrix made by a
+    transpose launch."""
+    n, h, w, _ = shape["in_shape"]
+    r, s, _, f = shape["filt"]
+    st, p = shape["st"], shape["p"]
+    ho, wo = oracle.out_size(h, r, st, p), oracle.out_size(w, s, st, p)
+    got = igc.conv2d_fwd_filter_in_kernel(shape["in_shape"], shape["filt"], (n, ho, wo, f),
+                                          filter_is_fcrs=False, dtype=shape["dt"], stride=st,
+                                          padding=p)
+    assert got == want
+    if want:
+        assert igc.conv2d_fwd_kernel_name(shape["in_shape"], shape["filt"], (n, ho, wo, f),
+                                          filter_is_fcrs=False, dtype=shape["dt"], stride=st,
+                                          padding=p) == "igemm_fwd_band_kernel"

@@ -5,7 +5,9 @@ type.  A fragment or epilogue read that runs ahead of its data -- a missing
 s_waitcnt or barrier around the direct-to-LDS requests -- then turns outputs
 into NaN instead of plausible stale values, and the comparison against the
 oracle (which also requires every output to be finite) fails.  One case per
-kernel variant, plus the transposed, general and fused-epilogue paths."""
+kernel variant, plus the transposed, general and fused-epilogue paths, and
+the band kernel's in-kernel filter transpose (whose rows would otherwise
+be found in LDS from an earlier launch of the same problem)."""
 import os
 import sys
 import zlib
@@ -16,7 +18,7 @@ import torch
 import datagen
 import implicit_gemm_nhwc_amd as igc
 import oracle
-from test_gpu_parity import PATH_CASES, TOL, _assert_close, _run
+from test_gpu_parity import FILTER_IN_KERNEL, PATH_CASES, TOL, _assert_close, _run
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -126,3 +128,21 @@ def test_supergroups_poisoned():
         torch.cuda.synchronize()
     ref = oracle.conv2d_general(x, wt, filter_is_fcrs=False, source=src, beta=0.5, **kw)
     _assert_close(out, ref, TOL["bfloat16"], "super-groups")
+
+
+@pytest.mark.parametrize("fcrs", [False, True])
+@pytest.mark.parametrize("case", FILTER_IN_KERNEL, ids=lambda c: c[0])
+def test_filter_in_kernel_poisoned(case, fcrs):
+    cid, dt, n, h, w, c, f, r, s, st, p, resid = case
+    ho, wo = oracle.out_size(h, r, st, p), oracle.out_size(w, s, st, p)
+    _say(f"poison filter in kernel {cid} fcrs={fcrs}")
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype=dt, fcrs=fcrs,
+                                   x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0) if resid else None,
+                                   out_hw=(ho, wo), seed=zlib.crc32(cid.encode()) % 1000)
+    beta = 0.5 if resid else 0.0
+    with igc.using_library(igc.POISON_LIB_PATH):
+        out = _run(x, wt, fcrs=fcrs, stride=st, pad=p, src=src, beta=beta)
+    ref = oracle.conv2d(x, wt, filter_is_fcrs=fcrs, stride=st, padding=p, source=src,
+                        beta=beta)
+    _assert_close(out, ref, TOL[dt], cid)

@@ -407,3 +407,67 @@ def test_empty_batch_and_zero_channels():
     assert igc.conv2d_fwd(x0, w0, out1, filter_is_fcrs=False, stride=1, padding=1) == 1
     torch.cuda.synchronize()
     assert torch.all(out1.float() == 0)
+
+
+# ------------------------------------------ filter transposed in the kernel
+# id, dtype, N, H, W, C, F, R, S, stride, pad, residual
+FILTER_IN_KERNEL = [
+    ("bf16_f64", "bfloat16", 2, 17, 15, 64, 64, 3, 3, 1, 1, True),
+    ("fp16_f40_zero_row_s2", "float16", 2, 19, 18, 32, 40, 3, 3, 2, 1, False),
+    ("fp16_f24_5x5", "float16", 2, 20, 20, 32, 24, 5, 5, 1, 2, True),
+    ("bf16_f16_1x1", "bfloat16", 2, 16, 18, 64, 16, 1, 1, 1, 0, False),
+    ("bf16_f32_1x3", "bfloat16", 1, 13, 30, 32, 32, 1, 3, 1, 1, True),
+    # blocks of more than one round per thread (RSCF: 2 per round)
+    ("bf16_f48_c128_rounds", "bfloat16", 1, 12, 14, 128, 48, 3, 3, 1, 1, False),
+    # the NK path only: C_out not a multiple of 8 (RSCF), R*S = 6 (FCRS), fp8
+    ("bf16_f5", "bfloat16", 1, 12, 13, 16, 5, 3, 3, 1, 1, False),
+    ("bf16_2x3", "bfloat16", 1, 12, 13, 32, 16, 2, 3, 1, 1, False),
+    ("fp8_f24", "float8_e4m3fn", 2, 14, 16, 64, 24, 3, 3, 1, 1, True),
+]
+
+
+def _in_kernel(dt, fcrs, f, r, s):
+    return dt != "float8_e4m3fn" and ((r * s in (1, 9, 25)) if fcrs else f % 8 == 0)
+
+
+@pytest.mark.parametrize("fcrs", [False, True])
+@pytest.mark.parametrize("case", FILTER_IN_KERNEL, ids=lambda c: c[0])
+def test_filter_in_kernel_matches_nk_path(case, fcrs):
+    """conv2d_fwd on the band kernel transposes a bf16 / fp16 stored filter
+    into LDS itself (RSCF with C_out a multiple of 8, FCRS with R*S of 1, 9
+    or 25): the same bits as the NK path (conv2d_filter_to_nk, then
+    conv2d_fwd_nk), the oracle's values, and the workspace left untouched.
+    Other filters take the NK path inside conv2d_fwd."""
+    cid, dt, n, h, w, c, f, r, s, st, p, resid = case
+    ho, wo = oracle.out_size(h, r, st, p), oracle.out_size(w, s, st, p)
+    _say(f"filter in kernel {cid} fcrs={fcrs}")
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype=dt, fcrs=fcrs,
+                                   x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0) if resid else None,
+                                   out_hw=(ho, wo), seed=zlib.crc32(cid.encode()) % 1000)
+    assert igc.conv2d_fwd_kernel_name(x.shape, wt.shape, (n, ho, wo, f), filter_is_fcrs=fcrs,
+                                      dtype=x.dtype, stride=st,
+                                      padding=p) == "igemm_fwd_band_kernel"
+    fused = _in_kernel(dt, fcrs, f, r, s)
+    assert igc.conv2d_fwd_filter_in_kernel(x.shape, wt.shape, (n, ho, wo, f),
+                                           filter_is_fcrs=fcrs, dtype=x.dtype, stride=st,
+                                           padding=p) == fused
+    beta = 0.5 if resid else 0.0
+    xd, wd = x.to(DEV), wt.to(DEV)
+    sd = None if src is None else src.to(DEV)
+    nkb = igc.conv2d_workspace_bytes(wt.shape, fcrs, wt.dtype)
+    ws = torch.full((nkb,), 0x5A, dtype=torch.uint8, device=DEV)
+    a = torch.empty((n, ho, wo, f), dtype=datagen.OUT_DTYPES[dt], device=DEV)
+    assert igc.conv2d_fwd(xd, wd, a, filter_is_fcrs=fcrs, stride=st, padding=p, source=sd,
+                          beta=beta, workspace=ws) == 1
+    nk = torch.empty(nkb, dtype=torch.uint8, device=DEV)
+    assert igc.conv2d_filter_to_nk(wd, nk, filter_is_fcrs=fcrs) == 1
+    b = torch.empty_like(a)
+    assert igc.conv2d_fwd_nk(xd, nk, wt.shape, b, filter_is_fcrs=fcrs, stride=st, padding=p,
+                             source=sd, beta=beta) == 1
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a), _bits(b))
+    if fused:
+        assert bool((ws == 0x5A).all())
+    ref = oracle.conv2d(x, wt, filter_is_fcrs=fcrs, stride=st, padding=p, source=src, beta=beta)
+    _assert_close(a, ref, TOL[dt], cid)
