@@ -539,11 +539,13 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
 // Its register transposes take whole 16-byte loads of 2-byte elements
 // (bf16, fp16): an RSCF filter needs C_out a multiple of 8, an FCRS filter
 // R*S of 1, 9 or 25 (the register transposes are built for those tap
-// counts: 1x1, 3x3, 5x5 filters).
+// counts: 1x1, 3x3, 5x5 filters).  (The tap-fold kernel keeps its NK
+// matrix: with its many small workgroups, making the rows in each one cost
+// more than the transpose launch saved, measured on the RGB layer: 22.0 ->
+// 23.9 us kernel.)
 bool filter_in_kernel(const Shape& s, int32_t dtype, int32_t fcrs, bool tapfold_ok = true) {
-    const int64_t vec = 16 / elem_bytes(dtype);
     if (s.M == 0 || s.F == 0 || dtype == IGC_DTYPE_FP8_E4M3FN) return false;
-    if (fcrs ? !(s.R * s.S == 1 || s.R * s.S == 9 || s.R * s.S == 25) : s.F % vec != 0)
+    if (fcrs ? !(s.R * s.S == 1 || s.R * s.S == 9 || s.R * s.S == 25) : s.F % 8 != 0)
         return false;
     BandPlan bp;
     return select_kernel(s, dtype, &bp, tapfold_ok, device_info()) == K_BAND;
