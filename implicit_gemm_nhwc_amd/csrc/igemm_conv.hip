@@ -538,15 +538,18 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
 // into its LDS itself, so no NK matrix and no transpose launch are needed.
 // Its register transposes take whole 16-byte loads of 2-byte elements
 // (bf16, fp16): an RSCF filter needs C_out a multiple of 8, an FCRS filter
-// R*S of 1, 9 or 25 (the register transposes are built for those tap
-// counts: 1x1, 3x3, 5x5 filters).  (The tap-fold kernel keeps its NK
+// R*S of 1 or 9 (the register transposes are built for those tap counts:
+// 1x1 and 3x3 filters; a 25-tap block needed 100 registers).  (The tap-fold kernel keeps its NK
 // matrix: with its many small workgroups, making the rows in each one cost
 // more than the transpose launch saved, measured on the RGB layer: 22.0 ->
 // 23.9 us kernel.)
-bool filter_in_kernel(const Shape& s, int32_t dtype, int32_t fcrs, bool tapfold_ok = true) {
+bool raw_filter_ok(const Shape& s, int32_t dtype, int32_t fcrs) {
     if (s.M == 0 || s.F == 0 || dtype == IGC_DTYPE_FP8_E4M3FN) return false;
-    if (fcrs ? !(s.R * s.S == 1 || s.R * s.S == 9 || s.R * s.S == 25) : s.F % 8 != 0)
-        return false;
+    return fcrs ? (s.R * s.S == 1 || s.R * s.S == 9) : s.F % 8 == 0;
+}
+
+bool filter_in_kernel(const Shape& s, int32_t dtype, int32_t fcrs, bool tapfold_ok = true) {
+    if (!raw_filter_ok(s, dtype, fcrs)) return false;
     BandPlan bp;
     return select_kernel(s, dtype, &bp, tapfold_ok, device_info()) == K_BAND;
 }
@@ -899,10 +902,11 @@ hipError_t run_transposed(const TPlan& t, const void* input, const void* filter,
 // takes the padding before each axis; the tap-fold kernel is left to the
 // page's paddings).  Several groups at unit dilation and stride (1,1) or
 // (2,2) run as super-groups on the band kernel when its gate admits them
-// (see supergroup_plan).  Any other problem runs on the tiled kernel with
-// its general geometry, the groups as one grouped launch (group g reads
-// input channels g*Cg.., NK rows, output channels, source channels and
-// scale / bias entries g*Fg..).
+// (see supergroup_plan); one group at stride 1 with dilation as dilation
+// phases on the band kernel (see dilation_plan).  Any other problem runs on
+// the tiled kernel with its general geometry, the groups as one grouped
+// launch (group g reads input channels g*Cg.., NK rows, output channels,
+// source channels and scale / bias entries g*Fg..).
 struct GShape {
     Shape s;          // C = C_in per group (Cg), F = all output channels
     int64_t cin;      // input channels, groups * Cg
@@ -914,6 +918,10 @@ struct GShape {
     Shape sg;         // one super-group's problem (C = q*Cg, F = q*Fg, its K,
                       // kpad and kpitch); N, H, W, Ho, Wo, R, S as s
     int64_t nk_bytes; // the NK matrix's bytes (all output channels' rows)
+    bool dil;         // dilation phases (sd below)
+    Shape sd;         // one dilation phase's problem: the input view H/dh x
+                      // W/dw, output Ho/dh x Wo/dw, padding pt/dh, pl/dw,
+                      // stride 1 and no dilation; C, F, R, S, K as s
 };
 
 int64_t out_size_general(int64_t in, int64_t k, int64_t st, int64_t dil, int64_t pb, int64_t pe) {
@@ -966,6 +974,38 @@ void supergroup_plan(GShape& t, int32_t dtype, const DevInfo& dev) {
         }
     }
     if (t.q > 0) t.nk_bytes = s.F * t.sg.kpitch * eb;
+}
+
+// Dilation phases: at stride 1, output row oh = a + dh*i (phase a < dh)
+// reads input rows oh - pt + dh*r = a + dh*(i + r - pt/dh) when dh divides
+// pt: only rows a, a + dh, ..., an undilated convolution with padding
+// pt/dh over every dh-th input row, and likewise along the width.  When dh
+// and dw divide the padding before each axis and the input and output
+// extents, the dh*dw phases have one shape and run as one grouped launch of
+// the band kernel: phase (a_h, a_w) reads the input view of every dh-th row
+// and dw-th column from pixel (a_h, a_w) and stores through an output map
+// (view pixel (i, j) -> output pixel (a_h + dh*i, a_w + dw*j)), with the
+// plain NK matrix.  The same products as the definition, only grouped by
+// phase.
+void dilation_plan(GShape& t, int32_t dtype, const DevInfo& dev) {
+    const Shape& s = t.s;
+    if (t.groups != 1 || t.sh != 1 || t.sw != 1 || (t.dh == 1 && t.dw == 1)) return;
+    if (t.pt % t.dh || t.pl % t.dw || s.H % t.dh || s.W % t.dw || s.Ho % t.dh || s.Wo % t.dw)
+        return;
+    if (s.M == 0 || s.F == 0 || s.H * s.W * s.C * elem_bytes(dtype) >= ((int64_t)1 << 31)) return;
+    Shape u = s;
+    u.H = s.H / t.dh; u.W = s.W / t.dw;
+    u.Ho = s.Ho / t.dh; u.Wo = s.Wo / t.dw;
+    u.st = 1;
+    u.pt = t.pt / t.dh; u.pl = t.pl / t.dw;
+    u.M = u.N * u.Ho * u.Wo;
+    Shape pl = u;
+    pl.N = u.N * t.dh * t.dw;
+    BandPlan bp;
+    if (!band_plan(pl, dtype, &bp, dev)) return;
+    if (bp.tiles >= ((int64_t)1 << 31)) return;
+    t.dil = true;
+    t.sd = u;
 }
 
 int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64_t filt_dims[4],
@@ -1034,8 +1074,10 @@ int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64
         if (rc != IGC_OK) return rc;
     }
     t.q = 0;
+    t.dil = false;
     t.nk_bytes = s.F * s.kpitch * eb;
     if (!t.fast) supergroup_plan(t, dtype, device_info());
+    if (!t.fast && t.q == 0) dilation_plan(t, dtype, device_info());
     if (g) *g = t;
     return IGC_OK;
 }
@@ -1117,6 +1159,60 @@ hipError_t launch_supergroups(const void* input, const void* nk, void* output,
     }
 }
 
+// The dilation phases' grouped launch of the band kernel: nk is the plain
+// NK matrix, or nullptr with wraw the stored filter (filter_in_kernel's
+// layout rules; the kernel transposes it itself).
+hipError_t launch_dilation_phases(const void* input, const void* nk, void* output,
+                                  const void* source, float beta, const igc_epilogue* epi,
+                                  const GShape& g, int32_t dtype, hipStream_t stream,
+                                  const void* wraw = nullptr, int32_t wfcrs = 0) {
+    const Shape& u = g.sd;
+    const Shape& s = g.s;
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t np = (int64_t)g.dh * g.dw;
+    Shape pl = u;
+    pl.N = u.N * np;
+    BandPlan bp;
+    if (!band_plan(pl, dtype, &bp, device_info())) return hipErrorInvalidValue;
+    bp.tiles = u.N * bp.tiles_h * bp.tiles_w;   // per phase
+    ConvArgs a = base_args(input, nk, output, source, beta, epi, u, dtype);
+    a.wraw = (const uint8_t*)wraw;
+    a.wrs = wfcrs ? (int)(s.R * s.S) : 0;
+    a.vrow = (int)(g.dh * s.W);
+    a.vcol = g.dw;
+    a.vimg = (int)(s.H * s.W);
+    a.ymap = 1;
+    a.Hy = (int)s.Ho;
+    a.Wy = (int)s.Wo;
+    a.ysh = g.dh;
+    a.ysw = g.dw;
+    if (np > 1) {
+        // phase (a_h, a_w) = (gh, gw) of a grid of dw columns; with one
+        // column (dw = 1) the launch is one-dimensional over the row phases
+        a.groups = (int)np;
+        const int64_t xr = s.W * s.C * eb, yr = s.Wo * s.F * 2;
+        if (g.dw > 1) {
+            a.gsplit = g.dw;
+            a.g_x = s.C * eb;
+            a.g_x2 = xr;
+            a.g_y = s.F * 2;
+            a.g_y2 = yr;
+            a.g_src = source ? s.F * 2 : 0;
+            a.g_src2 = source ? yr : 0;
+        } else {
+            a.g_x = xr;
+            a.g_y = yr;
+            a.g_src = source ? yr : 0;
+        }
+    }
+    const bool resid = source != nullptr;
+    switch (dtype) {
+        case IGC_DTYPE_BF16: return launch_band_any<DT_BF16>(resid, a, bp, stream);
+        case IGC_DTYPE_FP16: return launch_band_any<DT_FP16>(resid, a, bp, stream);
+        default: return launch_band_any<DT_FP8>(resid, a, bp, stream);
+    }
+}
+
 // The GEMM of a general problem whose NK matrix is in nk (all groups' rows,
 // group g's Fg rows starting at row g*Fg; super-group j's q*Fg rows starting
 // at row j*q*Fg).
@@ -1131,6 +1227,8 @@ hipError_t launch_general(const void* input, const void* nk, void* output, const
     const int64_t fg = s.F / g.groups;
     if (s.M == 0 || fg == 0) return hipSuccess;
     if (g.q > 0) return launch_supergroups(input, nk, output, source, beta, epi, g, dtype, stream);
+    if (g.dil)
+        return launch_dilation_phases(input, nk, output, source, beta, epi, g, dtype, stream);
     ConvArgs a = base_args(input, nk, output, source, beta, epi, s, dtype);
     a.F = (int)fg;
     a.sh = g.sh; a.sw = g.sw;
@@ -1555,7 +1653,7 @@ const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t fil
         }
     }
     if (g.s.M == 0 || g.s.F == 0) return "none";
-    return g.q > 0 ? "igemm_fwd_band_kernel" : "igemm_fwd_kernel";
+    return (g.q > 0 || g.dil) ? "igemm_fwd_band_kernel" : "igemm_fwd_kernel";
 }
 
 int32_t conv2d_fwd_filter_in_kernel(const int64_t in_nhwc[4], int32_t filter_is_fcrs,
@@ -1616,6 +1714,9 @@ int32_t conv2d_fwd_general(const void* input, const int64_t in_nhwc[4], const vo
     if (g.fast && filter_in_kernel(s, dtype, filter_is_fcrs, g.page))
         return hip_fail(launch_igemm(input, nullptr, output, source, beta, epilogue, s, dtype, st,
                                      nullptr, g.page, nullptr, filter, filter_is_fcrs));
+    if (g.dil && raw_filter_ok(s, dtype, filter_is_fcrs))
+        return hip_fail(launch_dilation_phases(input, nullptr, output, source, beta, epilogue, g,
+                                               dtype, st, filter, filter_is_fcrs));
     void* nk = workspace;
     bool owned = false;
     if (!nk && nk_bytes) {

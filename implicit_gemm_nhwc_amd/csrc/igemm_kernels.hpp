@@ -47,7 +47,7 @@ struct ConvArgs {
     const uint8_t* nk;  // [C_out][kpitch] transposed filter, zero past K
     // band kernel only: when set, the stored filter that the kernel
     // transposes into its LDS itself (nk is then unused): RSCF [R][S][C][F]
-    // when wrs == 0, else FCRS [F][C][R][S] with R*S == wrs (1, 9 or 25)
+    // when wrs == 0, else FCRS [F][C][R][S] with R*S == wrs (1 or 9)
     const uint8_t* wraw;
     int wrs;
     uint16_t* y;        // NHWC output (bf16 or fp16 bits)
@@ -103,11 +103,16 @@ struct ConvArgs {
     int64_t g_x;
     int g_c;
     // grouped launch on a grid of gsplit columns (gsplit > 1): problem
-    // gi = gh*gsplit + gw moves the output by gw*g_y + gh*g_y2 bytes, the
-    // source by gw*g_src + gh*g_src2, and its padding by -gh*g_pt, -gw*g_pl
+    // gi = gh*gsplit + gw moves the input by gw*g_x + gh*g_x2 bytes, the
+    // output by gw*g_y + gh*g_y2, the source by gw*g_src + gh*g_src2, and
+    // its padding by -gh*g_pt, -gw*g_pl
     int gsplit;
-    int64_t g_y2, g_src2;
+    int64_t g_x2, g_y2, g_src2;
     int g_pt, g_pl;
+    // band kernel: the input as a view of every vrow-th / vcol-th pixel
+    // (input pixel (ih, iw) of the view at pixel ih*vrow + iw*vcol of its
+    // image, images vimg pixels apart); 0 for the plain tensor (W, 1, H*W)
+    int vrow, vcol, vimg;
     int lds_bytes;      // dynamic LDS of the launch (the poison fill below)
 };
 
@@ -130,12 +135,12 @@ __device__ __forceinline__ int group_block(ConvArgs& a, int per) {
     if (a.groups > 1) {
         const int gi = b / per;
         b -= gi * per;
-        a.x += gi * a.g_x;
         if (a.scale) a.scale += (int64_t)gi * a.g_c;
         if (a.bias) a.bias += (int64_t)gi * a.g_c;
         a.nk += gi * a.g_nk;
         const int gh = a.gsplit > 1 ? gi / a.gsplit : 0;
         const int gw = gi - gh * (a.gsplit > 1 ? a.gsplit : 0);
+        a.x += gw * a.g_x + gh * a.g_x2;
         a.y = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.y) + gw * a.g_y +
                                           gh * a.g_y2);
         if (a.src)
@@ -941,9 +946,10 @@ __device__ __forceinline__ f32x16 mfma32<DT_FP8>(const i32x4* a, const i32x4* b,
 //    k = kb*VEC.. of VEC output channels cb*VEC..; its VEC loads (one per
 //    k) become the VEC output channels' chunks at k = kb*VEC (needs C_out a
 //    multiple of VEC);
-//  * FCRS [F][C][R][S] with R*S == RS: block (co, cb) = the RS taps of VEC
-//    input channels cb*VEC.. of output channel co, RS contiguous loads in
-//    (c, tap) order; tap t's chunk holds elements j*RS + t, j < VEC.
+//  * FCRS [F][C][R][S] with R*S == RS (1 or 9): block (co, cb) = the RS
+//    taps of VEC input channels cb*VEC.. of output channel co, RS
+//    contiguous loads in (c, tap) order; tap t's chunk holds elements
+//    j*RS + t, j < VEC.
 // K is a whole number of VEC (the band kernel's C_in * E is a multiple of
 // 32).  Consecutive threads take consecutive blocks (adjacent addresses).
 // load issues one round's loads (NB blocks per thread); store writes them
@@ -953,7 +959,7 @@ template <int E, int NT, int RS>
 struct FilterGather {
     static constexpr int VEC = 16 / E;
     static constexpr int NL = RS == 0 ? VEC : RS;              // loads per block
-    static constexpr int NB = (RS == 0 && E == 2) ? 2 : 1;     // blocks per thread per round
+    static constexpr int NB = 1;                                 // blocks per thread per round
     union Block {
         i32x4 w[NL];
         uint16_t h[NL * 8];
@@ -1048,10 +1054,14 @@ __device__ __forceinline__ void gather_filter(const ConvArgs& a, uint8_t* lds, i
 // are multiples of 8, else through an fp32 LDS stage.
 //
 // TM: 32-row blocks of output channels; TN: 32-pixel blocks per wave; U:
-// MFMA k-steps per unrolled block (1, 2 or 4, dividing the steps per tap).
+// MFMA k-steps per unrolled block (1, 2 or 4, dividing the steps per tap);
+// RAW: the filter comes as the stored filter (a.wraw) and is transposed
+// here (bf16 / fp16 only), a separate instantiation because the transpose's
+// registers would otherwise set every variant's register floor (and halve
+// the occupancy of the small ones).
 // The input pixel size C_in * elem bytes is a power-of-two multiple of the
 // MFMA k-step (cpp_log2 = log2 of its 16-byte chunks).
-template <int DT, int TM, int TN, int U, bool RESID>
+template <int DT, int TM, int TN, int U, bool RESID, bool RAW = false>
 __global__ __launch_bounds__(band_waves(DT) * 64) void igemm_fwd_band_kernel(ConvArgs a) {
     constexpr int BAND_WAVES = band_waves(DT);
     constexpr int E = DtTraits<DT>::E;
@@ -1100,7 +1110,10 @@ __global__ __launch_bounds__(band_waves(DT) * 64) void igemm_fwd_band_kernel(Con
         const float inv_spp = 1.0f / (float)spp;
         const int rs = a.prow >> 4;                   // LDS slots per patch row
         const int pblocks = (a.PH * rs + 63) >> 6;
-        const int64_t img = (int64_t)a.H * a.W * xbytes;
+        // the input view's strides in pixels (plain tensor: W, 1, H*W)
+        const int vrow = a.vrow ? a.vrow : a.W;
+        const int vcol = a.vcol ? a.vcol : 1;
+        const int64_t img = (int64_t)(a.vimg ? a.vimg : a.H * a.W) * xbytes;
         const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (int64_t)n * img, (uint32_t)img);
         uint8_t* patch = lds + a.patch_off;
         auto issue_patch = [&]() {
@@ -1116,7 +1129,7 @@ __global__ __launch_bounds__(band_waves(DT) * 64) void igemm_fwd_band_kernel(Con
                 const bool ok = (pos < cpp) & (pw < a.PW) & (ph < a.PH) &
                                 ((unsigned)ih < (unsigned)a.H) &
                                 ((unsigned)iw < (unsigned)a.W);
-                const uint32_t off = (uint32_t)((ih * a.W + iw) * xbytes + pos * 16);
+                const uint32_t off = (uint32_t)((ih * vrow + iw * vcol) * xbytes + pos * 16);
                 // non-temporal: each input line is wanted by this tile and
                 // at most its neighbours, which run at the same time, so the
                 // patch should not push the filter (read by every workgroup)
@@ -1131,25 +1144,18 @@ __global__ __launch_bounds__(band_waves(DT) * 64) void igemm_fwd_band_kernel(Con
                 ph += dph + car;
             }
         };
-        bool filter_done = false;
-        if constexpr (E == 2) {   // (fp8 filters always come as NK matrices)
-            if (a.wraw) {
-                // the stored filter, transposed here, then the zero row
-                // (row C_out) cleared when it is staged
-                switch (a.wrs) {
-                    case 0: gather_filter<E, NT, 0>(a, lds, tid, issue_patch); break;
-                    case 1: gather_filter<E, NT, 1>(a, lds, tid, issue_patch); break;
-                    case 9: gather_filter<E, NT, 9>(a, lds, tid, issue_patch); break;
-                    default: gather_filter<E, NT, 25>(a, lds, tid, issue_patch); break;
-                }
-                if (a.frows > a.F)
-                    for (int i = tid; i < a.fpitch / 16; i += NT)
-                        *reinterpret_cast<i32x4*>(lds + a.F * a.fpitch + i * 16) =
-                            i32x4{0, 0, 0, 0};
-                filter_done = true;
+        if constexpr (RAW && E == 2) {   // (fp8 filters always come as NK matrices)
+            // the stored filter, transposed here, then the zero row (row
+            // C_out) cleared when it is staged
+            switch (a.wrs) {
+                case 0: gather_filter<E, NT, 0>(a, lds, tid, issue_patch); break;
+                case 1: gather_filter<E, NT, 1>(a, lds, tid, issue_patch); break;
+                default: gather_filter<E, NT, 9>(a, lds, tid, issue_patch); break;
             }
-        }
-        if (!filter_done) {
+            if (a.frows > a.F)
+                for (int i = tid; i < a.fpitch / 16; i += NT)
+                    *reinterpret_cast<i32x4*>(lds + a.F * a.fpitch + i * 16) = i32x4{0, 0, 0, 0};
+        } else {
             issue_patch();
             // the filter after the patch: its rows come from L2, the patch's
             // mostly from HBM, so the longer requests go out first

@@ -11,9 +11,9 @@
 namespace igc {
 namespace {
 
-template <int DT, int TM, int TN, int U, bool RESID>
+template <int DT, int TM, int TN, int U, bool RESID, bool RAW>
 hipError_t launch_band(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
-    auto kern = igemm_fwd_band_kernel<DT, TM, TN, U, RESID>;
+    auto kern = igemm_fwd_band_kernel<DT, TM, TN, U, RESID, RAW>;
     static LdsAttr attr;
     const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)device_info().lds);
     if (attr_err != hipSuccess) return attr_err;
@@ -39,9 +39,18 @@ template <int DT, int TM, int TN, bool RESID>
 hipError_t launch_band_u(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
     constexpr int KSB = DT == DT_FP8 ? 64 : 32;
     const int steps = a.C * DtTraits<DT>::E / KSB;
-    if (steps % 4 == 0) return launch_band<DT, TM, TN, 4, RESID>(a, bp, stream);
-    if (steps % 2 == 0) return launch_band<DT, TM, TN, 2, RESID>(a, bp, stream);
-    return launch_band<DT, TM, TN, 1, RESID>(a, bp, stream);
+    // the stored filter transposed in the kernel: bf16 / fp16 only
+    if constexpr (DT != DT_FP8) {
+        if (a.wraw) {
+            if (steps % 4 == 0) return launch_band<DT, TM, TN, 4, RESID, true>(a, bp, stream);
+            if (steps % 2 == 0) return launch_band<DT, TM, TN, 2, RESID, true>(a, bp, stream);
+            return launch_band<DT, TM, TN, 1, RESID, true>(a, bp, stream);
+        }
+    }
+    if (a.wraw) return hipErrorInvalidValue;
+    if (steps % 4 == 0) return launch_band<DT, TM, TN, 4, RESID, false>(a, bp, stream);
+    if (steps % 2 == 0) return launch_band<DT, TM, TN, 2, RESID, false>(a, bp, stream);
+    return launch_band<DT, TM, TN, 1, RESID, false>(a, bp, stream);
 }
 
 template <int DT, int TM, bool RESID>

@@ -500,7 +500,7 @@ const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t fil
  * launch that transposes the stored filter into its LDS itself (no NK
  * matrix, the workspace is not touched): problems on the band kernel in
  * bf16 or fp16 with an RSCF filter of C_out a multiple of 8, or an FCRS
- * filter of R*S 1, 9 or 25.  0 when a filter transpose launch into the
+ * filter of R*S 1 or 9.  0 when a filter transpose launch into the
  * workspace precedes the GEMM kernel, or when the problem would be
  * declined.  conv2d_fwd_general does the same for its problems of one
  * group on the band kernel.  A library choice (page

@@ -770,3 +770,33 @@ def test_filter_in_kernel_query(shape, want):
         assert igc.conv2d_fwd_kernel_name(shape["in_shape"], shape["filt"], (n, ho, wo, f),
                                           filter_is_fcrs=False, dtype=shape["dt"], stride=st,
                                           padding=p) == "igemm_fwd_band_kernel"
+
+
+@pytest.mark.parametrize("shape,kernel", [
+    # stride 1, dilation dividing the padding before each axis and the
+    # extents: dilation phases on the band kernel
+    (dict(in_shape=(32, 56, 56, 64), filt=(3, 3, 64, 64), dil=2, pb=2, pe=2), "band"),
+    (dict(in_shape=(2, 24, 18, 32), filt=(3, 3, 32, 32), dil=3, pb=3, pe=3), "band"),
+    (dict(in_shape=(2, 20, 20, 32), filt=(3, 3, 32, 32), dil=2, pb=0, pe=0), "band"),
+    (dict(in_shape=(1, 16, 15, 32), filt=(3, 3, 32, 16), dil=(2, 1), pb=(2, 1), pe=(2, 1)),
+     "band"),
+    # an extent or a padding the dilation does not divide: the tiled kernel
+    (dict(in_shape=(1, 17, 16, 32), filt=(3, 3, 32, 16), dil=2, pb=2, pe=2), "tiled"),
+    (dict(in_shape=(1, 16, 16, 32), filt=(3, 3, 32, 16), dil=2, pb=1, pe=3), "tiled"),
+    (dict(in_shape=(1, 16, 16, 32), filt=(3, 3, 32, 16), dil=2, pb=2, pe=1), "tiled"),  # Ho 15
+    # C_out > 64: no band kernel
+    (dict(in_shape=(1, 16, 16, 32), filt=(3, 3, 32, 96), dil=2, pb=2, pe=2), "tiled"),
+])
+def test_general_dilation_phase_selection(shape, kernel):
+    n, h, w, c = shape["in_shape"]
+    r, s, _, f = shape["filt"]
+    p = igc.conv_params(stride=1, dilation=shape["dil"], pad_begin=shape["pb"],
+                        pad_end=shape["pe"])
+    ho, wo = igc.out_hw_general(h, w, r, s, p)
+    name = igc.conv2d_fwd_general_kernel_name(shape["in_shape"], shape["filt"], (n, ho, wo, f),
+                                              p, filter_is_fcrs=False, dtype=0)
+    assert name == {"band": "igemm_fwd_band_kernel", "tiled": "igemm_fwd_kernel"}[kernel]
+    # the plain NK matrix either way
+    assert igc.conv2d_fwd_general_workspace_bytes(
+        shape["in_shape"], shape["filt"], (n, ho, wo, f), p, filter_is_fcrs=False,
+        dtype=0) == igc.conv2d_workspace_bytes(shape["filt"], False, 0)

@@ -80,9 +80,34 @@ CASES = [
     ("sg_depthwise_x2_s2_bf16", "bfloat16", 2, 23, 20, 64, 128, 3, 3, 2, 1, 1, 1, 64),
     ("sg_depthwise_5x5_fp16", "float16", 1, 19, 33, 96, 96, 5, 5, 1, 1, 2, 2, 96),
     ("sg_g8_fg6_bf16", "bfloat16", 1, 15, 16, 128, 48, 3, 1, 1, 1, (1, 0), (1, 0), 8),
+    # one group, stride 1, dilation dividing the padding before each axis
+    # and the extents: dilation phases on the band kernel (input views of
+    # every dh-th row / dw-th column, output map)
+    ("dp_d2_same_bf16", "bfloat16", 2, 16, 20, 64, 48, 3, 3, 1, 2, 2, 2, 1),
+    ("dp_d3_fp16", "float16", 2, 24, 18, 32, 32, 3, 3, 1, 3, 3, 3, 1),
+    ("dp_d2_fp8", "float8_e4m3fn", 2, 20, 20, 64, 40, 3, 3, 1, 2, 2, 2, 1),
+    ("dp_d2x1_bf16", "bfloat16", 1, 16, 15, 32, 16, 3, 3, 1, (2, 1), (2, 1), (2, 1), 1),
+    ("dp_d1x3_fp16", "float16", 2, 13, 18, 32, 24, 3, 3, 1, (1, 3), (1, 3), (1, 3), 1),
+    ("dp_d2_5x5_bf16", "bfloat16", 1, 20, 24, 32, 24, 5, 5, 1, 2, 4, 4, 1),
+    ("dp_d2_valid_bf16", "bfloat16", 2, 20, 20, 32, 32, 3, 3, 1, 2, 0, 0, 1),
+    ("dp_d4_f5_fp16", "float16", 1, 32, 32, 32, 5, 3, 3, 1, 4, 4, 4, 1),
 ]
 
 ELEM = {"bfloat16": 2, "float16": 2, "float8_e4m3fn": 1}
+
+
+def _dilation_phases(case):
+    """Whether conv2d_fwd_general runs the case as dilation phases on the
+    band kernel: one group, stride 1, dilation above 1 dividing the padding
+    before each axis and the input and output extents."""
+    _, dt, n, h, w, c, f, r, s, st, dil, pb, pe, g = case
+    st, dil, pb, pe = _pair(st), _pair(dil), _pair(pb), _pair(pe)
+    if g != 1 or st != (1, 1) or dil == (1, 1):
+        return False
+    ho = oracle.out_size_general(h, r, 1, dil[0], pb[0], pe[0])
+    wo = oracle.out_size_general(w, s, 1, dil[1], pb[1], pe[1])
+    return (pb[0] % dil[0] == 0 and pb[1] % dil[1] == 0 and h % dil[0] == 0 and
+            w % dil[1] == 0 and ho % dil[0] == 0 and wo % dil[1] == 0)
 
 
 def _supergroup(case):
@@ -160,7 +185,7 @@ def test_general_parity(case):
         assert name != "igemm_fwd_tapfold_kernel"
         if want:
             assert name == want, name
-    elif _supergroup(case):
+    elif _supergroup(case) or _dilation_phases(case):
         assert name == "igemm_fwd_band_kernel", name
     else:
         assert name == "igemm_fwd_kernel", name
@@ -174,7 +199,8 @@ def test_general_parity(case):
 @pytest.mark.parametrize("case", [c for c in CASES if c[0] in (
     "dil2_s2_fp8", "g32_resnext_bf16", "g2_fg3_bf16", "all_fp16", "pad_tlbr_fp16",
     "g2_wide_bf16", "fast_band_tl_fp8", "fast_wide_asym_fp16", "sg_g16_fp8",
-    "sg_depthwise_x2_s2_bf16", "sg_g8_fg6_bf16", "depthwise_bf16")], ids=lambda c: c[0])
+    "sg_depthwise_x2_s2_bf16", "sg_g8_fg6_bf16", "depthwise_bf16", "dp_d2_same_bf16",
+    "dp_d2_fp8", "dp_d4_f5_fp16")], ids=lambda c: c[0])
 def test_general_fcrs_residual_epilogue(case):
     """FCRS filter, a residual source and the fused scale / bias / SiLU, with
     groups offsetting the coefficients; FCRS bits equal RSCF bits."""

@@ -146,3 +146,23 @@ def test_filter_in_kernel_poisoned(case, fcrs):
     ref = oracle.conv2d(x, wt, filter_is_fcrs=fcrs, stride=st, padding=p, source=src,
                         beta=beta)
     _assert_close(out, ref, TOL[dt], cid)
+
+
+def test_dilation_phases_poisoned():
+    """Dilation as phases on the band kernel (input views, output map, the
+    stored filter transposed in the kernel), with a residual source."""
+    _say("poison dilation phases")
+    x, wt, src = datagen.make_case(N=2, H=16, W=20, C=64, F=48, R=3, S=3, dtype="bfloat16",
+                                   fcrs=True, x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0), out_hw=(16, 20), seed=34)
+    kw = dict(stride=1, dilation=2, pad_begin=2, pad_end=2, groups=1)
+    p = igc.conv_params(**kw)
+    assert igc.conv2d_fwd_general_kernel_name(x.shape, wt.shape, (2, 16, 20, 48), p,
+                                              filter_is_fcrs=True,
+                                              dtype=x.dtype) == "igemm_fwd_band_kernel"
+    with igc.using_library(igc.POISON_LIB_PATH):
+        out = igc.conv2d_general(x.to(DEV), wt.to(DEV), filter_is_fcrs=True, source=src.to(DEV),
+                                 beta=0.5, **kw)
+        torch.cuda.synchronize()
+    ref = oracle.conv2d_general(x, wt, filter_is_fcrs=True, source=src, beta=0.5, **kw)
+    _assert_close(out, ref, TOL["bfloat16"], "dilation phases")

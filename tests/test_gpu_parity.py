@@ -427,15 +427,15 @@ FILTER_IN_KERNEL = [
 
 
 def _in_kernel(dt, fcrs, f, r, s):
-    return dt != "float8_e4m3fn" and ((r * s in (1, 9, 25)) if fcrs else f % 8 == 0)
+    return dt != "float8_e4m3fn" and ((r * s in (1, 9)) if fcrs else f % 8 == 0)
 
 
 @pytest.mark.parametrize("fcrs", [False, True])
 @pytest.mark.parametrize("case", FILTER_IN_KERNEL, ids=lambda c: c[0])
 def test_filter_in_kernel_matches_nk_path(case, fcrs):
     """conv2d_fwd on the band kernel transposes a bf16 / fp16 stored filter
-    into LDS itself (RSCF with C_out a multiple of 8, FCRS with R*S of 1, 9
-    or 25): the same bits as the NK path (conv2d_filter_to_nk, then
+    into LDS itself (RSCF with C_out a multiple of 8, FCRS with R*S of 1 or
+    9): the same bits as the NK path (conv2d_filter_to_nk, then
     conv2d_fwd_nk), the oracle's values, and the workspace left untouched.
     Other filters take the NK path inside conv2d_fwd."""
     cid, dt, n, h, w, c, f, r, s, st, p, resid = case
