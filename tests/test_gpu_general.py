@@ -9,6 +9,8 @@ import os
 import sys
 import zlib
 
+import numpy as np
+
 import pytest
 import torch
 
@@ -99,10 +101,15 @@ ELEM = {"bfloat16": 2, "float16": 2, "float8_e4m3fn": 1}
 def _dilation_phases(case):
     """Whether conv2d_fwd_general runs the case as dilation phases on the
     band kernel: one group, stride 1, dilation above 1 dividing the padding
-    before each axis and the input and output extents."""
+    before each axis and the input and output extents, and the band
+    kernel's channel rules (C_out <= 64, C_in * element bytes a
+    power-of-two multiple of the MFMA k-step)."""
     _, dt, n, h, w, c, f, r, s, st, dil, pb, pe, g = case
     st, dil, pb, pe = _pair(st), _pair(dil), _pair(pb), _pair(pe)
     if g != 1 or st != (1, 1) or dil == (1, 1):
+        return False
+    b, ksb = c * ELEM[dt], 64 if ELEM[dt] == 1 else 32
+    if f > 64 or b % ksb or (b // 16) & (b // 16 - 1):
         return False
     ho = oracle.out_size_general(h, r, 1, dil[0], pb[0], pe[0])
     wo = oracle.out_size_general(w, s, 1, dil[1], pb[1], pe[1])
@@ -314,3 +321,63 @@ def test_general_benchmark_layers_full_size(case):
     ref = _oracle(case, x, wt, False)
     err, scale = _assert_close(out, ref, TOL[dt], cid)
     _say(f"  max|err|/max|ref| = {err / max(scale, 1e-300):.3e}")
+
+
+def _sweep_general():
+    """Seeded random general problems over the paths conv2d_fwd_general
+    picks: super-groups (several groups, unit dilation, stride 1 or 2),
+    dilation phases (one group, stride 1, dilation dividing the padding and
+    the extents), the forward kernels (one group, unit dilation) and the
+    tiled kernel (the rest)."""
+    rng = np.random.default_rng(7)
+    cases = []
+    for i in range(36):
+        dt = ["bfloat16", "float16", "float8_e4m3fn"][i % 3]
+        kind = ["group", "dilate", "plain", "any"][(i // 3) % 4]
+        r = int(rng.choice([1, 3, 5]))
+        s_ = int(rng.choice([1, 3]))
+        if kind == "group":
+            g = int(rng.choice([2, 4, 8, 16, 32]))
+            cg = int(rng.choice([1, 2, 4, 8, 16, 32]))
+            fg = int(rng.choice([1, 2, 4, 8, 16]))
+            st, dil = int(rng.choice([1, 2])), 1
+        elif kind == "dilate":
+            g, cg, fg = 1, int(rng.choice([16, 32, 64])), int(rng.choice([8, 16, 24, 40, 64]))
+            st, dil = 1, int(rng.choice([2, 3]))
+        elif kind == "plain":
+            g, cg, fg = 1, int(rng.choice([16, 32, 64])), int(rng.choice([8, 16, 48, 64, 96]))
+            st, dil = int(rng.choice([1, 2])), 1
+        else:
+            g = int(rng.choice([1, 2, 4]))
+            cg, fg = int(rng.choice([3, 8, 16])), int(rng.choice([4, 8, 12]))
+            st, dil = int(rng.choice([1, 2, 3])), int(rng.choice([1, 2]))
+        if kind == "dilate":
+            pb = dil * int(rng.integers(0, 2)) * (r // 2)
+            pw = dil * int(rng.integers(0, 2)) * (s_ // 2)
+            h = dil * int(rng.integers(4, 10))
+            w = dil * int(rng.integers(4, 10))
+            pad_b, pad_e = (pb, pw), (pb, pw)
+        else:
+            pad_b = (int(rng.integers(0, 3)), int(rng.integers(0, 3)))
+            pad_e = (int(rng.integers(0, 3)), int(rng.integers(0, 3)))
+            h, w = int(rng.integers(6, 20)), int(rng.integers(6, 20))
+        n = int(rng.integers(1, 3))
+        cases.append((f"sweep{i}_{kind}", dt, n, h, w, g * cg, g * fg, r, s_, st, dil, pad_b,
+                      pad_e, g))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_general(), ids=lambda c: c[0])
+def test_general_random_sweep(case):
+    cid, dt = case[0], case[1]
+    p, oshape, x, wt, _ = _draw(case)
+    if oshape[1] < 1 or oshape[2] < 1:
+        pytest.skip("empty output")
+    name = igc.conv2d_fwd_general_kernel_name(x.shape, wt.shape, oshape, p, filter_is_fcrs=False,
+                                              dtype=x.dtype)
+    _say(f"general sweep {case[2:]} -> {oshape}, {name}")
+    if _supergroup(case) or _dilation_phases(case):
+        assert name == "igemm_fwd_band_kernel", name
+    out = _run(x, wt, oshape, p, False)
+    ref = _oracle(case, x, wt, False)
+    _assert_close(out, ref, TOL[dt], cid)
