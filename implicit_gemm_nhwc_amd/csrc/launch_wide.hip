@@ -52,12 +52,20 @@ hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     const int64_t co_tiles256 = (a.F + 255) / 256;
     const int64_t px_tiles256 = ((int64_t)a.M + 255) / 256;
     // grouped or mapped launches (the phases of a transposed convolution):
-    // 128 x 128 tiles in three stages (measured on the 4x4 stride-2
-    // upsampler, N=8 32x32 256->128 bf16, whole call: 22.0 us in two stages,
-    // 20.7 us in three)
-    if (a.groups > 1 || a.ymap)
+    // three stages (measured on the 4x4 stride-2 upsampler, N=8 32x32
+    // 256->128 bf16, whole call: 22.0 us in two stages, 20.7 us in three);
+    // 128 x 64 tiles when 128 x 128 ones would not give every CU two
+    // workgroups (upsampler: 256 tiles of 128 x 128, 20.9 us; 512 of
+    // 128 x 64, 20.0 us; 64 x 128, 21.5 us)
+    if (a.groups > 1 || a.ymap) {
+        const int64_t tiles128 = (((int64_t)a.M + 127) / 128) * ((a.F + 127) / 128) *
+                                 (a.groups > 1 ? a.groups : 1);
+        if (tiles128 < 2 * (int64_t)device_info().cus)
+            return tap128 ? launch_wide<DT, 2, 1, 2, 2, 128, 3, RESID, true, true>(a, stream)
+                          : launch_wide<DT, 2, 1, 2, 2, 128, 3, RESID, false, true>(a, stream);
         return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 3, RESID, true, true>(a, stream)
                       : launch_wide<DT, 2, 2, 2, 2, 128, 3, RESID, false, true>(a, stream);
+    }
     if (a.F > 128 && px_tiles256 * co_tiles256 >= device_info().cus)
         return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
                       : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
