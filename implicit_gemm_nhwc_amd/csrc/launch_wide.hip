@@ -44,7 +44,8 @@ hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
 // workgroup per CU) 35.1 us, 256x256 in 2 stages (98 tiles) 42.7 us.  On the
 // fp8 5x5 256->256 layer (256 tiles of 256x256): 256x256 in 2 stages 105 us,
 // 128x128 in 2 stages 115 us, 256x128 in 3 stages 125 us.  TAPK when C_in is
-// a whole number of k-tiles.
+// a whole number of k-tiles.  With at most one 128 x 128 tile per CU,
+// 128 x 64 tiles in three stages.
 template <int DT, bool RESID>
 hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     constexpr int E = DtTraits<DT>::E;
@@ -69,6 +70,14 @@ hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     if (a.F > 128 && px_tiles256 * co_tiles256 >= device_info().cus)
         return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
                       : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
+    // at most one 128 x 128 tile per CU: 128 x 64 tiles in three stages
+    // (72 KB, two workgroups per CU) fill the second workgroup slot
+    // (transposed 3x3 stride-1 layer, N=8 64x64 256->128 bf16, whole call:
+    // 33.9 -> 30.5 us; two stages 31.7 us)
+    const int64_t tiles128 = (((int64_t)a.M + 127) / 128) * ((a.F + 127) / 128);
+    if (tiles128 <= device_info().cus)
+        return tap128 ? launch_wide<DT, 2, 1, 2, 2, 128, 3, RESID, true>(a, stream)
+                      : launch_wide<DT, 2, 1, 2, 2, 128, 3, RESID, false>(a, stream);
     return tap128 ? launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, true>(a, stream)
                   : launch_wide<DT, 2, 2, 2, 2, 128, 2, RESID, false>(a, stream);
 }

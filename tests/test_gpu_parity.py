@@ -145,6 +145,9 @@ PATH_CASES = [
     ("wide256_fp8_walk", "float8_e4m3fn", 16, 64, 64, 80, 256, 3, 3, 1, 1, False, "wide"),
     ("wide128_bf16_walk_s2_f160", "bfloat16", 4, 30, 30, 96, 160, 3, 3, 2, 1, True, "wide"),
     ("wide128_fp8_tap", "float8_e4m3fn", 2, 20, 20, 128, 96, 3, 3, 1, 1, False, "wide"),
+    # more 128 x 128 tiles than CUs (384): 128 x 128 tiles; with fewer the
+    # cases above take 128 x 64 tiles in three stages
+    ("wide128_bf16_many_tiles", "bfloat16", 12, 64, 64, 64, 96, 3, 3, 1, 1, True, "wide"),
     ("band_u1_bf16", "bfloat16", 2, 20, 20, 16, 48, 3, 3, 1, 1, False, "band"),
     ("band_u2_fp16_tm1", "float16", 2, 20, 20, 32, 24, 5, 5, 1, 2, True, "band"),
     ("band_u1_fp8", "float8_e4m3fn", 2, 20, 20, 64, 64, 3, 3, 1, 1, False, "band"),
