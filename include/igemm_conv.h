@@ -444,7 +444,12 @@ size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t
  * kernel where it admits them: q consecutive groups become one problem of
  * q*Cg input and q*Fg output channels with a block-diagonal NK matrix
  * (zeros between different groups' channels), q*Fg <= 64 and q*Cg *
- * element bytes a power-of-two multiple of 32 (64 for fp8).  Any other
+ * element bytes a power-of-two multiple of 32 (64 for fp8).  One group at
+ * stride 1 whose dilation divides the padding before each axis and the
+ * input and output extents runs on the band kernel as dh*dw dilation
+ * phases (each an undilated convolution over every dh-th input row and
+ * dw-th column, stored through an output map; one grouped launch, the
+ * plain NK matrix).  Any other
  * problem runs on the tiled implicit-GEMM kernel, all groups in one launch
  * (as does any problem whose Cg * element bytes is not a multiple of 16:
  * the tiled kernel then gathers element by element).  Library limits: H + pt + pb,
