@@ -27,6 +27,7 @@ for _dt in ("BF16", "FP16", "FP8"):
     UNITS += [(f"launch_band_{_dt.lower()}", "launch_band.hip", [_d]),
               (f"launch_tapfold_{_dt.lower()}", "launch_tapfold.hip", [_d]),
               (f"launch_wide_{_dt.lower()}", "launch_wide.hip", [_d]),
+              (f"launch_patch_{_dt.lower()}", "launch_patch.hip", [_d]),
               (f"launch_resident_{_dt.lower()}", "launch_small.hip", [_d, "-DIGC_FAMILY=0"]),
               (f"launch_tiled_{_dt.lower()}", "launch_small.hip", [_d, "-DIGC_FAMILY=1"])]
 

@@ -409,19 +409,89 @@ bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& d
     return found;
 }
 
+// Plan of the patch-resident kernel (igemm_patch.hpp), or false when the
+// layer does not fit it: C_out > 64 and a multiple of 4, stride 1, R*S >= 2,
+// C_in a whole number of 128-byte chunks, an image's input and output each
+// below 2^31 bytes.  Workgroups of 64*TM output channels (TM = 4, or 2 when
+// C_out <= 128) and 256 pixel slots; the tile TH x TW of one image (TW =
+// W_out or a power of two from 8 to 256 below it, TH = 256 / TW or H_out)
+// must fill at least 192 of the slots, and the tiles at least one round of
+// one workgroup per CU, three quarters of the last round busy.  Among those:
+// the fewest rounds, then three filter stages over two, then the smallest
+// patch (the input bytes each tile stages).
+bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& dev) {
+    const int64_t E = elem_bytes(dtype);
+    if (s.F <= 64 || s.F % 4 != 0 || s.st != 1 || s.R * s.S < 2 || (s.C * E) % 128 != 0)
+        return false;
+    if (s.H * s.W * s.C * E >= ((int64_t)1 << 31) || s.Ho * s.Wo * s.F * 2 >= ((int64_t)1 << 31))
+        return false;
+    const int tm = s.F > 128 ? 4 : 2;
+    const int64_t bco = 64 * tm, bpx = 256;
+    const int64_t co_tiles = (s.F + bco - 1) / bco;
+    const int64_t epi = 4 * 32 * (tm * 32 * 4 + 16);   // the epilogue's per-wave regions
+    int64_t tws[7];
+    int ntw = 0;
+    if (s.Wo <= bpx) tws[ntw++] = s.Wo;
+    for (int64_t c : {8, 16, 32, 64, 128, 256})
+        if (c < s.Wo) tws[ntw++] = c;
+    bool found = false;
+    int64_t best_rounds = 0, best_patch = 0;
+    int best_ns = 0;
+    for (int k = 0; k < ntw; ++k) {
+        const int64_t tw = tws[k];
+        const int64_t th = s.Ho < bpx / tw ? s.Ho : bpx / tw;
+        if (th < 1 || th * tw < 192) continue;
+        const int64_t ph = th - 1 + s.R, pw = tw - 1 + s.S;
+        const int64_t prow = pw * PATCH_PP + (((tw - pw) * PATCH_PP) % 256 + 256) % 256;
+        const int64_t patch = (ph * prow + 1023) / 1024 * 1024;   // whole 1 KB request blocks
+        int ns = 0;
+        int64_t lds = 0;
+        for (int c : {3, 2}) {
+            lds = c * bco * 128 + patch;
+            if (lds < epi) lds = epi;
+            if (lds <= dev.lds) {
+                ns = c;
+                break;
+            }
+        }
+        if (ns == 0) continue;
+        const int64_t tiles_h = (s.Ho + th - 1) / th, tiles_w = (s.Wo + tw - 1) / tw;
+        const int64_t tiles = s.N * tiles_h * tiles_w * co_tiles;
+        if (tiles < dev.cus) continue;
+        const int64_t rounds = (tiles + dev.cus - 1) / dev.cus;
+        if (4 * (tiles - (rounds - 1) * dev.cus) < 3 * dev.cus) continue;
+        const bool better = !found || rounds < best_rounds ||
+                            (rounds == best_rounds &&
+                             (ns > best_ns || (ns == best_ns && patch < best_patch)));
+        if (better) {
+            found = true;
+            best_rounds = rounds;
+            best_ns = ns;
+            best_patch = patch;
+            *out = PatchPlan{(int)th, (int)tw, (int)ph, (int)pw, (int)prow, (int)lds,
+                             (int)tiles_h, (int)tiles_w, tm, ns, tiles};
+        }
+    }
+    return found;
+}
+
 // The kernel a problem goes to, in order of preference.
-enum KernelKind { K_NONE, K_TAPFOLD, K_BAND, K_WIDE, K_RESIDENT, K_TILED };
+enum KernelKind { K_NONE, K_TAPFOLD, K_BAND, K_PATCH, K_WIDE, K_RESIDENT, K_TILED };
 
 // tapfold_ok: the tap-fold kernel may be chosen (it has no output map and
-// is only exercised on the page's symmetric paddings).
+// is only exercised on the page's symmetric paddings); plain: one problem
+// with no output map (the patch kernel takes no grouped or mapped launch).
 KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp, bool tapfold_ok = true,
-                         const DevInfo& dev = DevInfo{}) {
+                         const DevInfo& dev = DevInfo{}, PatchPlan* pp = nullptr,
+                         bool plain = true) {
     if (s.M == 0 || s.F == 0) return K_NONE;
     // C_in not a whole number of 16-byte vectors: only the tiled kernel's
     // element gather takes it
     if ((s.C * elem_bytes(dtype)) % 16 != 0) return K_TILED;
     if (tapfold_ok && tapfold_plan(s, dtype, bp, dev)) return K_TAPFOLD;
     if (band_plan(s, dtype, bp, dev)) return K_BAND;
+    PatchPlan tmp;
+    if (plain && patch_plan(s, dtype, pp ? pp : &tmp, dev)) return K_PATCH;
     if (wide_ok(s, dtype)) return K_WIDE;
     if (resident_ok(s, dtype)) return K_RESIDENT;
     return K_TILED;
@@ -448,8 +518,9 @@ struct OutMap {
 
 template <int DT>
 hipError_t launch_kind(KernelKind kind, bool resid, const ConvArgs& a, const BandPlan& bp,
-                       hipStream_t stream) {
+                       const PatchPlan& pp, hipStream_t stream) {
     switch (kind) {
+        case K_PATCH: return launch_patch_any<DT>(resid, a, pp, stream);
         case K_TAPFOLD: return launch_tapfold_any<DT>(resid, a, bp, stream);
         case K_BAND: return launch_band_any<DT>(resid, a, bp, stream);
         case K_WIDE: return launch_wide_any<DT>(resid, a, stream);
@@ -523,14 +594,16 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
         tapfold_ok = false;
     }
     const bool resid = source != nullptr;
+    const bool plain = !(grp && grp->n > 1) && !map;
     BandPlan bp;
-    const KernelKind kind = select_kernel(s, dtype, &bp, tapfold_ok, device_info());
+    PatchPlan pp;
+    const KernelKind kind = select_kernel(s, dtype, &bp, tapfold_ok, device_info(), &pp, plain);
     if (kind == K_NONE) return hipSuccess;
     if (wraw && kind != K_BAND) return hipErrorInvalidValue;
     switch (dtype) {
-        case IGC_DTYPE_BF16: return launch_kind<DT_BF16>(kind, resid, a, bp, stream);
-        case IGC_DTYPE_FP16: return launch_kind<DT_FP16>(kind, resid, a, bp, stream);
-        default: return launch_kind<DT_FP8>(kind, resid, a, bp, stream);
+        case IGC_DTYPE_BF16: return launch_kind<DT_BF16>(kind, resid, a, bp, pp, stream);
+        case IGC_DTYPE_FP16: return launch_kind<DT_FP16>(kind, resid, a, bp, pp, stream);
+        default: return launch_kind<DT_FP8>(kind, resid, a, bp, pp, stream);
     }
 }
 
@@ -1501,6 +1574,7 @@ const char* conv2d_fwd_kernel_name(const int64_t in_nhwc[4], int32_t filter_is_f
         case K_NONE: return "none";
         case K_TAPFOLD: return "igemm_fwd_tapfold_kernel";
         case K_BAND: return "igemm_fwd_band_kernel";
+        case K_PATCH: return "igemm_fwd_patch_kernel";
         case K_WIDE: return "igemm_fwd_wide_kernel";
         case K_RESIDENT: return "igemm_fwd_resident_kernel";
         default: return "igemm_fwd_kernel";
@@ -1647,6 +1721,7 @@ const char* conv2d_fwd_general_kernel_name(const int64_t in_nhwc[4], int32_t fil
             case K_NONE: return "none";
             case K_TAPFOLD: return "igemm_fwd_tapfold_kernel";
             case K_BAND: return "igemm_fwd_band_kernel";
+            case K_PATCH: return "igemm_fwd_patch_kernel";
             case K_WIDE: return "igemm_fwd_wide_kernel";
             case K_RESIDENT: return "igemm_fwd_resident_kernel";
             default: return "igemm_fwd_kernel";

@@ -62,6 +62,15 @@ struct BandPlan {
     int groups;   // tap-fold kernel: input rows in the LDS ring
 };
 
+// Plan of the patch-resident kernel (patch_plan): output tile TH x TW, patch
+// PH x PW pixels at prow bytes per row, TM 32-channel blocks per wave (BCO =
+// 64*TM output channels per workgroup), nstage filter stages, tiles =
+// N * tiles_h * tiles_w * channel tiles workgroups of lds bytes.
+struct PatchPlan {
+    int TH, TW, PH, PW, prow, lds, tiles_h, tiles_w, TM, nstage;
+    int64_t tiles;
+};
+
 // Launchers of each kernel family, per element type DT (DT_BF16, DT_FP16 or
 // DT_FP8; resid: a residual source is read).  They fill the family's own fields of a and
 // enqueue one launch on the stream.
@@ -72,6 +81,9 @@ hipError_t launch_tapfold_any(bool resid, const ConvArgs& a, const BandPlan& bp,
                               hipStream_t stream);
 template <int DT>
 hipError_t launch_wide_any(bool resid, const ConvArgs& a, hipStream_t stream);
+template <int DT>
+hipError_t launch_patch_any(bool resid, const ConvArgs& a, const PatchPlan& pp,
+                            hipStream_t stream);
 template <int DT>
 hipError_t launch_resident_any(bool resid, const ConvArgs& a, hipStream_t stream);
 template <int DT>

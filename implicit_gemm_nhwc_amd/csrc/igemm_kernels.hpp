@@ -909,6 +909,9 @@ struct IntC { static constexpr int value = V; };
 // more than the 256 registers a wave has at two waves per SIMD.
 constexpr int band_waves(int dt) { return dt == DT_FP8 ? 4 : 8; }
 constexpr int BAND_MAX_TN = 4;   // 32-pixel blocks per wave at most
+// Patch-resident kernel (igemm_patch.hpp): LDS bytes per staged patch pixel,
+// one 128-byte chunk of its channels plus a 16-byte pad.
+constexpr int PATCH_PP = 144;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 

@@ -193,7 +193,7 @@ def test_kernel_selection():
     want = {"tiny_3x3_16c": "igemm_fwd_band_kernel",
             "resnet_3x3_64c_n32": "igemm_fwd_band_kernel",
             "strided_3x3_s2_128to256_n32": "igemm_fwd_wide_kernel",
-            "fp8_5x5_256c_residual_n16": "igemm_fwd_wide_kernel",
+            "fp8_5x5_256c_residual_n16": "igemm_fwd_patch_kernel",
             "rgb_3x3_128to3_512px": "igemm_fwd_tapfold_kernel"}
     dts = {"bfloat16": torch.bfloat16, "float16": torch.float16,
            "float8_e4m3fn": torch.float8_e4m3fn}
@@ -215,6 +215,35 @@ def test_kernel_selection():
     assert igc.conv2d_fwd_kernel_name((2, 8, 8, 64), (3, 3, 64, 65), (2, 8, 8, 65),
                                       filter_is_fcrs=False, dtype=torch.float16,
                                       padding=1) == "igemm_fwd_wide_kernel"
+
+
+def test_patch_kernel_selection():
+    """The patch-resident kernel takes stride-1 layers with C_out > 64 (a
+    multiple of 4), a spatial filter and C_in a whole number of 128-byte
+    chunks, when 256-pixel tiles of one image (at least 192 of their slots
+    used) give every CU a workgroup; the wide kernel takes the rest."""
+    def name(n, h, w, c, f, r, s, st, p, dt):
+        ho, wo = (h + 2 * p - r) // st + 1, (w + 2 * p - s) // st + 1
+        return igc.conv2d_fwd_kernel_name((n, h, w, c), (r, s, c, f), (n, ho, wo, f),
+                                          filter_is_fcrs=False, dtype=dt, stride=st, padding=p)
+    bf, f8 = torch.bfloat16, torch.float8_e4m3fn
+    patch, wide = "igemm_fwd_patch_kernel", "igemm_fwd_wide_kernel"
+    assert name(16, 64, 64, 256, 256, 5, 5, 1, 2, f8) == patch
+    assert name(16, 64, 64, 64, 256, 3, 3, 1, 1, bf) == patch       # one 128-byte chunk
+    assert name(16, 64, 66, 128, 128, 1, 3, 1, 0, f8) == patch      # 1 x 3
+    assert name(16, 64, 64, 64, 256, 3, 3, 2, 1, bf) == wide        # stride 2
+    assert name(16, 64, 64, 64, 256, 1, 1, 1, 0, bf) == wide        # no spatial filter
+    assert name(16, 64, 64, 96, 256, 3, 3, 1, 1, bf) == wide        # 192-byte pixels
+    assert name(16, 64, 64, 64, 130, 3, 3, 1, 1, bf) == wide        # C_out % 4 != 0
+    assert name(8, 64, 64, 64, 128, 3, 3, 1, 1, bf) == wide         # 128 tiles < 256 CUs
+    assert name(64, 7, 7, 64, 256, 3, 3, 1, 1, bf) == wide          # 49-pixel images
+    assert name(20, 50, 50, 64, 256, 3, 3, 1, 1, bf) == wide        # last round a quarter full
+    # the patch kernel takes no grouped or mapped launch: the general
+    # entry's fast path may use it, the transposed phases never
+    p = igc.conv_params(stride=1, pad_begin=1)
+    assert igc.conv2d_fwd_general_kernel_name((16, 64, 64, 64), (3, 3, 64, 256),
+                                              (16, 64, 64, 256), p, filter_is_fcrs=False,
+                                              dtype=0) == patch
 
 
 # ------------------------------------------------------------ fused epilogue
@@ -683,7 +712,8 @@ def test_general_gate_against_oracle_sizes():
         if got == 0 and not page:
             if fast:   # the forward kernels with per-side padding, never the tap-fold one
                 assert name in ("igemm_fwd_band_kernel", "igemm_fwd_wide_kernel",
-                                "igemm_fwd_resident_kernel", "igemm_fwd_kernel"), name
+                                "igemm_fwd_patch_kernel", "igemm_fwd_resident_kernel",
+                                "igemm_fwd_kernel"), name
             elif sgroups:
                 assert name == "igemm_fwd_band_kernel"
             else:

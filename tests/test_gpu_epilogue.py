@@ -163,14 +163,16 @@ def test_epilogue_random_sweep(case):
 
 @pytest.mark.parametrize("kern,dt,f", [("band", "bfloat16", 64), ("band", "float8_e4m3fn", 32),
                                        ("tapfold", "bfloat16", 3),
-                                       ("wide", "float16", 96), ("resident", "bfloat16", 32),
+                                       ("wide", "float16", 96), ("patch", "bfloat16", 128),
+                                       ("resident", "bfloat16", 32),
                                        ("tiled", "bfloat16", 64)])
 def test_epilogue_coefficients_at_4_byte_offsets(kern, dt, f):
     """scale and bias only 4-byte aligned (the gate's rule), on each kernel
     family, including the band kernel's 16-byte coefficient loads."""
     shapes = {"band": (2, 12, 12, 64 if dt != "float8_e4m3fn" else 128, 3),
               "tapfold": (2, 12, 12, 128, 3),
-              "wide": (2, 12, 12, 64, 3), "resident": (2, 12, 12, 48, 3),
+              "wide": (2, 12, 12, 64, 3), "patch": (16, 64, 64, 64, 3),
+              "resident": (2, 12, 12, 48, 3),
               "tiled": (1, 12, 12, 96, 5)}
     n, h, w, c, r = shapes[kern]
     p = (r - 1) // 2

@@ -140,7 +140,8 @@ def test_fp8_workload_fcrs_variant_bitwise():
 # pixels, so the epilogue may read the final MFMA's accumulators first.
 PATH_CASES = [
     # id, dtype, N, H, W, C, F, R, S, stride, pad, residual, kernel
-    ("wide256_bf16_tap", "bfloat16", 16, 64, 64, 64, 256, 3, 3, 1, 1, False, "wide"),
+    # (a 1x1 filter: with a spatial filter this layer takes the patch kernel)
+    ("wide256_bf16_tap", "bfloat16", 16, 64, 64, 64, 256, 1, 1, 1, 0, False, "wide"),
     ("wide256_fp16_walk", "float16", 16, 64, 64, 48, 192, 3, 3, 1, 1, True, "wide"),
     ("wide256_fp8_walk", "float8_e4m3fn", 16, 64, 64, 80, 256, 3, 3, 1, 1, False, "wide"),
     ("wide128_bf16_walk_s2_f160", "bfloat16", 4, 30, 30, 96, 160, 3, 3, 2, 1, True, "wide"),
@@ -183,8 +184,22 @@ PATH_CASES = [
     ("eg_bf16_c20_f130", "bfloat16", 1, 14, 13, 20, 130, 3, 3, 1, 0, True, "tiled"),
     ("eg_fp8_c3_s2", "float8_e4m3fn", 1, 33, 31, 3, 16, 3, 3, 2, 2, False, "tiled"),
     ("wide256_fp8_resid", "float8_e4m3fn", 16, 64, 64, 64, 256, 3, 3, 1, 1, True, "wide"),
+    # patch-resident kernel: stride 1, C_in a whole number of 128-byte
+    # chunks, at least one 256-pixel tile per CU.  One chunk; three chunks
+    # (two patch swaps) with C_out = 160 (channel rows past C_out masked);
+    # ragged 60 x 60 output (partial tiles) with C_out = 192; a 1 x 3
+    # filter without padding; 7 x 7 (padding 2: a ragged 62 x 62 output)
+    # with C_out = 256 (two filter stages beside the larger patch)
+    ("patch_bf16_3x3_one_chunk", "bfloat16", 16, 64, 64, 64, 256, 3, 3, 1, 1, False, "patch"),
+    ("patch_fp16_5x5_three_chunks_f160", "float16", 16, 64, 64, 192, 160, 5, 5, 1, 2, True,
+     "patch"),
+    ("patch_fp8_3x3_two_chunks", "float8_e4m3fn", 16, 64, 64, 256, 256, 3, 3, 1, 1, True, "patch"),
+    ("patch_bf16_ragged_f192", "bfloat16", 16, 60, 60, 128, 192, 3, 3, 1, 1, True, "patch"),
+    ("patch_fp8_1x3_f128", "float8_e4m3fn", 16, 64, 66, 128, 128, 1, 3, 1, 0, False, "patch"),
+    ("patch_bf16_7x7_two_stages", "bfloat16", 16, 64, 64, 64, 256, 7, 7, 1, 2, False, "patch"),
 ]
 _KERNEL = {"wide": "igemm_fwd_wide_kernel", "band": "igemm_fwd_band_kernel",
+           "patch": "igemm_fwd_patch_kernel",
            "tapfold": "igemm_fwd_tapfold_kernel",
            "resident": "igemm_fwd_resident_kernel", "tiled": "igemm_fwd_kernel"}
 
