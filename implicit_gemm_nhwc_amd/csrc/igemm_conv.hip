@@ -412,9 +412,10 @@ bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& d
 // Plan of the patch-resident kernel (igemm_patch.hpp), or false when the
 // layer does not fit it: C_out > 64 and a multiple of 4, stride 1, R*S >= 2,
 // C_in a whole number of 128-byte chunks, an image's input and output each
-// below 2^31 bytes.  Workgroups of 64*TM output channels (TM = 4, or 2 when
-// C_out <= 128) and 256 pixel slots; the tile TH x TW of one image (TW =
-// W_out or a power of two from 8 to 256 below it, TH = 256 / TW or H_out)
+// below 2^31 bytes (an output row below 2^24).  Workgroups of 64*TM output
+// channels (TM = 4, or 2 when C_out <= 128) and 256 pixel slots; the tile
+// TH x TW of one image (TW = W_out or a power of two from 8 to 256 below
+// it, at least 8; TH = 256 / TW or H_out)
 // must fill at least 192 of the slots, and the tiles at least one round of
 // one workgroup per CU, three quarters of the last round busy.  Among those:
 // the fewest rounds, then three filter stages over two, then the smallest
@@ -425,6 +426,8 @@ bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& de
         return false;
     if (s.H * s.W * s.C * E >= ((int64_t)1 << 31) || s.Ho * s.Wo * s.F * 2 >= ((int64_t)1 << 31))
         return false;
+    // the epilogue's 24-bit offset arithmetic: an output row below 2^24 bytes
+    if (s.Wo * s.F * 2 >= ((int64_t)1 << 24)) return false;
     const int tm = s.F > 128 ? 4 : 2;
     const int64_t bco = 64 * tm, bpx = 256;
     const int64_t co_tiles = (s.F + bco - 1) / bco;
@@ -440,7 +443,9 @@ bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& de
     for (int k = 0; k < ntw; ++k) {
         const int64_t tw = tws[k];
         const int64_t th = s.Ho < bpx / tw ? s.Ho : bpx / tw;
-        if (th < 1 || th * tw < 192) continue;
+        // (tiles at least 8 pixels wide: the epilogue walks a lane's pixels
+        // 2 or 4 columns at a time with at most one wrap per step)
+        if (tw < 8 || th < 1 || th * tw < 192) continue;
         const int64_t ph = th - 1 + s.R, pw = tw - 1 + s.S;
         const int64_t prow = pw * PATCH_PP + (((tw - pw) * PATCH_PP) % 256 + 256) % 256;
         const int64_t patch = (ph * prow + 1023) / 1024 * 1024;   // whole 1 KB request blocks

@@ -202,6 +202,20 @@ __device__ __forceinline__ uint16_t f32_to_out(float v, int dt) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two outputs rounded and packed into one 32-bit word (lo in the low half)
+// by one packed conversion (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32), the same
+// round-to-nearest-even as f32_to_out.
+__device__ __forceinline__ uint32_t pack_out2(float lo, float hi, int dt) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 f = {lo, hi};
+    if (dt == DT_FP16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, h2));
+    }
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2));
+}
+
 __device__ __forceinline__ float out_to_f32(uint16_t bits, int dt) {
     if (dt == DT_FP16) return (float)__builtin_bit_cast(_Float16, bits);
     return __builtin_bit_cast(float, (uint32_t)bits << 16);
@@ -1321,59 +1335,66 @@ __global__ __launch_bounds__(band_waves(DT) * 64) void igemm_fwd_band_kernel(Con
         // (v_permlane32_swap) leaves the lower half with all 8 channels of
         // group 2k and the upper half with group 2k+1, so every lane stores
         // 16 contiguous bytes and a store instruction writes 32 pixels x 32
-        // contiguous bytes.  No LDS, no barrier.
+        // contiguous bytes.  No LDS, no barrier.  EPI: the scale / bias /
+        // activation path, chosen once (a per-element select would cost its
+        // VALU work on every element).
+        auto run = [&](auto epic) {
+            constexpr bool EPI = decltype(epic)::value;
 #pragma unroll
-        for (int t = 0; t < TN; ++t) {
-            const int p = (wave + BAND_WAVES * t) * 32 + frag_row;
-            const int th = p / a.TW, tw = p - (p / a.TW) * a.TW;
-            const bool pix_ok = (p < P) & (th < th_n) & (tw < tw_n);
-            const int64_t obase = out_pixel3(a, n, oh0 + th, ow0 + tw) * a.ypitch;
+            for (int t = 0; t < TN; ++t) {
+                const int p = (wave + BAND_WAVES * t) * 32 + frag_row;
+                const int th = p / a.TW, tw = p - (p / a.TW) * a.TW;
+                const bool pix_ok = (p < P) & (th < th_n) & (tw < tw_n);
+                const int64_t obase = out_pixel3(a, n, oh0 + th, ow0 + tw) * a.ypitch;
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    float v[8];
+                    for (int k = 0; k < 2; ++k) {
+                        float v[8];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        // copy the elements out first: a bit cast applied to
-                        // a vector subscript reads element 0
-                        const float lo = acc[i][t][8 * k + j];
-                        const float hi = acc[i][t][8 * k + 4 + j];
-                        const auto r = __builtin_amdgcn_permlane32_swap(
-                            __builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi),
-                            false, false);
-                        const unsigned r0 = r[0], r1 = r[1];
-                        v[j] = __builtin_bit_cast(float, r0);
-                        v[4 + j] = __builtin_bit_cast(float, r1);
-                    }
-                    const int co = i * 32 + 8 * (2 * k + half);
-                    if (pix_ok & (co < a.F)) {
-                        if (a.epi) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const float sc = esc[i][k][e >> 2][e & 3];
-                                const float bi = ebi[i][k][e >> 2][e & 3];
-                                v[e] = __builtin_fmaf(sc, v[e], bi);
-                            }
+                        for (int j = 0; j < 4; ++j) {
+                            // copy the elements out first: a bit cast applied
+                            // to a vector subscript reads element 0
+                            const float lo = acc[i][t][8 * k + j];
+                            const float hi = acc[i][t][8 * k + 4 + j];
+                            const auto r = __builtin_amdgcn_permlane32_swap(
+                                __builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi),
+                                false, false);
+                            const unsigned r0 = r[0], r1 = r[1];
+                            v[j] = __builtin_bit_cast(float, r0);
+                            v[4 + j] = __builtin_bit_cast(float, r1);
                         }
-                        if constexpr (RESID) {
-                            const i32x4 sv = *reinterpret_cast<const i32x4*>(a.src + obase + co);
+                        const int co = i * 32 + 8 * (2 * k + half);
+                        if (pix_ok & (co < a.F)) {
+                            if constexpr (EPI) {
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const uint16_t hb = (uint16_t)((unsigned)sv[e >> 1] >> (16 * (e & 1)));
-                                v[e] = __builtin_fmaf(a.beta, out_to_f32(hb, ODT), v[e]);
+                                for (int e = 0; e < 8; ++e) {
+                                    const float sc = esc[i][k][e >> 2][e & 3];
+                                    const float bi = ebi[i][k][e >> 2][e & 3];
+                                    v[e] = __builtin_fmaf(sc, v[e], bi);
+                                }
                             }
-                        }
-                        if (a.epi) epi_act_n<8>(a, v);
-                        i32x4 ov;
+                            if constexpr (RESID) {
+                                const i32x4 sv = *reinterpret_cast<const i32x4*>(a.src + obase + co);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            ov[e] = (int)((unsigned)f32_to_out(v[2 * e], ODT) |
-                                          ((unsigned)f32_to_out(v[2 * e + 1], ODT) << 16));
-                        *reinterpret_cast<i32x4*>(a.y + obase + co) = ov;
+                                for (int e = 0; e < 8; ++e) {
+                                    const uint16_t hb =
+                                        (uint16_t)((unsigned)sv[e >> 1] >> (16 * (e & 1)));
+                                    v[e] = __builtin_fmaf(a.beta, out_to_f32(hb, ODT), v[e]);
+                                }
+                            }
+                            if constexpr (EPI) epi_act_n<8>(a, v);
+                            i32x4 ov;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                ov[e] = (int)pack_out2(v[2 * e], v[2 * e + 1], ODT);
+                            *reinterpret_cast<i32x4*>(a.y + obase + co) = ov;
+                        }
                     }
-                }
-        }
+            }
+        };
+        if (a.epi) run(IntC<1>{});
+        else run(IntC<0>{});
         return;
     }
     __syncthreads();  // patch and filter no longer read
@@ -1803,6 +1824,10 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                     srs, ((rel[q] * (uint32_t)a.F + co) * 2) | (rel[q] & OOB_OFFSET) | cmask, 0,
                     2);
         };
+        // EPI: the scale / bias / activation path, chosen once (a
+        // per-element select would cost its VALU work on every element)
+        auto run = [&](auto epic) {
+        constexpr bool EPI = decltype(epic)::value;
         if constexpr (RESID) load_src(0);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -1819,7 +1844,7 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
             for (int q = 0; q < NI; ++q) {
                 const f32x4 v4 = *reinterpret_cast<const f32x4*>(ereg + (q * PPI + pl) * EP + c4 * 16);
                 float v[4] = {v4[0], v4[1], v4[2], v4[3]};
-                if (a.epi) {
+                if constexpr (EPI) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(esc[e], v[e], ebi[e]);
                 }
@@ -1830,10 +1855,10 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                         v[e] = __builtin_fmaf(a.beta, out_to_f32(h, ODT), v[e]);
                     }
                 }
-                if (a.epi) epi_act_n<4>(a, v);
+                if constexpr (EPI) epi_act_n<4>(a, v);
                 u32x2 ov;
-                ov[0] = (uint32_t)f32_to_out(v[0], ODT) | ((uint32_t)f32_to_out(v[1], ODT) << 16);
-                ov[1] = (uint32_t)f32_to_out(v[2], ODT) | ((uint32_t)f32_to_out(v[3], ODT) << 16);
+                ov[0] = pack_out2(v[0], v[1], ODT);
+                ov[1] = pack_out2(v[2], v[3], ODT);
                 // non-temporal (cache policy NT): the output is written once
                 // and not read again by this kernel; each instruction writes
                 // 128 or 256 contiguous bytes per pixel (measured with C_out
@@ -1844,6 +1869,9 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_wide_kernel(ConvArgs
                     0, 2);
             }
         }
+        };
+        if (a.epi) run(IntC<1>{});
+        else run(IntC<0>{});
     } else {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {

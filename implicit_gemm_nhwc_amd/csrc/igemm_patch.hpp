@@ -325,14 +325,28 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_patch_kernel(ConvArg
     const uint32_t cmask = co < a.F ? 0u : OOB_OFFSET;
     const int th_n = min(a.TH, a.Ho - oh0);
     const int tw_n = min(a.TW, a.Wo - ow0);
-    const float inv_tw = 1.0f / (float)a.TW;
-    // byte offset of this lane's q-th pixel of block j in the image's output
-    auto pix_off = [&](int j, int q) -> uint32_t {
-        const int p = (wpx * TN + j) * 32 + q * PPI + pl;
-        const int tp = small_div(p, a.TW, inv_tw), tq = p - tp * a.TW;
-        const bool ok = (p < P) & (tp < th_n) & (tq < tw_n);
-        const uint32_t o = ((uint32_t)((oh0 + tp) * a.Wo + ow0 + tq) * (uint32_t)a.F + co) * 2u;
-        return ok ? (o | cmask) : OOB_OFFSET;
+    // this lane's pixels in block j: tile pixel p0 + q*PPI for q < NI, a
+    // run walked column by column (tq wraps at TW); byte offsets in the
+    // image's output, out of range for pixels past the tile or the image.
+    // 24-bit multiplies: an image has fewer than 2^24 pixels and a pixel
+    // row of the output fewer than 2^24 bytes.
+    uint32_t off[2][NI];
+    const uint32_t orow = (uint32_t)a.Wo * (uint32_t)a.F * 2u;   // output bytes per row
+    const uint32_t opix = (uint32_t)a.F * 2u;                    // output bytes per pixel
+    auto offsets = [&](int j, uint32_t (&o)[NI]) {
+        const int p0 = (wpx * TN + j) * 32 + pl;
+        int tp = p0 / a.TW, tq = p0 - (p0 / a.TW) * a.TW;
+#pragma unroll
+        for (int q = 0; q < NI; ++q) {
+            const bool ok = (p0 + q * PPI < P) & (tp < th_n) & (tq < tw_n);
+            const uint32_t v = __umul24((uint32_t)(oh0 + tp), orow) +
+                               __umul24((uint32_t)(ow0 + tq), opix) + (uint32_t)co * 2u;
+            o[q] = ok ? (v | cmask) : OOB_OFFSET;
+            tq += PPI;
+            const bool wrap = tq >= a.TW;
+            tq -= wrap ? a.TW : 0;
+            tp += wrap ? 1 : 0;
+        }
     };
     auto stage_block = [&](int j) {
 #pragma unroll
@@ -350,39 +364,49 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_patch_kernel(ConvArg
 #pragma unroll
         for (int q = 0; q < NI; ++q)
             // non-temporal: the source is read exactly once
-            sv[j & 1][q] = __builtin_amdgcn_raw_buffer_load_b64(srs, pix_off(j, q), 0, 2);
+            sv[j & 1][q] = __builtin_amdgcn_raw_buffer_load_b64(srs, off[j & 1][q], 0, 2);
     };
-    if constexpr (RESID) load_src(0);
+    // EPI: the scale / bias / activation path, chosen once for the whole
+    // epilogue (a per-element select would cost its VALU work every time)
+    auto run = [&](auto epic) {
+        constexpr bool EPI = decltype(epic)::value;
+        offsets(0, off[0]);
+        if constexpr (RESID) load_src(0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        if constexpr (RESID) {
-            if (j + 1 < TN) load_src(j + 1);
-        }
-        stage_block(j);
-#pragma unroll
-        for (int q = 0; q < NI; ++q) {
-            const f32x4 v4 = *reinterpret_cast<const f32x4*>(ereg + (q * PPI + pl) * EP + c4 * 16);
-            float v[4] = {v4[0], v4[1], v4[2], v4[3]};
-            if (a.epi) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(esc[e], v[e], ebi[e]);
+        for (int j = 0; j < TN; ++j) {
+            if (j + 1 < TN) {
+                offsets(j + 1, off[(j + 1) & 1]);
+                if constexpr (RESID) load_src(j + 1);
             }
-            if constexpr (RESID) {
+            stage_block(j);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint16_t h = (uint16_t)(sv[j & 1][q][e >> 1] >> (16 * (e & 1)));
-                    v[e] = __builtin_fmaf(a.beta, out_to_f32(h, ODT), v[e]);
+            for (int q = 0; q < NI; ++q) {
+                const f32x4 v4 =
+                    *reinterpret_cast<const f32x4*>(ereg + (q * PPI + pl) * EP + c4 * 16);
+                float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+                if constexpr (EPI) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(esc[e], v[e], ebi[e]);
                 }
+                if constexpr (RESID) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint16_t h = (uint16_t)(sv[j & 1][q][e >> 1] >> (16 * (e & 1)));
+                        v[e] = __builtin_fmaf(a.beta, out_to_f32(h, ODT), v[e]);
+                    }
+                }
+                if constexpr (EPI) epi_act_n<4>(a, v);
+                u32x2 ov;
+                ov[0] = pack_out2(v[0], v[1], ODT);
+                ov[1] = pack_out2(v[2], v[3], ODT);
+                // non-temporal: written once, 128 or 256 contiguous bytes
+                // per pixel per instruction
+                __builtin_amdgcn_raw_buffer_store_b64(ov, yrs, off[j & 1][q], 0, 2);
             }
-            if (a.epi) epi_act_n<4>(a, v);
-            u32x2 ov;
-            ov[0] = (uint32_t)f32_to_out(v[0], ODT) | ((uint32_t)f32_to_out(v[1], ODT) << 16);
-            ov[1] = (uint32_t)f32_to_out(v[2], ODT) | ((uint32_t)f32_to_out(v[3], ODT) << 16);
-            // non-temporal: written once, 128 or 256 contiguous bytes per
-            // pixel per instruction
-            __builtin_amdgcn_raw_buffer_store_b64(ov, yrs, pix_off(j, q), 0, 2);
         }
-    }
+    };
+    if (a.epi) run(IntC<1>{});
+    else run(IntC<0>{});
 }
 
 }  // namespace igc

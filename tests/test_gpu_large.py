@@ -62,9 +62,11 @@ def _windows(x, pix, r, s, st, p):
 
 # id, N, H, W, C, F, stride, pad, kernel; 3x3 bf16 RSCF filters
 LARGE = [
-    # two 943 MB images per 32-bit span (the wide kernel's limit), 2.8 GB in
+    # two 708 MB images per 32-bit span (the wide kernel's limit), 2.1 GB in
     # all, output 2.8 GB; 128-pixel tiles straddle the image boundaries
-    ("wide_3x1920", 3, 1920, 1920, 128, 128, 1, 1, "igemm_fwd_wide_kernel"),
+    ("wide_3x1920", 3, 1920, 1920, 96, 128, 1, 1, "igemm_fwd_wide_kernel"),
+    # the patch kernel's per-image buffers: 943 MB input and output images
+    ("patch_3x1920", 3, 1920, 1920, 128, 128, 1, 1, "igemm_fwd_patch_kernel"),
     # one image of 2,147,024,896 bytes, just under 2^31 (the band kernel's limit)
     ("band_5792sq", 1, 5792, 5792, 32, 8, 1, 1, "igemm_fwd_band_kernel"),
     # two 1.13 GB images exceed the wide kernel's span: the 64-bit fallback
