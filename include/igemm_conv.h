@@ -212,7 +212,8 @@ int32_t conv2d_fwd_noalloc(const void* input, const int64_t in_nhwc[4],
 
 /*
  * Name of the GEMM kernel conv2d_fwd / conv2d_fwd_nk launch for this problem
- * (a static string: "igemm_fwd_band_kernel", "igemm_fwd_wide_kernel",
+ * (a static string: "igemm_fwd_tapfold_kernel", "igemm_fwd_band_kernel",
+ * "igemm_fwd_patch_kernel", "igemm_fwd_wide_kernel",
  * "igemm_fwd_resident_kernel", "igemm_fwd_kernel", or "none" when nothing is
  * launched because the output is empty), or NULL when the shapes or
  * parameters would be declined.  Host-only; pointers play no part (their
