@@ -43,7 +43,8 @@ hipError_t launch_wide(ConvArgs a, hipStream_t stream) {
 // stages 31.0 us, 128x256 in 3 stages 30.7 us, 128x128 in 4 stages (one
 // workgroup per CU) 35.1 us, 256x256 in 2 stages (98 tiles) 42.7 us.  On the
 // fp8 5x5 256->256 layer (256 tiles of 256x256): 256x256 in 2 stages 105 us,
-// 128x128 in 2 stages 115 us, 256x128 in 3 stages 125 us.  TAPK when C_in is
+// 128x128 in 2 stages 115 us, 256x128 in 3 stages 125 us (these four-wave
+// figures predate the eight-wave 256 x 128 tile below).  TAPK when C_in is
 // a whole number of k-tiles.  With at most one 128 x 128 tile per CU,
 // 128 x 64 tiles in three stages.
 template <int DT, bool RESID>
@@ -70,6 +71,20 @@ hipError_t launch_wide_dt(const ConvArgs& a, hipStream_t stream) {
     if (a.F > 128 && px_tiles256 * co_tiles256 >= device_info().cus)
         return tap128 ? launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, true>(a, stream)
                       : launch_wide<DT, 4, 4, 2, 2, 128, 2, RESID, false>(a, stream);
+    // 128 x 128 tiles that would fill between 1.25 and 2 workgroups per CU
+    // (the second slot of many CUs empty) but 256 x 128 tiles that fit one
+    // round: 256 x 128 tiles, 8 waves of 64 x 64 (two per SIMD) in three
+    // stages (144 KB), which read 1.5 rather than 2 staged rows per 128
+    // outputs (strided 3x3 128->256 layer, N=32 56x56 fp16, alternating
+    // medians: 26.1 -> 24.0 us; in two stages 26.4 us)
+    {
+        const int64_t t128 = (((int64_t)a.M + 127) / 128) * ((a.F + 127) / 128);
+        const int64_t t256x128 = (((int64_t)a.M + 127) / 128) * ((a.F + 255) / 256);
+        const int64_t cus = device_info().cus;
+        if (a.F % 256 == 0 && 4 * t128 > 5 * cus && t128 < 2 * cus && t256x128 <= cus)
+            return tap128 ? launch_wide<DT, 2, 2, 4, 2, 128, 3, RESID, true>(a, stream)
+                          : launch_wide<DT, 2, 2, 4, 2, 128, 3, RESID, false>(a, stream);
+    }
     // at most one 128 x 128 tile per CU: 128 x 64 tiles in three stages
     // (72 KB, two workgroups per CU) fill the second workgroup slot
     // (transposed 3x3 stride-1 layer, N=8 64x64 256->128 bf16, whole call:

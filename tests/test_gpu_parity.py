@@ -149,6 +149,10 @@ PATH_CASES = [
     # more 128 x 128 tiles than CUs (384): 128 x 128 tiles; with fewer the
     # cases above take 128 x 64 tiles in three stages
     ("wide128_bf16_many_tiles", "bfloat16", 12, 64, 64, 64, 96, 3, 3, 1, 1, True, "wide"),
+    # 128 x 128 tiles between 1.25 and 2 per CU (368) and C_out a multiple of
+    # 256: 256 x 128 tiles of 8 waves, tap-aligned and walked k-tiles
+    ("wide256x128_bf16_tap_s2", "bfloat16", 30, 56, 56, 128, 256, 3, 3, 2, 1, True, "wide"),
+    ("wide256x128_fp8_walk_s2", "float8_e4m3fn", 30, 56, 56, 80, 256, 3, 3, 2, 1, False, "wide"),
     ("band_u1_bf16", "bfloat16", 2, 20, 20, 16, 48, 3, 3, 1, 1, False, "band"),
     ("band_u2_fp16_tm1", "float16", 2, 20, 20, 32, 24, 5, 5, 1, 2, True, "band"),
     ("band_u1_fp8", "float8_e4m3fn", 2, 20, 20, 64, 64, 3, 3, 1, 1, False, "band"),
