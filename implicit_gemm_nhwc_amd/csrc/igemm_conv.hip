@@ -415,11 +415,13 @@ bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& d
 // below 2^31 bytes (an output row below 2^24).  Workgroups of 64*TM output
 // channels (TM = 4, or 2 when C_out <= 128) and 256 pixel slots; the tile
 // TH x TW of one image (TW = W_out or a power of two from 8 to 256 below
-// it, at least 8; TH = 256 / TW or H_out)
-// must fill at least 192 of the slots, and the tiles at least one round of
-// one workgroup per CU, three quarters of the last round busy.  Among those:
-// the fewest rounds, then three filter stages over two, then the smallest
-// patch (the input bytes each tile stages).
+// it, at least 8; TH = 256 / TW or H_out) must fill at least 3/4 of the
+// slots, and the tiles at least one round of one workgroup per CU, three
+// quarters of the last round busy.  Among those: the fewest rounds, then
+// three filter stages over two, then the smallest patch (the input bytes
+// each tile stages).  When no 256-slot tile qualifies, the same with 128
+// pixel slots (two 32-pixel blocks per wave), which gives mid-size layers
+// enough tiles.
 bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& dev) {
     const int64_t E = elem_bytes(dtype);
     if (s.F <= 64 || s.F % 4 != 0 || s.st != 1 || s.R * s.S < 2 || (s.C * E) % 128 != 0)
@@ -429,55 +431,58 @@ bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& de
     // the epilogue's 24-bit offset arithmetic: an output row below 2^24 bytes
     if (s.Wo * s.F * 2 >= ((int64_t)1 << 24)) return false;
     const int tm = s.F > 128 ? 4 : 2;
-    const int64_t bco = 64 * tm, bpx = 256;
+    const int64_t bco = 64 * tm;
     const int64_t co_tiles = (s.F + bco - 1) / bco;
     const int64_t epi = 4 * 32 * (tm * 32 * 4 + 16);   // the epilogue's per-wave regions
-    int64_t tws[7];
-    int ntw = 0;
-    if (s.Wo <= bpx) tws[ntw++] = s.Wo;
-    for (int64_t c : {8, 16, 32, 64, 128, 256})
-        if (c < s.Wo) tws[ntw++] = c;
-    bool found = false;
-    int64_t best_rounds = 0, best_patch = 0;
-    int best_ns = 0;
-    for (int k = 0; k < ntw; ++k) {
-        const int64_t tw = tws[k];
-        const int64_t th = s.Ho < bpx / tw ? s.Ho : bpx / tw;
-        // (tiles at least 8 pixels wide: the epilogue walks a lane's pixels
-        // 2 or 4 columns at a time with at most one wrap per step)
-        if (tw < 8 || th < 1 || th * tw < 192) continue;
-        const int64_t ph = th - 1 + s.R, pw = tw - 1 + s.S;
-        const int64_t prow = pw * PATCH_PP + (((tw - pw) * PATCH_PP) % 256 + 256) % 256;
-        const int64_t patch = (ph * prow + 1023) / 1024 * 1024;   // whole 1 KB request blocks
-        int ns = 0;
-        int64_t lds = 0;
-        for (int c : {3, 2}) {
-            lds = c * bco * 128 + patch;
-            if (lds < epi) lds = epi;
-            if (lds <= dev.lds) {
-                ns = c;
-                break;
+    for (int64_t bpx : {256, 128}) {
+        int64_t tws[7];
+        int ntw = 0;
+        if (s.Wo <= bpx) tws[ntw++] = s.Wo;
+        for (int64_t c : {8, 16, 32, 64, 128, 256})
+            if (c < s.Wo && c <= bpx) tws[ntw++] = c;
+        bool found = false;
+        int64_t best_rounds = 0, best_patch = 0;
+        int best_ns = 0;
+        for (int k = 0; k < ntw; ++k) {
+            const int64_t tw = tws[k];
+            const int64_t th = s.Ho < bpx / tw ? s.Ho : bpx / tw;
+            // (tiles at least 8 pixels wide: the epilogue walks a lane's
+            // pixels 2 or 4 columns at a time with at most one wrap per step)
+            if (tw < 8 || th < 1 || 4 * th * tw < 3 * bpx) continue;
+            const int64_t ph = th - 1 + s.R, pw = tw - 1 + s.S;
+            const int64_t prow = pw * PATCH_PP + (((tw - pw) * PATCH_PP) % 256 + 256) % 256;
+            const int64_t patch = (ph * prow + 1023) / 1024 * 1024;   // whole 1 KB request blocks
+            int ns = 0;
+            int64_t lds = 0;
+            for (int c : {3, 2}) {
+                lds = c * bco * 128 + patch;
+                if (lds < epi) lds = epi;
+                if (lds <= dev.lds) {
+                    ns = c;
+                    break;
+                }
+            }
+            if (ns == 0) continue;
+            const int64_t tiles_h = (s.Ho + th - 1) / th, tiles_w = (s.Wo + tw - 1) / tw;
+            const int64_t tiles = s.N * tiles_h * tiles_w * co_tiles;
+            if (tiles < dev.cus) continue;
+            const int64_t rounds = (tiles + dev.cus - 1) / dev.cus;
+            if (4 * (tiles - (rounds - 1) * dev.cus) < 3 * dev.cus) continue;
+            const bool better = !found || rounds < best_rounds ||
+                                (rounds == best_rounds &&
+                                 (ns > best_ns || (ns == best_ns && patch < best_patch)));
+            if (better) {
+                found = true;
+                best_rounds = rounds;
+                best_ns = ns;
+                best_patch = patch;
+                *out = PatchPlan{(int)th, (int)tw, (int)ph, (int)pw, (int)prow, (int)lds,
+                                 (int)tiles_h, (int)tiles_w, tm, (int)(bpx / 64), ns, tiles};
             }
         }
-        if (ns == 0) continue;
-        const int64_t tiles_h = (s.Ho + th - 1) / th, tiles_w = (s.Wo + tw - 1) / tw;
-        const int64_t tiles = s.N * tiles_h * tiles_w * co_tiles;
-        if (tiles < dev.cus) continue;
-        const int64_t rounds = (tiles + dev.cus - 1) / dev.cus;
-        if (4 * (tiles - (rounds - 1) * dev.cus) < 3 * dev.cus) continue;
-        const bool better = !found || rounds < best_rounds ||
-                            (rounds == best_rounds &&
-                             (ns > best_ns || (ns == best_ns && patch < best_patch)));
-        if (better) {
-            found = true;
-            best_rounds = rounds;
-            best_ns = ns;
-            best_patch = patch;
-            *out = PatchPlan{(int)th, (int)tw, (int)ph, (int)pw, (int)prow, (int)lds,
-                             (int)tiles_h, (int)tiles_w, tm, ns, tiles};
-        }
+        if (found) return true;
     }
-    return found;
+    return false;
 }
 
 // The kernel a problem goes to, in order of preference.

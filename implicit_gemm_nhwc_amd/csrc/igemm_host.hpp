@@ -64,10 +64,11 @@ struct BandPlan {
 
 // Plan of the patch-resident kernel (patch_plan): output tile TH x TW, patch
 // PH x PW pixels at prow bytes per row, TM 32-channel blocks per wave (BCO =
-// 64*TM output channels per workgroup), nstage filter stages, tiles =
-// N * tiles_h * tiles_w * channel tiles workgroups of lds bytes.
+// 64*TM output channels per workgroup), TN 32-pixel blocks per wave (64*TN
+// pixel slots per workgroup), nstage filter stages, tiles = N * tiles_h *
+// tiles_w * channel tiles workgroups of lds bytes.
 struct PatchPlan {
-    int TH, TW, PH, PW, prow, lds, tiles_h, tiles_w, TM, nstage;
+    int TH, TW, PH, PW, prow, lds, tiles_h, tiles_w, TM, TN, nstage;
     int64_t tiles;
 };
 

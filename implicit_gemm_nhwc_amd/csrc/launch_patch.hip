@@ -35,10 +35,16 @@ hipError_t launch_patch(ConvArgs a, const PatchPlan& pp, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int DT, int TM, int TN, bool RESID>
+hipError_t launch_patch_tn(const ConvArgs& a, const PatchPlan& pp, hipStream_t stream) {
+    if (pp.nstage == 3) return launch_patch<DT, TM, TN, 3, RESID>(a, pp, stream);
+    return launch_patch<DT, TM, TN, 2, RESID>(a, pp, stream);
+}
+
 template <int DT, int TM, bool RESID>
 hipError_t launch_patch_tm(const ConvArgs& a, const PatchPlan& pp, hipStream_t stream) {
-    if (pp.nstage == 3) return launch_patch<DT, TM, 4, 3, RESID>(a, pp, stream);
-    return launch_patch<DT, TM, 4, 2, RESID>(a, pp, stream);
+    if (pp.TN == 4) return launch_patch_tn<DT, TM, 4, RESID>(a, pp, stream);
+    return launch_patch_tn<DT, TM, 2, RESID>(a, pp, stream);
 }
 
 template <int DT, bool RESID>

@@ -220,8 +220,9 @@ def test_kernel_selection():
 def test_patch_kernel_selection():
     """The patch-resident kernel takes stride-1 layers with C_out > 64 (a
     multiple of 4), a spatial filter and C_in a whole number of 128-byte
-    chunks, when 256-pixel tiles of one image (at least 192 of their slots
-    used) give every CU a workgroup; the wide kernel takes the rest."""
+    chunks, when 256-pixel (else 128-pixel) tiles of one image, at least
+    3/4 of their slots used, give every CU a workgroup; the wide kernel
+    takes the rest."""
     def name(n, h, w, c, f, r, s, st, p, dt):
         ho, wo = (h + 2 * p - r) // st + 1, (w + 2 * p - s) // st + 1
         return igc.conv2d_fwd_kernel_name((n, h, w, c), (r, s, c, f), (n, ho, wo, f),
@@ -235,9 +236,14 @@ def test_patch_kernel_selection():
     assert name(16, 64, 64, 64, 256, 1, 1, 1, 0, bf) == wide        # no spatial filter
     assert name(16, 64, 64, 96, 256, 3, 3, 1, 1, bf) == wide        # 192-byte pixels
     assert name(16, 64, 64, 64, 130, 3, 3, 1, 1, bf) == wide        # C_out % 4 != 0
-    assert name(8, 64, 64, 64, 128, 3, 3, 1, 1, bf) == wide         # 128 tiles < 256 CUs
+    # 128 tiles of 256 pixels, 256 of 128 pixels: the 128-pixel plan
+    assert name(8, 64, 64, 64, 128, 3, 3, 1, 1, bf) == patch
+    assert name(4, 64, 64, 64, 128, 3, 3, 1, 1, bf) == wide         # 128 tiles even of 128 pixels
     assert name(64, 7, 7, 64, 256, 3, 3, 1, 1, bf) == wide          # 49-pixel images
-    assert name(20, 50, 50, 64, 256, 3, 3, 1, 1, bf) == wide        # last round a quarter full
+    # 50 x 50: 256-pixel tiles leave the last round a quarter full, 100-pixel
+    # ones (2 x 50) fill 500 tiles
+    assert name(20, 50, 50, 64, 256, 3, 3, 1, 1, bf) == patch
+    assert name(5, 50, 50, 64, 256, 3, 3, 1, 1, bf) == wide         # too few tiles either way
     # the patch kernel takes no grouped or mapped launch: the general
     # entry's fast path may use it, the transposed phases never
     p = igc.conv_params(stride=1, pad_begin=1)

@@ -201,6 +201,10 @@ PATH_CASES = [
     ("patch_bf16_ragged_f192", "bfloat16", 16, 60, 60, 128, 192, 3, 3, 1, 1, True, "patch"),
     ("patch_fp8_1x3_f128", "float8_e4m3fn", 16, 64, 66, 128, 128, 1, 3, 1, 0, False, "patch"),
     ("patch_bf16_7x7_two_stages", "bfloat16", 16, 64, 64, 64, 256, 7, 7, 1, 2, False, "patch"),
+    # 128-pixel tiles (256-pixel ones would leave half the CUs idle): 64 and
+    # 128 output channels per wave
+    ("patch128_bf16_f128_resid", "bfloat16", 8, 64, 64, 64, 128, 3, 3, 1, 1, True, "patch"),
+    ("patch128_fp8_f256", "float8_e4m3fn", 8, 64, 64, 128, 256, 3, 3, 1, 1, False, "patch"),
 ]
 _KERNEL = {"wide": "igemm_fwd_wide_kernel", "band": "igemm_fwd_band_kernel",
            "patch": "igemm_fwd_patch_kernel",
