@@ -409,6 +409,12 @@ bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& d
     return found;
 }
 
+// An output map (ConvArgs::ymap): GEMM pixel (n, oh, ow) to output pixel
+// (n, oh*ysh, ow*ysw) of images of Hy x Wy pixels.
+struct OutMap {
+    int Hy, Wy, ysh, ysw;
+};
+
 // Plan of the patch-resident kernel (igemm_patch.hpp), or false when the
 // layer does not fit it: C_out > 64 and a multiple of 4, stride 1, R*S >= 2,
 // C_in a whole number of 128-byte chunks, an image's input and output each
@@ -421,15 +427,21 @@ bool tapfold_plan(const Shape& s, int32_t dtype, BandPlan* out, const DevInfo& d
 // three filter stages over two, then the smallest patch (the input bytes
 // each tile stages).  When no 256-slot tile qualifies, the same with 128
 // pixel slots (two 32-pixel blocks per wave), which gives mid-size layers
-// enough tiles.
-bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& dev) {
+// enough tiles.  A grouped launch of `groups` problems counts all their
+// tiles; an output map (map) sets the output image and row the limits
+// above apply to.
+bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& dev,
+                int groups = 1, const OutMap* map = nullptr) {
     const int64_t E = elem_bytes(dtype);
     if (s.F <= 64 || s.F % 4 != 0 || s.st != 1 || s.R * s.S < 2 || (s.C * E) % 128 != 0)
         return false;
-    if (s.H * s.W * s.C * E >= ((int64_t)1 << 31) || s.Ho * s.Wo * s.F * 2 >= ((int64_t)1 << 31))
+    const int64_t hy = map ? map->Hy : s.Ho, wy = map ? map->Wy : s.Wo;
+    const int64_t row_px = map ? (int64_t)map->ysh * map->Wy : s.Wo;   // pixels per tile row
+    if (s.H * s.W * s.C * E >= ((int64_t)1 << 31) || hy * wy * s.F * 2 >= ((int64_t)1 << 31))
         return false;
     // the epilogue's 24-bit offset arithmetic: an output row below 2^24 bytes
-    if (s.Wo * s.F * 2 >= ((int64_t)1 << 24)) return false;
+    if (row_px * s.F * 2 >= ((int64_t)1 << 24)) return false;
+    const int64_t ng = groups > 1 ? groups : 1;
     const int tm = s.F > 128 ? 4 : 2;
     const int64_t bco = 64 * tm;
     const int64_t co_tiles = (s.F + bco - 1) / bco;
@@ -464,10 +476,11 @@ bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& de
             }
             if (ns == 0) continue;
             const int64_t tiles_h = (s.Ho + th - 1) / th, tiles_w = (s.Wo + tw - 1) / tw;
-            const int64_t tiles = s.N * tiles_h * tiles_w * co_tiles;
-            if (tiles < dev.cus) continue;
-            const int64_t rounds = (tiles + dev.cus - 1) / dev.cus;
-            if (4 * (tiles - (rounds - 1) * dev.cus) < 3 * dev.cus) continue;
+            const int64_t tiles = s.N * tiles_h * tiles_w * co_tiles;   // per problem
+            const int64_t all = tiles * ng;
+            if (all < dev.cus) continue;
+            const int64_t rounds = (all + dev.cus - 1) / dev.cus;
+            if (4 * (all - (rounds - 1) * dev.cus) < 3 * dev.cus) continue;
             const bool better = !found || rounds < best_rounds ||
                                 (rounds == best_rounds &&
                                  (ns > best_ns || (ns == best_ns && patch < best_patch)));
@@ -489,11 +502,12 @@ bool patch_plan(const Shape& s, int32_t dtype, PatchPlan* out, const DevInfo& de
 enum KernelKind { K_NONE, K_TAPFOLD, K_BAND, K_PATCH, K_WIDE, K_RESIDENT, K_TILED };
 
 // tapfold_ok: the tap-fold kernel may be chosen (it has no output map and
-// is only exercised on the page's symmetric paddings); plain: one problem
-// with no output map (the patch kernel takes no grouped or mapped launch).
+// is only exercised on the page's symmetric paddings); groups, map: a
+// grouped launch of that many problems, an output map (the patch kernel's
+// plan counts the tiles of all the problems).
 KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp, bool tapfold_ok = true,
                          const DevInfo& dev = DevInfo{}, PatchPlan* pp = nullptr,
-                         bool plain = true) {
+                         int groups = 1, const OutMap* map = nullptr) {
     if (s.M == 0 || s.F == 0) return K_NONE;
     // C_in not a whole number of 16-byte vectors: only the tiled kernel's
     // element gather takes it
@@ -501,7 +515,7 @@ KernelKind select_kernel(const Shape& s, int32_t dtype, BandPlan* bp, bool tapfo
     if (tapfold_ok && tapfold_plan(s, dtype, bp, dev)) return K_TAPFOLD;
     if (band_plan(s, dtype, bp, dev)) return K_BAND;
     PatchPlan tmp;
-    if (plain && patch_plan(s, dtype, pp ? pp : &tmp, dev)) return K_PATCH;
+    if (patch_plan(s, dtype, pp ? pp : &tmp, dev, groups, map)) return K_PATCH;
     if (wide_ok(s, dtype)) return K_WIDE;
     if (resident_ok(s, dtype)) return K_RESIDENT;
     return K_TILED;
@@ -518,12 +532,6 @@ struct Group {
     int split = 0;
     int64_t y2 = 0, src2 = 0;
     int dpt = 0, dpl = 0;
-};
-
-// An output map (ConvArgs::ymap): GEMM pixel (n, oh, ow) to output pixel
-// (n, oh*ysh, ow*ysw) of images of Hy x Wy pixels.
-struct OutMap {
-    int Hy, Wy, ysh, ysw;
 };
 
 template <int DT>
@@ -604,10 +612,10 @@ hipError_t launch_igemm(const void* input, const void* nk, void* output, const v
         tapfold_ok = false;
     }
     const bool resid = source != nullptr;
-    const bool plain = !(grp && grp->n > 1) && !map;
     BandPlan bp;
     PatchPlan pp;
-    const KernelKind kind = select_kernel(s, dtype, &bp, tapfold_ok, device_info(), &pp, plain);
+    const KernelKind kind = select_kernel(s, dtype, &bp, tapfold_ok, device_info(), &pp,
+                                          grp ? grp->n : 1, map);
     if (kind == K_NONE) return hipSuccess;
     if (wraw && kind != K_BAND) return hipErrorInvalidValue;
     switch (dtype) {

@@ -60,10 +60,13 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_patch_kernel(ConvArg
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wco = wave / WPX, wpx = wave % WPX;
 
-    // tile: co_tiles channel tiles of each pixel tile are consecutive (one XCD)
+    // tile: co_tiles channel tiles of each pixel tile are consecutive (one
+    // XCD); a grouped launch (the phases of a transposed convolution) runs
+    // `groups` such problems, group_block moving NK, output, source and
+    // padding to this workgroup's
     const int per_img = a.tiles_h * a.tiles_w;
     const int ntile = a.px_tiles * a.co_tiles;   // px_tiles = N * per_img
-    const int tile = xcd_remap((int)blockIdx.x, ntile);
+    const int tile = xcd_remap(group_block(a, ntile), ntile);
     const int co_tile = tile % a.co_tiles;
     const int ptile = tile / a.co_tiles;
     const int n = ptile / per_img;
@@ -318,7 +321,9 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_patch_kernel(ConvArg
     float esc[4], ebi[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) epi_coef(a, co + e, &esc[e], &ebi[e]);
-    const int64_t oimg = (int64_t)a.Ho * a.Wo * a.F;   // output elements per image
+    // output pixel (n, oh, ow) is pixel (n, oh*ysh, ow*ysw) of Hy x Wy images
+    // (the identity without an output map)
+    const int64_t oimg = (int64_t)a.Hy * a.Wy * a.F;   // output elements per image
     const __amdgpu_buffer_rsrc_t yrs = make_rsrc(a.y + (int64_t)n * oimg, (uint32_t)(oimg * 2));
     const __amdgpu_buffer_rsrc_t srs =
         make_rsrc(RESID ? a.src + (int64_t)n * oimg : a.y, RESID ? (uint32_t)(oimg * 2) : 0u);
@@ -331,8 +336,8 @@ __global__ __launch_bounds__(WCO * WPX * 64) void igemm_fwd_patch_kernel(ConvArg
     // 24-bit multiplies: an image has fewer than 2^24 pixels and a pixel
     // row of the output fewer than 2^24 bytes.
     uint32_t off[2][NI];
-    const uint32_t orow = (uint32_t)a.Wo * (uint32_t)a.F * 2u;   // output bytes per row
-    const uint32_t opix = (uint32_t)a.F * 2u;                    // output bytes per pixel
+    const uint32_t orow = (uint32_t)(a.ysh * a.Wy) * (uint32_t)a.F * 2u;   // bytes per tile row
+    const uint32_t opix = (uint32_t)a.ysw * (uint32_t)a.F * 2u;            // bytes per tile column
     auto offsets = [&](int j, uint32_t (&o)[NI]) {
         const int p0 = (wpx * TN + j) * 32 + pl;
         int tp = p0 / a.TW, tq = p0 - (p0 / a.TW) * a.TW;

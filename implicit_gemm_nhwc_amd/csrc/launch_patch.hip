@@ -30,8 +30,8 @@ hipError_t launch_patch(ConvArgs a, const PatchPlan& pp, hipStream_t stream) {
     a.px_tiles = (int)(pp.tiles / a.co_tiles);
     if (pp.tiles == 0) return hipSuccess;
     a.lds_bytes = pp.lds;
-    hipLaunchKernelGGL(kern, dim3((unsigned)pp.tiles), dim3(WCO * WPX * 64), (size_t)pp.lds, stream,
-                       a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(pp.tiles * (a.groups > 1 ? a.groups : 1))),
+                       dim3(WCO * WPX * 64), (size_t)pp.lds, stream, a);
     return hipGetLastError();
 }
 

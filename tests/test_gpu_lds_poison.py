@@ -60,10 +60,11 @@ def test_kernel_paths_poisoned(case):
     _assert_close(out, ref, TOL[dt], cid)
 
 
-# dtype, N, H, W, C, F, (R, S), stride, dilation, padding: grouped band and
-# wide phases, one-by-one phases, dilated (tiled) phases
+# dtype, N, H, W, C, F, (R, S), stride, dilation, padding: grouped band,
+# wide and patch phases, one-by-one phases, dilated (tiled) phases
 TRANSPOSED = [
     ("bfloat16", 2, 10, 9, 32, 48, (4, 4), 2, 1, 1),
+    ("bfloat16", 8, 32, 32, 256, 128, (4, 4), 2, 1, 1),
     ("float8_e4m3fn", 1, 8, 8, 128, 136, (2, 2), 2, 1, 0),
     ("float16", 1, 7, 6, 32, 40, (3, 3), 3, 1, 1),
     ("bfloat16", 1, 9, 8, 64, 24, (3, 2), 2, (2, 1), (1, 0)),

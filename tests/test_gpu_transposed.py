@@ -53,9 +53,16 @@ CASES = [
     # (band kernel above for R = 4, 2, 6; wide kernel here)
     ("bfloat16", 2, 10, 12, 64, 96, 4, 2, 1, True),
     ("float8_e4m3fn", 1, 8, 8, 128, 256, 2, 2, 0, False),
-    # enough 128 x 128 tiles over the four phases (512) for the grouped wide
-    # launch to keep 128 x 128 tiles (smaller ones take 128 x 64)
+    # 128-byte channel chunks and enough 128-pixel tiles over the four phases
+    # (256): the grouped, mapped launch of the patch kernel, 128 and 256
+    # output channels per workgroup (the first is the benchmark's upsampler)
+    ("bfloat16", 8, 32, 32, 256, 128, 4, 2, 1, True),
+    ("float8_e4m3fn", 8, 32, 32, 128, 256, 4, 2, 1, False),
     ("bfloat16", 8, 32, 32, 64, 256, 4, 2, 1, True),
+    # 192-byte pixels: enough 128 x 128 tiles over the four phases (512) for
+    # the grouped wide launch to keep 128 x 128 tiles (smaller ones take
+    # 128 x 64)
+    ("bfloat16", 8, 32, 32, 96, 256, 4, 2, 1, True),
 ]
 
 
