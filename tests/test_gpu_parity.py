@@ -266,6 +266,61 @@ def test_random_sweep(case):
     _assert_close(out, ref, TOL[dt], str(case))
 
 
+def _patch_sweep_cases():
+    """Random layers the patch-resident kernel takes (stride 1, C_out > 64 and
+    a multiple of 4, C_in a whole number of 128-byte chunks, enough tiles:
+    draws the host-side kernel query sends elsewhere are skipped), with
+    ragged sizes, 1 x 2 up to 5 x 5 filters, every padding, residuals and
+    RSCF / FCRS filters; at most 30 GFLOP each for the oracle."""
+    rng = np.random.default_rng(77)
+    tdt = {"bfloat16": torch.bfloat16, "float16": torch.float16,
+           "float8_e4m3fn": torch.float8_e4m3fn}
+    cases = []
+    for i in range(400):
+        if len(cases) == 14:
+            break
+        dt = ["bfloat16", "float16", "float8_e4m3fn"][len(cases) % 3]
+        e = 1 if dt == "float8_e4m3fn" else 2
+        c = int(rng.choice([128, 256])) // e
+        f = int(rng.choice([68, 100, 128, 132, 192, 256]))
+        r = int(rng.integers(1, 6))
+        s = int(rng.integers(1 if r > 1 else 2, 6))
+        p = int(rng.integers(0, 3))
+        n = int(rng.choice([8, 12, 16]))
+        h = int(rng.integers(40, 80))
+        w = int(rng.integers(40, 80))
+        resid = bool(rng.integers(0, 2))
+        fcrs = bool(rng.integers(0, 2))
+        ho, wo = oracle.out_size(h, r, 1, p), oracle.out_size(w, s, 1, p)
+        if 2 * n * ho * wo * f * r * s * c > 30e9:
+            continue
+        ws = (f, c, r, s) if fcrs else (r, s, c, f)
+        if igc.conv2d_fwd_kernel_name((n, h, w, c), ws, (n, ho, wo, f), filter_is_fcrs=fcrs,
+                                      dtype=tdt[dt], stride=1,
+                                      padding=p) != "igemm_fwd_patch_kernel":
+            continue
+        cases.append((dt, fcrs, p, resid, n, h, w, c, f, r, s))
+    return cases
+
+
+@pytest.mark.parametrize("case", _patch_sweep_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_patch_random_sweep(case):
+    dt, fcrs, p, resid, n, h, w, c, f, r, s = case
+    ho, wo = oracle.out_size(h, r, 1, p), oracle.out_size(w, s, 1, p)
+    _say(f"patch sweep {case} -> out {n}x{ho}x{wo}x{f}")
+    x, wt, src = datagen.make_case(N=n, H=h, W=w, C=c, F=f, R=r, S=s, dtype=dt, fcrs=fcrs,
+                                   x_dist=("normal", 1.0), w_dist=("uniform", 1.0),
+                                   src_dist=("normal", 1.0) if resid else None,
+                                   out_hw=(ho, wo), seed=zlib.crc32(repr(case).encode()) % 1000)
+    assert igc.conv2d_fwd_kernel_name(x.shape, wt.shape, (n, ho, wo, f), filter_is_fcrs=fcrs,
+                                      dtype=x.dtype, stride=1,
+                                      padding=p) == "igemm_fwd_patch_kernel", case
+    beta = -0.75 if resid else 0.0
+    out = _run(x, wt, fcrs=fcrs, stride=1, pad=p, src=src, beta=beta)
+    ref = oracle.conv2d(x, wt, filter_is_fcrs=fcrs, stride=1, padding=p, source=src, beta=beta)
+    _assert_close(out, ref, TOL[dt], str(case))
+
+
 @pytest.mark.parametrize("dt", ["bfloat16", "float8_e4m3fn"])
 @pytest.mark.parametrize("m_extra", [1, 15, 17, 255, 257])
 def test_pixel_tails(dt, m_extra):
