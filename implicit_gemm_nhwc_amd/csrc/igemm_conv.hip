@@ -988,10 +988,10 @@ hipError_t run_transposed(const TPlan& t, const void* input, const void* filter,
 // The parameters page "dispatch_amd_4wave_conv2d" (Args) lists and its
 // dispatcher restricts, widened: per-axis stride, dilation, padding before
 // and after each axis, and channel groups.  A problem inside the page's gate
-// runs exactly as conv2d_fwd.  One group at unit dilation and stride (1,1)
-// or (2,2) with any other padding runs on the same forward kernels (each
-// takes the padding before each axis; the tap-fold kernel is left to the
-// page's paddings).  Several groups at unit dilation and stride (1,1) or
+// runs exactly as conv2d_fwd.  One group at unit dilation and equal strides
+// with any other padding or stride runs on the same forward kernels (each
+// takes the padding before each axis and any stride; the tap-fold kernel is
+// left to the page's problems).  Several groups at unit dilation and stride (1,1) or
 // (2,2) run as super-groups on the band kernel when its gate admits them
 // (see supergroup_plan); one group at stride 1 with dilation as dilation
 // phases on the band kernel (see dilation_plan).  Any other problem runs on
@@ -1003,7 +1003,7 @@ struct GShape {
     int64_t cin;      // input channels, groups * Cg
     int32_t sh, sw, dh, dw, pt, pl, pb, pr, groups;
     bool page;        // inside the page's gate: conv2d_fwd's kernels run it
-    bool fast;        // one group, unit dilation, stride (1,1) or (2,2), any
+    bool fast;        // one group, unit dilation, equal strides, any
                       // padding: the forward kernels (but the tap-fold one) run it
     int32_t q;        // > 0: groups run as super-groups of q (sg below)
     Shape sg;         // one super-group's problem (C = q*Cg, F = q*Fg, its K,
@@ -1151,8 +1151,10 @@ int32_t check_general_shapes(const int64_t in_nhwc[4], int32_t fcrs, const int64
     // tiles per group
     if ((s.M + 127) / 128 * ((s.F / t.groups + 15) / 16) * t.groups >= lim)
         return IGC_DECLINE_SIZE_LIMIT;
-    t.fast = t.groups == 1 && t.dh == 1 && t.dw == 1 && t.sh == t.sw && t.sh <= 2;
-    t.page = t.fast && t.pt == t.pb && t.pt == t.pl && t.pt == t.pr && t.pt <= 2;
+    // one group at unit dilation and equal strides: the forward kernels
+    // (their gathers take any stride; the page restricts it to 1 or 2)
+    t.fast = t.groups == 1 && t.dh == 1 && t.dw == 1 && t.sh == t.sw;
+    t.page = t.fast && t.sh <= 2 && t.pt == t.pb && t.pt == t.pl && t.pt == t.pr && t.pt <= 2;
     s.st = t.sh;
     s.pad = 0;
     s.pt = t.pt;

@@ -439,8 +439,8 @@ size_t conv2d_transposed_workspace_bytes(const int64_t in_nhwc[4], const int64_t
  *              allocation.
  * A problem inside the page's gate (one group, unit dilation, stride (1,1)
  * or (2,2), equal padding 0, 1 or 2 on every side) runs exactly as
- * conv2d_fwd_epilogue; one group at unit dilation and stride (1,1) or (2,2)
- * with other paddings runs on the same forward kernels.  Several groups at
+ * conv2d_fwd_epilogue; one group at unit dilation and equal strides (any)
+ * with other paddings or strides runs on the same forward kernels.  Several groups at
  * unit dilation and stride (1,1) or (2,2) run as super-groups on the band
  * kernel where it admits them: q consecutive groups become one problem of
  * q*Cg input and q*Fg output channels with a block-diagonal NK matrix

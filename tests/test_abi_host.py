@@ -711,7 +711,7 @@ def test_general_gate_against_oracle_sizes():
             pl == pr
         name = igc.conv2d_fwd_general_kernel_name(in_shape, filt, out, p, filter_is_fcrs=fcrs,
                                                   dtype=0)
-        fast = g == 1 and (dh, dw) == (1, 1) and sh == sw and sh <= 2
+        fast = g == 1 and (dh, dw) == (1, 1) and sh == sw
         # several groups of 16 bf16 channels (32 bytes, one MFMA k-step):
         # super-groups on the band kernel
         sgroups = g > 1 and (dh, dw) == (1, 1) and sh == sw and sh <= 2
@@ -763,6 +763,24 @@ def test_general_workspace_bytes(dt):
     i, f, o, p, fcrs, _ = _gen(dtype=dt, groups=4)
     assert igc.conv2d_fwd_general_workspace_bytes(i, f, o, p, filter_is_fcrs=fcrs,
                                                   dtype=dt) == 0
+
+
+@pytest.mark.parametrize("n,h,c,f,r,st,p,dt,want", [
+    (32, 224, 8, 96, 4, 4, 0, 0, "igemm_fwd_wide_kernel"),      # 4x4 stride-4 patchify
+    (2, 25, 64, 48, 3, 3, 1, 0, "igemm_fwd_band_kernel"),
+    (2, 20, 96, 16, 3, 3, 1, 0, "igemm_fwd_resident_kernel"),
+    (2, 25, 64, 128, 3, 3, 1, 1, "igemm_fwd_wide_kernel"),
+    (4, 64, 16, 64, 4, 4, 0, 1, "igemm_fwd_band_kernel"),
+])
+def test_general_equal_strides_beyond_two(n, h, c, f, r, st, p, dt, want):
+    """One group, unit dilation, equal strides above 2 (outside the page's
+    gate even with equal padding): accepted and run on the forward kernels,
+    not the tiled fallback."""
+    ho = (h + 2 * p - r) // st + 1
+    prm = igc.conv_params(stride=st, pad_begin=p)
+    shapes = ((n, h, h, c), (r, r, c, f), (n, ho, ho, f), prm)
+    assert igc.conv2d_fwd_general_query(*shapes, filter_is_fcrs=False, dtype=dt) == 0
+    assert igc.conv2d_fwd_general_kernel_name(*shapes, filter_is_fcrs=False, dtype=dt) == want
 
 
 @pytest.mark.parametrize("g,cg,fg,dt,want", [

@@ -74,6 +74,14 @@ CASES = [
     ("fast_wide_asym_fp16", "float16", 2, 15, 16, 128, 256, 3, 3, 2, 1, (0, 1), (2, 0), 1),
     ("fast_wide_big_pad_bf16", "bfloat16", 1, 12, 13, 64, 96, 3, 3, 1, 1, (5, 0), (0, 6), 1),
     ("fast_resident_bf16", "bfloat16", 2, 9, 11, 96, 16, 3, 3, 1, 1, (1, 0), (0, 2), 1),
+    # equal strides beyond 2: the same forward kernels (their gathers take
+    # any stride)
+    ("fast_s3_band_bf16", "bfloat16", 2, 25, 26, 64, 48, 3, 3, 3, 1, 1, 1, 1),
+    ("fast_s3_band_fp8", "float8_e4m3fn", 2, 25, 26, 64, 48, 3, 3, 3, 1, 1, 1, 1),
+    ("fast_s3_resident_bf16", "bfloat16", 2, 20, 22, 96, 16, 3, 3, 3, 1, 1, 1, 1),
+    ("fast_s3_wide_fp16", "float16", 2, 25, 26, 64, 128, 3, 3, 3, 1, 1, (0, 2), 1),
+    ("fast_s4_patchify_wide_bf16", "bfloat16", 4, 64, 64, 8, 96, 4, 4, 4, 1, 0, 0, 1),
+    ("fast_s4_band_fp16", "float16", 4, 64, 64, 16, 64, 4, 4, 4, 1, 0, 0, 1),
     # several groups, unit dilation, stride 1 or 2: super-groups on the band
     # kernel (block-diagonal NK matrix, pixel pitch C_in / C_out)
     ("sg_g32_many_tiles_bf16", "bfloat16", 3, 28, 30, 256, 256, 3, 3, 1, 1, 1, 1, 32),
@@ -138,7 +146,7 @@ def _supergroup(case):
 def _fast(case):
     _, _, _, _, _, _, _, _, _, st, dil, _, _, g = case
     st, dil = _pair(st), _pair(dil)
-    return g == 1 and dil == (1, 1) and st[0] == st[1] and st[0] <= 2
+    return g == 1 and dil == (1, 1) and st[0] == st[1]
 
 
 def _pair(v):
@@ -188,7 +196,13 @@ def test_general_parity(case):
                 "fast_band_tl_fp8": "igemm_fwd_band_kernel",
                 "fast_wide_asym_fp16": "igemm_fwd_wide_kernel",
                 "fast_wide_big_pad_bf16": "igemm_fwd_wide_kernel",
-                "fast_resident_bf16": "igemm_fwd_resident_kernel"}.get(cid)
+                "fast_resident_bf16": "igemm_fwd_resident_kernel",
+                "fast_s3_band_bf16": "igemm_fwd_band_kernel",
+                "fast_s3_band_fp8": "igemm_fwd_band_kernel",
+                "fast_s3_resident_bf16": "igemm_fwd_resident_kernel",
+                "fast_s3_wide_fp16": "igemm_fwd_wide_kernel",
+                "fast_s4_patchify_wide_bf16": "igemm_fwd_wide_kernel",
+                "fast_s4_band_fp16": "igemm_fwd_band_kernel"}.get(cid)
         assert name != "igemm_fwd_tapfold_kernel"
         if want:
             assert name == want, name
