@@ -13,7 +13,9 @@
 // further on, a uniform offset added to per-lane bases; A fragments come
 // from the filter stage.  This is the page's online gather (page
 // "dispatch_fused_im2col_conv2d_apple", summary) with the gathered columns
-// of all taps served from one staged patch.
+// of all taps served from one staged patch.  A grouped launch runs several
+// problems of one shape (the phases of a transposed convolution), storing
+// through the output map.
 //
 // K runs in the order (chunk, tap, channel in chunk) instead of the NK
 // matrix's (tap, channel): the same products, summed in another order.
