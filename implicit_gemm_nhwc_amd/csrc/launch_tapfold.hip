@@ -12,9 +12,9 @@
 namespace igc {
 namespace {
 
-template <int DT, int KS, bool T3, bool RESID>
-hipError_t launch_tf(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
-    auto kern = igemm_fwd_tapfold_kernel<DT, KS, T3, RESID>;
+template <int DT, int KS, bool T3, bool RESID, bool RPF>
+hipError_t launch_tf_kern(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
+    auto kern = igemm_fwd_tapfold_kernel<DT, KS, T3, RESID, RPF>;
     static LdsAttr attr;
     const hipError_t attr_err = ensure_lds(attr, (const void*)kern, (size_t)device_info().lds);
     if (attr_err != hipSuccess) return attr_err;
@@ -28,6 +28,21 @@ hipError_t launch_tf(ConvArgs a, const BandPlan& bp, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(bp.tiles * (a.groups > 1 ? a.groups : 1))),
                        dim3(TF_WAVES * 64), (size_t)bp.lds, stream, a);
     return hipGetLastError();
+}
+
+// Rows of at most TF_RPF_BLOCKS 1 KB blocks in a two-slot ring go through the
+// loader waves' registers (two rows in flight); others through the
+// load-to-LDS ring.  The register path is built where its A fragments fit
+// the four-waves-per-SIMD bound without spilling: up to 32 registers of
+// them (KS <= 8 for 16-bit types); fp8, whose fragments are twice as wide,
+// spills from KS = 4 and takes it up to KS = 2.
+template <int DT, int KS, bool T3, bool RESID>
+hipError_t launch_tf(const ConvArgs& a, const BandPlan& bp, hipStream_t stream) {
+    if constexpr (DT == DT_FP8 ? KS <= 2 : KS <= 8) {
+        if (bp.groups == 2 && (bp.prow >> 10) <= TF_RPF_BLOCKS)
+            return launch_tf_kern<DT, KS, T3, RESID, true>(a, bp, stream);
+    }
+    return launch_tf_kern<DT, KS, T3, RESID, false>(a, bp, stream);
 }
 
 template <int DT, bool T3, bool RESID>

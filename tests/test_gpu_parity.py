@@ -171,6 +171,12 @@ PATH_CASES = [
     ("tapfold_bf16_1x3_f8", "bfloat16", 1, 17, 300, 32, 8, 1, 3, 1, 0, False, "tapfold"),
     ("tapfold_fp8_s2_p2_resid", "float8_e4m3fn", 2, 19, 23, 128, 3, 3, 3, 2, 2, True, "tapfold"),
     ("tapfold_fp16_c256", "float16", 1, 9, 9, 256, 1, 3, 3, 1, 1, False, "tapfold"),
+    # rows of at most eight 1 KB blocks go through the loader registers (the
+    # cases above but c256 and the fp8 one below): three output rows per
+    # workgroup (five input rows through the two-slot ring); fp8 with
+    # C_in = 256 (four k-steps) keeps the load-to-LDS ring
+    ("tapfold_bf16_rgb_th3_resid", "bfloat16", 4, 128, 128, 128, 3, 3, 3, 1, 1, True, "tapfold"),
+    ("tapfold_fp8_c256_ring", "float8_e4m3fn", 2, 20, 40, 256, 3, 3, 3, 1, 1, False, "tapfold"),
     ("resident_c48", "bfloat16", 2, 20, 20, 48, 32, 3, 3, 1, 1, False, "resident"),
     ("resident_fp16_c48", "float16", 2, 10, 10, 48, 24, 3, 3, 1, 1, True, "resident"),
     ("resident_fp8_single", "float8_e4m3fn", 1, 4, 4, 48, 16, 3, 3, 1, 1, True, "resident"),
