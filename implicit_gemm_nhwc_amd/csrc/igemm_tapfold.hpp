@@ -24,8 +24,10 @@
 // measured); the 16-byte units are instead permuted within each 256-byte
 // window (stage_unit), which keeps the fragment reads of 16 consecutive
 // pixels on 16 different bank groups.  Per
-// input row, the 32-pixel blocks of P are computed (waves take blocks w,
-// w + 4, ...) and written to a ring of R + 1 fp32 P rows; the output row whose
+// input row, the 32-pixel blocks of P are computed (wave w takes blocks
+// 3 - w, 7 - w, ...: a one-block row goes to wave 3, which neither loads
+// nor, below 65 output columns, sums; 17.7 -> 17.4 us on the RGB layer) and
+// written to a ring of R + 1 fp32 P rows; the output row whose
 // last tap row this completes is summed, passed through the fused epilogue
 // and stored.  Waves 0 and 1 issue the row requests and wait on their
 // counter; waves 2 and 3 do the output sums and stores.  A wave that waits
@@ -34,7 +36,8 @@
 // row leave while the next rows are multiplied.  Two barriers per input row.
 // Short rows (at most TF_RPF_BLOCKS 1 KB blocks) take a second path: the
 // loader waves fetch rows into registers two rows ahead and write each into
-// its slot one row ahead, with one barrier per row.
+// its slot one row ahead, with one barrier per row; its first two rows are
+// requested together with the NK rows.
 #pragma once
 
 #include "igemm_kernels.hpp"
@@ -99,43 +102,6 @@ __attribute__((amdgpu_waves_per_eu(RPF ? 4 : 1, 8))) void igemm_fwd_tapfold_kern
     const int p_off = a.patch_off + NSLOT * a.prow;
     const int pslot = (a.PW * a.spitch * 4 + 15) & ~15;
 
-    // coefficients of the fused epilogue (1 and 0 when absent); loaded before
-    // any row request, so their wait holds up nothing
-    if (tid < a.F) {
-        coef[tid] = a.scale ? a.scale[tid] : 1.0f;
-        coef[32 + tid] = a.bias ? a.bias[tid] : 0.0f;
-    }
-    // the NK rows, by buffer-load-to-LDS
-    {
-        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, (uint32_t)nk_bytes);
-        const int fblocks = (nk_bytes + 1023) >> 10;
-        for (int b = wave; b < fblocks; b += TF_WAVES) {
-            const uint32_t off = (uint32_t)(b * 1024 + lane * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                frs, (__attribute__((address_space(3))) void*)(lds + NK_OFF + b * 1024), 16,
-                off < (uint32_t)nk_bytes ? off : OOB_OFFSET, 0, 0, 0);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    // A fragments into registers: folded row j = (co, tap) of this lane, its
-    // 8 (16 for fp8) channels of each k-step; rows past C_out*R*S are zero
-    i32x4 fa[KS][FR];
-    {
-        const int j = frag_row;
-        const int co = j / RS, tp = j - co * RS;
-        const bool ok = co < a.F;
-        const uint8_t* fp =
-            lds + NK_OFF + (ok ? co * a.kpitch * E + tp * cbytes : 0) + half * 16 * FR;
-#pragma unroll
-        for (int t = 0; t < KS; ++t)
-#pragma unroll
-            for (int f = 0; f < FR; ++f)
-                fa[t][f] = ok ? *reinterpret_cast<const i32x4*>(fp + t * KSB + f * 16)
-                              : i32x4{0, 0, 0, 0};
-    }
-    __syncthreads();   // every lane holds its fragments: the ring may be filled
-
     // ---- row requests (waves 0 and 1): input row q of the segment into ring
     // slot q % NSLOT.  Each wave instruction fills one 1 KB block of the
     // slot; lane t of block b fetches the 16-byte unit stage_unit(64 b + t).
@@ -164,6 +130,85 @@ __attribute__((amdgpu_waves_per_eu(RPF ? 4 : 1, 8))) void igemm_fwd_tapfold_kern
                 off | ((uint32_t)!ok << 31), 0, 0, 2);
         }
     };
+    constexpr int NBL = TF_RPF_BLOCKS / 2;
+    i32x4 rbuf[2][NBL];
+    auto load_row = [&](int q, i32x4 (&rb)[NBL]) {
+        const int ih = ih0 + q;
+        const bool row_ok = (q < a.PH) & ((unsigned)ih < (unsigned)a.H);
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int b = wave + 2 * j;
+            const int u = stage_unit(b * 64 + lane, cl);
+            const int px = u >> cl, pos = u & (cpp - 1);
+            const int iw = iw0 + px;
+            const bool ok = row_ok & (b < nrb) & (px < a.PW) & ((unsigned)iw < (unsigned)a.W);
+            const uint32_t off = (uint32_t)((ih * a.W + iw) * cbytes + pos * 16);
+            // non-temporal, as the ring requests
+            rb[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  xrs, off | ((uint32_t)!ok << 31), 0, 2));
+        }
+    };
+    auto store_row = [&](int q, const i32x4 (&rb)[NBL]) {
+        uint8_t* slot = lds + a.patch_off + (q & 1) * a.prow;
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int b = wave + 2 * j;
+            if (b < nrb) *reinterpret_cast<i32x4*>(slot + b * 1024 + lane * 16) = rb[j];
+        }
+    };
+    // coefficients of the fused epilogue (1 and 0 when absent); loaded before
+    // any row request, so their wait holds up nothing
+    if (tid < a.F) {
+        coef[tid] = a.scale ? a.scale[tid] : 1.0f;
+        coef[32 + tid] = a.bias ? a.bias[tid] : 0.0f;
+    }
+    // the NK rows, by buffer-load-to-LDS
+    {
+        const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.nk, (uint32_t)nk_bytes);
+        const int fblocks = (nk_bytes + 1023) >> 10;
+        for (int b = wave; b < fblocks; b += TF_WAVES) {
+            const uint32_t off = (uint32_t)(b * 1024 + lane * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                frs, (__attribute__((address_space(3))) void*)(lds + NK_OFF + b * 1024), 16,
+                off < (uint32_t)nk_bytes ? off : OOB_OFFSET, 0, 0, 0);
+        }
+        if constexpr (RPF) {
+            // rows 0 and 1 requested into registers behind the NK rows (the
+            // ring is not written until the fragments are taken): the wait
+            // covers the NK requests alone, loads completing in order
+            if (loader) {
+                load_row(0, rbuf[0]);
+                load_row(1, rbuf[1]);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NBL) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+    }
+    // (a plain barrier: a fence would also wait for the row requests)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // A fragments into registers: folded row j = (co, tap) of this lane, its
+    // 8 (16 for fp8) channels of each k-step; rows past C_out*R*S are zero
+    i32x4 fa[KS][FR];
+    {
+        const int j = frag_row;
+        const int co = j / RS, tp = j - co * RS;
+        const bool ok = co < a.F;
+        const uint8_t* fp =
+            lds + NK_OFF + (ok ? co * a.kpitch * E + tp * cbytes : 0) + half * 16 * FR;
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+#pragma unroll
+            for (int f = 0; f < FR; ++f)
+                fa[t][f] = ok ? *reinterpret_cast<const i32x4*>(fp + t * KSB + f * 16)
+                              : i32x4{0, 0, 0, 0};
+    }
+    // every lane holds its fragments: the ring may be filled (a plain
+    // barrier, which leaves the row requests in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
     const int nb = (a.PW + 31) >> 5;   // 32-pixel blocks per input row
     const int rp1 = a.R + 1;
     // the work on input row i between two barriers (row i in ring slot
@@ -173,7 +218,7 @@ __attribute__((amdgpu_waves_per_eu(RPF ? 4 : 1, 8))) void igemm_fwd_tapfold_kern
         if (i < a.PH) {
             const uint8_t* srow = lds + a.patch_off + (i % NSLOT) * a.prow;
             float* prow_p = reinterpret_cast<float*>(lds + p_off + (i % rp1) * pslot);
-            for (int blk = wave; blk < nb; blk += TF_WAVES) {
+            for (int blk = TF_WAVES - 1 - wave; blk < nb; blk += TF_WAVES) {
                 const int px = blk * 32 + frag_row;
                 // pixels past the row read pixel 0 (kept 16-aligned for the
                 // swizzle) and are never written
@@ -272,35 +317,8 @@ __attribute__((amdgpu_waves_per_eu(RPF ? 4 : 1, 8))) void igemm_fwd_tapfold_kern
         // step i - 1's barrier), while every wave works on row i; one
         // barrier per row.  With one row in flight per workgroup the row's
         // HBM latency was waited out every step (RGB layer: 22.2 -> 18.4 us).
-        constexpr int NBL = TF_RPF_BLOCKS / 2;
-        i32x4 rbuf[2][NBL];
-        auto load_row = [&](int q, i32x4 (&rb)[NBL]) {
-            const int ih = ih0 + q;
-            const bool row_ok = (q < a.PH) & ((unsigned)ih < (unsigned)a.H);
-#pragma unroll
-            for (int j = 0; j < NBL; ++j) {
-                const int b = wave + 2 * j;
-                const int u = stage_unit(b * 64 + lane, cl);
-                const int px = u >> cl, pos = u & (cpp - 1);
-                const int iw = iw0 + px;
-                const bool ok = row_ok & (b < nrb) & (px < a.PW) & ((unsigned)iw < (unsigned)a.W);
-                const uint32_t off = (uint32_t)((ih * a.W + iw) * cbytes + pos * 16);
-                // non-temporal, as the ring requests
-                rb[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      xrs, off | ((uint32_t)!ok << 31), 0, 2));
-            }
-        };
-        auto store_row = [&](int q, const i32x4 (&rb)[NBL]) {
-            uint8_t* slot = lds + a.patch_off + (q & 1) * a.prow;
-#pragma unroll
-            for (int j = 0; j < NBL; ++j) {
-                const int b = wave + 2 * j;
-                if (b < nrb) *reinterpret_cast<i32x4*>(slot + b * 1024 + lane * 16) = rb[j];
-            }
-        };
+        // Rows 0 and 1 were requested with the NK rows (18.7 -> 17.7 us).
         if (loader) {
-            load_row(0, rbuf[0]);
-            load_row(1, rbuf[1]);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NBL) : "memory");   // row 0 arrived
             store_row(0, rbuf[0]);
         }
