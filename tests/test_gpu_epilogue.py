@@ -162,7 +162,8 @@ def test_epilogue_random_sweep(case):
 
 
 @pytest.mark.parametrize("kern,dt,f", [("band", "bfloat16", 64), ("band", "float8_e4m3fn", 32),
-                                       ("tapfold", "bfloat16", 3),
+                                       ("tapfold", "bfloat16", 3), ("tapfold", "float16", 3),
+                                       ("tapfold", "float8_e4m3fn", 3),
                                        ("wide", "float16", 96), ("patch", "bfloat16", 128),
                                        ("resident", "bfloat16", 32),
                                        ("tiled", "bfloat16", 64)])
